@@ -1,0 +1,191 @@
+/*
+ * fd.h - C ABI of the MI355X (gfx950) single-query decode-attention library.
+ *
+ * One call computes, for every sequence b and query head h of a batch,
+ *     out[b,h] = softmax(scale * q[b,h] . K_b^T) V_b,    lse[b,h] = ln sum exp(...)
+ * over that sequence's cached keys and values, the way split-KV Flash-Decoding
+ * does it: the cache is cut into chunks along the sequence, every chunk yields
+ * a partial (m_i, l_i, O_i) in parallel, and the partials are merged exactly
+ * through the exp(m_i - m) rescale.
+ *   - Standard attention and its four steps: "Flash Decoding" explainer
+ *     (aiqz.cc), section 1.
+ *   - Split-KV partials and the exact merge: same page, section 2 (the
+ *     displayed merge assumes normalised partials; this library keeps
+ *     unnormalised O_i and divides by sum exp(m_i - m) l_i, which is the same
+ *     value).
+ *
+ * Conventions shared by every entry point
+ *   - All pointers except `ws_bytes` and `stream` are DEVICE pointers.  The
+ *     caller allocates every buffer; the library never allocates or frees.
+ *   - Layouts are dense row-major with the shapes given below; element types
+ *     are bf16 (raw 16-bit storage), fp32, fp16 (raw 16-bit storage), int8,
+ *     int32 or uint32 as stated.  Alignment: q, k, v, pools, out and packed
+ *     arrays 16 bytes; ws 256 bytes.
+ *   - Grouped-query heads: query head h reads kv-head h / (Hq / Hkv).
+ *   - `scale` is the score scale, normally 1/sqrt(d).  Scores, `phi`,
+ *     margins and `delta` are all in units of scale * (q . k).
+ *   - `out` is always fp32 [B, Hq, d]; `lse` (nullable) is fp32 [B, Hq].
+ *   - Workspace, two phases: with ws == NULL the call stores the bytes it
+ *     needs in *ws_bytes and returns FD_OK without touching the GPU; with
+ *     ws != NULL it returns FD_ERR_WORKSPACE if *ws_bytes is smaller.  The
+ *     workspace holds the per-chunk partials between the kernels of one call;
+ *     its contents are not meaningful to the caller.
+ *   - Work is enqueued on `stream` (a hipStream_t; NULL = default stream) and
+ *     returns without waiting.  Inputs must stay alive and unmodified until
+ *     the stream has passed the call.  Calls on one stream may reuse one
+ *     workspace; concurrent calls on different streams need their own.
+ *   - Arguments are validated before anything is enqueued; a non-zero return
+ *     means nothing was launched (except FD_ERR_HIP, reported after a launch
+ *     failed).  fd_last_error() then describes the failure.
+ *   - Non-finite values in q/K/V propagate; the kernels do not check data.
+ *   - Supported: d in {64, 128}; Hq / Hkv in {1, 2, 4, 8}; chunk a positive
+ *     multiple of 16 no larger than 65536.
+ */
+#ifndef FD_H_
+#define FD_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { FD_F32 = 0, FD_BF16 = 1 } fd_dtype_t;
+
+enum {
+  FD_OK = 0,
+  FD_ERR_ARG = 1,          /* null pointer, non-positive size, bad shape */
+  FD_ERR_UNSUPPORTED = 2,  /* valid but not implemented (d, group size, dtype) */
+  FD_ERR_WORKSPACE = 3,    /* *ws_bytes smaller than required */
+  FD_ERR_HIP = 4           /* a HIP call or kernel launch failed */
+};
+
+/* Message for the last non-FD_OK return on the calling thread ("" if none).
+ * The pointer stays valid until the next library call on that thread. */
+const char* fd_last_error(void);
+
+/* Library ABI version (increments on any signature or layout change). */
+int fd_abi_version(void);
+
+/*
+ * Dense decode attention over a contiguous cache.
+ *   dt      element type of q, k and v (FD_F32 or FD_BF16)
+ *   q       [B, Hq, d]
+ *   k, v    [B, Hkv, L, d]
+ *   out     fp32 [B, Hq, d];   lse  fp32 [B, Hq] or NULL
+ *   L       cached positions per sequence (>= 1)
+ *   chunk   positions per split-KV chunk; chunk c covers
+ *           [c*chunk, min((c+1)*chunk, L)), n_chunks = ceil(L / chunk).
+ * The result does not depend on `chunk` beyond fp32 rounding.
+ */
+int fd_decode_attn(fd_dtype_t dt, const void* q, const void* k, const void* v,
+                   float* out, float* lse,
+                   int B, int Hq, int Hkv, int L, int d, float scale, int chunk,
+                   void* ws, size_t* ws_bytes, void* stream);
+
+/*
+ * Dense decode attention over a paged cache ("Flash Decoding" explainer,
+ * section 3: the cache is cut into fixed-size pages allocated on demand).
+ *   dt              FD_BF16 or FD_F32 (element type of q and both pools)
+ *   k_pool, v_pool  [num_pages, Hkv, page_size, d]: one page holds page_size
+ *                   consecutive positions of every kv-head of one sequence
+ *   block_table     int32 [B, max_pages_per_seq]: position t of sequence b
+ *                   is slot t % page_size of page block_table[b, t / page_size]
+ *   seq_lens        int32 [B], device; 0 is allowed (out = 0, lse = -inf)
+ *   max_seq_len     host-side upper bound of seq_lens (sizes grid and
+ *                   workspace); must not exceed max_pages_per_seq * page_size
+ *   page_size       a power of two in [8, 1024]; chunk % page_size == 0
+ * Device-side values are clamped so that nothing is read out of bounds: a
+ * length above max_seq_len is treated as max_seq_len and a page id outside
+ * [0, num_pages) as the nearest valid id (the result is then meaningless).
+ */
+int fd_decode_attn_paged(fd_dtype_t dt, const void* q, const void* k_pool,
+                         const void* v_pool, const int32_t* block_table,
+                         const int32_t* seq_lens, float* out, float* lse,
+                         int B, int Hq, int Hkv, int d, int page_size,
+                         int max_pages_per_seq, int num_pages, int max_seq_len,
+                         float scale, int chunk,
+                         void* ws, size_t* ws_bytes, void* stream);
+
+/*
+ * Decode attention with a fixed ("unified") maximum and overflow fallback
+ * ("FlashDecoding" deployment blog, section 1 and the fixed_max_value /
+ * fallback_on_overflow settings of section 3): every chunk takes its
+ * exponentials against the caller's constant phi instead of its own maximum,
+ * so chunks need no shared running maximum and the merge needs no rescale.
+ * A chunk is out of range for head h when its largest score exceeds
+ * phi + margin_hi or falls below phi - margin_lo; such chunks are recomputed
+ * exactly with their own maximum, inside the same kernel, before the merge.
+ * The result is the dense result (softmax is shift invariant) for any finite
+ * phi.
+ *   Arguments as fd_decode_attn, plus
+ *   phi, margin_hi, margin_lo   finite; margins >= 0
+ *   chunk_flags   uint8 [B, Hq, n_chunks] or NULL: 1 where the chunk was out
+ *                 of range for that head, else 0.
+ */
+int fd_decode_attn_unified_max(fd_dtype_t dt, const void* q, const void* k,
+                               const void* v, float* out, float* lse,
+                               int B, int Hq, int Hkv, int L, int d, float scale,
+                               int chunk, float phi, float margin_hi,
+                               float margin_lo, uint8_t* chunk_flags,
+                               void* ws, size_t* ws_bytes, void* stream);
+
+/*
+ * FFD key format ("Faster Than Flash" digest, section 5 and Fig. 2: a 2-bit
+ * main part scanned for every position plus an 8-bit residual read only for
+ * candidates).  Per position, per group of 32 consecutive dimensions:
+ *   zero z = fp16(min x), step s = fp16((max x - min x) / 3)
+ *   code c = clamp(rne((x - z) / s), 0, 3)       (c = 0 when s == 0)
+ *   r = x - fma(s, c, z);  rs = fp16(max |r| / 127)
+ *   r8 = clamp(rne(r / rs), -127, 127)           (r8 = 0 when rs == 0)
+ * every step in fp32, round to nearest even.  2-bit key = z + s*c, refined
+ * key = z + s*c + rs*r8.  Arrays, all [B, Hkv, L_cap, ...]:
+ *   codes uint32 [.., d/16]: word w holds dims 16w..16w+15; dim 16w+2p at
+ *         bits 2p..2p+1, dim 16w+2p+1 at bits 16+2p..17+2p (p = 0..7)
+ *   zs    fp16   [.., d/32, 2]   (z, s)
+ *   res   int8   [.., d]
+ *   rs    fp16   [.., d/32]
+ *
+ * fd_ffd_pack quantises bf16 keys k [B, Hkv, L_cap, d] at positions
+ * [t_begin, t_end) of every (b, kv-head) into those arrays (a whole cache, or
+ * the positions appended this step).  Keys must be finite with |x| < 65504.
+ * d in {64, 128}; 0 <= t_begin <= t_end <= L_cap.  No workspace.
+ */
+int fd_ffd_pack(const void* k, uint32_t* codes, uint16_t* zs, int8_t* res,
+                uint16_t* rs, int B, int Hkv, int L_cap, int d, int t_begin,
+                int t_end, void* stream);
+
+/*
+ * FFD sparse decode ("Faster Than Flash" digest, sections 3-6, Fig. 2), per
+ * query head h of sequence b, over positions [0, L):
+ *   1. pseudo-max m^ = max of the refined scores at the anchors: the first
+ *      n_sink positions and the last n_local positions (section 4);
+ *      j* = the lowest anchor position attaining it
+ *   2. 2-bit scan score s~_j for every position (section 5)
+ *   3. candidates C = { j : s~_j >= m^ - delta } plus j* (section 3)
+ *   4. refined scores s^_j (2-bit + 8-bit residual key) for j in C
+ *   5. exact softmax over C with the refined scores, merged over chunks
+ *      with the exact rescale; out/lse as for the dense call.
+ *   q          bf16 [B, Hq, d];  v  bf16 [B, Hkv, L, d]
+ *   packed key arrays as for fd_ffd_pack, with L_cap = L
+ *   delta      >= 0 (the pages use 5 and 7);  n_sink, n_local >= 0,
+ *              n_sink + n_local >= 1
+ *   cand_mask  uint32 [B, Hq, ceil(L/32)] or NULL: bit j%32 of word j/32 set
+ *              when position j is in C
+ *   pseudo_max fp32 [B, Hq] or NULL: m^
+ *   chunk      positions per chunk (multiple of 16)
+ */
+int fd_ffd_sparse_decode(const void* q, const uint32_t* codes,
+                         const uint16_t* zs, const int8_t* res,
+                         const uint16_t* rs, const void* v, float* out,
+                         float* lse, int B, int Hq, int Hkv, int L, int d,
+                         float scale, float delta, int n_sink, int n_local,
+                         int chunk, uint32_t* cand_mask, float* pseudo_max,
+                         void* ws, size_t* ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FD_H_ */

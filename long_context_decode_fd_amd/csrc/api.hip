@@ -1,0 +1,283 @@
+// C ABI entry points (see include/fd.h): argument validation, workspace
+// sizing, kernel dispatch.  Nothing here allocates device memory.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+
+#include <string>
+
+#include "../../include/fd.h"
+#include "internal.hpp"
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return code;
+}
+
+int ok() {
+  g_err.clear();
+  return FD_OK;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+int check_heads(int B, int Hq, int Hkv, int d) {
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || d <= 0)
+    return fail(FD_ERR_ARG, "B=%d Hq=%d Hkv=%d d=%d must be positive", B, Hq, Hkv, d);
+  if (Hq % Hkv != 0) return fail(FD_ERR_ARG, "Hq=%d is not a multiple of Hkv=%d", Hq, Hkv);
+  const int G = Hq / Hkv;
+  if (G != 1 && G != 2 && G != 4 && G != 8)
+    return fail(FD_ERR_UNSUPPORTED, "group size Hq/Hkv=%d not in {1,2,4,8}", G);
+  if (d != 64 && d != 128) return fail(FD_ERR_UNSUPPORTED, "d=%d not in {64,128}", d);
+  return FD_OK;
+}
+
+int check_chunk(int chunk) {
+  if (chunk <= 0 || chunk % 16 != 0 || chunk > 65536)
+    return fail(FD_ERR_ARG, "chunk=%d must be a positive multiple of 16 <= 65536", chunk);
+  return FD_OK;
+}
+
+int check_scale(float scale) {
+  if (!(scale > 0.f) || !isfinite(scale))
+    return fail(FD_ERR_ARG, "scale must be finite and positive");
+  return FD_OK;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
+
+// Partials workspace: O [B*Hq*nc*d] fp32, then (m, l) [B*Hq*nc*2] fp32.
+size_t partial_bytes(int B, int Hq, int nc, int d) {
+  const size_t rows = (size_t)B * Hq * nc;
+  const size_t n = align256(rows * d * sizeof(float)) + align256(rows * 2 * sizeof(float));
+  return n > 256 ? n : 256;
+}
+
+int workspace_gate(void* ws, size_t* ws_bytes, size_t need) {
+  if (ws_bytes == nullptr) return fail(FD_ERR_ARG, "ws_bytes is NULL");
+  if (ws == nullptr) {
+    *ws_bytes = need;
+    return FD_OK;
+  }
+  if (((uintptr_t)ws & 255) != 0) return fail(FD_ERR_ARG, "ws must be 256-byte aligned");
+  if (*ws_bytes < need)
+    return fail(FD_ERR_WORKSPACE, "workspace of %zu bytes, %zu needed", *ws_bytes, need);
+  return FD_OK;
+}
+
+int hip_status(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(FD_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+void split_ws(void* ws, int B, int Hq, int nc, int d, float** o_part, float** ml_part) {
+  const size_t rows = (size_t)B * Hq * nc;
+  *o_part = reinterpret_cast<float*>(ws);
+  *ml_part = reinterpret_cast<float*>(reinterpret_cast<char*>(ws) +
+                                      align256(rows * d * sizeof(float)));
+}
+
+int run_split_kv(int mode, fd_dtype_t dt, const void* q, const void* k, const void* v,
+                 float* out, float* lse, int B, int Hq, int Hkv, int L, int d,
+                 float scale, int chunk, int nc, fdk::PartialArgs pa, void* ws,
+                 const int32_t* seq_lens, int max_seq_len, void* stream) {
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  float *o_part, *ml_part;
+  split_ws(ws, B, Hq, nc, d, &o_part, &ml_part);
+  pa.q = q;
+  pa.k = k;
+  pa.v = v;
+  pa.o_part = o_part;
+  pa.ml_part = ml_part;
+  pa.B = B;
+  pa.Hq = Hq;
+  pa.Hkv = Hkv;
+  pa.L = L;
+  pa.chunk = chunk;
+  pa.nc = nc;
+  pa.c_log2 = (float)((double)scale * 1.4426950408889634);
+  if (nc > 0) {
+    hipError_t e = fdk::launch_partial(mode, dt == FD_BF16, d, Hq / Hkv, pa, s);
+    if (e != hipSuccess) return hip_status(e, "partial kernel launch");
+  }
+  fdk::MergeArgs ma{o_part, ml_part, out, lse, seq_lens, Hq, nc, chunk, max_seq_len};
+  return hip_status(fdk::launch_merge(d, B, ma, s), "merge kernel launch");
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* fd_last_error(void) { return g_err.c_str(); }
+
+int fd_abi_version(void) { return 1; }
+
+int fd_decode_attn(fd_dtype_t dt, const void* q, const void* k, const void* v, float* out,
+                   float* lse, int B, int Hq, int Hkv, int L, int d, float scale, int chunk,
+                   void* ws, size_t* ws_bytes, void* stream) {
+  if (dt != FD_F32 && dt != FD_BF16) return fail(FD_ERR_ARG, "unknown dtype %d", (int)dt);
+  if (int e = check_heads(B, Hq, Hkv, d)) return e;
+  if (L <= 0) return fail(FD_ERR_ARG, "L=%d must be positive", L);
+  if (int e = check_chunk(chunk)) return e;
+  if (int e = check_scale(scale)) return e;
+  const int nc = (L + chunk - 1) / chunk;
+  if (int e = workspace_gate(ws, ws_bytes, partial_bytes(B, Hq, nc, d))) return e;
+  if (ws == nullptr) return ok();
+  if (!q || !k || !v || !out) return fail(FD_ERR_ARG, "q, k, v and out must not be NULL");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v))
+    return fail(FD_ERR_ARG, "q, k and v must be 16-byte aligned");
+  fdk::PartialArgs pa{};
+  return run_split_kv(fdk::kDense, dt, q, k, v, out, lse, B, Hq, Hkv, L, d, scale, chunk, nc,
+                      pa, ws, nullptr, L, stream);
+}
+
+int fd_decode_attn_paged(fd_dtype_t dt, const void* q, const void* k_pool,
+                         const void* v_pool, const int32_t* block_table,
+                         const int32_t* seq_lens, float* out, float* lse, int B, int Hq,
+                         int Hkv, int d, int page_size, int max_pages_per_seq,
+                         int num_pages, int max_seq_len, float scale, int chunk, void* ws,
+                         size_t* ws_bytes, void* stream) {
+  if (dt != FD_F32 && dt != FD_BF16) return fail(FD_ERR_ARG, "unknown dtype %d", (int)dt);
+  if (int e = check_heads(B, Hq, Hkv, d)) return e;
+  if (int e = check_chunk(chunk)) return e;
+  if (int e = check_scale(scale)) return e;
+  if (page_size < 8 || page_size > 1024 || (page_size & (page_size - 1)) != 0)
+    return fail(FD_ERR_ARG, "page_size=%d must be a power of two in [8, 1024]", page_size);
+  if (chunk % page_size != 0)
+    return fail(FD_ERR_ARG, "chunk=%d must be a multiple of page_size=%d", chunk, page_size);
+  if (chunk / page_size > 1024)
+    return fail(FD_ERR_UNSUPPORTED, "chunk/page_size=%d exceeds 1024", chunk / page_size);
+  if (max_pages_per_seq <= 0 || num_pages <= 0)
+    return fail(FD_ERR_ARG, "max_pages_per_seq and num_pages must be positive");
+  if (max_seq_len < 0 || (long long)max_seq_len > (long long)max_pages_per_seq * page_size)
+    return fail(FD_ERR_ARG, "max_seq_len=%d outside [0, max_pages_per_seq*page_size]",
+                max_seq_len);
+  int shift = 0;
+  while ((1 << shift) < page_size) ++shift;
+  const int nc = (max_seq_len + chunk - 1) / chunk;
+  if (int e = workspace_gate(ws, ws_bytes, partial_bytes(B, Hq, nc, d))) return e;
+  if (ws == nullptr) return ok();
+  if (!q || !k_pool || !v_pool || !block_table || !seq_lens || !out)
+    return fail(FD_ERR_ARG, "q, pools, block_table, seq_lens and out must not be NULL");
+  if (!aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool))
+    return fail(FD_ERR_ARG, "q and pools must be 16-byte aligned");
+  fdk::PartialArgs pa{};
+  pa.block_table = block_table;
+  pa.seq_lens = seq_lens;
+  pa.page_shift = shift;
+  pa.max_pages = max_pages_per_seq;
+  pa.num_pages = num_pages;
+  pa.max_seq_len = max_seq_len;
+  return run_split_kv(fdk::kPaged, dt, q, k_pool, v_pool, out, lse, B, Hq, Hkv, 0, d, scale,
+                      chunk, nc, pa, ws, seq_lens, max_seq_len, stream);
+}
+
+int fd_decode_attn_unified_max(fd_dtype_t dt, const void* q, const void* k, const void* v,
+                               float* out, float* lse, int B, int Hq, int Hkv, int L, int d,
+                               float scale, int chunk, float phi, float margin_hi,
+                               float margin_lo, uint8_t* chunk_flags, void* ws,
+                               size_t* ws_bytes, void* stream) {
+  if (dt != FD_F32 && dt != FD_BF16) return fail(FD_ERR_ARG, "unknown dtype %d", (int)dt);
+  if (int e = check_heads(B, Hq, Hkv, d)) return e;
+  if (L <= 0) return fail(FD_ERR_ARG, "L=%d must be positive", L);
+  if (int e = check_chunk(chunk)) return e;
+  if (int e = check_scale(scale)) return e;
+  if (!isfinite(phi)) return fail(FD_ERR_ARG, "phi must be finite");
+  if (!(margin_hi >= 0.f && margin_hi <= 60.f) || !(margin_lo >= 0.f && margin_lo <= 60.f))
+    return fail(FD_ERR_ARG, "margins must lie in [0, 60] (exp(60) bounds the fp32 sums)");
+  const int nc = (L + chunk - 1) / chunk;
+  if (int e = workspace_gate(ws, ws_bytes, partial_bytes(B, Hq, nc, d))) return e;
+  if (ws == nullptr) return ok();
+  if (!q || !k || !v || !out) return fail(FD_ERR_ARG, "q, k, v and out must not be NULL");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v))
+    return fail(FD_ERR_ARG, "q, k and v must be 16-byte aligned");
+  fdk::PartialArgs pa{};
+  pa.flags = chunk_flags;
+  pa.base_log2 = (float)((double)phi * 1.4426950408889634);
+  pa.flag_hi_raw = (float)(((double)phi + margin_hi) / (double)scale);
+  pa.flag_lo_raw = (float)(((double)phi - margin_lo) / (double)scale);
+  return run_split_kv(fdk::kUnified, dt, q, k, v, out, lse, B, Hq, Hkv, L, d, scale, chunk,
+                      nc, pa, ws, nullptr, L, stream);
+}
+
+int fd_ffd_pack(const void* k, uint32_t* codes, uint16_t* zs, int8_t* res, uint16_t* rs,
+                int B, int Hkv, int L_cap, int d, int t_begin, int t_end, void* stream) {
+  if (B <= 0 || Hkv <= 0 || L_cap <= 0)
+    return fail(FD_ERR_ARG, "B=%d Hkv=%d L_cap=%d must be positive", B, Hkv, L_cap);
+  if (d != 64 && d != 128) return fail(FD_ERR_UNSUPPORTED, "d=%d not in {64,128}", d);
+  if (t_begin < 0 || t_begin > t_end || t_end > L_cap)
+    return fail(FD_ERR_ARG, "need 0 <= t_begin=%d <= t_end=%d <= L_cap=%d", t_begin, t_end,
+                L_cap);
+  if (!k || !codes || !zs || !res || !rs) return fail(FD_ERR_ARG, "NULL array");
+  if (!aligned16(k) || !aligned16(codes) || !aligned16(res))
+    return fail(FD_ERR_ARG, "k, codes and res must be 16-byte aligned");
+  if (t_begin == t_end) return ok();
+  fdk::FfdPackArgs pa{reinterpret_cast<const uint16_t*>(k), codes, zs, res, rs, B, Hkv, L_cap,
+                      t_begin, t_end};
+  return hip_status(fdk::launch_ffd_pack(d, pa, reinterpret_cast<hipStream_t>(stream)),
+                    "pack kernel launch");
+}
+
+int fd_ffd_sparse_decode(const void* q, const uint32_t* codes, const uint16_t* zs,
+                         const int8_t* res, const uint16_t* rs, const void* v, float* out,
+                         float* lse, int B, int Hq, int Hkv, int L, int d, float scale,
+                         float delta, int n_sink, int n_local, int chunk, uint32_t* cand_mask,
+                         float* pseudo_max, void* ws, size_t* ws_bytes, void* stream) {
+  if (int e = check_heads(B, Hq, Hkv, d)) return e;
+  if (L <= 0) return fail(FD_ERR_ARG, "L=%d must be positive", L);
+  if (int e = check_chunk(chunk)) return e;
+  if (chunk % 32 != 0 || chunk > 1024)
+    return fail(FD_ERR_UNSUPPORTED, "FFD chunk=%d must be a multiple of 32 <= 1024", chunk);
+  if (int e = check_scale(scale)) return e;
+  if (!(delta >= 0.f)) return fail(FD_ERR_ARG, "delta must be >= 0");
+  if (n_sink < 0 || n_local < 0 || n_sink + n_local < 1)
+    return fail(FD_ERR_ARG, "need n_sink, n_local >= 0 and n_sink + n_local >= 1");
+  const int nc = (L + chunk - 1) / chunk;
+  const size_t need = partial_bytes(B, Hq, nc, d);
+  if (int e = workspace_gate(ws, ws_bytes, need)) return e;
+  if (ws == nullptr) return ok();
+  if (!q || !codes || !zs || !res || !rs || !v || !out)
+    return fail(FD_ERR_ARG, "q, packed keys, v and out must not be NULL");
+  if (!aligned16(q) || !aligned16(codes) || !aligned16(res) || !aligned16(v))
+    return fail(FD_ERR_ARG, "q, codes, res and v must be 16-byte aligned");
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  float *o_part, *ml_part;
+  split_ws(ws, B, Hq, nc, d, &o_part, &ml_part);
+  fdk::FfdArgs fa{};
+  fa.q = reinterpret_cast<const uint16_t*>(q);
+  fa.codes = codes;
+  fa.zs = zs;
+  fa.res = res;
+  fa.rs = rs;
+  fa.v = reinterpret_cast<const uint16_t*>(v);
+  fa.o_part = o_part;
+  fa.ml_part = ml_part;
+  fa.cand_mask = cand_mask;
+  fa.pseudo_max = pseudo_max;
+  fa.B = B;
+  fa.Hq = Hq;
+  fa.Hkv = Hkv;
+  fa.L = L;
+  fa.chunk = chunk;
+  fa.nc = nc;
+  fa.n_sink = n_sink;
+  fa.n_local = n_local;
+  fa.scale = scale;
+  fa.c_log2 = (float)((double)scale * 1.4426950408889634);
+  fa.delta_raw = isinf(delta) ? delta : (float)((double)delta / (double)scale);
+  hipError_t e = fdk::launch_ffd(d, Hq / Hkv, fa, s);
+  if (e != hipSuccess) return hip_status(e, "ffd kernel launch");
+  fdk::MergeArgs ma{o_part, ml_part, out, lse, nullptr, Hq, nc, chunk, L};
+  return hip_status(fdk::launch_merge(d, B, ma, s), "merge kernel launch");
+}
+
+}  // extern "C"

@@ -1,0 +1,99 @@
+// Device helpers shared by the decode-attention kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fdk {
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kWave = 64;
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kNegInf = -__builtin_inff();
+
+// Hardware base-2 exponential and logarithm (v_exp_f32 / v_log_f32).
+__device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float log2_hw(float x) { return __builtin_amdgcn_logf(x); }
+
+// exp2(a - b) that is 0 (not NaN) when both are -inf.
+__device__ __forceinline__ float exp2_diff(float a, float b) {
+  return exp2_hw(a - (b == kNegInf ? 0.f : b));
+}
+
+// Lane permutation inside a row of 16 lanes (DPP); every source lane is valid
+// for the controls used here, so no bound control is needed.
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+  return __int_as_float(
+      __builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+
+enum : int {
+  kQuadXor1 = 0xB1,       // quad_perm [1,0,3,2]
+  kQuadXor2 = 0x4E,       // quad_perm [2,3,0,1]
+  kRowHalfMirror = 0x141, // lane i <-> 7-i inside each half row
+  kRowMirror = 0x140,     // lane i <-> 15-i inside each row
+};
+
+// Sum over aligned groups of N lanes (N = 8, 16 or 32); every lane of the
+// group receives the group's sum.  After the two quad steps each quad holds
+// its sum; the half-row mirror pairs lane i with a lane of the other quad,
+// the row mirror pairs the two halves, and a swizzle swaps 16-lane halves.
+template <int N>
+__device__ __forceinline__ float group_sum(float x) {
+  static_assert(N == 8 || N == 16 || N == 32, "group size");
+  x += dpp<kQuadXor1>(x);
+  x += dpp<kQuadXor2>(x);
+  x += dpp<kRowHalfMirror>(x);
+  if constexpr (N >= 16) x += dpp<kRowMirror>(x);
+  if constexpr (N >= 32)
+    x += __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(x), 0x401F));
+  return x;
+}
+
+// Same groups, maximum.
+template <int N>
+__device__ __forceinline__ float group_max(float x) {
+  static_assert(N == 8 || N == 16 || N == 32, "group size");
+  x = fmaxf(x, dpp<kQuadXor1>(x));
+  x = fmaxf(x, dpp<kQuadXor2>(x));
+  x = fmaxf(x, dpp<kRowHalfMirror>(x));
+  if constexpr (N >= 16) x = fmaxf(x, dpp<kRowMirror>(x));
+  if constexpr (N >= 32)
+    x = fmaxf(x, __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(x), 0x401F)));
+  return x;
+}
+
+// Whole-wave reductions (used outside the hot loops).
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) x = fmaxf(x, __shfl_xor(x, o));
+  return x;
+}
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o);
+  return x;
+}
+
+// bf16 pairs packed in a 32-bit word -> fp32 (exact).
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
+                                         __builtin_bit_cast(bf16x2_t, b), c, false);
+}
+
+// 16-byte global loads.
+__device__ __forceinline__ u32x4 ld16(const void* p) {
+  return *reinterpret_cast<const u32x4*>(p);
+}
+
+}  // namespace fdk

@@ -1,0 +1,414 @@
+// FFD sparse decode for gfx950 ("Faster Than Flash" digest, longzhangge.com):
+// a 2-bit key scan of every position, a pseudo-maximum from attention-sink
+// and local-window anchors, top-delta selection, an 8-bit residual refine of
+// the candidates and exact attention over them (sections 3-6, Fig. 2), plus
+// the packer that produces the key format (section 5).
+//
+// One workgroup = one unit = (sequence, kv-head, chunk), fused:
+//   0. Anchors.  Every unit scores the anchor positions with the refined key
+//      (2-bit + residual) and takes m^ and j* itself; the computation is the
+//      same in every unit, so all units agree without a separate pass.
+//   1. Scan.  4 lanes per position (one 32-dim quantisation group each) read
+//      8 B of codes and 4 B of (zero, step).  Codes become exact bf16 values
+//      4 + c (a rotate and an and-or per pair, since bf16 4..7 differ only in
+//      two mantissa bits) and meet the bf16 query in v_dot2c_f32_bf16;
+//      sum q_i c_i = dot - 4 sum q_i.  The scan score and the G-bit candidate
+//      mask of every position stay in LDS (no write-back).
+//   2. Compaction of the positions that are a candidate for any head of the
+//      group (they share the residual and V loads).
+//   3. Refine + attend over the compacted list, 16 lanes per row: residual
+//      bytes become exact bf16 (r + 128) for dot2, V rows stream as in the
+//      dense kernel, each head's softmax covers only its own candidates.
+//   4. Row slots and waves merge into one partial per query head; the
+//      chunks merge in the common log-sum-exp kernel.
+#include "internal.hpp"
+#include "splitkv.hpp"
+
+namespace fdk {
+
+constexpr int kFfdMaxChunk = 1024;
+
+__device__ __forceinline__ float half_to_float(uint32_t bits16) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)bits16);
+}
+
+// bf16 pair (4 + c[2p], 4 + c[2p+1]) from a code word (dims 2p at bits 2p,
+// 2p+1 at bits 16+2p): rotate both 2-bit fields to mantissa bits 5..6 of
+// their half and set the exponent of 4.0 (bf16 0x4080 + c*0x20 = 4 + c).
+__device__ __forceinline__ uint32_t code_pair(uint32_t w, int p) {
+  const uint32_t rot = __builtin_amdgcn_alignbit(w, w, (uint32_t)((2 * p - 5) & 31));
+  return (rot & 0x00600060u) | 0x40804080u;
+}
+
+// bf16 pair from two small integers held exactly in fp32 (low half = a).
+__device__ __forceinline__ uint32_t pack_bf16_exact(float a, float b) {
+  return __builtin_amdgcn_perm(__float_as_uint(b), __float_as_uint(a), 0x07060302u);
+}
+
+// Residual part of the refined dot product for one lane's 8 dims:
+// rs * sum_i q_i r_i, with the residual bytes read as r + 128 (exact bf16).
+template <int G>
+__device__ __forceinline__ void residual_dot(const u32x2& rr, float rsf, const u32x4 (&qr)[G],
+                                             const float (&ql)[G], float (&out)[G]) {
+  const uint32_t u0 = rr.x ^ 0x80808080u, u1 = rr.y ^ 0x80808080u;
+  const uint32_t p0 = pack_bf16_exact((float)(u0 & 0xFF), (float)((u0 >> 8) & 0xFF));
+  const uint32_t p1 = pack_bf16_exact((float)((u0 >> 16) & 0xFF), (float)(u0 >> 24));
+  const uint32_t p2 = pack_bf16_exact((float)(u1 & 0xFF), (float)((u1 >> 8) & 0xFF));
+  const uint32_t p3 = pack_bf16_exact((float)((u1 >> 16) & 0xFF), (float)(u1 >> 24));
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    float a = dot2_bf16(qr[h].x, p0, 0.f);
+    float b = dot2_bf16(qr[h].y, p1, 0.f);
+    a = dot2_bf16(qr[h].z, p2, a);
+    b = dot2_bf16(qr[h].w, p3, b);
+    out[h] = rsf * fmaf(-128.f, ql[h], a + b);
+  }
+}
+
+template <int D, int G>
+__global__ __launch_bounds__(kThreads) void ffd_kernel(FfdArgs a) {
+  using Gm = Geo<uint16_t, D>;
+  constexpr int VEC = Gm::kVec, LPT = Gm::kLpt, TPL = Gm::kTpl;
+  constexpr int NG = D / 32;         // quantisation groups per position
+  constexpr int TPS = kWave / NG;    // positions per wave step in the scan
+  constexpr int CW = D / 16;         // code words per position
+
+  __shared__ float s_scan[kFfdMaxChunk][G];
+  __shared__ uint8_t s_mask[kFfdMaxChunk];
+  __shared__ uint16_t s_list[kFfdMaxChunk];
+  __shared__ int s_cnt[kWaves];
+  __shared__ float s_best[kWaves][G];
+  __shared__ int s_bidx[kWaves][G];
+  __shared__ CombineLds<G, D> s_cmb;
+
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & (kWave - 1);
+  const int grp = lane / LPT, col = lane % LPT;
+  const int c = blockIdx.x % a.nc;
+  const int bk = blockIdx.x / a.nc;
+  const int kvh = bk % a.Hkv, b = bk / a.Hkv;
+  const int L = a.L;
+  const int c0 = c * a.chunk, c1 = min(c0 + a.chunk, L), n = c1 - c0;
+  const size_t bkv = (size_t)b * a.Hkv + kvh;
+  const size_t rbase = bkv * (size_t)L;  // row index of position 0
+  const uint32_t* codes = a.codes;
+  const uint16_t* zs = a.zs;
+  const int8_t* res = a.res;
+  const uint16_t* rsa = a.rs;
+  const char* vb = reinterpret_cast<const char*>(a.v) + rbase * Gm::kRow;
+  const size_t hq0 = (size_t)b * a.Hq + (size_t)kvh * G;
+
+  // Query slices of the 16-lane (row) layout, and their partial sums.
+  u32x4 qr[G];
+  float ql[G];
+  {
+    const uint16_t* qp = a.q + hq0 * D + col * VEC;
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      qr[h] = ld16(qp + (size_t)h * D);
+      ql[h] = ((bf16_lo(qr[h].x) + bf16_hi(qr[h].x)) + (bf16_lo(qr[h].y) + bf16_hi(qr[h].y))) +
+              ((bf16_lo(qr[h].z) + bf16_hi(qr[h].z)) + (bf16_lo(qr[h].w) + bf16_hi(qr[h].w)));
+    }
+  }
+
+  // ---- 0. pseudo-maximum over the anchors (refined scores, raw units) ----
+  const int n_sk = min(a.n_sink, L);
+  const int loc0 = max(n_sk, L - a.n_local);
+  const int na = n_sk + (L - loc0);
+  float best[G];
+  int bidx[G];
+#pragma unroll
+  for (int h = 0; h < G; ++h) { best[h] = kNegInf; bidx[h] = 0x7fffffff; }
+  for (int k0 = wave * TPL; k0 < na; k0 += kWaves * TPL) {
+    const int k = min(k0 + grp, na - 1);
+    const int pos = k < n_sk ? k : loc0 + (k - n_sk);
+    const size_t row = rbase + pos;
+    const int gi = col / 4;  // 8 dims per lane, 4 lanes per group
+    const uint32_t w = codes[row * CW + col / 2];
+    const uint32_t zsb = *reinterpret_cast<const uint32_t*>(zs + (row * NG + gi) * 2);
+    const float z = half_to_float(zsb & 0xFFFF), st = half_to_float(zsb >> 16);
+    const u32x2 rr = *reinterpret_cast<const u32x2*>(res + row * D + col * 8);
+    const float rsf = half_to_float(rsa[row * NG + gi]);
+    float corr[G];
+    residual_dot<G>(rr, rsf, qr, ql, corr);
+    const int p0 = 4 * (col & 1);
+    const uint32_t k0p = code_pair(w, p0), k1p = code_pair(w, p0 + 1);
+    const uint32_t k2p = code_pair(w, p0 + 2), k3p = code_pair(w, p0 + 3);
+    const bool valid = k0 + grp < na;
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      float x = dot2_bf16(qr[h].x, k0p, 0.f);
+      float y = dot2_bf16(qr[h].y, k1p, 0.f);
+      x = dot2_bf16(qr[h].z, k2p, x);
+      y = dot2_bf16(qr[h].w, k3p, y);
+      const float part = fmaf(fmaf(-4.f, st, z), ql[h], st * (x + y)) + corr[h];
+      const float sc = group_sum<LPT>(part);
+      if (valid && (sc > best[h] || (sc == best[h] && pos < bidx[h]))) {
+        best[h] = sc;
+        bidx[h] = pos;
+      }
+    }
+  }
+#pragma unroll
+  for (int off = LPT; off < kWave; off <<= 1) {
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      const float ob = __shfl_xor(best[h], off);
+      const int oi = __shfl_xor(bidx[h], off);
+      if (ob > best[h] || (ob == best[h] && oi < bidx[h])) { best[h] = ob; bidx[h] = oi; }
+    }
+  }
+  if (lane == 0) {
+#pragma unroll
+    for (int h = 0; h < G; ++h) { s_best[wave][h] = best[h]; s_bidx[wave][h] = bidx[h]; }
+  }
+  __syncthreads();
+  float thr[G];
+  int jst[G];
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    float bb = s_best[0][h];
+    int bi = s_bidx[0][h];
+#pragma unroll
+    for (int w = 1; w < kWaves; ++w) {
+      const float ob = s_best[w][h];
+      const int oi = s_bidx[w][h];
+      if (ob > bb || (ob == bb && oi < bi)) { bb = ob; bi = oi; }
+    }
+    thr[h] = bb - a.delta_raw;
+    jst[h] = bi;
+    if (c == 0 && a.pseudo_max != nullptr && tid == 0) a.pseudo_max[hq0 + h] = bb * a.scale;
+  }
+
+  // ---- 1. 2-bit scan of the chunk: scores and candidate masks into LDS ----
+  {
+    const int gi = lane % NG, tk = lane / NG;
+    u32x4 qs[G][4];
+    float qg[G];
+    const uint16_t* qp = a.q + hq0 * D + gi * 32;
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      qg[h] = 0.f;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        qs[h][j] = ld16(qp + (size_t)h * D + j * 8);
+        qg[h] += (bf16_lo(qs[h][j].x) + bf16_hi(qs[h][j].x)) +
+                 (bf16_lo(qs[h][j].y) + bf16_hi(qs[h][j].y)) +
+                 (bf16_lo(qs[h][j].z) + bf16_hi(qs[h][j].z)) +
+                 (bf16_lo(qs[h][j].w) + bf16_hi(qs[h][j].w));
+      }
+    }
+    constexpr int kSteps = 4;
+    for (int r0 = wave * TPS * kSteps; r0 < n; r0 += kWaves * TPS * kSteps) {
+      u32x2 cw[kSteps];
+      uint32_t zz[kSteps];
+#pragma unroll
+      for (int u = 0; u < kSteps; ++u) {
+        const int jr = min(r0 + u * TPS + tk, n - 1);
+        const size_t row = rbase + c0 + jr;
+        cw[u] = *reinterpret_cast<const u32x2*>(codes + row * CW + 2 * gi);
+        zz[u] = *reinterpret_cast<const uint32_t*>(zs + (row * NG + gi) * 2);
+      }
+#pragma unroll
+      for (int u = 0; u < kSteps; ++u) {
+        const int jr = r0 + u * TPS + tk;
+        const float z = half_to_float(zz[u] & 0xFFFF), st = half_to_float(zz[u] >> 16);
+        const float zb = fmaf(-4.f, st, z);
+        uint32_t kp[16];
+#pragma unroll
+        for (int p = 0; p < 8; ++p) {
+          kp[p] = code_pair(cw[u].x, p);
+          kp[8 + p] = code_pair(cw[u].y, p);
+        }
+        uint32_t bits = 0;
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+          float x = 0.f, y = 0.f;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            x = dot2_bf16(qs[h][j].x, kp[4 * j + 0], x);
+            y = dot2_bf16(qs[h][j].y, kp[4 * j + 1], y);
+            x = dot2_bf16(qs[h][j].z, kp[4 * j + 2], x);
+            y = dot2_bf16(qs[h][j].w, kp[4 * j + 3], y);
+          }
+          float sc = fmaf(zb, qg[h], st * (x + y));
+          sc += dpp<kQuadXor1>(sc);
+          if constexpr (NG == 4) sc += dpp<kQuadXor2>(sc);
+          const bool cand = (sc >= thr[h]) || (c0 + jr == jst[h]);
+          bits |= cand ? (1u << h) : 0u;
+          if (jr < n && gi == (h % NG)) s_scan[jr][h] = sc;
+        }
+        if (jr < n && gi == 0) s_mask[jr] = (uint8_t)bits;
+      }
+    }
+  }
+  __syncthreads();
+
+  // Candidate bitmask output (optional): word j/32, bit j%32, per head.
+  if (a.cand_mask != nullptr) {
+    const int nw = (n + 31) / 32;
+    const size_t words = ((size_t)L + 31) / 32;
+    for (int idx = tid; idx < G * nw; idx += kThreads) {
+      const int h = idx / nw, wi = idx % nw;
+      uint32_t word = 0;
+      for (int k = 0; k < 32; ++k) {
+        const int jr = wi * 32 + k;
+        if (jr < n && ((s_mask[jr] >> h) & 1)) word |= 1u << k;
+      }
+      a.cand_mask[(hq0 + h) * words + (size_t)(c0 / 32) + wi] = word;
+    }
+  }
+
+  // ---- 2. compaction of the group's candidate union ----
+  int nu = 0;
+  for (int r0 = 0; r0 < n; r0 += kThreads) {
+    const int jr = r0 + tid;
+    const bool u = jr < n && s_mask[jr] != 0;
+    const unsigned long long bal = __ballot(u);
+    const int pre = __popcll(bal & ((1ull << lane) - 1ull));
+    if (lane == 0) s_cnt[wave] = __popcll(bal);
+    __syncthreads();
+    int off = nu, tot = 0;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      off += (w < wave) ? s_cnt[w] : 0;
+      tot += s_cnt[w];
+    }
+    if (u) s_list[off + pre] = (uint16_t)jr;
+    nu += tot;
+    __syncthreads();
+  }
+
+  // ---- 3. refine + exact attention over the candidates ----
+  float acc[G][VEC], m[G], l[G];
+  state_reset<G, VEC>(acc, m, l);
+  const int per = (((nu + kWaves - 1) / kWaves) + TPL - 1) / TPL * TPL;
+  const int t_beg = wave * per, t_end = min(t_beg + per, nu);
+  for (int t0 = t_beg; t0 < t_end; t0 += kNb * TPL) {
+    int jr[kNb];
+    u32x2 rr[kNb];
+    uint32_t rsb[kNb];
+    u32x4 vr[kNb];
+#pragma unroll
+    for (int i = 0; i < kNb; ++i) {
+      jr[i] = s_list[min(t0 + i * TPL + grp, t_end - 1)];
+      const size_t row = rbase + c0 + jr[i];
+      rr[i] = *reinterpret_cast<const u32x2*>(res + row * D + col * 8);
+      rsb[i] = rsa[row * NG + col / 4];
+    }
+#pragma unroll
+    for (int i = 0; i < kNb; ++i)
+      vr[i] = ld16(vb + (size_t)(c0 + jr[i]) * Gm::kRow + (size_t)col * 16);
+    float s[kNb][G];
+#pragma unroll
+    for (int i = 0; i < kNb; ++i) {
+      float corr[G];
+      residual_dot<G>(rr[i], half_to_float(rsb[i]), qr, ql, corr);
+      const uint32_t mk = s_mask[jr[i]];
+      const bool valid = t0 + i * TPL + grp < t_end;
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        const float sc = s_scan[jr[i]][h] + group_sum<LPT>(corr[h]);
+        s[i][h] = (valid && ((mk >> h) & 1)) ? sc : kNegInf;
+      }
+    }
+    online_update<uint16_t, G, VEC>(s, vr, a.c_log2, acc, m, l);
+  }
+  state_to_log2<G>(m, a.c_log2);
+
+  // ---- 4. one partial per query head ----
+  combine_store<G, D, VEC, LPT>(s_cmb, acc, m, l, a.o_part, a.ml_part,
+                                hq0 * a.nc + c, (size_t)a.nc);
+}
+
+// Packer: one thread per (position, 32-dim group).  Every step in fp32 with
+// round-to-nearest-even, in the order the format defines (see fd.h).
+template <int D>
+__global__ __launch_bounds__(kThreads) void ffd_pack_kernel(FfdPackArgs a) {
+  constexpr int NG = D / 32;
+  const int span = a.t_end - a.t_begin;
+  const size_t total = (size_t)a.B * a.Hkv * span * NG;
+  const size_t gid = (size_t)blockIdx.x * kThreads + threadIdx.x;
+  if (gid >= total) return;
+  const int gi = (int)(gid % NG);
+  const size_t pt = gid / NG;
+  const int t = a.t_begin + (int)(pt % span);
+  const size_t bkv = pt / span;
+  const size_t row = bkv * (size_t)a.Lcap + t;
+
+  float x[32];
+  const u32x4* src = reinterpret_cast<const u32x4*>(a.k + row * D + gi * 32);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const u32x4 w = src[j];
+    x[8 * j + 0] = bf16_lo(w.x); x[8 * j + 1] = bf16_hi(w.x);
+    x[8 * j + 2] = bf16_lo(w.y); x[8 * j + 3] = bf16_hi(w.y);
+    x[8 * j + 4] = bf16_lo(w.z); x[8 * j + 5] = bf16_hi(w.z);
+    x[8 * j + 6] = bf16_lo(w.w); x[8 * j + 7] = bf16_hi(w.w);
+  }
+  float mn = x[0], mx = x[0];
+#pragma unroll
+  for (int i = 1; i < 32; ++i) { mn = fminf(mn, x[i]); mx = fmaxf(mx, x[i]); }
+  const _Float16 z16 = (_Float16)mn;
+  const _Float16 s16 = (_Float16)((mx - mn) / 3.0f);
+  const float z = (float)z16, st = (float)s16;
+  uint32_t code[32];
+  float r[32];
+  float amax = 0.f;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) {
+    float cf = 0.f;
+    if (st != 0.f) cf = fminf(fmaxf(__builtin_rintf((x[i] - z) / st), 0.f), 3.f);
+    code[i] = (uint32_t)cf;
+    r[i] = x[i] - fmaf(st, cf, z);
+    amax = fmaxf(amax, fabsf(r[i]));
+  }
+  const _Float16 rs16 = (_Float16)(amax / 127.0f);
+  const float rsf = (float)rs16;
+  uint32_t rb[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) rb[j] = 0;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) {
+    float q = 0.f;
+    if (rsf != 0.f) q = fminf(fmaxf(__builtin_rintf(r[i] / rsf), -127.f), 127.f);
+    rb[i / 4] |= ((uint32_t)(int)q & 0xFFu) << (8 * (i % 4));
+  }
+  uint32_t w0 = 0, w1 = 0;
+#pragma unroll
+  for (int p = 0; p < 8; ++p) {
+    w0 |= (code[2 * p] << (2 * p)) | (code[2 * p + 1] << (16 + 2 * p));
+    w1 |= (code[16 + 2 * p] << (2 * p)) | (code[17 + 2 * p] << (16 + 2 * p));
+  }
+  *reinterpret_cast<u32x2*>(a.codes + row * (D / 16) + 2 * gi) = u32x2{w0, w1};
+  *reinterpret_cast<uint32_t*>(a.zs + (row * NG + gi) * 2) =
+      (uint32_t)__builtin_bit_cast(uint16_t, z16) |
+      ((uint32_t)__builtin_bit_cast(uint16_t, s16) << 16);
+  u32x4* dst = reinterpret_cast<u32x4*>(a.res + row * D + gi * 32);
+  dst[0] = u32x4{rb[0], rb[1], rb[2], rb[3]};
+  dst[1] = u32x4{rb[4], rb[5], rb[6], rb[7]};
+  a.rs[row * NG + gi] = __builtin_bit_cast(uint16_t, rs16);
+}
+
+hipError_t launch_ffd(int D, int G, const FfdArgs& a, hipStream_t s) {
+  const dim3 grid((unsigned)((size_t)a.B * a.Hkv * a.nc)), block(kThreads);
+#define FD_FFD_CASE(DD, GG)                                                     \
+  if (D == DD && G == GG) {                                                     \
+    hipLaunchKernelGGL((ffd_kernel<DD, GG>), grid, block, 0, s, a);             \
+    return hipGetLastError();                                                   \
+  }
+  FD_FFD_CASE(64, 1) FD_FFD_CASE(64, 2) FD_FFD_CASE(64, 4) FD_FFD_CASE(64, 8)
+  FD_FFD_CASE(128, 1) FD_FFD_CASE(128, 2) FD_FFD_CASE(128, 4) FD_FFD_CASE(128, 8)
+#undef FD_FFD_CASE
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_ffd_pack(int D, const FfdPackArgs& a, hipStream_t s) {
+  const size_t total = (size_t)a.B * a.Hkv * (a.t_end - a.t_begin) * (D / 32);
+  const dim3 grid((unsigned)((total + kThreads - 1) / kThreads)), block(kThreads);
+  if (D == 64) hipLaunchKernelGGL((ffd_pack_kernel<64>), grid, block, 0, s, a);
+  else if (D == 128) hipLaunchKernelGGL((ffd_pack_kernel<128>), grid, block, 0, s, a);
+  else return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+}  // namespace fdk

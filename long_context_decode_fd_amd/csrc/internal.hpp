@@ -1,0 +1,71 @@
+// Host-side launch interface between the C ABI (api.hip) and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace fdk {
+
+enum Mode : int { kDense = 0, kPaged = 1, kUnified = 2 };
+
+// Arguments of the split-KV partial kernel.  Scores are handled in units of
+// the raw dot product q.k; `c_log2` = scale * log2(e) turns them into base-2
+// exponents of the scaled score.
+struct PartialArgs {
+  const void* q;             // [B, Hq, D]
+  const void* k;             // dense/unified: [B, Hkv, L, D]; paged: [P, Hkv, page, D]
+  const void* v;
+  float* o_part;             // [B, Hq, nc, D]   unnormalised chunk outputs
+  float* ml_part;            // [B, Hq, nc, 2]   (m in log2 units, l)
+  uint8_t* flags;            // unified only, [B, Hq, nc] or null
+  const int32_t* block_table;  // paged only
+  const int32_t* seq_lens;     // paged only
+  int B, Hq, Hkv, L, chunk, nc;
+  int page_shift, max_pages, num_pages, max_seq_len;
+  float c_log2;
+  float base_log2;           // unified: phi * log2(e)
+  float flag_hi_raw;         // unified: (phi + margin_hi) / scale
+  float flag_lo_raw;         // unified: (phi - margin_lo) / scale
+};
+
+struct MergeArgs {
+  const float* o_part;
+  const float* ml_part;
+  float* out;                // [B, Hq, D]
+  float* lse;                // [B, Hq] or null
+  const int32_t* seq_lens;   // paged: chunk count per sequence; else null
+  int Hq, nc, chunk, max_seq_len;
+};
+
+hipError_t launch_partial(int mode, int is_bf16, int D, int G,
+                          const PartialArgs& a, hipStream_t s);
+hipError_t launch_merge(int D, int B, const MergeArgs& a, hipStream_t s);
+
+struct FfdPackArgs {
+  const uint16_t* k;   // bf16 [B, Hkv, Lcap, D]
+  uint32_t* codes;     // [B, Hkv, Lcap, D/16]
+  uint16_t* zs;        // [B, Hkv, Lcap, D/32, 2]
+  int8_t* res;         // [B, Hkv, Lcap, D]
+  uint16_t* rs;        // [B, Hkv, Lcap, D/32]
+  int B, Hkv, Lcap, t_begin, t_end;
+};
+hipError_t launch_ffd_pack(int D, const FfdPackArgs& a, hipStream_t s);
+
+struct FfdArgs {
+  const uint16_t* q;   // bf16 [B, Hq, D]
+  const uint32_t* codes;
+  const uint16_t* zs;
+  const int8_t* res;
+  const uint16_t* rs;
+  const uint16_t* v;   // bf16 [B, Hkv, L, D]
+  float* o_part;
+  float* ml_part;
+  uint32_t* cand_mask; // [B, Hq, ceil(L/32)] or null
+  float* pseudo_max;   // [B, Hq] or null (scaled units)
+  int B, Hq, Hkv, L, chunk, nc, n_sink, n_local;
+  float scale, c_log2, delta_raw;  // delta / scale
+};
+hipError_t launch_ffd(int D, int G, const FfdArgs& a, hipStream_t s);
+
+}  // namespace fdk

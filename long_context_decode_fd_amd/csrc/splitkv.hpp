@@ -1,0 +1,199 @@
+// Building blocks of one split-KV unit, shared by the dense/paged/fixed-max
+// kernel and the FFD kernel.
+//
+// Lane layout ("row slots"): a cache row of D elements is read by kLpt lanes
+// with 16 bytes each; a wave load covers kTpl consecutive rows.  Lane
+// (grp = lane / kLpt, col = lane % kLpt) owns dims [col*kVec, col*kVec + kVec)
+// of row slot grp.  Every row slot keeps its own softmax state (m, l, O) for
+// the G query heads of the kv-head; slots are merged once at the end of the
+// unit ("Flash Decoding" explainer, section 2: the same exact merge that
+// joins chunks joins slots).
+#pragma once
+
+#include <type_traits>
+
+#include "common.hpp"
+
+namespace fdk {
+
+constexpr int kWaves = 4;
+constexpr int kThreads = kWaves * kWave;
+constexpr int kNb = 8;  // rows per slot per batch (loads per tensor per batch)
+
+template <typename E, int D>
+struct Geo {
+  static constexpr int kVec = 16 / (int)sizeof(E);  // elements per lane per row
+  static constexpr int kLpt = D / kVec;              // lanes per cache row
+  static constexpr int kTpl = kWave / kLpt;          // rows per wave load
+  static constexpr int kRow = D * (int)sizeof(E);    // bytes per cache row
+  static_assert(kLpt == 8 || kLpt == 16 || kLpt == 32, "row split");
+};
+
+// q . k over one lane's 16-byte slice.
+template <typename E>
+__device__ __forceinline__ float slice_dot(const u32x4& q, const u32x4& k) {
+  if constexpr (std::is_same<E, uint16_t>::value) {
+    float a = dot2_bf16(q.x, k.x, 0.f);
+    float b = dot2_bf16(q.y, k.y, 0.f);
+    a = dot2_bf16(q.z, k.z, a);
+    b = dot2_bf16(q.w, k.w, b);
+    return a + b;
+  } else {
+    float a = __uint_as_float(q.x) * __uint_as_float(k.x);
+    float b = __uint_as_float(q.y) * __uint_as_float(k.y);
+    a = fmaf(__uint_as_float(q.z), __uint_as_float(k.z), a);
+    b = fmaf(__uint_as_float(q.w), __uint_as_float(k.w), b);
+    return a + b;
+  }
+}
+
+// One lane's 16-byte slice of a V row as fp32.
+template <typename E>
+__device__ __forceinline__ void slice_vals(const u32x4& v, float* f) {
+  if constexpr (std::is_same<E, uint16_t>::value) {
+    f[0] = bf16_lo(v.x); f[1] = bf16_hi(v.x);
+    f[2] = bf16_lo(v.y); f[3] = bf16_hi(v.y);
+    f[4] = bf16_lo(v.z); f[5] = bf16_hi(v.z);
+    f[6] = bf16_lo(v.w); f[7] = bf16_hi(v.w);
+  } else {
+    f[0] = __uint_as_float(v.x); f[1] = __uint_as_float(v.y);
+    f[2] = __uint_as_float(v.z); f[3] = __uint_as_float(v.w);
+  }
+}
+
+template <int G, int VEC>
+__device__ __forceinline__ void state_reset(float (&acc)[G][VEC], float (&m)[G],
+                                            float (&l)[G]) {
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    m[h] = kNegInf;
+    l[h] = 0.f;
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) acc[h][e] = 0.f;
+  }
+}
+
+// Online-softmax update of a row slot with a batch of kNb rows.
+// s[i][h]: raw dot products q_h . k_i (-inf for rows that do not count);
+// m[h]: running maximum in the same raw units.  The accumulator is rescaled
+// only when some slot of the wave saw a larger maximum.
+template <typename E, int G, int VEC>
+__device__ __forceinline__ void online_update(const float (&s)[kNb][G],
+                                              const u32x4 (&vr)[kNb], float c_log2,
+                                              float (&acc)[G][VEC], float (&m)[G],
+                                              float (&l)[G]) {
+  float mb[G];
+  bool grow = false;
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    mb[h] = m[h];
+#pragma unroll
+    for (int i = 0; i < kNb; ++i) mb[h] = fmaxf(mb[h], s[i][h]);
+    grow |= mb[h] > m[h];
+  }
+  if (__any(grow)) {
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      const float a = (mb[h] == m[h]) ? 1.f : exp2_hw((m[h] - mb[h]) * c_log2);
+      l[h] *= a;
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) acc[h][e] *= a;
+      m[h] = mb[h];
+    }
+  }
+  float bias[G];
+#pragma unroll
+  for (int h = 0; h < G; ++h) bias[h] = (m[h] == kNegInf) ? 0.f : m[h] * c_log2;
+#pragma unroll
+  for (int i = 0; i < kNb; ++i) {
+    float vf[VEC];
+    slice_vals<E>(vr[i], vf);
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      const float p = exp2_hw(fmaf(s[i][h], c_log2, -bias[h]));
+      l[h] += p;
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) acc[h][e] = fmaf(p, vf[e], acc[h][e]);
+    }
+  }
+}
+
+// Raw running maximum -> log2 units of the scaled score.
+template <int G>
+__device__ __forceinline__ void state_to_log2(float (&m)[G], float c_log2) {
+#pragma unroll
+  for (int h = 0; h < G; ++h) m[h] = (m[h] == kNegInf) ? kNegInf : m[h] * c_log2;
+}
+
+// LDS scratch of the unit combine.
+template <int G, int D>
+struct CombineLds {
+  float acc[kWaves][G][D];
+  float ml[kWaves][G][2];
+};
+
+// Merge the row slots of every wave, then the waves, and write the unit's
+// partial for each of its G query heads: O (unnormalised, relative to m),
+// m (log2 units) and l.  m must already be in log2 units.  `prow0` is the
+// partial row index of query head 0 of the group; heads are `hstride` rows
+// apart.
+template <int G, int D, int VEC, int LPT>
+__device__ __forceinline__ void combine_store(CombineLds<G, D>& lds, float (&acc)[G][VEC],
+                                              float (&m)[G], float (&l)[G], float* o_part,
+                                              float* ml_part, size_t prow0, size_t hstride) {
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & (kWave - 1);
+#pragma unroll
+  for (int off = LPT; off < kWave; off <<= 1) {
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      const float mo = __shfl_xor(m[h], off);
+      const float lo = __shfl_xor(l[h], off);
+      const float M = fmaxf(m[h], mo);
+      const float wa = exp2_diff(m[h], M), wb = exp2_diff(mo, M);
+      l[h] = l[h] * wa + lo * wb;
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) {
+        const float ao = __shfl_xor(acc[h][e], off);
+        acc[h][e] = acc[h][e] * wa + ao * wb;
+      }
+      m[h] = M;
+    }
+  }
+  if (lane < LPT) {
+#pragma unroll
+    for (int h = 0; h < G; ++h)
+#pragma unroll
+      for (int e = 0; e < VEC; e += 4)
+        *reinterpret_cast<f32x4*>(&lds.acc[wave][h][lane * VEC + e]) =
+            f32x4{acc[h][e], acc[h][e + 1], acc[h][e + 2], acc[h][e + 3]};
+  }
+  if (lane == 0) {
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      lds.ml[wave][h][0] = m[h];
+      lds.ml[wave][h][1] = l[h];
+    }
+  }
+  __syncthreads();
+  for (int idx = tid; idx < G * D; idx += kThreads) {
+    const int h = idx / D, dd = idx % D;
+    float M = kNegInf;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, lds.ml[w][h][0]);
+    float o = 0.f, ls = 0.f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      const float wt = exp2_diff(lds.ml[w][h][0], M);
+      o = fmaf(wt, lds.acc[w][h][dd], o);
+      ls = fmaf(wt, lds.ml[w][h][1], ls);
+    }
+    const size_t prow = prow0 + (size_t)h * hstride;
+    o_part[prow * D + dd] = o;
+    if (dd == 0) {
+      ml_part[prow * 2] = M;
+      ml_part[prow * 2 + 1] = ls;
+    }
+  }
+}
+
+}  // namespace fdk

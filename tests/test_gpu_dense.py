@@ -1,0 +1,105 @@
+"""GPU parity of the dense split-KV path against the fp64 oracle."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import long_context_decode_fd_amd as fd
+import workloads as W
+from oracle import flash_decoding as ofd
+from tests.helpers import TOL, banner, f64, max_err
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+def _check(c, chunk=None, tol=None):
+    chunk = c.chunk if chunk is None else chunk
+    out, lse = fd.decode_attn(c.q, c.k, c.v, chunk=chunk)
+    torch.cuda.synchronize()
+    ref, lref = ofd.dense_attention(f64(c.q), f64(c.k), f64(c.v), c.scale)
+    tol = TOL[c.q.dtype] if tol is None else tol
+    eo, el = max_err(f64(out), ref), max_err(f64(lse), lref)
+    assert eo <= tol and el <= tol, (eo, el)
+    return out, lse
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("G", [1, 2, 4, 8])
+def test_shapes_groups_dtypes(dtype, d, G):
+    banner(f"dense dtype={dtype} d={d} G={G}")
+    c = W.dense_case(2, 8 if G < 8 else 16, (8 if G < 8 else 16) // G, 1000, d, dtype, 256,
+                     seed=10 + G, device=DEV)
+    _check(c)
+
+
+@pytest.mark.parametrize("L", [1, 2, 15, 16, 17, 255, 256, 257, 511, 512, 513, 4097])
+def test_lengths_around_chunk_edges(L):
+    banner(f"dense L={L}")
+    _check(W.dense_case(2, 8, 2, L, 128, "bf16", 256, seed=L, device=DEV))
+
+
+def test_config1_fp32_mha():
+    banner("dense config1 fp32")
+    _check(W.config_case(1, device=DEV))
+
+
+@pytest.mark.parametrize("chunk", [16, 48, 128, 512, 4096])
+def test_chunk_independence(chunk):
+    banner(f"dense chunk={chunk}")
+    c = W.dense_case(1, 8, 2, 3000, 128, "f32", 512, seed=5, device=DEV)
+    out, lse = fd.decode_attn(c.q, c.k, c.v, chunk=chunk)
+    ref, lref = fd.decode_attn(c.q, c.k, c.v, chunk=3008)   # one chunk
+    assert max_err(f64(out), f64(ref)) < 1e-5 and max_err(f64(lse), f64(lref)) < 1e-5
+    _check(c, chunk=chunk)
+
+
+def test_single_key_is_value_bitwise():
+    c = W.dense_case(2, 8, 8, 1, 64, "f32", 16, seed=3, device=DEV)
+    out, lse = fd.decode_attn(c.q, c.k, c.v, chunk=16)
+    torch.cuda.synchronize()
+    assert torch.equal(out, c.v[:, :, 0].float())
+
+
+def test_zero_query_is_mean():
+    c = W.dense_case(1, 4, 4, 777, 128, "f32", 64, seed=4, device=DEV)
+    q = torch.zeros_like(c.q)
+    out, lse = fd.decode_attn(q, c.k, c.v, chunk=64)
+    assert max_err(f64(out), f64(c.v).mean(2)) < 1e-5
+    assert max_err(f64(lse), np.full((1, 4), math.log(777))) < 1e-5
+
+
+def test_large_shift_no_overflow():
+    # scores around +1000: the running maximum keeps exp finite
+    c = W.dense_case(1, 4, 1, 2000, 64, "f32", 128, seed=6, device=DEV)
+    qd = f64(c.q)[0, 0]
+    w = 1000.0 * qd / (c.scale * (qd @ qd))
+    k = c.k + torch.as_tensor(w, dtype=torch.float32, device=DEV)
+    out, lse = fd.decode_attn(c.q[:, :1].contiguous(), k, c.v, chunk=128)
+    ref, lref = ofd.dense_attention(f64(c.q)[:, :1], f64(k), f64(c.v), c.scale)
+    assert np.all(np.isfinite(f64(out)))
+    assert max_err(f64(out), ref) < 1e-4 and max_err(f64(lse), lref) < 1e-3
+
+
+def test_deterministic_bitwise():
+    c = W.dense_case(2, 32, 8, 5000, 128, "bf16", 512, seed=7, device=DEV)
+    a, la = fd.decode_attn(c.q, c.k, c.v, chunk=512)
+    b, lb = fd.decode_attn(c.q, c.k, c.v, chunk=512)
+    assert torch.equal(a, b) and torch.equal(la, lb)
+
+
+def test_config2_full_size_sampled():
+    banner("dense config2 full size")
+    c = W.config_case(2, device=DEV)
+    out, lse = fd.decode_attn(c.q, c.k, c.v, chunk=c.chunk)
+    torch.cuda.synchronize()
+    rows = [(0, 0), (0, 31), (3, 5), (7, 12), (7, 31), (5, 20)]
+    G = 4
+    for b, h in rows:
+        K = f64(c.k[b, h // G]); V = f64(c.v[b, h // G])
+        r, lr = ofd.attention_row(f64(c.q[b, h]), K, V, c.scale)
+        assert max_err(f64(out[b, h]), r) <= 2e-3
+        assert abs(float(lse[b, h]) - lr) <= 2e-3
+    assert torch.isfinite(out).all()
