@@ -1,0 +1,418 @@
+#!/usr/bin/env python3
+"""Decode-attention benchmark on one MI355X.
+
+Prints ONE JSON line.  The headline workload is dense GQA decode over a
+contiguous bf16 cache: B = 8 sequences, Hq = 32 query heads, Hkv = 8 kv-heads,
+head dim 128, 32768 cached positions, split-KV chunks of 512.  A step is one
+decode-attention call over the whole batch (every kernel of the call).
+
+  value      = algorithmic bytes of a step / step time   (GB/s, KV read +
+               query + output), inputs resident in HBM
+  ms_per_step, us_per_step, pct_of_peak (of 8 TB/s)
+  roofline   = the split-KV partial kernel alone (the dominant kernel), timed
+               with HIP events on the launch stream: KV + query bytes per
+               launch / mean launch time, against 8 TB/s
+  cpu_baseline = the fp64 CPU oracle on a bounded sample of the same workload
+  variants   = the paged, fixed-maximum and FFD entry points on their own
+               workloads (same timing method), for the whole hot path
+
+K/V live in several copies that the timed steps rotate through, so each call
+reads data that is not resident in the 256 MB last-level cache.
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1]
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes as C
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_GBS = 8000.0       # MI355X HBM3E peak, GB/s
+METRIC = "us/decode step and achieved KV-read HBM GB/s (% of peak) at 32K-128K ctx"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_partial_dense_b8_h32x8_d128_l32768.txt")
+KERNEL_SOURCES = ["attn.hip", "splitkv.hpp", "common.hpp"]
+
+
+def parse_args():
+    p = argparse.ArgumentParser(description=__doc__,
+                                formatter_class=argparse.RawDescriptionHelpFormatter)
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=30)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--copies", type=int, default=3, help="rotated K/V copies")
+    p.add_argument("--no-variants", action="store_true")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-seconds", type=float, default=12.0,
+                   help="target CPU time of the oracle sample")
+    p.add_argument("--copy-calibration", action="store_true",
+                   help="only run a 1 GiB device copy (counter scale for --pmc runs)")
+    return p.parse_args()
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "long_context_decode_fd_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic():
+    """HBM bytes per launch of the partial kernel from the committed counter
+    summary, if it was taken on the current kernel sources; else None."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    vals = {}
+    for line in open(TRAFFIC_FILE):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            vals[k.strip()] = v.strip()
+    if vals.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    try:
+        return int(float(vals["traffic_bytes_per_dispatch"]))
+    except (KeyError, ValueError):
+        return None
+
+
+class Timer:
+    """Back-to-back calls on the current stream, timed with HIP events."""
+
+    def __init__(self, torch):
+        self.torch = torch
+
+    def run(self, calls, steps, warmup):
+        torch = self.torch
+        for i in range(warmup):
+            calls[i % len(calls)]()
+        torch.cuda.synchronize()
+        s = torch.cuda.current_stream()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+        ev[0].record(s)
+        for i in range(steps):
+            calls[i % len(calls)]()
+            ev[i + 1].record(s)
+        torch.cuda.synchronize()
+        per = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(steps))
+        total = ev[0].elapsed_time(ev[steps])
+        return dict(ms=total / steps, p10=per[len(per) // 10],
+                    p50=per[len(per) // 2], p90=per[(9 * len(per)) // 10])
+
+
+def vp(t):
+    return C.c_void_p(t.data_ptr())
+
+
+def check_rc(lib, rc):
+    if rc != 0:
+        raise RuntimeError(f"library call failed ({rc}): {lib.fd_last_error().decode()}")
+
+
+def gbs(nbytes, ms):
+    return nbytes / (ms * 1e-3) / 1e9
+
+
+def copy_calibration():
+    import torch
+    n = 1 << 30
+    x = torch.empty(n, dtype=torch.uint8, device="cuda:0")
+    y = torch.empty_like(x)
+    x.fill_(1)
+    for _ in range(3):
+        y.copy_(x)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes_read": n, "copy_calibration_bytes_written": n,
+                      "dispatches": 3}), flush=True)
+
+
+def dense_headline(torch, fd, W, args, timer):
+    cfg = W.CONFIGS[2]
+    B, Hq, Hkv, L, d, chunk = cfg["B"], cfg["Hq"], cfg["Hkv"], cfg["L"], cfg["d"], cfg["chunk"]
+    case = W.config_case(2, device="cuda:0")
+    ks = [case.k] + [case.k.clone() for _ in range(args.copies - 1)]
+    vs = [case.v] + [case.v.clone() for _ in range(args.copies - 1)]
+    lib = fd.lib()
+    out = torch.empty((B, Hq, d), dtype=torch.float32, device="cuda:0")
+    lse = torch.empty((B, Hq), dtype=torch.float32, device="cuda:0")
+    wsn = fd.workspace_bytes("fd_decode_attn", B=B, Hq=Hq, Hkv=Hkv, L=L, d=d, chunk=chunk)
+    ws = torch.empty(wsn, dtype=torch.uint8, device="cuda:0")
+    size = C.c_size_t(wsn)
+    st = C.c_void_p(torch.cuda.current_stream().cuda_stream)
+    scale = case.scale
+
+    def mk_full(k, v):
+        a = (fd.FD_BF16, vp(case.q), vp(k), vp(v), vp(out), vp(lse), B, Hq, Hkv, L, d, scale,
+             chunk, vp(ws), C.byref(size), st)
+        return lambda: lib.fd_decode_attn(*a)
+
+    def mk_part(k, v):
+        a = (fd.FD_BF16, vp(case.q), vp(k), vp(v), B, Hq, Hkv, L, d, scale, chunk, vp(ws),
+             C.byref(size), st)
+        return lambda: lib.fd_decode_attn_partials(*a)
+
+    full = [mk_full(k, v) for k, v in zip(ks, vs)]
+    part = [mk_part(k, v) for k, v in zip(ks, vs)]
+    check_rc(lib, full[0]())
+    check_rc(lib, part[0]())
+    t_full = timer.run(full, args.steps, args.warmup)
+    t_part = timer.run(part, args.steps, args.warmup)
+
+    kv_bytes = 2 * B * Hkv * L * d * 2
+    q_bytes = B * Hq * d * 2
+    out_bytes = B * Hq * d * 4 + B * Hq * 4
+    step_bytes = kv_bytes + q_bytes + out_bytes
+    part_bytes = kv_bytes + q_bytes
+    achieved = gbs(part_bytes, t_part["ms"])
+    return case, dict(
+        t_full=t_full, t_part=t_part, step_bytes=step_bytes, part_bytes=part_bytes,
+        value=gbs(step_bytes, t_full["ms"]), achieved=achieved,
+        workload=dict(workload="dense GQA decode, contiguous bf16 KV cache", B=B, Hq=Hq,
+                      Hkv=Hkv, head_dim=d, kv_len=L, chunk=chunk, n_chunks=L // chunk,
+                      scale="1/sqrt(128)", kv_copies_rotated=args.copies))
+
+
+def cpu_baseline(torch, case, target_s):
+    """fp64 oracle on whole sequences of the headline workload until about
+    target_s seconds of oracle time; bf16 -> fp64 conversion excluded."""
+    import numpy as np
+    from oracle import flash_decoding as ofd
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = 1
+    B, Hq, d = case.q.shape
+    Hkv, L = case.k.shape[1], case.k.shape[2]
+    G = Hq // Hkv
+    t_oracle, t_conv, done = 0.0, 0.0, 0
+    for b in range(B):
+        t0 = time.perf_counter()
+        K = case.k[b].to("cpu", torch.float64).numpy()
+        V = case.v[b].to("cpu", torch.float64).numpy()
+        qb = case.q[b].to("cpu", torch.float64).numpy()
+        t1 = time.perf_counter()
+        for h in range(Hq):
+            ofd.attention_row(qb[h], K[h // G], V[h // G], case.scale)
+        t2 = time.perf_counter()
+        t_conv += t1 - t0
+        t_oracle += t2 - t1
+        done += 1
+        if t_oracle >= target_s:
+            break
+    seq_bytes = 2 * Hkv * L * d * 2 + Hq * d * 2 + Hq * d * 4 + Hq * 4
+    return dict(value=round(gbs(done * seq_bytes, t_oracle * 1e3), 4), unit="GB/s",
+                cores=int(threads), kind="oracle",
+                sample=(f"{done} of {B} sequences (all {Hq} query heads each) of the headline "
+                        f"workload; fp64 numpy oracle, {t_oracle:.2f} s; bf16->fp64 input "
+                        f"conversion {t_conv:.2f} s excluded"),
+                us_per_step_equiv=round(t_oracle / done * B * 1e6, 1),
+                host_cpus=len(os.sched_getaffinity(0)))
+
+
+def variant_paged(torch, fd, W, args, timer):
+    cfg = W.CONFIGS[3]
+    c = W.config_case(3, device="cuda:0")
+    B, Hq, d = c.q.shape
+    Hkv = c.k_pool.shape[1]
+    lens = c.meta["lens"]
+    max_len = int(max(lens))
+    lib = fd.lib()
+    out = torch.empty((B, Hq, d), dtype=torch.float32, device="cuda:0")
+    lse = torch.empty((B, Hq), dtype=torch.float32, device="cuda:0")
+    wsn = fd.workspace_bytes("fd_decode_attn_paged", B=B, Hq=Hq, Hkv=Hkv, d=d, page=c.page,
+                             max_pages=c.block_table.shape[1], max_seq_len=max_len,
+                             chunk=c.chunk)
+    ws = torch.empty(wsn, dtype=torch.uint8, device="cuda:0")
+    size = C.c_size_t(wsn)
+    st = C.c_void_p(torch.cuda.current_stream().cuda_stream)
+    a = (fd.FD_BF16, vp(c.q), vp(c.k_pool), vp(c.v_pool), vp(c.block_table), vp(c.seq_lens),
+         vp(out), vp(lse), B, Hq, Hkv, d, c.page, c.block_table.shape[1], c.k_pool.shape[0],
+         max_len, c.scale, c.chunk, vp(ws), C.byref(size), st)
+    call = lambda: lib.fd_decode_attn_paged(*a)  # noqa: E731
+    check_rc(lib, call())
+    t = timer.run([call], args.steps, args.warmup)
+    total_len = int(sum(lens))
+    nbytes = (2 * total_len * Hkv * d * 2 + B * Hq * d * 2 + B * Hq * (d + 1) * 4
+              + 4 * int(sum((L + c.page - 1) // c.page for L in lens)))
+    return dict(workload=f"paged ragged GQA decode bf16, B={B}, Hq={Hq}, Hkv={Hkv}, d={d}, "
+                         f"page={c.page}, lens U[{cfg['len_lo']},{cfg['len_hi']}] "
+                         f"(sum {total_len}, max {max_len}), chunk={c.chunk}",
+                us_per_step=round(t["ms"] * 1e3, 2), p10_us=round(t["p10"] * 1e3, 2),
+                p90_us=round(t["p90"] * 1e3, 2), bytes=nbytes,
+                gbs=round(gbs(nbytes, t["ms"]), 1),
+                pct_of_peak=round(100 * gbs(nbytes, t["ms"]) / PEAK_GBS, 1))
+
+
+def variant_unified(torch, fd, W, args, timer):
+    c = W.config_case(4, device="cuda:0")
+    B, Hq, d = c.q.shape
+    Hkv, L = c.k.shape[1], c.k.shape[2]
+    nc = (L + c.chunk - 1) // c.chunk
+    ks = [c.k] + [c.k.clone() for _ in range(args.copies - 1)]
+    vs = [c.v] + [c.v.clone() for _ in range(args.copies - 1)]
+    lib = fd.lib()
+    out = torch.empty((B, Hq, d), dtype=torch.float32, device="cuda:0")
+    lse = torch.empty((B, Hq), dtype=torch.float32, device="cuda:0")
+    flags = torch.zeros((B, Hq, nc), dtype=torch.uint8, device="cuda:0")
+    wsn = fd.workspace_bytes("fd_decode_attn_unified_max", B=B, Hq=Hq, Hkv=Hkv, L=L, d=d,
+                             chunk=c.chunk)
+    ws = torch.empty(wsn, dtype=torch.uint8, device="cuda:0")
+    size = C.c_size_t(wsn)
+    st = C.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+    def mk_u(k, v):
+        a = (fd.FD_BF16, vp(c.q), vp(k), vp(v), vp(out), vp(lse), B, Hq, Hkv, L, d, c.scale,
+             c.chunk, c.phi, c.margin_hi, c.margin_lo, vp(flags), vp(ws), C.byref(size), st)
+        return lambda: lib.fd_decode_attn_unified_max(*a)
+
+    def mk_d(k, v):
+        a = (fd.FD_BF16, vp(c.q), vp(k), vp(v), vp(out), vp(lse), B, Hq, Hkv, L, d, c.scale,
+             c.chunk, vp(ws), C.byref(size), st)
+        return lambda: lib.fd_decode_attn(*a)
+
+    uni = [mk_u(k, v) for k, v in zip(ks, vs)]
+    den = [mk_d(k, v) for k, v in zip(ks, vs)]
+    check_rc(lib, uni[0]())
+    torch.cuda.synchronize()
+    flagged_heads = int(flags.sum())
+    G = Hq // Hkv
+    unit_flags = flags.view(B, Hkv, G, nc).amax(2)
+    fallback_units = int(unit_flags.sum())
+    t_u = timer.run(uni, args.steps, args.warmup)
+    check_rc(lib, den[0]())
+    t_d = timer.run(den, args.steps, args.warmup)
+    nbytes = 2 * B * Hkv * L * d * 2 + B * Hq * d * 2 + B * Hq * (d + 1) * 4
+    return dict(workload=f"fixed-maximum decode bf16, B={B}, Hq={Hq}, Hkv={Hkv}, d={d}, L={L}, "
+                         f"chunk={c.chunk}, phi={c.phi}, margins +{c.margin_hi}/-{c.margin_lo}, "
+                         f"{len(c.overflow_heads)} heads planted above phi",
+                us_per_step=round(t_u["ms"] * 1e3, 2), p10_us=round(t_u["p10"] * 1e3, 2),
+                p90_us=round(t_u["p90"] * 1e3, 2), bytes=nbytes,
+                gbs=round(gbs(nbytes, t_u["ms"]), 1),
+                pct_of_peak=round(100 * gbs(nbytes, t_u["ms"]) / PEAK_GBS, 1),
+                flagged_head_chunks=flagged_heads, fallback_units=fallback_units,
+                fallback_reread_bytes=fallback_units * c.chunk * d * 2 * 2,
+                dense_same_data_us_per_step=round(t_d["ms"] * 1e3, 2),
+                dense_over_unified=round(t_d["ms"] / t_u["ms"], 3))
+
+
+def variant_ffd(torch, fd, W, args, timer):
+    import numpy as np
+    c = W.config_case(5, device="cuda:0")
+    B, Hq, d = c.q.shape
+    Hkv, L = c.v.shape[1], c.v.shape[2]
+    G = Hq // Hkv
+    lib = fd.lib()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    packs = [fd.ffd_pack(c.k)]
+    torch.cuda.synchronize()
+    pack_ms = (time.perf_counter() - t0) * 1e3
+    for _ in range(args.copies - 1):
+        packs.append({k: v.clone() for k, v in packs[0].items()})
+    vs = [c.v] + [c.v.clone() for _ in range(args.copies - 1)]
+    out = torch.empty((B, Hq, d), dtype=torch.float32, device="cuda:0")
+    lse = torch.empty((B, Hq), dtype=torch.float32, device="cuda:0")
+    wsn = fd.workspace_bytes("fd_ffd_sparse_decode", B=B, Hq=Hq, Hkv=Hkv, L=L, d=d,
+                             chunk=c.chunk)
+    ws = torch.empty(wsn, dtype=torch.uint8, device="cuda:0")
+    size = C.c_size_t(wsn)
+    st = C.c_void_p(torch.cuda.current_stream().cuda_stream)
+    res = {}
+    for delta in c.deltas:
+        def mk(p, v):
+            a = (vp(c.q), vp(p["codes"]), vp(p["zs"]), vp(p["res"]), vp(p["rs"]), vp(v),
+                 vp(out), vp(lse), B, Hq, Hkv, L, d, c.scale, float(delta), c.n_sink,
+                 c.n_local, c.chunk, None, None, vp(ws), C.byref(size), st)
+            return lambda: lib.fd_ffd_sparse_decode(*a)
+        calls = [mk(p, v) for p, v in zip(packs, vs)]
+        check_rc(lib, calls[0]())
+        _, _, mask, _ = fd.ffd_sparse_decode(c.q, packs[0], c.v, delta, c.n_sink, c.n_local,
+                                             chunk=c.chunk, want_mask=True)
+        m = mask.cpu().numpy().view(np.uint32).reshape(B, Hkv, G, -1)
+        per_head = np.unpackbits(m.view(np.uint8), axis=-1).sum(-1)   # [B,Hkv,G]
+        union = np.bitwise_or.reduce(m, axis=2)
+        n_union = int(np.unpackbits(union.view(np.uint8), axis=-1).sum())
+        t = timer.run(calls, args.steps, args.warmup)
+        n_anchor = min(L, c.n_sink + c.n_local)
+        nbytes = (B * Hkv * L * (d // 4 + d // 32 * 4) + n_union * (d + d // 32 * 2 + 2 * d)
+                  + B * Hkv * n_anchor * (d // 4 + d // 32 * 6 + d)
+                  + B * Hq * d * 2 + B * Hq * (d + 1) * 4)
+        res[f"delta_{delta:g}"] = dict(
+            us_per_step=round(t["ms"] * 1e3, 2), p10_us=round(t["p10"] * 1e3, 2),
+            p90_us=round(t["p90"] * 1e3, 2), bytes=int(nbytes),
+            gbs=round(gbs(nbytes, t["ms"]), 1),
+            pct_of_peak=round(100 * gbs(nbytes, t["ms"]) / PEAK_GBS, 1),
+            kept_per_head=round(float(per_head.mean()) / L, 4),
+            kept_group_union=round(n_union / (B * Hkv * L), 4),
+            dense_bf16_equiv_bytes=2 * B * Hkv * L * d * 2)
+    return dict(workload=f"FFD sparse decode, B={B}, Hq={Hq}, Hkv={Hkv}, d={d}, L={L}, "
+                         f"chunk={c.chunk}, sinks={c.n_sink}, local={c.n_local}",
+                pack_ms_whole_cache=round(pack_ms, 2), **res)
+
+
+def main():
+    args = parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "
+              "(the multi-GPU split is a design note, not a built path)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    if args.copy_calibration:
+        copy_calibration()
+        return
+    import long_context_decode_fd_amd as fd
+    import workloads as W
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    timer = Timer(torch)
+    case, h = dense_headline(torch, fd, W, args, timer)
+    line = {
+        "metric": METRIC,
+        "value": round(h["value"], 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(h["t_full"]["ms"], 5),
+        "us_per_step": round(h["t_full"]["ms"] * 1e3, 2),
+        "us_per_step_p10_p50_p90": [round(h["t_full"][k] * 1e3, 2) for k in ("p10", "p50", "p90")],
+        "pct_of_peak": round(100 * h["value"] / PEAK_GBS, 1),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic: seeded iid N(0,1) q/K/V rounded to bf16 (no model weights)",
+        "config": h["workload"],
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "partial_kernel (split-KV chunk partials)",
+            "achieved": round(h["achieved"], 1),
+            "peak": PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(h["achieved"] / PEAK_GBS, 4),
+            "traffic": read_traffic(),
+            "algorithmic_bytes_per_launch": h["part_bytes"],
+            "launch_us_mean": round(h["t_part"]["ms"] * 1e3, 2),
+        },
+    }
+    if not args.no_variants:
+        line["variants"] = {
+            "paged": variant_paged(torch, fd, W, args, timer),
+            "unified_max": variant_unified(torch, fd, W, args, timer),
+            "ffd": variant_ffd(torch, fd, W, args, timer),
+        }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(torch, case, args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -85,6 +85,32 @@ int fd_decode_attn(fd_dtype_t dt, const void* q, const void* k, const void* v,
                    void* ws, size_t* ws_bytes, void* stream);
 
 /*
+ * The two stages of fd_decode_attn, for callers that merge partials
+ * themselves -- e.g. partials of one sequence computed on several devices and
+ * gathered along the chunk axis ("Flash Decoding" explainer, section 2: the
+ * merge needs only (m_i, l_i, O_i) of every block).
+ *
+ * fd_decode_attn_partials takes the arguments of fd_decode_attn minus out
+ * and lse, and leaves the chunk partials in ws (same workspace size):
+ *   O   fp32 [B, Hq, n_chunks, d] at byte offset 0, O_c = sum_j 2^(s_j - m_c) v_j
+ *   ML  fp32 [B, Hq, n_chunks, 2] at byte offset round_up(B*Hq*n_chunks*d*4, 256):
+ *       (m_c, l_c) with m_c = log2(e) * max_j scale*q.k_j and
+ *       l_c = sum_j 2^(s_j - m_c), where s_j = log2(e) * scale * q.k_j.
+ * fd_merge_partials merges such partials into out fp32 [B, Hq, d] and lse
+ * fp32 [B, Hq] (nullable):
+ *   M = max_c m_c, out = sum_c 2^(m_c-M) O_c / sum_c 2^(m_c-M) l_c,
+ *   lse = ln 2 * (M + log2 sum_c 2^(m_c-M) l_c).
+ * n_chunks >= 1; o_part and ml_part 16-byte aligned.
+ */
+int fd_decode_attn_partials(fd_dtype_t dt, const void* q, const void* k,
+                            const void* v, int B, int Hq, int Hkv, int L, int d,
+                            float scale, int chunk, void* ws, size_t* ws_bytes,
+                            void* stream);
+
+int fd_merge_partials(const float* o_part, const float* ml_part, float* out,
+                      float* lse, int B, int Hq, int n_chunks, int d, void* stream);
+
+/*
  * Dense decode attention over a paged cache ("Flash Decoding" explainer,
  * section 3: the cache is cut into fixed-size pages allocated on demand).
  *   dt              FD_BF16 or FD_F32 (element type of q and both pools)

@@ -22,7 +22,7 @@ import torch
 from . import _abi
 from ._abi import FD_BF16, FD_F32, FdError  # noqa: F401
 
-__all__ = ["decode_attn", "decode_attn_paged", "decode_attn_unified_max", "ffd_pack",
+__all__ = ["decode_attn", "decode_attn_partials", "merge_partials", "decode_attn_paged", "decode_attn_unified_max", "ffd_pack",
            "ffd_sparse_decode", "workspace_bytes", "FdError", "lib"]
 
 
@@ -100,6 +100,48 @@ def decode_attn(q, k, v, chunk=512, scale=None, out=None, lse=None, want_lse=Tru
                 scale, int(chunk), ws, wsb, st)
     workspace, size = _workspace(L_.fd_decode_attn, args, workspace, dev)
     _abi.check(L_.fd_decode_attn(*args(_ptr(workspace), C.byref(size))))
+    return out, lse
+
+
+def decode_attn_partials(q, k, v, chunk=512, scale=None, workspace=None):
+    """First stage of decode_attn: chunk partials into ``workspace`` (uint8
+    tensor, allocated if None or too small).  Returns (workspace, n_chunks)."""
+    B, Hq, d = q.shape
+    Hkv, L = k.shape[1], k.shape[2]
+    dev = q.device
+    _need(q, "q", device=dev)
+    _need(k, "k", (B, Hkv, L, d), q.dtype, dev)
+    _need(v, "v", (B, Hkv, L, d), q.dtype, dev)
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    L_ = lib()
+    st = _stream(dev)
+
+    def args(ws, wsb):
+        return (_dt(q), _ptr(q), _ptr(k), _ptr(v), B, Hq, Hkv, L, d, scale, int(chunk), ws,
+                wsb, st)
+    workspace, size = _workspace(L_.fd_decode_attn_partials, args, workspace, dev)
+    _abi.check(L_.fd_decode_attn_partials(*args(_ptr(workspace), C.byref(size))))
+    return workspace, (L + int(chunk) - 1) // int(chunk)
+
+
+def partial_views(workspace, B, Hq, n_chunks, d):
+    """(O [B,Hq,nc,d], ML [B,Hq,nc,2]) fp32 views of a partials workspace."""
+    n_o = B * Hq * n_chunks * d
+    off = ((n_o * 4 + 255) // 256) * 256
+    o = workspace[:n_o * 4].view(torch.float32).view(B, Hq, n_chunks, d)
+    ml = workspace[off:off + B * Hq * n_chunks * 8].view(torch.float32).view(B, Hq, n_chunks, 2)
+    return o, ml
+
+
+def merge_partials(o_part, ml_part, out=None, lse=None, want_lse=True):
+    """Exact merge of chunk partials O [B,Hq,nc,d], ML [B,Hq,nc,2] (fp32)."""
+    B, Hq, nc, d = o_part.shape
+    dev = o_part.device
+    _need(o_part, "o_part", dtype=torch.float32)
+    _need(ml_part, "ml_part", (B, Hq, nc, 2), torch.float32, dev)
+    out, lse = _outs(B, Hq, d, dev, out, lse, want_lse)
+    _abi.check(lib().fd_merge_partials(_ptr(o_part), _ptr(ml_part), _ptr(out), _ptr(lse), B,
+                                       Hq, nc, d, _stream(dev)))
     return out, lse
 
 

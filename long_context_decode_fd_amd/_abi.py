@@ -22,6 +22,9 @@ SIGNATURES = {
     "fd_abi_version": [],
     "fd_decode_attn": [_i, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f, _i,
                        _vp, _szp, _vp],
+    "fd_decode_attn_partials": [_i, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f, _i, _vp, _szp,
+                                _vp],
+    "fd_merge_partials": [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _vp],
     "fd_decode_attn_paged": [_i, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i,
                              _i, _i, _i, _i, _f, _i, _vp, _szp, _vp],
     "fd_decode_attn_unified_max": [_i, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i,

@@ -86,6 +86,7 @@ void split_ws(void* ws, int B, int Hq, int nc, int d, float** o_part, float** ml
                                       align256(rows * d * sizeof(float)));
 }
 
+// Enqueue the partial kernel and (when out != NULL) the merge.
 int run_split_kv(int mode, fd_dtype_t dt, const void* q, const void* k, const void* v,
                  float* out, float* lse, int B, int Hq, int Hkv, int L, int d,
                  float scale, int chunk, int nc, fdk::PartialArgs pa, void* ws,
@@ -109,6 +110,7 @@ int run_split_kv(int mode, fd_dtype_t dt, const void* q, const void* k, const vo
     hipError_t e = fdk::launch_partial(mode, dt == FD_BF16, d, Hq / Hkv, pa, s);
     if (e != hipSuccess) return hip_status(e, "partial kernel launch");
   }
+  if (out == nullptr) return ok();
   fdk::MergeArgs ma{o_part, ml_part, out, lse, seq_lens, Hq, nc, chunk, max_seq_len};
   return hip_status(fdk::launch_merge(d, B, ma, s), "merge kernel launch");
 }
@@ -138,6 +140,38 @@ int fd_decode_attn(fd_dtype_t dt, const void* q, const void* k, const void* v, f
   fdk::PartialArgs pa{};
   return run_split_kv(fdk::kDense, dt, q, k, v, out, lse, B, Hq, Hkv, L, d, scale, chunk, nc,
                       pa, ws, nullptr, L, stream);
+}
+
+int fd_decode_attn_partials(fd_dtype_t dt, const void* q, const void* k, const void* v,
+                            int B, int Hq, int Hkv, int L, int d, float scale, int chunk,
+                            void* ws, size_t* ws_bytes, void* stream) {
+  if (dt != FD_F32 && dt != FD_BF16) return fail(FD_ERR_ARG, "unknown dtype %d", (int)dt);
+  if (int e = check_heads(B, Hq, Hkv, d)) return e;
+  if (L <= 0) return fail(FD_ERR_ARG, "L=%d must be positive", L);
+  if (int e = check_chunk(chunk)) return e;
+  if (int e = check_scale(scale)) return e;
+  const int nc = (L + chunk - 1) / chunk;
+  if (int e = workspace_gate(ws, ws_bytes, partial_bytes(B, Hq, nc, d))) return e;
+  if (ws == nullptr) return ok();
+  if (!q || !k || !v) return fail(FD_ERR_ARG, "q, k and v must not be NULL");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v))
+    return fail(FD_ERR_ARG, "q, k and v must be 16-byte aligned");
+  fdk::PartialArgs pa{};
+  return run_split_kv(fdk::kDense, dt, q, k, v, nullptr, nullptr, B, Hq, Hkv, L, d, scale,
+                      chunk, nc, pa, ws, nullptr, L, stream);
+}
+
+int fd_merge_partials(const float* o_part, const float* ml_part, float* out, float* lse,
+                      int B, int Hq, int n_chunks, int d, void* stream) {
+  if (B <= 0 || Hq <= 0 || n_chunks <= 0)
+    return fail(FD_ERR_ARG, "B=%d Hq=%d n_chunks=%d must be positive", B, Hq, n_chunks);
+  if (d != 64 && d != 128) return fail(FD_ERR_UNSUPPORTED, "d=%d not in {64,128}", d);
+  if (!o_part || !ml_part || !out) return fail(FD_ERR_ARG, "o_part, ml_part, out NULL");
+  if (!aligned16(o_part) || !aligned16(ml_part))
+    return fail(FD_ERR_ARG, "o_part and ml_part must be 16-byte aligned");
+  fdk::MergeArgs ma{o_part, ml_part, out, lse, nullptr, Hq, n_chunks, 1, 0};
+  return hip_status(fdk::launch_merge(d, B, ma, reinterpret_cast<hipStream_t>(stream)),
+                    "merge kernel launch");
 }
 
 int fd_decode_attn_paged(fd_dtype_t dt, const void* q, const void* k_pool,

@@ -1,0 +1,163 @@
+"""GPU parity of the paged and fixed-maximum paths against the fp64 oracle."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import long_context_decode_fd_amd as fd
+import workloads as W
+from oracle import flash_decoding as ofd
+from oracle import paged as opg
+from oracle import unified as oun
+from tests.helpers import TOL, banner, f64, max_err
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+def _paged_run(c, max_len=None):
+    max_len = int(max(c.meta["lens"])) if max_len is None else max_len
+    out, lse = fd.decode_attn_paged(c.q, c.k_pool, c.v_pool, c.block_table, c.seq_lens,
+                                    max_len, chunk=c.chunk)
+    torch.cuda.synchronize()
+    return out, lse
+
+
+def _paged_ref(c, rows=None):
+    return opg.paged_attention(f64(c.q), f64(c.k_pool), f64(c.v_pool),
+                               c.block_table.cpu().numpy(), c.seq_lens.cpu().numpy(), c.page,
+                               c.scale, rows=rows)
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+@pytest.mark.parametrize("d,G", [(128, 4), (64, 1), (128, 8), (64, 2)])
+def test_paged_ragged(dtype, d, G):
+    banner(f"paged d={d} G={G} {dtype}")
+    lens = [0, 1, 15, 16, 17, 63, 64, 65, 200, 1000]
+    Hq = 16 if G == 8 else 8
+    c = W.paged_case(len(lens), Hq, Hq // G, d, 0, 1024, page=16, chunk=64, seed=d + G,
+                     device=DEV, lens=lens)
+    if dtype == torch.float32:
+        c.q, c.k_pool, c.v_pool = c.q.float(), c.k_pool.float(), c.v_pool.float()
+    out, lse = _paged_run(c)
+    ref, lref = _paged_ref(c)
+    assert max_err(f64(out), ref) <= TOL[dtype]
+    assert max_err(f64(lse), lref) <= TOL[dtype]
+    assert torch.all(out[0] == 0) and torch.all(torch.isinf(lse[0]))
+
+
+@pytest.mark.parametrize("page,chunk", [(8, 64), (32, 128), (64, 64)])
+def test_paged_page_sizes(page, chunk):
+    c = W.paged_case(4, 8, 2, 128, 100, 700, page=page, chunk=chunk, seed=page, device=DEV)
+    out, lse = _paged_run(c)
+    ref, lref = _paged_ref(c)
+    assert max_err(f64(out), ref) <= 2e-3 and max_err(f64(lse), lref) <= 2e-3
+
+
+def test_paged_equals_dense_and_relabel_invariant():
+    lens = [300, 300, 300]
+    c = W.paged_case(3, 8, 2, 128, 0, 512, page=16, chunk=128, seed=9, device=DEV, lens=lens)
+    out, lse = _paged_run(c)
+    # contiguous copy of the same sequences
+    pg = c.block_table[:, :19].long()                    # 19 pages of 16 cover 300
+    k = c.k_pool[pg].permute(0, 2, 1, 3, 4).reshape(3, 2, 19 * 16, 128)[:, :, :300].contiguous()
+    v = c.v_pool[pg].permute(0, 2, 1, 3, 4).reshape(3, 2, 19 * 16, 128)[:, :, :300].contiguous()
+    o2, l2 = fd.decode_attn(c.q, k, v, chunk=128)
+    assert torch.equal(out, o2) and torch.equal(lse, l2)
+    # relabelling the pool's pages: same arithmetic, bitwise equal
+    P = c.k_pool.shape[0]
+    perm = torch.randperm(P, generator=torch.Generator().manual_seed(1)).to(DEV)
+    inv = torch.argsort(perm)
+    table = torch.where(c.block_table >= 0, inv[c.block_table.clamp(min=0).long()].int(),
+                        c.block_table)
+    o3, l3 = fd.decode_attn_paged(c.q, c.k_pool[perm].contiguous(), c.v_pool[perm].contiguous(),
+                                  table.contiguous(), c.seq_lens, 300, chunk=128)
+    assert torch.equal(out, o3) and torch.equal(lse, l3)
+
+
+def test_paged_config3_full_size_sampled():
+    banner("paged config3 full size")
+    c = W.config_case(3, device=DEV)
+    out, lse = _paged_run(c)
+    rows = [(0, 0), (3, 17), (9, 31), (15, 8)]
+    ref, lref = _paged_ref(c, rows)
+    for b, h in rows:
+        assert max_err(f64(out[b, h]), ref[b, h]) <= 2e-3
+        assert abs(float(lse[b, h]) - lref[b, h]) <= 2e-3
+    assert torch.isfinite(out).all()
+
+
+def _unified_check(c, phi, margin_hi, margin_lo):
+    out, lse, flags = fd.decode_attn_unified_max(c.q, c.k, c.v, phi, chunk=c.chunk,
+                                                 margin_hi=margin_hi, margin_lo=margin_lo)
+    torch.cuda.synchronize()
+    q, k, v = f64(c.q), f64(c.k), f64(c.v)
+    ref, lref, rflags = oun.unified_attention(q, k, v, c.scale, phi, margin_hi, margin_lo,
+                                              c.chunk)
+    tol = TOL[c.q.dtype]
+    assert max_err(f64(out), ref) <= tol and max_err(f64(lse), lref) <= tol
+    # flags agree except where a chunk maximum sits within 1e-4 of a bound
+    B, Hq, d = q.shape
+    G = Hq // k.shape[1]
+    got = flags.cpu().numpy()
+    for b in range(B):
+        for h in range(Hq):
+            s = c.scale * (k[b, h // G] @ q[b, h])
+            for ci, (a0, a1) in enumerate(ofd.chunk_bounds(k.shape[2], c.chunk)):
+                mx = s[a0:a1].max()
+                near = min(abs(mx - (phi + margin_hi)), abs(mx - (phi - margin_lo))) <= 1e-4
+                if not near:
+                    assert got[b, h, ci] == rflags[b, h, ci], (b, h, ci)
+    return got
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("phi", [3.0, 0.0, 60.0, -60.0])
+def test_unified_any_phi_is_exact(dtype, phi):
+    banner(f"unified phi={phi} {dtype}")
+    c = W.dense_case(2, 8, 2, 1500, 128, dtype, 256, seed=21, device=DEV)
+    flags = _unified_check(c, phi, 10.0, 40.0)
+    if phi >= 60.0 or phi <= -60.0:
+        assert flags.all()          # every chunk out of range -> all recomputed
+    if phi == 3.0:
+        assert not flags.any()
+
+
+def test_unified_tight_margins_mixed_flags():
+    c = W.dense_case(1, 8, 8, 4000, 64, "f32", 128, seed=22, device=DEV)
+    flags = _unified_check(c, 1.0, 1.5, 1.0)
+    assert flags.any() and not flags.all()
+
+
+def test_unified_overflow_plant():
+    # one key 100 above phi: exp(100) overflows fp32 without the fallback
+    c = W.dense_case(1, 4, 1, 2048, 64, "f32", 256, seed=23, device=DEV)
+    phi = 2.0
+    qh = f64(c.q)[0, 0]
+    key = (phi + 100.0) / c.scale * qh / (qh @ qh)
+    c.k[0, 0, 1234] = torch.as_tensor(key, dtype=torch.float32, device=DEV)
+    flags = _unified_check(c, phi, 10.0, 40.0)
+    assert flags[0, 0, 1234 // 256] == 1
+
+
+def test_unified_config4_full_size_sampled():
+    banner("unified config4 full size")
+    c = W.config_case(4, device=DEV)
+    out, lse, flags = fd.decode_attn_unified_max(c.q, c.k, c.v, c.phi, chunk=c.chunk,
+                                                 margin_hi=c.margin_hi, margin_lo=c.margin_lo)
+    torch.cuda.synchronize()
+    G = 4
+    rows = [(b, h) for b, h, _ in c.overflow_heads] + [(0, 0), (2, 19), (3, 31)]
+    for b, h in rows:
+        r, lr = ofd.attention_row(f64(c.q[b, h]), f64(c.k[b, h // G]), f64(c.v[b, h // G]),
+                                  c.scale)
+        assert max_err(f64(out[b, h]), r) <= 2e-3
+        assert abs(float(lse[b, h]) - lr) <= 2e-3
+    for b, h, j in c.overflow_heads:
+        assert flags[b, h, j // c.chunk] == 1
+    assert torch.isfinite(out).all()
+    # only planted heads leave the range on this workload
+    planted = {(b, h, j // c.chunk) for b, h, j in c.overflow_heads}
+    got = {tuple(x) for x in torch.nonzero(flags).tolist()}
+    assert got == planted
