@@ -135,8 +135,8 @@ int fd_decode_attn(fd_dtype_t dt, const void* q, const void* k, const void* v, f
   if (int e = workspace_gate(ws, ws_bytes, partial_bytes(B, Hq, nc, d))) return e;
   if (ws == nullptr) return ok();
   if (!q || !k || !v || !out) return fail(FD_ERR_ARG, "q, k, v and out must not be NULL");
-  if (!aligned16(q) || !aligned16(k) || !aligned16(v))
-    return fail(FD_ERR_ARG, "q, k and v must be 16-byte aligned");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
+    return fail(FD_ERR_ARG, "q, k, v and out must be 16-byte aligned");
   fdk::PartialArgs pa{};
   return run_split_kv(fdk::kDense, dt, q, k, v, out, lse, B, Hq, Hkv, L, d, scale, chunk, nc,
                       pa, ws, nullptr, L, stream);
@@ -167,8 +167,8 @@ int fd_merge_partials(const float* o_part, const float* ml_part, float* out, flo
     return fail(FD_ERR_ARG, "B=%d Hq=%d n_chunks=%d must be positive", B, Hq, n_chunks);
   if (d != 64 && d != 128) return fail(FD_ERR_UNSUPPORTED, "d=%d not in {64,128}", d);
   if (!o_part || !ml_part || !out) return fail(FD_ERR_ARG, "o_part, ml_part, out NULL");
-  if (!aligned16(o_part) || !aligned16(ml_part))
-    return fail(FD_ERR_ARG, "o_part and ml_part must be 16-byte aligned");
+  if (!aligned16(o_part) || !aligned16(ml_part) || !aligned16(out))
+    return fail(FD_ERR_ARG, "o_part, ml_part and out must be 16-byte aligned");
   fdk::MergeArgs ma{o_part, ml_part, out, lse, nullptr, Hq, n_chunks, 1, 0};
   return hip_status(fdk::launch_merge(d, B, ma, reinterpret_cast<hipStream_t>(stream)),
                     "merge kernel launch");
@@ -202,8 +202,8 @@ int fd_decode_attn_paged(fd_dtype_t dt, const void* q, const void* k_pool,
   if (ws == nullptr) return ok();
   if (!q || !k_pool || !v_pool || !block_table || !seq_lens || !out)
     return fail(FD_ERR_ARG, "q, pools, block_table, seq_lens and out must not be NULL");
-  if (!aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool))
-    return fail(FD_ERR_ARG, "q and pools must be 16-byte aligned");
+  if (!aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool) || !aligned16(out))
+    return fail(FD_ERR_ARG, "q, pools and out must be 16-byte aligned");
   fdk::PartialArgs pa{};
   pa.block_table = block_table;
   pa.seq_lens = seq_lens;
@@ -232,11 +232,11 @@ int fd_decode_attn_unified_max(fd_dtype_t dt, const void* q, const void* k, cons
   if (int e = workspace_gate(ws, ws_bytes, partial_bytes(B, Hq, nc, d))) return e;
   if (ws == nullptr) return ok();
   if (!q || !k || !v || !out) return fail(FD_ERR_ARG, "q, k, v and out must not be NULL");
-  if (!aligned16(q) || !aligned16(k) || !aligned16(v))
-    return fail(FD_ERR_ARG, "q, k and v must be 16-byte aligned");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
+    return fail(FD_ERR_ARG, "q, k, v and out must be 16-byte aligned");
   fdk::PartialArgs pa{};
   pa.flags = chunk_flags;
-  pa.base_log2 = (float)((double)phi * 1.4426950408889634);
+  pa.phi_raw = (float)((double)phi / (double)scale);
   pa.flag_hi_raw = (float)(((double)phi + margin_hi) / (double)scale);
   pa.flag_lo_raw = (float)(((double)phi - margin_lo) / (double)scale);
   return run_split_kv(fdk::kUnified, dt, q, k, v, out, lse, B, Hq, Hkv, L, d, scale, chunk,
@@ -281,8 +281,9 @@ int fd_ffd_sparse_decode(const void* q, const uint32_t* codes, const uint16_t* z
   if (ws == nullptr) return ok();
   if (!q || !codes || !zs || !res || !rs || !v || !out)
     return fail(FD_ERR_ARG, "q, packed keys, v and out must not be NULL");
-  if (!aligned16(q) || !aligned16(codes) || !aligned16(res) || !aligned16(v))
-    return fail(FD_ERR_ARG, "q, codes, res and v must be 16-byte aligned");
+  if (!aligned16(q) || !aligned16(codes) || !aligned16(res) || !aligned16(v) ||
+      !aligned16(out) || ((uintptr_t)zs & 3) != 0)
+    return fail(FD_ERR_ARG, "q, codes, res, v, out must be 16-byte and zs 4-byte aligned");
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   float *o_part, *ml_part;
   split_ws(ws, B, Hq, nc, d, &o_part, &ml_part);

@@ -17,12 +17,21 @@
 //     for fp32) and a DPP butterfly sums the slices of a row.
 //   * P stays fp32; O accumulates in fp32 (see splitkv.hpp for the row-slot
 //     softmax state and the end-of-unit combine).
+#include <atomic>
+
 #include "internal.hpp"
 #include "splitkv.hpp"
 
 namespace fdk {
 
 constexpr int kMaxChunkPages = 1024;
+
+#ifndef FD_PIPELINE
+#define FD_PIPELINE 0
+#endif
+#ifndef FD_WAVES_PER_EU
+#define FD_WAVES_PER_EU 1
+#endif
 
 // Byte offset (in rows) of cache position t for one kv-head.
 struct RowMap {
@@ -37,24 +46,55 @@ struct RowMap {
   }
 };
 
-// Fixed-maximum update: p = 2^(s*c - base), no running maximum and no
-// rescale; the largest raw score is tracked only for the range check.
-template <typename E, int G, int VEC>
-__device__ __forceinline__ void fixed_update(const float (&s)[kNb][G], const u32x4 (&vr)[kNb],
-                                             float c_log2, float base_log2,
-                                             float (&acc)[G][VEC], float (&mx)[G],
-                                             float (&l)[G]) {
+// Fixed-maximum update with in-flight fallback.  A row slot takes
+// p = 2^((s - phi) c) while its running maximum stays inside
+// [phi - margin_lo, phi + margin_hi]: no rescale, no dependence on other
+// slots or chunks.  The first batch that takes the running maximum out of
+// that range switches the slot, for the rest of the chunk, to the exact
+// computation with its own maximum: the accumulator is rescaled once from
+// phi to that maximum and later batches rescale only when it grows.  Nothing
+// is read twice, and a value never meets an exponent outside the range.
+// m: running maximum (raw), base: the slot's reference (phi or m, raw),
+// on: the slot has switched.
+template <typename E, int G, int VEC, int NB>
+__device__ __forceinline__ void fixed_update(const float (&s)[NB][G], const u32x4 (&vr)[NB],
+                                             float c_log2, float phi_raw, float hi_raw,
+                                             float lo_raw, float (&acc)[G][VEC], float (&m)[G],
+                                             float (&base)[G], bool (&on)[G], float (&l)[G]) {
+  float mb[G];
+  bool need[G];
+  bool change = false;
 #pragma unroll
-  for (int h = 0; h < G; ++h)
+  for (int h = 0; h < G; ++h) {
+    mb[h] = m[h];
 #pragma unroll
-    for (int i = 0; i < kNb; ++i) mx[h] = fmaxf(mx[h], s[i][h]);
+    for (int i = 0; i < NB; ++i) mb[h] = fmaxf(mb[h], s[i][h]);
+    const bool out = (mb[h] > hi_raw) || (mb[h] < lo_raw && mb[h] != kNegInf);
+    need[h] = on[h] ? (mb[h] > m[h]) : out;
+    change |= need[h];
+    m[h] = mb[h];
+  }
+  (void)phi_raw;
+  if (__any(change)) {
 #pragma unroll
-  for (int i = 0; i < kNb; ++i) {
+    for (int h = 0; h < G; ++h) {
+      if (need[h]) {
+        const float a = exp2_hw((base[h] - mb[h]) * c_log2);
+        l[h] *= a;
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) acc[h][e] *= a;
+        base[h] = mb[h];
+        on[h] = true;
+      }
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < NB; ++i) {
     float vf[VEC];
     slice_vals<E>(vr[i], vf);
 #pragma unroll
     for (int h = 0; h < G; ++h) {
-      const float p = exp2_hw(fmaf(s[i][h], c_log2, -base_log2));
+      const float p = exp2_hw((s[i][h] - base[h]) * c_log2);
       l[h] += p;
 #pragma unroll
       for (int e = 0; e < VEC; ++e) acc[h][e] = fmaf(p, vf[e], acc[h][e]);
@@ -64,164 +104,209 @@ __device__ __forceinline__ void fixed_update(const float (&s)[kNb][G], const u32
 
 // Stream rows [t_beg, t_end) of one kv-head through the G query heads.  On
 // return m[h] is in log2 units of the scaled score: the slot's own maximum
-// (FIXED = false) or base_log2 (FIXED = true, where mx[h] receives the largest
-// raw dot product for the range check).
+// (FIXED = false) or its reference -- phi, or its own maximum after a switch
+// (FIXED = true, where mx[h] also receives the largest raw dot product for
+// the range flags).  A slot that saw no row returns m = -inf, l = 0.
 template <bool FIXED, typename E, int D, int G>
 __device__ __forceinline__ void scan_rows(const char* __restrict__ kb,
                                           const char* __restrict__ vb, const RowMap& rm,
-                                          int t_beg, int t_end, const u32x4 (&qv)[G],
-                                          float c_log2, float base_log2,
+                                          int t_beg, int t_end, int t_step,
+                                          const u32x4 (&qv)[G], float c_log2,
+                                          const PartialArgs& a,
                                           float (&acc)[G][Geo<E, D>::kVec], float (&m)[G],
                                           float (&l)[G], float (&mx)[G]) {
   using Gm = Geo<E, D>;
   constexpr int LPT = Gm::kLpt, TPL = Gm::kTpl, ROW = Gm::kRow;
+  constexpr int NB = batch_rows<G>();
   const int lane = threadIdx.x & (kWave - 1);
   const int grp = lane / LPT, col = lane % LPT;
   state_reset<G, Gm::kVec>(acc, m, l);
+  float base[G];
+  bool on[G];
 #pragma unroll
-  for (int h = 0; h < G; ++h) mx[h] = kNegInf;
+  for (int h = 0; h < G; ++h) {
+    mx[h] = kNegInf;
+    base[h] = a.phi_raw;
+    on[h] = false;
+  }
 
-  for (int t0 = t_beg; t0 < t_end; t0 += kNb * TPL) {
-    size_t off[kNb];
+  // One batch: NB rows per slot, K and V.
+  auto load = [&](int t0, u32x4 (&kr)[NB], u32x4 (&vr)[NB]) {
+    size_t off[NB];
 #pragma unroll
-    for (int i = 0; i < kNb; ++i) {
+    for (int i = 0; i < NB; ++i) {
       const int t = min(t0 + i * TPL + grp, t_end - 1);
       off[i] = rm.row(t) * ROW + (size_t)col * 16;
     }
-    u32x4 kr[kNb], vr[kNb];
 #pragma unroll
-    for (int i = 0; i < kNb; ++i) kr[i] = ld16(kb + off[i]);
+    for (int i = 0; i < NB; ++i) kr[i] = ld16_stream(kb + off[i]);
 #pragma unroll
-    for (int i = 0; i < kNb; ++i) vr[i] = ld16(vb + off[i]);
-
-    float s[kNb][G];
+    for (int i = 0; i < NB; ++i) vr[i] = ld16_stream(vb + off[i]);
+  };
+  auto compute = [&](int t0, const u32x4 (&kr)[NB], const u32x4 (&vr)[NB]) {
+    float s[NB][G];
+    float flat[NB * G];
 #pragma unroll
-    for (int i = 0; i < kNb; ++i)
+    for (int i = 0; i < NB; ++i)
 #pragma unroll
-      for (int h = 0; h < G; ++h) s[i][h] = group_sum<LPT>(slice_dot<E>(qv[h], kr[i]));
-    if (t0 + kNb * TPL > t_end) {
+      for (int h = 0; h < G; ++h) flat[i * G + h] = slice_dot<E>(qv[h], kr[i]);
+    group_sum_n<LPT>(flat);
 #pragma unroll
-      for (int i = 0; i < kNb; ++i)
+    for (int i = 0; i < NB; ++i)
+#pragma unroll
+      for (int h = 0; h < G; ++h) s[i][h] = flat[i * G + h];
+    if (t0 + NB * TPL > t_end) {
+#pragma unroll
+      for (int i = 0; i < NB; ++i)
         if (t0 + i * TPL + grp >= t_end)
 #pragma unroll
           for (int h = 0; h < G; ++h) s[i][h] = kNegInf;
     }
-    if constexpr (FIXED) fixed_update<E, G, Gm::kVec>(s, vr, c_log2, base_log2, acc, mx, l);
-    else online_update<E, G, Gm::kVec>(s, vr, c_log2, acc, m, l);
+    if constexpr (FIXED)
+      fixed_update<E, G, Gm::kVec, NB>(s, vr, c_log2, a.phi_raw, a.flag_hi_raw, a.flag_lo_raw,
+                                       acc, mx, base, on, l);
+    else online_update<E, G, Gm::kVec, NB>(s, vr, c_log2, acc, m, l);
+  };
+  constexpr int STEP = NB * TPL;
+#if FD_PIPELINE
+  // Two register buffers: the loads of the next batch are in flight while
+  // the current one is computed.
+  if (t_beg < t_end) {
+    u32x4 ka[NB], va[NB], kc[NB], vc[NB];
+    load(t_beg, ka, va);
+    for (int t0 = t_beg; t0 < t_end; t0 += 2 * STEP) {
+      if (t0 + STEP < t_end) load(t0 + STEP, kc, vc);
+      compute(t0, ka, va);
+      if (t0 + STEP >= t_end) break;
+      if (t0 + 2 * STEP < t_end) load(t0 + 2 * STEP, ka, va);
+      compute(t0 + STEP, kc, vc);
+    }
   }
+#else
+  for (int t0 = t_beg; t0 < t_end; t0 += t_step) {
+    u32x4 kr[NB], vr[NB];
+    load(t0, kr, vr);
+    compute(t0, kr, vr);
+  }
+#endif
   if constexpr (FIXED) {
 #pragma unroll
-    for (int h = 0; h < G; ++h) m[h] = base_log2;
+    for (int h = 0; h < G; ++h) m[h] = (mx[h] == kNegInf) ? kNegInf : base[h] * c_log2;
   } else {
     state_to_log2<G>(m, c_log2);
   }
 }
 
+
+// Split-KV partials.  Work assignment: every wavefront owns whole chunks
+// (units) and walks units w, w + W, w + 2W, ... of the flattened
+// (sequence, kv-head, chunk) list, W = waves in the grid.  The host sizes the
+// grid so that every wave gets the same number of units (the pages' advice:
+// a block count that is a multiple of what the cores run at once), which
+// keeps each wave's stream of 16-byte loads long and leaves no ragged last
+// round.  Row slots of a wave are merged with shuffles; there is no LDS
+// combine and no workgroup barrier.
 template <int MODE, typename E, int D, int G>
-__global__ __launch_bounds__(kThreads) void partial_kernel(PartialArgs a) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(FD_WAVES_PER_EU)))
+void partial_kernel(PartialArgs a) {
   using Gm = Geo<E, D>;
   constexpr int VEC = Gm::kVec, LPT = Gm::kLpt, TPL = Gm::kTpl;
   constexpr bool kFixed = MODE == kUnified;
-  __shared__ CombineLds<G, D> s_cmb;
-  __shared__ float s_mx[kWaves][G];
-  __shared__ int s_pid[MODE == kPaged ? kMaxChunkPages : 1];
+  constexpr int kPid = MODE == kPaged ? kMaxChunkPages : 1;
+  __shared__ int s_pid[MODE == kPaged ? kWaves : 1][kPid];
 
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & (kWave - 1);
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & (kWave - 1);
   const int col = lane % LPT;
-  const int c = blockIdx.x % a.nc;
-  const int bk = blockIdx.x / a.nc;
-  const int kvh = bk % a.Hkv, b = bk / a.Hkv;
+  const int n_units = a.B * a.Hkv * a.nc;
+  const int stride = (int)gridDim.x * kWaves;
 
-  int L = a.L;
-  if constexpr (MODE == kPaged) L = min(max(a.seq_lens[b], 0), a.max_seq_len);
-  const int c0 = c * a.chunk;
-  if (c0 >= L) return;  // whole workgroup: chunk past this sequence's end
-  const int c1 = min(c0 + a.chunk, L);
+  for (int u = (int)blockIdx.x * kWaves + wave; u < n_units; u += stride) {
+    const int c = u % a.nc;
+    const int bk = u / a.nc;
+    const int kvh = bk % a.Hkv, b = bk / a.Hkv;
+    int L = a.L;
+    if constexpr (MODE == kPaged) L = min(max(a.seq_lens[b], 0), a.max_seq_len);
+    const int c0 = c * a.chunk;
+    if (c0 >= L) continue;  // whole wave: chunk past this sequence's end
+    const int c1 = min(c0 + a.chunk, L);
 
-  RowMap rm{nullptr, c0, a.page_shift, a.Hkv, kvh};
-  const char* kb;
-  const char* vb;
-  if constexpr (MODE == kPaged) {
-    const int first = c0 >> a.page_shift;
-    const int npg = (c1 - c0 + (1 << a.page_shift) - 1) >> a.page_shift;
-    const int32_t* bt = a.block_table + (size_t)b * a.max_pages + first;
-    for (int i = tid; i < npg; i += kThreads) s_pid[i] = min(max(bt[i], 0), a.num_pages - 1);
-    __syncthreads();
-    rm.pid = s_pid;
-    kb = reinterpret_cast<const char*>(a.k);
-    vb = reinterpret_cast<const char*>(a.v);
-  } else {
-    const size_t base = ((size_t)b * a.Hkv + kvh) * (size_t)a.L * Gm::kRow;
-    kb = reinterpret_cast<const char*>(a.k) + base;
-    vb = reinterpret_cast<const char*>(a.v) + base;
-  }
-
-  // This wave's rows: a quarter of the chunk, rounded up to whole loads.
-  const int n = c1 - c0;
-  const int per = (((n + kWaves - 1) / kWaves) + TPL - 1) / TPL * TPL;
-  const int t_beg = c0 + wave * per;
-  const int t_end = min(t_beg + per, c1);
-
-  u32x4 qv[G];
-  {
-    const E* qp = reinterpret_cast<const E*>(a.q) +
-                  ((size_t)b * a.Hq + (size_t)kvh * G) * D + col * VEC;
-#pragma unroll
-    for (int h = 0; h < G; ++h) qv[h] = ld16(qp + (size_t)h * D);
-  }
-
-  float acc[G][VEC], m[G], l[G], mx[G];
-  scan_rows<kFixed, E, D, G>(kb, vb, rm, t_beg, t_end, qv, a.c_log2, a.base_log2, acc, m, l,
-                             mx);
-
-  if constexpr (kFixed) {
-    // Range check of each head's chunk maximum.  Any head out of range sends
-    // the whole unit through the exact path (its own maximum), which is the
-    // fallback recompute; its flag is reported.
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-      const float w = wave_max(mx[h]);
-      if (lane == 0) s_mx[wave][h] = w;
+    RowMap rm{nullptr, c0, a.page_shift, a.Hkv, kvh};
+    const char* kb;
+    const char* vb;
+    if constexpr (MODE == kPaged) {
+      // Page ids of this chunk into this wave's LDS row (read back by the
+      // same wave only, so no barrier is needed).
+      const int first = c0 >> a.page_shift;
+      const int npg = (c1 - c0 + (1 << a.page_shift) - 1) >> a.page_shift;
+      const int32_t* bt = a.block_table + (size_t)b * a.max_pages + first;
+      for (int i = lane; i < npg; i += kWave) s_pid[wave][i] = min(max(bt[i], 0), a.num_pages - 1);
+      rm.pid = s_pid[wave];
+      kb = reinterpret_cast<const char*>(a.k);
+      vb = reinterpret_cast<const char*>(a.v);
+    } else {
+      const size_t base = ((size_t)b * a.Hkv + kvh) * (size_t)a.L * Gm::kRow;
+      kb = reinterpret_cast<const char*>(a.k) + base;
+      vb = reinterpret_cast<const char*>(a.v) + base;
     }
-    __syncthreads();
-    bool any = false;
-    bool flag[G];
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-      const float mm = fmaxf(fmaxf(s_mx[0][h], s_mx[1][h]), fmaxf(s_mx[2][h], s_mx[3][h]));
-      flag[h] = (mm > a.flag_hi_raw) || (mm < a.flag_lo_raw);
-      any |= flag[h];
-    }
-    if (a.flags != nullptr && tid < G) {
-      bool f = false;
-#pragma unroll
-      for (int h = 0; h < G; ++h) f = (h == tid) ? flag[h] : f;
-      a.flags[((size_t)b * a.Hq + (size_t)kvh * G + tid) * a.nc + c] = f ? 1 : 0;
-    }
-    if (any)
-      scan_rows<false, E, D, G>(kb, vb, rm, t_beg, t_end, qv, a.c_log2, a.base_log2, acc, m,
-                                l, mx);
-  }
 
-  const size_t prow0 = ((size_t)b * a.Hq + (size_t)kvh * G) * a.nc + c;
-  combine_store<G, D, VEC, LPT>(s_cmb, acc, m, l, a.o_part, a.ml_part, prow0, (size_t)a.nc);
+    u32x4 qv[G];
+    {
+      const E* qp = reinterpret_cast<const E*>(a.q) +
+                    ((size_t)b * a.Hq + (size_t)kvh * G) * D + col * VEC;
+#pragma unroll
+      for (int h = 0; h < G; ++h) qv[h] = ld16(qp + (size_t)h * D);
+    }
+
+    float acc[G][VEC], m[G], l[G], mx[G];
+    scan_rows<kFixed, E, D, G>(kb, vb, rm, c0, c1, batch_rows<G>() * TPL, qv, a.c_log2, a, acc,
+                               m, l, mx);
+
+    if constexpr (kFixed) {
+      // Range flags of each head's chunk maximum (the slots that left the
+      // range already finished the chunk on the exact path).
+      if (a.flags != nullptr) {
+        bool flag[G];
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+          const float mm = wave_max(mx[h]);
+          flag[h] = (mm > a.flag_hi_raw) || (mm < a.flag_lo_raw);
+        }
+        if (lane < G) {
+          bool f = false;
+#pragma unroll
+          for (int h = 0; h < G; ++h) f = (h == lane) ? flag[h] : f;
+          a.flags[((size_t)b * a.Hq + (size_t)kvh * G + lane) * a.nc + c] = f ? 1 : 0;
+        }
+      }
+    }
+
+    const size_t prow0 = ((size_t)b * a.Hq + (size_t)kvh * G) * a.nc + c;
+    wave_combine_store<G, D, VEC, LPT>(acc, m, l, a.o_part, a.ml_part, prow0, (size_t)a.nc);
+  }
 }
 
 // Exact merge of a row's chunk partials ("Flash Decoding" explainer,
 // section 2, steps 2-4, with unnormalised O_i):
 //   M = max_i m_i,  w_i = 2^(m_i - M),
 //   out = sum_i w_i O_i / sum_i w_i l_i,  lse = (M + log2 sum_i w_i l_i) ln 2.
-// One workgroup per (sequence, query head); wave w takes chunks w, w+4, ...
-// and every lane D/64 dims.  The summation order is fixed, so runs are
-// bitwise reproducible.  Rows whose chunks all carry the same m (the
-// fixed-maximum path without fallback) get weights of exactly 1: a plain sum.
+// One workgroup per (sequence, query head).  The weights of up to 256 chunks
+// at a time go to LDS; thread (chunk lane cl, column group cg) then sums
+// chunks cl, cl + CL, ... of 4 columns with independent 16-byte loads, and
+// the chunk lanes are reduced through LDS.  The order of every sum is fixed,
+// so runs are bitwise reproducible.  Rows whose chunks all carry the same m
+// (the fixed-maximum path without fallback) get weights of exactly 1.
+constexpr int kMergeWaves = 4;
+constexpr int kMergeThreads = kMergeWaves * kWave;
+
 template <int D>
-__global__ __launch_bounds__(kThreads) void merge_kernel(MergeArgs a) {
-  constexpr int VPT = D / kWave;
-  __shared__ float s_m[kWaves];
-  __shared__ float s_l[kWaves];
-  __shared__ float s_o[kWaves][D];
+__global__ __launch_bounds__(kMergeThreads) void merge_kernel(MergeArgs a) {
+  constexpr int CG = D / 4;             // 16-byte column groups of a row
+  constexpr int CL = kMergeThreads / CG;     // chunk lanes
+  __shared__ float s_red[kMergeWaves];
+  __shared__ float s_w[kMergeThreads];
+  __shared__ f32x4 s_o[CL][CG];
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & (kWave - 1);
+  const int cl = tid / CG, cg = tid % CG;
   const size_t row = blockIdx.x;
   int n = a.nc;
   if (a.seq_lens != nullptr) {
@@ -235,48 +320,107 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(MergeArgs a) {
     return;
   }
   const float* ml = a.ml_part + row * a.nc * 2;
-  const float* op = a.o_part + row * a.nc * D;
+  const f32x4* op = reinterpret_cast<const f32x4*>(a.o_part + row * a.nc * D);
 
   float mx = kNegInf;
-  for (int c = tid; c < n; c += kThreads) mx = fmaxf(mx, ml[2 * c]);
+  for (int c = tid; c < n; c += kMergeThreads) mx = fmaxf(mx, ml[2 * c]);
   mx = wave_max(mx);
-  if (lane == 0) s_m[w] = mx;
+  if (lane == 0) s_red[w] = mx;
   __syncthreads();
-  const float M = fmaxf(fmaxf(s_m[0], s_m[1]), fmaxf(s_m[2], s_m[3]));
+  const float M = fmaxf(fmaxf(s_red[0], s_red[1]), fmaxf(s_red[2], s_red[3]));
 
-  float o[VPT];
-#pragma unroll
-  for (int v = 0; v < VPT; ++v) o[v] = 0.f;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   float ls = 0.f;
-  for (int c = w; c < n; c += kWaves) {
-    const float wt = exp2_diff(ml[2 * c], M);
-    ls = fmaf(wt, ml[2 * c + 1], ls);
-#pragma unroll
-    for (int v = 0; v < VPT; ++v) o[v] = fmaf(wt, op[(size_t)c * D + lane * VPT + v], o[v]);
+  for (int c0 = 0; c0 < n; c0 += kMergeThreads) {
+    const int c = c0 + tid;
+    float wt = 0.f;
+    if (c < n) {
+      wt = exp2_diff(ml[2 * c], M);
+      ls = fmaf(wt, ml[2 * c + 1], ls);
+    }
+    __syncthreads();   // previous tile's s_w reads are done
+    s_w[tid] = wt;
+    __syncthreads();
+    const int nt = min(kMergeThreads, n - c0);
+    for (int k = cl; k < nt; k += CL) {
+      const f32x4 o = op[(size_t)(c0 + k) * CG + cg];
+      const float x = s_w[k];
+      acc.x = fmaf(x, o.x, acc.x);
+      acc.y = fmaf(x, o.y, acc.y);
+      acc.z = fmaf(x, o.z, acc.z);
+      acc.w = fmaf(x, o.w, acc.w);
+    }
   }
-#pragma unroll
-  for (int v = 0; v < VPT; ++v) s_o[w][lane * VPT + v] = o[v];
-  if (lane == 0) s_l[w] = ls;
+  s_o[cl][cg] = acc;
+  ls = wave_sum(ls);
   __syncthreads();
-  if (tid < D) {
-    const float den = (s_l[0] + s_l[1]) + (s_l[2] + s_l[3]);
-    const float num = (s_o[0][tid] + s_o[1][tid]) + (s_o[2][tid] + s_o[3][tid]);
-    a.out[row * D + tid] = num / den;
+  if (lane == 0) s_red[w] = ls;
+  __syncthreads();
+  if (tid < CG) {
+    f32x4 t = s_o[0][tid];
+#pragma unroll
+    for (int k = 1; k < CL; ++k) {
+      const f32x4 u = s_o[k][tid];
+      t.x += u.x; t.y += u.y; t.z += u.z; t.w += u.w;
+    }
+    const float den = (s_red[0] + s_red[1]) + (s_red[2] + s_red[3]);
+    reinterpret_cast<f32x4*>(a.out + row * D)[tid] =
+        f32x4{t.x / den, t.y / den, t.z / den, t.w / den};
     if (tid == 0 && a.lse != nullptr) a.lse[row] = (M + log2_hw(den)) * kLn2;
   }
 }
 
+// Compute units of the current device (cached per device).
+static int cu_count() {
+  static std::atomic<int> cached[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+  int n = cached[dev].load(std::memory_order_relaxed);
+  if (n <= 0) {
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        n <= 0)
+      n = 256;
+    cached[dev].store(n, std::memory_order_relaxed);
+  }
+  return n;
+}
+
+// Workgroups of this kernel that fit on one compute unit.
+template <class K>
+static int blocks_per_cu(K kernel) {
+  int n = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kernel, kThreads, 0) != hipSuccess ||
+      n <= 0)
+    n = 1;
+  return n;
+}
+
+// Grid for `units` wave-sized units: the fewest equal rounds the resident
+// waves allow, and just enough workgroups for them.
+static unsigned unit_grid(int per_cu, size_t units) {
+  const size_t slots = (size_t)cu_count() * per_cu * kWaves;
+  const size_t rounds = (units + slots - 1) / slots;
+  return (unsigned)((units + kWaves * rounds - 1) / (kWaves * rounds));
+}
+
+template <int MODE, typename E, int D, int G>
+static hipError_t launch_p4(const PartialArgs& a, hipStream_t s) {
+  auto kernel = partial_kernel<MODE, E, D, G>;
+  static const int per_cu = blocks_per_cu(kernel);   // one per instantiation
+  const size_t units = (size_t)a.B * a.Hkv * a.nc;
+  hipLaunchKernelGGL(kernel, dim3(unit_grid(per_cu, units)), dim3(kThreads), 0, s, a);
+  return hipGetLastError();
+}
+
 template <int MODE, typename E, int D>
 static hipError_t launch_p3(int G, const PartialArgs& a, hipStream_t s) {
-  const dim3 grid((unsigned)((size_t)a.B * a.Hkv * a.nc)), block(kThreads);
   switch (G) {
-    case 1: hipLaunchKernelGGL((partial_kernel<MODE, E, D, 1>), grid, block, 0, s, a); break;
-    case 2: hipLaunchKernelGGL((partial_kernel<MODE, E, D, 2>), grid, block, 0, s, a); break;
-    case 4: hipLaunchKernelGGL((partial_kernel<MODE, E, D, 4>), grid, block, 0, s, a); break;
-    case 8: hipLaunchKernelGGL((partial_kernel<MODE, E, D, 8>), grid, block, 0, s, a); break;
-    default: return hipErrorInvalidValue;
+    case 1: return launch_p4<MODE, E, D, 1>(a, s);
+    case 2: return launch_p4<MODE, E, D, 2>(a, s);
+    case 4: return launch_p4<MODE, E, D, 4>(a, s);
+    case 8: return launch_p4<MODE, E, D, 8>(a, s);
   }
-  return hipGetLastError();
+  return hipErrorInvalidValue;
 }
 
 template <int MODE>
@@ -302,7 +446,7 @@ hipError_t launch_partial(int mode, int is_bf16, int D, int G, const PartialArgs
 }
 
 hipError_t launch_merge(int D, int B, const MergeArgs& a, hipStream_t s) {
-  const dim3 grid((unsigned)((size_t)B * a.Hq)), block(kThreads);
+  const dim3 grid((unsigned)((size_t)B * a.Hq)), block(kMergeThreads);
   if (D == 64) hipLaunchKernelGGL((merge_kernel<64>), grid, block, 0, s, a);
   else if (D == 128) hipLaunchKernelGGL((merge_kernel<128>), grid, block, 0, s, a);
   else return hipErrorInvalidValue;

@@ -69,6 +69,7 @@ template <int D, int G>
 __global__ __launch_bounds__(kThreads) void ffd_kernel(FfdArgs a) {
   using Gm = Geo<uint16_t, D>;
   constexpr int VEC = Gm::kVec, LPT = Gm::kLpt, TPL = Gm::kTpl;
+  constexpr int kNb = 8;             // rows per slot per batch in the refine
   constexpr int NG = D / 32;         // quantisation groups per position
   constexpr int TPS = kWave / NG;    // positions per wave step in the scan
   constexpr int CW = D / 16;         // code words per position
@@ -311,7 +312,7 @@ __global__ __launch_bounds__(kThreads) void ffd_kernel(FfdArgs a) {
         s[i][h] = (valid && ((mk >> h) & 1)) ? sc : kNegInf;
       }
     }
-    online_update<uint16_t, G, VEC>(s, vr, a.c_log2, acc, m, l);
+    online_update<uint16_t, G, VEC, kNb>(s, vr, a.c_log2, acc, m, l);
   }
   state_to_log2<G>(m, a.c_log2);
 

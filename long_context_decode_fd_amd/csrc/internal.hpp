@@ -24,7 +24,7 @@ struct PartialArgs {
   int B, Hq, Hkv, L, chunk, nc;
   int page_shift, max_pages, num_pages, max_seq_len;
   float c_log2;
-  float base_log2;           // unified: phi * log2(e)
+  float phi_raw;             // unified: phi / scale
   float flag_hi_raw;         // unified: (phi + margin_hi) / scale
   float flag_lo_raw;         // unified: (phi - margin_lo) / scale
 };

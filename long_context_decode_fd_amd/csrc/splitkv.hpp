@@ -16,9 +16,19 @@
 
 namespace fdk {
 
-constexpr int kWaves = 4;
+#ifndef FD_WAVES
+#define FD_WAVES 4
+#endif
+constexpr int kWaves = FD_WAVES;      // wavefronts per split-KV unit
 constexpr int kThreads = kWaves * kWave;
-constexpr int kNb = 8;  // rows per slot per batch (loads per tensor per batch)
+// Rows per slot per batch (loads per tensor per batch) of the split-KV
+// kernels: deep batches keep many 16-byte loads in flight per wave, but the
+// K, V and score registers of a batch grow with it and with G.
+#ifndef FD_NB
+#define FD_NB 16
+#endif
+template <int G>
+constexpr int batch_rows() { return G >= 8 ? (FD_NB > 8 ? 8 : FD_NB) : FD_NB; }
 
 template <typename E, int D>
 struct Geo {
@@ -33,11 +43,12 @@ struct Geo {
 template <typename E>
 __device__ __forceinline__ float slice_dot(const u32x4& q, const u32x4& k) {
   if constexpr (std::is_same<E, uint16_t>::value) {
+    // one accumulation chain: v_dot2c accumulates into its destination, so
+    // every extra chain costs a zero-initialising move
     float a = dot2_bf16(q.x, k.x, 0.f);
-    float b = dot2_bf16(q.y, k.y, 0.f);
+    a = dot2_bf16(q.y, k.y, a);
     a = dot2_bf16(q.z, k.z, a);
-    b = dot2_bf16(q.w, k.w, b);
-    return a + b;
+    return dot2_bf16(q.w, k.w, a);
   } else {
     float a = __uint_as_float(q.x) * __uint_as_float(k.x);
     float b = __uint_as_float(q.y) * __uint_as_float(k.y);
@@ -73,13 +84,13 @@ __device__ __forceinline__ void state_reset(float (&acc)[G][VEC], float (&m)[G],
   }
 }
 
-// Online-softmax update of a row slot with a batch of kNb rows.
+// Online-softmax update of a row slot with a batch of NB rows.
 // s[i][h]: raw dot products q_h . k_i (-inf for rows that do not count);
 // m[h]: running maximum in the same raw units.  The accumulator is rescaled
 // only when some slot of the wave saw a larger maximum.
-template <typename E, int G, int VEC>
-__device__ __forceinline__ void online_update(const float (&s)[kNb][G],
-                                              const u32x4 (&vr)[kNb], float c_log2,
+template <typename E, int G, int VEC, int NB>
+__device__ __forceinline__ void online_update(const float (&s)[NB][G],
+                                              const u32x4 (&vr)[NB], float c_log2,
                                               float (&acc)[G][VEC], float (&m)[G],
                                               float (&l)[G]) {
   float mb[G];
@@ -88,7 +99,7 @@ __device__ __forceinline__ void online_update(const float (&s)[kNb][G],
   for (int h = 0; h < G; ++h) {
     mb[h] = m[h];
 #pragma unroll
-    for (int i = 0; i < kNb; ++i) mb[h] = fmaxf(mb[h], s[i][h]);
+    for (int i = 0; i < NB; ++i) mb[h] = fmaxf(mb[h], s[i][h]);
     grow |= mb[h] > m[h];
   }
   if (__any(grow)) {
@@ -105,7 +116,7 @@ __device__ __forceinline__ void online_update(const float (&s)[kNb][G],
 #pragma unroll
   for (int h = 0; h < G; ++h) bias[h] = (m[h] == kNegInf) ? 0.f : m[h] * c_log2;
 #pragma unroll
-  for (int i = 0; i < kNb; ++i) {
+  for (int i = 0; i < NB; ++i) {
     float vf[VEC];
     slice_vals<E>(vr[i], vf);
 #pragma unroll
@@ -123,6 +134,51 @@ template <int G>
 __device__ __forceinline__ void state_to_log2(float (&m)[G], float c_log2) {
 #pragma unroll
   for (int h = 0; h < G; ++h) m[h] = (m[h] == kNegInf) ? kNegInf : m[h] * c_log2;
+}
+
+// Merge the row slots of one wave (shuffles only) and write the wave's
+// partial for each of its G query heads: O (unnormalised, relative to m),
+// m (log2 units) and l.  Lanes col < LPT hold the merged slot afterwards.
+template <int G, int D, int VEC, int LPT>
+__device__ __forceinline__ void wave_combine_store(float (&acc)[G][VEC], float (&m)[G],
+                                                   float (&l)[G], float* o_part,
+                                                   float* ml_part, size_t prow0,
+                                                   size_t hstride) {
+  const int lane = threadIdx.x & (kWave - 1);
+#pragma unroll
+  for (int off = LPT; off < kWave; off <<= 1) {
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      const float mo = __shfl_xor(m[h], off);
+      const float lo = __shfl_xor(l[h], off);
+      const float M = fmaxf(m[h], mo);
+      const float wa = exp2_diff(m[h], M), wb = exp2_diff(mo, M);
+      l[h] = l[h] * wa + lo * wb;
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) {
+        const float ao = __shfl_xor(acc[h][e], off);
+        acc[h][e] = acc[h][e] * wa + ao * wb;
+      }
+      m[h] = M;
+    }
+  }
+  if (lane < LPT) {
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      float* dst = o_part + (prow0 + (size_t)h * hstride) * D + lane * VEC;
+#pragma unroll
+      for (int e = 0; e < VEC; e += 4)
+        *reinterpret_cast<f32x4*>(dst + e) =
+            f32x4{acc[h][e], acc[h][e + 1], acc[h][e + 2], acc[h][e + 3]};
+    }
+  }
+  if (lane == 0) {
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      const size_t prow = prow0 + (size_t)h * hstride;
+      *reinterpret_cast<f32x2*>(ml_part + prow * 2) = f32x2{m[h], l[h]};
+    }
+  }
 }
 
 // LDS scratch of the unit combine.
