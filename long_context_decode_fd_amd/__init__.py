@@ -7,6 +7,7 @@ stream); every step of the computation runs in the HIP kernels of
 
 Entry points (names follow the C ABI):
   decode_attn            dense contiguous cache
+  decode_attn_partials, merge_partials   its two stages
   decode_attn_paged      paged cache with a block table
   decode_attn_unified_max  fixed maximum with exact fallback
   ffd_pack               2-bit + 8-bit residual key format
@@ -22,8 +23,9 @@ import torch
 from . import _abi
 from ._abi import FD_BF16, FD_F32, FdError  # noqa: F401
 
-__all__ = ["decode_attn", "decode_attn_partials", "merge_partials", "decode_attn_paged", "decode_attn_unified_max", "ffd_pack",
-           "ffd_sparse_decode", "workspace_bytes", "FdError", "lib"]
+__all__ = ["decode_attn", "decode_attn_partials", "merge_partials", "partial_views",
+           "decode_attn_paged", "decode_attn_unified_max", "ffd_pack", "ffd_sparse_decode",
+           "workspace_bytes", "FdError", "lib"]
 
 
 def lib():
