@@ -17,6 +17,7 @@
 //     for fp32) and a DPP butterfly sums the slices of a row.
 //   * P stays fp32; O accumulates in fp32 (see splitkv.hpp for the row-slot
 //     softmax state and the end-of-unit combine).
+#include <algorithm>
 #include <atomic>
 
 #include "internal.hpp"
@@ -107,7 +108,7 @@ __device__ __forceinline__ void fixed_update(const float (&s)[NB][G], const u32x
 // (FIXED = false) or its reference -- phi, or its own maximum after a switch
 // (FIXED = true, where mx[h] also receives the largest raw dot product for
 // the range flags).  A slot that saw no row returns m = -inf, l = 0.
-template <bool FIXED, typename E, int D, int G>
+template <bool FIXED, typename E, int D, int G, int NB>
 __device__ __forceinline__ void scan_rows(const char* __restrict__ kb,
                                           const char* __restrict__ vb, const RowMap& rm,
                                           int t_beg, int t_end, int t_step,
@@ -117,7 +118,6 @@ __device__ __forceinline__ void scan_rows(const char* __restrict__ kb,
                                           float (&l)[G], float (&mx)[G]) {
   using Gm = Geo<E, D>;
   constexpr int LPT = Gm::kLpt, TPL = Gm::kTpl, ROW = Gm::kRow;
-  constexpr int NB = batch_rows<G>();
   const int lane = threadIdx.x & (kWave - 1);
   const int grp = lane / LPT, col = lane % LPT;
   state_reset<G, Gm::kVec>(acc, m, l);
@@ -217,17 +217,47 @@ void partial_kernel(PartialArgs a) {
 
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & (kWave - 1);
   const int col = lane % LPT;
-  const int n_units = a.B * a.Hkv * a.nc;
   const int stride = (int)gridDim.x * kWaves;
 
+  // Units: contiguous caches have B*Hkv*nc equal units.  Paged caches have
+  // ragged lengths, so only the real units -- Hkv * ceil(L_b / chunk) for
+  // sequence b -- are numbered (sequence-major), and every wave walks its
+  // share of them; `seq_first`/`seq_units` track the sequence of the current
+  // unit as the wave's unit index grows.
+  int n_units = a.B * a.Hkv * a.nc;
+  int seq_b = 0, seq_first = 0, seq_units = 0;
+  auto seq_len = [&](int bb) { return min(max(a.seq_lens[bb], 0), a.max_seq_len); };
+  if constexpr (MODE == kPaged) {
+    int tot = 0;
+    for (int bb = lane; bb < a.B; bb += kWave) tot += (seq_len(bb) + a.chunk - 1) / a.chunk;
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) tot += __shfl_xor(tot, o);
+    n_units = tot * a.Hkv;
+    seq_units = a.Hkv * ((seq_len(0) + a.chunk - 1) / a.chunk);
+  }
+
   for (int u = (int)blockIdx.x * kWaves + wave; u < n_units; u += stride) {
-    const int c = u % a.nc;
-    const int bk = u / a.nc;
-    const int kvh = bk % a.Hkv, b = bk / a.Hkv;
-    int L = a.L;
-    if constexpr (MODE == kPaged) L = min(max(a.seq_lens[b], 0), a.max_seq_len);
+    int b, kvh, c, L;
+    if constexpr (MODE == kPaged) {
+      while (u >= seq_first + seq_units) {      // wave-uniform
+        seq_first += seq_units;
+        ++seq_b;
+        seq_units = a.Hkv * ((seq_len(seq_b) + a.chunk - 1) / a.chunk);
+      }
+      b = seq_b;
+      const int r = u - seq_first;
+      kvh = r % a.Hkv;
+      c = r / a.Hkv;
+      L = seq_len(b);
+    } else {
+      c = u % a.nc;
+      const int bk = u / a.nc;
+      kvh = bk % a.Hkv;
+      b = bk / a.Hkv;
+      L = a.L;
+    }
     const int c0 = c * a.chunk;
-    if (c0 >= L) continue;  // whole wave: chunk past this sequence's end
+    if (c0 >= L) continue;  // not reached: every numbered unit is real
     const int c1 = min(c0 + a.chunk, L);
 
     RowMap rm{nullptr, c0, a.page_shift, a.Hkv, kvh};
@@ -258,8 +288,10 @@ void partial_kernel(PartialArgs a) {
     }
 
     float acc[G][VEC], m[G], l[G], mx[G];
-    scan_rows<kFixed, E, D, G>(kb, vb, rm, c0, c1, batch_rows<G>() * TPL, qv, a.c_log2, a, acc,
-                               m, l, mx);
+    constexpr int kNbMode =
+        batch_rows<G, MODE == kUnified ? FD_NB_FIXED : (MODE == kPaged ? FD_NB_PAGED : FD_NB)>();
+    scan_rows<kFixed, E, D, G, kNbMode>(kb, vb, rm, c0, c1, kNbMode * TPL, qv, a.c_log2, a, acc,
+                                        m, l, mx);
 
     if constexpr (kFixed) {
       // Range flags of each head's chunk maximum (the slots that left the
@@ -408,7 +440,12 @@ static hipError_t launch_p4(const PartialArgs& a, hipStream_t s) {
   auto kernel = partial_kernel<MODE, E, D, G>;
   static const int per_cu = blocks_per_cu(kernel);   // one per instantiation
   const size_t units = (size_t)a.B * a.Hkv * a.nc;
-  hipLaunchKernelGGL(kernel, dim3(unit_grid(per_cu, units)), dim3(kThreads), 0, s, a);
+  // Paged: the number of real units is known only on the device, so every
+  // resident wave takes part (at most `units` waves).
+  const unsigned grid = MODE == kPaged
+      ? (unsigned)std::min<size_t>((size_t)cu_count() * per_cu, (units + kWaves - 1) / kWaves)
+      : unit_grid(per_cu, units);
+  hipLaunchKernelGGL(kernel, dim3(grid), dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }
 

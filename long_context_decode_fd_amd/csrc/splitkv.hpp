@@ -27,8 +27,14 @@ constexpr int kThreads = kWaves * kWave;
 #ifndef FD_NB
 #define FD_NB 16
 #endif
-template <int G>
-constexpr int batch_rows() { return G >= 8 ? (FD_NB > 8 ? 8 : FD_NB) : FD_NB; }
+#ifndef FD_NB_FIXED
+#define FD_NB_FIXED FD_NB
+#endif
+#ifndef FD_NB_PAGED
+#define FD_NB_PAGED 8      // page-id lookups per row: shallower batches measured faster
+#endif
+template <int G, int NBMAX = FD_NB>
+constexpr int batch_rows() { return G >= 8 ? (NBMAX > 8 ? 8 : NBMAX) : NBMAX; }
 
 template <typename E, int D>
 struct Geo {

@@ -103,3 +103,39 @@ def test_config2_full_size_sampled():
         assert max_err(f64(out[b, h]), r) <= 2e-3
         assert abs(float(lse[b, h]) - lr) <= 2e-3
     assert torch.isfinite(out).all()
+
+
+def test_partials_then_merge_equals_full_call():
+    c = W.dense_case(2, 16, 4, 3000, 128, "bf16", 256, seed=41, device=DEV)
+    out, lse = fd.decode_attn(c.q, c.k, c.v, chunk=256)
+    ws, nc = fd.decode_attn_partials(c.q, c.k, c.v, chunk=256)
+    o_part, ml_part = fd.partial_views(ws, 2, 16, nc, 128)
+    out2, lse2 = fd.merge_partials(o_part, ml_part)
+    assert torch.equal(out, out2) and torch.equal(lse, lse2)
+
+
+def test_merge_independent_of_chunk_order():
+    c = W.dense_case(1, 8, 2, 4000, 64, "f32", 128, seed=42, device=DEV)
+    ws, nc = fd.decode_attn_partials(c.q, c.k, c.v, chunk=128)
+    o_part, ml_part = fd.partial_views(ws, 1, 8, nc, 64)
+    ref, lref = fd.merge_partials(o_part.clone(), ml_part.clone())
+    perm = torch.randperm(nc, generator=torch.Generator().manual_seed(3)).to(DEV)
+    out, lse = fd.merge_partials(o_part[:, :, perm].contiguous(), ml_part[:, :, perm].contiguous())
+    assert max_err(f64(out), f64(ref)) < 1e-6 and max_err(f64(lse), f64(lref)) < 1e-6
+
+
+def test_sequence_split_merged_from_two_halves():
+    # Two devices' worth of a sequence-parallel split, on one GPU: partials of
+    # each half of the cache, gathered along the chunk axis, one merge.
+    c = W.dense_case(2, 32, 8, 4096, 128, "bf16", 512, seed=43, device=DEV)
+    parts = []
+    for lo, hi in ((0, 2048), (2048, 4096)):
+        k = c.k[:, :, lo:hi].contiguous()
+        v = c.v[:, :, lo:hi].contiguous()
+        ws, nc = fd.decode_attn_partials(c.q, k, v, chunk=512)
+        parts.append([t.clone() for t in fd.partial_views(ws, 2, 32, nc, 128)])
+    o = torch.cat([p[0] for p in parts], dim=2).contiguous()
+    ml = torch.cat([p[1] for p in parts], dim=2).contiguous()
+    out, lse = fd.merge_partials(o, ml)
+    ref, lref = ofd.dense_attention(f64(c.q), f64(c.k), f64(c.v), c.scale)
+    assert max_err(f64(out), ref) <= 2e-3 and max_err(f64(lse), lref) <= 2e-3
