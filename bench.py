@@ -47,7 +47,7 @@ def parse_args():
                                 formatter_class=argparse.RawDescriptionHelpFormatter)
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=50)
-    p.add_argument("--warmup", type=int, default=30)
+    p.add_argument("--warmup", type=int, default=200)
     p.add_argument("--copies", type=int, default=3, help="rotated K/V copies")
     p.add_argument("--no-variants", action="store_true")
     p.add_argument("--no-cpu-baseline", action="store_true")

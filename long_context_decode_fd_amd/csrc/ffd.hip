@@ -28,6 +28,25 @@ namespace fdk {
 
 constexpr int kFfdMaxChunk = 1024;
 
+#ifndef FD_FFD_NT
+#define FD_FFD_NT 1
+#endif
+#ifndef FD_FFD_SCAN_STEPS
+#define FD_FFD_SCAN_STEPS 4
+#endif
+#ifndef FD_FFD_BATCHED_SUM
+#define FD_FFD_BATCHED_SUM 0
+#endif
+
+template <class T>
+__device__ __forceinline__ T ffd_load(const T* p) {
+#if FD_FFD_NT
+  return __builtin_nontemporal_load(p);
+#else
+  return *p;
+#endif
+}
+
 __device__ __forceinline__ float half_to_float(uint32_t bits16) {
   return (float)__builtin_bit_cast(_Float16, (uint16_t)bits16);
 }
@@ -198,7 +217,7 @@ __global__ __launch_bounds__(kThreads) void ffd_kernel(FfdArgs a) {
                  (bf16_lo(qs[h][j].w) + bf16_hi(qs[h][j].w));
       }
     }
-    constexpr int kSteps = 4;
+    constexpr int kSteps = FD_FFD_SCAN_STEPS;
     for (int r0 = wave * TPS * kSteps; r0 < n; r0 += kWaves * TPS * kSteps) {
       u32x2 cw[kSteps];
       uint32_t zz[kSteps];
@@ -206,8 +225,8 @@ __global__ __launch_bounds__(kThreads) void ffd_kernel(FfdArgs a) {
       for (int u = 0; u < kSteps; ++u) {
         const int jr = min(r0 + u * TPS + tk, n - 1);
         const size_t row = rbase + c0 + jr;
-        cw[u] = *reinterpret_cast<const u32x2*>(codes + row * CW + 2 * gi);
-        zz[u] = *reinterpret_cast<const uint32_t*>(zs + (row * NG + gi) * 2);
+        cw[u] = ffd_load(reinterpret_cast<const u32x2*>(codes + row * CW + 2 * gi));
+        zz[u] = ffd_load(reinterpret_cast<const uint32_t*>(zs + (row * NG + gi) * 2));
       }
 #pragma unroll
       for (int u = 0; u < kSteps; ++u) {
@@ -293,13 +312,35 @@ __global__ __launch_bounds__(kThreads) void ffd_kernel(FfdArgs a) {
     for (int i = 0; i < kNb; ++i) {
       jr[i] = s_list[min(t0 + i * TPL + grp, t_end - 1)];
       const size_t row = rbase + c0 + jr[i];
-      rr[i] = *reinterpret_cast<const u32x2*>(res + row * D + col * 8);
+      rr[i] = ffd_load(reinterpret_cast<const u32x2*>(res + row * D + col * 8));
       rsb[i] = rsa[row * NG + col / 4];
     }
 #pragma unroll
     for (int i = 0; i < kNb; ++i)
-      vr[i] = ld16(vb + (size_t)(c0 + jr[i]) * Gm::kRow + (size_t)col * 16);
+      vr[i] = ffd_load(reinterpret_cast<const u32x4*>(vb + (size_t)(c0 + jr[i]) * Gm::kRow +
+                                                      (size_t)col * 16));
     float s[kNb][G];
+#if FD_FFD_BATCHED_SUM
+    float corr[kNb * G];
+#pragma unroll
+    for (int i = 0; i < kNb; ++i) {
+      float ci[G];
+      residual_dot<G>(rr[i], half_to_float(rsb[i]), qr, ql, ci);
+#pragma unroll
+      for (int h = 0; h < G; ++h) corr[i * G + h] = ci[h];
+    }
+    group_sum_n<LPT>(corr);
+#pragma unroll
+    for (int i = 0; i < kNb; ++i) {
+      const uint32_t mk = s_mask[jr[i]];
+      const bool valid = t0 + i * TPL + grp < t_end;
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        const float sc = s_scan[jr[i]][h] + corr[i * G + h];
+        s[i][h] = (valid && ((mk >> h) & 1)) ? sc : kNegInf;
+      }
+    }
+#else
 #pragma unroll
     for (int i = 0; i < kNb; ++i) {
       float corr[G];
@@ -312,6 +353,7 @@ __global__ __launch_bounds__(kThreads) void ffd_kernel(FfdArgs a) {
         s[i][h] = (valid && ((mk >> h) & 1)) ? sc : kNegInf;
       }
     }
+#endif
     online_update<uint16_t, G, VEC, kNb>(s, vr, a.c_log2, acc, m, l);
   }
   state_to_log2<G>(m, a.c_log2);
