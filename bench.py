@@ -370,6 +370,70 @@ def variant_ffd(torch, fd, W, args, timer):
                 pack_ms_whole_cache=round(pack_ms, 2), **res)
 
 
+def variant_ffd_peaked(torch, fd, W, args, timer):
+    """FFD against dense attention on the same peaked data: sharp queries
+    whose heads of a group attend alike (per-head sparsity at the levels the
+    FFD digest reports).  Dense reads the bf16 keys, FFD the packed ones."""
+    import numpy as np
+    c = W.config_case(6, device="cuda:0")
+    B, Hq, d = c.q.shape
+    Hkv, L = c.v.shape[1], c.v.shape[2]
+    G = Hq // Hkv
+    lib = fd.lib()
+    packs = [fd.ffd_pack(c.k)]
+    packs += [{k: v.clone() for k, v in packs[0].items()} for _ in range(args.copies - 1)]
+    ks = [c.k] + [c.k.clone() for _ in range(args.copies - 1)]
+    vs = [c.v] + [c.v.clone() for _ in range(args.copies - 1)]
+    out = torch.empty((B, Hq, d), dtype=torch.float32, device="cuda:0")
+    lse = torch.empty((B, Hq), dtype=torch.float32, device="cuda:0")
+    wsn = max(fd.workspace_bytes("fd_ffd_sparse_decode", B=B, Hq=Hq, Hkv=Hkv, L=L, d=d,
+                                 chunk=c.chunk),
+              fd.workspace_bytes("fd_decode_attn", B=B, Hq=Hq, Hkv=Hkv, L=L, d=d, chunk=512))
+    ws = torch.empty(wsn, dtype=torch.uint8, device="cuda:0")
+    size = C.c_size_t(wsn)
+    st = C.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+    def mk_d(k, v):
+        a = (fd.FD_BF16, vp(c.q), vp(k), vp(v), vp(out), vp(lse), B, Hq, Hkv, L, d, c.scale,
+             512, vp(ws), C.byref(size), st)
+        return lambda: lib.fd_decode_attn(*a)
+    groups = {"dense": [mk_d(k, v) for k, v in zip(ks, vs)]}
+    info = {}
+    for delta in c.deltas:
+        def mk(p, v, delta=delta):
+            a = (vp(c.q), vp(p["codes"]), vp(p["zs"]), vp(p["res"]), vp(p["rs"]), vp(v),
+                 vp(out), vp(lse), B, Hq, Hkv, L, d, c.scale, float(delta), c.n_sink,
+                 c.n_local, c.chunk, None, None, vp(ws), C.byref(size), st)
+            return lambda: lib.fd_ffd_sparse_decode(*a)
+        key = f"delta_{delta:g}"
+        groups[key] = [mk(p, v) for p, v in zip(packs, vs)]
+        check_rc(lib, groups[key][0]())
+        _, _, mask, _ = fd.ffd_sparse_decode(c.q, packs[0], c.v, delta, c.n_sink, c.n_local,
+                                             chunk=c.chunk, want_mask=True)
+        m = mask.cpu().numpy().view(np.uint32).reshape(B, Hkv, G, -1)
+        per_head = np.unpackbits(m.view(np.uint8), axis=-1).sum(-1)
+        n_union = int(np.unpackbits(np.bitwise_or.reduce(m, axis=2).view(np.uint8),
+                                    axis=-1).sum())
+        n_anchor = min(L, c.n_sink + c.n_local)
+        nbytes = (B * Hkv * L * (d // 4 + d // 32 * 4) + n_union * (d + d // 32 * 2 + 2 * d)
+                  + B * Hkv * n_anchor * (d // 4 + d // 32 * 6 + d)
+                  + B * Hq * d * 2 + B * Hq * (d + 1) * 4)
+        info[key] = dict(bytes=int(nbytes), kept_per_head=round(float(per_head.mean()) / L, 4),
+                         kept_group_union=round(n_union / (B * Hkv * L), 4))
+    check_rc(lib, groups["dense"][0]())
+    t = interleaved(timer, groups, args.steps, args.warmup)
+    dense_bytes = 2 * B * Hkv * L * d * 2 + B * Hq * d * 2 + B * Hq * (d + 1) * 4
+    res = dict(dense_us_per_step=round(t["dense"]["ms"] * 1e3, 2),
+               dense_gbs=round(gbs(dense_bytes, t["dense"]["ms"]), 1))
+    for key, inf in info.items():
+        ms = t[key]["ms"]
+        res[key] = dict(us_per_step=round(ms * 1e3, 2), gbs=round(gbs(inf["bytes"], ms), 1),
+                        pct_of_peak=round(100 * gbs(inf["bytes"], ms) / PEAK_GBS, 1),
+                        speedup_vs_dense=round(t["dense"]["ms"] / ms, 3), **inf)
+    return dict(workload=f"FFD vs dense on peaked queries (scale 5, group-shared 0.95), "
+                         f"B={B}, Hq={Hq}, Hkv={Hkv}, d={d}, L={L}, chunk={c.chunk}", **res)
+
+
 def main():
     args = parse_args()
     if args.gpus != 1:
@@ -419,6 +483,7 @@ def main():
             "paged": variant_paged(torch, fd, W, args, timer),
             "unified_max": variant_unified(torch, fd, W, args, timer),
             "ffd": variant_ffd(torch, fd, W, args, timer),
+            "ffd_peaked": variant_ffd_peaked(torch, fd, W, args, timer),
         }
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(torch, case, args.cpu_seconds)

@@ -269,14 +269,18 @@ int fd_ffd_sparse_decode(const void* q, const uint32_t* codes, const uint16_t* z
   if (int e = check_heads(B, Hq, Hkv, d)) return e;
   if (L <= 0) return fail(FD_ERR_ARG, "L=%d must be positive", L);
   if (int e = check_chunk(chunk)) return e;
-  if (chunk % 32 != 0 || chunk > 1024)
-    return fail(FD_ERR_UNSUPPORTED, "FFD chunk=%d must be a multiple of 32 <= 1024", chunk);
+  {
+    const int cmax = (Hq / Hkv) >= 8 ? 1024 : 2048;
+    if (chunk % 32 != 0 || chunk > cmax)
+      return fail(FD_ERR_UNSUPPORTED, "FFD chunk=%d must be a multiple of 32 <= %d", chunk,
+                  cmax);
+  }
   if (int e = check_scale(scale)) return e;
   if (!(delta >= 0.f)) return fail(FD_ERR_ARG, "delta must be >= 0");
   if (n_sink < 0 || n_local < 0 || n_sink + n_local < 1)
     return fail(FD_ERR_ARG, "need n_sink, n_local >= 0 and n_sink + n_local >= 1");
   const int nc = (L + chunk - 1) / chunk;
-  const size_t need = partial_bytes(B, Hq, nc, d);
+  const size_t need = partial_bytes(B, Hq, nc, d) + 2 * align256((size_t)B * Hq * 4);
   if (int e = workspace_gate(ws, ws_bytes, need)) return e;
   if (ws == nullptr) return ok();
   if (!q || !codes || !zs || !res || !rs || !v || !out)
@@ -287,7 +291,10 @@ int fd_ffd_sparse_decode(const void* q, const uint32_t* codes, const uint16_t* z
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   float *o_part, *ml_part;
   split_ws(ws, B, Hq, nc, d, &o_part, &ml_part);
+  char* tail = reinterpret_cast<char*>(ws) + partial_bytes(B, Hq, nc, d);
   fdk::FfdArgs fa{};
+  fa.anchor_max = reinterpret_cast<float*>(tail);
+  fa.anchor_pos = reinterpret_cast<int32_t*>(tail + align256((size_t)B * Hq * 4));
   fa.q = reinterpret_cast<const uint16_t*>(q);
   fa.codes = codes;
   fa.zs = zs;

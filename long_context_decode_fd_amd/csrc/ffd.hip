@@ -5,9 +5,9 @@
 // the packer that produces the key format (section 5).
 //
 // One workgroup = one unit = (sequence, kv-head, chunk), fused:
-//   0. Anchors.  Every unit scores the anchor positions with the refined key
-//      (2-bit + residual) and takes m^ and j* itself; the computation is the
-//      same in every unit, so all units agree without a separate pass.
+//   0. Anchors.  A small kernel scores the anchor positions of every
+//      (sequence, kv-head) with the refined key (2-bit + residual) once and
+//      leaves m^ and j* per query head in the workspace.
 //   1. Scan.  4 lanes per position (one 32-dim quantisation group each) read
 //      8 B of codes and 4 B of (zero, step).  Codes become exact bf16 values
 //      4 + c (a rotate and an and-or per pair, since bf16 4..7 differ only in
@@ -26,7 +26,10 @@
 
 namespace fdk {
 
-constexpr int kFfdMaxChunk = 1024;
+// Largest chunk whose scan scores fit in LDS: 2048 positions (G <= 4),
+// 1024 for groups of 8.
+template <int G>
+constexpr int ffd_max_chunk() { return G >= 8 ? 1024 : 2048; }
 
 #ifndef FD_FFD_NT
 #define FD_FFD_NT 1
@@ -84,40 +87,29 @@ __device__ __forceinline__ void residual_dot(const u32x2& rr, float rsf, const u
   }
 }
 
+// Pseudo-maximum (FFD digest, section 4): for every (sequence, query head),
+// the largest refined score over the anchor positions -- the first n_sink and
+// the last n_local positions -- and the lowest anchor position attaining it.
+// One workgroup per (sequence, kv-head), 16 lanes per anchor row; stored in
+// raw dot-product units for the scan kernel (and scaled, if requested).
 template <int D, int G>
-__global__ __launch_bounds__(kThreads) void ffd_kernel(FfdArgs a) {
+__global__ __launch_bounds__(kThreads) void ffd_anchor_kernel(FfdArgs a) {
   using Gm = Geo<uint16_t, D>;
   constexpr int VEC = Gm::kVec, LPT = Gm::kLpt, TPL = Gm::kTpl;
-  constexpr int kNb = 8;             // rows per slot per batch in the refine
-  constexpr int NG = D / 32;         // quantisation groups per position
-  constexpr int TPS = kWave / NG;    // positions per wave step in the scan
-  constexpr int CW = D / 16;         // code words per position
-
-  __shared__ float s_scan[kFfdMaxChunk][G];
-  __shared__ uint8_t s_mask[kFfdMaxChunk];
-  __shared__ uint16_t s_list[kFfdMaxChunk];
-  __shared__ int s_cnt[kWaves];
+  constexpr int NG = D / 32;
+  constexpr int CW = D / 16;
   __shared__ float s_best[kWaves][G];
   __shared__ int s_bidx[kWaves][G];
-  __shared__ CombineLds<G, D> s_cmb;
-
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & (kWave - 1);
   const int grp = lane / LPT, col = lane % LPT;
-  const int c = blockIdx.x % a.nc;
-  const int bk = blockIdx.x / a.nc;
-  const int kvh = bk % a.Hkv, b = bk / a.Hkv;
+  const int kvh = blockIdx.x % a.Hkv, b = blockIdx.x / a.Hkv;
   const int L = a.L;
-  const int c0 = c * a.chunk, c1 = min(c0 + a.chunk, L), n = c1 - c0;
-  const size_t bkv = (size_t)b * a.Hkv + kvh;
-  const size_t rbase = bkv * (size_t)L;  // row index of position 0
+  const size_t rbase = ((size_t)b * a.Hkv + kvh) * (size_t)L;
+  const size_t hq0 = (size_t)b * a.Hq + (size_t)kvh * G;
   const uint32_t* codes = a.codes;
   const uint16_t* zs = a.zs;
   const int8_t* res = a.res;
   const uint16_t* rsa = a.rs;
-  const char* vb = reinterpret_cast<const char*>(a.v) + rbase * Gm::kRow;
-  const size_t hq0 = (size_t)b * a.Hq + (size_t)kvh * G;
-
-  // Query slices of the 16-lane (row) layout, and their partial sums.
   u32x4 qr[G];
   float ql[G];
   {
@@ -129,8 +121,6 @@ __global__ __launch_bounds__(kThreads) void ffd_kernel(FfdArgs a) {
               ((bf16_lo(qr[h].z) + bf16_hi(qr[h].z)) + (bf16_lo(qr[h].w) + bf16_hi(qr[h].w)));
     }
   }
-
-  // ---- 0. pseudo-maximum over the anchors (refined scores, raw units) ----
   const int n_sk = min(a.n_sink, L);
   const int loc0 = max(n_sk, L - a.n_local);
   const int na = n_sk + (L - loc0);
@@ -182,8 +172,6 @@ __global__ __launch_bounds__(kThreads) void ffd_kernel(FfdArgs a) {
     for (int h = 0; h < G; ++h) { s_best[wave][h] = best[h]; s_bidx[wave][h] = bidx[h]; }
   }
   __syncthreads();
-  float thr[G];
-  int jst[G];
 #pragma unroll
   for (int h = 0; h < G; ++h) {
     float bb = s_best[0][h];
@@ -194,9 +182,67 @@ __global__ __launch_bounds__(kThreads) void ffd_kernel(FfdArgs a) {
       const int oi = s_bidx[w][h];
       if (ob > bb || (ob == bb && oi < bi)) { bb = ob; bi = oi; }
     }
-    thr[h] = bb - a.delta_raw;
-    jst[h] = bi;
-    if (c == 0 && a.pseudo_max != nullptr && tid == 0) a.pseudo_max[hq0 + h] = bb * a.scale;
+    if (tid == 0) {
+      a.anchor_max[hq0 + h] = bb;
+      a.anchor_pos[hq0 + h] = bi;
+      if (a.pseudo_max != nullptr) a.pseudo_max[hq0 + h] = bb * a.scale;
+    }
+  }
+}
+
+
+template <int D, int G>
+__global__ __launch_bounds__(kThreads) void ffd_kernel(FfdArgs a) {
+  using Gm = Geo<uint16_t, D>;
+  constexpr int VEC = Gm::kVec, LPT = Gm::kLpt, TPL = Gm::kTpl;
+  constexpr int kNb = 8;             // rows per slot per batch in the refine
+  constexpr int NG = D / 32;         // quantisation groups per position
+  constexpr int TPS = kWave / NG;    // positions per wave step in the scan
+  constexpr int CW = D / 16;         // code words per position
+
+  constexpr int kFfdMaxChunk = ffd_max_chunk<G>();
+  __shared__ float s_scan[kFfdMaxChunk][G];
+  __shared__ uint8_t s_mask[kFfdMaxChunk];
+  __shared__ uint16_t s_list[kFfdMaxChunk];
+  __shared__ int s_cnt[kWaves];
+  __shared__ CombineLds<G, D> s_cmb;
+
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & (kWave - 1);
+  const int grp = lane / LPT, col = lane % LPT;
+  const int c = blockIdx.x % a.nc;
+  const int bk = blockIdx.x / a.nc;
+  const int kvh = bk % a.Hkv, b = bk / a.Hkv;
+  const int L = a.L;
+  const int c0 = c * a.chunk, c1 = min(c0 + a.chunk, L), n = c1 - c0;
+  const size_t bkv = (size_t)b * a.Hkv + kvh;
+  const size_t rbase = bkv * (size_t)L;  // row index of position 0
+  const uint32_t* codes = a.codes;
+  const uint16_t* zs = a.zs;
+  const int8_t* res = a.res;
+  const uint16_t* rsa = a.rs;
+  const char* vb = reinterpret_cast<const char*>(a.v) + rbase * Gm::kRow;
+  const size_t hq0 = (size_t)b * a.Hq + (size_t)kvh * G;
+
+  // Query slices of the 16-lane (row) layout, and their partial sums.
+  u32x4 qr[G];
+  float ql[G];
+  {
+    const uint16_t* qp = a.q + hq0 * D + col * VEC;
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      qr[h] = ld16(qp + (size_t)h * D);
+      ql[h] = ((bf16_lo(qr[h].x) + bf16_hi(qr[h].x)) + (bf16_lo(qr[h].y) + bf16_hi(qr[h].y))) +
+              ((bf16_lo(qr[h].z) + bf16_hi(qr[h].z)) + (bf16_lo(qr[h].w) + bf16_hi(qr[h].w)));
+    }
+  }
+
+  // ---- 0. pseudo-maximum and its anchor, computed once per (b, head) ----
+  float thr[G];
+  int jst[G];
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    thr[h] = a.anchor_max[hq0 + h] - a.delta_raw;
+    jst[h] = a.anchor_pos[hq0 + h];
   }
 
   // ---- 1. 2-bit scan of the chunk: scores and candidate masks into LDS ----
@@ -434,10 +480,14 @@ __global__ __launch_bounds__(kThreads) void ffd_pack_kernel(FfdPackArgs a) {
 
 hipError_t launch_ffd(int D, int G, const FfdArgs& a, hipStream_t s) {
   const dim3 grid((unsigned)((size_t)a.B * a.Hkv * a.nc)), block(kThreads);
-#define FD_FFD_CASE(DD, GG)                                                     \
-  if (D == DD && G == GG) {                                                     \
-    hipLaunchKernelGGL((ffd_kernel<DD, GG>), grid, block, 0, s, a);             \
-    return hipGetLastError();                                                   \
+#define FD_FFD_CASE(DD, GG)                                                          \
+  if (D == DD && G == GG) {                                                          \
+    hipLaunchKernelGGL((ffd_anchor_kernel<DD, GG>), dim3((unsigned)(a.B * a.Hkv)), block, 0, \
+                       s, a);                                                        \
+    hipError_t e = hipGetLastError();                                                \
+    if (e != hipSuccess) return e;                                                   \
+    hipLaunchKernelGGL((ffd_kernel<DD, GG>), grid, block, 0, s, a);                  \
+    return hipGetLastError();                                                        \
   }
   FD_FFD_CASE(64, 1) FD_FFD_CASE(64, 2) FD_FFD_CASE(64, 4) FD_FFD_CASE(64, 8)
   FD_FFD_CASE(128, 1) FD_FFD_CASE(128, 2) FD_FFD_CASE(128, 4) FD_FFD_CASE(128, 8)

@@ -63,6 +63,8 @@ struct FfdArgs {
   float* ml_part;
   uint32_t* cand_mask; // [B, Hq, ceil(L/32)] or null
   float* pseudo_max;   // [B, Hq] or null (scaled units)
+  float* anchor_max;   // workspace [B, Hq]: m^ in raw dot units
+  int32_t* anchor_pos; // workspace [B, Hq]: j*
   int B, Hq, Hkv, L, chunk, nc, n_sink, n_local;
   float scale, c_log2, delta_raw;  // delta / scale
 };

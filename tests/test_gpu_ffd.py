@@ -182,3 +182,25 @@ def test_ffd_config5_full_size_sampled():
                 _row_check(q, packed_ref, v64, b, h, G, c.scale, delta, c.n_sink, c.n_local,
                            o, l_, cm, pm)
         assert torch.isfinite(out).all()
+
+
+def test_ffd_peaked_workload_sampled():
+    # Sharp, group-correlated queries: most positions are dropped, so the
+    # compaction and the per-head masks really matter.
+    banner("ffd peaked workload")
+    c = W.config_case(6, device=DEV, L=16384)
+    ph = offd.pack_keys(f64(c.k).astype(np.float32))
+    pk = packed_to_device(ph, DEV)
+    G = 4
+    q, v64 = f64(c.q), f64(c.v)
+    for delta in c.deltas:
+        out, lse, cand, pmax = fd.ffd_sparse_decode(c.q, pk, c.v, delta, c.n_sink, c.n_local,
+                                                    chunk=c.chunk, want_mask=True,
+                                                    want_pseudo_max=True)
+        torch.cuda.synchronize()
+        cm = cand.cpu().numpy().view(np.uint32)
+        kept = np.unpackbits(cm.view(np.uint8), axis=-1).sum() / cm.size / 32
+        assert kept < 0.4, kept
+        for b, h in ((0, 0), (1, 9), (3, 30)):
+            _row_check(q, ph, v64, b, h, G, c.scale, delta, c.n_sink, c.n_local, f64(out),
+                       f64(lse), cm, f64(pmax))

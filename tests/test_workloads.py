@@ -92,3 +92,15 @@ def test_ffd_case_sinks_and_needles():
     rest = s[..., 4:-64]
     frac_high = (rest > 3.5).double().mean().item()
     assert 0.005 < frac_high < 0.03
+
+
+def test_ffd_peaked_queries_share_group_direction():
+    c = W.ffd_case(1, 8, 2, 256, 64, seed=3, q_scale=5.0, q_shared=0.95)
+    q = c.q.float()
+    assert 4.0 < float(q.std()) < 6.0
+    cos = torch.nn.functional.cosine_similarity(q[0, 0], q[0, 1], dim=0)
+    assert float(cos) > 0.8                       # same group: nearly aligned
+    cos2 = torch.nn.functional.cosine_similarity(q[0, 0], q[0, 4], dim=0)
+    assert abs(float(cos2)) < 0.5                 # other group: unrelated
+    base = W.config_case(5, L=256, B=1)
+    assert base.q.float().std() < 1.5

@@ -52,6 +52,12 @@ CONFIGS = {
     5: dict(kind="ffd", B=4, Hq=32, Hkv=8, L=65536, d=128, n_sink=4,
             n_local=64, deltas=(5.0, 7.0), sink_shift=3.0, plant_frac=0.01,
             plant_shift=5.0, chunk=1024, seed=105),
+    # Peaked queries (sharper softmax, heads of a group alike): per-head
+    # sparsity ~83 % at delta 5 and ~73 % at delta 7, the levels the FFD digest
+    # reports; the union over a group of 4 keeps ~29 % / ~41 % of positions.
+    6: dict(kind="ffd", B=4, Hq=32, Hkv=8, L=65536, d=128, n_sink=4,
+            n_local=64, deltas=(5.0, 7.0), sink_shift=3.0, plant_frac=0.01,
+            plant_shift=5.0, chunk=1024, seed=106, q_scale=5.0, q_shared=0.95),
 }
 
 
@@ -268,7 +274,7 @@ def unified_case(B, Hq, Hkv, L, d, chunk=512, plant_frac=0.02, plant_coef=0.5,
 
 def ffd_case(B, Hq, Hkv, L, d, n_sink=4, n_local=64, deltas=(5.0, 7.0),
              sink_shift=3.0, plant_frac=0.01, plant_shift=5.0, chunk=1024,
-             seed=0, device="cpu") -> FfdCase:
+             seed=0, device="cpu", q_scale=1.0, q_shared=0.0) -> FfdCase:
     """Keys with attention-sink and needle structure for the sparse path.
 
     The first n_sink keys of every (sequence, kv-head) get the minimum-norm
@@ -276,11 +282,20 @@ def ffd_case(B, Hq, Hkv, L, d, n_sink=4, n_local=64, deltas=(5.0, 7.0),
     plant_frac*L) keys drawn from positions [n_sink, L - n_local) get one that
     raises it by plant_shift (kept out of the anchor window, so the
     pseudo-maximum taken from the anchors sits below the true maximum).
+
+    Peaked variant: q = q_scale * (rho * u_g + sqrt(1 - rho^2) * e_h) with
+    rho = q_shared, one u_g per kv-head group and one e_h per head (all
+    N(0, 1)): scores spread by q_scale (sharper softmax) and the heads of a
+    group attend to similar positions.  q_scale = 1, q_shared = 0 is plain iid.
     """
     G = Hq // Hkv
     rs = np.random.default_rng(seed)
     g = _gen(seed, device)
-    q = _randn((B, Hq, d), g, device).to(torch.bfloat16)
+    q = _randn((B, Hq, d), g, device)
+    if q_shared != 0.0:
+        u = _randn((B, Hkv, 1, d), g, device).expand(B, Hkv, G, d).reshape(B, Hq, d)
+        q = q_shared * u + math.sqrt(1.0 - q_shared * q_shared) * q
+    q = (q_scale * q).to(torch.bfloat16)
     k = _randn((B, Hkv, L, d), g, device)
     v = _randn((B, Hkv, L, d), g, device).to(torch.bfloat16)
     qd = q.double().cpu().numpy()
