@@ -7,16 +7,15 @@
 // fixed-maximum variant follows the "FlashDecoding" deployment blog,
 // section 1 and its fixed_max_value / fallback_on_overflow settings.
 //
-// One workgroup = one unit = (sequence, kv-head, chunk):
-//   * 4 wavefronts split the chunk into 4 contiguous ranges of rows.
-//   * Each lane reads 16 bytes per row; one wave load covers kTpl rows
-//     (4 rows of a d = 128 bf16 cache, 1 KiB of contiguous HBM).  The K and V
-//     rows of a batch of kNb loads are issued together before any math.
+// Every wavefront owns whole units = (sequence, kv-head, chunk):
+//   * A lane holds two 16-byte pieces of a cache row (one for G = 8), so 8
+//     lanes share a d = 128 bf16 row and one wave load covers 8 half rows.
+//     The K and V loads of a batch overlap the math of the previous one.
 //   * QK^T for the G query heads of the kv-head (GQA packing): each lane dots
-//     its slice with the G query slices (v_dot2c_f32_bf16 for bf16, fp32 FMA
-//     for fp32) and a DPP butterfly sums the slices of a row.
+//     its pieces with the G query pieces (v_dot2c_f32_bf16 for bf16, fp32 FMA
+//     for fp32) and a DPP butterfly sums the pieces of a row.
 //   * P stays fp32; O accumulates in fp32 (see splitkv.hpp for the row-slot
-//     softmax state and the end-of-unit combine).
+//     softmax state and the end-of-unit merge).
 #include <algorithm>
 #include <atomic>
 
@@ -27,12 +26,14 @@ namespace fdk {
 
 constexpr int kMaxChunkPages = 1024;
 
-#ifndef FD_PIPELINE
-#define FD_PIPELINE 0
-#endif
 #ifndef FD_WAVES_PER_EU
 #define FD_WAVES_PER_EU 1
 #endif
+// 16-byte pieces of a cache row per lane (see Geo in splitkv.hpp).
+#ifndef FD_PIECES
+#define FD_PIECES 2
+#endif
+constexpr int kP = FD_PIECES;
 
 // Byte offset (in rows) of cache position t for one kv-head.
 struct RowMap {
@@ -57,8 +58,8 @@ struct RowMap {
 // is read twice, and a value never meets an exponent outside the range.
 // m: running maximum (raw), base: the slot's reference (phi or m, raw),
 // on: the slot has switched.
-template <typename E, int G, int VEC, int NB>
-__device__ __forceinline__ void fixed_update(const float (&s)[NB][G], const u32x4 (&vr)[NB],
+template <typename E, int G, int VEC, int NB, int P>
+__device__ __forceinline__ void fixed_update(const float (&s)[NB][G], const u32x4 (&vr)[NB * P],
                                              float c_log2, float phi_raw, float hi_raw,
                                              float lo_raw, float (&acc)[G][VEC], float (&m)[G],
                                              float (&base)[G], bool (&on)[G], float (&l)[G]) {
@@ -92,7 +93,8 @@ __device__ __forceinline__ void fixed_update(const float (&s)[NB][G], const u32x
 #pragma unroll
   for (int i = 0; i < NB; ++i) {
     float vf[VEC];
-    slice_vals<E>(vr[i], vf);
+#pragma unroll
+    for (int pc = 0; pc < P; ++pc) slice_vals<E>(vr[i * P + pc], vf + pc * (VEC / P));
 #pragma unroll
     for (int h = 0; h < G; ++h) {
       const float p = exp2_hw((s[i][h] - base[h]) * c_log2);
@@ -108,15 +110,15 @@ __device__ __forceinline__ void fixed_update(const float (&s)[NB][G], const u32x
 // (FIXED = false) or its reference -- phi, or its own maximum after a switch
 // (FIXED = true, where mx[h] also receives the largest raw dot product for
 // the range flags).  A slot that saw no row returns m = -inf, l = 0.
-template <bool FIXED, typename E, int D, int G, int NB>
+template <bool FIXED, typename E, int D, int G, int NB, int kP>
 __device__ __forceinline__ void scan_rows(const char* __restrict__ kb,
                                           const char* __restrict__ vb, const RowMap& rm,
-                                          int t_beg, int t_end, int t_step,
-                                          const u32x4 (&qv)[G], float c_log2,
+                                          int t_beg, int t_end,
+                                          const u32x4 (&qv)[G][kP], float c_log2,
                                           const PartialArgs& a,
-                                          float (&acc)[G][Geo<E, D>::kVec], float (&m)[G],
+                                          float (&acc)[G][Geo<E, D, kP>::kVec], float (&m)[G],
                                           float (&l)[G], float (&mx)[G]) {
-  using Gm = Geo<E, D>;
+  using Gm = Geo<E, D, kP>;
   constexpr int LPT = Gm::kLpt, TPL = Gm::kTpl, ROW = Gm::kRow;
   const int lane = threadIdx.x & (kWave - 1);
   const int grp = lane / LPT, col = lane % LPT;
@@ -130,65 +132,65 @@ __device__ __forceinline__ void scan_rows(const char* __restrict__ kb,
     on[h] = false;
   }
 
-  // One batch: NB rows per slot, K and V.
-  auto load = [&](int t0, u32x4 (&kr)[NB], u32x4 (&vr)[NB]) {
-    size_t off[NB];
+  // A batch is NB rows per slot.  The V rows of batch j are requested before
+  // the scores of batch j are computed, and the K rows of batch j + 1 before
+  // the PV update of batch j, so the wave's loads stay in flight while it
+  // computes.
+  constexpr int STEP = NB * TPL;
+  auto offsets = [&](int t0, size_t (&off)[NB]) {
 #pragma unroll
     for (int i = 0; i < NB; ++i) {
       const int t = min(t0 + i * TPL + grp, t_end - 1);
       off[i] = rm.row(t) * ROW + (size_t)col * 16;
     }
-#pragma unroll
-    for (int i = 0; i < NB; ++i) kr[i] = ld16_stream(kb + off[i]);
-#pragma unroll
-    for (int i = 0; i < NB; ++i) vr[i] = ld16_stream(vb + off[i]);
   };
-  auto compute = [&](int t0, const u32x4 (&kr)[NB], const u32x4 (&vr)[NB]) {
-    float s[NB][G];
+  // piece pc of row i: bytes off[i] + pc * ROW / P; register kr[i * P + pc]
+  auto issue = [&](const char* __restrict__ src, const size_t (&off)[NB],
+                   u32x4 (&r)[NB * kP]) {
+#pragma unroll
+    for (int i = 0; i < NB; ++i)
+#pragma unroll
+      for (int pc = 0; pc < kP; ++pc)
+        r[i * kP + pc] = ld16_stream(src + off[i] + (size_t)pc * (ROW / kP));
+  };
+  auto scores = [&](int t0, const u32x4 (&kr)[NB * kP], float (&s)[NB][G]) {
     float flat[NB * G];
 #pragma unroll
     for (int i = 0; i < NB; ++i)
 #pragma unroll
-      for (int h = 0; h < G; ++h) flat[i * G + h] = slice_dot<E>(qv[h], kr[i]);
+      for (int h = 0; h < G; ++h) flat[i * G + h] = pieces_dot<E, kP>(qv[h], kr + i * kP);
     group_sum_n<LPT>(flat);
 #pragma unroll
     for (int i = 0; i < NB; ++i)
 #pragma unroll
       for (int h = 0; h < G; ++h) s[i][h] = flat[i * G + h];
-    if (t0 + NB * TPL > t_end) {
+    if (t0 + STEP > t_end) {
 #pragma unroll
       for (int i = 0; i < NB; ++i)
         if (t0 + i * TPL + grp >= t_end)
 #pragma unroll
           for (int h = 0; h < G; ++h) s[i][h] = kNegInf;
     }
-    if constexpr (FIXED)
-      fixed_update<E, G, Gm::kVec, NB>(s, vr, c_log2, a.phi_raw, a.flag_hi_raw, a.flag_lo_raw,
-                                       acc, mx, base, on, l);
-    else online_update<E, G, Gm::kVec, NB>(s, vr, c_log2, acc, m, l);
   };
-  constexpr int STEP = NB * TPL;
-#if FD_PIPELINE
-  // Two register buffers: the loads of the next batch are in flight while
-  // the current one is computed.
   if (t_beg < t_end) {
-    u32x4 ka[NB], va[NB], kc[NB], vc[NB];
-    load(t_beg, ka, va);
-    for (int t0 = t_beg; t0 < t_end; t0 += 2 * STEP) {
-      if (t0 + STEP < t_end) load(t0 + STEP, kc, vc);
-      compute(t0, ka, va);
-      if (t0 + STEP >= t_end) break;
-      if (t0 + 2 * STEP < t_end) load(t0 + 2 * STEP, ka, va);
-      compute(t0 + STEP, kc, vc);
+    u32x4 kr[NB * kP], vr[NB * kP];
+    size_t off[NB];
+    offsets(t_beg, off);
+    issue(kb, off, kr);
+    for (int t0 = t_beg; t0 < t_end; t0 += STEP) {
+      issue(vb, off, vr);
+      float s[NB][G];
+      scores(t0, kr, s);
+      if (t0 + STEP < t_end) {
+        offsets(t0 + STEP, off);
+        issue(kb, off, kr);
+      }
+      if constexpr (FIXED)
+        fixed_update<E, G, Gm::kVec, NB, kP>(s, vr, c_log2, a.phi_raw, a.flag_hi_raw,
+                                             a.flag_lo_raw, acc, mx, base, on, l);
+      else online_update<E, G, Gm::kVec, NB, kP>(s, vr, c_log2, acc, m, l);
     }
   }
-#else
-  for (int t0 = t_beg; t0 < t_end; t0 += t_step) {
-    u32x4 kr[NB], vr[NB];
-    load(t0, kr, vr);
-    compute(t0, kr, vr);
-  }
-#endif
   if constexpr (FIXED) {
 #pragma unroll
     for (int h = 0; h < G; ++h) m[h] = (mx[h] == kNegInf) ? kNegInf : base[h] * c_log2;
@@ -209,14 +211,22 @@ __device__ __forceinline__ void scan_rows(const char* __restrict__ kb,
 template <int MODE, typename E, int D, int G>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(FD_WAVES_PER_EU)))
 void partial_kernel(PartialArgs a) {
-  using Gm = Geo<E, D>;
-  constexpr int VEC = Gm::kVec, LPT = Gm::kLpt, TPL = Gm::kTpl;
+  // two pieces per lane halve the per-row work; G = 8 keeps one piece, as
+  // its accumulators already fill the registers
+  constexpr int kPg = G >= 8 ? 1 : kP;
+  using Gm = Geo<E, D, kPg>;
+  constexpr int VEC = Gm::kVec, LPT = Gm::kLpt, PV = Gm::kPv, TPL = Gm::kTpl;
+  // rows per slot per batch: the batch depth counts load instructions per
+  // tensor, and each row takes kPg of them
+  constexpr int kNbLoads =
+      batch_rows<G, MODE == kUnified ? FD_NB_FIXED : (MODE == kPaged ? FD_NB_PAGED : FD_NB)>();
+  constexpr int kNbMode = kNbLoads / kPg > 0 ? kNbLoads / kPg : 1;
   constexpr bool kFixed = MODE == kUnified;
   constexpr int kPid = MODE == kPaged ? kMaxChunkPages : 1;
   __shared__ int s_pid[MODE == kPaged ? kWaves : 1][kPid];
 
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & (kWave - 1);
-  const int col = lane % LPT;
+  const int col = lane % LPT, grp = lane / LPT;
   const int stride = (int)gridDim.x * kWaves;
 
   // Units: contiguous caches have B*Hkv*nc equal units.  Paged caches have
@@ -235,6 +245,27 @@ void partial_kernel(PartialArgs a) {
     n_units = tot * a.Hkv;
     seq_units = a.Hkv * ((seq_len(0) + a.chunk - 1) / a.chunk);
   }
+
+  // Finished units wait in registers -- row slot j of the wave keeps the j-th
+  // -- until every slot holds one or the wave runs out of units, and are
+  // then written together.  Stores count on the same vector-memory counter
+  // as loads, so a store issued between units would make the next unit's
+  // first loads wait for it (measured: 11 us of 169 on the 1 GiB workload).
+  float keep_acc[G][VEC], keep_m[G], keep_l[G];
+  size_t keep_row = 0;
+  unsigned keep_flags = 0;
+  int held = 0;   // wave-uniform
+  auto flush = [&]() {
+    if (grp < held) {
+      store_partial<G, D, VEC, kPg>(keep_acc, keep_m, keep_l, a.o_part, a.ml_part, keep_row,
+                                   (size_t)a.nc, col, col == 0);
+      if constexpr (kFixed) {
+        if (a.flags != nullptr && col < G)
+          a.flags[keep_row + (size_t)col * a.nc] = (uint8_t)((keep_flags >> col) & 1u);
+      }
+    }
+    held = 0;
+  };
 
   for (int u = (int)blockIdx.x * kWaves + wave; u < n_units; u += stride) {
     int b, kvh, c, L;
@@ -279,42 +310,45 @@ void partial_kernel(PartialArgs a) {
       vb = reinterpret_cast<const char*>(a.v) + base;
     }
 
-    u32x4 qv[G];
+    u32x4 qv[G][kPg];
     {
       const E* qp = reinterpret_cast<const E*>(a.q) +
-                    ((size_t)b * a.Hq + (size_t)kvh * G) * D + col * VEC;
+                    ((size_t)b * a.Hq + (size_t)kvh * G) * D + col * PV;
 #pragma unroll
-      for (int h = 0; h < G; ++h) qv[h] = ld16(qp + (size_t)h * D);
+      for (int h = 0; h < G; ++h)
+#pragma unroll
+        for (int pc = 0; pc < kPg; ++pc) qv[h][pc] = ld16(qp + (size_t)h * D + pc * (D / kPg));
     }
 
     float acc[G][VEC], m[G], l[G], mx[G];
-    constexpr int kNbMode =
-        batch_rows<G, MODE == kUnified ? FD_NB_FIXED : (MODE == kPaged ? FD_NB_PAGED : FD_NB)>();
-    scan_rows<kFixed, E, D, G, kNbMode>(kb, vb, rm, c0, c1, kNbMode * TPL, qv, a.c_log2, a, acc,
-                                        m, l, mx);
+    scan_rows<kFixed, E, D, G, kNbMode, kPg>(kb, vb, rm, c0, c1, qv, a.c_log2, a, acc, m, l, mx);
 
+    unsigned flag_bits = 0;
     if constexpr (kFixed) {
       // Range flags of each head's chunk maximum (the slots that left the
       // range already finished the chunk on the exact path).
-      if (a.flags != nullptr) {
-        bool flag[G];
 #pragma unroll
-        for (int h = 0; h < G; ++h) {
-          const float mm = wave_max(mx[h]);
-          flag[h] = (mm > a.flag_hi_raw) || (mm < a.flag_lo_raw);
-        }
-        if (lane < G) {
-          bool f = false;
-#pragma unroll
-          for (int h = 0; h < G; ++h) f = (h == lane) ? flag[h] : f;
-          a.flags[((size_t)b * a.Hq + (size_t)kvh * G + lane) * a.nc + c] = f ? 1 : 0;
-        }
+      for (int h = 0; h < G; ++h) {
+        const float mm = wave_max(mx[h]);
+        if ((mm > a.flag_hi_raw) || (mm < a.flag_lo_raw)) flag_bits |= 1u << h;
       }
     }
 
-    const size_t prow0 = ((size_t)b * a.Hq + (size_t)kvh * G) * a.nc + c;
-    wave_combine_store<G, D, VEC, LPT>(acc, m, l, a.o_part, a.ml_part, prow0, (size_t)a.nc);
+    wave_merge<G, VEC, LPT>(acc, m, l);
+    if (grp == held) {
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        keep_m[h] = m[h];
+        keep_l[h] = l[h];
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) keep_acc[h][e] = acc[h][e];
+      }
+      keep_row = ((size_t)b * a.Hq + (size_t)kvh * G) * a.nc + c;
+      keep_flags = flag_bits;
+    }
+    if (++held == TPL) flush();
   }
+  flush();
 }
 
 // Exact merge of a row's chunk partials ("Flash Decoding" explainer,

@@ -40,16 +40,16 @@ enum : int {
   kRowMirror = 0x140,     // lane i <-> 15-i inside each row
 };
 
-// Sum over aligned groups of N lanes (N = 8, 16 or 32); every lane of the
+// Sum over aligned groups of N lanes (N = 4, 8, 16 or 32); every lane of the
 // group receives the group's sum.  After the two quad steps each quad holds
 // its sum; the half-row mirror pairs lane i with a lane of the other quad,
 // the row mirror pairs the two halves, and a swizzle swaps 16-lane halves.
 template <int N>
 __device__ __forceinline__ float group_sum(float x) {
-  static_assert(N == 8 || N == 16 || N == 32, "group size");
+  static_assert(N == 4 || N == 8 || N == 16 || N == 32, "group size");
   x += dpp<kQuadXor1>(x);
   x += dpp<kQuadXor2>(x);
-  x += dpp<kRowHalfMirror>(x);
+  if constexpr (N >= 8) x += dpp<kRowHalfMirror>(x);
   if constexpr (N >= 16) x += dpp<kRowMirror>(x);
   if constexpr (N >= 32)
     x += __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(x), 0x401F));
@@ -60,13 +60,15 @@ __device__ __forceinline__ float group_sum(float x) {
 // across the whole array, so no step waits on the one just issued.
 template <int N, int M>
 __device__ __forceinline__ void group_sum_n(float (&x)[M]) {
-  static_assert(N == 8 || N == 16 || N == 32, "group size");
+  static_assert(N == 4 || N == 8 || N == 16 || N == 32, "group size");
 #pragma unroll
   for (int k = 0; k < M; ++k) x[k] += dpp<kQuadXor1>(x[k]);
 #pragma unroll
   for (int k = 0; k < M; ++k) x[k] += dpp<kQuadXor2>(x[k]);
+  if constexpr (N >= 8) {
 #pragma unroll
-  for (int k = 0; k < M; ++k) x[k] += dpp<kRowHalfMirror>(x[k]);
+    for (int k = 0; k < M; ++k) x[k] += dpp<kRowHalfMirror>(x[k]);
+  }
   if constexpr (N >= 16) {
 #pragma unroll
     for (int k = 0; k < M; ++k) x[k] += dpp<kRowMirror>(x[k]);
@@ -81,10 +83,10 @@ __device__ __forceinline__ void group_sum_n(float (&x)[M]) {
 // Same groups, maximum.
 template <int N>
 __device__ __forceinline__ float group_max(float x) {
-  static_assert(N == 8 || N == 16 || N == 32, "group size");
+  static_assert(N == 4 || N == 8 || N == 16 || N == 32, "group size");
   x = fmaxf(x, dpp<kQuadXor1>(x));
   x = fmaxf(x, dpp<kQuadXor2>(x));
-  x = fmaxf(x, dpp<kRowHalfMirror>(x));
+  if constexpr (N >= 8) x = fmaxf(x, dpp<kRowHalfMirror>(x));
   if constexpr (N >= 16) x = fmaxf(x, dpp<kRowMirror>(x));
   if constexpr (N >= 32)
     x = fmaxf(x, __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(x), 0x401F)));

@@ -21,9 +21,10 @@ namespace fdk {
 #endif
 constexpr int kWaves = FD_WAVES;      // wavefronts per split-KV unit
 constexpr int kThreads = kWaves * kWave;
-// Rows per slot per batch (loads per tensor per batch) of the split-KV
-// kernels: deep batches keep many 16-byte loads in flight per wave, but the
-// K, V and score registers of a batch grow with it and with G.
+// Load instructions per tensor per wave in one batch of the split-KV
+// kernels (the K and V loads of a batch): deep batches keep many 16-byte
+// loads in flight per wave, but the K, V and score registers of a batch grow
+// with the depth and with G.
 #ifndef FD_NB
 #define FD_NB 16
 #endif
@@ -36,13 +37,24 @@ constexpr int kThreads = kWaves * kWave;
 template <int G, int NBMAX = FD_NB>
 constexpr int batch_rows() { return G >= 8 ? (NBMAX > 8 ? 8 : NBMAX) : NBMAX; }
 
-template <typename E, int D>
+// Lane layout of a cache row: each of kLpt lanes holds P 16-byte pieces of
+// the row; piece p of lane `col` is bytes [p * kRow / P + col * 16, +16).
+// One wave load instruction (fixed p) covers kTpl rows.  More pieces per
+// lane mean fewer lanes per row, hence fewer butterfly steps per score and
+// fewer lanes that redo the per-row exponential.
+template <typename E, int D, int P = 1>
 struct Geo {
-  static constexpr int kVec = 16 / (int)sizeof(E);  // elements per lane per row
+  static constexpr int kPieces = P;
+  static constexpr int kPv = 16 / (int)sizeof(E);    // elements per piece
+  static constexpr int kVec = P * kPv;               // elements per lane per row
   static constexpr int kLpt = D / kVec;              // lanes per cache row
   static constexpr int kTpl = kWave / kLpt;          // rows per wave load
   static constexpr int kRow = D * (int)sizeof(E);    // bytes per cache row
-  static_assert(kLpt == 8 || kLpt == 16 || kLpt == 32, "row split");
+  static_assert(kLpt == 4 || kLpt == 8 || kLpt == 16 || kLpt == 32, "row split");
+  // element index (0..D) of a lane's value e
+  static __device__ __forceinline__ int dim(int col, int e) {
+    return (e / kPv) * (D / P) + col * kPv + e % kPv;
+  }
 };
 
 // q . k over one lane's 16-byte slice.
@@ -61,6 +73,30 @@ __device__ __forceinline__ float slice_dot(const u32x4& q, const u32x4& k) {
     a = fmaf(__uint_as_float(q.z), __uint_as_float(k.z), a);
     b = fmaf(__uint_as_float(q.w), __uint_as_float(k.w), b);
     return a + b;
+  }
+}
+
+// q . k over a lane's P pieces, one accumulation chain.
+template <typename E, int P>
+__device__ __forceinline__ float pieces_dot(const u32x4* q, const u32x4* k) {
+  if constexpr (std::is_same<E, uint16_t>::value) {
+    float a = dot2_bf16(q[0].x, k[0].x, 0.f);
+    a = dot2_bf16(q[0].y, k[0].y, a);
+    a = dot2_bf16(q[0].z, k[0].z, a);
+    a = dot2_bf16(q[0].w, k[0].w, a);
+#pragma unroll
+    for (int p = 1; p < P; ++p) {
+      a = dot2_bf16(q[p].x, k[p].x, a);
+      a = dot2_bf16(q[p].y, k[p].y, a);
+      a = dot2_bf16(q[p].z, k[p].z, a);
+      a = dot2_bf16(q[p].w, k[p].w, a);
+    }
+    return a;
+  } else {
+    float a = slice_dot<E>(q[0], k[0]);
+#pragma unroll
+    for (int p = 1; p < P; ++p) a += slice_dot<E>(q[p], k[p]);
+    return a;
   }
 }
 
@@ -94,9 +130,9 @@ __device__ __forceinline__ void state_reset(float (&acc)[G][VEC], float (&m)[G],
 // s[i][h]: raw dot products q_h . k_i (-inf for rows that do not count);
 // m[h]: running maximum in the same raw units.  The accumulator is rescaled
 // only when some slot of the wave saw a larger maximum.
-template <typename E, int G, int VEC, int NB>
+template <typename E, int G, int VEC, int NB, int P = 1>
 __device__ __forceinline__ void online_update(const float (&s)[NB][G],
-                                              const u32x4 (&vr)[NB], float c_log2,
+                                              const u32x4 (&vr)[NB * P], float c_log2,
                                               float (&acc)[G][VEC], float (&m)[G],
                                               float (&l)[G]) {
   float mb[G];
@@ -124,7 +160,8 @@ __device__ __forceinline__ void online_update(const float (&s)[NB][G],
 #pragma unroll
   for (int i = 0; i < NB; ++i) {
     float vf[VEC];
-    slice_vals<E>(vr[i], vf);
+#pragma unroll
+    for (int pc = 0; pc < P; ++pc) slice_vals<E>(vr[i * P + pc], vf + pc * (VEC / P));
 #pragma unroll
     for (int h = 0; h < G; ++h) {
       const float p = exp2_hw(fmaf(s[i][h], c_log2, -bias[h]));
@@ -142,15 +179,10 @@ __device__ __forceinline__ void state_to_log2(float (&m)[G], float c_log2) {
   for (int h = 0; h < G; ++h) m[h] = (m[h] == kNegInf) ? kNegInf : m[h] * c_log2;
 }
 
-// Merge the row slots of one wave (shuffles only) and write the wave's
-// partial for each of its G query heads: O (unnormalised, relative to m),
-// m (log2 units) and l.  Lanes col < LPT hold the merged slot afterwards.
-template <int G, int D, int VEC, int LPT>
-__device__ __forceinline__ void wave_combine_store(float (&acc)[G][VEC], float (&m)[G],
-                                                   float (&l)[G], float* o_part,
-                                                   float* ml_part, size_t prow0,
-                                                   size_t hstride) {
-  const int lane = threadIdx.x & (kWave - 1);
+// Merge the row slots of one wave with shuffles: afterwards every lane holds
+// the merged state (O relative to m, m in log2 units, l) of its column.
+template <int G, int VEC, int LPT>
+__device__ __forceinline__ void wave_merge(float (&acc)[G][VEC], float (&m)[G], float (&l)[G]) {
 #pragma unroll
   for (int off = LPT; off < kWave; off <<= 1) {
 #pragma unroll
@@ -168,22 +200,28 @@ __device__ __forceinline__ void wave_combine_store(float (&acc)[G][VEC], float (
       m[h] = M;
     }
   }
-  if (lane < LPT) {
+}
+
+// Write one lane's column of a merged state as the partial rows
+// prow0 + h * hstride (h < G): O (unnormalised), and (m, l) if `with_ml`.
+template <int G, int D, int VEC, int P>
+__device__ __forceinline__ void store_partial(const float (&acc)[G][VEC], const float (&m)[G],
+                                              const float (&l)[G], float* o_part,
+                                              float* ml_part, size_t prow0, size_t hstride,
+                                              int col, bool with_ml) {
+  constexpr int PV = VEC / P;   // contiguous elements per piece
 #pragma unroll
-    for (int h = 0; h < G; ++h) {
-      float* dst = o_part + (prow0 + (size_t)h * hstride) * D + lane * VEC;
+  for (int h = 0; h < G; ++h) {
+    float* dst = o_part + (prow0 + (size_t)h * hstride) * D + col * PV;
 #pragma unroll
-      for (int e = 0; e < VEC; e += 4)
-        *reinterpret_cast<f32x4*>(dst + e) =
-            f32x4{acc[h][e], acc[h][e + 1], acc[h][e + 2], acc[h][e + 3]};
-    }
+    for (int e = 0; e < VEC; e += 4)
+      *reinterpret_cast<f32x4*>(dst + (e / PV) * (D / P) + e % PV) =
+          f32x4{acc[h][e], acc[h][e + 1], acc[h][e + 2], acc[h][e + 3]};
   }
-  if (lane == 0) {
+  if (with_ml) {
 #pragma unroll
-    for (int h = 0; h < G; ++h) {
-      const size_t prow = prow0 + (size_t)h * hstride;
-      *reinterpret_cast<f32x2*>(ml_part + prow * 2) = f32x2{m[h], l[h]};
-    }
+    for (int h = 0; h < G; ++h)
+      *reinterpret_cast<f32x2*>(ml_part + (prow0 + (size_t)h * hstride) * 2) = f32x2{m[h], l[h]};
   }
 }
 
