@@ -35,19 +35,6 @@ constexpr int kMaxChunkPages = 1024;
 #endif
 constexpr int kP = FD_PIECES;
 
-// Byte offset (in rows) of cache position t for one kv-head.
-struct RowMap {
-  const int* pid;   // paged: LDS page ids of the chunk, else null
-  int c0;           // first position of the chunk
-  int shift;        // log2(page size)
-  int hkv, kvh;
-  __device__ __forceinline__ size_t row(int t) const {
-    if (pid == nullptr) return (size_t)t;
-    const int p = pid[(t - c0) >> shift];
-    return ((size_t)(p * hkv + kvh) << shift) | (size_t)(t & ((1 << shift) - 1));
-  }
-};
-
 // Fixed-maximum update with in-flight fallback.  A row slot takes
 // p = 2^((s - phi) c) while its running maximum stays inside
 // [phi - margin_lo, phi + margin_hi]: no rescale, no dependence on other
@@ -105,100 +92,10 @@ __device__ __forceinline__ void fixed_update(const float (&s)[NB][G], const u32x
   }
 }
 
-// Stream rows [t_beg, t_end) of one kv-head through the G query heads.  On
-// return m[h] is in log2 units of the scaled score: the slot's own maximum
-// (FIXED = false) or its reference -- phi, or its own maximum after a switch
-// (FIXED = true, where mx[h] also receives the largest raw dot product for
-// the range flags).  A slot that saw no row returns m = -inf, l = 0.
-template <bool FIXED, typename E, int D, int G, int NB, int kP>
-__device__ __forceinline__ void scan_rows(const char* __restrict__ kb,
-                                          const char* __restrict__ vb, const RowMap& rm,
-                                          int t_beg, int t_end,
-                                          const u32x4 (&qv)[G][kP], float c_log2,
-                                          const PartialArgs& a,
-                                          float (&acc)[G][Geo<E, D, kP>::kVec], float (&m)[G],
-                                          float (&l)[G], float (&mx)[G]) {
-  using Gm = Geo<E, D, kP>;
-  constexpr int LPT = Gm::kLpt, TPL = Gm::kTpl, ROW = Gm::kRow;
-  const int lane = threadIdx.x & (kWave - 1);
-  const int grp = lane / LPT, col = lane % LPT;
-  state_reset<G, Gm::kVec>(acc, m, l);
-  float base[G];
-  bool on[G];
-#pragma unroll
-  for (int h = 0; h < G; ++h) {
-    mx[h] = kNegInf;
-    base[h] = a.phi_raw;
-    on[h] = false;
-  }
-
-  // A batch is NB rows per slot.  The V rows of batch j are requested before
-  // the scores of batch j are computed, and the K rows of batch j + 1 before
-  // the PV update of batch j, so the wave's loads stay in flight while it
-  // computes.
-  constexpr int STEP = NB * TPL;
-  auto offsets = [&](int t0, size_t (&off)[NB]) {
-#pragma unroll
-    for (int i = 0; i < NB; ++i) {
-      const int t = min(t0 + i * TPL + grp, t_end - 1);
-      off[i] = rm.row(t) * ROW + (size_t)col * 16;
-    }
-  };
-  // piece pc of row i: bytes off[i] + pc * ROW / P; register kr[i * P + pc]
-  auto issue = [&](const char* __restrict__ src, const size_t (&off)[NB],
-                   u32x4 (&r)[NB * kP]) {
-#pragma unroll
-    for (int i = 0; i < NB; ++i)
-#pragma unroll
-      for (int pc = 0; pc < kP; ++pc)
-        r[i * kP + pc] = ld16_stream(src + off[i] + (size_t)pc * (ROW / kP));
-  };
-  auto scores = [&](int t0, const u32x4 (&kr)[NB * kP], float (&s)[NB][G]) {
-    float flat[NB * G];
-#pragma unroll
-    for (int i = 0; i < NB; ++i)
-#pragma unroll
-      for (int h = 0; h < G; ++h) flat[i * G + h] = pieces_dot<E, kP>(qv[h], kr + i * kP);
-    group_sum_n<LPT>(flat);
-#pragma unroll
-    for (int i = 0; i < NB; ++i)
-#pragma unroll
-      for (int h = 0; h < G; ++h) s[i][h] = flat[i * G + h];
-    if (t0 + STEP > t_end) {
-#pragma unroll
-      for (int i = 0; i < NB; ++i)
-        if (t0 + i * TPL + grp >= t_end)
-#pragma unroll
-          for (int h = 0; h < G; ++h) s[i][h] = kNegInf;
-    }
-  };
-  if (t_beg < t_end) {
-    u32x4 kr[NB * kP], vr[NB * kP];
-    size_t off[NB];
-    offsets(t_beg, off);
-    issue(kb, off, kr);
-    for (int t0 = t_beg; t0 < t_end; t0 += STEP) {
-      issue(vb, off, vr);
-      float s[NB][G];
-      scores(t0, kr, s);
-      if (t0 + STEP < t_end) {
-        offsets(t0 + STEP, off);
-        issue(kb, off, kr);
-      }
-      if constexpr (FIXED)
-        fixed_update<E, G, Gm::kVec, NB, kP>(s, vr, c_log2, a.phi_raw, a.flag_hi_raw,
-                                             a.flag_lo_raw, acc, mx, base, on, l);
-      else online_update<E, G, Gm::kVec, NB, kP>(s, vr, c_log2, acc, m, l);
-    }
-  }
-  if constexpr (FIXED) {
-#pragma unroll
-    for (int h = 0; h < G; ++h) m[h] = (mx[h] == kNegInf) ? kNegInf : base[h] * c_log2;
-  } else {
-    state_to_log2<G>(m, c_log2);
-  }
-}
-
+// One unit of work: chunk c of (sequence b, kv-head kvh), positions [c0, c1).
+struct Unit {
+  int b, kvh, c, c0, c1;
+};
 
 // Split-KV partials.  Work assignment: every wavefront owns whole chunks
 // (units) and walks units w, w + W, w + 2W, ... of the flattened
@@ -208,6 +105,14 @@ __device__ __forceinline__ void scan_rows(const char* __restrict__ kb,
 // keeps each wave's stream of 16-byte loads long and leaves no ragged last
 // round.  Row slots of a wave are merged with shuffles; there is no LDS
 // combine and no workgroup barrier.
+//
+// Streaming: a batch is NB rows per row slot.  The V rows of batch j are
+// requested before the scores of batch j are computed, and the K rows of the
+// next batch before the PV update of batch j -- across unit boundaries too:
+// the last batch of a unit requests the next unit's query and first K rows
+// (a paged cache has the next unit's page ids staged in LDS by then), and the
+// row slots are merged while those loads are in flight.  So a wave's loads
+// never stop between its first and its last unit.
 template <int MODE, typename E, int D, int G>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(FD_WAVES_PER_EU)))
 void partial_kernel(PartialArgs a) {
@@ -215,15 +120,19 @@ void partial_kernel(PartialArgs a) {
   // its accumulators already fill the registers
   constexpr int kPg = G >= 8 ? 1 : kP;
   using Gm = Geo<E, D, kPg>;
-  constexpr int VEC = Gm::kVec, LPT = Gm::kLpt, PV = Gm::kPv, TPL = Gm::kTpl;
+  constexpr int VEC = Gm::kVec, LPT = Gm::kLpt, PV = Gm::kPv, TPL = Gm::kTpl, ROW = Gm::kRow;
   // rows per slot per batch: the batch depth counts load instructions per
   // tensor, and each row takes kPg of them
   constexpr int kNbLoads =
       batch_rows<G, MODE == kUnified ? FD_NB_FIXED : (MODE == kPaged ? FD_NB_PAGED : FD_NB)>();
-  constexpr int kNbMode = kNbLoads / kPg > 0 ? kNbLoads / kPg : 1;
+  constexpr int NB = kNbLoads / kPg > 0 ? kNbLoads / kPg : 1;
+  constexpr int STEP = NB * TPL;   // rows per wave batch
   constexpr bool kFixed = MODE == kUnified;
-  constexpr int kPid = MODE == kPaged ? kMaxChunkPages : 1;
-  __shared__ int s_pid[MODE == kPaged ? kWaves : 1][kPid];
+  constexpr bool kPagedMode = MODE == kPaged;
+  constexpr int kPid = kPagedMode ? kMaxChunkPages : 1;
+  // paged: page ids of the current and the next unit of each wave (written
+  // and read by that wave only, so no barrier is needed)
+  __shared__ int s_pid[kPagedMode ? kWaves : 1][2][kPid];
 
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & (kWave - 1);
   const int col = lane % LPT, grp = lane / LPT;
@@ -232,12 +141,12 @@ void partial_kernel(PartialArgs a) {
   // Units: contiguous caches have B*Hkv*nc equal units.  Paged caches have
   // ragged lengths, so only the real units -- Hkv * ceil(L_b / chunk) for
   // sequence b -- are numbered (sequence-major), and every wave walks its
-  // share of them; `seq_first`/`seq_units` track the sequence of the current
-  // unit as the wave's unit index grows.
+  // share of them; `seq_first`/`seq_units` track the sequence of a unit as
+  // the wave's unit index grows.  Every numbered unit has c0 < c1.
   int n_units = a.B * a.Hkv * a.nc;
   int seq_b = 0, seq_first = 0, seq_units = 0;
   auto seq_len = [&](int bb) { return min(max(a.seq_lens[bb], 0), a.max_seq_len); };
-  if constexpr (MODE == kPaged) {
+  if constexpr (kPagedMode) {
     int tot = 0;
     for (int bb = lane; bb < a.B; bb += kWave) tot += (seq_len(bb) + a.chunk - 1) / a.chunk;
 #pragma unroll
@@ -245,6 +154,98 @@ void partial_kernel(PartialArgs a) {
     n_units = tot * a.Hkv;
     seq_units = a.Hkv * ((seq_len(0) + a.chunk - 1) / a.chunk);
   }
+  auto decode = [&](int u, Unit& x) {   // u must grow from call to call
+    int L;
+    if constexpr (kPagedMode) {
+      while (u >= seq_first + seq_units) {      // wave-uniform
+        seq_first += seq_units;
+        ++seq_b;
+        seq_units = a.Hkv * ((seq_len(seq_b) + a.chunk - 1) / a.chunk);
+      }
+      x.b = seq_b;
+      const int r = u - seq_first;
+      x.kvh = r % a.Hkv;
+      x.c = r / a.Hkv;
+      L = seq_len(seq_b);
+    } else {
+      x.c = u % a.nc;
+      const int bk = u / a.nc;
+      x.kvh = bk % a.Hkv;
+      x.b = bk / a.Hkv;
+      L = a.L;
+    }
+    x.c0 = x.c * a.chunk;
+    x.c1 = min(x.c0 + a.chunk, L);
+  };
+
+  // Paged addressing: the page ids of a unit's chunk.
+  const int shift = a.page_shift, pmask = (1 << a.page_shift) - 1;
+  auto n_pages = [&](const Unit& x) { return (x.c1 - x.c0 + pmask) >> shift; };
+  auto page_ids = [&](const Unit& x) {
+    return a.block_table + (size_t)x.b * a.max_pages + (x.c0 >> shift);
+  };
+  auto stage_pages = [&](const Unit& x, int buf) {
+    const int npg = n_pages(x);
+    const int32_t* bt = page_ids(x);
+    for (int i = lane; i < npg; i += kWave) s_pid[wave][buf][i] = min(max(bt[i], 0), a.num_pages - 1);
+  };
+
+  const char* kbase = reinterpret_cast<const char*>(a.k);
+  const char* vbase = reinterpret_cast<const char*>(a.v);
+  // Byte offsets (from the tensor base) of this lane's rows of the batch
+  // starting at t0; rows past the unit's end repeat its last row (masked).
+  auto offsets = [&](const Unit& x, int buf, int t0, size_t (&off)[NB]) {
+    const size_t head = kPagedMode ? 0 : ((size_t)x.b * a.Hkv + x.kvh) * (size_t)a.L;
+#pragma unroll
+    for (int i = 0; i < NB; ++i) {
+      const int t = min(t0 + i * TPL + grp, x.c1 - 1);
+      size_t row;
+      if constexpr (kPagedMode) {
+        const int p = s_pid[wave][buf][(t - x.c0) >> shift];
+        row = (((size_t)p * a.Hkv + x.kvh) << shift) | (size_t)(t & pmask);
+      } else {
+        row = head + (size_t)t;
+      }
+      off[i] = row * ROW + (size_t)col * 16;
+    }
+  };
+  // piece pc of row i: bytes off[i] + pc * ROW / kPg; register r[i * kPg + pc]
+  auto issue = [&](const char* __restrict__ src, const size_t (&off)[NB],
+                   u32x4 (&r)[NB * kPg]) {
+#pragma unroll
+    for (int i = 0; i < NB; ++i)
+#pragma unroll
+      for (int pc = 0; pc < kPg; ++pc)
+        r[i * kPg + pc] = ld16_stream(src + off[i] + (size_t)pc * (ROW / kPg));
+  };
+  u32x4 qv[G][kPg];
+  auto load_q = [&](const Unit& x) {
+    const E* qp = reinterpret_cast<const E*>(a.q) +
+                  ((size_t)x.b * a.Hq + (size_t)x.kvh * G) * D + col * PV;
+#pragma unroll
+    for (int h = 0; h < G; ++h)
+#pragma unroll
+      for (int pc = 0; pc < kPg; ++pc) qv[h][pc] = ld16(qp + (size_t)h * D + pc * (D / kPg));
+  };
+  auto scores = [&](const Unit& x, int t0, const u32x4 (&kr)[NB * kPg], float (&s)[NB][G]) {
+    float flat[NB * G];
+#pragma unroll
+    for (int i = 0; i < NB; ++i)
+#pragma unroll
+      for (int h = 0; h < G; ++h) flat[i * G + h] = pieces_dot<E, kPg>(qv[h], kr + i * kPg);
+    group_sum_n<LPT>(flat);
+#pragma unroll
+    for (int i = 0; i < NB; ++i)
+#pragma unroll
+      for (int h = 0; h < G; ++h) s[i][h] = flat[i * G + h];
+    if (t0 + STEP > x.c1) {
+#pragma unroll
+      for (int i = 0; i < NB; ++i)
+        if (t0 + i * TPL + grp >= x.c1)
+#pragma unroll
+          for (int h = 0; h < G; ++h) s[i][h] = kNegInf;
+    }
+  };
 
   // Finished units wait in registers -- row slot j of the wave keeps the j-th
   // -- until every slot holds one or the wave runs out of units, and are
@@ -267,71 +268,85 @@ void partial_kernel(PartialArgs a) {
     held = 0;
   };
 
-  for (int u = (int)blockIdx.x * kWaves + wave; u < n_units; u += stride) {
-    int b, kvh, c, L;
-    if constexpr (MODE == kPaged) {
-      while (u >= seq_first + seq_units) {      // wave-uniform
-        seq_first += seq_units;
-        ++seq_b;
-        seq_units = a.Hkv * ((seq_len(seq_b) + a.chunk - 1) / a.chunk);
+  int u = (int)blockIdx.x * kWaves + wave;
+  if (u >= n_units) return;
+  Unit cur;
+  decode(u, cur);
+  int buf = 0;
+  if constexpr (kPagedMode) stage_pages(cur, buf);
+  u32x4 kr[NB * kPg], vr[NB * kPg];
+  size_t off[NB];
+  load_q(cur);
+  offsets(cur, buf, cur.c0, off);
+  issue(kbase, off, kr);
+
+  while (true) {
+    const int un = u + stride;
+    const bool has_next = un < n_units;   // wave-uniform
+    Unit nxt = cur;
+    if (has_next) decode(un, nxt);
+    // paged: the next unit's page ids, one per lane when they fit (written
+    // to LDS once the first batch of this unit has arrived)
+    int pid_next = 0;
+    bool pid_inline = false;
+    if constexpr (kPagedMode) {
+      if (has_next) {
+        const int npg = n_pages(nxt);
+        pid_inline = npg <= kWave;
+        if (pid_inline && lane < npg) pid_next = page_ids(nxt)[lane];
       }
-      b = seq_b;
-      const int r = u - seq_first;
-      kvh = r % a.Hkv;
-      c = r / a.Hkv;
-      L = seq_len(b);
-    } else {
-      c = u % a.nc;
-      const int bk = u / a.nc;
-      kvh = bk % a.Hkv;
-      b = bk / a.Hkv;
-      L = a.L;
-    }
-    const int c0 = c * a.chunk;
-    if (c0 >= L) continue;  // not reached: every numbered unit is real
-    const int c1 = min(c0 + a.chunk, L);
-
-    RowMap rm{nullptr, c0, a.page_shift, a.Hkv, kvh};
-    const char* kb;
-    const char* vb;
-    if constexpr (MODE == kPaged) {
-      // Page ids of this chunk into this wave's LDS row (read back by the
-      // same wave only, so no barrier is needed).
-      const int first = c0 >> a.page_shift;
-      const int npg = (c1 - c0 + (1 << a.page_shift) - 1) >> a.page_shift;
-      const int32_t* bt = a.block_table + (size_t)b * a.max_pages + first;
-      for (int i = lane; i < npg; i += kWave) s_pid[wave][i] = min(max(bt[i], 0), a.num_pages - 1);
-      rm.pid = s_pid[wave];
-      kb = reinterpret_cast<const char*>(a.k);
-      vb = reinterpret_cast<const char*>(a.v);
-    } else {
-      const size_t base = ((size_t)b * a.Hkv + kvh) * (size_t)a.L * Gm::kRow;
-      kb = reinterpret_cast<const char*>(a.k) + base;
-      vb = reinterpret_cast<const char*>(a.v) + base;
     }
 
-    u32x4 qv[G][kPg];
-    {
-      const E* qp = reinterpret_cast<const E*>(a.q) +
-                    ((size_t)b * a.Hq + (size_t)kvh * G) * D + col * PV;
+    float acc[G][VEC], m[G], l[G], mx[G], base[G];
+    bool on[G];
+    state_reset<G, VEC>(acc, m, l);
 #pragma unroll
-      for (int h = 0; h < G; ++h)
-#pragma unroll
-        for (int pc = 0; pc < kPg; ++pc) qv[h][pc] = ld16(qp + (size_t)h * D + pc * (D / kPg));
+    for (int h = 0; h < G; ++h) {
+      mx[h] = kNegInf;
+      base[h] = a.phi_raw;
+      on[h] = false;
     }
-
-    float acc[G][VEC], m[G], l[G], mx[G];
-    scan_rows<kFixed, E, D, G, kNbMode, kPg>(kb, vb, rm, c0, c1, qv, a.c_log2, a, acc, m, l, mx);
-
+    for (int t0 = cur.c0; t0 < cur.c1; t0 += STEP) {
+      issue(vbase, off, vr);
+      float s[NB][G];
+      scores(cur, t0, kr, s);
+      if constexpr (kPagedMode) {
+        if (has_next && t0 == cur.c0) {
+          if (pid_inline) {
+            if (lane < n_pages(nxt)) s_pid[wave][buf ^ 1][lane] = min(max(pid_next, 0), a.num_pages - 1);
+          } else {
+            stage_pages(nxt, buf ^ 1);
+          }
+        }
+      }
+      if (t0 + STEP < cur.c1) {
+        offsets(cur, buf, t0 + STEP, off);
+        issue(kbase, off, kr);
+      } else if (has_next) {
+        load_q(nxt);
+        offsets(nxt, buf ^ 1, nxt.c0, off);
+        issue(kbase, off, kr);
+      }
+      if constexpr (kFixed)
+        fixed_update<E, G, VEC, NB, kPg>(s, vr, a.c_log2, a.phi_raw, a.flag_hi_raw,
+                                         a.flag_lo_raw, acc, mx, base, on, l);
+      else online_update<E, G, VEC, NB, kPg>(s, vr, a.c_log2, acc, m, l);
+    }
+    // m in log2 units of the scaled score: the slot's own maximum, or for
+    // the fixed maximum its reference (phi, or its own maximum after a
+    // switch); a slot that saw no row has m = -inf, l = 0
     unsigned flag_bits = 0;
     if constexpr (kFixed) {
-      // Range flags of each head's chunk maximum (the slots that left the
-      // range already finished the chunk on the exact path).
 #pragma unroll
       for (int h = 0; h < G; ++h) {
+        m[h] = (mx[h] == kNegInf) ? kNegInf : base[h] * a.c_log2;
+        // range flag of each head's chunk maximum (slots that left the range
+        // already finished the chunk on the exact path)
         const float mm = wave_max(mx[h]);
         if ((mm > a.flag_hi_raw) || (mm < a.flag_lo_raw)) flag_bits |= 1u << h;
       }
+    } else {
+      state_to_log2<G>(m, a.c_log2);
     }
 
     wave_merge<G, VEC, LPT>(acc, m, l);
@@ -343,10 +358,14 @@ void partial_kernel(PartialArgs a) {
 #pragma unroll
         for (int e = 0; e < VEC; ++e) keep_acc[h][e] = acc[h][e];
       }
-      keep_row = ((size_t)b * a.Hq + (size_t)kvh * G) * a.nc + c;
+      keep_row = ((size_t)cur.b * a.Hq + (size_t)cur.kvh * G) * a.nc + cur.c;
       keep_flags = flag_bits;
     }
     if (++held == TPL) flush();
+    if (!has_next) break;
+    cur = nxt;
+    u = un;
+    buf ^= 1;
   }
   flush();
 }

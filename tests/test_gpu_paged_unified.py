@@ -47,7 +47,7 @@ def test_paged_ragged(dtype, d, G):
     assert torch.all(out[0] == 0) and torch.all(torch.isinf(lse[0]))
 
 
-@pytest.mark.parametrize("page,chunk", [(8, 64), (32, 128), (64, 64)])
+@pytest.mark.parametrize("page,chunk", [(8, 64), (32, 128), (64, 64), (8, 1024), (16, 2048)])
 def test_paged_page_sizes(page, chunk):
     c = W.paged_case(4, 8, 2, 128, 100, 700, page=page, chunk=chunk, seed=page, device=DEV)
     out, lse = _paged_run(c)
