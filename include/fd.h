@@ -200,7 +200,8 @@ int fd_ffd_pack(const void* k, uint32_t* codes, uint16_t* zs, int8_t* res,
  *   cand_mask  uint32 [B, Hq, ceil(L/32)] or NULL: bit j%32 of word j/32 set
  *              when position j is in C
  *   pseudo_max fp32 [B, Hq] or NULL: m^
- *   chunk      positions per chunk (multiple of 16)
+ *   chunk      positions per chunk: a multiple of 32, at most 2048
+ *              (1024 when Hq / Hkv = 8); FD_ERR_UNSUPPORTED otherwise
  */
 int fd_ffd_sparse_decode(const void* q, const uint32_t* codes,
                          const uint16_t* zs, const int8_t* res,

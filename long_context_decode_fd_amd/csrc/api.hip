@@ -270,6 +270,8 @@ int fd_ffd_sparse_decode(const void* q, const uint32_t* codes, const uint16_t* z
   if (L <= 0) return fail(FD_ERR_ARG, "L=%d must be positive", L);
   if (int e = check_chunk(chunk)) return e;
   {
+    // the kernel keeps a chunk's scan scores, masks and candidate list in
+    // LDS: (4 G + 3) bytes per position, at most 38 KiB with these limits
     const int cmax = (Hq / Hkv) >= 8 ? 1024 : 2048;
     if (chunk % 32 != 0 || chunk > cmax)
       return fail(FD_ERR_UNSUPPORTED, "FFD chunk=%d must be a multiple of 32 <= %d", chunk,

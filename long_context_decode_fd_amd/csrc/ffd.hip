@@ -26,20 +26,33 @@
 
 namespace fdk {
 
-// Largest chunk whose scan scores fit in LDS: 2048 positions (G <= 4),
-// 1024 for groups of 8.
-template <int G>
-constexpr int ffd_max_chunk() { return G >= 8 ? 1024 : 2048; }
-
 #ifndef FD_FFD_NT
 #define FD_FFD_NT 1
 #endif
 #ifndef FD_FFD_SCAN_STEPS
-#define FD_FFD_SCAN_STEPS 4
+#define FD_FFD_SCAN_STEPS 8
 #endif
 #ifndef FD_FFD_BATCHED_SUM
 #define FD_FFD_BATCHED_SUM 0
 #endif
+#ifndef FD_FFD_NB
+#define FD_FFD_NB 8
+#endif
+
+// Dynamic LDS of the FFD kernel for a chunk of `chunk` positions: scan
+// scores [chunk][G] (fp32), candidate masks [chunk] (u8), candidate list
+// [chunk] (u16).  Sized to the chunk so that short chunks leave room for
+// more resident workgroups.
+template <int G>
+__host__ __device__ constexpr size_t ffd_lds_mask_off(int chunk) { return (size_t)chunk * G * 4; }
+template <int G>
+__host__ __device__ constexpr size_t ffd_lds_list_off(int chunk) {
+  return (ffd_lds_mask_off<G>(chunk) + (size_t)chunk + 3) & ~(size_t)3;
+}
+template <int G>
+__host__ __device__ constexpr size_t ffd_lds_bytes(int chunk) {
+  return ffd_lds_list_off<G>(chunk) + (size_t)chunk * 2;
+}
 
 template <class T>
 __device__ __forceinline__ T ffd_load(const T* p) {
@@ -195,15 +208,15 @@ template <int D, int G>
 __global__ __launch_bounds__(kThreads) void ffd_kernel(FfdArgs a) {
   using Gm = Geo<uint16_t, D>;
   constexpr int VEC = Gm::kVec, LPT = Gm::kLpt, TPL = Gm::kTpl;
-  constexpr int kNb = 8;             // rows per slot per batch in the refine
+  constexpr int kNb = FD_FFD_NB;     // rows per slot per batch in the refine
   constexpr int NG = D / 32;         // quantisation groups per position
   constexpr int TPS = kWave / NG;    // positions per wave step in the scan
   constexpr int CW = D / 16;         // code words per position
 
-  constexpr int kFfdMaxChunk = ffd_max_chunk<G>();
-  __shared__ float s_scan[kFfdMaxChunk][G];
-  __shared__ uint8_t s_mask[kFfdMaxChunk];
-  __shared__ uint16_t s_list[kFfdMaxChunk];
+  extern __shared__ __align__(16) unsigned char s_dyn[];
+  float (*s_scan)[G] = reinterpret_cast<float (*)[G]>(s_dyn);
+  uint8_t* s_mask = s_dyn + ffd_lds_mask_off<G>(a.chunk);
+  uint16_t* s_list = reinterpret_cast<uint16_t*>(s_dyn + ffd_lds_list_off<G>(a.chunk));
   __shared__ int s_cnt[kWaves];
   __shared__ CombineLds<G, D> s_cmb;
 
@@ -486,7 +499,7 @@ hipError_t launch_ffd(int D, int G, const FfdArgs& a, hipStream_t s) {
                        s, a);                                                        \
     hipError_t e = hipGetLastError();                                                \
     if (e != hipSuccess) return e;                                                   \
-    hipLaunchKernelGGL((ffd_kernel<DD, GG>), grid, block, 0, s, a);                  \
+    hipLaunchKernelGGL((ffd_kernel<DD, GG>), grid, block, ffd_lds_bytes<GG>(a.chunk), s, a); \
     return hipGetLastError();                                                        \
   }
   FD_FFD_CASE(64, 1) FD_FFD_CASE(64, 2) FD_FFD_CASE(64, 4) FD_FFD_CASE(64, 8)
