@@ -158,6 +158,35 @@ int fd_decode_attn_unified_max(fd_dtype_t dt, const void* q, const void* k,
                                void* ws, size_t* ws_bytes, void* stream);
 
 /*
+ * Cache append ("Flash Decoding" explainer, section 3: each generated token
+ * adds its key and value rows to the cache; a paged cache keeps them in
+ * fixed-size pages listed by the block table).  Writes the step's M new rows
+ * per (sequence, kv-head); the FFD key format of appended keys is made with
+ * fd_ffd_pack over the same position range.
+ *
+ * fd_kv_append: contiguous cache, every sequence at the same position.
+ *   k_new, v_new       [B, Hkv, M, d] (dt)
+ *   k_cache, v_cache   [B, Hkv, L_cap, d] (dt); rows t .. t+M-1 are written
+ *   0 <= t and t + M <= L_cap, else FD_ERR_ARG (nothing written)
+ * fd_kv_append_paged: pools [num_pages, Hkv, page_size, d]; sequence b
+ *   writes positions pos[b] .. pos[b]+M-1 (pos: int32 [B], device) to slot
+ *   p % page_size of page block_table[b, p / page_size].  A position below
+ *   0, past the table row (p / page_size >= max_pages_per_seq) or whose
+ *   table entry is not in [0, num_pages) is skipped, not written.
+ * All arrays 16-byte aligned; caller-owned; asynchronous on `stream`.  The
+ * new rows must not overlap the cache rows they are written to.
+ */
+int fd_kv_append(fd_dtype_t dt, const void* k_new, const void* v_new,
+                 void* k_cache, void* v_cache, int B, int Hkv, int M,
+                 int L_cap, int d, int t, void* stream);
+
+int fd_kv_append_paged(fd_dtype_t dt, const void* k_new, const void* v_new,
+                       void* k_pool, void* v_pool, const int32_t* block_table,
+                       const int32_t* pos, int B, int Hkv, int M, int d,
+                       int page_size, int max_pages_per_seq, int num_pages,
+                       void* stream);
+
+/*
  * FFD key format ("Faster Than Flash" digest, section 5 and Fig. 2: a 2-bit
  * main part scanned for every position plus an 8-bit residual read only for
  * candidates).  Per position, per group of 32 consecutive dimensions:

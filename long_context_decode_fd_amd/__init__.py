@@ -10,6 +10,7 @@ Entry points (names follow the C ABI):
   decode_attn_partials, merge_partials   its two stages
   decode_attn_paged      paged cache with a block table
   decode_attn_unified_max  fixed maximum with exact fallback
+  kv_append, kv_append_paged   the step's new K/V rows into the cache
   ffd_pack               2-bit + 8-bit residual key format
   ffd_sparse_decode      FFD: 2-bit scan, pseudo-max, top-delta, refine
 """
@@ -24,7 +25,8 @@ from . import _abi
 from ._abi import FD_BF16, FD_F32, FdError  # noqa: F401
 
 __all__ = ["decode_attn", "decode_attn_partials", "merge_partials", "partial_views",
-           "decode_attn_paged", "decode_attn_unified_max", "ffd_pack", "ffd_sparse_decode",
+           "decode_attn_paged", "decode_attn_unified_max", "kv_append", "kv_append_paged",
+           "ffd_pack", "ffd_sparse_decode",
            "workspace_bytes", "FdError", "lib"]
 
 
@@ -203,6 +205,40 @@ def decode_attn_unified_max(q, k, v, phi, chunk=512, margin_hi=10.0, margin_lo=4
     workspace, size = _workspace(L_.fd_decode_attn_unified_max, args, workspace, dev)
     _abi.check(L_.fd_decode_attn_unified_max(*args(_ptr(workspace), C.byref(size))))
     return out, lse, flags
+
+
+def kv_append(k_new, v_new, k_cache, v_cache, t):
+    """Write k_new/v_new [B,Hkv,M,d] into rows t..t+M-1 of the contiguous
+    caches [B,Hkv,L_cap,d] (same dtype)."""
+    B, Hkv, M, d = k_new.shape
+    L_cap = k_cache.shape[2]
+    dev = k_new.device
+    _need(k_new, "k_new", device=dev)
+    _need(v_new, "v_new", (B, Hkv, M, d), k_new.dtype, dev)
+    _need(k_cache, "k_cache", (B, Hkv, L_cap, d), k_new.dtype, dev)
+    _need(v_cache, "v_cache", (B, Hkv, L_cap, d), k_new.dtype, dev)
+    _abi.check(lib().fd_kv_append(_dt(k_new), _ptr(k_new), _ptr(v_new), _ptr(k_cache),
+                                  _ptr(v_cache), B, Hkv, M, L_cap, d, int(t), _stream(dev)))
+
+
+def kv_append_paged(k_new, v_new, k_pool, v_pool, block_table, pos):
+    """Write k_new/v_new [B,Hkv,M,d] at positions pos[b]..pos[b]+M-1 (pos int32
+    [B], device) of the paged pools [P,Hkv,page,d] through block_table int32
+    [B,max_pages]; positions without a valid page are skipped."""
+    B, Hkv, M, d = k_new.shape
+    P, page = k_pool.shape[0], k_pool.shape[2]
+    dev = k_new.device
+    _need(k_new, "k_new", device=dev)
+    _need(v_new, "v_new", (B, Hkv, M, d), k_new.dtype, dev)
+    _need(k_pool, "k_pool", (P, Hkv, page, d), k_new.dtype, dev)
+    _need(v_pool, "v_pool", (P, Hkv, page, d), k_new.dtype, dev)
+    _need(block_table, "block_table", dtype=torch.int32, device=dev)
+    _need(pos, "pos", (B,), torch.int32, dev)
+    if block_table.dim() != 2 or block_table.shape[0] != B:
+        raise ValueError("block_table must be [B, max_pages]")
+    _abi.check(lib().fd_kv_append_paged(_dt(k_new), _ptr(k_new), _ptr(v_new), _ptr(k_pool),
+                                        _ptr(v_pool), _ptr(block_table), _ptr(pos), B, Hkv, M,
+                                        d, page, block_table.shape[1], P, _stream(dev)))
 
 
 def ffd_pack(k, t_begin=0, t_end=None, out=None):

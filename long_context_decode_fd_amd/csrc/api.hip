@@ -243,6 +243,61 @@ int fd_decode_attn_unified_max(fd_dtype_t dt, const void* q, const void* k, cons
                       nc, pa, ws, nullptr, L, stream);
 }
 
+int fd_kv_append(fd_dtype_t dt, const void* k_new, const void* v_new, void* k_cache,
+                 void* v_cache, int B, int Hkv, int M, int L_cap, int d, int t, void* stream) {
+  if (dt != FD_F32 && dt != FD_BF16) return fail(FD_ERR_ARG, "unknown dtype %d", (int)dt);
+  if (B <= 0 || Hkv <= 0 || M <= 0 || L_cap <= 0)
+    return fail(FD_ERR_ARG, "B=%d Hkv=%d M=%d L_cap=%d must be positive", B, Hkv, M, L_cap);
+  if (d != 64 && d != 128) return fail(FD_ERR_UNSUPPORTED, "d=%d not in {64,128}", d);
+  if (t < 0 || t > L_cap - M)
+    return fail(FD_ERR_ARG, "rows t=%d .. t+M-1=%d outside the cache of %d", t, t + M - 1, L_cap);
+  if (!k_new || !v_new || !k_cache || !v_cache) return fail(FD_ERR_ARG, "NULL array");
+  if (!aligned16(k_new) || !aligned16(v_new) || !aligned16(k_cache) || !aligned16(v_cache))
+    return fail(FD_ERR_ARG, "arrays must be 16-byte aligned");
+  fdk::AppendArgs a{};
+  a.k_new = static_cast<const char*>(k_new);
+  a.v_new = static_cast<const char*>(v_new);
+  a.k_dst = static_cast<char*>(k_cache);
+  a.v_dst = static_cast<char*>(v_cache);
+  a.B = B; a.Hkv = Hkv; a.M = M; a.L_cap = L_cap; a.t0 = t;
+  a.row_bytes = d * (dt == FD_BF16 ? 2 : 4);
+  return hip_status(fdk::launch_append(false, a, reinterpret_cast<hipStream_t>(stream)),
+                    "append kernel launch");
+}
+
+int fd_kv_append_paged(fd_dtype_t dt, const void* k_new, const void* v_new, void* k_pool,
+                       void* v_pool, const int32_t* block_table, const int32_t* pos, int B,
+                       int Hkv, int M, int d, int page_size, int max_pages_per_seq,
+                       int num_pages, void* stream) {
+  if (dt != FD_F32 && dt != FD_BF16) return fail(FD_ERR_ARG, "unknown dtype %d", (int)dt);
+  if (B <= 0 || Hkv <= 0 || M <= 0 || max_pages_per_seq <= 0 || num_pages <= 0)
+    return fail(FD_ERR_ARG, "B=%d Hkv=%d M=%d max_pages=%d num_pages=%d must be positive", B,
+                Hkv, M, max_pages_per_seq, num_pages);
+  if (d != 64 && d != 128) return fail(FD_ERR_UNSUPPORTED, "d=%d not in {64,128}", d);
+  if (page_size < 8 || page_size > 1024 || (page_size & (page_size - 1)) != 0)
+    return fail(FD_ERR_ARG, "page_size=%d must be a power of two in [8, 1024]", page_size);
+  if (!k_new || !v_new || !k_pool || !v_pool || !block_table || !pos)
+    return fail(FD_ERR_ARG, "NULL array");
+  if (!aligned16(k_new) || !aligned16(v_new) || !aligned16(k_pool) || !aligned16(v_pool))
+    return fail(FD_ERR_ARG, "arrays must be 16-byte aligned");
+  fdk::AppendArgs a{};
+  a.k_new = static_cast<const char*>(k_new);
+  a.v_new = static_cast<const char*>(v_new);
+  a.k_dst = static_cast<char*>(k_pool);
+  a.v_dst = static_cast<char*>(v_pool);
+  a.block_table = block_table;
+  a.pos = pos;
+  a.B = B; a.Hkv = Hkv; a.M = M;
+  a.row_bytes = d * (dt == FD_BF16 ? 2 : 4);
+  int shift = 0;
+  while ((1 << shift) < page_size) ++shift;
+  a.page_shift = shift;
+  a.max_pages = max_pages_per_seq;
+  a.num_pages = num_pages;
+  return hip_status(fdk::launch_append(true, a, reinterpret_cast<hipStream_t>(stream)),
+                    "paged append kernel launch");
+}
+
 int fd_ffd_pack(const void* k, uint32_t* codes, uint16_t* zs, int8_t* res, uint16_t* rs,
                 int B, int Hkv, int L_cap, int d, int t_begin, int t_end, void* stream) {
   if (B <= 0 || Hkv <= 0 || L_cap <= 0)

@@ -70,4 +70,15 @@ struct FfdArgs {
 };
 hipError_t launch_ffd(int D, int G, const FfdArgs& a, hipStream_t s);
 
+struct AppendArgs {
+  const char* k_new;   // [B, Hkv, M, row]
+  const char* v_new;
+  char* k_dst;         // contiguous [B, Hkv, L_cap, row] or pool [P, Hkv, page, row]
+  char* v_dst;
+  const int32_t* block_table;  // paged only
+  const int32_t* pos;          // paged only: first write position per sequence
+  int B, Hkv, M, L_cap, t0, row_bytes, page_shift, max_pages, num_pages;
+};
+hipError_t launch_append(bool paged, const AppendArgs& a, hipStream_t s);
+
 }  // namespace fdk

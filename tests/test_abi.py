@@ -102,3 +102,20 @@ def test_workspace_too_small():
                             C.c_void_p(256), None, 1, 8, 2, 64, 128, 0.1, 32,
                             C.c_void_p(256), C.byref(size), None)
     assert rc == _abi.FD_ERR_WORKSPACE
+
+
+def test_append_validation():
+    lib = fd.lib()
+    p = C.c_void_p(256)        # never dereferenced: validation fails first
+    # contiguous: rows t .. t+M-1 must fit in the cache
+    for (M, L_cap, d, t, code) in [(2, 10, 128, 9, _abi.FD_ERR_ARG), (1, 10, 128, -1, _abi.FD_ERR_ARG),
+                                   (0, 10, 128, 0, _abi.FD_ERR_ARG), (1, 10, 96, 0, _abi.FD_ERR_UNSUPPORTED)]:
+        assert lib.fd_kv_append(1, p, p, p, p, 2, 2, M, L_cap, d, t, None) == code
+    assert lib.fd_kv_append(1, None, p, p, p, 2, 2, 1, 10, 128, 0, None) == _abi.FD_ERR_ARG
+    assert lib.fd_kv_append(1, C.c_void_p(264), p, p, p, 2, 2, 1, 10, 128, 0, None) == _abi.FD_ERR_ARG
+    # paged: page size a power of two in [8, 1024]; positive sizes
+    for (page, maxp, P, code) in [(12, 4, 8, _abi.FD_ERR_ARG), (16, 0, 8, _abi.FD_ERR_ARG),
+                                  (16, 4, 0, _abi.FD_ERR_ARG), (2048, 4, 8, _abi.FD_ERR_ARG)]:
+        assert lib.fd_kv_append_paged(1, p, p, p, p, p, p, 2, 2, 1, 128, page, maxp, P, None) == code
+    assert lib.fd_kv_append_paged(1, p, p, p, p, None, p, 2, 2, 1, 128, 16, 4, 8, None) == _abi.FD_ERR_ARG
+    assert lib.fd_kv_append_paged(7, p, p, p, p, p, p, 2, 2, 1, 128, 16, 4, 8, None) == _abi.FD_ERR_ARG
