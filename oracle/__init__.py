@@ -28,4 +28,4 @@ Pinned by ``tests/test_oracle_*.py``; see each function for its pin.  The one
 part with no pin is the pages' end-to-end sparsity / speed / quality figures,
 which need trained models: parity unpinned there.
 """
-from . import flash_decoding, paged, unified, ffd, append  # noqa: F401
+from . import flash_decoding, paged, unified, ffd, append, multi_row  # noqa: F401
