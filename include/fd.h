@@ -158,6 +158,25 @@ int fd_decode_attn_unified_max(fd_dtype_t dt, const void* q, const void* k,
                                void* ws, size_t* ws_bytes, void* stream);
 
 /*
+ * Multi-row decode attention: M new query tokens per sequence whose keys and
+ * values are already in the cache at positions L-M .. L-1; token r attends to
+ * positions 0 .. L-M+r ("Flash Decoding" explainer, section 1: a query sees
+ * every key up to its own position).  The G*M query rows of a kv-head share
+ * each K and V row (the flat-GEMM case of the "FlashDecoding" deployment
+ * blog, section 1), computed on the matrix cores; M = 1 takes the
+ * single-query kernel of fd_decode_attn.
+ *   q     [B, M, Hq, d]; k, v [B, Hkv, L, d]; L >= M
+ *   out   fp32 [B, M, Hq, d];  lse fp32 [B, M, Hq] or NULL
+ *   M = 1: dt bf16 or fp32.  M >= 2: bf16 only and G*M <= 16, else
+ *   FD_ERR_UNSUPPORTED.  Workspace: chunk partials of the B*M*Hq rows
+ *   (same layout as fd_decode_attn_partials with M*Hq heads).
+ */
+int fd_decode_attn_multi(fd_dtype_t dt, const void* q, const void* k,
+                         const void* v, float* out, float* lse, int B, int M,
+                         int Hq, int Hkv, int L, int d, float scale, int chunk,
+                         void* ws, size_t* ws_bytes, void* stream);
+
+/*
  * Cache append ("Flash Decoding" explainer, section 3: each generated token
  * adds its key and value rows to the cache; a paged cache keeps them in
  * fixed-size pages listed by the block table).  Writes the step's M new rows

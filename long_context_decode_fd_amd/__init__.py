@@ -10,6 +10,7 @@ Entry points (names follow the C ABI):
   decode_attn_partials, merge_partials   its two stages
   decode_attn_paged      paged cache with a block table
   decode_attn_unified_max  fixed maximum with exact fallback
+  decode_attn_multi      several new query tokens per sequence (causal)
   kv_append, kv_append_paged   the step's new K/V rows into the cache
   ffd_pack               2-bit + 8-bit residual key format
   ffd_sparse_decode      FFD: 2-bit scan, pseudo-max, top-delta, refine
@@ -25,7 +26,8 @@ from . import _abi
 from ._abi import FD_BF16, FD_F32, FdError  # noqa: F401
 
 __all__ = ["decode_attn", "decode_attn_partials", "merge_partials", "partial_views",
-           "decode_attn_paged", "decode_attn_unified_max", "kv_append", "kv_append_paged",
+           "decode_attn_paged", "decode_attn_unified_max", "decode_attn_multi", "kv_append",
+           "kv_append_paged",
            "ffd_pack", "ffd_sparse_decode",
            "workspace_bytes", "FdError", "lib"]
 
@@ -207,6 +209,36 @@ def decode_attn_unified_max(q, k, v, phi, chunk=512, margin_hi=10.0, margin_lo=4
     return out, lse, flags
 
 
+def decode_attn_multi(q, k, v, chunk=512, scale=None, out=None, lse=None, want_lse=True,
+                      workspace=None):
+    """Multi-row decode: q [B,M,Hq,d] (M new tokens whose K/V sit at positions
+    L-M..L-1 of k/v [B,Hkv,L,d]); token r sees positions 0..L-M+r.
+    Returns (out fp32 [B,M,Hq,d], lse fp32 [B,M,Hq] or None)."""
+    B, M, Hq, d = q.shape
+    Hkv, L = k.shape[1], k.shape[2]
+    dev = q.device
+    _need(q, "q", device=dev)
+    _need(k, "k", (B, Hkv, L, d), q.dtype, dev)
+    _need(v, "v", (B, Hkv, L, d), q.dtype, dev)
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    if out is None:
+        out = torch.empty((B, M, Hq, d), dtype=torch.float32, device=dev)
+    _need(out, "out", (B, M, Hq, d), torch.float32, dev)
+    if lse is None and want_lse:
+        lse = torch.empty((B, M, Hq), dtype=torch.float32, device=dev)
+    if lse is not None:
+        _need(lse, "lse", (B, M, Hq), torch.float32, dev)
+    L_ = lib()
+    st = _stream(dev)
+
+    def args(ws, wsb):
+        return (_dt(q), _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, M, Hq, Hkv, L, d,
+                scale, int(chunk), ws, wsb, st)
+    workspace, size = _workspace(L_.fd_decode_attn_multi, args, workspace, dev)
+    _abi.check(L_.fd_decode_attn_multi(*args(_ptr(workspace), C.byref(size))))
+    return out, lse
+
+
 def kv_append(k_new, v_new, k_cache, v_cache, t):
     """Write k_new/v_new [B,Hkv,M,d] into rows t..t+M-1 of the contiguous
     caches [B,Hkv,L_cap,d] (same dtype)."""
@@ -309,6 +341,10 @@ def workspace_bytes(entry: str, **kw) -> int:
         rc = L_.fd_decode_attn(g("dt", FD_BF16), None, None, None, None, None, g("B"),
                                g("Hq"), g("Hkv"), g("L"), g("d"), g("scale", 0.1),
                                g("chunk"), None, C.byref(need), None)
+    elif entry == "fd_decode_attn_multi":
+        rc = L_.fd_decode_attn_multi(g("dt", FD_BF16), None, None, None, None, None, g("B"),
+                                     g("M"), g("Hq"), g("Hkv"), g("L"), g("d"), g("scale", 0.1),
+                                     g("chunk"), None, C.byref(need), None)
     elif entry == "fd_decode_attn_unified_max":
         rc = L_.fd_decode_attn_unified_max(g("dt", FD_BF16), None, None, None, None, None,
                                            g("B"), g("Hq"), g("Hkv"), g("L"), g("d"),

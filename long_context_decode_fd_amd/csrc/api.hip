@@ -243,6 +243,44 @@ int fd_decode_attn_unified_max(fd_dtype_t dt, const void* q, const void* k, cons
                       nc, pa, ws, nullptr, L, stream);
 }
 
+int fd_decode_attn_multi(fd_dtype_t dt, const void* q, const void* k, const void* v,
+                         float* out, float* lse, int B, int M, int Hq, int Hkv, int L, int d,
+                         float scale, int chunk, void* ws, size_t* ws_bytes, void* stream) {
+  if (dt != FD_F32 && dt != FD_BF16) return fail(FD_ERR_ARG, "unknown dtype %d", (int)dt);
+  if (int e = check_heads(B, Hq, Hkv, d)) return e;
+  if (M <= 0) return fail(FD_ERR_ARG, "M=%d must be positive", M);
+  if (L < M) return fail(FD_ERR_ARG, "L=%d must be at least M=%d", L, M);
+  if (int e = check_chunk(chunk)) return e;
+  if (int e = check_scale(scale)) return e;
+  const int G = Hq / Hkv;
+  if (M > 1 && G * M > 16)
+    return fail(FD_ERR_UNSUPPORTED, "G*M=%d query rows per kv-head exceed 16", G * M);
+  if (M > 1 && dt != FD_BF16)
+    return fail(FD_ERR_UNSUPPORTED, "several query tokens need bf16 inputs");
+  const int nc = (L + chunk - 1) / chunk;
+  if (int e = workspace_gate(ws, ws_bytes, partial_bytes(B, M * Hq, nc, d))) return e;
+  if (ws == nullptr) return ok();
+  if (!q || !k || !v || !out) return fail(FD_ERR_ARG, "q, k, v and out must not be NULL");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
+    return fail(FD_ERR_ARG, "q, k, v and out must be 16-byte aligned");
+  if (M == 1) {
+    // one query row per head: the single-query kernel (q [B, 1, Hq, d] is
+    // q [B, Hq, d])
+    fdk::PartialArgs pa{};
+    return run_split_kv(fdk::kDense, dt, q, k, v, out, lse, B, Hq, Hkv, L, d, scale, chunk, nc,
+                        pa, ws, nullptr, L, stream);
+  }
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  float *o_part, *ml_part;
+  split_ws(ws, B, M * Hq, nc, d, &o_part, &ml_part);
+  fdk::MultiArgs ma{q, k, v, o_part, ml_part, B, M, Hq, Hkv, L, chunk, nc,
+                    (float)((double)scale * 1.4426950408889634)};
+  hipError_t e = fdk::launch_multi(d, ma, s);
+  if (e != hipSuccess) return hip_status(e, "multi-row kernel launch");
+  fdk::MergeArgs mg{o_part, ml_part, out, lse, nullptr, M * Hq, nc, chunk, L};
+  return hip_status(fdk::launch_merge(d, B, mg, s), "merge kernel launch");
+}
+
 int fd_kv_append(fd_dtype_t dt, const void* k_new, const void* v_new, void* k_cache,
                  void* v_cache, int B, int Hkv, int M, int L_cap, int d, int t, void* stream) {
   if (dt != FD_F32 && dt != FD_BF16) return fail(FD_ERR_ARG, "unknown dtype %d", (int)dt);

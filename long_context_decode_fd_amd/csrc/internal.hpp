@@ -70,6 +70,19 @@ struct FfdArgs {
 };
 hipError_t launch_ffd(int D, int G, const FfdArgs& a, hipStream_t s);
 
+// Multi-row decode: q [B, M, Hq, D] bf16, k/v [B, Hkv, L, D] bf16, partials
+// for the rows (b, r, h) in the same layout as PartialArgs with M*Hq heads.
+struct MultiArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  float* o_part;
+  float* ml_part;
+  int B, M, Hq, Hkv, L, chunk, nc;
+  float c_log2;
+};
+hipError_t launch_multi(int D, const MultiArgs& a, hipStream_t s);
+
 struct AppendArgs {
   const char* k_new;   // [B, Hkv, M, row]
   const char* v_new;

@@ -1,0 +1,251 @@
+// Multi-row decode attention for gfx950: M new query tokens per sequence,
+// each attending to the cache up to its own position ("Flash Decoding"
+// explainer, section 1; the tokens' keys and values are already appended at
+// positions L-M .. L-1).  The G query heads of a kv-head times the M tokens
+// give R = G*M <= 16 query rows that share every K and V row -- the flat
+// GEMM case of the "FlashDecoding" deployment blog (section 1), which here
+// runs on the matrix cores:
+//
+//   * S^T = K Q^T per 16-position tile with v_mfma_f32_16x16x32_bf16: the A
+//     operand is 16 K rows straight from HBM (lane (n, quad) holds 16 bytes
+//     of row n per k-step), the B operand the query rows (same lane map).
+//     In the 16x16 result a lane holds one query row n and four consecutive
+//     positions 4*quad .. 4*quad+3, which is exactly the A operand layout of
+//     v_mfma_f32_16x16x16_bf16 for P V.
+//   * Online softmax per query row over the wave's batch (row maximum across
+//     the four lanes of the row with two shuffles); p in fp32, split into
+//     bf16 hi + lo parts so that P V keeps fp32-level accuracy (two MFMAs).
+//   * V tiles pass through a small per-wave LDS tile to be read transposed
+//     (four positions of one dim per lane, the B operand of P V).
+//   * Split-KV as in the single-query kernel: one wavefront per chunk,
+//     partials (O, m, l) per (token, head, chunk), merged by the common exact
+//     log-sum-exp kernel.
+#include <algorithm>
+
+#include "internal.hpp"
+#include "splitkv.hpp"
+
+namespace fdk {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+
+#ifndef FD_MR_TILES
+#define FD_MR_TILES 4   // 16-position tiles per wave batch: 16 K and 16 V loads at d = 128
+#endif
+
+__device__ __forceinline__ f32x4 mfma_qk(const u32x4& a, const u32x4& b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                  __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x4 mfma_pv(const u32x2& a, const u32x2& b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4_t, a),
+                                                    __builtin_bit_cast(s16x4_t, b), c, 0, 0, 0);
+}
+
+// fp32 -> bf16 bits, round to nearest even (finite inputs).
+__device__ __forceinline__ uint32_t bf16_bits(float x) {
+  const uint32_t u = __float_as_uint(x);
+  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+// p = hi + lo with hi = bf16(p), lo = bf16(p - hi): two bf16 pairs from four
+// fp32 values.
+__device__ __forceinline__ void split_bf16(const float (&p)[4], u32x2& hi, u32x2& lo) {
+  uint32_t h[4], l[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    h[e] = bf16_bits(p[e]);
+    l[e] = bf16_bits(p[e] - __uint_as_float(h[e] << 16));
+  }
+  hi = u32x2{h[0] | (h[1] << 16), h[2] | (h[3] << 16)};
+  lo = u32x2{l[0] | (l[1] << 16), l[2] | (l[3] << 16)};
+}
+
+template <int D>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1)))
+void multi_kernel(MultiArgs a) {
+  constexpr int KS = D / 32;             // 16-byte pieces per lane per row = QK k-steps
+  constexpr int DB = D / 16;             // 16-dim blocks of the P V product
+  constexpr int TT = FD_MR_TILES;
+  constexpr int STEP = 16 * TT;          // positions per wave batch
+  constexpr int ROWB = D * 2;            // bytes per cache row
+  constexpr int LSTR = ROWB + 8;         // LDS row stride: rows 4 apart sit 8 banks apart
+  __shared__ __align__(16) unsigned char s_v[kWaves][16 * LSTR];
+
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & (kWave - 1);
+  const int n = lane & 15, qd = lane >> 4;
+  const int G = a.Hq / a.Hkv, R = G * a.M;
+  const int stride = (int)gridDim.x * kWaves;
+  const int n_units = a.B * a.Hkv * a.nc;
+  unsigned char* lv = s_v[wave];
+  const float c_log2 = a.c_log2;
+
+  for (int u = (int)blockIdx.x * kWaves + wave; u < n_units; u += stride) {
+    const int c = u % a.nc, bk = u / a.nc;
+    const int kvh = bk % a.Hkv, b = bk / a.Hkv;
+    const int c0 = c * a.chunk, c1 = min(c0 + a.chunk, a.L);
+    const size_t head = ((size_t)b * a.Hkv + kvh) * (size_t)a.L * ROWB;
+    const char* kb = reinterpret_cast<const char*>(a.k) + head;
+    const char* vb = reinterpret_cast<const char*>(a.v) + head;
+
+    // Query row n of this lane: token r = n / G, head kvh*G + n % G; its
+    // last visible position is L - M + r.  Rows n >= R are padding (q = 0).
+    const int r_n = n / G;
+    const int lim = a.L - a.M + r_n;
+    u32x4 qf[KS];
+    if (n < R) {
+      const uint16_t* qp = reinterpret_cast<const uint16_t*>(a.q) +
+                           (((size_t)b * a.M + r_n) * a.Hq + (size_t)kvh * G + n % G) * D +
+                           (D / 4) * qd;
+#pragma unroll
+      for (int s = 0; s < KS; ++s) qf[s] = ld16(qp + 8 * s);
+    } else {
+#pragma unroll
+      for (int s = 0; s < KS; ++s) qf[s] = u32x4{0, 0, 0, 0};
+    }
+
+    // lane (n, qd) loads bytes [(D/2)*qd, (D/2)*(qd+1)) of row T + 16*tt + n
+    // (rows past the chunk repeat its last row and are masked)
+    auto issue = [&](const char* __restrict__ src, int T, u32x4 (&r)[TT][KS]) {
+#pragma unroll
+      for (int tt = 0; tt < TT; ++tt) {
+        const int t = min(T + 16 * tt + n, c1 - 1);
+        const char* p = src + (size_t)t * ROWB + (D / 2) * qd;
+#pragma unroll
+        for (int s = 0; s < KS; ++s) r[tt][s] = ld16_stream(p + 16 * s);
+      }
+    };
+
+    f32x4 o[DB];
+#pragma unroll
+    for (int db = 0; db < DB; ++db) o[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float m = kNegInf, l = 0.f;   // row n's running maximum (raw) and this lane's part of l
+    u32x4 kr[TT][KS], vr[TT][KS];
+    issue(kb, c0, kr);
+    for (int T = c0; T < c1; T += STEP) {
+      issue(vb, T, vr);
+      float sc[TT][4];
+#pragma unroll
+      for (int tt = 0; tt < TT; ++tt) {
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < KS; ++s) acc = mfma_qk(kr[tt][s], qf[s], acc);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int pos = T + 16 * tt + 4 * qd + e;
+          sc[tt][e] = (pos < c1 && pos <= lim) ? acc[e] : kNegInf;
+        }
+      }
+      if (T + STEP < c1) issue(kb, T + STEP, kr);
+
+      float bm = kNegInf;
+#pragma unroll
+      for (int tt = 0; tt < TT; ++tt)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) bm = fmaxf(bm, sc[tt][e]);
+      bm = fmaxf(bm, __shfl_xor(bm, 16));
+      bm = fmaxf(bm, __shfl_xor(bm, 32));
+      const float mn = fmaxf(m, bm);
+      if (__any(mn > m)) {
+        const float alpha = (mn == m) ? 1.f : exp2_hw((m - mn) * c_log2);
+        l *= alpha;
+        // O rows 4*qd + e take the factors of those rows (held by lanes 4*qd + e)
+        float ae[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) ae[e] = __shfl(alpha, 4 * qd + e);
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) o[db][e] *= ae[e];
+        m = mn;
+      }
+      const float bias = (m == kNegInf) ? 0.f : m * c_log2;
+
+#pragma unroll
+      for (int tt = 0; tt < TT; ++tt) {
+        float p[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          p[e] = exp2_hw(fmaf(sc[tt][e], c_log2, -bias));
+          l += p[e];
+        }
+        u32x2 ph, pl;
+        split_bf16(p, ph, pl);
+        // V tile through LDS: row n of the tile, then four positions of one
+        // dim per lane (this wave's region; LDS keeps the wave's order)
+#pragma unroll
+        for (int s = 0; s < KS; ++s)
+          *reinterpret_cast<u32x4*>(lv + n * LSTR + (D / 2) * qd + 16 * s) = vr[tt][s];
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+          const uint16_t* col = reinterpret_cast<const uint16_t*>(lv + (16 * db + n) * 2);
+          const uint32_t x0 = (uint32_t)col[(4 * qd + 0) * (LSTR / 2)] |
+                              ((uint32_t)col[(4 * qd + 1) * (LSTR / 2)] << 16);
+          const uint32_t x1 = (uint32_t)col[(4 * qd + 2) * (LSTR / 2)] |
+                              ((uint32_t)col[(4 * qd + 3) * (LSTR / 2)] << 16);
+          const u32x2 vv = {x0, x1};
+          o[db] = mfma_pv(ph, vv, o[db]);
+          o[db] = mfma_pv(pl, vv, o[db]);
+        }
+      }
+    }
+
+    // l of row n: the four lanes of the row hold parts
+    l += __shfl_xor(l, 16);
+    l += __shfl_xor(l, 32);
+    // partial rows ((b*M + r)*Hq + h)*nc + c
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int row = 4 * qd + e;
+      if (row < R) {
+        const size_t prow =
+            (((size_t)b * a.M + row / G) * a.Hq + (size_t)kvh * G + row % G) * a.nc + c;
+#pragma unroll
+        for (int db = 0; db < DB; ++db) a.o_part[prow * D + 16 * db + n] = o[db][e];
+      }
+    }
+    if (qd == 0 && n < R) {
+      const size_t prow = (((size_t)b * a.M + r_n) * a.Hq + (size_t)kvh * G + n % G) * a.nc + c;
+      *reinterpret_cast<f32x2*>(a.ml_part + prow * 2) =
+          f32x2{(m == kNegInf) ? kNegInf : m * c_log2, l};
+    }
+  }
+}
+
+// Workgroups of this kernel that fit on one compute unit.
+template <class K>
+static int multi_blocks_per_cu(K kernel) {
+  int n = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kernel, kThreads, 0) != hipSuccess ||
+      n <= 0)
+    n = 1;
+  return n;
+}
+
+template <int D>
+static hipError_t launch_multi_d(const MultiArgs& a, hipStream_t s) {
+  auto kernel = multi_kernel<D>;
+  static const int per_cu = multi_blocks_per_cu(kernel);
+  int dev = 0, cus = 256;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      cus <= 0)
+    cus = 256;
+  // equal rounds for every wave, as for the single-query kernel
+  const size_t units = (size_t)a.B * a.Hkv * a.nc;
+  const size_t slots = (size_t)cus * per_cu * kWaves;
+  const size_t rounds = (units + slots - 1) / slots;
+  const unsigned grid = (unsigned)((units + kWaves * rounds - 1) / (kWaves * rounds));
+  hipLaunchKernelGGL(kernel, dim3(grid), dim3(kThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_multi(int D, const MultiArgs& a, hipStream_t s) {
+  if (D == 64) return launch_multi_d<64>(a, s);
+  if (D == 128) return launch_multi_d<128>(a, s);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace fdk

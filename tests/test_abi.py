@@ -119,3 +119,19 @@ def test_append_validation():
         assert lib.fd_kv_append_paged(1, p, p, p, p, p, p, 2, 2, 1, 128, page, maxp, P, None) == code
     assert lib.fd_kv_append_paged(1, p, p, p, p, None, p, 2, 2, 1, 128, 16, 4, 8, None) == _abi.FD_ERR_ARG
     assert lib.fd_kv_append_paged(7, p, p, p, p, p, p, 2, 2, 1, 128, 16, 4, 8, None) == _abi.FD_ERR_ARG
+
+
+def test_multi_row_validation_and_workspace():
+    base = dict(B=2, M=4, Hq=8, Hkv=2, L=100, d=128, chunk=32)
+    # partials of the B*M*Hq*n_chunks = 2*4*8*4 = 256 rows: O and (m, l)
+    assert fd.workspace_bytes("fd_decode_attn_multi", **base) == 256 * 128 * 4 + 256 * 2 * 4
+    for bad, code in [(dict(M=8), _abi.FD_ERR_UNSUPPORTED),          # G*M = 32 rows
+                      (dict(dt=_abi.FD_F32), _abi.FD_ERR_UNSUPPORTED),   # fp32 with M >= 2
+                      (dict(M=0), _abi.FD_ERR_ARG), (dict(L=3), _abi.FD_ERR_ARG),
+                      (dict(chunk=20), _abi.FD_ERR_ARG)]:
+        kw = dict(base); kw.update(bad)
+        with pytest.raises(fd.FdError) as e:
+            fd.workspace_bytes("fd_decode_attn_multi", **kw)
+        assert e.value.code == code, bad
+    # one token: the single-query path, any dtype
+    assert fd.workspace_bytes("fd_decode_attn_multi", **dict(base, M=1, dt=_abi.FD_F32)) > 0

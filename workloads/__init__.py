@@ -8,6 +8,6 @@ recipes.
 """
 from .synth import (  # noqa: F401
     DenseCase, PagedCase, UnifiedCase, FfdCase,
-    dense_case, paged_case, unified_case, ffd_case,
+    dense_case, paged_case, unified_case, ffd_case, multi_case,
     config_case, CONFIGS,
 )

@@ -32,7 +32,7 @@ import torch
 
 __all__ = [
     "DenseCase", "PagedCase", "UnifiedCase", "FfdCase",
-    "dense_case", "paged_case", "unified_case", "ffd_case",
+    "dense_case", "paged_case", "unified_case", "ffd_case", "multi_case",
     "config_case", "CONFIGS",
 ]
 
@@ -149,6 +149,21 @@ def dense_case(B, Hq, Hkv, L, d, dtype="bf16", chunk=512, seed=0,
     v = _store(_randn((B, Hkv, L, d), g, device), dtype)
     return DenseCase(q, k, v, 1.0 / math.sqrt(d), int(chunk),
                      dict(B=B, Hq=Hq, Hkv=Hkv, L=L, d=d, dtype=dtype, seed=seed))
+
+
+def multi_case(B, M, Hq, Hkv, L, d, chunk=512, seed=0, device="cpu",
+               q_scale=1.0) -> DenseCase:
+    """Several new query tokens per sequence: q [B, M, Hq, d] (times
+    ``q_scale`` for sharper scores), K, V [B, Hkv, L, d], the M tokens' keys
+    and values being the last M positions; all iid N(0, 1), drawn in that
+    order, stored as bf16."""
+    g = _gen(seed, device)
+    q = (q_scale * _randn((B, M, Hq, d), g, device)).to(torch.bfloat16)
+    k = _randn((B, Hkv, L, d), g, device).to(torch.bfloat16)
+    v = _randn((B, Hkv, L, d), g, device).to(torch.bfloat16)
+    return DenseCase(q, k, v, 1.0 / math.sqrt(d), int(chunk),
+                     dict(B=B, M=M, Hq=Hq, Hkv=Hkv, L=L, d=d, dtype="bf16", seed=seed,
+                          q_scale=q_scale))
 
 
 def paged_case(B, Hq, Hkv, d, len_lo, len_hi, page=16, chunk=512, seed=0,
