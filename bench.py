@@ -13,8 +13,8 @@ decode-attention call over the whole batch (every kernel of the call).
                with HIP events on the launch stream: KV + query bytes per
                launch / mean launch time, against 8 TB/s
   cpu_baseline = the fp64 CPU oracle on a bounded sample of the same workload
-  variants   = the paged, fixed-maximum, FFD and cache-append entry points on
-               their own workloads (same timing method), for the whole hot path
+  variants   = the paged, fixed-maximum, FFD, multi-row and cache-append entry
+               points on their own workloads (same timing method)
 
 K/V live in several copies that the timed steps rotate through, so each call
 reads data that is not resident in the 256 MB last-level cache.
@@ -230,6 +230,49 @@ def cpu_baseline(torch, case, target_s):
                         f"bf16->fp64 input conversion {t_conv:.2f} s excluded"),
                 us_per_step_equiv=round(t_oracle / done * B * 1e6, 1),
                 host_cpus=len(os.sched_getaffinity(0)))
+
+
+def variant_multi(torch, fd, W, args, timer):
+    """Multi-row decode on the headline shape (B 8, Hq 32, Hkv 8, d 128,
+    L 32768, chunk 512) with M = 2 and 4 new tokens per sequence (G*M = 8
+    and 16 query rows per kv-head, matrix-core kernel), beside M separate
+    single-query calls on the same cache."""
+    B, Hq, Hkv, L, d, chunk = 8, 32, 8, 32768, 128, 512
+    base = W.multi_case(B, 4, Hq, Hkv, L, d, chunk=chunk, seed=102, device="cuda:0")
+    ks = [base.k] + [base.k.clone() for _ in range(args.copies - 1)]
+    vs = [base.v] + [base.v.clone() for _ in range(args.copies - 1)]
+    lib = fd.lib()
+    st = C.c_void_p(torch.cuda.current_stream().cuda_stream)
+    kv_bytes = 2 * B * Hkv * L * d * 2
+    res = dict(workload=f"multi-row decode bf16, B={B}, Hq={Hq}, Hkv={Hkv}, d={d}, L={L}, "
+                        f"chunk={chunk}, token r sees positions 0..L-M+r")
+    t_single = None
+    for M in (1, 2, 4):
+        q = base.q[:, :M].contiguous()
+        out = torch.empty((B, M, Hq, d), dtype=torch.float32, device="cuda:0")
+        lse = torch.empty((B, M, Hq), dtype=torch.float32, device="cuda:0")
+        wsn = fd.workspace_bytes("fd_decode_attn_multi", B=B, M=M, Hq=Hq, Hkv=Hkv, L=L, d=d,
+                                 chunk=chunk)
+        ws = torch.empty(wsn, dtype=torch.uint8, device="cuda:0")
+        size = C.c_size_t(wsn)
+        calls = []
+        for k, v in zip(ks, vs):
+            a = (fd.FD_BF16, vp(q), vp(k), vp(v), vp(out), vp(lse), B, M, Hq, Hkv, L, d,
+                 base.scale, chunk, vp(ws), C.byref(size), st)
+            calls.append(lambda a=a: lib.fd_decode_attn_multi(*a))
+        check_rc(lib, calls[0]())
+        t = timer.run(calls, args.steps, args.warmup)
+        nbytes = kv_bytes + B * M * Hq * d * 2 + B * M * Hq * (d + 1) * 4
+        if M == 1:
+            t_single = t["ms"]
+            continue
+        res[f"M_{M}"] = dict(rows_per_kv_head=M * Hq // Hkv, us_per_step=round(t["ms"] * 1e3, 2),
+                             p10_us=round(t["p10"] * 1e3, 2), p90_us=round(t["p90"] * 1e3, 2),
+                             bytes=nbytes, gbs=round(gbs(nbytes, t["ms"]), 1),
+                             pct_of_peak=round(100 * gbs(nbytes, t["ms"]) / PEAK_GBS, 1),
+                             m_single_query_calls_us=round(M * t_single * 1e3, 2),
+                             speedup_vs_single_calls=round(M * t_single / t["ms"], 2))
+    return res
 
 
 def variant_append(torch, fd, W, args, timer):
@@ -525,6 +568,7 @@ def main():
             "unified_max": variant_unified(torch, fd, W, args, timer),
             "ffd": variant_ffd(torch, fd, W, args, timer),
             "ffd_peaked": variant_ffd_peaked(torch, fd, W, args, timer),
+            "multi_row": variant_multi(torch, fd, W, args, timer),
             "append": variant_append(torch, fd, W, args, timer),
         }
     if not args.no_cpu_baseline:

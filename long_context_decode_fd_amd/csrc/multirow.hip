@@ -6,17 +6,20 @@
 // GEMM case of the "FlashDecoding" deployment blog (section 1), which here
 // runs on the matrix cores:
 //
+//   * K and V rows arrive with fully coalesced 16-byte loads (one wave load
+//     = 1 KiB of consecutive rows) and pass through a small per-wave LDS
+//     tile, from which each lane reads its MFMA operand.
 //   * S^T = K Q^T per 16-position tile with v_mfma_f32_16x16x32_bf16: the A
-//     operand is 16 K rows straight from HBM (lane (n, quad) holds 16 bytes
-//     of row n per k-step), the B operand the query rows (same lane map).
-//     In the 16x16 result a lane holds one query row n and four consecutive
+//     operand is 16 K rows (lane (n, quad) holds dims 32s + 8 quad .. +8 of
+//     row n at k-step s), the B operand the query rows (same lane map).  In
+//     the 16x16 result a lane holds one query row n and four consecutive
 //     positions 4*quad .. 4*quad+3, which is exactly the A operand layout of
 //     v_mfma_f32_16x16x16_bf16 for P V.
 //   * Online softmax per query row over the wave's batch (row maximum across
 //     the four lanes of the row with two shuffles); p in fp32, split into
 //     bf16 hi + lo parts so that P V keeps fp32-level accuracy (two MFMAs).
-//   * V tiles pass through a small per-wave LDS tile to be read transposed
-//     (four positions of one dim per lane, the B operand of P V).
+//   * V tiles are read back from LDS transposed with ds_read_b64_tr_b16 (four
+//     positions of one dim per lane, the B operand of P V).
 //   * Split-KV as in the single-query kernel: one wavefront per chunk,
 //     partials (O, m, l) per (token, head, chunk), merged by the common exact
 //     log-sum-exp kernel.
@@ -31,7 +34,7 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
 
 #ifndef FD_MR_TILES
-#define FD_MR_TILES 4   // 16-position tiles per wave batch: 16 K and 16 V loads at d = 128
+#define FD_MR_TILES 2   // 16-position tiles per wave batch: 8 K and 8 V loads at d = 128
 #endif
 
 __device__ __forceinline__ f32x4 mfma_qk(const u32x4& a, const u32x4& b, f32x4 c) {
@@ -66,79 +69,129 @@ __device__ __forceinline__ void split_bf16(const float (&p)[4], u32x2& hi, u32x2
 template <int D>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1)))
 void multi_kernel(MultiArgs a) {
-  constexpr int KS = D / 32;             // 16-byte pieces per lane per row = QK k-steps
+  constexpr int KS = D / 32;             // QK k-steps (32 dims each)
   constexpr int DB = D / 16;             // 16-dim blocks of the P V product
   constexpr int TT = FD_MR_TILES;
   constexpr int STEP = 16 * TT;          // positions per wave batch
   constexpr int ROWB = D * 2;            // bytes per cache row
+  constexpr int LPR = ROWB / 16;         // lanes per row in a coalesced load
+  constexpr int RPI = kWave / LPR;       // rows per wave load
+  constexpr int NI = 16 / RPI;           // wave loads per 16-row tile (= KS)
   constexpr int LSTR = ROWB + 8;         // LDS row stride: rows 4 apart sit 8 banks apart
-  __shared__ __align__(16) unsigned char s_v[kWaves][16 * LSTR];
+  __shared__ __align__(16) unsigned char s_kv[kWaves][2][16 * LSTR];
 
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & (kWave - 1);
   const int n = lane & 15, qd = lane >> 4;
   const int G = a.Hq / a.Hkv, R = G * a.M;
   const int stride = (int)gridDim.x * kWaves;
   const int n_units = a.B * a.Hkv * a.nc;
-  unsigned char* lv = s_v[wave];
+  unsigned char* lk = s_kv[wave][0];
+  unsigned char* lv = s_kv[wave][1];
+  const int lrow = lane / LPR, lcol = lane % LPR;   // coalesced-load lane map
+  // Transposing LDS read (ds_read_b64_tr_b16): in each 16-lane group, lane i
+  // receives element i % 4 of the 8-byte reads of lanes i/4, 4 + i/4, 8 + i/4
+  // and 12 + i/4.  Lane n of quad qd therefore points at row 4*qd + n/4, dims
+  // 16*db + 4*(n % 4) of the V tile, and gets V[4*qd + e][16*db + n], e < 4:
+  // four positions of one dim, the B operand of P V.
+  const int tr_off = (4 * qd + (n >> 2)) * LSTR + 8 * (n & 3);
   const float c_log2 = a.c_log2;
 
-  for (int u = (int)blockIdx.x * kWaves + wave; u < n_units; u += stride) {
-    const int c = u % a.nc, bk = u / a.nc;
-    const int kvh = bk % a.Hkv, b = bk / a.Hkv;
-    const int c0 = c * a.chunk, c1 = min(c0 + a.chunk, a.L);
-    const size_t head = ((size_t)b * a.Hkv + kvh) * (size_t)a.L * ROWB;
-    const char* kb = reinterpret_cast<const char*>(a.k) + head;
-    const char* vb = reinterpret_cast<const char*>(a.v) + head;
-
-    // Query row n of this lane: token r = n / G, head kvh*G + n % G; its
-    // last visible position is L - M + r.  Rows n >= R are padding (q = 0).
-    const int r_n = n / G;
-    const int lim = a.L - a.M + r_n;
-    u32x4 qf[KS];
+  struct UnitM {
+    int b, kvh, c, c0, c1;
+  };
+  auto decode = [&](int u, UnitM& x) {
+    x.c = u % a.nc;
+    const int bk = u / a.nc;
+    x.kvh = bk % a.Hkv;
+    x.b = bk / a.Hkv;
+    x.c0 = x.c * a.chunk;
+    x.c1 = min(x.c0 + a.chunk, a.L);
+  };
+  auto base_of = [&](const void* t, const UnitM& x) {
+    return reinterpret_cast<const char*>(t) + ((size_t)x.b * a.Hkv + x.kvh) * (size_t)a.L * ROWB;
+  };
+  // Query row n of this lane: token r = n / G, head kvh*G + n % G; its last
+  // visible position is L - M + r.  Rows n >= R are padding (q = 0).
+  const int r_n = n / G;
+  const int lim = a.L - a.M + r_n;
+  u32x4 qf[KS];
+  auto load_q = [&](const UnitM& x) {
     if (n < R) {
       const uint16_t* qp = reinterpret_cast<const uint16_t*>(a.q) +
-                           (((size_t)b * a.M + r_n) * a.Hq + (size_t)kvh * G + n % G) * D +
-                           (D / 4) * qd;
+                           (((size_t)x.b * a.M + r_n) * a.Hq + (size_t)x.kvh * G + n % G) * D +
+                           8 * qd;
 #pragma unroll
-      for (int s = 0; s < KS; ++s) qf[s] = ld16(qp + 8 * s);
+      for (int s = 0; s < KS; ++s) qf[s] = ld16(qp + 32 * s);
     } else {
 #pragma unroll
       for (int s = 0; s < KS; ++s) qf[s] = u32x4{0, 0, 0, 0};
     }
-
-    // lane (n, qd) loads bytes [(D/2)*qd, (D/2)*(qd+1)) of row T + 16*tt + n
-    // (rows past the chunk repeat its last row and are masked)
-    auto issue = [&](const char* __restrict__ src, int T, u32x4 (&r)[TT][KS]) {
+  };
+  // wave load i of tile tt: rows T + 16*tt + RPI*i + lrow, bytes 16*lcol
+  // (rows past the chunk end c1 repeat its last row and are masked)
+  auto issue = [&](const char* __restrict__ src, int T, int c1, u32x4 (&r)[TT][NI]) {
 #pragma unroll
-      for (int tt = 0; tt < TT; ++tt) {
-        const int t = min(T + 16 * tt + n, c1 - 1);
-        const char* p = src + (size_t)t * ROWB + (D / 2) * qd;
+    for (int tt = 0; tt < TT; ++tt)
 #pragma unroll
-        for (int s = 0; s < KS; ++s) r[tt][s] = ld16_stream(p + 16 * s);
+      for (int i = 0; i < NI; ++i) {
+        const int t = min(T + 16 * tt + RPI * i + lrow, c1 - 1);
+        r[tt][i] = ld16_stream(src + (size_t)t * ROWB + 16 * lcol);
       }
-    };
+  };
+  // a tile of 16 rows into this wave's LDS tile (row-major, stride LSTR)
+  auto to_lds = [&](unsigned char* dst, const u32x4 (&r)[NI]) {
+#pragma unroll
+    for (int i = 0; i < NI; ++i)
+      *reinterpret_cast<u32x4*>(dst + (RPI * i + lrow) * LSTR + 16 * lcol) = r[i];
+  };
+
+  int u = (int)blockIdx.x * kWaves + wave;
+  if (u >= n_units) return;
+  UnitM cur;
+  decode(u, cur);
+  u32x4 kr[TT][NI], vr[TT][NI];
+  load_q(cur);
+  issue(base_of(a.k, cur), cur.c0, cur.c1, kr);
+  // The last batch of a unit requests the next unit's query and first K rows
+  // before the unit's partials are stored: stores count on the same
+  // vector-memory counter as loads, so loads issued after them would wait.
+  while (true) {
+    const int un = u + stride;
+    const bool has_next = un < n_units;
+    UnitM nxt = cur;
+    if (has_next) decode(un, nxt);
+    const int b = cur.b, kvh = cur.kvh, c = cur.c, c0 = cur.c0, c1 = cur.c1;
+    const char* kb = base_of(a.k, cur);
+    const char* vb = base_of(a.v, cur);
 
     f32x4 o[DB];
 #pragma unroll
     for (int db = 0; db < DB; ++db) o[db] = f32x4{0.f, 0.f, 0.f, 0.f};
     float m = kNegInf, l = 0.f;   // row n's running maximum (raw) and this lane's part of l
-    u32x4 kr[TT][KS], vr[TT][KS];
-    issue(kb, c0, kr);
     for (int T = c0; T < c1; T += STEP) {
-      issue(vb, T, vr);
+      issue(vb, T, c1, vr);
       float sc[TT][4];
 #pragma unroll
       for (int tt = 0; tt < TT; ++tt) {
+        // A operand of k-step s: dims 32s + 8 qd .. +8 of row n
+        to_lds(lk, kr[tt]);
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int s = 0; s < KS; ++s) acc = mfma_qk(kr[tt][s], qf[s], acc);
+        for (int s = 0; s < KS; ++s)
+          acc = mfma_qk(*reinterpret_cast<const u32x4*>(lk + n * LSTR + 64 * s + 16 * qd), qf[s],
+                        acc);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int pos = T + 16 * tt + 4 * qd + e;
           sc[tt][e] = (pos < c1 && pos <= lim) ? acc[e] : kNegInf;
         }
       }
-      if (T + STEP < c1) issue(kb, T + STEP, kr);
+      if (T + STEP < c1) {
+        issue(kb, T + STEP, c1, kr);
+      } else if (has_next) {
+        load_q(nxt);
+        issue(base_of(a.k, nxt), nxt.c0, nxt.c1, kr);
+      }
 
       float bm = kNegInf;
 #pragma unroll
@@ -173,19 +226,14 @@ void multi_kernel(MultiArgs a) {
         }
         u32x2 ph, pl;
         split_bf16(p, ph, pl);
-        // V tile through LDS: row n of the tile, then four positions of one
-        // dim per lane (this wave's region; LDS keeps the wave's order)
-#pragma unroll
-        for (int s = 0; s < KS; ++s)
-          *reinterpret_cast<u32x4*>(lv + n * LSTR + (D / 2) * qd + 16 * s) = vr[tt][s];
+        // V tile through LDS, read back as four positions of one dim per
+        // lane (this wave's region; LDS keeps the wave's order)
+        to_lds(lv, vr[tt]);
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
-          const uint16_t* col = reinterpret_cast<const uint16_t*>(lv + (16 * db + n) * 2);
-          const uint32_t x0 = (uint32_t)col[(4 * qd + 0) * (LSTR / 2)] |
-                              ((uint32_t)col[(4 * qd + 1) * (LSTR / 2)] << 16);
-          const uint32_t x1 = (uint32_t)col[(4 * qd + 2) * (LSTR / 2)] |
-                              ((uint32_t)col[(4 * qd + 3) * (LSTR / 2)] << 16);
-          const u32x2 vv = {x0, x1};
+          const u32x2 vv = __builtin_bit_cast(
+              u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                         (__attribute__((address_space(3))) s16x4_t*)(lv + tr_off + 32 * db)));
           o[db] = mfma_pv(ph, vv, o[db]);
           o[db] = mfma_pv(pl, vv, o[db]);
         }
@@ -211,6 +259,9 @@ void multi_kernel(MultiArgs a) {
       *reinterpret_cast<f32x2*>(a.ml_part + prow * 2) =
           f32x2{(m == kNegInf) ? kNegInf : m * c_log2, l};
     }
+    if (!has_next) break;
+    cur = nxt;
+    u = un;
   }
 }
 
