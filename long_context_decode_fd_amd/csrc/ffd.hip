@@ -11,9 +11,11 @@
 //   1. Scan.  4 lanes per position (one 32-dim quantisation group each) read
 //      8 B of codes and 4 B of (zero, step).  Codes become exact bf16 values
 //      4 + c (a rotate and an and-or per pair, since bf16 4..7 differ only in
-//      two mantissa bits) and meet the bf16 query in v_dot2c_f32_bf16;
-//      sum q_i c_i = dot - 4 sum q_i.  The scan score and the G-bit candidate
-//      mask of every position stay in LDS (no write-back).
+//      two mantissa bits); sum q_i c_i = sum q_i (4 + c_i) - 4 sum q_i.  At
+//      d = 128 with G = 4 or 8 the products run on the matrix cores (the
+//      groups of 4 heads stacked block-diagonally in one 16x16x32 tile), else
+//      in v_dot2c_f32_bf16.  The scan score and the G-bit candidate mask of
+//      every position stay in LDS (no write-back).
 //   2. Compaction of the positions that are a candidate for any head of the
 //      group (they share the residual and V loads).
 //   3. Refine + attend over the compacted list, 16 lanes per row: residual
@@ -38,6 +40,10 @@ namespace fdk {
 #ifndef FD_FFD_NB
 #define FD_FFD_NB 8
 #endif
+#ifndef FD_FFD_MFMA_TILES
+#define FD_FFD_MFMA_TILES 8
+#endif
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 
 // Dynamic LDS of the FFD kernel for a chunk of `chunk` positions: scan
 // scores [chunk][G] (fp32), candidate masks [chunk] (u8), candidate list
@@ -259,7 +265,89 @@ __global__ __launch_bounds__(kThreads) void ffd_kernel(FfdArgs a) {
   }
 
   // ---- 1. 2-bit scan of the chunk: scores and candidate masks into LDS ----
-  {
+  if constexpr (D == 128 && (G == 4 || G == 8)) {
+    // On the matrix cores.  For each 16-row tile of heads 4*tt .. 4*tt+3 the
+    // four quantisation groups are stacked block-diagonally: row i = 4g + e
+    // is (group g, head 4*tt + e), and k-step t of v_mfma_f32_16x16x32_bf16
+    // gives lane quad g the 8 dims 32g + 8t .. +8 of group g.  A = query
+    // (zero outside the row's own group), B = codes of 16 positions as exact
+    // bf16 4 + c, so C[(g, h)][pos] = sum over group g of q_h,i (4 + c_i).
+    // Lane (pos n16, quad g) loads that position's codes and (zero, step) of
+    // group g and receives C for exactly that group: one fma per head gives
+    // the group's part of the score, two shuffles sum the four groups.
+    constexpr int NT = G / 4;
+    constexpr int TB = FD_FFD_MFMA_TILES;     // 16-position tiles per load round
+    const int n16 = lane & 15, qg = lane >> 4;
+    u32x4 qa[NT][4];
+    float qsum[NT][4];
+#pragma unroll
+    for (int tt = 0; tt < NT; ++tt) {
+      const uint16_t* qrow = a.q + (hq0 + 4 * tt + (n16 & 3)) * D + 32 * qg;
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+        qa[tt][t] = (n16 >> 2) == qg ? ld16(qrow + 8 * t) : u32x4{0, 0, 0, 0};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint16_t* qh = a.q + (hq0 + 4 * tt + e) * D + 32 * qg;
+        float sum = 0.f;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const u32x4 w = ld16(qh + 8 * t);
+          sum += (bf16_lo(w.x) + bf16_hi(w.x)) + (bf16_lo(w.y) + bf16_hi(w.y)) +
+                 (bf16_lo(w.z) + bf16_hi(w.z)) + (bf16_lo(w.w) + bf16_hi(w.w));
+        }
+        qsum[tt][e] = sum;
+      }
+    }
+    for (int p0 = wave * 16 * TB; p0 < n; p0 += kWaves * 16 * TB) {
+      u32x2 cw[TB];
+      uint32_t zz[TB];
+#pragma unroll
+      for (int bt = 0; bt < TB; ++bt) {
+        const int jr = min(p0 + 16 * bt + n16, n - 1);
+        const size_t row = rbase + c0 + jr;
+        cw[bt] = ffd_load(reinterpret_cast<const u32x2*>(codes + row * CW + 2 * qg));
+        zz[bt] = ffd_load(reinterpret_cast<const uint32_t*>(zs + (row * NG + qg) * 2));
+      }
+#pragma unroll
+      for (int bt = 0; bt < TB; ++bt) {
+        const int jr = p0 + 16 * bt + n16;
+        u32x4 bk[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const uint32_t w = t < 2 ? cw[bt].x : cw[bt].y;
+          const int pb = 4 * (t & 1);
+          bk[t] = u32x4{code_pair(w, pb), code_pair(w, pb + 1), code_pair(w, pb + 2),
+                        code_pair(w, pb + 3)};
+        }
+        const float z = half_to_float(zz[bt] & 0xFFFF), st = half_to_float(zz[bt] >> 16);
+        const float zb = fmaf(-4.f, st, z);
+        uint32_t bits = 0;
+#pragma unroll
+        for (int tt = 0; tt < NT; ++tt) {
+          f32x4 cc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int t = 0; t < 4; ++t)
+            cc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                __builtin_bit_cast(bf16x8_t, qa[tt][t]), __builtin_bit_cast(bf16x8_t, bk[t]),
+                cc, 0, 0, 0);
+          float sc[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            sc[e] = fmaf(zb, qsum[tt][e], st * cc[e]);
+            sc[e] += __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(sc[e]), 0x401F));
+            sc[e] += __shfl_xor(sc[e], 32);
+            const int h = 4 * tt + e;
+            const bool cand = (sc[e] >= thr[h]) || (c0 + jr == jst[h]);
+            bits |= cand ? (1u << h) : 0u;
+          }
+          if (qg == 0 && jr < n)
+            *reinterpret_cast<f32x4*>(&s_scan[jr][4 * tt]) = f32x4{sc[0], sc[1], sc[2], sc[3]};
+        }
+        if (qg == 0 && jr < n) s_mask[jr] = (uint8_t)bits;
+      }
+    }
+  } else {
     const int gi = lane % NG, tk = lane / NG;
     u32x4 qs[G][4];
     float qg[G];
