@@ -18,9 +18,12 @@
 //      every position stay in LDS (no write-back).
 //   2. Compaction of the positions that are a candidate for any head of the
 //      group (they share the residual and V loads).
-//   3. Refine + attend over the compacted list, 16 lanes per row: residual
-//      bytes become exact bf16 (r + 128) for dot2, V rows stream as in the
-//      dense kernel, each head's softmax covers only its own candidates.
+//   3. Refine + attend over the compacted list: residual bytes become exact
+//      bf16 (r + 128); each head's softmax covers only its own candidates.
+//      At d = 128 with G = 4 or 8 on the matrix cores, 16 candidates per
+//      tile (refinement in the scan's group-stacked tile, P V with the
+//      candidates' V rows read back transposed from LDS); else 16 lanes per
+//      row with dot2 and V rows streamed as in the dense kernel.
 //   4. Row slots and waves merge into one partial per query head; the
 //      chunks merge in the common log-sum-exp kernel.
 #include "internal.hpp"
@@ -44,6 +47,7 @@ namespace fdk {
 #define FD_FFD_MFMA_TILES 8
 #endif
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
 
 // Dynamic LDS of the FFD kernel for a chunk of `chunk` positions: scan
 // scores [chunk][G] (fp32), candidate masks [chunk] (u8), candidate list
@@ -210,6 +214,60 @@ __global__ __launch_bounds__(kThreads) void ffd_anchor_kernel(FfdArgs a) {
 }
 
 
+// Query operand of the group-stacked tiles (d = 128): for tile tt (heads
+// 4*tt .. 4*tt+3), lane (row i = lane % 16, quad g = lane / 16) at k-step t
+// holds q[head 4*tt + i % 4][dims 32g + 8t .. +8] if row i belongs to group
+// g (i / 4 == g), zeros otherwise; qsum[tt][e] = sum of q over group g for
+// head 4*tt + e.  q points at head 0 of the kv-group.
+template <int G>
+__device__ __forceinline__ void stacked_query(const uint16_t* q, int lane, u32x4 (&qa)[G / 4][4],
+                                              float (&qsum)[G / 4][4]) {
+  constexpr int D = 128;
+  const int n16 = lane & 15, qg = lane >> 4;
+#pragma unroll
+  for (int tt = 0; tt < G / 4; ++tt) {
+    const uint16_t* qrow = q + (4 * tt + (n16 & 3)) * D + 32 * qg;
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+      qa[tt][t] = (n16 >> 2) == qg ? ld16(qrow + 8 * t) : u32x4{0, 0, 0, 0};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const uint16_t* qh = q + (4 * tt + e) * D + 32 * qg;
+      float sum = 0.f;
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const u32x4 w = ld16(qh + 8 * t);
+        sum += (bf16_lo(w.x) + bf16_hi(w.x)) + (bf16_lo(w.y) + bf16_hi(w.y)) +
+               (bf16_lo(w.z) + bf16_hi(w.z)) + (bf16_lo(w.w) + bf16_hi(w.w));
+      }
+      qsum[tt][e] = sum;
+    }
+  }
+}
+
+__device__ __forceinline__ f32x4 mfma_16x16x32(const u32x4& a, const u32x4& b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                  __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x4 mfma_16x16x16(const u32x2& a, const u32x2& b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4_t, a),
+                                                    __builtin_bit_cast(s16x4_t, b), c, 0, 0, 0);
+}
+
+// Four residual bytes (dims in byte order) -> two bf16 pairs of r + 128, exact.
+__device__ __forceinline__ u32x2 residual_pairs(uint32_t w) {
+  const uint32_t u = w ^ 0x80808080u;
+  return u32x2{pack_bf16_exact((float)(u & 0xFF), (float)((u >> 8) & 0xFF)),
+               pack_bf16_exact((float)((u >> 16) & 0xFF), (float)(u >> 24))};
+}
+
+// fp32 -> bf16 bits, round to nearest even (finite inputs); p = hi + lo.
+__device__ __forceinline__ uint32_t ffd_bf16_bits(float x) {
+  const uint32_t u = __float_as_uint(x);
+  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
 template <int D, int G>
 __global__ __launch_bounds__(kThreads) void ffd_kernel(FfdArgs a) {
   using Gm = Geo<uint16_t, D>;
@@ -280,25 +338,7 @@ __global__ __launch_bounds__(kThreads) void ffd_kernel(FfdArgs a) {
     const int n16 = lane & 15, qg = lane >> 4;
     u32x4 qa[NT][4];
     float qsum[NT][4];
-#pragma unroll
-    for (int tt = 0; tt < NT; ++tt) {
-      const uint16_t* qrow = a.q + (hq0 + 4 * tt + (n16 & 3)) * D + 32 * qg;
-#pragma unroll
-      for (int t = 0; t < 4; ++t)
-        qa[tt][t] = (n16 >> 2) == qg ? ld16(qrow + 8 * t) : u32x4{0, 0, 0, 0};
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const uint16_t* qh = a.q + (hq0 + 4 * tt + e) * D + 32 * qg;
-        float sum = 0.f;
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          const u32x4 w = ld16(qh + 8 * t);
-          sum += (bf16_lo(w.x) + bf16_hi(w.x)) + (bf16_lo(w.y) + bf16_hi(w.y)) +
-                 (bf16_lo(w.z) + bf16_hi(w.z)) + (bf16_lo(w.w) + bf16_hi(w.w));
-        }
-        qsum[tt][e] = sum;
-      }
-    }
+    stacked_query<G>(a.q + hq0 * D, lane, qa, qsum);
     for (int p0 = wave * 16 * TB; p0 < n; p0 += kWaves * 16 * TB) {
       u32x2 cw[TB];
       uint32_t zz[TB];
@@ -328,9 +368,7 @@ __global__ __launch_bounds__(kThreads) void ffd_kernel(FfdArgs a) {
           f32x4 cc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
           for (int t = 0; t < 4; ++t)
-            cc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                __builtin_bit_cast(bf16x8_t, qa[tt][t]), __builtin_bit_cast(bf16x8_t, bk[t]),
-                cc, 0, 0, 0);
+            cc = mfma_16x16x32(qa[tt][t], bk[t], cc);
           float sc[4];
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
@@ -446,6 +484,175 @@ __global__ __launch_bounds__(kThreads) void ffd_kernel(FfdArgs a) {
   }
 
   // ---- 3. refine + exact attention over the candidates ----
+  if constexpr (D == 128 && (G == 4 || G == 8)) {
+    // On the matrix cores, 16 candidates per tile (a wave takes tiles
+    // wave, wave + 4, ...):
+    //   residual: the same group-stacked tile as the scan, B = residual bytes
+    //     as exact bf16 r + 128: C[(g, h)][cand] = sum_g q_h,i (r_i + 128),
+    //     so the refinement is rs_g (C - 128 qsum_h,g), summed over g;
+    //   softmax per head across the tile's 16 lanes (DPP), p in fp32;
+    //   P V: p staged in LDS as [head][candidate] and read back as the A
+    //     operand of v_mfma_f32_16x16x16_bf16 (rows = heads, split bf16
+    //     hi + lo for fp32-level accuracy), V rows through an LDS tile read
+    //     back transposed (ds_read_b64_tr_b16) as the B operand.
+    constexpr int NT = G / 4;
+    constexpr int VSTR = 2 * D + 8;   // LDS row stride of the V tile
+    __shared__ __align__(16) unsigned char s_vt[kWaves][16 * VSTR];
+    __shared__ __align__(16) float s_pb[kWaves][G][16];
+    const int n16 = lane & 15, qg = lane >> 4;
+    u32x4 qa[NT][4];
+    float qsum[NT][4];
+    stacked_query<G>(a.q + hq0 * D, lane, qa, qsum);
+    unsigned char* lv = s_vt[wave];
+    const int tr_off = (4 * qg + (n16 >> 2)) * VSTR + 8 * (n16 & 3);
+    f32x4 o[D / 16];
+#pragma unroll
+    for (int db = 0; db < D / 16; ++db) o[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float mh[G], lh[G];   // raw running maximum per head; this lane's part of l
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      mh[h] = kNegInf;
+      lh[h] = 0.f;
+    }
+    for (int t0 = wave * 16; t0 < nu; t0 += kWaves * 16) {
+      const int jn = t0 + n16;                      // this lane's candidate slot
+      const int jr = s_list[min(jn, nu - 1)];
+      const size_t row = rbase + c0 + jr;
+      const u32x4 r0 = ffd_load(reinterpret_cast<const u32x4*>(res + row * D + 32 * qg));
+      const u32x4 r1 = ffd_load(reinterpret_cast<const u32x4*>(res + row * D + 32 * qg + 16));
+      const float rsf = half_to_float(rsa[row * NG + qg]);
+      u32x4 vr[4];   // V rows of tile slots 4i + qg, 16 bytes at 16 * n16
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int jv = s_list[min(t0 + 4 * i + qg, nu - 1)];
+        vr[i] = ffd_load(reinterpret_cast<const u32x4*>(vb + (size_t)(c0 + jv) * Gm::kRow +
+                                                        16 * n16));
+      }
+      const uint32_t mk = s_mask[jr];
+      const bool valid = jn < nu;
+      u32x4 bk[4];
+      {
+        const uint32_t w[8] = {r0.x, r0.y, r0.z, r0.w, r1.x, r1.y, r1.z, r1.w};
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const u32x2 lo = residual_pairs(w[2 * t]), hi = residual_pairs(w[2 * t + 1]);
+          bk[t] = u32x4{lo.x, lo.y, hi.x, hi.y};
+        }
+      }
+      float sh[G];   // refined raw scores of this lane's candidate
+#pragma unroll
+      for (int tt = 0; tt < NT; ++tt) {
+        f32x4 cc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int t = 0; t < 4; ++t) cc = mfma_16x16x32(qa[tt][t], bk[t], cc);
+        const f32x4 sv = *reinterpret_cast<const f32x4*>(&s_scan[jr][4 * tt]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          float corr = rsf * fmaf(-128.f, qsum[tt][e], cc[e]);
+          corr += __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(corr), 0x401F));
+          corr += __shfl_xor(corr, 32);
+          const int h = 4 * tt + e;
+          sh[h] = (valid && ((mk >> h) & 1u)) ? sv[e] + corr : kNegInf;
+        }
+      }
+      // online softmax per head over the tile (all lanes of a 16-lane row
+      // hold the same candidate set, every quad the same values)
+      bool grow = false;
+      float alpha[G];
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        const float mn = fmaxf(mh[h], group_max<16>(sh[h]));
+        alpha[h] = (mn == mh[h]) ? 1.f : exp2_hw((mh[h] - mn) * a.c_log2);
+        grow |= mn > mh[h];
+        mh[h] = mn;
+      }
+      if (__any(grow)) {
+#pragma unroll
+        for (int h = 0; h < G; ++h) lh[h] *= alpha[h];
+        // O row 4*qg + e is head 4*qg + e (rows >= G are padding)
+        float ae[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          ae[e] = 1.f;
+#pragma unroll
+          for (int h = e; h < G; h += 4) ae[e] = (h == 4 * qg + e) ? alpha[h] : ae[e];
+        }
+#pragma unroll
+        for (int db = 0; db < D / 16; ++db)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) o[db][e] *= ae[e];
+      }
+      float* pb = &s_pb[wave][0][0];
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        const float bias = (mh[h] == kNegInf) ? 0.f : mh[h] * a.c_log2;
+        const float p = exp2_hw(fmaf(sh[h], a.c_log2, -bias));
+        lh[h] += p;
+        if ((h & 3) == qg) pb[h * 16 + n16] = p;
+      }
+      // A operand: lane (head row n16, quad q) takes p[n16][4q .. 4q+3]
+      u32x2 ph = {0u, 0u}, pl = {0u, 0u};
+      if (n16 < G) {
+        const f32x4 pv = *reinterpret_cast<const f32x4*>(pb + n16 * 16 + 4 * qg);
+        uint32_t hb[4], lb[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          hb[e] = ffd_bf16_bits(pv[e]);
+          lb[e] = ffd_bf16_bits(pv[e] - __uint_as_float(hb[e] << 16));
+        }
+        ph = u32x2{hb[0] | (hb[1] << 16), hb[2] | (hb[3] << 16)};
+        pl = u32x2{lb[0] | (lb[1] << 16), lb[2] | (lb[3] << 16)};
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        *reinterpret_cast<u32x4*>(lv + (4 * i + qg) * VSTR + 16 * n16) = vr[i];
+#pragma unroll
+      for (int db = 0; db < D / 16; ++db) {
+        const u32x2 vv = __builtin_bit_cast(
+            u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                       (__attribute__((address_space(3))) s16x4_t*)(lv + tr_off + 32 * db)));
+        o[db] = mfma_16x16x16(ph, vv, o[db]);
+        o[db] = mfma_16x16x16(pl, vv, o[db]);
+      }
+    }
+    // ---- 4. waves merge into one partial per query head ----
+#pragma unroll
+    for (int h = 0; h < G; ++h) lh[h] = group_sum<16>(lh[h]);
+#pragma unroll
+    for (int db = 0; db < D / 16; ++db)
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (4 * qg + e < G) s_cmb.acc[wave][4 * qg + e][16 * db + n16] = o[db][e];
+    if (lane == 0) {
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        s_cmb.ml[wave][h][0] = (mh[h] == kNegInf) ? kNegInf : mh[h] * a.c_log2;
+        s_cmb.ml[wave][h][1] = lh[h];
+      }
+    }
+    __syncthreads();
+    const size_t prow0 = hq0 * a.nc + c;
+    for (int idx = tid; idx < G * D; idx += kThreads) {
+      const int h = idx / D, dd = idx % D;
+      float M = kNegInf;
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) M = fmaxf(M, s_cmb.ml[w][h][0]);
+      float ov = 0.f, ls = 0.f;
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) {
+        const float wt = exp2_diff(s_cmb.ml[w][h][0], M);
+        ov = fmaf(wt, s_cmb.acc[w][h][dd], ov);
+        ls = fmaf(wt, s_cmb.ml[w][h][1], ls);
+      }
+      const size_t prow = prow0 + (size_t)h * a.nc;
+      a.o_part[prow * D + dd] = ov;
+      if (dd == 0) {
+        a.ml_part[prow * 2] = M;
+        a.ml_part[prow * 2 + 1] = ls;
+      }
+    }
+    return;
+  }
   float acc[G][VEC], m[G], l[G];
   state_reset<G, VEC>(acc, m, l);
   const int per = (((nu + kWaves - 1) / kWaves) + TPL - 1) / TPL * TPL;
