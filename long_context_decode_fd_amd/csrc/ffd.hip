@@ -151,33 +151,46 @@ __global__ __launch_bounds__(kThreads) void ffd_anchor_kernel(FfdArgs a) {
   int bidx[G];
 #pragma unroll
   for (int h = 0; h < G; ++h) { best[h] = kNegInf; bidx[h] = 0x7fffffff; }
-  for (int k0 = wave * TPL; k0 < na; k0 += kWaves * TPL) {
-    const int k = min(k0 + grp, na - 1);
-    const int pos = k < n_sk ? k : loc0 + (k - n_sk);
-    const size_t row = rbase + pos;
-    const int gi = col / 4;  // 8 dims per lane, 4 lanes per group
-    const uint32_t w = codes[row * CW + col / 2];
-    const uint32_t zsb = *reinterpret_cast<const uint32_t*>(zs + (row * NG + gi) * 2);
-    const float z = half_to_float(zsb & 0xFFFF), st = half_to_float(zsb >> 16);
-    const u32x2 rr = *reinterpret_cast<const u32x2*>(res + row * D + col * 8);
-    const float rsf = half_to_float(rsa[row * NG + gi]);
-    float corr[G];
-    residual_dot<G>(rr, rsf, qr, ql, corr);
-    const int p0 = 4 * (col & 1);
-    const uint32_t k0p = code_pair(w, p0), k1p = code_pair(w, p0 + 1);
-    const uint32_t k2p = code_pair(w, p0 + 2), k3p = code_pair(w, p0 + 3);
-    const bool valid = k0 + grp < na;
+  // All loads of up to NIT rounds (kWaves * TPL anchors each) are issued
+  // before any arithmetic: one memory latency instead of one per round.
+  constexpr int NIT = 8;
+  const int gi = col / 4;  // 8 dims per lane, 4 lanes per group
+  for (int kb = 0; kb < na; kb += kWaves * TPL * NIT) {
+    uint32_t w[NIT], zsb[NIT];
+    u32x2 rr[NIT];
+    uint32_t rsb[NIT];
+    int pos[NIT];
 #pragma unroll
-    for (int h = 0; h < G; ++h) {
-      float x = dot2_bf16(qr[h].x, k0p, 0.f);
-      float y = dot2_bf16(qr[h].y, k1p, 0.f);
-      x = dot2_bf16(qr[h].z, k2p, x);
-      y = dot2_bf16(qr[h].w, k3p, y);
-      const float part = fmaf(fmaf(-4.f, st, z), ql[h], st * (x + y)) + corr[h];
-      const float sc = group_sum<LPT>(part);
-      if (valid && (sc > best[h] || (sc == best[h] && pos < bidx[h]))) {
-        best[h] = sc;
-        bidx[h] = pos;
+    for (int it = 0; it < NIT; ++it) {
+      const int k = min(kb + (it * kWaves + wave) * TPL + grp, na - 1);
+      pos[it] = k < n_sk ? k : loc0 + (k - n_sk);
+      const size_t row = rbase + pos[it];
+      w[it] = codes[row * CW + col / 2];
+      zsb[it] = *reinterpret_cast<const uint32_t*>(zs + (row * NG + gi) * 2);
+      rr[it] = *reinterpret_cast<const u32x2*>(res + row * D + col * 8);
+      rsb[it] = rsa[row * NG + gi];
+    }
+#pragma unroll
+    for (int it = 0; it < NIT; ++it) {
+      const bool valid = kb + (it * kWaves + wave) * TPL + grp < na;
+      const float z = half_to_float(zsb[it] & 0xFFFF), st = half_to_float(zsb[it] >> 16);
+      float corr[G];
+      residual_dot<G>(rr[it], half_to_float(rsb[it]), qr, ql, corr);
+      const int p0 = 4 * (col & 1);
+      const uint32_t k0p = code_pair(w[it], p0), k1p = code_pair(w[it], p0 + 1);
+      const uint32_t k2p = code_pair(w[it], p0 + 2), k3p = code_pair(w[it], p0 + 3);
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        float x = dot2_bf16(qr[h].x, k0p, 0.f);
+        float y = dot2_bf16(qr[h].y, k1p, 0.f);
+        x = dot2_bf16(qr[h].z, k2p, x);
+        y = dot2_bf16(qr[h].w, k3p, y);
+        const float part = fmaf(fmaf(-4.f, st, z), ql[h], st * (x + y)) + corr[h];
+        const float sc = group_sum<LPT>(part);
+        if (valid && (sc > best[h] || (sc == best[h] && pos[it] < bidx[h]))) {
+          best[h] = sc;
+          bidx[h] = pos[it];
+        }
       }
     }
   }
