@@ -32,7 +32,7 @@ constexpr int kThreads = kWaves * kWave;
 #define FD_NB_FIXED FD_NB
 #endif
 #ifndef FD_NB_PAGED
-#define FD_NB_PAGED 8      // page-id lookups per row: shallower batches measured faster
+#define FD_NB_PAGED FD_NB
 #endif
 template <int G, int NBMAX = FD_NB>
 constexpr int batch_rows() { return G >= 8 ? (NBMAX > 8 ? 8 : NBMAX) : NBMAX; }
