@@ -232,6 +232,35 @@ def cpu_baseline(torch, case, target_s):
                 host_cpus=len(os.sched_getaffinity(0)))
 
 
+def variant_dense_128k(torch, fd, W, args, timer):
+    """Dense GQA decode at the long end of the 32K-128K range: B 2, L 131072
+    (the same 1.07 GB of KV as the headline), chunk 512."""
+    B, Hq, Hkv, L, d, chunk = 2, 32, 8, 131072, 128, 512
+    c = W.dense_case(B, Hq, Hkv, L, d, "bf16", chunk, seed=1202, device="cuda:0")
+    ks = [c.k] + [c.k.clone() for _ in range(args.copies - 1)]
+    vs = [c.v] + [c.v.clone() for _ in range(args.copies - 1)]
+    lib = fd.lib()
+    out = torch.empty((B, Hq, d), dtype=torch.float32, device="cuda:0")
+    lse = torch.empty((B, Hq), dtype=torch.float32, device="cuda:0")
+    wsn = fd.workspace_bytes("fd_decode_attn", B=B, Hq=Hq, Hkv=Hkv, L=L, d=d, chunk=chunk)
+    ws = torch.empty(wsn, dtype=torch.uint8, device="cuda:0")
+    size = C.c_size_t(wsn)
+    st = C.c_void_p(torch.cuda.current_stream().cuda_stream)
+    calls = []
+    for k, v in zip(ks, vs):
+        a = (fd.FD_BF16, vp(c.q), vp(k), vp(v), vp(out), vp(lse), B, Hq, Hkv, L, d, c.scale,
+             chunk, vp(ws), C.byref(size), st)
+        calls.append(lambda a=a: lib.fd_decode_attn(*a))
+    check_rc(lib, calls[0]())
+    t = timer.run(calls, args.steps, args.warmup)
+    nbytes = 2 * B * Hkv * L * d * 2 + B * Hq * d * 2 + B * Hq * (d + 1) * 4
+    return dict(workload=f"dense GQA decode bf16, B={B}, Hq={Hq}, Hkv={Hkv}, d={d}, L={L}, "
+                         f"chunk={chunk}", us_per_step=round(t["ms"] * 1e3, 2),
+                p10_us=round(t["p10"] * 1e3, 2), p90_us=round(t["p90"] * 1e3, 2), bytes=nbytes,
+                gbs=round(gbs(nbytes, t["ms"]), 1),
+                pct_of_peak=round(100 * gbs(nbytes, t["ms"]) / PEAK_GBS, 1))
+
+
 def variant_multi(torch, fd, W, args, timer):
     """Multi-row decode on the headline shape (B 8, Hq 32, Hkv 8, d 128,
     L 32768, chunk 512) with M = 2 and 4 new tokens per sequence (G*M = 8
@@ -564,6 +593,7 @@ def main():
     }
     if not args.no_variants:
         line["variants"] = {
+            "dense_128k": variant_dense_128k(torch, fd, W, args, timer),
             "paged": variant_paged(torch, fd, W, args, timer),
             "unified_max": variant_unified(torch, fd, W, args, timer),
             "ffd": variant_ffd(torch, fd, W, args, timer),

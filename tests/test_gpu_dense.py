@@ -105,6 +105,21 @@ def test_config2_full_size_sampled():
     assert torch.isfinite(out).all()
 
 
+def test_dense_128k_sampled():
+    """The long end of the 32K-128K range: B 2, L 131072, chunk 512."""
+    banner("dense 128K sampled")
+    c = W.dense_case(2, 32, 8, 131072, 128, "bf16", 512, seed=1202, device=DEV)
+    out, lse = fd.decode_attn(c.q, c.k, c.v, chunk=c.chunk)
+    torch.cuda.synchronize()
+    G = 4
+    for b, h in [(0, 0), (0, 17), (1, 9), (1, 31)]:
+        r, lr = ofd.attention_row(f64(c.q[b, h]), f64(c.k[b, h // G]), f64(c.v[b, h // G]),
+                                  c.scale)
+        assert max_err(f64(out[b, h]), r) <= 2e-3
+        assert abs(float(lse[b, h]) - lr) <= 2e-3
+    assert torch.isfinite(out).all()
+
+
 def test_partials_then_merge_equals_full_call():
     c = W.dense_case(2, 16, 4, 3000, 128, "bf16", 256, seed=41, device=DEV)
     out, lse = fd.decode_attn(c.q, c.k, c.v, chunk=256)
