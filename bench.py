@@ -263,11 +263,11 @@ def variant_dense_128k(torch, fd, W, args, timer):
 
 def variant_multi(torch, fd, W, args, timer):
     """Multi-row decode on the headline shape (B 8, Hq 32, Hkv 8, d 128,
-    L 32768, chunk 512) with M = 2 and 4 new tokens per sequence (G*M = 8
-    and 16 query rows per kv-head, matrix-core kernel), beside M separate
+    L 32768, chunk 512) with M = 2, 4 and 8 new tokens per sequence (G*M = 8,
+    16 and 32 query rows per kv-head, matrix-core kernel), beside M separate
     single-query calls on the same cache."""
     B, Hq, Hkv, L, d, chunk = 8, 32, 8, 32768, 128, 512
-    base = W.multi_case(B, 4, Hq, Hkv, L, d, chunk=chunk, seed=102, device="cuda:0")
+    base = W.multi_case(B, 8, Hq, Hkv, L, d, chunk=chunk, seed=102, device="cuda:0")
     ks = [base.k] + [base.k.clone() for _ in range(args.copies - 1)]
     vs = [base.v] + [base.v.clone() for _ in range(args.copies - 1)]
     lib = fd.lib()
@@ -276,7 +276,7 @@ def variant_multi(torch, fd, W, args, timer):
     res = dict(workload=f"multi-row decode bf16, B={B}, Hq={Hq}, Hkv={Hkv}, d={d}, L={L}, "
                         f"chunk={chunk}, token r sees positions 0..L-M+r")
     t_single = None
-    for M in (1, 2, 4):
+    for M in (1, 2, 4, 8):
         q = base.q[:, :M].contiguous()
         out = torch.empty((B, M, Hq, d), dtype=torch.float32, device="cuda:0")
         lse = torch.empty((B, M, Hq), dtype=torch.float32, device="cuda:0")

@@ -167,7 +167,7 @@ int fd_decode_attn_unified_max(fd_dtype_t dt, const void* q, const void* k,
  * single-query kernel of fd_decode_attn.
  *   q     [B, M, Hq, d]; k, v [B, Hkv, L, d]; L >= M
  *   out   fp32 [B, M, Hq, d];  lse fp32 [B, M, Hq] or NULL
- *   M = 1: dt bf16 or fp32.  M >= 2: bf16 only and G*M <= 16, else
+ *   M = 1: dt bf16 or fp32.  M >= 2: bf16 only and G*M <= 32, else
  *   FD_ERR_UNSUPPORTED.  Workspace: chunk partials of the B*M*Hq rows
  *   (same layout as fd_decode_attn_partials with M*Hq heads).
  */

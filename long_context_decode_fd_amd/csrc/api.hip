@@ -253,8 +253,8 @@ int fd_decode_attn_multi(fd_dtype_t dt, const void* q, const void* k, const void
   if (int e = check_chunk(chunk)) return e;
   if (int e = check_scale(scale)) return e;
   const int G = Hq / Hkv;
-  if (M > 1 && G * M > 16)
-    return fail(FD_ERR_UNSUPPORTED, "G*M=%d query rows per kv-head exceed 16", G * M);
+  if (M > 1 && G * M > 32)
+    return fail(FD_ERR_UNSUPPORTED, "G*M=%d query rows per kv-head exceed 32", G * M);
   if (M > 1 && dt != FD_BF16)
     return fail(FD_ERR_UNSUPPORTED, "several query tokens need bf16 inputs");
   const int nc = (L + chunk - 1) / chunk;

@@ -2,7 +2,8 @@
 // each attending to the cache up to its own position ("Flash Decoding"
 // explainer, section 1; the tokens' keys and values are already appended at
 // positions L-M .. L-1).  The G query heads of a kv-head times the M tokens
-// give R = G*M <= 16 query rows that share every K and V row -- the flat
+// give R = G*M <= 32 query rows (one or two tiles of 16) that share every K
+// and V row -- the flat
 // GEMM case of the "FlashDecoding" deployment blog (section 1), which here
 // runs on the matrix cores:
 //
@@ -37,6 +38,7 @@ typedef short s16x4_t __attribute__((ext_vector_type(4)));
 #define FD_MR_TILES 2   // 16-position tiles per wave batch: 8 K and 8 V loads at d = 128
 #endif
 
+
 __device__ __forceinline__ f32x4 mfma_qk(const u32x4& a, const u32x4& b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
                                                   __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
@@ -66,7 +68,9 @@ __device__ __forceinline__ void split_bf16(const float (&p)[4], u32x2& hi, u32x2
   lo = u32x2{l[0] | (l[1] << 16), l[2] | (l[3] << 16)};
 }
 
-template <int D>
+// QT = query tiles of 16 rows (R = G*M <= 16 * QT); both share every K and V
+// tile.
+template <int D, int QT>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1)))
 void multi_kernel(MultiArgs a) {
   constexpr int KS = D / 32;             // QK k-steps (32 dims each)
@@ -110,21 +114,26 @@ void multi_kernel(MultiArgs a) {
   auto base_of = [&](const void* t, const UnitM& x) {
     return reinterpret_cast<const char*>(t) + ((size_t)x.b * a.Hkv + x.kvh) * (size_t)a.L * ROWB;
   };
-  // Query row n of this lane: token r = n / G, head kvh*G + n % G; its last
-  // visible position is L - M + r.  Rows n >= R are padding (q = 0).
-  const int r_n = n / G;
-  const int lim = a.L - a.M + r_n;
-  u32x4 qf[KS];
+  // Query row n + 16*qt of this lane: token r = row / G, head kvh*G + row % G;
+  // its last visible position is L - M + r.  Rows >= R are padding (q = 0).
+  int lim[QT];
+#pragma unroll
+  for (int qt = 0; qt < QT; ++qt) lim[qt] = a.L - a.M + (n + 16 * qt) / G;
+  u32x4 qf[QT][KS];
   auto load_q = [&](const UnitM& x) {
-    if (n < R) {
-      const uint16_t* qp = reinterpret_cast<const uint16_t*>(a.q) +
-                           (((size_t)x.b * a.M + r_n) * a.Hq + (size_t)x.kvh * G + n % G) * D +
-                           8 * qd;
 #pragma unroll
-      for (int s = 0; s < KS; ++s) qf[s] = ld16(qp + 32 * s);
-    } else {
+    for (int qt = 0; qt < QT; ++qt) {
+      const int row = n + 16 * qt;
+      if (row < R) {
+        const uint16_t* qp =
+            reinterpret_cast<const uint16_t*>(a.q) +
+            (((size_t)x.b * a.M + row / G) * a.Hq + (size_t)x.kvh * G + row % G) * D + 8 * qd;
 #pragma unroll
-      for (int s = 0; s < KS; ++s) qf[s] = u32x4{0, 0, 0, 0};
+        for (int s = 0; s < KS; ++s) qf[qt][s] = ld16(qp + 32 * s);
+      } else {
+#pragma unroll
+        for (int s = 0; s < KS; ++s) qf[qt][s] = u32x4{0, 0, 0, 0};
+      }
     }
   };
   // wave load i of tile tt: rows T + 16*tt + RPI*i + lrow, bytes 16*lcol
@@ -164,27 +173,38 @@ void multi_kernel(MultiArgs a) {
     const char* kb = base_of(a.k, cur);
     const char* vb = base_of(a.v, cur);
 
-    f32x4 o[DB];
+    f32x4 o[QT][DB];
+    float m[QT], l[QT];   // row's running maximum (raw) and this lane's part of l
 #pragma unroll
-    for (int db = 0; db < DB; ++db) o[db] = f32x4{0.f, 0.f, 0.f, 0.f};
-    float m = kNegInf, l = 0.f;   // row n's running maximum (raw) and this lane's part of l
+    for (int qt = 0; qt < QT; ++qt) {
+      m[qt] = kNegInf;
+      l[qt] = 0.f;
+#pragma unroll
+      for (int db = 0; db < DB; ++db) o[qt][db] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
     for (int T = c0; T < c1; T += STEP) {
       issue(vb, T, c1, vr);
-      float sc[TT][4];
+      float sc[QT][TT][4];
 #pragma unroll
       for (int tt = 0; tt < TT; ++tt) {
         // A operand of k-step s: dims 32s + 8 qd .. +8 of row n
         to_lds(lk, kr[tt]);
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        f32x4 acc[QT];
 #pragma unroll
-        for (int s = 0; s < KS; ++s)
-          acc = mfma_qk(*reinterpret_cast<const u32x4*>(lk + n * LSTR + 64 * s + 16 * qd), qf[s],
-                        acc);
+        for (int qt = 0; qt < QT; ++qt) acc[qt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int pos = T + 16 * tt + 4 * qd + e;
-          sc[tt][e] = (pos < c1 && pos <= lim) ? acc[e] : kNegInf;
+        for (int s = 0; s < KS; ++s) {
+          const u32x4 ka = *reinterpret_cast<const u32x4*>(lk + n * LSTR + 64 * s + 16 * qd);
+#pragma unroll
+          for (int qt = 0; qt < QT; ++qt) acc[qt] = mfma_qk(ka, qf[qt][s], acc[qt]);
         }
+#pragma unroll
+        for (int qt = 0; qt < QT; ++qt)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int pos = T + 16 * tt + 4 * qd + e;
+            sc[qt][tt][e] = (pos < c1 && pos <= lim[qt]) ? acc[qt][e] : kNegInf;
+          }
       }
       if (T + STEP < c1) {
         issue(kb, T + STEP, c1, kr);
@@ -193,39 +213,46 @@ void multi_kernel(MultiArgs a) {
         issue(base_of(a.k, nxt), nxt.c0, nxt.c1, kr);
       }
 
-      float bm = kNegInf;
+      float bias[QT];
 #pragma unroll
-      for (int tt = 0; tt < TT; ++tt)
+      for (int qt = 0; qt < QT; ++qt) {
+        float bm = kNegInf;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) bm = fmaxf(bm, sc[tt][e]);
-      bm = fmaxf(bm, __shfl_xor(bm, 16));
-      bm = fmaxf(bm, __shfl_xor(bm, 32));
-      const float mn = fmaxf(m, bm);
-      if (__any(mn > m)) {
-        const float alpha = (mn == m) ? 1.f : exp2_hw((m - mn) * c_log2);
-        l *= alpha;
-        // O rows 4*qd + e take the factors of those rows (held by lanes 4*qd + e)
-        float ae[4];
+        for (int tt = 0; tt < TT; ++tt)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) ae[e] = __shfl(alpha, 4 * qd + e);
+          for (int e = 0; e < 4; ++e) bm = fmaxf(bm, sc[qt][tt][e]);
+        bm = fmaxf(bm, __shfl_xor(bm, 16));
+        bm = fmaxf(bm, __shfl_xor(bm, 32));
+        const float mn = fmaxf(m[qt], bm);
+        if (__any(mn > m[qt])) {
+          const float alpha = (mn == m[qt]) ? 1.f : exp2_hw((m[qt] - mn) * c_log2);
+          l[qt] *= alpha;
+          // O rows 4*qd + e take the factors of those rows (held by lanes 4*qd + e)
+          float ae[4];
 #pragma unroll
-        for (int db = 0; db < DB; ++db)
+          for (int e = 0; e < 4; ++e) ae[e] = __shfl(alpha, 4 * qd + e);
 #pragma unroll
-          for (int e = 0; e < 4; ++e) o[db][e] *= ae[e];
-        m = mn;
+          for (int db = 0; db < DB; ++db)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) o[qt][db][e] *= ae[e];
+          m[qt] = mn;
+        }
+        bias[qt] = (m[qt] == kNegInf) ? 0.f : m[qt] * c_log2;
       }
-      const float bias = (m == kNegInf) ? 0.f : m * c_log2;
 
 #pragma unroll
       for (int tt = 0; tt < TT; ++tt) {
-        float p[4];
+        u32x2 ph[QT], pl[QT];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          p[e] = exp2_hw(fmaf(sc[tt][e], c_log2, -bias));
-          l += p[e];
+        for (int qt = 0; qt < QT; ++qt) {
+          float p[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            p[e] = exp2_hw(fmaf(sc[qt][tt][e], c_log2, -bias[qt]));
+            l[qt] += p[e];
+          }
+          split_bf16(p, ph[qt], pl[qt]);
         }
-        u32x2 ph, pl;
-        split_bf16(p, ph, pl);
         // V tile through LDS, read back as four positions of one dim per
         // lane (this wave's region; LDS keeps the wave's order)
         to_lds(lv, vr[tt]);
@@ -234,30 +261,38 @@ void multi_kernel(MultiArgs a) {
           const u32x2 vv = __builtin_bit_cast(
               u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
                          (__attribute__((address_space(3))) s16x4_t*)(lv + tr_off + 32 * db)));
-          o[db] = mfma_pv(ph, vv, o[db]);
-          o[db] = mfma_pv(pl, vv, o[db]);
+#pragma unroll
+          for (int qt = 0; qt < QT; ++qt) {
+            o[qt][db] = mfma_pv(ph[qt], vv, o[qt][db]);
+            o[qt][db] = mfma_pv(pl[qt], vv, o[qt][db]);
+          }
         }
       }
     }
 
-    // l of row n: the four lanes of the row hold parts
-    l += __shfl_xor(l, 16);
-    l += __shfl_xor(l, 32);
-    // partial rows ((b*M + r)*Hq + h)*nc + c
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int row = 4 * qd + e;
-      if (row < R) {
-        const size_t prow =
-            (((size_t)b * a.M + row / G) * a.Hq + (size_t)kvh * G + row % G) * a.nc + c;
+    for (int qt = 0; qt < QT; ++qt) {
+      // l of row n + 16*qt: the four lanes of the row hold parts
+      l[qt] += __shfl_xor(l[qt], 16);
+      l[qt] += __shfl_xor(l[qt], 32);
+      // partial rows ((b*M + r)*Hq + h)*nc + c
 #pragma unroll
-        for (int db = 0; db < DB; ++db) a.o_part[prow * D + 16 * db + n] = o[db][e];
+      for (int e = 0; e < 4; ++e) {
+        const int row = 16 * qt + 4 * qd + e;
+        if (row < R) {
+          const size_t prow =
+              (((size_t)b * a.M + row / G) * a.Hq + (size_t)kvh * G + row % G) * a.nc + c;
+#pragma unroll
+          for (int db = 0; db < DB; ++db) a.o_part[prow * D + 16 * db + n] = o[qt][db][e];
+        }
       }
-    }
-    if (qd == 0 && n < R) {
-      const size_t prow = (((size_t)b * a.M + r_n) * a.Hq + (size_t)kvh * G + n % G) * a.nc + c;
-      *reinterpret_cast<f32x2*>(a.ml_part + prow * 2) =
-          f32x2{(m == kNegInf) ? kNegInf : m * c_log2, l};
+      const int rown = n + 16 * qt;
+      if (qd == 0 && rown < R) {
+        const size_t prow =
+            (((size_t)b * a.M + rown / G) * a.Hq + (size_t)kvh * G + rown % G) * a.nc + c;
+        *reinterpret_cast<f32x2*>(a.ml_part + prow * 2) =
+            f32x2{(m[qt] == kNegInf) ? kNegInf : m[qt] * c_log2, l[qt]};
+      }
     }
     if (!has_next) break;
     cur = nxt;
@@ -275,9 +310,9 @@ static int multi_blocks_per_cu(K kernel) {
   return n;
 }
 
-template <int D>
+template <int D, int QT>
 static hipError_t launch_multi_d(const MultiArgs& a, hipStream_t s) {
-  auto kernel = multi_kernel<D>;
+  auto kernel = multi_kernel<D, QT>;
   static const int per_cu = multi_blocks_per_cu(kernel);
   int dev = 0, cus = 256;
   if (hipGetDevice(&dev) != hipSuccess ||
@@ -294,8 +329,9 @@ static hipError_t launch_multi_d(const MultiArgs& a, hipStream_t s) {
 }
 
 hipError_t launch_multi(int D, const MultiArgs& a, hipStream_t s) {
-  if (D == 64) return launch_multi_d<64>(a, s);
-  if (D == 128) return launch_multi_d<128>(a, s);
+  const bool two = (a.Hq / a.Hkv) * a.M > 16;
+  if (D == 64) return two ? launch_multi_d<64, 2>(a, s) : launch_multi_d<64, 1>(a, s);
+  if (D == 128) return two ? launch_multi_d<128, 2>(a, s) : launch_multi_d<128, 1>(a, s);
   return hipErrorInvalidValue;
 }
 

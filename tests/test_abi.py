@@ -125,7 +125,7 @@ def test_multi_row_validation_and_workspace():
     base = dict(B=2, M=4, Hq=8, Hkv=2, L=100, d=128, chunk=32)
     # partials of the B*M*Hq*n_chunks = 2*4*8*4 = 256 rows: O and (m, l)
     assert fd.workspace_bytes("fd_decode_attn_multi", **base) == 256 * 128 * 4 + 256 * 2 * 4
-    for bad, code in [(dict(M=8), _abi.FD_ERR_UNSUPPORTED),          # G*M = 32 rows
+    for bad, code in [(dict(M=9), _abi.FD_ERR_UNSUPPORTED),          # G*M = 36 rows
                       (dict(dt=_abi.FD_F32), _abi.FD_ERR_UNSUPPORTED),   # fp32 with M >= 2
                       (dict(M=0), _abi.FD_ERR_ARG), (dict(L=3), _abi.FD_ERR_ARG),
                       (dict(chunk=20), _abi.FD_ERR_ARG)]:

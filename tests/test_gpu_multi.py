@@ -30,7 +30,8 @@ def _check(c, chunk, rows=None):
 
 
 @pytest.mark.parametrize("d", [128, 64])
-@pytest.mark.parametrize("G,M", [(4, 4), (4, 2), (4, 3), (8, 2), (2, 8), (1, 16), (1, 5)])
+@pytest.mark.parametrize("G,M", [(4, 4), (4, 2), (4, 3), (8, 2), (2, 8), (1, 16), (1, 5),
+                                 (8, 4), (4, 8), (2, 12), (1, 20), (8, 3)])
 def test_multi_row_small(d, G, M):
     banner(f"multi d={d} G={G} M={M}")
     Hkv = 2
@@ -76,4 +77,13 @@ def test_multi_row_full_size_sampled():
     banner("multi full size B=8 L=32768 M=4")
     c = W.multi_case(8, 4, 32, 8, 32768, 128, seed=102, device=DEV)
     rows = [(0, 0, 0), (0, 3, 31), (3, 1, 17), (5, 2, 8), (7, 3, 30), (7, 0, 1)]
+    _check(c, chunk=512, rows=rows)
+
+
+def test_multi_row_two_query_tiles_full_size_sampled():
+    """Headline shape with eight new tokens per sequence (G*M = 32 rows: two
+    query tiles sharing every K and V tile)."""
+    banner("multi full size B=8 L=32768 M=8")
+    c = W.multi_case(8, 8, 32, 8, 32768, 128, seed=108, device=DEV)
+    rows = [(0, 0, 0), (0, 7, 31), (2, 4, 13), (6, 3, 22), (7, 7, 3), (7, 5, 30)]
     _check(c, chunk=512, rows=rows)
