@@ -376,7 +376,8 @@ void partial_kernel(PartialArgs a) {
 //   out = sum_i w_i O_i / sum_i w_i l_i,  lse = (M + log2 sum_i w_i l_i) ln 2.
 // One workgroup per (sequence, query head).  The weights of up to 256 chunks
 // at a time go to LDS; thread (chunk lane cl, column group cg) then sums
-// chunks cl, cl + CL, ... of 4 columns with independent 16-byte loads, and
+// chunks cl, cl + CL, ... of 4 columns with independent 16-byte loads (the
+// loads of the first 64 chunks are issued before the maximum is known), and
 // the chunk lanes are reduced through LDS.  The order of every sum is fixed,
 // so runs are bitwise reproducible.  Rows whose chunks all carry the same m
 // (the fixed-maximum path without fallback) get weights of exactly 1.
@@ -387,6 +388,7 @@ template <int D>
 __global__ __launch_bounds__(kMergeThreads) void merge_kernel(MergeArgs a) {
   constexpr int CG = D / 4;             // 16-byte column groups of a row
   constexpr int CL = kMergeThreads / CG;     // chunk lanes
+  constexpr int kPre = 64 / CL > 0 ? 64 / CL : 1;   // chunks of 64 loaded up front
   __shared__ float s_red[kMergeWaves];
   __shared__ float s_w[kMergeThreads];
   __shared__ f32x4 s_o[CL][CG];
@@ -404,11 +406,21 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(MergeArgs a) {
     if (tid == 0 && a.lse != nullptr) a.lse[row] = kNegInf;
     return;
   }
-  const float* ml = a.ml_part + row * a.nc * 2;
   const f32x4* op = reinterpret_cast<const f32x4*>(a.o_part + row * a.nc * D);
+  const f32x2* mlp = reinterpret_cast<const f32x2*>(a.ml_part + row * a.nc * 2);
 
-  float mx = kNegInf;
-  for (int c = tid; c < n; c += kMergeThreads) mx = fmaxf(mx, ml[2 * c]);
+  // Everything the first kPre * CL chunks need is requested before any
+  // arithmetic, so the (m, l) and O loads share one memory latency.
+  f32x4 pre[kPre];
+#pragma unroll
+  for (int j = 0; j < kPre; ++j) {
+    const int k = cl + j * CL;
+    pre[j] = k < n ? op[(size_t)k * CG + cg] : f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  const f32x2 ml0 = tid < n ? mlp[tid] : f32x2{kNegInf, 0.f};
+
+  float mx = ml0.x;
+  for (int c = tid + kMergeThreads; c < n; c += kMergeThreads) mx = fmaxf(mx, mlp[c].x);
   mx = wave_max(mx);
   if (lane == 0) s_red[w] = mx;
   __syncthreads();
@@ -420,14 +432,28 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(MergeArgs a) {
     const int c = c0 + tid;
     float wt = 0.f;
     if (c < n) {
-      wt = exp2_diff(ml[2 * c], M);
-      ls = fmaf(wt, ml[2 * c + 1], ls);
+      const f32x2 mlc = c0 == 0 ? ml0 : mlp[c];
+      wt = exp2_diff(mlc.x, M);
+      ls = fmaf(wt, mlc.y, ls);
     }
     __syncthreads();   // previous tile's s_w reads are done
     s_w[tid] = wt;
     __syncthreads();
     const int nt = min(kMergeThreads, n - c0);
-    for (int k = cl; k < nt; k += CL) {
+    int k = cl;
+    if (c0 == 0) {
+#pragma unroll
+      for (int j = 0; j < kPre; ++j, k += CL) {
+        if (k < nt) {
+          const float x = s_w[k];
+          acc.x = fmaf(x, pre[j].x, acc.x);
+          acc.y = fmaf(x, pre[j].y, acc.y);
+          acc.z = fmaf(x, pre[j].z, acc.z);
+          acc.w = fmaf(x, pre[j].w, acc.w);
+        }
+      }
+    }
+    for (; k < nt; k += CL) {
       const f32x4 o = op[(size_t)(c0 + k) * CG + cg];
       const float x = s_w[k];
       acc.x = fmaf(x, o.x, acc.x);
