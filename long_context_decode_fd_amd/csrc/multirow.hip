@@ -37,6 +37,12 @@ typedef short s16x4_t __attribute__((ext_vector_type(4)));
 #ifndef FD_MR_TILES
 #define FD_MR_TILES 2   // 16-position tiles per wave batch: 8 K and 8 V loads at d = 128
 #endif
+#ifndef FD_MR_WAVES_PER_EU
+#define FD_MR_WAVES_PER_EU 1
+#endif
+#ifndef FD_MR_HOLD
+#define FD_MR_HOLD 4    // finished units held in registers before their partials are written
+#endif
 
 
 __device__ __forceinline__ f32x4 mfma_qk(const u32x4& a, const u32x4& b, f32x4 c) {
@@ -71,7 +77,7 @@ __device__ __forceinline__ void split_bf16(const float (&p)[4], u32x2& hi, u32x2
 // QT = query tiles of 16 rows (R = G*M <= 16 * QT); both share every K and V
 // tile.
 template <int D, int QT>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1)))
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(FD_MR_WAVES_PER_EU)))
 void multi_kernel(MultiArgs a) {
   constexpr int KS = D / 32;             // QK k-steps (32 dims each)
   constexpr int DB = D / 16;             // 16-dim blocks of the P V product
@@ -82,6 +88,9 @@ void multi_kernel(MultiArgs a) {
   constexpr int RPI = kWave / LPR;       // rows per wave load
   constexpr int NI = 16 / RPI;           // wave loads per 16-row tile (= KS)
   constexpr int LSTR = ROWB + 8;         // LDS row stride: rows 4 apart sit 8 banks apart
+  constexpr int OSTR = D * 4 + 16;       // fp32 O row stride of the store staging
+  constexpr int ORPI = kWave * 16 / (D * 4);   // O rows per wave store
+  static_assert(16 * OSTR <= 2 * 16 * LSTR, "O staging must fit the wave's K/V tiles");
   __shared__ __align__(16) unsigned char s_kv[kWaves][2][16 * LSTR];
 
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & (kWave - 1);
@@ -153,6 +162,72 @@ void multi_kernel(MultiArgs a) {
     for (int i = 0; i < NI; ++i)
       *reinterpret_cast<u32x4*>(dst + (RPI * i + lrow) * LSTR + 16 * lcol) = r[i];
   };
+
+  // Partials of unit uu, rows ((b*M + r)*Hq + h)*nc + c.  With one query
+  // tile, O goes through the wave's LDS tiles (free between units: the next
+  // unit's K rows are still in registers) so that every store writes 16
+  // bytes per lane and whole rows, instead of 4 bytes per lane in 64-byte
+  // pieces.
+  unsigned char* ost = s_kv[wave][0];
+  auto store_unit = [&](const f32x4 (&o)[QT][DB], const float (&m)[QT], const float (&l)[QT],
+                        int uu) {
+    UnitM x;
+    decode(uu, x);
+#pragma unroll
+    for (int qt = 0; qt < QT; ++qt) {
+      const int rown = n + 16 * qt;
+      if (qd == 0 && rown < R) {
+        const size_t prow =
+            (((size_t)x.b * a.M + rown / G) * a.Hq + (size_t)x.kvh * G + rown % G) * a.nc + x.c;
+        *reinterpret_cast<f32x2*>(a.ml_part + prow * 2) =
+            f32x2{(m[qt] == kNegInf) ? kNegInf : m[qt] * c_log2, l[qt]};
+      }
+      if constexpr (QT == 1) {
+        // lane (n, qd) holds O rows 4*qd + e, dims 16*db + n
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+#pragma unroll
+          for (int db = 0; db < DB; ++db)
+            *reinterpret_cast<float*>(ost + (4 * qd + e) * OSTR + (16 * db + n) * 4) = o[qt][db][e];
+        // read back: wave store i covers rows ORPI*i .. +ORPI, 16 bytes per lane
+        constexpr int LPO = kWave / ORPI;   // lanes per O row
+#pragma unroll
+        for (int i = 0; i < 16 / ORPI; ++i) {
+          const int rr = ORPI * i + lane / LPO, cb = 16 * (lane % LPO);
+          const f32x4 v = *reinterpret_cast<const f32x4*>(ost + rr * OSTR + cb);
+          const int row = 16 * qt + rr;
+          if (row < R) {
+            const size_t prow =
+                (((size_t)x.b * a.M + row / G) * a.Hq + (size_t)x.kvh * G + row % G) * a.nc + x.c;
+            *reinterpret_cast<f32x4*>(reinterpret_cast<unsigned char*>(a.o_part + prow * D) + cb) =
+                v;
+          }
+        }
+      } else {
+        // two query tiles: straight from the MFMA layout (the staging
+        // measured slower at this register load)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int row = 16 * qt + 4 * qd + e;
+          if (row < R) {
+            const size_t prow =
+                (((size_t)x.b * a.M + row / G) * a.Hq + (size_t)x.kvh * G + row % G) * a.nc + x.c;
+#pragma unroll
+            for (int db = 0; db < DB; ++db) a.o_part[prow * D + 16 * db + n] = o[qt][db][e];
+          }
+        }
+      }
+    }
+  };
+  // Finished units wait in registers (up to H of them, one query tile only)
+  // and are written together when H are held or the wave has no unit left.
+  // Stores count on the same vector-memory counter as loads: partials
+  // stored between units made the next unit's first K wait for them.
+  constexpr int H = QT == 1 ? FD_MR_HOLD : 1;
+  f32x4 hold_o[H][QT][DB];
+  float hold_m[H][QT], hold_l[H][QT];
+  int hold_u[H];
+  int held = 0;   // wave-uniform
 
   int u = (int)blockIdx.x * kWaves + wave;
   if (u >= n_units) return;
@@ -275,24 +350,29 @@ void multi_kernel(MultiArgs a) {
       // l of row n + 16*qt: the four lanes of the row hold parts
       l[qt] += __shfl_xor(l[qt], 16);
       l[qt] += __shfl_xor(l[qt], 32);
-      // partial rows ((b*M + r)*Hq + h)*nc + c
+    }
+    if constexpr (H > 1) {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int row = 16 * qt + 4 * qd + e;
-        if (row < R) {
-          const size_t prow =
-              (((size_t)b * a.M + row / G) * a.Hq + (size_t)kvh * G + row % G) * a.nc + c;
+      for (int h = 0; h < H; ++h) {
+        if (held == h) {   // wave-uniform
 #pragma unroll
-          for (int db = 0; db < DB; ++db) a.o_part[prow * D + 16 * db + n] = o[qt][db][e];
+          for (int qt = 0; qt < QT; ++qt) {
+            hold_m[h][qt] = m[qt];
+            hold_l[h][qt] = l[qt];
+#pragma unroll
+            for (int db = 0; db < DB; ++db) hold_o[h][qt][db] = o[qt][db];
+          }
+          hold_u[h] = u;
         }
       }
-      const int rown = n + 16 * qt;
-      if (qd == 0 && rown < R) {
-        const size_t prow =
-            (((size_t)b * a.M + rown / G) * a.Hq + (size_t)kvh * G + rown % G) * a.nc + c;
-        *reinterpret_cast<f32x2*>(a.ml_part + prow * 2) =
-            f32x2{(m[qt] == kNegInf) ? kNegInf : m[qt] * c_log2, l[qt]};
+      if (++held == H || !has_next) {
+#pragma unroll
+        for (int h = 0; h < H; ++h)
+          if (h < held) store_unit(hold_o[h], hold_m[h], hold_l[h], hold_u[h]);
+        held = 0;
       }
+    } else {
+      store_unit(o, m, l, u);
     }
     if (!has_next) break;
     cur = nxt;

@@ -87,3 +87,20 @@ def test_multi_row_two_query_tiles_full_size_sampled():
     c = W.multi_case(8, 8, 32, 8, 32768, 128, seed=108, device=DEV)
     rows = [(0, 0, 0), (0, 7, 31), (2, 4, 13), (6, 3, 22), (7, 7, 3), (7, 5, 30)]
     _check(c, chunk=512, rows=rows)
+
+
+def test_multi_row_many_units_per_wave_sampled():
+    """Chunks of 32 at the headline shape: 16,384 units, so every wave
+    finishes many units and writes its held partials several times."""
+    banner("multi full size B=8 L=32768 M=4 chunk=32")
+    c = W.multi_case(8, 4, 32, 8, 32768, 128, seed=103, device=DEV)
+    rows = [(0, 0, 0), (1, 3, 31), (4, 2, 9), (6, 1, 20), (7, 3, 2)]
+    _check(c, chunk=32, rows=rows)
+
+
+def test_multi_row_many_units_two_query_tiles_sampled():
+    """As above with two query tiles (G*M = 32) and a ragged last chunk."""
+    banner("multi B=4 L=20000 M=8 chunk=48")
+    c = W.multi_case(4, 8, 32, 8, 20000, 128, seed=109, device=DEV)
+    rows = [(0, 0, 0), (1, 7, 31), (2, 4, 16), (3, 6, 5)]
+    _check(c, chunk=48, rows=rows)
