@@ -139,43 +139,99 @@ void partial_kernel(PartialArgs a) {
   const int stride = (int)gridDim.x * kWaves;
 
   // Units: contiguous caches have B*Hkv*nc equal units.  Paged caches have
-  // ragged lengths, so only the real units -- Hkv * ceil(L_b / chunk) for
-  // sequence b -- are numbered (sequence-major), and every wave walks its
-  // share of them; `seq_first`/`seq_units` track the sequence of a unit as
-  // the wave's unit index grows.  Every numbered unit has c0 < c1.
+  // ragged lengths, so only the real units are numbered: first the whole
+  // chunks of every sequence (sequence-major, kv-head fastest; `seq_first` /
+  // `seq_units` track the sequence as the wave's unit index grows), then the
+  // last, partial chunk of every sequence that has one (one unit per
+  // kv-head), longest first when there are at most kMaxSortedSeqs sequences.
+  // Waves take units round-robin, so each wave's last round holds the
+  // shortest units (longest-processing-time-first order), and the waves
+  // finish closer together.  Every numbered unit has c0 < c1.
+  constexpr int kMaxSortedSeqs = 128;
+  __shared__ int s_tail[kPagedMode ? kWaves : 1][kPagedMode ? kMaxSortedSeqs : 1];
   int n_units = a.B * a.Hkv * a.nc;
+  int n_whole = n_units;
   int seq_b = 0, seq_first = 0, seq_units = 0;
+  int tail_r = -1, tail_b = -1;
   auto seq_len = [&](int bb) { return min(max(a.seq_lens[bb], 0), a.max_seq_len); };
+  // the same for a wave-uniform index, through the scalar cache: its wait
+  // is on the LDS/scalar counter, not on the vector-memory counter that the
+  // K and V loads in flight hold
+  auto seq_len_u = [&](int bb) {
+    const auto* sl = (const __attribute__((address_space(4))) int32_t*)a.seq_lens;
+    return min(max(sl[__builtin_amdgcn_readfirstlane(bb)], 0), a.max_seq_len);
+  };
+  const bool sorted_tail = a.B <= kMaxSortedSeqs;
   if constexpr (kPagedMode) {
-    int tot = 0;
-    for (int bb = lane; bb < a.B; bb += kWave) tot += (seq_len(bb) + a.chunk - 1) / a.chunk;
+    int whole = 0, part = 0;
+    for (int bb = lane; bb < a.B; bb += kWave) {
+      const int L = seq_len(bb);
+      whole += L / a.chunk;
+      part += L % a.chunk != 0;
+    }
 #pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) tot += __shfl_xor(tot, o);
-    n_units = tot * a.Hkv;
-    seq_units = a.Hkv * ((seq_len(0) + a.chunk - 1) / a.chunk);
-  }
-  auto decode = [&](int u, Unit& x) {   // u must grow from call to call
-    int L;
-    if constexpr (kPagedMode) {
-      while (u >= seq_first + seq_units) {      // wave-uniform
-        seq_first += seq_units;
-        ++seq_b;
-        seq_units = a.Hkv * ((seq_len(seq_b) + a.chunk - 1) / a.chunk);
+    for (int o = 32; o >= 1; o >>= 1) {
+      whole += __shfl_xor(whole, o);
+      part += __shfl_xor(part, o);
+    }
+    n_whole = whole * a.Hkv;
+    n_units = (whole + part) * a.Hkv;
+    seq_units = a.Hkv * (seq_len_u(0) / a.chunk);
+    if (sorted_tail) {
+      // rank of each partial chunk: longer remainder first, then lower b
+      for (int bb = lane; bb < a.B; bb += kWave) {
+        const int rem = seq_len(bb) % a.chunk;
+        int rank = 0;
+        for (int o = 0; o < a.B; ++o) {
+          const int ro = seq_len_u(o) % a.chunk;
+          rank += ro != 0 && (ro > rem || (ro == rem && o < bb));
+        }
+        if (rem != 0) s_tail[wave][rank] = bb;
       }
-      x.b = seq_b;
-      const int r = u - seq_first;
-      x.kvh = r % a.Hkv;
-      x.c = r / a.Hkv;
-      L = seq_len(seq_b);
+    }
+  }
+  // sequence of the r-th partial chunk; r grows from call to call
+  auto tail_seq = [&](int r) {
+    if (sorted_tail) return s_tail[wave][r];
+    while (tail_r < r) {      // wave-uniform
+      do {
+        ++tail_b;
+      } while (seq_len_u(tail_b) % a.chunk == 0);
+      ++tail_r;
+    }
+    return tail_b;
+  };
+  auto decode = [&](int u, Unit& x) {   // u must grow from call to call
+    if constexpr (kPagedMode) {
+      if (u < n_whole) {
+        while (u >= seq_first + seq_units) {      // wave-uniform
+          seq_first += seq_units;
+          ++seq_b;
+          seq_units = a.Hkv * (seq_len_u(seq_b) / a.chunk);
+        }
+        x.b = seq_b;
+        const int r = u - seq_first;
+        x.kvh = r % a.Hkv;
+        x.c = r / a.Hkv;
+        x.c0 = x.c * a.chunk;
+        x.c1 = x.c0 + a.chunk;
+      } else {
+        const int p = u - n_whole;
+        x.kvh = p % a.Hkv;
+        x.b = tail_seq(p / a.Hkv);
+        const int L = seq_len_u(x.b);
+        x.c = L / a.chunk;
+        x.c0 = x.c * a.chunk;
+        x.c1 = L;
+      }
     } else {
       x.c = u % a.nc;
       const int bk = u / a.nc;
       x.kvh = bk % a.Hkv;
       x.b = bk / a.Hkv;
-      L = a.L;
+      x.c0 = x.c * a.chunk;
+      x.c1 = min(x.c0 + a.chunk, a.L);
     }
-    x.c0 = x.c * a.chunk;
-    x.c1 = min(x.c0 + a.chunk, L);
   };
 
   // Paged addressing: the page ids of a unit's chunk.
@@ -201,7 +257,7 @@ void partial_kernel(PartialArgs a) {
       const int t = min(t0 + i * TPL + grp, x.c1 - 1);
       size_t row;
       if constexpr (kPagedMode) {
-        const int p = s_pid[wave][buf][(t - x.c0) >> shift];
+        const int p = min(max(s_pid[wave][buf][(t - x.c0) >> shift], 0), a.num_pages - 1);
         row = (((size_t)p * a.Hkv + x.kvh) << shift) | (size_t)(t & pmask);
       } else {
         row = head + (size_t)t;
@@ -306,14 +362,17 @@ void partial_kernel(PartialArgs a) {
       base[h] = a.phi_raw;
       on[h] = false;
     }
-    for (int t0 = cur.c0; t0 < cur.c1; t0 += STEP) {
+    // every unit has at least one row (c0 < c1): a loop without a zero-trip
+    // path, so that no load issued above looks pending at the unit's end
+    int t0 = cur.c0;
+    do {
       issue(vbase, off, vr);
       float s[NB][G];
       scores(cur, t0, kr, s);
       if constexpr (kPagedMode) {
         if (has_next && t0 == cur.c0) {
           if (pid_inline) {
-            if (lane < n_pages(nxt)) s_pid[wave][buf ^ 1][lane] = min(max(pid_next, 0), a.num_pages - 1);
+            if (lane < n_pages(nxt)) s_pid[wave][buf ^ 1][lane] = pid_next;
           } else {
             stage_pages(nxt, buf ^ 1);
           }
@@ -331,7 +390,8 @@ void partial_kernel(PartialArgs a) {
         fixed_update<E, G, VEC, NB, kPg>(s, vr, a.c_log2, a.phi_raw, a.flag_hi_raw,
                                          a.flag_lo_raw, acc, mx, base, on, l);
       else online_update<E, G, VEC, NB, kPg>(s, vr, a.c_log2, acc, m, l);
-    }
+      t0 += STEP;
+    } while (t0 < cur.c1);
     // m in log2 units of the scaled score: the slot's own maximum, or for
     // the fixed maximum its reference (phi, or its own maximum after a
     // switch); a slot that saw no row has m = -inf, l = 0
@@ -376,9 +436,9 @@ void partial_kernel(PartialArgs a) {
 //   out = sum_i w_i O_i / sum_i w_i l_i,  lse = (M + log2 sum_i w_i l_i) ln 2.
 // One workgroup per (sequence, query head).  The weights of up to 256 chunks
 // at a time go to LDS; thread (chunk lane cl, column group cg) then sums
-// chunks cl, cl + CL, ... of 4 columns with independent 16-byte loads (the
-// loads of the first 64 chunks are issued before the maximum is known), and
-// the chunk lanes are reduced through LDS.  The order of every sum is fixed,
+// chunks cl, cl + CL, ... of 4 columns with independent 16-byte loads, 64
+// chunks at a time (the loads of the first 64 are issued before the maximum
+// is known), and the chunk lanes are reduced through LDS.  The order of every sum is fixed,
 // so runs are bitwise reproducible.  Rows whose chunks all carry the same m
 // (the fixed-maximum path without fallback) get weights of exactly 1.
 constexpr int kMergeWaves = 4;
@@ -440,26 +500,31 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(MergeArgs a) {
     s_w[tid] = wt;
     __syncthreads();
     const int nt = min(kMergeThreads, n - c0);
-    int k = cl;
-    if (c0 == 0) {
+    // groups of kPre chunks per thread: all loads of a group are issued
+    // before its sums (the first group of the first tile is already loaded)
+    for (int k0 = 0; k0 < nt; k0 += kPre * CL) {
+      f32x4 o[kPre];
+      if (c0 == 0 && k0 == 0) {
 #pragma unroll
-      for (int j = 0; j < kPre; ++j, k += CL) {
-        if (k < nt) {
-          const float x = s_w[k];
-          acc.x = fmaf(x, pre[j].x, acc.x);
-          acc.y = fmaf(x, pre[j].y, acc.y);
-          acc.z = fmaf(x, pre[j].z, acc.z);
-          acc.w = fmaf(x, pre[j].w, acc.w);
+        for (int j = 0; j < kPre; ++j) o[j] = pre[j];
+      } else {
+#pragma unroll
+        for (int j = 0; j < kPre; ++j) {
+          const int k = k0 + cl + j * CL;
+          o[j] = k < nt ? op[(size_t)(c0 + k) * CG + cg] : f32x4{0.f, 0.f, 0.f, 0.f};
         }
       }
-    }
-    for (; k < nt; k += CL) {
-      const f32x4 o = op[(size_t)(c0 + k) * CG + cg];
-      const float x = s_w[k];
-      acc.x = fmaf(x, o.x, acc.x);
-      acc.y = fmaf(x, o.y, acc.y);
-      acc.z = fmaf(x, o.z, acc.z);
-      acc.w = fmaf(x, o.w, acc.w);
+#pragma unroll
+      for (int j = 0; j < kPre; ++j) {
+        const int k = k0 + cl + j * CL;
+        if (k < nt) {
+          const float x = s_w[k];
+          acc.x = fmaf(x, o[j].x, acc.x);
+          acc.y = fmaf(x, o[j].y, acc.y);
+          acc.z = fmaf(x, o[j].z, acc.z);
+          acc.w = fmaf(x, o[j].w, acc.w);
+        }
+      }
     }
   }
   s_o[cl][cg] = acc;

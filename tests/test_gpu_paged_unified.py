@@ -77,6 +77,34 @@ def test_paged_equals_dense_and_relabel_invariant():
     assert torch.equal(out, o3) and torch.equal(lse, l3)
 
 
+@pytest.mark.parametrize("B", [129, 300])
+def test_paged_many_sequences(B):
+    """More sequences than the partial chunks are sorted for (they are then
+    taken in sequence order): empty ones, exact chunk multiples, ragged."""
+    banner(f"paged many sequences B={B}")
+    rs = np.random.default_rng(B)
+    lens = rs.integers(0, 400, size=B)
+    lens[::7] = 0
+    lens[3::11] = 64 * rs.integers(1, 6, size=len(lens[3::11]))
+    c = W.paged_case(B, 8, 2, 128, 0, 400, page=16, chunk=64, seed=B, device=DEV,
+                     lens=lens)
+    out, lse = _paged_run(c, max_len=400)
+    ref, lref = _paged_ref(c)
+    assert max_err(f64(out), ref) <= 2e-3 and max_err(f64(lse), lref) <= 2e-3
+
+
+def test_paged_equal_remainders():
+    """Sequences whose last chunks are equally long (ties in the
+    longest-first order of the partial chunks)."""
+    banner("paged equal remainders")
+    lens = [128 * k + 17 for k in range(1, 9)] + [128 * k + 90 for k in range(1, 9)] + [256, 0]
+    c = W.paged_case(len(lens), 8, 2, 128, 0, 2000, page=16, chunk=128, seed=5, device=DEV,
+                     lens=lens)
+    out, lse = _paged_run(c)
+    ref, lref = _paged_ref(c)
+    assert max_err(f64(out), ref) <= 2e-3 and max_err(f64(lse), lref) <= 2e-3
+
+
 def test_paged_config3_full_size_sampled():
     banner("paged config3 full size")
     c = W.config_case(3, device=DEV)
