@@ -44,8 +44,10 @@ CONFIGS = {
             chunk=1024, seed=101),
     2: dict(kind="dense", B=8, Hq=32, Hkv=8, L=32768, d=128, dtype="bf16",
             chunk=512, seed=102),
+    # chunk 1024 for the ragged paged batch: 7 units per resident wave, the
+    # best of a sweep over 256 .. 2048 (512: 614 us, 1024: 578 us on MI355X)
     3: dict(kind="paged", B=16, Hq=32, Hkv=8, d=128, len_lo=1024,
-            len_hi=131072, page=16, chunk=512, seed=103),
+            len_hi=131072, page=16, chunk=1024, seed=103),
     4: dict(kind="unified", B=4, Hq=32, Hkv=8, L=65536, d=128, chunk=512,
             plant_frac=0.02, plant_coef=0.5, over_frac=0.01, over_shift=15.0,
             margin_hi=10.0, margin_lo=40.0, seed=104, cal_seed=1104),
