@@ -229,7 +229,12 @@ void multi_kernel(MultiArgs a) {
   int hold_u[H];
   int held = 0;   // wave-uniform
 
-  int u = (int)blockIdx.x * kWaves + wave;
+  // wave w takes the consecutive units [w*per, (w+1)*per): consecutive
+  // chunks of one (sequence, kv-head), a single contiguous stretch of K and
+  // V (measured 186 -> 174 us at M = 4 against taking every W-th unit)
+  const int per = (n_units + stride - 1) / stride;
+  int u = ((int)blockIdx.x * kWaves + wave) * per;
+  const int u_end = min(u + per, n_units);
   if (u >= n_units) return;
   UnitM cur;
   decode(u, cur);
@@ -240,8 +245,8 @@ void multi_kernel(MultiArgs a) {
   // before the unit's partials are stored: stores count on the same
   // vector-memory counter as loads, so loads issued after them would wait.
   while (true) {
-    const int un = u + stride;
-    const bool has_next = un < n_units;
+    const int un = u + 1;
+    const bool has_next = un < u_end;
     UnitM nxt = cur;
     if (has_next) decode(un, nxt);
     const int b = cur.b, kvh = cur.kvh, c = cur.c, c0 = cur.c0, c1 = cur.c1;

@@ -180,9 +180,13 @@ __device__ __forceinline__ void state_to_log2(float (&m)[G], float c_log2) {
 }
 
 // Merge the row slots of one wave with shuffles: afterwards every lane holds
-// the merged state (O relative to m, m in log2 units, l) of its column.
+// the merged state (O relative to m, m in log2 units, l) of its column.  The
+// two weighted terms are rounded separately and then added (no fused
+// multiply-add), so both partners of a step get the same bits and every row
+// slot ends with the identical merged state, whichever slot keeps it.
 template <int G, int VEC, int LPT>
 __device__ __forceinline__ void wave_merge(float (&acc)[G][VEC], float (&m)[G], float (&l)[G]) {
+#pragma clang fp contract(off)
 #pragma unroll
   for (int off = LPT; off < kWave; off <<= 1) {
 #pragma unroll
