@@ -265,7 +265,7 @@ def variant_multi(torch, fd, W, args, timer):
     """Multi-row decode on the headline shape (B 8, Hq 32, Hkv 8, d 128,
     L 32768, chunk 512) with M = 2, 4 and 8 new tokens per sequence (G*M = 8,
     16 and 32 query rows per kv-head, matrix-core kernel), beside M separate
-    single-query calls on the same cache."""
+    single-query calls on the same cache; each also at chunk 2048."""
     B, Hq, Hkv, L, d, chunk = 8, 32, 8, 32768, 128, 512
     base = W.multi_case(B, 8, Hq, Hkv, L, d, chunk=chunk, seed=102, device="cuda:0")
     ks = [base.k] + [base.k.clone() for _ in range(args.copies - 1)]
@@ -301,6 +301,23 @@ def variant_multi(torch, fd, W, args, timer):
                              pct_of_peak=round(100 * gbs(nbytes, t["ms"]) / PEAK_GBS, 1),
                              m_single_query_calls_us=round(M * t_single * 1e3, 2),
                              speedup_vs_single_calls=round(M * t_single / t["ms"], 2))
+        # the same call with chunks of 2048 (16 per sequence): a quarter of the
+        # partials (G*M rows of d+2 floats per chunk) to write and merge
+        ch2 = 2048
+        wsn2 = fd.workspace_bytes("fd_decode_attn_multi", B=B, M=M, Hq=Hq, Hkv=Hkv, L=L, d=d,
+                                  chunk=ch2)
+        ws2 = torch.empty(wsn2, dtype=torch.uint8, device="cuda:0")
+        size2 = C.c_size_t(wsn2)
+        calls2 = []
+        for k, v in zip(ks, vs):
+            a = (fd.FD_BF16, vp(q), vp(k), vp(v), vp(out), vp(lse), B, M, Hq, Hkv, L, d,
+                 base.scale, ch2, vp(ws2), C.byref(size2), st)
+            calls2.append(lambda a=a: lib.fd_decode_attn_multi(*a))
+        check_rc(lib, calls2[0]())
+        t2 = timer.run(calls2, args.steps, args.warmup)
+        res[f"M_{M}"].update(us_per_step_chunk2048=round(t2["ms"] * 1e3, 2),
+                             pct_of_peak_chunk2048=round(
+                                 100 * gbs(nbytes, t2["ms"]) / PEAK_GBS, 1))
     return res
 
 

@@ -170,6 +170,10 @@ int fd_decode_attn_unified_max(fd_dtype_t dt, const void* q, const void* k,
  *   M = 1: dt bf16 or fp32.  M >= 2: bf16 only and G*M <= 32, else
  *   FD_ERR_UNSUPPORTED.  Workspace: chunk partials of the B*M*Hq rows
  *   (same layout as fd_decode_attn_partials with M*Hq heads).
+ *   chunk: each chunk writes G*M partial rows of (d + 2) floats per kv-head
+ *   and the merge reads them back, so large M favours long chunks (on
+ *   MI355X at L = 32768, B = 8: 2048 beat 512 by 4 % at M = 2 and 12 % at
+ *   M = 8).
  */
 int fd_decode_attn_multi(fd_dtype_t dt, const void* q, const void* k,
                          const void* v, float* out, float* lse, int B, int M,
