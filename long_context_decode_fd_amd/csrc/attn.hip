@@ -34,6 +34,10 @@ constexpr int kMaxChunkPages = 1024;
 #define FD_PIECES 2
 #endif
 constexpr int kP = FD_PIECES;
+// Contiguous caches: K and V batches through buffer loads (see `issue_c`).
+#ifndef FD_BUF_DENSE
+#define FD_BUF_DENSE 1
+#endif
 
 // Fixed-maximum update with in-flight fallback.  A row slot takes
 // p = 2^((s - phi) c) while its running maximum stays inside
@@ -275,6 +279,36 @@ void partial_kernel(PartialArgs a) {
       for (int pc = 0; pc < kPg; ++pc)
         r[i * kPg + pc] = ld16_stream(src + off[i] + (size_t)pc * (ROW / kPg));
   };
+  // Contiguous caches with FD_BUF_DENSE: a batch of the tensor at `src`
+  // starting at row t0 of unit x is read through one buffer descriptor whose
+  // base is that row and whose byte limit ends at the unit's end c1, so rows
+  // past c1 read as zeros without touching memory (their scores are masked,
+  // their p is 0).  Load (i, pc) of this lane sits at byte
+  // i * TPL * ROW + pc * ROW / kPg + grp * ROW + col * 16 of the batch: the
+  // multiple of 4096 comes from one of kNvo lane offsets fixed for the whole
+  // kernel, the rest is the instruction's immediate, so the batch costs no
+  // per-load address arithmetic.  The range check covers the lane offset
+  // plus the immediate.
+  constexpr int kBatchBytes = STEP * ROW;
+  constexpr int kNvo = (kBatchBytes + 4095) / 4096;
+  int lane_voff[kNvo];
+#pragma unroll
+  for (int j = 0; j < kNvo; ++j) lane_voff[j] = j * 4096 + grp * ROW + col * 16;
+  auto issue_c = [&](const char* __restrict__ src, const Unit& x, int t0,
+                     u32x4 (&r)[NB * kPg]) {
+    const size_t head = ((size_t)x.b * a.Hkv + x.kvh) * (size_t)a.L;
+    const __amdgpu_buffer_rsrc_t rs =
+        buffer_rsrc(src + (head + (size_t)t0) * ROW, min(x.c1 - t0, STEP) * ROW);
+#pragma unroll
+    for (int i = 0; i < NB; ++i)
+#pragma unroll
+      for (int pc = 0; pc < kPg; ++pc) {
+        constexpr int kPcBytes = ROW / kPg;
+        const int byte = i * TPL * ROW;
+        r[i * kPg + pc] = ld16_buf(rs, lane_voff[byte / 4096] + byte % 4096 + pc * kPcBytes);
+      }
+  };
+  constexpr bool kBufC = FD_BUF_DENSE && !kPagedMode;
   u32x4 qv[G][kPg];
   auto load_q = [&](const Unit& x) {
     const E* qp = reinterpret_cast<const E*>(a.q) +
@@ -331,7 +365,9 @@ void partial_kernel(PartialArgs a) {
   // W-th unit).  Paged caches keep the round-robin order above, whose last
   // round holds the shortest units.
   const int per = kPagedMode ? 1 : (n_units + stride - 1) / stride;
-  int u = ((int)blockIdx.x * kWaves + wave) * per;
+  // wave-uniform by construction; readfirstlane lets the compiler keep the
+  // unit (and the buffer descriptors built from it) in scalar registers
+  int u = __builtin_amdgcn_readfirstlane(((int)blockIdx.x * kWaves + wave) * per);
   const int u_end = kPagedMode ? n_units : min(u + per, n_units);
   const int ustep = kPagedMode ? stride : 1;
   if (u >= n_units) return;
@@ -342,8 +378,12 @@ void partial_kernel(PartialArgs a) {
   u32x4 kr[NB * kPg], vr[NB * kPg];
   size_t off[NB];
   load_q(cur);
-  offsets(cur, buf, cur.c0, off);
-  issue(kbase, off, kr);
+  if constexpr (kBufC) {
+    issue_c(kbase, cur, cur.c0, kr);
+  } else {
+    offsets(cur, buf, cur.c0, off);
+    issue(kbase, off, kr);
+  }
 
   while (true) {
     const int un = u + ustep;
@@ -375,7 +415,8 @@ void partial_kernel(PartialArgs a) {
     // path, so that no load issued above looks pending at the unit's end
     int t0 = cur.c0;
     do {
-      issue(vbase, off, vr);
+      if constexpr (kBufC) issue_c(vbase, cur, t0, vr);
+      else issue(vbase, off, vr);
       float s[NB][G];
       scores(cur, t0, kr, s);
       if constexpr (kPagedMode) {
@@ -388,12 +429,20 @@ void partial_kernel(PartialArgs a) {
         }
       }
       if (t0 + STEP < cur.c1) {
-        offsets(cur, buf, t0 + STEP, off);
-        issue(kbase, off, kr);
+        if constexpr (kBufC) {
+          issue_c(kbase, cur, t0 + STEP, kr);
+        } else {
+          offsets(cur, buf, t0 + STEP, off);
+          issue(kbase, off, kr);
+        }
       } else if (has_next) {
         load_q(nxt);
-        offsets(nxt, buf ^ 1, nxt.c0, off);
-        issue(kbase, off, kr);
+        if constexpr (kBufC) {
+          issue_c(kbase, nxt, nxt.c0, kr);
+        } else {
+          offsets(nxt, buf ^ 1, nxt.c0, off);
+          issue(kbase, off, kr);
+        }
       }
       if constexpr (kFixed)
         fixed_update<E, G, VEC, NB, kPg>(s, vr, a.c_log2, a.phi_raw, a.flag_hi_raw,

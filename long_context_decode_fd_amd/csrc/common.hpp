@@ -132,4 +132,28 @@ __device__ __forceinline__ u32x4 ld16_stream(const void* p) {
 #endif
 }
 
+// Raw buffer descriptors (gfx9 family): word 3 of a plain byte-addressed
+// buffer, and the cache-policy bit that marks a buffer load non-temporal.
+constexpr int kBufferDword3 = 0x00020000;
+constexpr int kBufferNonTemporal = 2;
+
+// Descriptor of `bytes` bytes at p.  p and bytes must be wave-uniform; they
+// are read from the first active lane, so the descriptor lives in scalar
+// registers and the loads need no per-lane descriptor.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* p, int bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+  void* q = reinterpret_cast<void*>(((uint64_t)hi << 32) | lo);
+  return __builtin_amdgcn_make_buffer_rsrc(q, 0, __builtin_amdgcn_readfirstlane(bytes),
+                                           kBufferDword3);
+}
+
+// 16-byte non-temporal buffer load at byte offset `off` of descriptor r
+// (zeros, and no memory access, when off + 16 exceeds its limit).
+__device__ __forceinline__ u32x4 ld16_buf(__amdgpu_buffer_rsrc_t r, int off) {
+  return __builtin_bit_cast(u32x4,
+                            __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kBufferNonTemporal));
+}
+
 }  // namespace fdk

@@ -37,6 +37,24 @@ typedef short s16x4_t __attribute__((ext_vector_type(4)));
 #ifndef FD_MR_TILES
 #define FD_MR_TILES 2   // 16-position tiles per wave batch: 8 K and 8 V loads at d = 128
 #endif
+#ifndef FD_MR_TILES2
+#define FD_MR_TILES2 FD_MR_TILES   // the same with two query tiles
+#endif
+#ifndef FD_MR_PV32_Q1
+#define FD_MR_PV32_Q1 0   // P V on 16x16x32 tile pairs with one query tile
+#endif
+#ifndef FD_MR_PV32_Q2
+#define FD_MR_PV32_Q2 1   // ... with two query tiles
+#endif
+#ifndef FD_MR_BUF_Q1
+#define FD_MR_BUF_Q1 1   // K/V tiles through buffer loads (see issue below), one query tile
+#endif
+#ifndef FD_MR_BUF_Q2
+#define FD_MR_BUF_Q2 0   // ... two query tiles (measured slower: 219 -> 250 us at M = 8)
+#endif
+#ifndef FD_MR_HWSPLIT
+#define FD_MR_HWSPLIT 1   // hi/lo split of P by the hardware bf16 conversion
+#endif
 #ifndef FD_MR_WAVES_PER_EU
 #define FD_MR_WAVES_PER_EU 1
 #endif
@@ -55,15 +73,18 @@ __device__ __forceinline__ f32x4 mfma_pv(const u32x2& a, const u32x2& b, f32x4 c
                                                     __builtin_bit_cast(s16x4_t, b), c, 0, 0, 0);
 }
 
-// fp32 -> bf16 bits, round to nearest even (finite inputs).
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+// p = hi + lo with hi = bf16(p), lo = bf16(p - hi), both rounded to nearest
+// even by the hardware conversion (two values per instruction): two bf16
+// pairs from four fp32 values.
 __device__ __forceinline__ uint32_t bf16_bits(float x) {
   const uint32_t u = __float_as_uint(x);
   return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
 }
-
-// p = hi + lo with hi = bf16(p), lo = bf16(p - hi): two bf16 pairs from four
-// fp32 values.
 __device__ __forceinline__ void split_bf16(const float (&p)[4], u32x2& hi, u32x2& lo) {
+#if !FD_MR_HWSPLIT
+  {
   uint32_t h[4], l[4];
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
@@ -72,6 +93,20 @@ __device__ __forceinline__ void split_bf16(const float (&p)[4], u32x2& hi, u32x2
   }
   hi = u32x2{h[0] | (h[1] << 16), h[2] | (h[3] << 16)};
   lo = u32x2{l[0] | (l[1] << 16), l[2] | (l[3] << 16)};
+  return;
+  }
+#endif
+  uint32_t h[2], l[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const float a = p[2 * j], b = p[2 * j + 1];
+    h[j] = __builtin_bit_cast(uint32_t, bf16x2_t{(__bf16)a, (__bf16)b});
+    const float ra = a - __uint_as_float(h[j] << 16);
+    const float rb = b - __uint_as_float(h[j] & 0xFFFF0000u);
+    l[j] = __builtin_bit_cast(uint32_t, bf16x2_t{(__bf16)ra, (__bf16)rb});
+  }
+  hi = u32x2{h[0], h[1]};
+  lo = u32x2{l[0], l[1]};
 }
 
 // QT = query tiles of 16 rows (R = G*M <= 16 * QT); both share every K and V
@@ -81,7 +116,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(FD_MR_
 void multi_kernel(MultiArgs a) {
   constexpr int KS = D / 32;             // QK k-steps (32 dims each)
   constexpr int DB = D / 16;             // 16-dim blocks of the P V product
-  constexpr int TT = FD_MR_TILES;
+  constexpr int TT = QT == 1 ? FD_MR_TILES : FD_MR_TILES2;
   constexpr int STEP = 16 * TT;          // positions per wave batch
   constexpr int ROWB = D * 2;            // bytes per cache row
   constexpr int LPR = ROWB / 16;         // lanes per row in a coalesced load
@@ -145,16 +180,33 @@ void multi_kernel(MultiArgs a) {
       }
     }
   };
-  // wave load i of tile tt: rows T + 16*tt + RPI*i + lrow, bytes 16*lcol
-  // (rows past the chunk end c1 repeat its last row and are masked)
+  // wave load i of tile tt: rows T + 16*tt + RPI*i + lrow, bytes 16*lcol.
+  // Buffer loads: each 16-row tile gets a descriptor whose base is the tile's
+  // first row and whose byte limit ends at the chunk end c1, so every lane
+  // uses the same offset (lrow, lcol) plus an immediate per load, with no
+  // per-load address arithmetic; rows at or past c1 are outside the limit
+  // and read as zeros without touching memory (their scores are masked and
+  // their p is 0).  The range check covers the lane offset plus the
+  // immediate; the scalar offset is 0.
+  const int lane_off = lrow * ROWB + 16 * lcol;
   auto issue = [&](const char* __restrict__ src, int T, int c1, u32x4 (&r)[TT][NI]) {
+    constexpr bool kBuf = QT == 1 ? FD_MR_BUF_Q1 : FD_MR_BUF_Q2;
 #pragma unroll
-    for (int tt = 0; tt < TT; ++tt)
+    for (int tt = 0; tt < TT; ++tt) {
+      if constexpr (kBuf) {
+      const int t0 = T + 16 * tt;
+      const int nrow = min(max(c1 - t0, 0), 16);
+      const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(src + (size_t)t0 * ROWB, nrow * ROWB);
+#pragma unroll
+      for (int i = 0; i < NI; ++i) r[tt][i] = ld16_buf(rs, lane_off + RPI * i * ROWB);
+      } else {
 #pragma unroll
       for (int i = 0; i < NI; ++i) {
         const int t = min(T + 16 * tt + RPI * i + lrow, c1 - 1);
         r[tt][i] = ld16_stream(src + (size_t)t * ROWB + 16 * lcol);
       }
+      }
+    }
   };
   // a tile of 16 rows into this wave's LDS tile (row-major, stride LSTR)
   auto to_lds = [&](unsigned char* dst, const u32x4 (&r)[NI]) {
@@ -233,7 +285,9 @@ void multi_kernel(MultiArgs a) {
   // chunks of one (sequence, kv-head), a single contiguous stretch of K and
   // V (measured 186 -> 174 us at M = 4 against taking every W-th unit)
   const int per = (n_units + stride - 1) / stride;
-  int u = ((int)blockIdx.x * kWaves + wave) * per;
+  // wave-uniform by construction; readfirstlane lets the compiler keep the
+  // unit (and the descriptors built from it) in scalar registers
+  int u = __builtin_amdgcn_readfirstlane(((int)blockIdx.x * kWaves + wave) * per);
   const int u_end = min(u + per, n_units);
   if (u >= n_units) return;
   UnitM cur;
@@ -339,9 +393,9 @@ void multi_kernel(MultiArgs a) {
         bias[qt] = (m[qt] == kNegInf) ? 0.f : m[qt] * c_log2;
       }
 
+      u32x2 ph[QT][TT], pl[QT][TT];
 #pragma unroll
-      for (int tt = 0; tt < TT; ++tt) {
-        u32x2 ph[QT], pl[QT];
+      for (int tt = 0; tt < TT; ++tt)
 #pragma unroll
         for (int qt = 0; qt < QT; ++qt) {
           float p[4];
@@ -350,10 +404,42 @@ void multi_kernel(MultiArgs a) {
             p[e] = exp2_hw(fmaf(sc[qt][tt][e], c_log2, -bias[qt]));
             l[qt] += p[e];
           }
-          split_bf16(p, ph[qt], pl[qt]);
+          split_bf16(p, ph[qt][tt], pl[qt][tt]);
         }
-        // V tile through LDS, read back as four positions of one dim per
-        // lane (this wave's region; LDS keeps the wave's order)
+      // P V over pairs of 16-position tiles with v_mfma_f32_16x16x32_bf16:
+      // k = 8 qd + j stands for position 4 qd + j % 4 of tile 2 tp + j / 4,
+      // so a lane's A operand is its P values of both tiles and its B
+      // operand the transposed reads of both V tiles (each staged in one of
+      // the wave's two LDS tiles; the K tiles are no longer needed here, and
+      // LDS keeps the wave's order).
+      constexpr bool kPv32 = QT == 1 ? FD_MR_PV32_Q1 : FD_MR_PV32_Q2;
+      constexpr int NTP = kPv32 ? TT / 2 : 0;   // tile pairs on 16x16x32
+#pragma unroll
+      for (int tp = 0; tp < NTP; ++tp) {
+        to_lds(lk, vr[2 * tp]);
+        to_lds(lv, vr[2 * tp + 1]);
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+          const u32x2 v0 = __builtin_bit_cast(
+              u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                         (__attribute__((address_space(3))) s16x4_t*)(lk + tr_off + 32 * db)));
+          const u32x2 v1 = __builtin_bit_cast(
+              u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                         (__attribute__((address_space(3))) s16x4_t*)(lv + tr_off + 32 * db)));
+          const u32x4 vb = u32x4{v0.x, v0.y, v1.x, v1.y};
+#pragma unroll
+          for (int qt = 0; qt < QT; ++qt) {
+            const u32x2 h0 = ph[qt][2 * tp], h1 = ph[qt][2 * tp + 1];
+            const u32x2 l0 = pl[qt][2 * tp], l1 = pl[qt][2 * tp + 1];
+            o[qt][db] = mfma_qk(u32x4{h0.x, h0.y, h1.x, h1.y}, vb, o[qt][db]);
+            o[qt][db] = mfma_qk(u32x4{l0.x, l0.y, l1.x, l1.y}, vb, o[qt][db]);
+          }
+        }
+      }
+      // the remaining tiles one at a time on v_mfma_f32_16x16x16_bf16
+      // (position 4 qd + e)
+#pragma unroll
+      for (int tt = 2 * NTP; tt < TT; ++tt) {
         to_lds(lv, vr[tt]);
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
@@ -362,8 +448,8 @@ void multi_kernel(MultiArgs a) {
                          (__attribute__((address_space(3))) s16x4_t*)(lv + tr_off + 32 * db)));
 #pragma unroll
           for (int qt = 0; qt < QT; ++qt) {
-            o[qt][db] = mfma_pv(ph[qt], vv, o[qt][db]);
-            o[qt][db] = mfma_pv(pl[qt], vv, o[qt][db]);
+            o[qt][db] = mfma_pv(ph[qt][tt], vv, o[qt][db]);
+            o[qt][db] = mfma_pv(pl[qt][tt], vv, o[qt][db]);
           }
         }
       }
