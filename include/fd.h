@@ -39,7 +39,9 @@
  *     failed).  fd_last_error() then describes the failure.
  *   - Non-finite values in q/K/V propagate; the kernels do not check data.
  *   - Supported: d in {64, 128}; Hq / Hkv in {1, 2, 4, 8}; chunk a positive
- *     multiple of 16 no larger than 65536.
+ *     multiple of 16 no larger than 65536; B * (query rows per sequence) *
+ *     (number of chunks) at most 2^31 - 1 (the kernels index partial rows
+ *     with 32-bit integers), else FD_ERR_UNSUPPORTED.
  */
 #ifndef FD_H_
 #define FD_H_

@@ -53,6 +53,17 @@ int check_scale(float scale) {
   return FD_OK;
 }
 
+// The kernels number units (sequence, kv-head, chunk) and rows of queries
+// with 32-bit integers.
+int check_units(int B, int H, int nc) {
+  if ((long long)B * H * nc > 0x7FFFFFFFLL || (long long)B * H > 0x7FFFFFFFLL / 2)
+    return fail(FD_ERR_UNSUPPORTED, "B=%d x %d heads x %d chunks exceeds 32-bit unit indices",
+                B, H, nc);
+  return FD_OK;
+}
+
+int n_chunks_of(int L, int chunk) { return (int)(((long long)L + chunk - 1) / chunk); }
+
 bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
 
 // Partials workspace: O [B*Hq*nc*d] fp32, then (m, l) [B*Hq*nc*2] fp32.
@@ -131,7 +142,8 @@ int fd_decode_attn(fd_dtype_t dt, const void* q, const void* k, const void* v, f
   if (L <= 0) return fail(FD_ERR_ARG, "L=%d must be positive", L);
   if (int e = check_chunk(chunk)) return e;
   if (int e = check_scale(scale)) return e;
-  const int nc = (L + chunk - 1) / chunk;
+  const int nc = n_chunks_of(L, chunk);
+  if (int e = check_units(B, Hq, nc)) return e;
   if (int e = workspace_gate(ws, ws_bytes, partial_bytes(B, Hq, nc, d))) return e;
   if (ws == nullptr) return ok();
   if (!q || !k || !v || !out) return fail(FD_ERR_ARG, "q, k, v and out must not be NULL");
@@ -150,7 +162,8 @@ int fd_decode_attn_partials(fd_dtype_t dt, const void* q, const void* k, const v
   if (L <= 0) return fail(FD_ERR_ARG, "L=%d must be positive", L);
   if (int e = check_chunk(chunk)) return e;
   if (int e = check_scale(scale)) return e;
-  const int nc = (L + chunk - 1) / chunk;
+  const int nc = n_chunks_of(L, chunk);
+  if (int e = check_units(B, Hq, nc)) return e;
   if (int e = workspace_gate(ws, ws_bytes, partial_bytes(B, Hq, nc, d))) return e;
   if (ws == nullptr) return ok();
   if (!q || !k || !v) return fail(FD_ERR_ARG, "q, k and v must not be NULL");
@@ -166,6 +179,7 @@ int fd_merge_partials(const float* o_part, const float* ml_part, float* out, flo
   if (B <= 0 || Hq <= 0 || n_chunks <= 0)
     return fail(FD_ERR_ARG, "B=%d Hq=%d n_chunks=%d must be positive", B, Hq, n_chunks);
   if (d != 64 && d != 128) return fail(FD_ERR_UNSUPPORTED, "d=%d not in {64,128}", d);
+  if (int e = check_units(B, Hq, n_chunks)) return e;
   if (!o_part || !ml_part || !out) return fail(FD_ERR_ARG, "o_part, ml_part, out NULL");
   if (!aligned16(o_part) || !aligned16(ml_part) || !aligned16(out))
     return fail(FD_ERR_ARG, "o_part, ml_part and out must be 16-byte aligned");
@@ -197,7 +211,8 @@ int fd_decode_attn_paged(fd_dtype_t dt, const void* q, const void* k_pool,
                 max_seq_len);
   int shift = 0;
   while ((1 << shift) < page_size) ++shift;
-  const int nc = (max_seq_len + chunk - 1) / chunk;
+  const int nc = n_chunks_of(max_seq_len, chunk);
+  if (int e = check_units(B, Hq, nc)) return e;
   if (int e = workspace_gate(ws, ws_bytes, partial_bytes(B, Hq, nc, d))) return e;
   if (ws == nullptr) return ok();
   if (!q || !k_pool || !v_pool || !block_table || !seq_lens || !out)
@@ -228,7 +243,8 @@ int fd_decode_attn_unified_max(fd_dtype_t dt, const void* q, const void* k, cons
   if (!isfinite(phi)) return fail(FD_ERR_ARG, "phi must be finite");
   if (!(margin_hi >= 0.f && margin_hi <= 60.f) || !(margin_lo >= 0.f && margin_lo <= 60.f))
     return fail(FD_ERR_ARG, "margins must lie in [0, 60] (exp(60) bounds the fp32 sums)");
-  const int nc = (L + chunk - 1) / chunk;
+  const int nc = n_chunks_of(L, chunk);
+  if (int e = check_units(B, Hq, nc)) return e;
   if (int e = workspace_gate(ws, ws_bytes, partial_bytes(B, Hq, nc, d))) return e;
   if (ws == nullptr) return ok();
   if (!q || !k || !v || !out) return fail(FD_ERR_ARG, "q, k, v and out must not be NULL");
@@ -257,7 +273,8 @@ int fd_decode_attn_multi(fd_dtype_t dt, const void* q, const void* k, const void
     return fail(FD_ERR_UNSUPPORTED, "G*M=%d query rows per kv-head exceed 32", G * M);
   if (M > 1 && dt != FD_BF16)
     return fail(FD_ERR_UNSUPPORTED, "several query tokens need bf16 inputs");
-  const int nc = (L + chunk - 1) / chunk;
+  const int nc = n_chunks_of(L, chunk);
+  if (int e = check_units(B, M * Hq, nc)) return e;
   if (int e = workspace_gate(ws, ws_bytes, partial_bytes(B, M * Hq, nc, d))) return e;
   if (ws == nullptr) return ok();
   if (!q || !k || !v || !out) return fail(FD_ERR_ARG, "q, k, v and out must not be NULL");
@@ -374,7 +391,8 @@ int fd_ffd_sparse_decode(const void* q, const uint32_t* codes, const uint16_t* z
   if (!(delta >= 0.f)) return fail(FD_ERR_ARG, "delta must be >= 0");
   if (n_sink < 0 || n_local < 0 || n_sink + n_local < 1)
     return fail(FD_ERR_ARG, "need n_sink, n_local >= 0 and n_sink + n_local >= 1");
-  const int nc = (L + chunk - 1) / chunk;
+  const int nc = n_chunks_of(L, chunk);
+  if (int e = check_units(B, Hq, nc)) return e;
   const size_t need = partial_bytes(B, Hq, nc, d) + 2 * align256((size_t)B * Hq * 4);
   if (int e = workspace_gate(ws, ws_bytes, need)) return e;
   if (ws == nullptr) return ok();

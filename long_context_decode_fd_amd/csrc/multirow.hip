@@ -303,7 +303,7 @@ void multi_kernel(MultiArgs a) {
     const bool has_next = un < u_end;
     UnitM nxt = cur;
     if (has_next) decode(un, nxt);
-    const int b = cur.b, kvh = cur.kvh, c = cur.c, c0 = cur.c0, c1 = cur.c1;
+    const int c0 = cur.c0, c1 = cur.c1;
     const char* kb = base_of(a.k, cur);
     const char* vb = base_of(a.v, cur);
 

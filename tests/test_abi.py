@@ -48,6 +48,10 @@ def test_workspace_sizes():
     (dict(chunk=0), _abi.FD_ERR_ARG),
     (dict(B=0), _abi.FD_ERR_ARG),
     (dict(scale=-1.0), _abi.FD_ERR_ARG),
+    # units (sequence, kv-head, chunk) beyond 32-bit indices, and a length
+    # whose chunk count would wrap in 32-bit arithmetic
+    (dict(B=4096, Hq=64, Hkv=64, L=2**31 - 1, chunk=65536), _abi.FD_ERR_UNSUPPORTED),
+    (dict(B=1, Hq=16, Hkv=16, L=2**31 - 1, chunk=16), _abi.FD_ERR_UNSUPPORTED),
 ])
 def test_validation_errors(kw, code):
     args = dict(B=2, Hq=8, Hkv=2, L=100, d=128, chunk=32)
@@ -55,6 +59,14 @@ def test_validation_errors(kw, code):
     with pytest.raises(fd.FdError) as e:
         fd.workspace_bytes("fd_decode_attn", **args)
     assert e.value.code == code
+
+
+def test_chunk_count_near_int_max():
+    # L + chunk - 1 exceeds 32 bits here; the chunk count must not wrap
+    L, chunk, B, Hq = 2**31 - 1, 65536, 1, 8
+    nc = -(-L // chunk)
+    n = fd.workspace_bytes("fd_decode_attn", B=B, Hq=Hq, Hkv=8, L=L, d=128, chunk=chunk)
+    assert n == B * Hq * nc * 128 * 4 + B * Hq * nc * 2 * 4
 
 
 def test_unified_and_ffd_validation():
