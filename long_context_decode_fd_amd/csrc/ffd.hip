@@ -275,12 +275,6 @@ __device__ __forceinline__ u32x2 residual_pairs(uint32_t w) {
                pack_bf16_exact((float)((u >> 16) & 0xFF), (float)(u >> 24))};
 }
 
-// fp32 -> bf16 bits, round to nearest even (finite inputs); p = hi + lo.
-__device__ __forceinline__ uint32_t ffd_bf16_bits(float x) {
-  const uint32_t u = __float_as_uint(x);
-  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
-}
-
 template <int D, int G>
 __global__ __launch_bounds__(kThreads) void ffd_kernel(FfdArgs a) {
   using Gm = Geo<uint16_t, D>;
@@ -527,20 +521,46 @@ __global__ __launch_bounds__(kThreads) void ffd_kernel(FfdArgs a) {
       mh[h] = kNegInf;
       lh[h] = 0.f;
     }
+    // Loads of a tile go through buffer descriptors of this chunk's residual,
+    // step and V rows.  The next tile's residuals are requested as soon as
+    // the current ones are unpacked and its V rows as soon as the current
+    // ones are in LDS, so a tile's loads travel during the previous tile's
+    // math without extra registers.  Slots past the candidate list (and the
+    // whole tile after a wave's last) get an offset beyond the descriptor's
+    // limit: the load is still issued, so every path has the same loads in
+    // flight and the compiler's wait counts stay exact, but it reads zeros
+    // without touching memory.
+    const __amdgpu_buffer_rsrc_t rs_res = buffer_rsrc(res + (rbase + c0) * D, n * D);
+    const __amdgpu_buffer_rsrc_t rs_rs = buffer_rsrc(rsa + (rbase + c0) * NG, n * NG * 2);
+    const __amdgpu_buffer_rsrc_t rs_v = buffer_rsrc(vb + (size_t)c0 * Gm::kRow, n * Gm::kRow);
+    auto res_issue = [&](int t0, u32x4& r0, u32x4& r1, uint32_t& rsh) {
+      const int jn = t0 + n16;
+      const int jr = s_list[min(jn, nu - 1)];
+      const int off = jn < nu ? jr * D + 32 * qg : n * D;
+      r0 = ld16_buf(rs_res, off);
+      r1 = ld16_buf(rs_res, off + 16);
+      rsh = __builtin_amdgcn_raw_buffer_load_b16(
+          rs_rs, jn < nu ? (jr * NG + qg) * 2 : n * NG * 2, 0, kBufferNonTemporal);
+    };
+    auto v_issue = [&](int t0, u32x4 (&vr)[4]) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int jj = t0 + 4 * i + qg;
+        const int jv = s_list[min(jj, nu - 1)];
+        vr[i] = ld16_buf(rs_v, jj < nu ? jv * Gm::kRow + 16 * n16 : n * Gm::kRow);
+      }
+    };
+    u32x4 r0, r1;
+    uint32_t rsh = 0;
+    u32x4 vr[4];   // V rows of tile slots 4i + qg, 16 bytes at 16 * n16
+    if (wave * 16 < nu) {
+      res_issue(wave * 16, r0, r1, rsh);
+      v_issue(wave * 16, vr);
+    }
     for (int t0 = wave * 16; t0 < nu; t0 += kWaves * 16) {
       const int jn = t0 + n16;                      // this lane's candidate slot
       const int jr = s_list[min(jn, nu - 1)];
-      const size_t row = rbase + c0 + jr;
-      const u32x4 r0 = ffd_load(reinterpret_cast<const u32x4*>(res + row * D + 32 * qg));
-      const u32x4 r1 = ffd_load(reinterpret_cast<const u32x4*>(res + row * D + 32 * qg + 16));
-      const float rsf = half_to_float(rsa[row * NG + qg]);
-      u32x4 vr[4];   // V rows of tile slots 4i + qg, 16 bytes at 16 * n16
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int jv = s_list[min(t0 + 4 * i + qg, nu - 1)];
-        vr[i] = ffd_load(reinterpret_cast<const u32x4*>(vb + (size_t)(c0 + jv) * Gm::kRow +
-                                                        16 * n16));
-      }
+      const float rsf = half_to_float(rsh);
       const uint32_t mk = s_mask[jr];
       const bool valid = jn < nu;
       u32x4 bk[4];
@@ -552,6 +572,7 @@ __global__ __launch_bounds__(kThreads) void ffd_kernel(FfdArgs a) {
           bk[t] = u32x4{lo.x, lo.y, hi.x, hi.y};
         }
       }
+      res_issue(t0 + kWaves * 16, r0, r1, rsh);
       float sh[G];   // refined raw scores of this lane's candidate
 #pragma unroll
       for (int tt = 0; tt < NT; ++tt) {
@@ -607,18 +628,24 @@ __global__ __launch_bounds__(kThreads) void ffd_kernel(FfdArgs a) {
       u32x2 ph = {0u, 0u}, pl = {0u, 0u};
       if (n16 < G) {
         const f32x4 pv = *reinterpret_cast<const f32x4*>(pb + n16 * 16 + 4 * qg);
-        uint32_t hb[4], lb[4];
+        // hi = bf16(p), lo = bf16(p - hi), rounded to nearest even by the
+        // hardware conversion (two values per instruction)
+        uint32_t hb[2], lb[2];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          hb[e] = ffd_bf16_bits(pv[e]);
-          lb[e] = ffd_bf16_bits(pv[e] - __uint_as_float(hb[e] << 16));
+        for (int j = 0; j < 2; ++j) {
+          const float x0 = pv[2 * j], x1 = pv[2 * j + 1];
+          hb[j] = __builtin_bit_cast(uint32_t, bf16x2_t{(__bf16)x0, (__bf16)x1});
+          lb[j] = __builtin_bit_cast(
+              uint32_t, bf16x2_t{(__bf16)(x0 - __uint_as_float(hb[j] << 16)),
+                                 (__bf16)(x1 - __uint_as_float(hb[j] & 0xFFFF0000u))});
         }
-        ph = u32x2{hb[0] | (hb[1] << 16), hb[2] | (hb[3] << 16)};
-        pl = u32x2{lb[0] | (lb[1] << 16), lb[2] | (lb[3] << 16)};
+        ph = u32x2{hb[0], hb[1]};
+        pl = u32x2{lb[0], lb[1]};
       }
 #pragma unroll
       for (int i = 0; i < 4; ++i)
         *reinterpret_cast<u32x4*>(lv + (4 * i + qg) * VSTR + 16 * n16) = vr[i];
+      v_issue(t0 + kWaves * 16, vr);
 #pragma unroll
       for (int db = 0; db < D / 16; ++db) {
         const u32x2 vv = __builtin_bit_cast(
