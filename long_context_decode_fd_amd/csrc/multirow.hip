@@ -1,527 +1,15 @@
-// Multi-row decode attention for gfx950: M new query tokens per sequence,
-// each attending to the cache up to its own position ("Flash Decoding"
-// explainer, section 1; the tokens' keys and values are already appended at
-// positions L-M .. L-1).  The G query heads of a kv-head times the M tokens
-// give R = G*M <= 32 query rows (one or two tiles of 16) that share every K
-// and V row -- the flat
-// GEMM case of the "FlashDecoding" deployment blog (section 1), which here
-// runs on the matrix cores:
-//
-//   * K and V rows arrive with fully coalesced 16-byte loads (one wave load
-//     = 1 KiB of consecutive rows) and pass through a small per-wave LDS
-//     tile, from which each lane reads its MFMA operand.
-//   * S^T = K Q^T per 16-position tile with v_mfma_f32_16x16x32_bf16: the A
-//     operand is 16 K rows (lane (n, quad) holds dims 32s + 8 quad .. +8 of
-//     row n at k-step s), the B operand the query rows (same lane map).  In
-//     the 16x16 result a lane holds one query row n and four consecutive
-//     positions 4*quad .. 4*quad+3, which is exactly the A operand layout of
-//     v_mfma_f32_16x16x16_bf16 for P V.
-//   * Online softmax per query row over the wave's batch (row maximum across
-//     the four lanes of the row with two shuffles); p in fp32, split into
-//     bf16 hi + lo parts so that P V keeps fp32-level accuracy (two MFMAs).
-//   * V tiles are read back from LDS transposed with ds_read_b64_tr_b16 (four
-//     positions of one dim per lane, the B operand of P V).
-//   * Split-KV as in the single-query kernel: one wavefront per chunk,
-//     partials (O, m, l) per (token, head, chunk), merged by the common exact
-//     log-sum-exp kernel.
-#include <algorithm>
-
-#include "internal.hpp"
-#include "splitkv.hpp"
+// Multi-row decode, one query tile (G*M <= 16 rows per kv-head), and the
+// dispatch between one and two tiles (the kernel is in multirow.hpp).
+#include "multirow.hpp"
 
 namespace fdk {
 
-typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-typedef short s16x4_t __attribute__((ext_vector_type(4)));
-
-#ifndef FD_MR_TILES
-#define FD_MR_TILES 2   // 16-position tiles per wave batch: 8 K and 8 V loads at d = 128
-#endif
-#ifndef FD_MR_TILES2
-#define FD_MR_TILES2 FD_MR_TILES   // the same with two query tiles
-#endif
-#ifndef FD_MR_PV32_Q1
-#define FD_MR_PV32_Q1 0   // P V on 16x16x32 tile pairs with one query tile
-#endif
-#ifndef FD_MR_PV32_Q2
-#define FD_MR_PV32_Q2 1   // ... with two query tiles
-#endif
-#ifndef FD_MR_BUF_Q1
-#define FD_MR_BUF_Q1 1   // K/V tiles through buffer loads (see issue below), one query tile
-#endif
-#ifndef FD_MR_BUF_Q2
-#define FD_MR_BUF_Q2 0   // ... two query tiles (measured slower: 219 -> 250 us at M = 8)
-#endif
-#ifndef FD_MR_HWSPLIT
-#define FD_MR_HWSPLIT 1   // hi/lo split of P by the hardware bf16 conversion
-#endif
-#ifndef FD_MR_WAVES_PER_EU
-#define FD_MR_WAVES_PER_EU 1
-#endif
-#ifndef FD_MR_HOLD
-#define FD_MR_HOLD 4    // finished units held in registers before their partials are written
-#endif
-
-
-__device__ __forceinline__ f32x4 mfma_qk(const u32x4& a, const u32x4& b, f32x4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
-                                                  __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
-}
-
-__device__ __forceinline__ f32x4 mfma_pv(const u32x2& a, const u32x2& b, f32x4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4_t, a),
-                                                    __builtin_bit_cast(s16x4_t, b), c, 0, 0, 0);
-}
-
-typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-
-// p = hi + lo with hi = bf16(p), lo = bf16(p - hi), both rounded to nearest
-// even by the hardware conversion (two values per instruction): two bf16
-// pairs from four fp32 values.
-__device__ __forceinline__ uint32_t bf16_bits(float x) {
-  const uint32_t u = __float_as_uint(x);
-  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
-}
-__device__ __forceinline__ void split_bf16(const float (&p)[4], u32x2& hi, u32x2& lo) {
-#if !FD_MR_HWSPLIT
-  {
-  uint32_t h[4], l[4];
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    h[e] = bf16_bits(p[e]);
-    l[e] = bf16_bits(p[e] - __uint_as_float(h[e] << 16));
-  }
-  hi = u32x2{h[0] | (h[1] << 16), h[2] | (h[3] << 16)};
-  lo = u32x2{l[0] | (l[1] << 16), l[2] | (l[3] << 16)};
-  return;
-  }
-#endif
-  uint32_t h[2], l[2];
-#pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const float a = p[2 * j], b = p[2 * j + 1];
-    h[j] = __builtin_bit_cast(uint32_t, bf16x2_t{(__bf16)a, (__bf16)b});
-    const float ra = a - __uint_as_float(h[j] << 16);
-    const float rb = b - __uint_as_float(h[j] & 0xFFFF0000u);
-    l[j] = __builtin_bit_cast(uint32_t, bf16x2_t{(__bf16)ra, (__bf16)rb});
-  }
-  hi = u32x2{h[0], h[1]};
-  lo = u32x2{l[0], l[1]};
-}
-
-// QT = query tiles of 16 rows (R = G*M <= 16 * QT); both share every K and V
-// tile.
-template <int D, int QT>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(FD_MR_WAVES_PER_EU)))
-void multi_kernel(MultiArgs a) {
-  constexpr int KS = D / 32;             // QK k-steps (32 dims each)
-  constexpr int DB = D / 16;             // 16-dim blocks of the P V product
-  constexpr int TT = QT == 1 ? FD_MR_TILES : FD_MR_TILES2;
-  constexpr int STEP = 16 * TT;          // positions per wave batch
-  constexpr int ROWB = D * 2;            // bytes per cache row
-  constexpr int LPR = ROWB / 16;         // lanes per row in a coalesced load
-  constexpr int RPI = kWave / LPR;       // rows per wave load
-  constexpr int NI = 16 / RPI;           // wave loads per 16-row tile (= KS)
-  constexpr int LSTR = ROWB + 8;         // LDS row stride: rows 4 apart sit 8 banks apart
-  constexpr int OSTR = D * 4 + 16;       // fp32 O row stride of the store staging
-  constexpr int ORPI = kWave * 16 / (D * 4);   // O rows per wave store
-  static_assert(16 * OSTR <= 2 * 16 * LSTR, "O staging must fit the wave's K/V tiles");
-  __shared__ __align__(16) unsigned char s_kv[kWaves][2][16 * LSTR];
-
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & (kWave - 1);
-  const int n = lane & 15, qd = lane >> 4;
-  const int G = a.Hq / a.Hkv, R = G * a.M;
-  const int stride = (int)gridDim.x * kWaves;
-  const int n_units = a.B * a.Hkv * a.nc;
-  unsigned char* lk = s_kv[wave][0];
-  unsigned char* lv = s_kv[wave][1];
-  const int lrow = lane / LPR, lcol = lane % LPR;   // coalesced-load lane map
-  // Transposing LDS read (ds_read_b64_tr_b16): in each 16-lane group, lane i
-  // receives element i % 4 of the 8-byte reads of lanes i/4, 4 + i/4, 8 + i/4
-  // and 12 + i/4.  Lane n of quad qd therefore points at row 4*qd + n/4, dims
-  // 16*db + 4*(n % 4) of the V tile, and gets V[4*qd + e][16*db + n], e < 4:
-  // four positions of one dim, the B operand of P V.
-  const int tr_off = (4 * qd + (n >> 2)) * LSTR + 8 * (n & 3);
-  const float c_log2 = a.c_log2;
-
-  struct UnitM {
-    int b, kvh, c, c0, c1;
-  };
-  auto decode = [&](int u, UnitM& x) {
-    x.c = u % a.nc;
-    const int bk = u / a.nc;
-    x.kvh = bk % a.Hkv;
-    x.b = bk / a.Hkv;
-    x.c0 = x.c * a.chunk;
-    x.c1 = min(x.c0 + a.chunk, a.L);
-  };
-  auto base_of = [&](const void* t, const UnitM& x) {
-    return reinterpret_cast<const char*>(t) + ((size_t)x.b * a.Hkv + x.kvh) * (size_t)a.L * ROWB;
-  };
-  // Query row n + 16*qt of this lane: token r = row / G, head kvh*G + row % G;
-  // its last visible position is L - M + r.  Rows >= R are padding (q = 0).
-  int lim[QT];
-#pragma unroll
-  for (int qt = 0; qt < QT; ++qt) lim[qt] = a.L - a.M + (n + 16 * qt) / G;
-  u32x4 qf[QT][KS];
-  auto load_q = [&](const UnitM& x) {
-#pragma unroll
-    for (int qt = 0; qt < QT; ++qt) {
-      const int row = n + 16 * qt;
-      if (row < R) {
-        const uint16_t* qp =
-            reinterpret_cast<const uint16_t*>(a.q) +
-            (((size_t)x.b * a.M + row / G) * a.Hq + (size_t)x.kvh * G + row % G) * D + 8 * qd;
-#pragma unroll
-        for (int s = 0; s < KS; ++s) qf[qt][s] = ld16(qp + 32 * s);
-      } else {
-#pragma unroll
-        for (int s = 0; s < KS; ++s) qf[qt][s] = u32x4{0, 0, 0, 0};
-      }
-    }
-  };
-  // wave load i of tile tt: rows T + 16*tt + RPI*i + lrow, bytes 16*lcol.
-  // Buffer loads: each 16-row tile gets a descriptor whose base is the tile's
-  // first row and whose byte limit ends at the chunk end c1, so every lane
-  // uses the same offset (lrow, lcol) plus an immediate per load, with no
-  // per-load address arithmetic; rows at or past c1 are outside the limit
-  // and read as zeros without touching memory (their scores are masked and
-  // their p is 0).  The range check covers the lane offset plus the
-  // immediate; the scalar offset is 0.
-  const int lane_off = lrow * ROWB + 16 * lcol;
-  auto issue = [&](const char* __restrict__ src, int T, int c1, u32x4 (&r)[TT][NI]) {
-    constexpr bool kBuf = QT == 1 ? FD_MR_BUF_Q1 : FD_MR_BUF_Q2;
-#pragma unroll
-    for (int tt = 0; tt < TT; ++tt) {
-      if constexpr (kBuf) {
-      const int t0 = T + 16 * tt;
-      const int nrow = min(max(c1 - t0, 0), 16);
-      const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(src + (size_t)t0 * ROWB, nrow * ROWB);
-#pragma unroll
-      for (int i = 0; i < NI; ++i) r[tt][i] = ld16_buf(rs, lane_off + RPI * i * ROWB);
-      } else {
-#pragma unroll
-      for (int i = 0; i < NI; ++i) {
-        const int t = min(T + 16 * tt + RPI * i + lrow, c1 - 1);
-        r[tt][i] = ld16_stream(src + (size_t)t * ROWB + 16 * lcol);
-      }
-      }
-    }
-  };
-  // a tile of 16 rows into this wave's LDS tile (row-major, stride LSTR)
-  auto to_lds = [&](unsigned char* dst, const u32x4 (&r)[NI]) {
-#pragma unroll
-    for (int i = 0; i < NI; ++i)
-      *reinterpret_cast<u32x4*>(dst + (RPI * i + lrow) * LSTR + 16 * lcol) = r[i];
-  };
-
-  // Partials of unit uu, rows ((b*M + r)*Hq + h)*nc + c.  With one query
-  // tile, O goes through the wave's LDS tiles (free between units: the next
-  // unit's K rows are still in registers) so that every store writes 16
-  // bytes per lane and whole rows, instead of 4 bytes per lane in 64-byte
-  // pieces.
-  unsigned char* ost = s_kv[wave][0];
-  auto store_unit = [&](const f32x4 (&o)[QT][DB], const float (&m)[QT], const float (&l)[QT],
-                        int uu) {
-    UnitM x;
-    decode(uu, x);
-#pragma unroll
-    for (int qt = 0; qt < QT; ++qt) {
-      const int rown = n + 16 * qt;
-      if (qd == 0 && rown < R) {
-        const size_t prow =
-            (((size_t)x.b * a.M + rown / G) * a.Hq + (size_t)x.kvh * G + rown % G) * a.nc + x.c;
-        *reinterpret_cast<f32x2*>(a.ml_part + prow * 2) =
-            f32x2{(m[qt] == kNegInf) ? kNegInf : m[qt] * c_log2, l[qt]};
-      }
-      if constexpr (QT == 1) {
-        // lane (n, qd) holds O rows 4*qd + e, dims 16*db + n
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-#pragma unroll
-          for (int db = 0; db < DB; ++db)
-            *reinterpret_cast<float*>(ost + (4 * qd + e) * OSTR + (16 * db + n) * 4) = o[qt][db][e];
-        // read back: wave store i covers rows ORPI*i .. +ORPI, 16 bytes per lane
-        constexpr int LPO = kWave / ORPI;   // lanes per O row
-#pragma unroll
-        for (int i = 0; i < 16 / ORPI; ++i) {
-          const int rr = ORPI * i + lane / LPO, cb = 16 * (lane % LPO);
-          const f32x4 v = *reinterpret_cast<const f32x4*>(ost + rr * OSTR + cb);
-          const int row = 16 * qt + rr;
-          if (row < R) {
-            const size_t prow =
-                (((size_t)x.b * a.M + row / G) * a.Hq + (size_t)x.kvh * G + row % G) * a.nc + x.c;
-            *reinterpret_cast<f32x4*>(reinterpret_cast<unsigned char*>(a.o_part + prow * D) + cb) =
-                v;
-          }
-        }
-      } else {
-        // two query tiles: straight from the MFMA layout (the staging
-        // measured slower at this register load)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int row = 16 * qt + 4 * qd + e;
-          if (row < R) {
-            const size_t prow =
-                (((size_t)x.b * a.M + row / G) * a.Hq + (size_t)x.kvh * G + row % G) * a.nc + x.c;
-#pragma unroll
-            for (int db = 0; db < DB; ++db) a.o_part[prow * D + 16 * db + n] = o[qt][db][e];
-          }
-        }
-      }
-    }
-  };
-  // Finished units wait in registers (up to H of them, one query tile only)
-  // and are written together when H are held or the wave has no unit left.
-  // Stores count on the same vector-memory counter as loads: partials
-  // stored between units made the next unit's first K wait for them.
-  constexpr int H = QT == 1 ? FD_MR_HOLD : 1;
-  f32x4 hold_o[H][QT][DB];
-  float hold_m[H][QT], hold_l[H][QT];
-  int hold_u[H];
-  int held = 0;   // wave-uniform
-
-  // wave w takes the consecutive units [w*per, (w+1)*per): consecutive
-  // chunks of one (sequence, kv-head), a single contiguous stretch of K and
-  // V (measured 186 -> 174 us at M = 4 against taking every W-th unit)
-  const int per = (n_units + stride - 1) / stride;
-  // wave-uniform by construction; readfirstlane lets the compiler keep the
-  // unit (and the descriptors built from it) in scalar registers
-  int u = __builtin_amdgcn_readfirstlane(((int)blockIdx.x * kWaves + wave) * per);
-  const int u_end = min(u + per, n_units);
-  if (u >= n_units) return;
-  UnitM cur;
-  decode(u, cur);
-  u32x4 kr[TT][NI], vr[TT][NI];
-  load_q(cur);
-  issue(base_of(a.k, cur), cur.c0, cur.c1, kr);
-  // The last batch of a unit requests the next unit's query and first K rows
-  // before the unit's partials are stored: stores count on the same
-  // vector-memory counter as loads, so loads issued after them would wait.
-  while (true) {
-    const int un = u + 1;
-    const bool has_next = un < u_end;
-    UnitM nxt = cur;
-    if (has_next) decode(un, nxt);
-    const int c0 = cur.c0, c1 = cur.c1;
-    const char* kb = base_of(a.k, cur);
-    const char* vb = base_of(a.v, cur);
-
-    f32x4 o[QT][DB];
-    float m[QT], l[QT];   // row's running maximum (raw) and this lane's part of l
-#pragma unroll
-    for (int qt = 0; qt < QT; ++qt) {
-      m[qt] = kNegInf;
-      l[qt] = 0.f;
-#pragma unroll
-      for (int db = 0; db < DB; ++db) o[qt][db] = f32x4{0.f, 0.f, 0.f, 0.f};
-    }
-    for (int T = c0; T < c1; T += STEP) {
-      issue(vb, T, c1, vr);
-      float sc[QT][TT][4];
-#pragma unroll
-      for (int tt = 0; tt < TT; ++tt) {
-        // A operand of k-step s: dims 32s + 8 qd .. +8 of row n
-        to_lds(lk, kr[tt]);
-        f32x4 acc[QT];
-#pragma unroll
-        for (int qt = 0; qt < QT; ++qt) acc[qt] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int s = 0; s < KS; ++s) {
-          const u32x4 ka = *reinterpret_cast<const u32x4*>(lk + n * LSTR + 64 * s + 16 * qd);
-#pragma unroll
-          for (int qt = 0; qt < QT; ++qt) acc[qt] = mfma_qk(ka, qf[qt][s], acc[qt]);
-        }
-#pragma unroll
-        for (int qt = 0; qt < QT; ++qt)
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int pos = T + 16 * tt + 4 * qd + e;
-            sc[qt][tt][e] = (pos < c1 && pos <= lim[qt]) ? acc[qt][e] : kNegInf;
-          }
-      }
-      if constexpr (QT == 1) {
-        // one query tile: K is requested on every path (after the wave's
-        // last batch, this batch's rows again, unused), so the compiler's
-        // wait counts agree on all paths and P V waits for this batch's V
-        // rows only, not for these loads (measured 189 -> 182 us at M = 4;
-        // with two tiles, whose registers are full, it measured slower)
-        const char* src = kb;
-        int t_next = T + STEP, c_end = c1;
-        if (T + STEP >= c1 && has_next) {
-          load_q(nxt);
-          src = base_of(a.k, nxt);
-          t_next = nxt.c0;
-          c_end = nxt.c1;
-        } else if (T + STEP >= c1) {
-          t_next = T;
-        }
-        issue(src, t_next, c_end, kr);
-      } else {
-        if (T + STEP < c1) {
-          issue(kb, T + STEP, c1, kr);
-        } else if (has_next) {
-          load_q(nxt);
-          issue(base_of(a.k, nxt), nxt.c0, nxt.c1, kr);
-        }
-      }
-
-      float bias[QT];
-#pragma unroll
-      for (int qt = 0; qt < QT; ++qt) {
-        float bm = kNegInf;
-#pragma unroll
-        for (int tt = 0; tt < TT; ++tt)
-#pragma unroll
-          for (int e = 0; e < 4; ++e) bm = fmaxf(bm, sc[qt][tt][e]);
-        bm = fmaxf(bm, __shfl_xor(bm, 16));
-        bm = fmaxf(bm, __shfl_xor(bm, 32));
-        const float mn = fmaxf(m[qt], bm);
-        if (__any(mn > m[qt])) {
-          const float alpha = (mn == m[qt]) ? 1.f : exp2_hw((m[qt] - mn) * c_log2);
-          l[qt] *= alpha;
-          // O rows 4*qd + e take the factors of those rows (held by lanes 4*qd + e)
-          float ae[4];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) ae[e] = __shfl(alpha, 4 * qd + e);
-#pragma unroll
-          for (int db = 0; db < DB; ++db)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) o[qt][db][e] *= ae[e];
-          m[qt] = mn;
-        }
-        bias[qt] = (m[qt] == kNegInf) ? 0.f : m[qt] * c_log2;
-      }
-
-      u32x2 ph[QT][TT], pl[QT][TT];
-#pragma unroll
-      for (int tt = 0; tt < TT; ++tt)
-#pragma unroll
-        for (int qt = 0; qt < QT; ++qt) {
-          float p[4];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            p[e] = exp2_hw(fmaf(sc[qt][tt][e], c_log2, -bias[qt]));
-            l[qt] += p[e];
-          }
-          split_bf16(p, ph[qt][tt], pl[qt][tt]);
-        }
-      // P V over pairs of 16-position tiles with v_mfma_f32_16x16x32_bf16:
-      // k = 8 qd + j stands for position 4 qd + j % 4 of tile 2 tp + j / 4,
-      // so a lane's A operand is its P values of both tiles and its B
-      // operand the transposed reads of both V tiles (each staged in one of
-      // the wave's two LDS tiles; the K tiles are no longer needed here, and
-      // LDS keeps the wave's order).
-      constexpr bool kPv32 = QT == 1 ? FD_MR_PV32_Q1 : FD_MR_PV32_Q2;
-      constexpr int NTP = kPv32 ? TT / 2 : 0;   // tile pairs on 16x16x32
-#pragma unroll
-      for (int tp = 0; tp < NTP; ++tp) {
-        to_lds(lk, vr[2 * tp]);
-        to_lds(lv, vr[2 * tp + 1]);
-#pragma unroll
-        for (int db = 0; db < DB; ++db) {
-          const u32x2 v0 = __builtin_bit_cast(
-              u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                         (__attribute__((address_space(3))) s16x4_t*)(lk + tr_off + 32 * db)));
-          const u32x2 v1 = __builtin_bit_cast(
-              u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                         (__attribute__((address_space(3))) s16x4_t*)(lv + tr_off + 32 * db)));
-          const u32x4 vb = u32x4{v0.x, v0.y, v1.x, v1.y};
-#pragma unroll
-          for (int qt = 0; qt < QT; ++qt) {
-            const u32x2 h0 = ph[qt][2 * tp], h1 = ph[qt][2 * tp + 1];
-            const u32x2 l0 = pl[qt][2 * tp], l1 = pl[qt][2 * tp + 1];
-            o[qt][db] = mfma_qk(u32x4{h0.x, h0.y, h1.x, h1.y}, vb, o[qt][db]);
-            o[qt][db] = mfma_qk(u32x4{l0.x, l0.y, l1.x, l1.y}, vb, o[qt][db]);
-          }
-        }
-      }
-      // the remaining tiles one at a time on v_mfma_f32_16x16x16_bf16
-      // (position 4 qd + e)
-#pragma unroll
-      for (int tt = 2 * NTP; tt < TT; ++tt) {
-        to_lds(lv, vr[tt]);
-#pragma unroll
-        for (int db = 0; db < DB; ++db) {
-          const u32x2 vv = __builtin_bit_cast(
-              u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                         (__attribute__((address_space(3))) s16x4_t*)(lv + tr_off + 32 * db)));
-#pragma unroll
-          for (int qt = 0; qt < QT; ++qt) {
-            o[qt][db] = mfma_pv(ph[qt][tt], vv, o[qt][db]);
-            o[qt][db] = mfma_pv(pl[qt][tt], vv, o[qt][db]);
-          }
-        }
-      }
-    }
-
-#pragma unroll
-    for (int qt = 0; qt < QT; ++qt) {
-      // l of row n + 16*qt: the four lanes of the row hold parts
-      l[qt] += __shfl_xor(l[qt], 16);
-      l[qt] += __shfl_xor(l[qt], 32);
-    }
-    if constexpr (H > 1) {
-#pragma unroll
-      for (int h = 0; h < H; ++h) {
-        if (held == h) {   // wave-uniform
-#pragma unroll
-          for (int qt = 0; qt < QT; ++qt) {
-            hold_m[h][qt] = m[qt];
-            hold_l[h][qt] = l[qt];
-#pragma unroll
-            for (int db = 0; db < DB; ++db) hold_o[h][qt][db] = o[qt][db];
-          }
-          hold_u[h] = u;
-        }
-      }
-      if (++held == H || !has_next) {
-#pragma unroll
-        for (int h = 0; h < H; ++h)
-          if (h < held) store_unit(hold_o[h], hold_m[h], hold_l[h], hold_u[h]);
-        held = 0;
-      }
-    } else {
-      store_unit(o, m, l, u);
-    }
-    if (!has_next) break;
-    cur = nxt;
-    u = un;
-  }
-}
-
-// Workgroups of this kernel that fit on one compute unit.
-template <class K>
-static int multi_blocks_per_cu(K kernel) {
-  int n = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kernel, kThreads, 0) != hipSuccess ||
-      n <= 0)
-    n = 1;
-  return n;
-}
-
-template <int D, int QT>
-static hipError_t launch_multi_d(const MultiArgs& a, hipStream_t s) {
-  auto kernel = multi_kernel<D, QT>;
-  static const int per_cu = multi_blocks_per_cu(kernel);
-  int dev = 0, cus = 256;
-  if (hipGetDevice(&dev) != hipSuccess ||
-      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-      cus <= 0)
-    cus = 256;
-  // equal rounds for every wave, as for the single-query kernel
-  const size_t units = (size_t)a.B * a.Hkv * a.nc;
-  const size_t slots = (size_t)cus * per_cu * kWaves;
-  const size_t rounds = (units + slots - 1) / slots;
-  const unsigned grid = (unsigned)((units + kWaves * rounds - 1) / (kWaves * rounds));
-  hipLaunchKernelGGL(kernel, dim3(grid), dim3(kThreads), 0, s, a);
-  return hipGetLastError();
-}
+hipError_t launch_multi_q2(int D, const MultiArgs& a, hipStream_t s);
 
 hipError_t launch_multi(int D, const MultiArgs& a, hipStream_t s) {
-  const bool two = (a.Hq / a.Hkv) * a.M > 16;
-  if (D == 64) return two ? launch_multi_d<64, 2>(a, s) : launch_multi_d<64, 1>(a, s);
-  if (D == 128) return two ? launch_multi_d<128, 2>(a, s) : launch_multi_d<128, 1>(a, s);
+  if ((a.Hq / a.Hkv) * a.M > 16) return launch_multi_q2(D, a, s);
+  if (D == 64) return launch_multi_d<64, 1>(a, s);
+  if (D == 128) return launch_multi_d<128, 1>(a, s);
   return hipErrorInvalidValue;
 }
 
