@@ -86,12 +86,13 @@ __device__ __forceinline__ void fixed_update(const float (&s)[NB][G], const u32x
     float vf[VEC];
 #pragma unroll
     for (int pc = 0; pc < P; ++pc) slice_vals<E>(vr[i * P + pc], vf + pc * (VEC / P));
+    float p[G];
+    row_exp2<G>(s[i], base, [c_log2](float x, float b) { return (x - b) * c_log2; }, p);
 #pragma unroll
     for (int h = 0; h < G; ++h) {
-      const float p = exp2_hw((s[i][h] - base[h]) * c_log2);
-      l[h] += p;
+      l[h] += p[h];
 #pragma unroll
-      for (int e = 0; e < VEC; ++e) acc[h][e] = fmaf(p, vf[e], acc[h][e]);
+      for (int e = 0; e < VEC; ++e) acc[h][e] = fmaf(p[h], vf[e], acc[h][e]);
     }
   }
 }

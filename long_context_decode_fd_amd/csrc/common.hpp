@@ -93,6 +93,33 @@ __device__ __forceinline__ float group_max(float x) {
   return x;
 }
 
+// The two values of lane i's pair {i, i ^ OFF} (OFF = 4, 8, 16 or 32),
+// without the LDS crossbar: a and b are the pair's two values (for OFF >= 16
+// in the order lower lane, upper lane in both lanes; for OFF < 16 own value,
+// then the partner's).  Results that are symmetric in a and b are therefore
+// bitwise equal in both lanes.  Every lane of the wave must be active.
+template <int OFF>
+__device__ __forceinline__ void lane_pair(float x, float& a, float& b) {
+  static_assert(OFF == 4 || OFF == 8 || OFF == 16 || OFF == 32, "pair offset");
+  if constexpr (OFF == 16 || OFF == 32) {
+    // v_permlane{16,32}_swap of x with itself: element 0 holds lane
+    // i & ~OFF's value, element 1 lane i | OFF's
+    const uint32_t u = __float_as_uint(x);
+    const auto r = OFF == 16 ? __builtin_amdgcn_permlane16_swap(u, u, false, false)
+                             : __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    a = __uint_as_float(r[0]);
+    b = __uint_as_float(r[1]);
+  } else if constexpr (OFF == 8) {
+    a = x;
+    b = dpp<0x128>(x);   // row_ror:8 = lane i ^ 8 inside a row of 16
+  } else {
+    const float up = dpp<0x104>(x);   // row_shl:4: lane i + 4
+    const float dn = dpp<0x114>(x);   // row_shr:4: lane i - 4
+    a = x;
+    b = (__lane_id() & 4) ? dn : up;
+  }
+}
+
 // Whole-wave reductions (used outside the hot loops).
 __device__ __forceinline__ float wave_max(float x) {
 #pragma unroll

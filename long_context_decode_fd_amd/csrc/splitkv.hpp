@@ -126,6 +126,37 @@ __device__ __forceinline__ void state_reset(float (&acc)[G][VEC], float (&m)[G],
   }
 }
 
+// Exponentials of one cache row for the G heads of the kv-head:
+// p[h] = exp2(f(x[h], y[h])).  Every lane of a row holds the same x and y
+// (the row sums are reduced symmetrically), so for G = 2 or 4 each lane
+// evaluates only head lane % G and takes the others from the lanes of its
+// quad, which hold heads 0 .. G-1 of the same row: one exponential (a
+// quarter-rate instruction) and G moves instead of G exponentials, with the
+// same bits.  F maps (x, y) to the exponent.
+template <int G, class F>
+__device__ __forceinline__ void row_exp2(const float (&x)[G], const float (&y)[G], F f,
+                                         float (&p)[G]) {
+  if constexpr (G == 2 || G == 4) {
+    const int hs = (int)(threadIdx.x % G);
+    float xs = x[0], ys = y[0];
+#pragma unroll
+    for (int h = 1; h < G; ++h) {
+      xs = hs == h ? x[h] : xs;
+      ys = hs == h ? y[h] : ys;
+    }
+    const float pm = exp2_hw(f(xs, ys));
+    p[0] = dpp<0x00>(pm);   // quad_perm [0,0,0,0]
+    p[1] = dpp<0x55>(pm);   // quad_perm [1,1,1,1]
+    if constexpr (G == 4) {
+      p[2] = dpp<0xAA>(pm);
+      p[3] = dpp<0xFF>(pm);
+    }
+  } else {
+#pragma unroll
+    for (int h = 0; h < G; ++h) p[h] = exp2_hw(f(x[h], y[h]));
+  }
+}
+
 // Online-softmax update of a row slot with a batch of NB rows.
 // s[i][h]: raw dot products q_h . k_i (-inf for rows that do not count);
 // m[h]: running maximum in the same raw units.  The accumulator is rescaled
@@ -162,12 +193,13 @@ __device__ __forceinline__ void online_update(const float (&s)[NB][G],
     float vf[VEC];
 #pragma unroll
     for (int pc = 0; pc < P; ++pc) slice_vals<E>(vr[i * P + pc], vf + pc * (VEC / P));
+    float p[G];
+    row_exp2<G>(s[i], bias, [c_log2](float x, float b) { return fmaf(x, c_log2, -b); }, p);
 #pragma unroll
     for (int h = 0; h < G; ++h) {
-      const float p = exp2_hw(fmaf(s[i][h], c_log2, -bias[h]));
-      l[h] += p;
+      l[h] += p[h];
 #pragma unroll
-      for (int e = 0; e < VEC; ++e) acc[h][e] = fmaf(p, vf[e], acc[h][e]);
+      for (int e = 0; e < VEC; ++e) acc[h][e] = fmaf(p[h], vf[e], acc[h][e]);
     }
   }
 }
@@ -179,6 +211,35 @@ __device__ __forceinline__ void state_to_log2(float (&m)[G], float c_log2) {
   for (int h = 0; h < G; ++h) m[h] = (m[h] == kNegInf) ? kNegInf : m[h] * c_log2;
 }
 
+// One exchange of the slot merge: lanes i and i ^ OFF combine their states
+// (then OFF * 2, ... up to 32).  Both lanes of a pair compute the same
+// symmetric expression, so they end with identical bits; the two weighted
+// terms are rounded separately before the add (no fused multiply-add).
+template <int OFF, int G, int VEC>
+__device__ __forceinline__ void slot_merge_step(float (&acc)[G][VEC], float (&m)[G],
+                                                float (&l)[G]) {
+#pragma clang fp contract(off)
+  if constexpr (OFF < kWave) {
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      float ma, mb, la, lb;
+      lane_pair<OFF>(m[h], ma, mb);
+      lane_pair<OFF>(l[h], la, lb);
+      const float M = fmaxf(ma, mb);
+      const float wa = exp2_diff(ma, M), wb = exp2_diff(mb, M);
+      l[h] = la * wa + lb * wb;
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) {
+        float xa, xb;
+        lane_pair<OFF>(acc[h][e], xa, xb);
+        acc[h][e] = xa * wa + xb * wb;
+      }
+      m[h] = M;
+    }
+    slot_merge_step<OFF * 2, G, VEC>(acc, m, l);
+  }
+}
+
 // Merge the row slots of one wave with shuffles: afterwards every lane holds
 // the merged state (O relative to m, m in log2 units, l) of its column.  The
 // two weighted terms are rounded separately and then added (no fused
@@ -187,23 +248,7 @@ __device__ __forceinline__ void state_to_log2(float (&m)[G], float c_log2) {
 template <int G, int VEC, int LPT>
 __device__ __forceinline__ void wave_merge(float (&acc)[G][VEC], float (&m)[G], float (&l)[G]) {
 #pragma clang fp contract(off)
-#pragma unroll
-  for (int off = LPT; off < kWave; off <<= 1) {
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-      const float mo = __shfl_xor(m[h], off);
-      const float lo = __shfl_xor(l[h], off);
-      const float M = fmaxf(m[h], mo);
-      const float wa = exp2_diff(m[h], M), wb = exp2_diff(mo, M);
-      l[h] = l[h] * wa + lo * wb;
-#pragma unroll
-      for (int e = 0; e < VEC; ++e) {
-        const float ao = __shfl_xor(acc[h][e], off);
-        acc[h][e] = acc[h][e] * wa + ao * wb;
-      }
-      m[h] = M;
-    }
-  }
+  slot_merge_step<LPT, G, VEC>(acc, m, l);
 }
 
 // Write one lane's column of a merged state as the partial rows
@@ -246,23 +291,7 @@ __device__ __forceinline__ void combine_store(CombineLds<G, D>& lds, float (&acc
                                               float (&m)[G], float (&l)[G], float* o_part,
                                               float* ml_part, size_t prow0, size_t hstride) {
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & (kWave - 1);
-#pragma unroll
-  for (int off = LPT; off < kWave; off <<= 1) {
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-      const float mo = __shfl_xor(m[h], off);
-      const float lo = __shfl_xor(l[h], off);
-      const float M = fmaxf(m[h], mo);
-      const float wa = exp2_diff(m[h], M), wb = exp2_diff(mo, M);
-      l[h] = l[h] * wa + lo * wb;
-#pragma unroll
-      for (int e = 0; e < VEC; ++e) {
-        const float ao = __shfl_xor(acc[h][e], off);
-        acc[h][e] = acc[h][e] * wa + ao * wb;
-      }
-      m[h] = M;
-    }
-  }
+  slot_merge_step<LPT, G, VEC>(acc, m, l);
   if (lane < LPT) {
 #pragma unroll
     for (int h = 0; h < G; ++h)
