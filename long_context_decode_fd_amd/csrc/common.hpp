@@ -40,59 +40,6 @@ enum : int {
   kRowMirror = 0x140,     // lane i <-> 15-i inside each row
 };
 
-// Sum over aligned groups of N lanes (N = 4, 8, 16 or 32); every lane of the
-// group receives the group's sum.  After the two quad steps each quad holds
-// its sum; the half-row mirror pairs lane i with a lane of the other quad,
-// the row mirror pairs the two halves, and a swizzle swaps 16-lane halves.
-template <int N>
-__device__ __forceinline__ float group_sum(float x) {
-  static_assert(N == 4 || N == 8 || N == 16 || N == 32, "group size");
-  x += dpp<kQuadXor1>(x);
-  x += dpp<kQuadXor2>(x);
-  if constexpr (N >= 8) x += dpp<kRowHalfMirror>(x);
-  if constexpr (N >= 16) x += dpp<kRowMirror>(x);
-  if constexpr (N >= 32)
-    x += __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(x), 0x401F));
-  return x;
-}
-
-// group_sum over every element of an array, one butterfly step at a time
-// across the whole array, so no step waits on the one just issued.
-template <int N, int M>
-__device__ __forceinline__ void group_sum_n(float (&x)[M]) {
-  static_assert(N == 4 || N == 8 || N == 16 || N == 32, "group size");
-#pragma unroll
-  for (int k = 0; k < M; ++k) x[k] += dpp<kQuadXor1>(x[k]);
-#pragma unroll
-  for (int k = 0; k < M; ++k) x[k] += dpp<kQuadXor2>(x[k]);
-  if constexpr (N >= 8) {
-#pragma unroll
-    for (int k = 0; k < M; ++k) x[k] += dpp<kRowHalfMirror>(x[k]);
-  }
-  if constexpr (N >= 16) {
-#pragma unroll
-    for (int k = 0; k < M; ++k) x[k] += dpp<kRowMirror>(x[k]);
-  }
-  if constexpr (N >= 32) {
-#pragma unroll
-    for (int k = 0; k < M; ++k)
-      x[k] += __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(x[k]), 0x401F));
-  }
-}
-
-// Same groups, maximum.
-template <int N>
-__device__ __forceinline__ float group_max(float x) {
-  static_assert(N == 4 || N == 8 || N == 16 || N == 32, "group size");
-  x = fmaxf(x, dpp<kQuadXor1>(x));
-  x = fmaxf(x, dpp<kQuadXor2>(x));
-  if constexpr (N >= 8) x = fmaxf(x, dpp<kRowHalfMirror>(x));
-  if constexpr (N >= 16) x = fmaxf(x, dpp<kRowMirror>(x));
-  if constexpr (N >= 32)
-    x = fmaxf(x, __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(x), 0x401F)));
-  return x;
-}
-
 // The two values of lane i's pair {i, i ^ OFF} (OFF = 4, 8, 16 or 32),
 // without the LDS crossbar: a and b are the pair's two values (for OFF >= 16
 // in the order lower lane, upper lane in both lanes; for OFF < 16 own value,
@@ -118,6 +65,70 @@ __device__ __forceinline__ void lane_pair(float x, float& a, float& b) {
     a = x;
     b = (__lane_id() & 4) ? dn : up;
   }
+}
+
+// Sum and maximum over lane i's pair {i, i ^ OFF}, the same bits in both lanes.
+template <int OFF>
+__device__ __forceinline__ float pair_sum(float x) {
+  float a, b;
+  lane_pair<OFF>(x, a, b);
+  return a + b;
+}
+template <int OFF>
+__device__ __forceinline__ float pair_max(float x) {
+  float a, b;
+  lane_pair<OFF>(x, a, b);
+  return fmaxf(a, b);
+}
+
+// Sum over aligned groups of N lanes (N = 4, 8, 16 or 32); every lane of the
+// group receives the group's sum.  After the two quad steps each quad holds
+// its sum; the half-row mirror pairs lane i with a lane of the other quad,
+// the row mirror pairs the two halves, and a pair exchange joins two rows of 16.
+template <int N>
+__device__ __forceinline__ float group_sum(float x) {
+  static_assert(N == 4 || N == 8 || N == 16 || N == 32, "group size");
+  x += dpp<kQuadXor1>(x);
+  x += dpp<kQuadXor2>(x);
+  if constexpr (N >= 8) x += dpp<kRowHalfMirror>(x);
+  if constexpr (N >= 16) x += dpp<kRowMirror>(x);
+  if constexpr (N >= 32) x = pair_sum<16>(x);
+  return x;
+}
+
+// group_sum over every element of an array, one butterfly step at a time
+// across the whole array, so no step waits on the one just issued.
+template <int N, int M>
+__device__ __forceinline__ void group_sum_n(float (&x)[M]) {
+  static_assert(N == 4 || N == 8 || N == 16 || N == 32, "group size");
+#pragma unroll
+  for (int k = 0; k < M; ++k) x[k] += dpp<kQuadXor1>(x[k]);
+#pragma unroll
+  for (int k = 0; k < M; ++k) x[k] += dpp<kQuadXor2>(x[k]);
+  if constexpr (N >= 8) {
+#pragma unroll
+    for (int k = 0; k < M; ++k) x[k] += dpp<kRowHalfMirror>(x[k]);
+  }
+  if constexpr (N >= 16) {
+#pragma unroll
+    for (int k = 0; k < M; ++k) x[k] += dpp<kRowMirror>(x[k]);
+  }
+  if constexpr (N >= 32) {
+#pragma unroll
+    for (int k = 0; k < M; ++k) x[k] = pair_sum<16>(x[k]);
+  }
+}
+
+// Same groups, maximum.
+template <int N>
+__device__ __forceinline__ float group_max(float x) {
+  static_assert(N == 4 || N == 8 || N == 16 || N == 32, "group size");
+  x = fmaxf(x, dpp<kQuadXor1>(x));
+  x = fmaxf(x, dpp<kQuadXor2>(x));
+  if constexpr (N >= 8) x = fmaxf(x, dpp<kRowHalfMirror>(x));
+  if constexpr (N >= 16) x = fmaxf(x, dpp<kRowMirror>(x));
+  if constexpr (N >= 32) x = pair_max<16>(x);
+  return x;
 }
 
 // Whole-wave reductions (used outside the hot loops).

@@ -380,8 +380,7 @@ __global__ __launch_bounds__(kThreads) void ffd_kernel(FfdArgs a) {
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             sc[e] = fmaf(zb, qsum[tt][e], st * cc[e]);
-            sc[e] += __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(sc[e]), 0x401F));
-            sc[e] += __shfl_xor(sc[e], 32);
+            sc[e] = pair_sum<32>(pair_sum<16>(sc[e]));
             const int h = 4 * tt + e;
             const bool cand = (sc[e] >= thr[h]) || (c0 + jr == jst[h]);
             bits |= cand ? (1u << h) : 0u;
@@ -583,8 +582,7 @@ __global__ __launch_bounds__(kThreads) void ffd_kernel(FfdArgs a) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           float corr = rsf * fmaf(-128.f, qsum[tt][e], cc[e]);
-          corr += __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(corr), 0x401F));
-          corr += __shfl_xor(corr, 32);
+          corr = pair_sum<32>(pair_sum<16>(corr));
           const int h = 4 * tt + e;
           sh[h] = (valid && ((mk >> h) & 1u)) ? sv[e] + corr : kNegInf;
         }

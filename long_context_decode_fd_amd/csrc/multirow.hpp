@@ -376,8 +376,7 @@ void multi_kernel(MultiArgs a) {
         for (int tt = 0; tt < TT; ++tt)
 #pragma unroll
           for (int e = 0; e < 4; ++e) bm = fmaxf(bm, sc[qt][tt][e]);
-        bm = fmaxf(bm, __shfl_xor(bm, 16));
-        bm = fmaxf(bm, __shfl_xor(bm, 32));
+        bm = pair_max<32>(pair_max<16>(bm));
         const float mn = fmaxf(m[qt], bm);
         if (__any(mn > m[qt])) {
           const float alpha = (mn == m[qt]) ? 1.f : exp2_hw((m[qt] - mn) * c_log2);
@@ -463,8 +462,7 @@ void multi_kernel(MultiArgs a) {
 #pragma unroll
     for (int qt = 0; qt < QT; ++qt) {
       // l of row n + 16*qt: the four lanes of the row hold parts
-      l[qt] += __shfl_xor(l[qt], 16);
-      l[qt] += __shfl_xor(l[qt], 32);
+      l[qt] = pair_sum<32>(pair_sum<16>(l[qt]));
     }
     if constexpr (H > 1) {
 #pragma unroll
