@@ -40,7 +40,8 @@ typedef short s16x4_t __attribute__((ext_vector_type(4)));
 #define FD_MR_TILES 2   // 16-position tiles per wave batch: 8 K and 8 V loads at d = 128
 #endif
 #ifndef FD_MR_TILES2
-#define FD_MR_TILES2 FD_MR_TILES   // the same with two query tiles
+#define FD_MR_TILES2 4   // with two query tiles (deeper batches pay once the K=32 P V and
+                         // the vector-register accumulators freed registers)
 #endif
 #ifndef FD_MR_PV32_Q1
 #define FD_MR_PV32_Q1 0   // P V on 16x16x32 tile pairs with one query tile
@@ -52,7 +53,8 @@ typedef short s16x4_t __attribute__((ext_vector_type(4)));
 #define FD_MR_BUF_Q1 1   // K/V tiles through buffer loads (see issue below), one query tile
 #endif
 #ifndef FD_MR_BUF_Q2
-#define FD_MR_BUF_Q2 0   // ... two query tiles (measured slower: 219 -> 250 us at M = 8)
+#define FD_MR_BUF_Q2 1   // ... two query tiles (with 4-tile batches; at 2 tiles it measured
+                         // slower, 214 -> 255 us at M = 8)
 #endif
 #ifndef FD_MR_HWSPLIT
 #define FD_MR_HWSPLIT 1   // hi/lo split of P by the hardware bf16 conversion
