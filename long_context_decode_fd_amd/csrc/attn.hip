@@ -339,22 +339,49 @@ void partial_kernel(PartialArgs a) {
     }
   };
 
-  // Finished units wait in registers -- row slot j of the wave keeps the j-th
-  // -- until every slot holds one or the wave runs out of units, and are
-  // then written together.  Stores count on the same vector-memory counter
-  // as loads, so a store issued between units would make the next unit's
-  // first loads wait for it (measured: 11 us of 169 on the 1 GiB workload).
-  float keep_acc[G][VEC], keep_m[G], keep_l[G];
-  size_t keep_row = 0;
+  // Finished units wait in registers until H are held or the wave runs out
+  // of units, and are then written together.  Stores count on the same
+  // vector-memory counter as loads, so a store issued between units would
+  // make the next unit's first loads wait for it (measured: 11 us of 169 on
+  // the 1 GiB workload).  After the reduce-scatter every lane has NK values
+  // of the unit and NCOPY lanes have the same ones, so the copies take turns:
+  // held unit j stays in keep_o[j / NCOPY] of the lanes with copy index
+  // j % NCOPY, which also write it.  The unit's (m, l) and flags stay with
+  // the lanes of row slot j.
+  using SS = SlotScatter<LPT, G, VEC>;
+  constexpr int NK = SS::NK, NCOPY = SS::NCOPY;
+  constexpr int NSLOT = 64 / NK;   // units held per lane (64 registers)
+  constexpr int H = TPL < NSLOT * NCOPY ? TPL : NSLOT * NCOPY;
+  const int cpy = SS::copy(lane);
+  float keep_o[(H + NCOPY - 1) / NCOPY][NK], keep_m[G], keep_l[G];
+  size_t keep_rows[H];
+  size_t keep_row_ml = 0;
   unsigned keep_flags = 0;
   int held = 0;   // wave-uniform
   auto flush = [&]() {
+#pragma unroll
+    for (int j = 0; j < H; ++j) {
+      if (j < held && cpy == j % NCOPY) {
+#pragma unroll
+        for (int k = 0; k < NK; k += 4) {
+          const int K = SS::index(lane, k);
+          const int h = K / VEC, e = K % VEC;
+          float* dst = a.o_part + (keep_rows[j] + (size_t)h * a.nc) * D + Gm::dim(col, e);
+          const float* kv = keep_o[j / NCOPY];
+          *reinterpret_cast<f32x4*>(dst) = f32x4{kv[k], kv[k + 1], kv[k + 2], kv[k + 3]};
+        }
+      }
+    }
     if (grp < held) {
-      store_partial<G, D, VEC, kPg>(keep_acc, keep_m, keep_l, a.o_part, a.ml_part, keep_row,
-                                   (size_t)a.nc, col, col == 0);
+      if (col == 0) {
+#pragma unroll
+        for (int h = 0; h < G; ++h)
+          *reinterpret_cast<f32x2*>(a.ml_part + (keep_row_ml + (size_t)h * a.nc) * 2) =
+              f32x2{keep_m[h], keep_l[h]};
+      }
       if constexpr (kFixed) {
         if (a.flags != nullptr && col < G)
-          a.flags[keep_row + (size_t)col * a.nc] = (uint8_t)((keep_flags >> col) & 1u);
+          a.flags[keep_row_ml + (size_t)col * a.nc] = (uint8_t)((keep_flags >> col) & 1u);
       }
     }
     held = 0;
@@ -468,19 +495,29 @@ void partial_kernel(PartialArgs a) {
       state_to_log2<G>(m, a.c_log2);
     }
 
-    wave_merge<G, VEC, LPT>(acc, m, l);
+    float kept[NK];
+    slot_reduce_scatter<LPT, G, VEC>(acc, m, l, kept);
+    const size_t row0 = ((size_t)cur.b * a.Hq + (size_t)cur.kvh * G) * a.nc + cur.c;
+#pragma unroll
+    for (int j = 0; j < H; ++j) {
+      if (held == j) {   // wave-uniform
+        if (cpy == j % NCOPY) {
+#pragma unroll
+          for (int k = 0; k < NK; ++k) keep_o[j / NCOPY][k] = kept[k];
+        }
+        keep_rows[j] = row0;
+      }
+    }
     if (grp == held) {
 #pragma unroll
       for (int h = 0; h < G; ++h) {
         keep_m[h] = m[h];
         keep_l[h] = l[h];
-#pragma unroll
-        for (int e = 0; e < VEC; ++e) keep_acc[h][e] = acc[h][e];
       }
-      keep_row = ((size_t)cur.b * a.Hq + (size_t)cur.kvh * G) * a.nc + cur.c;
+      keep_row_ml = row0;
       keep_flags = flag_bits;
     }
-    if (++held == TPL) flush();
+    if (++held == H) flush();
     if (!has_next) break;
     cur = nxt;
     u = un;

@@ -240,6 +240,109 @@ __device__ __forceinline__ void slot_merge_step(float (&acc)[G][VEC], float (&m)
   }
 }
 
+// Reduce-scatter of the row slots' states at a unit's end (the same exact
+// merge as wave_merge, split so that no lane does all of it).  First the
+// largest slot maximum M per head and one rescale of each slot to it
+// (2^(m - M)); the exchanges then only add.  Exchanges over fewer than 16
+// lanes (DPP) add every value; the exchanges over 16 and 32 lanes swap two
+// different values per instruction (v_permlane16_swap / v_permlane32_swap
+// of x_k with x_{k + n/2}): lanes of one half receive both lanes' x_k, the
+// others both lanes' x_{k + n/2}, so each lane adds and keeps half, then a
+// quarter, of the values.  Each step adds two values (commutative), so the
+// result does not depend on which lane computes it.  Afterwards m = M
+// and l (summed over all slots) are the same in every lane, and kept[k] is
+// the merged value of flat index h * VEC + e = index(lane, k).
+template <int LPT, int G, int VEC>
+struct SlotScatter {
+  static constexpr int NV = G * VEC;
+  // the exchange over 32 lanes always splits; the one over 16 lanes splits
+  // too when it starts below 32 lanes and leaves at least 4 values per lane
+  // (16-byte stores), otherwise it adds every value
+  static constexpr bool S16 = LPT <= 16 && NV >= 16;
+  static constexpr int NK = NV >> (S16 ? 2 : 1);   // values each lane keeps
+  static __device__ __forceinline__ int index(int lane, int k) {
+    if constexpr (S16)
+      return ((lane >> 4) & 1) * (NV / 2) + ((lane >> 5) & 1) * (NV / 4) + k;
+    else
+      return ((lane >> 5) & 1) * (NV / 2) + k;
+  }
+  // Lanes that differ only in the bits of the adding exchanges (DUP) hold
+  // the same values: NCOPY copies of each, told apart by copy(lane).
+  static constexpr int DUP = (LPT < 16 ? 16 - LPT : 0) | (!S16 && LPT <= 16 ? 16 : 0);
+  static constexpr int NCOPY = 64 * NK / (LPT * NV);
+  static __device__ __forceinline__ int copy(int lane) {
+    int r = 0, o = 0;
+#pragma unroll
+    for (int bit = 0; bit < 6; ++bit) {
+      if ((DUP >> bit) & 1) {
+        r |= ((lane >> bit) & 1) << o;
+        ++o;
+      }
+    }
+    return r;
+  }
+};
+
+template <int OFF>
+__device__ __forceinline__ float slot_max(float x) {
+  if constexpr (OFF < kWave) return slot_max<OFF * 2>(pair_max<OFF>(x));
+  else return x;
+}
+template <int OFF>
+__device__ __forceinline__ float slot_sum(float x) {
+  if constexpr (OFF < kWave) return slot_sum<OFF * 2>(pair_sum<OFF>(x));
+  else return x;
+}
+
+__device__ __forceinline__ void swap_add16(float x, float y, float& out) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(y), false,
+                                                  false);
+  out = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ void swap_add32(float x, float y, float& out) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(y), false,
+                                                  false);
+  out = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+template <int LPT, int G, int VEC>
+__device__ __forceinline__ void slot_reduce_scatter(
+    float (&acc)[G][VEC], float (&m)[G], float (&l)[G],
+    float (&kept)[(G * VEC) >> ((LPT <= 16 && G * VEC >= 16) ? 2 : 1)]) {
+  using SS = SlotScatter<LPT, G, VEC>;
+  constexpr int NV = SS::NV;
+  float x[NV];
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    const float M = slot_max<LPT>(m[h]);
+    const float f = exp2_diff(m[h], M);
+    l[h] = slot_sum<LPT>(l[h] * f);
+    m[h] = M;
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) x[h * VEC + e] = acc[h][e] * f;
+  }
+  // DPP exchanges (offsets LPT .. 8): full sums
+#pragma unroll
+  for (int k = 0; k < NV; ++k) {
+    if constexpr (LPT <= 4) x[k] = pair_sum<4>(x[k]);
+    if constexpr (LPT <= 8) x[k] = pair_sum<8>(x[k]);
+  }
+  if constexpr (SS::S16) {
+    float y[NV / 2];
+#pragma unroll
+    for (int k = 0; k < NV / 2; ++k) swap_add16(x[k], x[k + NV / 2], y[k]);
+#pragma unroll
+    for (int k = 0; k < NV / 4; ++k) swap_add32(y[k], y[k + NV / 4], kept[k]);
+  } else {
+    if constexpr (LPT <= 16) {
+#pragma unroll
+      for (int k = 0; k < NV; ++k) x[k] = pair_sum<16>(x[k]);
+    }
+#pragma unroll
+    for (int k = 0; k < NV / 2; ++k) swap_add32(x[k], x[k + NV / 2], kept[k]);
+  }
+}
+
 // Merge the row slots of one wave with shuffles: afterwards every lane holds
 // the merged state (O relative to m, m in log2 units, l) of its column.  The
 // two weighted terms are rounded separately and then added (no fused
