@@ -132,15 +132,18 @@ __device__ __forceinline__ float group_max(float x) {
 }
 
 // Whole-wave reductions (used outside the hot loops).
+// Pairs at distance 32, 16, 8, 4, 2, 1 in that order, every exchange
+// without the LDS crossbar; each step is commutative, so every lane ends with
+// the same bits.
 __device__ __forceinline__ float wave_max(float x) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) x = fmaxf(x, __shfl_xor(x, o));
-  return x;
+  x = pair_max<4>(pair_max<8>(pair_max<16>(pair_max<32>(x))));
+  x = fmaxf(x, dpp<kQuadXor2>(x));
+  return fmaxf(x, dpp<kQuadXor1>(x));
 }
 __device__ __forceinline__ float wave_sum(float x) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o);
-  return x;
+  x = pair_sum<4>(pair_sum<8>(pair_sum<16>(pair_sum<32>(x))));
+  x += dpp<kQuadXor2>(x);
+  return x + dpp<kQuadXor1>(x);
 }
 
 // bf16 pairs packed in a 32-bit word -> fp32 (exact).
