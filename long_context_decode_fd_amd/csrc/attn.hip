@@ -530,22 +530,22 @@ void partial_kernel(PartialArgs a) {
 // section 2, steps 2-4, with unnormalised O_i):
 //   M = max_i m_i,  w_i = 2^(m_i - M),
 //   out = sum_i w_i O_i / sum_i w_i l_i,  lse = (M + log2 sum_i w_i l_i) ln 2.
-// One workgroup per (sequence, query head).  The weights of up to 256 chunks
-// at a time go to LDS; thread (chunk lane cl, column group cg) then sums
-// chunks cl, cl + CL, ... of 4 columns with independent 16-byte loads, 64
-// chunks at a time (the loads of the first 64 are issued before the maximum
-// is known), and the chunk lanes are reduced through LDS.  The order of every sum is fixed,
-// so runs are bitwise reproducible.  Rows whose chunks all carry the same m
-// (the fixed-maximum path without fallback) get weights of exactly 1.
-constexpr int kMergeWaves = 4;
-constexpr int kMergeThreads = kMergeWaves * kWave;
-
-template <int D>
-__global__ __launch_bounds__(kMergeThreads) void merge_kernel(MergeArgs a) {
+// One workgroup of W waves per (sequence, query head).  The weights of up to
+// 64 W chunks at a time go to LDS; thread (chunk lane cl, column group cg)
+// then sums chunks cl, cl + CL, ... of 4 columns with independent 16-byte
+// loads, 16 W chunks at a time (the loads of the first 16 W are issued
+// before the maximum is known), and the chunk lanes are reduced through LDS.
+// Rows of many chunks take W = 16, so that their loads also share one
+// memory latency.  The order of every sum is fixed, so runs are bitwise
+// reproducible.  Rows whose chunks all carry the same m (the fixed-maximum
+// path without fallback) get weights of exactly 1.
+template <int D, int W>
+__global__ __launch_bounds__(W * kWave) void merge_kernel(MergeArgs a) {
+  constexpr int kMergeThreads = W * kWave;
   constexpr int CG = D / 4;             // 16-byte column groups of a row
   constexpr int CL = kMergeThreads / CG;     // chunk lanes
-  constexpr int kPre = 64 / CL > 0 ? 64 / CL : 1;   // chunks of 64 loaded up front
-  __shared__ float s_red[kMergeWaves];
+  constexpr int kPre = 16 * W / CL > 0 ? 16 * W / CL : 1;   // chunks loaded up front, per lane
+  __shared__ float s_red[W];
   __shared__ float s_w[kMergeThreads];
   __shared__ f32x4 s_o[CL][CG];
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & (kWave - 1);
@@ -580,7 +580,9 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(MergeArgs a) {
   mx = wave_max(mx);
   if (lane == 0) s_red[w] = mx;
   __syncthreads();
-  const float M = fmaxf(fmaxf(s_red[0], s_red[1]), fmaxf(s_red[2], s_red[3]));
+  float M = s_red[0];
+#pragma unroll
+  for (int i = 1; i < W; ++i) M = fmaxf(M, s_red[i]);
 
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   float ls = 0.f;
@@ -635,7 +637,9 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(MergeArgs a) {
       const f32x4 u = s_o[k][tid];
       t.x += u.x; t.y += u.y; t.z += u.z; t.w += u.w;
     }
-    const float den = (s_red[0] + s_red[1]) + (s_red[2] + s_red[3]);
+    float den = 0.f;
+#pragma unroll
+    for (int i = 0; i < W; i += 2) den += s_red[i] + s_red[i + 1];
     reinterpret_cast<f32x4*>(a.out + row * D)[tid] =
         f32x4{t.x / den, t.y / den, t.z / den, t.w / den};
     if (tid == 0 && a.lse != nullptr) a.lse[row] = (M + log2_hw(den)) * kLn2;
@@ -723,9 +727,13 @@ hipError_t launch_partial(int mode, int is_bf16, int D, int G, const PartialArgs
 }
 
 hipError_t launch_merge(int D, int B, const MergeArgs& a, hipStream_t s) {
-  const dim3 grid((unsigned)((size_t)B * a.Hq)), block(kMergeThreads);
-  if (D == 64) hipLaunchKernelGGL((merge_kernel<64>), grid, block, 0, s, a);
-  else if (D == 128) hipLaunchKernelGGL((merge_kernel<128>), grid, block, 0, s, a);
+  const dim3 grid((unsigned)((size_t)B * a.Hq));
+  const bool wide = a.nc >= 128;   // many chunks per row: 16 waves
+  const dim3 block(wide ? 16 * kWave : 4 * kWave);
+  if (D == 64 && wide) hipLaunchKernelGGL((merge_kernel<64, 16>), grid, block, 0, s, a);
+  else if (D == 64) hipLaunchKernelGGL((merge_kernel<64, 4>), grid, block, 0, s, a);
+  else if (D == 128 && wide) hipLaunchKernelGGL((merge_kernel<128, 16>), grid, block, 0, s, a);
+  else if (D == 128) hipLaunchKernelGGL((merge_kernel<128, 4>), grid, block, 0, s, a);
   else return hipErrorInvalidValue;
   return hipGetLastError();
 }
