@@ -539,18 +539,19 @@ void partial_kernel(PartialArgs a) {
 // memory latency.  The order of every sum is fixed, so runs are bitwise
 // reproducible.  Rows whose chunks all carry the same m (the fixed-maximum
 // path without fallback) get weights of exactly 1.
-template <int D, int W>
+template <int D, int W, int CS>
 __global__ __launch_bounds__(W * kWave) void merge_kernel(MergeArgs a) {
   constexpr int kMergeThreads = W * kWave;
-  constexpr int CG = D / 4;             // 16-byte column groups of a row
+  constexpr int CG = D / 4 / CS;        // 16-byte column groups of this workgroup's columns
   constexpr int CL = kMergeThreads / CG;     // chunk lanes
-  constexpr int kPre = 16 * W / CL > 0 ? 16 * W / CL : 1;   // chunks loaded up front, per lane
+  constexpr int kPre = 16 * W * CS / CL > 0 ? 16 * W * CS / CL : 1;   // chunks up front, per lane
   __shared__ float s_red[W];
   __shared__ float s_w[kMergeThreads];
   __shared__ f32x4 s_o[CL][CG];
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & (kWave - 1);
   const int cl = tid / CG, cg = tid % CG;
-  const size_t row = blockIdx.x;
+  const size_t row = blockIdx.x / CS;
+  const int cs = (int)(blockIdx.x % CS);   // this workgroup's share of the columns
   int n = a.nc;
   if (a.seq_lens != nullptr) {
     const int b = (int)(row / a.Hq);
@@ -558,11 +559,13 @@ __global__ __launch_bounds__(W * kWave) void merge_kernel(MergeArgs a) {
     n = min((L + a.chunk - 1) / a.chunk, a.nc);
   }
   if (n == 0) {
-    if (tid < D) a.out[row * D + tid] = 0.f;
-    if (tid == 0 && a.lse != nullptr) a.lse[row] = kNegInf;
+    if (tid < D / CS) a.out[row * D + cs * (D / CS) + tid] = 0.f;
+    if (tid == 0 && cs == 0 && a.lse != nullptr) a.lse[row] = kNegInf;
     return;
   }
-  const f32x4* op = reinterpret_cast<const f32x4*>(a.o_part + row * a.nc * D);
+  // column group cg of this workgroup is column group cs * CG + cg of the row;
+  // chunk k's groups start at op[k * (D / 4)]
+  const f32x4* op = reinterpret_cast<const f32x4*>(a.o_part + row * a.nc * D) + cs * CG;
   const f32x2* mlp = reinterpret_cast<const f32x2*>(a.ml_part + row * a.nc * 2);
 
   // Everything the first kPre * CL chunks need is requested before any
@@ -571,7 +574,7 @@ __global__ __launch_bounds__(W * kWave) void merge_kernel(MergeArgs a) {
 #pragma unroll
   for (int j = 0; j < kPre; ++j) {
     const int k = cl + j * CL;
-    pre[j] = k < n ? op[(size_t)k * CG + cg] : f32x4{0.f, 0.f, 0.f, 0.f};
+    pre[j] = k < n ? op[(size_t)k * (D / 4) + cg] : f32x4{0.f, 0.f, 0.f, 0.f};
   }
   const f32x2 ml0 = tid < n ? mlp[tid] : f32x2{kNegInf, 0.f};
 
@@ -609,7 +612,7 @@ __global__ __launch_bounds__(W * kWave) void merge_kernel(MergeArgs a) {
 #pragma unroll
         for (int j = 0; j < kPre; ++j) {
           const int k = k0 + cl + j * CL;
-          o[j] = k < nt ? op[(size_t)(c0 + k) * CG + cg] : f32x4{0.f, 0.f, 0.f, 0.f};
+          o[j] = k < nt ? op[(size_t)(c0 + k) * (D / 4) + cg] : f32x4{0.f, 0.f, 0.f, 0.f};
         }
       }
 #pragma unroll
@@ -640,9 +643,9 @@ __global__ __launch_bounds__(W * kWave) void merge_kernel(MergeArgs a) {
     float den = 0.f;
 #pragma unroll
     for (int i = 0; i < W; i += 2) den += s_red[i] + s_red[i + 1];
-    reinterpret_cast<f32x4*>(a.out + row * D)[tid] =
+    reinterpret_cast<f32x4*>(a.out + row * D)[cs * CG + tid] =
         f32x4{t.x / den, t.y / den, t.z / den, t.w / den};
-    if (tid == 0 && a.lse != nullptr) a.lse[row] = (M + log2_hw(den)) * kLn2;
+    if (tid == 0 && cs == 0 && a.lse != nullptr) a.lse[row] = (M + log2_hw(den)) * kLn2;
   }
 }
 
@@ -726,14 +729,24 @@ hipError_t launch_partial(int mode, int is_bf16, int D, int G, const PartialArgs
   return hipErrorInvalidValue;
 }
 
+#ifndef FD_MERGE_WIDE_W
+#define FD_MERGE_WIDE_W 4
+#endif
+#ifndef FD_MERGE_WIDE_CS
+#define FD_MERGE_WIDE_CS 4
+#endif
 hipError_t launch_merge(int D, int B, const MergeArgs& a, hipStream_t s) {
-  const dim3 grid((unsigned)((size_t)B * a.Hq));
-  const bool wide = a.nc >= 128;   // many chunks per row: 16 waves
-  const dim3 block(wide ? 16 * kWave : 4 * kWave);
-  if (D == 64 && wide) hipLaunchKernelGGL((merge_kernel<64, 16>), grid, block, 0, s, a);
-  else if (D == 64) hipLaunchKernelGGL((merge_kernel<64, 4>), grid, block, 0, s, a);
-  else if (D == 128 && wide) hipLaunchKernelGGL((merge_kernel<128, 16>), grid, block, 0, s, a);
-  else if (D == 128) hipLaunchKernelGGL((merge_kernel<128, 4>), grid, block, 0, s, a);
+  const size_t rows = (size_t)B * a.Hq;
+  // rows of many chunks: their columns split over FD_MERGE_WIDE_CS
+  // workgroups of FD_MERGE_WIDE_W waves
+  constexpr int WW = FD_MERGE_WIDE_W, CS = FD_MERGE_WIDE_CS;
+  const bool wide = a.nc >= 128;
+  const dim3 grid((unsigned)(wide ? rows * CS : rows));
+  const dim3 block(wide ? WW * kWave : 4 * kWave);
+  if (D == 64 && wide) hipLaunchKernelGGL((merge_kernel<64, WW, CS>), grid, block, 0, s, a);
+  else if (D == 64) hipLaunchKernelGGL((merge_kernel<64, 4, 1>), grid, block, 0, s, a);
+  else if (D == 128 && wide) hipLaunchKernelGGL((merge_kernel<128, WW, CS>), grid, block, 0, s, a);
+  else if (D == 128) hipLaunchKernelGGL((merge_kernel<128, 4, 1>), grid, block, 0, s, a);
   else return hipErrorInvalidValue;
   return hipGetLastError();
 }
