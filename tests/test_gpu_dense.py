@@ -154,3 +154,12 @@ def test_sequence_split_merged_from_two_halves():
     out, lse = fd.merge_partials(o, ml)
     ref, lref = ofd.dense_attention(f64(c.q), f64(c.k), f64(c.v), c.scale)
     assert max_err(f64(out), ref) <= 2e-3 and max_err(f64(lse), lref) <= 2e-3
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_merge_of_many_chunks(d):
+    """Rows of 128 chunks or more take the merge whose columns are split over
+    several workgroups; 257 chunks also cross its 256-chunk weight tile."""
+    banner(f"dense many chunks d={d}")
+    c = W.dense_case(2, 8, 2, 16 * 256 + 5, d, "bf16", 16, seed=41 + d, device=DEV)
+    _check(c)

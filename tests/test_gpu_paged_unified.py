@@ -190,3 +190,20 @@ def test_unified_config4_full_size_sampled():
     planted = {(b, h, j // c.chunk) for b, h, j in c.overflow_heads}
     got = {tuple(x) for x in torch.nonzero(flags).tolist()}
     assert got == planted
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_paged_merge_of_many_chunks(d):
+    """Paged rows of 0 to 257 chunks of 16 positions: the merge for rows of
+    many chunks reads each row's own chunk count from the sequence lengths."""
+    banner(f"paged many chunks d={d}")
+    lens = [0, 1, 16, 17, 2047, 2048, 16 * 256 + 5, 300]
+    c = W.paged_case(len(lens), 8, 2, d, 0, max(lens), page=16, chunk=16, seed=7 + d,
+                     device=DEV, lens=lens)
+    out, lse = _paged_run(c)
+    ref, lref = _paged_ref(c)
+    keep = np.asarray(lens) > 0
+    assert torch.all(out[~torch.as_tensor(keep, device=out.device)] == 0)
+    eo = max_err(f64(out)[keep], ref[keep])
+    el = max_err(f64(lse)[keep], lref[keep])
+    assert eo <= TOL[torch.bfloat16] and el <= TOL[torch.bfloat16], (eo, el)
