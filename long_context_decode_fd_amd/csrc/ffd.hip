@@ -26,6 +26,8 @@
 //      row with dot2 and V rows streamed as in the dense kernel.
 //   4. Row slots and waves merge into one partial per query head; the
 //      chunks merge in the common log-sum-exp kernel.
+#include <type_traits>
+
 #include "internal.hpp"
 #include "splitkv.hpp"
 
@@ -194,15 +196,25 @@ __global__ __launch_bounds__(kThreads) void ffd_anchor_kernel(FfdArgs a) {
       }
     }
   }
-#pragma unroll
-  for (int off = LPT; off < kWave; off <<= 1) {
+  // (largest score, then lowest position) over the wave's lanes, by pair
+  // exchanges; the order is total, so both lanes of a pair agree
+  auto argmax_step = [&](auto off_tag) {
+    constexpr int OFF = decltype(off_tag)::value;
 #pragma unroll
     for (int h = 0; h < G; ++h) {
-      const float ob = __shfl_xor(best[h], off);
-      const int oi = __shfl_xor(bidx[h], off);
-      if (ob > best[h] || (ob == best[h] && oi < bidx[h])) { best[h] = ob; bidx[h] = oi; }
+      float b0, b1, i0, i1;
+      lane_pair<OFF>(best[h], b0, b1);
+      lane_pair<OFF>(__int_as_float(bidx[h]), i0, i1);
+      const int j0 = __float_as_int(i0), j1 = __float_as_int(i1);
+      const bool second = b1 > b0 || (b1 == b0 && j1 < j0);
+      best[h] = second ? b1 : b0;
+      bidx[h] = second ? j1 : j0;
     }
-  }
+  };
+  if constexpr (LPT <= 4) argmax_step(std::integral_constant<int, 4>{});
+  if constexpr (LPT <= 8) argmax_step(std::integral_constant<int, 8>{});
+  if constexpr (LPT <= 16) argmax_step(std::integral_constant<int, 16>{});
+  argmax_step(std::integral_constant<int, 32>{});
   if (lane == 0) {
 #pragma unroll
     for (int h = 0; h < G; ++h) { s_best[wave][h] = best[h]; s_bidx[wave][h] = bidx[h]; }
