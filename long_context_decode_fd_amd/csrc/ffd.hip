@@ -112,40 +112,42 @@ __device__ __forceinline__ void residual_dot(const u32x2& rr, float rsf, const u
   }
 }
 
-// Pseudo-maximum (FFD digest, section 4): for every (sequence, query head),
-// the largest refined score over the anchor positions -- the first n_sink and
-// the last n_local positions -- and the lowest anchor position attaining it.
-// One workgroup per (sequence, kv-head), 16 lanes per anchor row; stored in
-// raw dot-product units for the scan kernel (and scaled, if requested).
+// Query slices of the 16-lane (row) layout (dims off .. off + 8 of each head
+// of the kv-group) and their sums.
 template <int D, int G>
-__global__ __launch_bounds__(kThreads) void ffd_anchor_kernel(FfdArgs a) {
+__device__ __forceinline__ void anchor_query(const FfdArgs& a, size_t hq0, int off,
+                                             u32x4 (&qr)[G], float (&ql)[G]) {
+  const uint16_t* qp = a.q + hq0 * D + off;
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    qr[h] = ld16(qp + (size_t)h * D);
+    ql[h] = ((bf16_lo(qr[h].x) + bf16_hi(qr[h].x)) + (bf16_lo(qr[h].y) + bf16_hi(qr[h].y))) +
+            ((bf16_lo(qr[h].z) + bf16_hi(qr[h].z)) + (bf16_lo(qr[h].w) + bf16_hi(qr[h].w)));
+  }
+}
+
+// Pseudo-maximum (FFD digest, section 4): for every query head of
+// (sequence b, kv-head kvh), the largest refined score over the anchor
+// positions -- the first n_sink and the last n_local positions -- and the
+// lowest anchor position attaining it, in raw dot-product units.  Run by a
+// whole workgroup, 16 lanes per anchor row; every thread receives the result.
+template <int D, int G>
+__device__ __forceinline__ void anchor_best(const FfdArgs& a, int b, int kvh,
+                                            const u32x4 (&qr)[G], const float (&ql)[G],
+                                            float (&s_best)[kWaves][G], int (&s_bidx)[kWaves][G],
+                                            float (&out_best)[G], int (&out_pos)[G]) {
   using Gm = Geo<uint16_t, D>;
-  constexpr int VEC = Gm::kVec, LPT = Gm::kLpt, TPL = Gm::kTpl;
+  constexpr int LPT = Gm::kLpt, TPL = Gm::kTpl;
   constexpr int NG = D / 32;
   constexpr int CW = D / 16;
-  __shared__ float s_best[kWaves][G];
-  __shared__ int s_bidx[kWaves][G];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & (kWave - 1);
   const int grp = lane / LPT, col = lane % LPT;
-  const int kvh = blockIdx.x % a.Hkv, b = blockIdx.x / a.Hkv;
   const int L = a.L;
   const size_t rbase = ((size_t)b * a.Hkv + kvh) * (size_t)L;
-  const size_t hq0 = (size_t)b * a.Hq + (size_t)kvh * G;
   const uint32_t* codes = a.codes;
   const uint16_t* zs = a.zs;
   const int8_t* res = a.res;
   const uint16_t* rsa = a.rs;
-  u32x4 qr[G];
-  float ql[G];
-  {
-    const uint16_t* qp = a.q + hq0 * D + col * VEC;
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-      qr[h] = ld16(qp + (size_t)h * D);
-      ql[h] = ((bf16_lo(qr[h].x) + bf16_hi(qr[h].x)) + (bf16_lo(qr[h].y) + bf16_hi(qr[h].y))) +
-              ((bf16_lo(qr[h].z) + bf16_hi(qr[h].z)) + (bf16_lo(qr[h].w) + bf16_hi(qr[h].w)));
-    }
-  }
   const int n_sk = min(a.n_sink, L);
   const int loc0 = max(n_sk, L - a.n_local);
   const int na = n_sk + (L - loc0);
@@ -230,10 +232,35 @@ __global__ __launch_bounds__(kThreads) void ffd_anchor_kernel(FfdArgs a) {
       const int oi = s_bidx[w][h];
       if (ob > bb || (ob == bb && oi < bi)) { bb = ob; bi = oi; }
     }
-    if (tid == 0) {
-      a.anchor_max[hq0 + h] = bb;
-      a.anchor_pos[hq0 + h] = bi;
-      if (a.pseudo_max != nullptr) a.pseudo_max[hq0 + h] = bb * a.scale;
+    out_best[h] = bb;
+    out_pos[h] = bi;
+  }
+}
+
+// Pseudo-maximum kernel: one workgroup per (sequence, kv-head) runs
+// anchor_best and leaves m^ (raw units) and j* per query head in the
+// workspace for the FFD kernel (and m^ scaled in pseudo_max, if requested).
+template <int D, int G>
+__global__ __launch_bounds__(kThreads) void ffd_anchor_kernel(FfdArgs a) {
+  using Gm = Geo<uint16_t, D>;
+  constexpr int VEC = Gm::kVec, LPT = Gm::kLpt;
+  __shared__ float s_best[kWaves][G];
+  __shared__ int s_bidx[kWaves][G];
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), col = lane % LPT;
+  const int kvh = blockIdx.x % a.Hkv, b = blockIdx.x / a.Hkv;
+  const size_t hq0 = (size_t)b * a.Hq + (size_t)kvh * G;
+  u32x4 qr[G];
+  float ql[G];
+  anchor_query<D, G>(a, hq0, col * VEC, qr, ql);
+  float bb[G];
+  int bi[G];
+  anchor_best<D, G>(a, b, kvh, qr, ql, s_best, s_bidx, bb, bi);
+  if (tid == 0) {
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      a.anchor_max[hq0 + h] = bb[h];
+      a.anchor_pos[hq0 + h] = bi[h];
+      if (a.pseudo_max != nullptr) a.pseudo_max[hq0 + h] = bb[h] * a.scale;
     }
   }
 }
@@ -322,19 +349,13 @@ __global__ __launch_bounds__(kThreads) void ffd_kernel(FfdArgs a) {
   // Query slices of the 16-lane (row) layout, and their partial sums.
   u32x4 qr[G];
   float ql[G];
-  {
-    const uint16_t* qp = a.q + hq0 * D + col * VEC;
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-      qr[h] = ld16(qp + (size_t)h * D);
-      ql[h] = ((bf16_lo(qr[h].x) + bf16_hi(qr[h].x)) + (bf16_lo(qr[h].y) + bf16_hi(qr[h].y))) +
-              ((bf16_lo(qr[h].z) + bf16_hi(qr[h].z)) + (bf16_lo(qr[h].w) + bf16_hi(qr[h].w)));
-    }
-  }
+  anchor_query<D, G>(a, hq0, col * VEC, qr, ql);
 
-  // ---- 0. pseudo-maximum and its anchor, computed once per (b, head) ----
+  // ---- 0. pseudo-maximum and its anchor ----
   float thr[G];
   int jst[G];
+  // computed once per (sequence, kv-head) by ffd_anchor_kernel (scoring the
+  // anchors in every chunk's workgroup instead measured 14-15 us slower)
 #pragma unroll
   for (int h = 0; h < G; ++h) {
     thr[h] = a.anchor_max[hq0 + h] - a.delta_raw;
