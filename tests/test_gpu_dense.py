@@ -120,6 +120,23 @@ def test_dense_128k_sampled():
     assert torch.isfinite(out).all()
 
 
+def test_many_units_per_wave_sampled():
+    """Chunks of 16 over L 65536: 131,072 units, 128 per wave, so every wave
+    writes its held partials many times mid-run, and the merge walks 4,096
+    chunks per row in tiles of 256."""
+    banner("dense many units per wave")
+    c = W.dense_case(4, 32, 8, 65536, 128, "bf16", 16, seed=1203, device=DEV)
+    out, lse = fd.decode_attn(c.q, c.k, c.v, chunk=c.chunk)
+    torch.cuda.synchronize()
+    G = 4
+    for b, h in [(0, 0), (1, 13), (2, 22), (3, 31)]:
+        r, lr = ofd.attention_row(f64(c.q[b, h]), f64(c.k[b, h // G]), f64(c.v[b, h // G]),
+                                  c.scale)
+        assert max_err(f64(out[b, h]), r) <= 2e-3
+        assert abs(float(lse[b, h]) - lr) <= 2e-3
+    assert torch.isfinite(out).all()
+
+
 def test_partials_then_merge_equals_full_call():
     c = W.dense_case(2, 16, 4, 3000, 128, "bf16", 256, seed=41, device=DEV)
     out, lse = fd.decode_attn(c.q, c.k, c.v, chunk=256)

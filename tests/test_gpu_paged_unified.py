@@ -170,6 +170,16 @@ def test_unified_overflow_plant():
     assert flags[0, 0, 1234 // 256] == 1
 
 
+def test_unified_many_units_per_wave():
+    """Chunks of 16 over L 32768: 16 units per wave, so held partials and
+    their range flags are written mid-run; tight margins mix flagged and
+    unflagged chunks."""
+    banner("unified many units per wave")
+    c = W.dense_case(2, 16, 4, 32768, 128, "bf16", 16, seed=29, device=DEV)
+    flags = _unified_check(c, 1.0, 1.0, 1.5)
+    assert 0 < int(flags.sum()) < flags.size
+
+
 def test_unified_config4_full_size_sampled():
     banner("unified config4 full size")
     c = W.config_case(4, device=DEV)
