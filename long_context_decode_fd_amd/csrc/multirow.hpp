@@ -56,6 +56,9 @@ typedef short s16x4_t __attribute__((ext_vector_type(4)));
 #define FD_MR_BUF_Q2 1   // ... two query tiles (with 4-tile batches; at 2 tiles it measured
                          // slower, 214 -> 255 us at M = 8)
 #endif
+#ifndef FD_MR_HOLD_Q2
+#define FD_MR_HOLD_Q2 1   // two query tiles: one finished unit held in LDS
+#endif
 #ifndef FD_MR_HWSPLIT
 #define FD_MR_HWSPLIT 1   // hi/lo split of P by the hardware bf16 conversion
 #endif
@@ -225,8 +228,9 @@ void multi_kernel(MultiArgs a) {
   // bytes per lane and whole rows, instead of 4 bytes per lane in 64-byte
   // pieces.
   unsigned char* ost = s_kv[wave][0];
+  // staged (two query tiles): the unit's 32 O rows are in LDS there
   auto store_unit = [&](const f32x4 (&o)[QT][DB], const float (&m)[QT], const float (&l)[QT],
-                        int uu) {
+                        int uu, const unsigned char* staged = nullptr) {
     UnitM x;
     decode(uu, x);
 #pragma unroll
@@ -259,9 +263,22 @@ void multi_kernel(MultiArgs a) {
                 v;
           }
         }
+      } else if (staged != nullptr) {
+        // two query tiles held in LDS: rows 16 qt .. 16 qt + 15 at staged
+        constexpr int LPO = kWave / ORPI;   // lanes per O row
+#pragma unroll
+        for (int i = 0; i < 16 / ORPI; ++i) {
+          const int rr = 16 * qt + ORPI * i + lane / LPO, cb = 16 * (lane % LPO);
+          const f32x4 v = *reinterpret_cast<const f32x4*>(staged + rr * OSTR + cb);
+          if (rr < R) {
+            const size_t prow =
+                (((size_t)x.b * a.M + rr / G) * a.Hq + (size_t)x.kvh * G + rr % G) * a.nc + x.c;
+            *reinterpret_cast<f32x4*>(reinterpret_cast<unsigned char*>(a.o_part + prow * D) + cb) =
+                v;
+          }
+        }
       } else {
-        // two query tiles: straight from the MFMA layout (the staging
-        // measured slower at this register load)
+        // two query tiles: straight from the MFMA layout
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int row = 16 * qt + 4 * qd + e;
@@ -281,6 +298,15 @@ void multi_kernel(MultiArgs a) {
   // stored between units made the next unit's first K wait for them.
   constexpr int H = QT == 1 ? FD_MR_HOLD : 1;
   f32x4 hold_o[H][QT][DB];
+#if FD_MR_HOLD_Q2
+  // two query tiles: no registers to spare, so one finished unit waits in
+  // LDS (32 O rows) and is written together with the next one, which halves
+  // the store events between units
+  __shared__ __align__(16) unsigned char s_hold2[QT == 2 ? kWaves : 1][QT == 2 ? 32 * OSTR : 16];
+  float h2_m[QT], h2_l[QT];
+  int h2_u = 0;
+  bool h2_held = false;   // wave-uniform
+#endif
   float hold_m[H][QT], hold_l[H][QT];
   int hold_u[H];
   int held = 0;   // wave-uniform
@@ -487,7 +513,30 @@ void multi_kernel(MultiArgs a) {
         held = 0;
       }
     } else {
+#if FD_MR_HOLD_Q2
+      if (!h2_held && has_next) {
+        // lane (n, qd) holds rows 16 qt + 4 qd + e, dims 16 db + n
+#pragma unroll
+        for (int qt = 0; qt < QT; ++qt) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+#pragma unroll
+            for (int db = 0; db < DB; ++db)
+              *reinterpret_cast<float*>(s_hold2[wave] + (16 * qt + 4 * qd + e) * OSTR +
+                                        (16 * db + n) * 4) = o[qt][db][e];
+          h2_m[qt] = m[qt];
+          h2_l[qt] = l[qt];
+        }
+        h2_u = u;
+        h2_held = true;
+      } else {
+        if (h2_held) store_unit(o, h2_m, h2_l, h2_u, s_hold2[wave]);
+        store_unit(o, m, l, u);
+        h2_held = false;
+      }
+#else
       store_unit(o, m, l, u);
+#endif
     }
     if (!has_next) break;
     cur = nxt;
