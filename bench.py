@@ -445,6 +445,35 @@ def variant_unified(torch, fd, W, args, timer):
                 dense_over_unified=round(t_d["ms"] / t_u["ms"], 3))
 
 
+def selection_quality(torch, q, k, scale, mask, delta):
+    """How FFD's candidate set C compares with the exact top-delta set
+    T = { j : s_j >= max_j s_j - delta } of the true scores s_j = scale q.K_j
+    (FFD digest, section 3), per query head: recall |C & T| / |T|, and the
+    share of the softmax mass that C keeps, sum_{j in C} e^{s_j - m} over
+    sum_j e^{s_j - m}.  q [B,Hq,d], k [B,Hkv,L,d], mask int32 [B,Hq,ceil(L/32)]
+    (bit j%32 of word j/32).  Plain fp32 products outside any timed region: a
+    diagnostic of the selection, not part of the decode path."""
+    B, Hq, d = q.shape
+    Hkv, L = k.shape[1], k.shape[2]
+    G = Hq // Hkv
+    shifts = torch.arange(32, device=mask.device, dtype=torch.int32)
+    rec, mass = [], []
+    for b in range(B):
+        qt = q[b].float().reshape(Hkv, G, d).transpose(1, 2).contiguous()   # [Hkv, d, G]
+        s = (torch.matmul(k[b].float(), qt) * scale).transpose(1, 2).reshape(Hq, L)
+        m = s.amax(-1, keepdim=True)
+        top = s >= m - delta
+        cand = ((mask[b].unsqueeze(-1) >> shifts) & 1).reshape(Hq, -1)[:, :L].bool()
+        rec.append((cand & top).sum(-1).double() / top.sum(-1).double())
+        w = torch.exp((s - m).double())
+        mass.append((w * cand).sum(-1) / w.sum(-1))
+    rec, mass = torch.cat(rec), torch.cat(mass)
+    return dict(recall_exact_topdelta_mean=round(float(rec.mean()), 5),
+                recall_exact_topdelta_min=round(float(rec.min()), 5),
+                softmax_mass_kept_mean=round(float(mass.mean()), 6),
+                softmax_mass_kept_min=round(float(mass.min()), 6))
+
+
 def variant_ffd(torch, fd, W, args, timer):
     import numpy as np
     c = W.config_case(5, device="cuda:0")
@@ -482,6 +511,8 @@ def variant_ffd(torch, fd, W, args, timer):
         per_head = np.unpackbits(m.view(np.uint8), axis=-1).sum(-1)   # [B,Hkv,G]
         union = np.bitwise_or.reduce(m, axis=2)
         n_union = int(np.unpackbits(union.view(np.uint8), axis=-1).sum())
+        quality = selection_quality(torch, c.q, c.k, c.scale, mask, delta)
+        del mask
         t = timer.run(calls, args.steps, args.warmup)
         n_anchor = min(L, c.n_sink + c.n_local)
         nbytes = (B * Hkv * L * (d // 4 + d // 32 * 4) + n_union * (d + d // 32 * 2 + 2 * d)
@@ -494,7 +525,7 @@ def variant_ffd(torch, fd, W, args, timer):
             pct_of_peak=round(100 * gbs(nbytes, t["ms"]) / PEAK_GBS, 1),
             kept_per_head=round(float(per_head.mean()) / L, 4),
             kept_group_union=round(n_union / (B * Hkv * L), 4),
-            dense_bf16_equiv_bytes=2 * B * Hkv * L * d * 2)
+            dense_bf16_equiv_bytes=2 * B * Hkv * L * d * 2, **quality)
     return dict(workload=f"FFD sparse decode, B={B}, Hq={Hq}, Hkv={Hkv}, d={d}, L={L}, "
                          f"chunk={c.chunk}, sinks={c.n_sink}, local={c.n_local}",
                 pack_ms_whole_cache=round(pack_ms, 2), **res)
@@ -549,7 +580,9 @@ def variant_ffd_peaked(torch, fd, W, args, timer):
                   + B * Hkv * n_anchor * (d // 4 + d // 32 * 6 + d)
                   + B * Hq * d * 2 + B * Hq * (d + 1) * 4)
         info[key] = dict(bytes=int(nbytes), kept_per_head=round(float(per_head.mean()) / L, 4),
-                         kept_group_union=round(n_union / (B * Hkv * L), 4))
+                         kept_group_union=round(n_union / (B * Hkv * L), 4),
+                         **selection_quality(torch, c.q, c.k, c.scale, mask, delta))
+        del mask
     check_rc(lib, groups["dense"][0]())
     t = interleaved(timer, groups, args.steps, args.warmup)
     dense_bytes = 2 * B * Hkv * L * d * 2 + B * Hq * d * 2 + B * Hq * (d + 1) * 4
