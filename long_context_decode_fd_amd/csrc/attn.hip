@@ -560,8 +560,8 @@ void partial_kernel(PartialArgs a) {
 // then sums chunks cl, cl + CL, ... of 4 columns with independent 16-byte
 // loads, 16 W chunks at a time (the loads of the first 16 W are issued
 // before the maximum is known), and the chunk lanes are reduced through LDS.
-// Rows of many chunks take W = 16, so that their loads also share one
-// memory latency.  The order of every sum is fixed, so runs are bitwise
+// Rows of many chunks split their columns over CS workgroups, so that
+// more loads share one memory latency.  The order of every sum is fixed, so runs are bitwise
 // reproducible.  Rows whose chunks all carry the same m (the fixed-maximum
 // path without fallback) get weights of exactly 1.
 template <int D, int W, int CS>
@@ -757,22 +757,26 @@ hipError_t launch_partial(int mode, int is_bf16, int D, int G, const PartialArgs
 #ifndef FD_MERGE_WIDE_W
 #define FD_MERGE_WIDE_W 4
 #endif
-#ifndef FD_MERGE_WIDE_CS
-#define FD_MERGE_WIDE_CS 4
-#endif
 hipError_t launch_merge(int D, int B, const MergeArgs& a, hipStream_t s) {
   const size_t rows = (size_t)B * a.Hq;
-  // rows of many chunks: their columns split over FD_MERGE_WIDE_CS
-  // workgroups of FD_MERGE_WIDE_W waves
-  constexpr int WW = FD_MERGE_WIDE_W, CS = FD_MERGE_WIDE_CS;
-  const bool wide = a.nc >= 128;
-  const dim3 grid((unsigned)(wide ? rows * CS : rows));
-  const dim3 block(wide ? WW * kWave : 4 * kWave);
-  if (D == 64 && wide) hipLaunchKernelGGL((merge_kernel<64, WW, CS>), grid, block, 0, s, a);
-  else if (D == 64) hipLaunchKernelGGL((merge_kernel<64, 4, 1>), grid, block, 0, s, a);
-  else if (D == 128 && wide) hipLaunchKernelGGL((merge_kernel<128, WW, CS>), grid, block, 0, s, a);
-  else if (D == 128) hipLaunchKernelGGL((merge_kernel<128, 4, 1>), grid, block, 0, s, a);
-  else return hipErrorInvalidValue;
+  // Rows of 64 chunks or more split their columns over 2 workgroups, rows
+  // of 128 or more over 4 (FD_MERGE_WIDE_W waves each): more workgroups in
+  // flight for the same latency-bound walk over the chunks.
+  constexpr int WW = FD_MERGE_WIDE_W;
+  const int cs = a.nc >= 128 ? 4 : a.nc >= 64 ? 2 : 1;
+  const dim3 grid((unsigned)(rows * cs));
+  const dim3 block(cs > 1 ? WW * kWave : 4 * kWave);
+  if (D == 64) {
+    if (cs == 4) hipLaunchKernelGGL((merge_kernel<64, WW, 4>), grid, block, 0, s, a);
+    else if (cs == 2) hipLaunchKernelGGL((merge_kernel<64, WW, 2>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((merge_kernel<64, 4, 1>), grid, block, 0, s, a);
+  } else if (D == 128) {
+    if (cs == 4) hipLaunchKernelGGL((merge_kernel<128, WW, 4>), grid, block, 0, s, a);
+    else if (cs == 2) hipLaunchKernelGGL((merge_kernel<128, WW, 2>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((merge_kernel<128, 4, 1>), grid, block, 0, s, a);
+  } else {
+    return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 

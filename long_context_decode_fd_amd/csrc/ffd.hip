@@ -114,16 +114,27 @@ __device__ __forceinline__ void residual_dot(const u32x2& rr, float rsf, const u
 
 // Query slices of the 16-lane (row) layout (dims off .. off + 8 of each head
 // of the kv-group) and their sums.
+template <int G>
+__device__ __forceinline__ void query_sums(const u32x4 (&qr)[G], float (&ql)[G]) {
+#pragma unroll
+  for (int h = 0; h < G; ++h)
+    ql[h] = ((bf16_lo(qr[h].x) + bf16_hi(qr[h].x)) + (bf16_lo(qr[h].y) + bf16_hi(qr[h].y))) +
+            ((bf16_lo(qr[h].z) + bf16_hi(qr[h].z)) + (bf16_lo(qr[h].w) + bf16_hi(qr[h].w)));
+}
+
+template <int D, int G>
+__device__ __forceinline__ void anchor_query_load(const FfdArgs& a, size_t hq0, int off,
+                                                  u32x4 (&qr)[G]) {
+  const uint16_t* qp = a.q + hq0 * D + off;
+#pragma unroll
+  for (int h = 0; h < G; ++h) qr[h] = ld16(qp + (size_t)h * D);
+}
+
 template <int D, int G>
 __device__ __forceinline__ void anchor_query(const FfdArgs& a, size_t hq0, int off,
                                              u32x4 (&qr)[G], float (&ql)[G]) {
-  const uint16_t* qp = a.q + hq0 * D + off;
-#pragma unroll
-  for (int h = 0; h < G; ++h) {
-    qr[h] = ld16(qp + (size_t)h * D);
-    ql[h] = ((bf16_lo(qr[h].x) + bf16_hi(qr[h].x)) + (bf16_lo(qr[h].y) + bf16_hi(qr[h].y))) +
-            ((bf16_lo(qr[h].z) + bf16_hi(qr[h].z)) + (bf16_lo(qr[h].w) + bf16_hi(qr[h].w)));
-  }
+  anchor_query_load<D, G>(a, hq0, off, qr);
+  query_sums<G>(qr, ql);
 }
 
 // Pseudo-maximum (FFD digest, section 4): for every query head of
@@ -131,9 +142,11 @@ __device__ __forceinline__ void anchor_query(const FfdArgs& a, size_t hq0, int o
 // positions -- the first n_sink and the last n_local positions -- and the
 // lowest anchor position attaining it, in raw dot-product units.  Run by a
 // whole workgroup, 16 lanes per anchor row; every thread receives the result.
+// qr may still be in flight: its sums are formed after the anchor rows'
+// loads are issued, so both share one memory latency.
 template <int D, int G>
 __device__ __forceinline__ void anchor_best(const FfdArgs& a, int b, int kvh,
-                                            const u32x4 (&qr)[G], const float (&ql)[G],
+                                            const u32x4 (&qr)[G],
                                             float (&s_best)[kWaves][G], int (&s_bidx)[kWaves][G],
                                             float (&out_best)[G], int (&out_pos)[G]) {
   using Gm = Geo<uint16_t, D>;
@@ -157,9 +170,11 @@ __device__ __forceinline__ void anchor_best(const FfdArgs& a, int b, int kvh,
   for (int h = 0; h < G; ++h) { best[h] = kNegInf; bidx[h] = 0x7fffffff; }
   // All loads of up to NIT rounds (kWaves * TPL anchors each) are issued
   // before any arithmetic: one memory latency instead of one per round.
+  // The first pass is peeled out of the loop (na >= 1 always) so that its
+  // loads are issued before the query sums wait for qr.
   constexpr int NIT = 8;
   const int gi = col / 4;  // 8 dims per lane, 4 lanes per group
-  for (int kb = 0; kb < na; kb += kWaves * TPL * NIT) {
+  auto pass = [&](int kb) {
     uint32_t w[NIT], zsb[NIT];
     u32x2 rr[NIT];
     uint32_t rsb[NIT];
@@ -174,6 +189,11 @@ __device__ __forceinline__ void anchor_best(const FfdArgs& a, int b, int kvh,
       rr[it] = *reinterpret_cast<const u32x2*>(res + row * D + col * 8);
       rsb[it] = rsa[row * NG + gi];
     }
+    // keep the scheduler from pulling conversions of early loads in among
+    // the later ones (each would wait for the loads issued before it)
+    __builtin_amdgcn_sched_barrier(0);
+    float ql[G];
+    query_sums<G>(qr, ql);
 #pragma unroll
     for (int it = 0; it < NIT; ++it) {
       const bool valid = kb + (it * kWaves + wave) * TPL + grp < na;
@@ -197,7 +217,9 @@ __device__ __forceinline__ void anchor_best(const FfdArgs& a, int b, int kvh,
         }
       }
     }
-  }
+  };
+  pass(0);
+  for (int kb = kWaves * TPL * NIT; kb < na; kb += kWaves * TPL * NIT) pass(kb);
   // (largest score, then lowest position) over the wave's lanes, by pair
   // exchanges; the order is total, so both lanes of a pair agree
   auto argmax_step = [&](auto off_tag) {
@@ -250,11 +272,10 @@ __global__ __launch_bounds__(kThreads) void ffd_anchor_kernel(FfdArgs a) {
   const int kvh = blockIdx.x % a.Hkv, b = blockIdx.x / a.Hkv;
   const size_t hq0 = (size_t)b * a.Hq + (size_t)kvh * G;
   u32x4 qr[G];
-  float ql[G];
-  anchor_query<D, G>(a, hq0, col * VEC, qr, ql);
+  anchor_query_load<D, G>(a, hq0, col * VEC, qr);
   float bb[G];
   int bi[G];
-  anchor_best<D, G>(a, b, kvh, qr, ql, s_best, s_bidx, bb, bi);
+  anchor_best<D, G>(a, b, kvh, qr, s_best, s_bidx, bb, bi);
   if (tid == 0) {
 #pragma unroll
     for (int h = 0; h < G; ++h) {

@@ -180,3 +180,13 @@ def test_merge_of_many_chunks(d):
     banner(f"dense many chunks d={d}")
     c = W.dense_case(2, 8, 2, 16 * 256 + 5, d, "bf16", 16, seed=41 + d, device=DEV)
     _check(c)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("nc", [63, 64, 100, 127, 128])
+def test_merge_tier_edges(d, nc):
+    """Rows of 63 / 64-127 / 128+ chunks take the merge with its columns in
+    1 / 2 / 4 workgroups; the last chunk is ragged."""
+    banner(f"dense merge tiers d={d} nc={nc}")
+    c = W.dense_case(2, 8, 2, 16 * (nc - 1) + 7, d, "bf16", 16, seed=300 + nc + d, device=DEV)
+    _check(c)
