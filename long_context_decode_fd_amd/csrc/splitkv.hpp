@@ -241,7 +241,7 @@ __device__ __forceinline__ void slot_merge_step(float (&acc)[G][VEC], float (&m)
 }
 
 // Reduce-scatter of the row slots' states at a unit's end (the same exact
-// merge as wave_merge, split so that no lane does all of it).  First the
+// merge as slot_merge_step, split so that no lane does all of it).  First the
 // largest slot maximum M per head and one rescale of each slot to it
 // (2^(m - M)); the exchanges then only add.  Exchanges over fewer than 16
 // lanes (DPP) add every value; the exchanges over 16 and 32 lanes swap two
@@ -340,40 +340,6 @@ __device__ __forceinline__ void slot_reduce_scatter(
     }
 #pragma unroll
     for (int k = 0; k < NV / 2; ++k) swap_add32(x[k], x[k + NV / 2], kept[k]);
-  }
-}
-
-// Merge the row slots of one wave with shuffles: afterwards every lane holds
-// the merged state (O relative to m, m in log2 units, l) of its column.  The
-// two weighted terms are rounded separately and then added (no fused
-// multiply-add), so both partners of a step get the same bits and every row
-// slot ends with the identical merged state, whichever slot keeps it.
-template <int G, int VEC, int LPT>
-__device__ __forceinline__ void wave_merge(float (&acc)[G][VEC], float (&m)[G], float (&l)[G]) {
-#pragma clang fp contract(off)
-  slot_merge_step<LPT, G, VEC>(acc, m, l);
-}
-
-// Write one lane's column of a merged state as the partial rows
-// prow0 + h * hstride (h < G): O (unnormalised), and (m, l) if `with_ml`.
-template <int G, int D, int VEC, int P>
-__device__ __forceinline__ void store_partial(const float (&acc)[G][VEC], const float (&m)[G],
-                                              const float (&l)[G], float* o_part,
-                                              float* ml_part, size_t prow0, size_t hstride,
-                                              int col, bool with_ml) {
-  constexpr int PV = VEC / P;   // contiguous elements per piece
-#pragma unroll
-  for (int h = 0; h < G; ++h) {
-    float* dst = o_part + (prow0 + (size_t)h * hstride) * D + col * PV;
-#pragma unroll
-    for (int e = 0; e < VEC; e += 4)
-      *reinterpret_cast<f32x4*>(dst + (e / PV) * (D / P) + e % PV) =
-          f32x4{acc[h][e], acc[h][e + 1], acc[h][e + 2], acc[h][e + 3]};
-  }
-  if (with_ml) {
-#pragma unroll
-    for (int h = 0; h < G; ++h)
-      *reinterpret_cast<f32x2*>(ml_part + (prow0 + (size_t)h * hstride) * 2) = f32x2{m[h], l[h]};
   }
 }
 
