@@ -514,7 +514,9 @@ void multi_kernel(MultiArgs a) {
       }
     } else {
 #if FD_MR_HOLD_Q2
-      if (!h2_held && has_next) {
+      if constexpr (QT != 2) {
+        store_unit(o, m, l, u);
+      } else if (!h2_held && has_next) {
         // lane (n, qd) holds rows 16 qt + 4 qd + e, dims 16 db + n
 #pragma unroll
         for (int qt = 0; qt < QT; ++qt) {
