@@ -190,3 +190,20 @@ def test_merge_tier_edges(d, nc):
     banner(f"dense merge tiers d={d} nc={nc}")
     c = W.dense_case(2, 8, 2, 16 * (nc - 1) + 7, d, "bf16", 16, seed=300 + nc + d, device=DEV)
     _check(c)
+
+
+def test_dense_one_million_positions_sampled():
+    """One sequence of 2^20 + 77 positions (512 MiB of K/V): 2,049 chunks of
+    512 with a ragged last one, so the merge walks 9 tiles of 256 chunks, the
+    last holding a single chunk."""
+    banner("dense 1M sampled")
+    L = (1 << 20) + 77
+    c = W.dense_case(1, 8, 1, L, 128, "bf16", 512, seed=1204, device=DEV)
+    out, lse = fd.decode_attn(c.q, c.k, c.v, chunk=c.chunk)
+    torch.cuda.synchronize()
+    K, V = f64(c.k[0, 0]), f64(c.v[0, 0])
+    for h in (0, 3, 7):
+        r, lr = ofd.attention_row(f64(c.q[0, h]), K, V, c.scale)
+        assert max_err(f64(out[0, h]), r) <= 2e-3
+        assert abs(float(lse[0, h]) - lr) <= 2e-3
+    assert torch.isfinite(out).all()
