@@ -217,3 +217,20 @@ def test_paged_merge_of_many_chunks(d):
     eo = max_err(f64(out)[keep], ref[keep])
     el = max_err(f64(lse)[keep], lref[keep])
     assert eo <= TOL[torch.bfloat16] and el <= TOL[torch.bfloat16], (eo, el)
+
+
+def test_paged_one_million_positions_sampled():
+    """A pool holding one sequence of 2^20 + 5 positions (65,537 pages of 16)
+    beside a short one: 1,025 chunks of 1,024 for the long row, 3 for the
+    short one, in one call."""
+    banner("paged 1M sampled")
+    lens = [(1 << 20) + 5, 3000]
+    c = W.paged_case(2, 8, 2, 128, 0, max(lens), page=16, chunk=1024, seed=1205, device=DEV,
+                     lens=lens)
+    out, lse = _paged_run(c)
+    rows = [(0, 0), (0, 5), (1, 3)]
+    ref, lref = _paged_ref(c, rows)
+    for b, h in rows:
+        assert max_err(f64(out[b, h]), ref[b, h]) <= 2e-3
+        assert abs(float(lse[b, h]) - lref[b, h]) <= 2e-3
+    assert torch.isfinite(out).all()
