@@ -204,3 +204,20 @@ def test_ffd_peaked_workload_sampled():
         for b, h in ((0, 0), (1, 9), (3, 30)):
             _row_check(q, ph, v64, b, h, G, c.scale, delta, c.n_sink, c.n_local, f64(out),
                        f64(lse), cm, f64(pmax))
+
+
+def test_ffd_one_million_positions():
+    """One sequence of 2^20 + 33 positions (1,025 chunks of 1,024, a ragged
+    last one), keys packed by the oracle, every head checked in full."""
+    banner("ffd 1M")
+    L = (1 << 20) + 33
+    c = W.ffd_case(1, 4, 1, L, 128, n_sink=4, n_local=64, chunk=1024, seed=1206, device=DEV)
+    ph = offd.pack_keys(f64(c.k).astype(np.float32))
+    out, lse, cand, pmax = fd.ffd_sparse_decode(c.q, packed_to_device(ph, DEV), c.v, 5.0,
+                                                c.n_sink, c.n_local, chunk=c.chunk,
+                                                want_mask=True, want_pseudo_max=True)
+    torch.cuda.synchronize()
+    q, v64 = f64(c.q), f64(c.v)
+    o, l_, cm, pm = f64(out), f64(lse), cand.cpu().numpy().view(np.uint32), f64(pmax)
+    for h in range(4):
+        _row_check(q, ph, v64, 0, h, 4, c.scale, 5.0, c.n_sink, c.n_local, o, l_, cm, pm)
