@@ -104,3 +104,13 @@ def test_multi_row_many_units_two_query_tiles_sampled():
     c = W.multi_case(4, 8, 32, 8, 20000, 128, seed=109, device=DEV)
     rows = [(0, 0, 0), (1, 7, 31), (2, 4, 16), (3, 6, 5)]
     _check(c, chunk=48, rows=rows)
+
+
+@pytest.mark.parametrize("M", [4, 8])
+def test_multi_row_one_million_positions_sampled(M):
+    """M new tokens at the end of a cache of 2^20 + 3 positions (2,049 chunks
+    of 512): one and two query tiles."""
+    banner(f"multi 1M M={M}")
+    c = W.multi_case(1, M, 16, 4, (1 << 20) + 3, 128, seed=1208 + M, device=DEV)
+    rows = [(0, 0, 0), (0, M - 1, 15), (0, M // 2, 6)]
+    _check(c, chunk=512, rows=rows)

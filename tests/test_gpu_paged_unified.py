@@ -234,3 +234,12 @@ def test_paged_one_million_positions_sampled():
         assert max_err(f64(out[b, h]), ref[b, h]) <= 2e-3
         assert abs(float(lse[b, h]) - lref[b, h]) <= 2e-3
     assert torch.isfinite(out).all()
+
+
+def test_unified_one_million_positions():
+    """Fixed maximum over one sequence of 2^20 + 9 positions (2,049 chunks of
+    512); tight margins mix chunks inside and outside the range."""
+    banner("unified 1M")
+    c = W.dense_case(1, 8, 2, (1 << 20) + 9, 128, "bf16", 512, seed=1207, device=DEV)
+    flags = _unified_check(c, 1.0, 1.0, 1.5)
+    assert 0 < int(flags.sum()) < flags.size
