@@ -37,6 +37,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 PEAK_GBS = 8000.0       # MI355X HBM3E peak, GB/s
+VARIANTS = ("dense_128k", "paged", "unified_max", "ffd", "ffd_peaked", "multi_row", "append")
 METRIC = "us/decode step and achieved KV-read HBM GB/s (% of peak) at 32K-128K ctx"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_partial_dense_b8_h32x8_d128_l32768.txt")
 KERNEL_SOURCES = ["attn.hip", "splitkv.hpp", "common.hpp"]
@@ -55,6 +56,10 @@ def parse_args():
                    help="target CPU time of the oracle sample")
     p.add_argument("--copy-calibration", action="store_true",
                    help="only run a 1 GiB device copy (counter scale for --pmc runs)")
+    p.add_argument("--variants", default=",".join(VARIANTS),
+                   help="comma-separated subset of the variant workloads to run")
+    p.add_argument("--ffd-deltas", default=None,
+                   help="comma-separated deltas for the FFD workloads (default 5,7)")
     return p.parse_args()
 
 
@@ -445,6 +450,12 @@ def variant_unified(torch, fd, W, args, timer):
                 dense_over_unified=round(t_d["ms"] / t_u["ms"], 3))
 
 
+def _ffd_override(args):
+    if args.ffd_deltas is None:
+        return {}
+    return dict(deltas=tuple(float(x) for x in args.ffd_deltas.split(",") if x))
+
+
 def selection_quality(torch, q, k, scale, mask, delta):
     """How FFD's candidate set C compares with the exact top-delta set
     T = { j : s_j >= max_j s_j - delta } of the true scores s_j = scale q.K_j
@@ -476,7 +487,7 @@ def selection_quality(torch, q, k, scale, mask, delta):
 
 def variant_ffd(torch, fd, W, args, timer):
     import numpy as np
-    c = W.config_case(5, device="cuda:0")
+    c = W.config_case(5, device="cuda:0", **_ffd_override(args))
     B, Hq, d = c.q.shape
     Hkv, L = c.v.shape[1], c.v.shape[2]
     G = Hq // Hkv
@@ -536,7 +547,7 @@ def variant_ffd_peaked(torch, fd, W, args, timer):
     whose heads of a group attend alike (per-head sparsity at the levels the
     FFD digest reports).  Dense reads the bf16 keys, FFD the packed ones."""
     import numpy as np
-    c = W.config_case(6, device="cuda:0")
+    c = W.config_case(6, device="cuda:0", **_ffd_override(args))
     B, Hq, d = c.q.shape
     Hkv, L = c.v.shape[1], c.v.shape[2]
     G = Hq // Hkv
@@ -642,15 +653,15 @@ def main():
         },
     }
     if not args.no_variants:
-        line["variants"] = {
-            "dense_128k": variant_dense_128k(torch, fd, W, args, timer),
-            "paged": variant_paged(torch, fd, W, args, timer),
-            "unified_max": variant_unified(torch, fd, W, args, timer),
-            "ffd": variant_ffd(torch, fd, W, args, timer),
-            "ffd_peaked": variant_ffd_peaked(torch, fd, W, args, timer),
-            "multi_row": variant_multi(torch, fd, W, args, timer),
-            "append": variant_append(torch, fd, W, args, timer),
-        }
+        fns = dict(dense_128k=variant_dense_128k, paged=variant_paged,
+                   unified_max=variant_unified, ffd=variant_ffd, ffd_peaked=variant_ffd_peaked,
+                   multi_row=variant_multi, append=variant_append)
+        want = [x for x in args.variants.split(",") if x]
+        unknown = [x for x in want if x not in fns]
+        if unknown:
+            sys.exit(f"unknown variants {unknown}; choose from {list(fns)}")
+        line["variants"] = {name: fns[name](torch, fd, W, args, timer)
+                            for name in VARIANTS if name in want}
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(torch, case, args.cpu_seconds)
     print(json.dumps(line), flush=True)
