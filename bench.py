@@ -450,6 +450,15 @@ def variant_unified(torch, fd, W, args, timer):
                 dense_over_unified=round(t_d["ms"] / t_u["ms"], 3))
 
 
+def selected_variants(spec):
+    """Variant names of a comma-separated --variants value, checked."""
+    want = [x for x in spec.split(",") if x]
+    unknown = [x for x in want if x not in VARIANTS]
+    if unknown:
+        sys.exit(f"unknown variants {unknown}; choose from {list(VARIANTS)}")
+    return want
+
+
 def _ffd_override(args):
     if args.ffd_deltas is None:
         return {}
@@ -610,6 +619,8 @@ def variant_ffd_peaked(torch, fd, W, args, timer):
 
 def main():
     args = parse_args()
+    want = selected_variants(args.variants)
+    _ffd_override(args)   # rejects a malformed --ffd-deltas before any GPU work
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "
               "(the multi-GPU split is a design note, not a built path)", file=sys.stderr)
@@ -656,10 +667,6 @@ def main():
         fns = dict(dense_128k=variant_dense_128k, paged=variant_paged,
                    unified_max=variant_unified, ffd=variant_ffd, ffd_peaked=variant_ffd_peaked,
                    multi_row=variant_multi, append=variant_append)
-        want = [x for x in args.variants.split(",") if x]
-        unknown = [x for x in want if x not in fns]
-        if unknown:
-            sys.exit(f"unknown variants {unknown}; choose from {list(fns)}")
         line["variants"] = {name: fns[name](torch, fd, W, args, timer)
                             for name in VARIANTS if name in want}
     if not args.no_cpu_baseline:
