@@ -362,8 +362,8 @@ int fd_ffd_pack(const void* k, uint32_t* codes, uint16_t* zs, int8_t* res, uint1
     return fail(FD_ERR_ARG, "need 0 <= t_begin=%d <= t_end=%d <= L_cap=%d", t_begin, t_end,
                 L_cap);
   if (!k || !codes || !zs || !res || !rs) return fail(FD_ERR_ARG, "NULL array");
-  if (!aligned16(k) || !aligned16(codes) || !aligned16(res))
-    return fail(FD_ERR_ARG, "k, codes and res must be 16-byte aligned");
+  if (!aligned16(k) || !aligned16(codes) || !aligned16(res) || ((uintptr_t)zs & 3) != 0)
+    return fail(FD_ERR_ARG, "k, codes and res must be 16-byte and zs 4-byte aligned");
   if (t_begin == t_end) return ok();
   fdk::FfdPackArgs pa{reinterpret_cast<const uint16_t*>(k), codes, zs, res, rs, B, Hkv, L_cap,
                       t_begin, t_end};

@@ -26,24 +26,8 @@ namespace fdk {
 
 constexpr int kMaxChunkPages = 1024;
 
-#ifndef FD_WAVES_PER_EU
-#define FD_WAVES_PER_EU 1
-#endif
 // 16-byte pieces of a cache row per lane (see Geo in splitkv.hpp).
-#ifndef FD_PIECES
-#define FD_PIECES 2
-#endif
-constexpr int kP = FD_PIECES;
-// Finished units' merged values wait in LDS (1) or in registers (0): in LDS
-// they leave the batch loop more vector registers (headline step 167.8 ->
-// 166.4 us).
-#ifndef FD_KEEP_LDS
-#define FD_KEEP_LDS 1
-#endif
-// Contiguous caches: K and V batches through buffer loads (see `issue_c`).
-#ifndef FD_BUF_DENSE
-#define FD_BUF_DENSE 1
-#endif
+constexpr int kP = 2;
 
 // Fixed-maximum update with in-flight fallback.  A row slot takes
 // p = 2^((s - phi) c) while its running maximum stays inside
@@ -126,7 +110,7 @@ struct Unit {
 // row slots are merged while those loads are in flight.  So a wave's loads
 // never stop between its first and its last unit.
 template <int MODE, typename E, int D, int G>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(FD_WAVES_PER_EU)))
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1)))
 void partial_kernel(PartialArgs a) {
   // two pieces per lane halve the per-row work; G = 8 keeps one piece, as
   // its accumulators already fill the registers
@@ -135,8 +119,7 @@ void partial_kernel(PartialArgs a) {
   constexpr int VEC = Gm::kVec, LPT = Gm::kLpt, PV = Gm::kPv, TPL = Gm::kTpl, ROW = Gm::kRow;
   // rows per slot per batch: the batch depth counts load instructions per
   // tensor, and each row takes kPg of them
-  constexpr int kNbLoads =
-      batch_rows<G, MODE == kUnified ? FD_NB_FIXED : (MODE == kPaged ? FD_NB_PAGED : FD_NB)>();
+  constexpr int kNbLoads = batch_rows<G>();
   constexpr int NB = kNbLoads / kPg > 0 ? kNbLoads / kPg : 1;
   constexpr int STEP = NB * TPL;   // rows per wave batch
   constexpr bool kFixed = MODE == kUnified;
@@ -286,7 +269,7 @@ void partial_kernel(PartialArgs a) {
       for (int pc = 0; pc < kPg; ++pc)
         r[i * kPg + pc] = ld16_stream(src + off[i] + (size_t)pc * (ROW / kPg));
   };
-  // Contiguous caches with FD_BUF_DENSE: a batch of the tensor at `src`
+  // Contiguous caches: a batch of the tensor at `src`
   // starting at row t0 of unit x is read through one buffer descriptor whose
   // base is that row and whose byte limit ends at the unit's end c1, so rows
   // past c1 read as zeros without touching memory (their scores are masked,
@@ -315,7 +298,7 @@ void partial_kernel(PartialArgs a) {
         r[i * kPg + pc] = ld16_buf(rs, lane_voff[byte / 4096] + byte % 4096 + pc * kPcBytes);
       }
   };
-  constexpr bool kBufC = FD_BUF_DENSE && !kPagedMode;
+  constexpr bool kBufC = !kPagedMode;
   u32x4 qv[G][kPg];
   auto load_q = [&](const Unit& x) {
     const E* qp = reinterpret_cast<const E*>(a.q) +
@@ -345,28 +328,25 @@ void partial_kernel(PartialArgs a) {
     }
   };
 
-  // Finished units wait in registers until H are held or the wave runs out
-  // of units, and are then written together.  Stores count on the same
+  // Finished units wait (in LDS) until H are held or the wave runs out of
+  // units, and are then written together.  Stores count on the same
   // vector-memory counter as loads, so a store issued between units would
   // make the next unit's first loads wait for it (measured: 11 us of 169 on
   // the 1 GiB workload).  After the reduce-scatter every lane has NK values
   // of the unit and NCOPY lanes have the same ones, so the copies take turns:
-  // held unit j stays in keep_o[j / NCOPY] of the lanes with copy index
-  // j % NCOPY, which also write it.  The unit's (m, l) and flags stay with
-  // the lanes of row slot j.
+  // held unit j stays in slot j / NCOPY of s_keep for the lanes with copy
+  // index j % NCOPY, which also write it.  The unit's (m, l) and flags stay
+  // with the lanes of row slot j.
   using SS = SlotScatter<LPT, G, VEC>;
   constexpr int NK = SS::NK, NCOPY = SS::NCOPY;
-  constexpr int NSLOT = 64 / NK;   // units held per lane (64 registers)
+  constexpr int NSLOT = 64 / NK;   // units held per lane (64 values)
   constexpr int H = TPL < NSLOT * NCOPY ? TPL : NSLOT * NCOPY;
   const int cpy = SS::copy(lane);
   constexpr int NSLOTS = (H + NCOPY - 1) / NCOPY;
-#if FD_KEEP_LDS
   // held values in LDS (lane-major 16-byte groups: conflict-free), which
-  // keeps the batch loop's working set in the vector registers
+  // keeps the batch loop's working set in the vector registers (headline step
+  // 167.8 -> 166.4 us against holding them in registers)
   __shared__ __align__(16) f32x4 s_keep[kWaves][NSLOTS][NK / 4][kWave];
-#else
-  float keep_o[NSLOTS][NK];
-#endif
   float keep_m[G], keep_l[G];
   size_t keep_rows[H];
   size_t keep_row_ml = 0;
@@ -381,12 +361,7 @@ void partial_kernel(PartialArgs a) {
           const int K = SS::index(lane, k);
           const int h = K / VEC, e = K % VEC;
           float* dst = a.o_part + (keep_rows[j] + (size_t)h * a.nc) * D + Gm::dim(col, e);
-#if FD_KEEP_LDS
           *reinterpret_cast<f32x4*>(dst) = s_keep[wave][j / NCOPY][k / 4][lane];
-#else
-          const float* kv = keep_o[j / NCOPY];
-          *reinterpret_cast<f32x4*>(dst) = f32x4{kv[k], kv[k + 1], kv[k + 2], kv[k + 3]};
-#endif
         }
       }
     }
@@ -520,15 +495,10 @@ void partial_kernel(PartialArgs a) {
     for (int j = 0; j < H; ++j) {
       if (held == j) {   // wave-uniform
         if (cpy == j % NCOPY) {
-#if FD_KEEP_LDS
 #pragma unroll
           for (int k = 0; k < NK; k += 4)
             s_keep[wave][j / NCOPY][k / 4][lane] =
                 f32x4{kept[k], kept[k + 1], kept[k + 2], kept[k + 3]};
-#else
-#pragma unroll
-          for (int k = 0; k < NK; ++k) keep_o[j / NCOPY][k] = kept[k];
-#endif
         }
         keep_rows[j] = row0;
       }
@@ -754,15 +724,12 @@ hipError_t launch_partial(int mode, int is_bf16, int D, int G, const PartialArgs
   return hipErrorInvalidValue;
 }
 
-#ifndef FD_MERGE_WIDE_W
-#define FD_MERGE_WIDE_W 4
-#endif
 hipError_t launch_merge(int D, int B, const MergeArgs& a, hipStream_t s) {
   const size_t rows = (size_t)B * a.Hq;
   // Rows of 64 chunks or more split their columns over 2 workgroups, rows
-  // of 128 or more over 4 (FD_MERGE_WIDE_W waves each): more workgroups in
-  // flight for the same latency-bound walk over the chunks.
-  constexpr int WW = FD_MERGE_WIDE_W;
+  // of 128 or more over 4 (of 4 waves each): more workgroups in flight for
+  // the same latency-bound walk over the chunks.
+  constexpr int WW = 4;
   const int cs = a.nc >= 128 ? 4 : a.nc >= 64 ? 2 : 1;
   const dim3 grid((unsigned)(rows * cs));
   const dim3 block(cs > 1 ? WW * kWave : 4 * kWave);

@@ -162,15 +162,8 @@ __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
 __device__ __forceinline__ u32x4 ld16(const void* p) {
   return *reinterpret_cast<const u32x4*>(p);
 }
-#ifndef FD_NT_LOADS
-#define FD_NT_LOADS 1
-#endif
 __device__ __forceinline__ u32x4 ld16_stream(const void* p) {
-#if FD_NT_LOADS
   return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
-#else
-  return *reinterpret_cast<const u32x4*>(p);
-#endif
 }
 
 // Raw buffer descriptors (gfx9 family): word 3 of a plain byte-addressed

@@ -33,21 +33,11 @@
 
 namespace fdk {
 
-#ifndef FD_FFD_NT
-#define FD_FFD_NT 1
-#endif
-#ifndef FD_FFD_SCAN_STEPS
-#define FD_FFD_SCAN_STEPS 8
-#endif
-#ifndef FD_FFD_BATCHED_SUM
-#define FD_FFD_BATCHED_SUM 0
-#endif
-#ifndef FD_FFD_NB
-#define FD_FFD_NB 8
-#endif
-#ifndef FD_FFD_MFMA_TILES
-#define FD_FFD_MFMA_TILES 8
-#endif
+// load rounds of the scan (positions per lane per round) and rows per slot
+// per batch of the dot-product refine
+constexpr int kScanSteps = 8;
+constexpr int kScanTiles = 8;   // 16-position tiles per round on the matrix cores
+constexpr int kRefineRows = 8;
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
 
@@ -68,11 +58,7 @@ __host__ __device__ constexpr size_t ffd_lds_bytes(int chunk) {
 
 template <class T>
 __device__ __forceinline__ T ffd_load(const T* p) {
-#if FD_FFD_NT
   return __builtin_nontemporal_load(p);
-#else
-  return *p;
-#endif
 }
 
 __device__ __forceinline__ float half_to_float(uint32_t bits16) {
@@ -339,7 +325,7 @@ template <int D, int G>
 __global__ __launch_bounds__(kThreads) void ffd_kernel(FfdArgs a) {
   using Gm = Geo<uint16_t, D>;
   constexpr int VEC = Gm::kVec, LPT = Gm::kLpt, TPL = Gm::kTpl;
-  constexpr int kNb = FD_FFD_NB;     // rows per slot per batch in the refine
+  constexpr int kNb = kRefineRows;   // rows per slot per batch in the refine
   constexpr int NG = D / 32;         // quantisation groups per position
   constexpr int TPS = kWave / NG;    // positions per wave step in the scan
   constexpr int CW = D / 16;         // code words per position
@@ -395,7 +381,7 @@ __global__ __launch_bounds__(kThreads) void ffd_kernel(FfdArgs a) {
     // group g and receives C for exactly that group: one fma per head gives
     // the group's part of the score, two shuffles sum the four groups.
     constexpr int NT = G / 4;
-    constexpr int TB = FD_FFD_MFMA_TILES;     // 16-position tiles per load round
+    constexpr int TB = kScanTiles;            // 16-position tiles per load round
     const int n16 = lane & 15, qg = lane >> 4;
     u32x4 qa[NT][4];
     float qsum[NT][4];
@@ -462,7 +448,7 @@ __global__ __launch_bounds__(kThreads) void ffd_kernel(FfdArgs a) {
                  (bf16_lo(qs[h][j].w) + bf16_hi(qs[h][j].w));
       }
     }
-    constexpr int kSteps = FD_FFD_SCAN_STEPS;
+    constexpr int kSteps = kScanSteps;
     for (int r0 = wave * TPS * kSteps; r0 < n; r0 += kWaves * TPS * kSteps) {
       u32x2 cw[kSteps];
       uint32_t zz[kSteps];
@@ -671,8 +657,9 @@ __global__ __launch_bounds__(kThreads) void ffd_kernel(FfdArgs a) {
       float* pb = &s_pb[wave][0][0];
 #pragma unroll
       for (int h = 0; h < G; ++h) {
-        const float bias = (mh[h] == kNegInf) ? 0.f : mh[h] * a.c_log2;
-        const float p = exp2_hw(fmaf(sh[h], a.c_log2, -bias));
+        // exponent (s - m) c: exactly 0, p exactly 1, at the running maximum
+        const float base = (mh[h] == kNegInf) ? 0.f : mh[h];
+        const float p = exp2_hw((sh[h] - base) * a.c_log2);
         lh[h] += p;
         if ((h & 3) == qg) pb[h * 16 + n16] = p;
       }
@@ -766,27 +753,6 @@ __global__ __launch_bounds__(kThreads) void ffd_kernel(FfdArgs a) {
       vr[i] = ffd_load(reinterpret_cast<const u32x4*>(vb + (size_t)(c0 + jr[i]) * Gm::kRow +
                                                       (size_t)col * 16));
     float s[kNb][G];
-#if FD_FFD_BATCHED_SUM
-    float corr[kNb * G];
-#pragma unroll
-    for (int i = 0; i < kNb; ++i) {
-      float ci[G];
-      residual_dot<G>(rr[i], half_to_float(rsb[i]), qr, ql, ci);
-#pragma unroll
-      for (int h = 0; h < G; ++h) corr[i * G + h] = ci[h];
-    }
-    group_sum_n<LPT>(corr);
-#pragma unroll
-    for (int i = 0; i < kNb; ++i) {
-      const uint32_t mk = s_mask[jr[i]];
-      const bool valid = t0 + i * TPL + grp < t_end;
-#pragma unroll
-      for (int h = 0; h < G; ++h) {
-        const float sc = s_scan[jr[i]][h] + corr[i * G + h];
-        s[i][h] = (valid && ((mk >> h) & 1)) ? sc : kNegInf;
-      }
-    }
-#else
 #pragma unroll
     for (int i = 0; i < kNb; ++i) {
       float corr[G];
@@ -799,7 +765,6 @@ __global__ __launch_bounds__(kThreads) void ffd_kernel(FfdArgs a) {
         s[i][h] = (valid && ((mk >> h) & 1)) ? sc : kNegInf;
       }
     }
-#endif
     online_update<uint16_t, G, VEC, kNb>(s, vr, a.c_log2, acc, m, l);
   }
   state_to_log2<G>(m, a.c_log2);

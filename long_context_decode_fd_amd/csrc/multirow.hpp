@@ -36,38 +36,14 @@ namespace fdk {
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
 
-#ifndef FD_MR_TILES
-#define FD_MR_TILES 2   // 16-position tiles per wave batch: 8 K and 8 V loads at d = 128
-#endif
-#ifndef FD_MR_TILES2
-#define FD_MR_TILES2 4   // with two query tiles (deeper batches pay once the K=32 P V and
-                         // the vector-register accumulators freed registers)
-#endif
-#ifndef FD_MR_PV32_Q1
-#define FD_MR_PV32_Q1 0   // P V on 16x16x32 tile pairs with one query tile
-#endif
-#ifndef FD_MR_PV32_Q2
-#define FD_MR_PV32_Q2 1   // ... with two query tiles
-#endif
-#ifndef FD_MR_BUF_Q1
-#define FD_MR_BUF_Q1 1   // K/V tiles through buffer loads (see issue below), one query tile
-#endif
-#ifndef FD_MR_BUF_Q2
-#define FD_MR_BUF_Q2 1   // ... two query tiles (with 4-tile batches; at 2 tiles it measured
-                         // slower, 214 -> 255 us at M = 8)
-#endif
-#ifndef FD_MR_HOLD_Q2
-#define FD_MR_HOLD_Q2 1   // two query tiles: one finished unit held in LDS
-#endif
-#ifndef FD_MR_HWSPLIT
-#define FD_MR_HWSPLIT 1   // hi/lo split of P by the hardware bf16 conversion
-#endif
-#ifndef FD_MR_WAVES_PER_EU
-#define FD_MR_WAVES_PER_EU 1
-#endif
-#ifndef FD_MR_HOLD
-#define FD_MR_HOLD 4    // finished units held in registers before their partials are written
-#endif
+// 16-position tiles per wave batch: 8 K and 8 V loads at d = 128 with one
+// query tile; 4 tiles with two (deeper batches pay once the 16x16x32 P V and
+// the vector-register accumulators freed registers).
+template <int QT>
+constexpr int mr_tiles() { return QT == 1 ? 2 : 4; }
+// finished units held in registers before their partials are written (one
+// query tile)
+constexpr int kMrHold = 4;
 
 
 __device__ __forceinline__ f32x4 mfma_qk(const u32x4& a, const u32x4& b, f32x4 c) {
@@ -80,29 +56,10 @@ __device__ __forceinline__ f32x4 mfma_pv(const u32x2& a, const u32x2& b, f32x4 c
                                                     __builtin_bit_cast(s16x4_t, b), c, 0, 0, 0);
 }
 
-typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-
 // p = hi + lo with hi = bf16(p), lo = bf16(p - hi), both rounded to nearest
 // even by the hardware conversion (two values per instruction): two bf16
 // pairs from four fp32 values.
-__device__ __forceinline__ uint32_t bf16_bits(float x) {
-  const uint32_t u = __float_as_uint(x);
-  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
-}
 __device__ __forceinline__ void split_bf16(const float (&p)[4], u32x2& hi, u32x2& lo) {
-#if !FD_MR_HWSPLIT
-  {
-  uint32_t h[4], l[4];
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    h[e] = bf16_bits(p[e]);
-    l[e] = bf16_bits(p[e] - __uint_as_float(h[e] << 16));
-  }
-  hi = u32x2{h[0] | (h[1] << 16), h[2] | (h[3] << 16)};
-  lo = u32x2{l[0] | (l[1] << 16), l[2] | (l[3] << 16)};
-  return;
-  }
-#endif
   uint32_t h[2], l[2];
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
@@ -119,11 +76,11 @@ __device__ __forceinline__ void split_bf16(const float (&p)[4], u32x2& hi, u32x2
 // QT = query tiles of 16 rows (R = G*M <= 16 * QT); both share every K and V
 // tile.
 template <int D, int QT>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(FD_MR_WAVES_PER_EU)))
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1)))
 void multi_kernel(MultiArgs a) {
   constexpr int KS = D / 32;             // QK k-steps (32 dims each)
   constexpr int DB = D / 16;             // 16-dim blocks of the P V product
-  constexpr int TT = QT == 1 ? FD_MR_TILES : FD_MR_TILES2;
+  constexpr int TT = mr_tiles<QT>();
   constexpr int STEP = 16 * TT;          // positions per wave batch
   constexpr int ROWB = D * 2;            // bytes per cache row
   constexpr int LPR = ROWB / 16;         // lanes per row in a coalesced load
@@ -197,22 +154,13 @@ void multi_kernel(MultiArgs a) {
   // immediate; the scalar offset is 0.
   const int lane_off = lrow * ROWB + 16 * lcol;
   auto issue = [&](const char* __restrict__ src, int T, int c1, u32x4 (&r)[TT][NI]) {
-    constexpr bool kBuf = QT == 1 ? FD_MR_BUF_Q1 : FD_MR_BUF_Q2;
 #pragma unroll
     for (int tt = 0; tt < TT; ++tt) {
-      if constexpr (kBuf) {
       const int t0 = T + 16 * tt;
       const int nrow = min(max(c1 - t0, 0), 16);
       const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(src + (size_t)t0 * ROWB, nrow * ROWB);
 #pragma unroll
       for (int i = 0; i < NI; ++i) r[tt][i] = ld16_buf(rs, lane_off + RPI * i * ROWB);
-      } else {
-#pragma unroll
-      for (int i = 0; i < NI; ++i) {
-        const int t = min(T + 16 * tt + RPI * i + lrow, c1 - 1);
-        r[tt][i] = ld16_stream(src + (size_t)t * ROWB + 16 * lcol);
-      }
-      }
     }
   };
   // a tile of 16 rows into this wave's LDS tile (row-major, stride LSTR)
@@ -296,9 +244,8 @@ void multi_kernel(MultiArgs a) {
   // and are written together when H are held or the wave has no unit left.
   // Stores count on the same vector-memory counter as loads: partials
   // stored between units made the next unit's first K wait for them.
-  constexpr int H = QT == 1 ? FD_MR_HOLD : 1;
+  constexpr int H = QT == 1 ? kMrHold : 1;
   f32x4 hold_o[H][QT][DB];
-#if FD_MR_HOLD_Q2
   // two query tiles: no registers to spare, so one finished unit waits in
   // LDS (32 O rows) and is written together with the next one, which halves
   // the store events between units
@@ -306,7 +253,6 @@ void multi_kernel(MultiArgs a) {
   float h2_m[QT], h2_l[QT];
   int h2_u = 0;
   bool h2_held = false;   // wave-uniform
-#endif
   float hold_m[H][QT], hold_l[H][QT];
   int hold_u[H];
   int held = 0;   // wave-uniform
@@ -396,7 +342,7 @@ void multi_kernel(MultiArgs a) {
         }
       }
 
-      float bias[QT];
+      float base[QT];   // running maximum (raw), 0 while it is -inf
 #pragma unroll
       for (int qt = 0; qt < QT; ++qt) {
         float bm = kNegInf;
@@ -419,7 +365,8 @@ void multi_kernel(MultiArgs a) {
             for (int e = 0; e < 4; ++e) o[qt][db][e] *= ae[e];
           m[qt] = mn;
         }
-        bias[qt] = (m[qt] == kNegInf) ? 0.f : m[qt] * c_log2;
+        // exponent (s - m) c: exactly 0 at the running maximum
+        base[qt] = (m[qt] == kNegInf) ? 0.f : m[qt];
       }
 
       u32x2 ph[QT][TT], pl[QT][TT];
@@ -430,7 +377,7 @@ void multi_kernel(MultiArgs a) {
           float p[4];
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            p[e] = exp2_hw(fmaf(sc[qt][tt][e], c_log2, -bias[qt]));
+            p[e] = exp2_hw((sc[qt][tt][e] - base[qt]) * c_log2);
             l[qt] += p[e];
           }
           split_bf16(p, ph[qt][tt], pl[qt][tt]);
@@ -441,8 +388,8 @@ void multi_kernel(MultiArgs a) {
       // operand the transposed reads of both V tiles (each staged in one of
       // the wave's two LDS tiles; the K tiles are no longer needed here, and
       // LDS keeps the wave's order).
-      constexpr bool kPv32 = QT == 1 ? FD_MR_PV32_Q1 : FD_MR_PV32_Q2;
-      constexpr int NTP = kPv32 ? TT / 2 : 0;   // tile pairs on 16x16x32
+      // (with one query tile this form measured 3 % slower: register pressure)
+      constexpr int NTP = QT == 2 ? TT / 2 : 0;   // tile pairs on 16x16x32
 #pragma unroll
       for (int tp = 0; tp < NTP; ++tp) {
         to_lds(lk, vr[2 * tp]);
@@ -513,7 +460,6 @@ void multi_kernel(MultiArgs a) {
         held = 0;
       }
     } else {
-#if FD_MR_HOLD_Q2
       if constexpr (QT != 2) {
         store_unit(o, m, l, u);
       } else if (!h2_held && has_next) {
@@ -536,9 +482,6 @@ void multi_kernel(MultiArgs a) {
         store_unit(o, m, l, u);
         h2_held = false;
       }
-#else
-      store_unit(o, m, l, u);
-#endif
     }
     if (!has_next) break;
     cur = nxt;

@@ -12,6 +12,12 @@ def f64(t: torch.Tensor) -> np.ndarray:
     return t.detach().to("cpu", torch.float64).numpy()
 
 
+def f32(t: torch.Tensor) -> np.ndarray:
+    """Exact float32 copy of a bf16/fp32 device tensor (half the host memory
+    of f64 for large pools)."""
+    return t.detach().to("cpu", torch.float32).numpy()
+
+
 def max_err(a, b) -> float:
     a = np.asarray(a, dtype=np.float64)
     b = np.asarray(b, dtype=np.float64)

@@ -28,6 +28,92 @@ def test_exports_every_declared_symbol():
     assert fd.lib().fd_abi_version() == 1
 
 
+# The exported C ABI, argument by argument (type, name), as include/fd.h
+# declares it.  A change to any signature must change this table, the ctypes
+# declarations in _abi.py and fd_abi_version together.
+EXPECTED_PROTOTYPES = {
+    "fd_last_error": ("const char*", []),
+    "fd_abi_version": ("int", []),
+    "fd_decode_attn": ("int", [
+        "fd_dtype_t dt", "const void* q", "const void* k", "const void* v", "float* out",
+        "float* lse", "int B", "int Hq", "int Hkv", "int L", "int d", "float scale", "int chunk",
+        "void* ws", "size_t* ws_bytes", "void* stream"]),
+    "fd_decode_attn_partials": ("int", [
+        "fd_dtype_t dt", "const void* q", "const void* k", "const void* v", "int B", "int Hq",
+        "int Hkv", "int L", "int d", "float scale", "int chunk", "void* ws", "size_t* ws_bytes",
+        "void* stream"]),
+    "fd_merge_partials": ("int", [
+        "const float* o_part", "const float* ml_part", "float* out", "float* lse", "int B",
+        "int Hq", "int n_chunks", "int d", "void* stream"]),
+    "fd_decode_attn_paged": ("int", [
+        "fd_dtype_t dt", "const void* q", "const void* k_pool", "const void* v_pool",
+        "const int32_t* block_table", "const int32_t* seq_lens", "float* out", "float* lse",
+        "int B", "int Hq", "int Hkv", "int d", "int page_size", "int max_pages_per_seq",
+        "int num_pages", "int max_seq_len", "float scale", "int chunk", "void* ws",
+        "size_t* ws_bytes", "void* stream"]),
+    "fd_decode_attn_unified_max": ("int", [
+        "fd_dtype_t dt", "const void* q", "const void* k", "const void* v", "float* out",
+        "float* lse", "int B", "int Hq", "int Hkv", "int L", "int d", "float scale", "int chunk",
+        "float phi", "float margin_hi", "float margin_lo", "uint8_t* chunk_flags", "void* ws",
+        "size_t* ws_bytes", "void* stream"]),
+    "fd_decode_attn_multi": ("int", [
+        "fd_dtype_t dt", "const void* q", "const void* k", "const void* v", "float* out",
+        "float* lse", "int B", "int M", "int Hq", "int Hkv", "int L", "int d", "float scale",
+        "int chunk", "void* ws", "size_t* ws_bytes", "void* stream"]),
+    "fd_kv_append": ("int", [
+        "fd_dtype_t dt", "const void* k_new", "const void* v_new", "void* k_cache",
+        "void* v_cache", "int B", "int Hkv", "int M", "int L_cap", "int d", "int t",
+        "void* stream"]),
+    "fd_kv_append_paged": ("int", [
+        "fd_dtype_t dt", "const void* k_new", "const void* v_new", "void* k_pool",
+        "void* v_pool", "const int32_t* block_table", "const int32_t* pos", "int B", "int Hkv",
+        "int M", "int d", "int page_size", "int max_pages_per_seq", "int num_pages",
+        "void* stream"]),
+    "fd_ffd_pack": ("int", [
+        "const void* k", "uint32_t* codes", "uint16_t* zs", "int8_t* res", "uint16_t* rs",
+        "int B", "int Hkv", "int L_cap", "int d", "int t_begin", "int t_end", "void* stream"]),
+    "fd_ffd_sparse_decode": ("int", [
+        "const void* q", "const uint32_t* codes", "const uint16_t* zs", "const int8_t* res",
+        "const uint16_t* rs", "const void* v", "float* out", "float* lse", "int B", "int Hq",
+        "int Hkv", "int L", "int d", "float scale", "float delta", "int n_sink", "int n_local",
+        "int chunk", "uint32_t* cand_mask", "float* pseudo_max", "void* ws", "size_t* ws_bytes",
+        "void* stream"]),
+}
+
+
+def _prototypes():
+    """(return type, [argument declarations]) of every function in fd.h."""
+    txt = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
+    found = {}
+    for m in re.finditer(r"(int|const char\*)\s+(fd_[a-z_0-9]+)\s*\(([^)]*)\)\s*;", txt):
+        args = [" ".join(a.split()) for a in m.group(3).split(",")]
+        found[m.group(2)] = (m.group(1), [] if args == ["void"] else args)
+    return found
+
+
+def _ctypes_kind(decl):
+    ctype = decl.rsplit(" ", 1)[0]
+    if ctype == "size_t*":
+        return "size_t*"
+    if ctype.endswith("*"):
+        return "pointer"
+    return {"int": "int", "fd_dtype_t": "int", "float": "float"}[ctype]
+
+
+def test_exported_argument_lists_are_pinned():
+    """The header's prototypes equal the pinned table, and the ctypes
+    declarations the binding calls through agree with them argument by
+    argument (pointer / size_t* / int / float)."""
+    assert _prototypes() == EXPECTED_PROTOTYPES
+    kinds = {C.c_void_p: "pointer", C.c_int: "int", C.c_float: "float",
+             C.POINTER(C.c_size_t): "size_t*"}
+    for name, (ret, args) in EXPECTED_PROTOTYPES.items():
+        if name == "fd_last_error":
+            continue
+        assert ret == "int", name
+        assert [kinds[t] for t in _abi.SIGNATURES[name]] == [_ctypes_kind(a) for a in args], name
+
+
 def test_workspace_sizes():
     # O partials [B,Hq,nc,d] fp32 + (m,l) [B,Hq,nc,2] fp32, each 256-aligned
     n = fd.workspace_bytes("fd_decode_attn", B=8, Hq=32, Hkv=8, L=32768, d=128, chunk=512)
@@ -147,3 +233,17 @@ def test_multi_row_validation_and_workspace():
         assert e.value.code == code, bad
     # one token: the single-query path, any dtype
     assert fd.workspace_bytes("fd_decode_attn_multi", **dict(base, M=1, dt=_abi.FD_F32)) > 0
+
+
+def test_ffd_pack_rejects_misaligned_zs():
+    """The packer stores each (zero, step) pair as one 32-bit word, so zs must
+    be 4-byte aligned, as fd_ffd_sparse_decode also requires.  The pointers
+    are never dereferenced: validation fails first."""
+    lib = fd.lib()
+    p = C.c_void_p(256)
+    assert lib.fd_ffd_pack(p, p, C.c_void_p(258), p, p, 1, 1, 16, 128, 0, 16,
+                           None) == _abi.FD_ERR_ARG
+    assert b"zs" in lib.fd_last_error()
+    for args in [(p, p, C.c_void_p(258), p, p, p, p, p, 1, 8, 2, 64, 128, 0.1, 5.0, 4, 64, 32,
+                  None, None, p, C.byref(C.c_size_t(1 << 30)), None)]:
+        assert lib.fd_ffd_sparse_decode(*args) == _abi.FD_ERR_ARG

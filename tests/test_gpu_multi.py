@@ -72,23 +72,26 @@ def test_multi_row_chunk_independence():
     assert max_err(f64(o1), f64(o2)) <= 1e-5 and max_err(f64(l1), f64(l2)) <= 1e-5
 
 
-def test_multi_row_full_size_sampled():
-    """Headline shape with four new tokens per sequence (G*M = 16 rows)."""
+def test_multi_row_full_size():
+    """Headline shape with four new tokens per sequence (G*M = 16 rows):
+    every (sequence, token, head) row."""
     banner("multi full size B=8 L=32768 M=4")
     c = W.multi_case(8, 4, 32, 8, 32768, 128, seed=102, device=DEV)
-    rows = [(0, 0, 0), (0, 3, 31), (3, 1, 17), (5, 2, 8), (7, 3, 30), (7, 0, 1)]
-    _check(c, chunk=512, rows=rows)
+    _check(c, chunk=512)
 
 
-def test_multi_row_two_query_tiles_full_size_sampled():
+def test_multi_row_two_query_tiles_full_size():
     """Headline shape with eight new tokens per sequence (G*M = 32 rows: two
-    query tiles sharing every K and V tile)."""
+    query tiles sharing every K and V tile): every row."""
     banner("multi full size B=8 L=32768 M=8")
     c = W.multi_case(8, 8, 32, 8, 32768, 128, seed=108, device=DEV)
-    rows = [(0, 0, 0), (0, 7, 31), (2, 4, 13), (6, 3, 22), (7, 7, 3), (7, 5, 30)]
-    _check(c, chunk=512, rows=rows)
+    _check(c, chunk=512)
 
 
+# The remaining large multi-row cases check a sample of rows: the oracle
+# streams a row's whole fp64 K and V prefix for every row (64 MB per row at
+# L 32768, 2 GB at 2^20), so every row would take minutes of host time; the
+# two headline-shape tests above check every row.
 def test_multi_row_many_units_per_wave_sampled():
     """Chunks of 32 at the headline shape: 16,384 units, so every wave
     finishes many units and writes its held partials several times."""

@@ -10,7 +10,7 @@ import workloads as W
 from oracle import flash_decoding as ofd
 from oracle import paged as opg
 from oracle import unified as oun
-from tests.helpers import TOL, banner, f64, max_err
+from tests.helpers import TOL, banner, f32, f64, max_err
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
@@ -25,7 +25,10 @@ def _paged_run(c, max_len=None):
 
 
 def _paged_ref(c, rows=None):
-    return opg.paged_attention(f64(c.q), f64(c.k_pool), f64(c.v_pool),
+    # the pools as exact fp32 copies (bf16 and fp32 values are fp32): half
+    # the host memory of fp64, and the oracle's gather widens each
+    # sequence's rows to fp64
+    return opg.paged_attention(f64(c.q), f32(c.k_pool), f32(c.v_pool),
                                c.block_table.cpu().numpy(), c.seq_lens.cpu().numpy(), c.page,
                                c.scale, rows=rows)
 
@@ -105,16 +108,16 @@ def test_paged_equal_remainders():
     assert max_err(f64(out), ref) <= 2e-3 and max_err(f64(lse), lref) <= 2e-3
 
 
-def test_paged_config3_full_size_sampled():
+def test_paged_config3_full_size():
+    """Paged ragged workload (16 sequences, lengths U[1024, 131072], page 16,
+    chunk 1024): every one of the 512 (sequence, head) rows."""
     banner("paged config3 full size")
     c = W.config_case(3, device=DEV)
     out, lse = _paged_run(c)
-    rows = [(0, 0), (3, 17), (9, 31), (15, 8)]
-    ref, lref = _paged_ref(c, rows)
-    for b, h in rows:
-        assert max_err(f64(out[b, h]), ref[b, h]) <= 2e-3
-        assert abs(float(lse[b, h]) - lref[b, h]) <= 2e-3
     assert torch.isfinite(out).all()
+    ref, lref = _paged_ref(c)
+    eo, el = max_err(f64(out), ref), max_err(f64(lse), lref)
+    assert eo <= 2e-3 and el <= 2e-3, (eo, el)
 
 
 def _unified_check(c, phi, margin_hi, margin_lo):
@@ -180,25 +183,16 @@ def test_unified_many_units_per_wave():
     assert 0 < int(flags.sum()) < flags.size
 
 
-def test_unified_config4_full_size_sampled():
+def test_unified_config4_full_size():
+    """Fixed-maximum workload (B 4, L 65536, chunk 512, 2 heads planted
+    above phi): every (sequence, head) row against the dense definition,
+    every chunk flag against the oracle's outside the 1e-4 band, and only the
+    planted chunks flagged."""
     banner("unified config4 full size")
     c = W.config_case(4, device=DEV)
-    out, lse, flags = fd.decode_attn_unified_max(c.q, c.k, c.v, c.phi, chunk=c.chunk,
-                                                 margin_hi=c.margin_hi, margin_lo=c.margin_lo)
-    torch.cuda.synchronize()
-    G = 4
-    rows = [(b, h) for b, h, _ in c.overflow_heads] + [(0, 0), (2, 19), (3, 31)]
-    for b, h in rows:
-        r, lr = ofd.attention_row(f64(c.q[b, h]), f64(c.k[b, h // G]), f64(c.v[b, h // G]),
-                                  c.scale)
-        assert max_err(f64(out[b, h]), r) <= 2e-3
-        assert abs(float(lse[b, h]) - lr) <= 2e-3
-    for b, h, j in c.overflow_heads:
-        assert flags[b, h, j // c.chunk] == 1
-    assert torch.isfinite(out).all()
-    # only planted heads leave the range on this workload
+    flags = _unified_check(c, c.phi, c.margin_hi, c.margin_lo)
     planted = {(b, h, j // c.chunk) for b, h, j in c.overflow_heads}
-    got = {tuple(x) for x in torch.nonzero(flags).tolist()}
+    got = {tuple(x) for x in np.argwhere(flags).tolist()}
     assert got == planted
 
 
@@ -219,20 +213,17 @@ def test_paged_merge_of_many_chunks(d):
     assert eo <= TOL[torch.bfloat16] and el <= TOL[torch.bfloat16], (eo, el)
 
 
-def test_paged_one_million_positions_sampled():
+def test_paged_one_million_positions():
     """A pool holding one sequence of 2^20 + 5 positions (65,537 pages of 16)
     beside a short one: 1,025 chunks of 1,024 for the long row, 3 for the
-    short one, in one call."""
-    banner("paged 1M sampled")
+    short one, in one call.  Every row checked."""
+    banner("paged 1M")
     lens = [(1 << 20) + 5, 3000]
     c = W.paged_case(2, 8, 2, 128, 0, max(lens), page=16, chunk=1024, seed=1205, device=DEV,
                      lens=lens)
     out, lse = _paged_run(c)
-    rows = [(0, 0), (0, 5), (1, 3)]
-    ref, lref = _paged_ref(c, rows)
-    for b, h in rows:
-        assert max_err(f64(out[b, h]), ref[b, h]) <= 2e-3
-        assert abs(float(lse[b, h]) - lref[b, h]) <= 2e-3
+    ref, lref = _paged_ref(c)
+    assert max_err(f64(out), ref) <= 2e-3 and max_err(f64(lse), lref) <= 2e-3
     assert torch.isfinite(out).all()
 
 

@@ -13,7 +13,7 @@ from oracle import flash_decoding as ofd
 from oracle import multi_row as omr
 from oracle import paged as opg
 from tests.helpers import TOL, banner, f64, max_err, packed_to_device
-from tests.test_gpu_ffd import _row_check
+from tests.test_gpu_ffd import _check_all
 from tests.test_gpu_paged_unified import _unified_check
 
 pytestmark = pytest.mark.gpu
@@ -121,8 +121,5 @@ def test_ffd_random(i):
                                                 n_sink, n_local, chunk=chunk, want_mask=True,
                                                 want_pseudo_max=True)
     torch.cuda.synchronize()
-    q, v64 = f64(c.q), f64(c.v)
-    o, l_, cm, pm = f64(out), f64(lse), cand.cpu().numpy().view(np.uint32), f64(pmax)
-    for b in range(B):
-        for h in range(Hq):
-            _row_check(q, ph, v64, b, h, G, c.scale, delta, n_sink, n_local, o, l_, cm, pm)
+    _check_all(f64(c.q), ph, f64(c.v), G, c.scale, delta, n_sink, n_local, f64(out), f64(lse),
+               cand.cpu().numpy().view(np.uint32), f64(pmax))
