@@ -16,7 +16,9 @@
  *
  * Conventions shared by every entry point
  *   - All pointers except `ws_bytes` and `stream` are DEVICE pointers.  The
- *     caller allocates every buffer; the library never allocates or frees.
+ *     caller allocates every buffer (fd_decode_attn_noalloc aside, whose
+ *     partials buffer is a static array of the library); the library never
+ *     allocates or frees.
  *   - Layouts are dense row-major with the shapes given below; element types
  *     are bf16 (raw 16-bit storage), fp32, fp16 (raw 16-bit storage), int8,
  *     int32 or uint32 as stated.  Alignment: q, k, v, pools, out and packed
@@ -85,6 +87,30 @@ int fd_decode_attn(fd_dtype_t dt, const void* q, const void* k, const void* v,
                    float* out, float* lse,
                    int B, int Hq, int Hkv, int L, int d, float scale, int chunk,
                    void* ws, size_t* ws_bytes, void* stream);
+
+/*
+ * fd_decode_attn without a workspace and without any allocation, for callers
+ * that cannot allocate device memory: code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc.  Same arguments (minus ws,
+ * ws_bytes), kernels and result as fd_decode_attn.  The chunk partials go to
+ * a buffer the library owns: FD_NOALLOC_BYTES on every device the library
+ * runs on, held until the process ends.  The call uses the current device's
+ * buffer (`stream` must belong to the current device).
+ *   - FD_ERR_WORKSPACE, with nothing launched, when the partials need more:
+ *     round_up(B*Hq*n_chunks*d*4, 256) + round_up(B*Hq*n_chunks*8, 256)
+ *     bytes (8.5 MB at B 8, Hq 32, d 128, 64 chunks).
+ *   - Every call on one device shares that device's buffer, and it keeps the
+ *     last call's contents (nothing in it needs clearing: every partial a
+ *     call reads, that call writes first).  Calls that may overlap on one
+ *     device (different streams, or several host threads) race and must be
+ *     ordered by the caller.
+ */
+#define FD_NOALLOC_BYTES (32u << 20)
+
+int fd_decode_attn_noalloc(fd_dtype_t dt, const void* q, const void* k, const void* v,
+                           float* out, float* lse,
+                           int B, int Hq, int Hkv, int L, int d, float scale, int chunk,
+                           void* stream);
 
 /*
  * The two stages of fd_decode_attn, for callers that merge partials

@@ -7,6 +7,7 @@ stream); every step of the computation runs in the HIP kernels of
 
 Entry points (names follow the C ABI):
   decode_attn            dense contiguous cache
+  decode_attn_noalloc    the same without a workspace (library-owned buffer)
   decode_attn_partials, merge_partials   its two stages
   decode_attn_paged      paged cache with a block table
   decode_attn_unified_max  fixed maximum with exact fallback
@@ -25,7 +26,7 @@ import torch
 from . import _abi
 from ._abi import FD_BF16, FD_F32, FdError  # noqa: F401
 
-__all__ = ["decode_attn", "decode_attn_partials", "merge_partials", "partial_views",
+__all__ = ["decode_attn", "decode_attn_noalloc", "decode_attn_partials", "merge_partials", "partial_views",
            "decode_attn_paged", "decode_attn_unified_max", "decode_attn_multi", "kv_append",
            "kv_append_paged",
            "ffd_pack", "ffd_sparse_decode",
@@ -106,6 +107,24 @@ def decode_attn(q, k, v, chunk=512, scale=None, out=None, lse=None, want_lse=Tru
                 scale, int(chunk), ws, wsb, st)
     workspace, size = _workspace(L_.fd_decode_attn, args, workspace, dev)
     _abi.check(L_.fd_decode_attn(*args(_ptr(workspace), C.byref(size))))
+    return out, lse
+
+
+def decode_attn_noalloc(q, k, v, chunk=512, scale=None, out=None, lse=None, want_lse=True):
+    """decode_attn without a workspace: the chunk partials go to the library's
+    own per-device buffer (FD_NOALLOC_BYTES); nothing is allocated when out
+    (and lse, if wanted) are given.  Calls that overlap on one device race."""
+    B, Hq, d = q.shape
+    Hkv, L = k.shape[1], k.shape[2]
+    dev = q.device
+    _need(q, "q", device=dev)
+    _need(k, "k", (B, Hkv, L, d), q.dtype, dev)
+    _need(v, "v", (B, Hkv, L, d), q.dtype, dev)
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    out, lse = _outs(B, Hq, d, dev, out, lse, want_lse)
+    _abi.check(lib().fd_decode_attn_noalloc(_dt(q), _ptr(q), _ptr(k), _ptr(v), _ptr(out),
+                                            _ptr(lse), B, Hq, Hkv, L, d, scale, int(chunk),
+                                            _stream(dev)))
     return out, lse
 
 

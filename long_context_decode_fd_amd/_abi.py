@@ -12,6 +12,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfd_amd.s
 
 FD_F32, FD_BF16 = 0, 1
 FD_OK, FD_ERR_ARG, FD_ERR_UNSUPPORTED, FD_ERR_WORKSPACE, FD_ERR_HIP = range(5)
+FD_NOALLOC_BYTES = 32 << 20   # the library-owned partials buffer of fd_decode_attn_noalloc
 ERROR_NAMES = {FD_ERR_ARG: "FD_ERR_ARG", FD_ERR_UNSUPPORTED: "FD_ERR_UNSUPPORTED",
                FD_ERR_WORKSPACE: "FD_ERR_WORKSPACE", FD_ERR_HIP: "FD_ERR_HIP"}
 
@@ -22,6 +23,7 @@ SIGNATURES = {
     "fd_abi_version": [],
     "fd_decode_attn": [_i, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f, _i,
                        _vp, _szp, _vp],
+    "fd_decode_attn_noalloc": [_i, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f, _i, _vp],
     "fd_decode_attn_partials": [_i, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f, _i, _vp, _szp,
                                 _vp],
     "fd_merge_partials": [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _vp],

@@ -4,10 +4,18 @@
 #include <stdarg.h>
 #include <stdio.h>
 
+#include <atomic>
+#include <mutex>
 #include <string>
 
 #include "../../include/fd.h"
 #include "internal.hpp"
+
+// Chunk partials of fd_decode_attn_noalloc: a buffer owned by the library,
+// one copy on every device the library runs on (held until the process
+// ends).  Host code never uses this name as an address: the device address
+// of each device's copy comes from hipGetSymbolAddress (scratch_ptr below).
+static __device__ __align__(256) unsigned char scratch[FD_NOALLOC_BYTES];
 
 namespace {
 
@@ -126,6 +134,34 @@ int run_split_kv(int mode, fd_dtype_t dt, const void* q, const void* k, const vo
   return hip_status(fdk::launch_merge(d, B, ma, s), "merge kernel launch");
 }
 
+// Device address of `scratch` on each device, resolved once per device
+// with that device current (the first fd_decode_attn_noalloc call there).
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch[kMaxDevices];
+std::mutex g_scratch_mu;
+
+int scratch_ptr(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(FD_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(FD_ERR_UNSUPPORTED, "device %d beyond the %d the library tracks", dev,
+                kMaxDevices);
+  void* p = g_scratch[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch[dev].load(std::memory_order_relaxed);
+    if (p == nullptr) {
+      e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+      if (e != hipSuccess || p == nullptr)
+        return fail(FD_ERR_HIP, "hipGetSymbolAddress(scratch): %s", hipGetErrorString(e));
+      g_scratch[dev].store(p, std::memory_order_release);
+    }
+  }
+  *out = p;
+  return FD_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -149,6 +185,32 @@ int fd_decode_attn(fd_dtype_t dt, const void* q, const void* k, const void* v, f
   if (!q || !k || !v || !out) return fail(FD_ERR_ARG, "q, k, v and out must not be NULL");
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
     return fail(FD_ERR_ARG, "q, k, v and out must be 16-byte aligned");
+  fdk::PartialArgs pa{};
+  return run_split_kv(fdk::kDense, dt, q, k, v, out, lse, B, Hq, Hkv, L, d, scale, chunk, nc,
+                      pa, ws, nullptr, L, stream);
+}
+
+int fd_decode_attn_noalloc(fd_dtype_t dt, const void* q, const void* k, const void* v,
+                           float* out, float* lse, int B, int Hq, int Hkv, int L, int d,
+                           float scale, int chunk, void* stream) {
+  if (dt != FD_F32 && dt != FD_BF16) return fail(FD_ERR_ARG, "unknown dtype %d", (int)dt);
+  if (int e = check_heads(B, Hq, Hkv, d)) return e;
+  if (L <= 0) return fail(FD_ERR_ARG, "L=%d must be positive", L);
+  if (int e = check_chunk(chunk)) return e;
+  if (int e = check_scale(scale)) return e;
+  const int nc = n_chunks_of(L, chunk);
+  if (int e = check_units(B, Hq, nc)) return e;
+  const size_t need = partial_bytes(B, Hq, nc, d);
+  if (need > (size_t)FD_NOALLOC_BYTES)
+    return fail(FD_ERR_WORKSPACE,
+                "%zu bytes of chunk partials exceed the library's %zu-byte buffer "
+                "(use fd_decode_attn with a workspace, or longer chunks)",
+                need, (size_t)FD_NOALLOC_BYTES);
+  if (!q || !k || !v || !out) return fail(FD_ERR_ARG, "q, k, v and out must not be NULL");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
+    return fail(FD_ERR_ARG, "q, k, v and out must be 16-byte aligned");
+  void* ws = nullptr;
+  if (int e = scratch_ptr(&ws)) return e;
   fdk::PartialArgs pa{};
   return run_split_kv(fdk::kDense, dt, q, k, v, out, lse, B, Hq, Hkv, L, d, scale, chunk, nc,
                       pa, ws, nullptr, L, stream);

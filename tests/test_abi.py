@@ -38,6 +38,10 @@ EXPECTED_PROTOTYPES = {
         "fd_dtype_t dt", "const void* q", "const void* k", "const void* v", "float* out",
         "float* lse", "int B", "int Hq", "int Hkv", "int L", "int d", "float scale", "int chunk",
         "void* ws", "size_t* ws_bytes", "void* stream"]),
+    "fd_decode_attn_noalloc": ("int", [
+        "fd_dtype_t dt", "const void* q", "const void* k", "const void* v", "float* out",
+        "float* lse", "int B", "int Hq", "int Hkv", "int L", "int d", "float scale", "int chunk",
+        "void* stream"]),
     "fd_decode_attn_partials": ("int", [
         "fd_dtype_t dt", "const void* q", "const void* k", "const void* v", "int B", "int Hq",
         "int Hkv", "int L", "int d", "float scale", "int chunk", "void* ws", "size_t* ws_bytes",
