@@ -8,7 +8,10 @@ from __future__ import annotations
 import ctypes as C
 import os
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfd_amd.so")
+# FD_AMD_LIB selects another build of the same ABI (the host-sanitizer
+# build of the CPU checks); by default the in-tree library.
+LIB_PATH = os.environ.get("FD_AMD_LIB") or os.path.join(
+    os.path.dirname(os.path.abspath(__file__)), "libfd_amd.so")
 
 FD_F32, FD_BF16 = 0, 1
 FD_OK, FD_ERR_ARG, FD_ERR_UNSUPPORTED, FD_ERR_WORKSPACE, FD_ERR_HIP = range(5)

@@ -3,6 +3,7 @@
 #include <math.h>
 #include <stdarg.h>
 #include <stdio.h>
+#include <string.h>
 
 #include <atomic>
 #include <mutex>
@@ -33,6 +34,16 @@ int fail(int code, const char* fmt, ...) {
 
 int ok() {
   g_err.clear();
+  return FD_OK;
+}
+
+// A caller of the C ABI may pass any int as fd_dtype_t; in C++ an enum
+// value outside its enumerators' range is undefined, so the argument is
+// never read as an enum before this check: its integer representation is.
+int check_dtype(const fd_dtype_t* dt) {
+  int code;
+  memcpy(&code, dt, sizeof code);
+  if (code != FD_F32 && code != FD_BF16) return fail(FD_ERR_ARG, "unknown dtype %d", code);
   return FD_OK;
 }
 
@@ -173,7 +184,7 @@ int fd_abi_version(void) { return 1; }
 int fd_decode_attn(fd_dtype_t dt, const void* q, const void* k, const void* v, float* out,
                    float* lse, int B, int Hq, int Hkv, int L, int d, float scale, int chunk,
                    void* ws, size_t* ws_bytes, void* stream) {
-  if (dt != FD_F32 && dt != FD_BF16) return fail(FD_ERR_ARG, "unknown dtype %d", (int)dt);
+  if (int e = check_dtype(&dt)) return e;
   if (int e = check_heads(B, Hq, Hkv, d)) return e;
   if (L <= 0) return fail(FD_ERR_ARG, "L=%d must be positive", L);
   if (int e = check_chunk(chunk)) return e;
@@ -193,7 +204,7 @@ int fd_decode_attn(fd_dtype_t dt, const void* q, const void* k, const void* v, f
 int fd_decode_attn_noalloc(fd_dtype_t dt, const void* q, const void* k, const void* v,
                            float* out, float* lse, int B, int Hq, int Hkv, int L, int d,
                            float scale, int chunk, void* stream) {
-  if (dt != FD_F32 && dt != FD_BF16) return fail(FD_ERR_ARG, "unknown dtype %d", (int)dt);
+  if (int e = check_dtype(&dt)) return e;
   if (int e = check_heads(B, Hq, Hkv, d)) return e;
   if (L <= 0) return fail(FD_ERR_ARG, "L=%d must be positive", L);
   if (int e = check_chunk(chunk)) return e;
@@ -219,7 +230,7 @@ int fd_decode_attn_noalloc(fd_dtype_t dt, const void* q, const void* k, const vo
 int fd_decode_attn_partials(fd_dtype_t dt, const void* q, const void* k, const void* v,
                             int B, int Hq, int Hkv, int L, int d, float scale, int chunk,
                             void* ws, size_t* ws_bytes, void* stream) {
-  if (dt != FD_F32 && dt != FD_BF16) return fail(FD_ERR_ARG, "unknown dtype %d", (int)dt);
+  if (int e = check_dtype(&dt)) return e;
   if (int e = check_heads(B, Hq, Hkv, d)) return e;
   if (L <= 0) return fail(FD_ERR_ARG, "L=%d must be positive", L);
   if (int e = check_chunk(chunk)) return e;
@@ -256,7 +267,7 @@ int fd_decode_attn_paged(fd_dtype_t dt, const void* q, const void* k_pool,
                          int Hkv, int d, int page_size, int max_pages_per_seq,
                          int num_pages, int max_seq_len, float scale, int chunk, void* ws,
                          size_t* ws_bytes, void* stream) {
-  if (dt != FD_F32 && dt != FD_BF16) return fail(FD_ERR_ARG, "unknown dtype %d", (int)dt);
+  if (int e = check_dtype(&dt)) return e;
   if (int e = check_heads(B, Hq, Hkv, d)) return e;
   if (int e = check_chunk(chunk)) return e;
   if (int e = check_scale(scale)) return e;
@@ -297,7 +308,7 @@ int fd_decode_attn_unified_max(fd_dtype_t dt, const void* q, const void* k, cons
                                float scale, int chunk, float phi, float margin_hi,
                                float margin_lo, uint8_t* chunk_flags, void* ws,
                                size_t* ws_bytes, void* stream) {
-  if (dt != FD_F32 && dt != FD_BF16) return fail(FD_ERR_ARG, "unknown dtype %d", (int)dt);
+  if (int e = check_dtype(&dt)) return e;
   if (int e = check_heads(B, Hq, Hkv, d)) return e;
   if (L <= 0) return fail(FD_ERR_ARG, "L=%d must be positive", L);
   if (int e = check_chunk(chunk)) return e;
@@ -324,7 +335,7 @@ int fd_decode_attn_unified_max(fd_dtype_t dt, const void* q, const void* k, cons
 int fd_decode_attn_multi(fd_dtype_t dt, const void* q, const void* k, const void* v,
                          float* out, float* lse, int B, int M, int Hq, int Hkv, int L, int d,
                          float scale, int chunk, void* ws, size_t* ws_bytes, void* stream) {
-  if (dt != FD_F32 && dt != FD_BF16) return fail(FD_ERR_ARG, "unknown dtype %d", (int)dt);
+  if (int e = check_dtype(&dt)) return e;
   if (int e = check_heads(B, Hq, Hkv, d)) return e;
   if (M <= 0) return fail(FD_ERR_ARG, "M=%d must be positive", M);
   if (L < M) return fail(FD_ERR_ARG, "L=%d must be at least M=%d", L, M);
@@ -362,7 +373,7 @@ int fd_decode_attn_multi(fd_dtype_t dt, const void* q, const void* k, const void
 
 int fd_kv_append(fd_dtype_t dt, const void* k_new, const void* v_new, void* k_cache,
                  void* v_cache, int B, int Hkv, int M, int L_cap, int d, int t, void* stream) {
-  if (dt != FD_F32 && dt != FD_BF16) return fail(FD_ERR_ARG, "unknown dtype %d", (int)dt);
+  if (int e = check_dtype(&dt)) return e;
   if (B <= 0 || Hkv <= 0 || M <= 0 || L_cap <= 0)
     return fail(FD_ERR_ARG, "B=%d Hkv=%d M=%d L_cap=%d must be positive", B, Hkv, M, L_cap);
   if (d != 64 && d != 128) return fail(FD_ERR_UNSUPPORTED, "d=%d not in {64,128}", d);
@@ -386,7 +397,7 @@ int fd_kv_append_paged(fd_dtype_t dt, const void* k_new, const void* v_new, void
                        void* v_pool, const int32_t* block_table, const int32_t* pos, int B,
                        int Hkv, int M, int d, int page_size, int max_pages_per_seq,
                        int num_pages, void* stream) {
-  if (dt != FD_F32 && dt != FD_BF16) return fail(FD_ERR_ARG, "unknown dtype %d", (int)dt);
+  if (int e = check_dtype(&dt)) return e;
   if (B <= 0 || Hkv <= 0 || M <= 0 || max_pages_per_seq <= 0 || num_pages <= 0)
     return fail(FD_ERR_ARG, "B=%d Hkv=%d M=%d max_pages=%d num_pages=%d must be positive", B,
                 Hkv, M, max_pages_per_seq, num_pages);
