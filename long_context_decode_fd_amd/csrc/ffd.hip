@@ -4,42 +4,36 @@
 // the candidates and exact attention over them (sections 3-6, Fig. 2), plus
 // the packer that produces the key format (section 5).
 //
-// One workgroup = one unit = (sequence, kv-head, chunk), fused:
-//   0. Anchors.  A small kernel scores the anchor positions of every
-//      (sequence, kv-head) with the refined key (2-bit + residual) once and
-//      leaves m^ and j* per query head in the workspace.
+//   0. Anchors (every shape).  ffd_anchor_kernel scores the anchor positions
+//      of every (sequence, kv-head) with the refined key (2-bit + residual)
+//      once and leaves m^ and j* per query head in the workspace.
+//   1-4. At d = 128 with G = 4 or 8 the wave-streamed kernel of ffd_wave.hip
+//      (matrix cores, one wavefront per chunk) does the rest.  Every other
+//      shape runs ffd_kernel below, one workgroup per unit = (sequence,
+//      kv-head, chunk), fused:
 //   1. Scan.  4 lanes per position (one 32-dim quantisation group each) read
 //      8 B of codes and 4 B of (zero, step).  Codes become exact bf16 values
 //      4 + c (a rotate and an and-or per pair, since bf16 4..7 differ only in
-//      two mantissa bits); sum q_i c_i = sum q_i (4 + c_i) - 4 sum q_i.  At
-//      d = 128 with G = 4 or 8 the products run on the matrix cores (the
-//      groups of 4 heads stacked block-diagonally in one 16x16x32 tile), else
-//      in v_dot2c_f32_bf16.  The scan score and the G-bit candidate mask of
-//      every position stay in LDS (no write-back).
+//      two mantissa bits); sum q_i c_i = sum q_i (4 + c_i) - 4 sum q_i, with
+//      v_dot2c_f32_bf16.  The scan score and the G-bit candidate mask of every
+//      position stay in LDS (no write-back).
 //   2. Compaction of the positions that are a candidate for any head of the
 //      group (they share the residual and V loads).
 //   3. Refine + attend over the compacted list: residual bytes become exact
-//      bf16 (r + 128); each head's softmax covers only its own candidates.
-//      At d = 128 with G = 4 or 8 on the matrix cores, 16 candidates per
-//      tile (refinement in the scan's group-stacked tile, P V with the
-//      candidates' V rows read back transposed from LDS); else 16 lanes per
-//      row with dot2 and V rows streamed as in the dense kernel.
+//      bf16 (r + 128), 16 lanes per row with dot2, V rows streamed as in the
+//      dense kernel; each head's softmax covers only its own candidates.
 //   4. Row slots and waves merge into one partial per query head; the
 //      chunks merge in the common log-sum-exp kernel.
 #include <type_traits>
 
-#include "internal.hpp"
-#include "splitkv.hpp"
+#include "ffd_common.hpp"
 
 namespace fdk {
 
 // load rounds of the scan (positions per lane per round) and rows per slot
 // per batch of the dot-product refine
 constexpr int kScanSteps = 8;
-constexpr int kScanTiles = 8;   // 16-position tiles per round on the matrix cores
 constexpr int kRefineRows = 8;
-typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-typedef short s16x4_t __attribute__((ext_vector_type(4)));
 
 // Dynamic LDS of the FFD kernel for a chunk of `chunk` positions: scan
 // scores [chunk][G] (fp32), candidate masks [chunk] (u8), candidate list
@@ -54,28 +48,6 @@ __host__ __device__ constexpr size_t ffd_lds_list_off(int chunk) {
 template <int G>
 __host__ __device__ constexpr size_t ffd_lds_bytes(int chunk) {
   return ffd_lds_list_off<G>(chunk) + (size_t)chunk * 2;
-}
-
-template <class T>
-__device__ __forceinline__ T ffd_load(const T* p) {
-  return __builtin_nontemporal_load(p);
-}
-
-__device__ __forceinline__ float half_to_float(uint32_t bits16) {
-  return (float)__builtin_bit_cast(_Float16, (uint16_t)bits16);
-}
-
-// bf16 pair (4 + c[2p], 4 + c[2p+1]) from a code word (dims 2p at bits 2p,
-// 2p+1 at bits 16+2p): rotate both 2-bit fields to mantissa bits 5..6 of
-// their half and set the exponent of 4.0 (bf16 0x4080 + c*0x20 = 4 + c).
-__device__ __forceinline__ uint32_t code_pair(uint32_t w, int p) {
-  const uint32_t rot = __builtin_amdgcn_alignbit(w, w, (uint32_t)((2 * p - 5) & 31));
-  return (rot & 0x00600060u) | 0x40804080u;
-}
-
-// bf16 pair from two small integers held exactly in fp32 (low half = a).
-__device__ __forceinline__ uint32_t pack_bf16_exact(float a, float b) {
-  return __builtin_amdgcn_perm(__float_as_uint(b), __float_as_uint(a), 0x07060302u);
 }
 
 // Residual part of the refined dot product for one lane's 8 dims:
@@ -273,54 +245,6 @@ __global__ __launch_bounds__(kThreads) void ffd_anchor_kernel(FfdArgs a) {
 }
 
 
-// Query operand of the group-stacked tiles (d = 128): for tile tt (heads
-// 4*tt .. 4*tt+3), lane (row i = lane % 16, quad g = lane / 16) at k-step t
-// holds q[head 4*tt + i % 4][dims 32g + 8t .. +8] if row i belongs to group
-// g (i / 4 == g), zeros otherwise; qsum[tt][e] = sum of q over group g for
-// head 4*tt + e.  q points at head 0 of the kv-group.
-template <int G>
-__device__ __forceinline__ void stacked_query(const uint16_t* q, int lane, u32x4 (&qa)[G / 4][4],
-                                              float (&qsum)[G / 4][4]) {
-  constexpr int D = 128;
-  const int n16 = lane & 15, qg = lane >> 4;
-#pragma unroll
-  for (int tt = 0; tt < G / 4; ++tt) {
-    const uint16_t* qrow = q + (4 * tt + (n16 & 3)) * D + 32 * qg;
-#pragma unroll
-    for (int t = 0; t < 4; ++t)
-      qa[tt][t] = (n16 >> 2) == qg ? ld16(qrow + 8 * t) : u32x4{0, 0, 0, 0};
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const uint16_t* qh = q + (4 * tt + e) * D + 32 * qg;
-      float sum = 0.f;
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const u32x4 w = ld16(qh + 8 * t);
-        sum += (bf16_lo(w.x) + bf16_hi(w.x)) + (bf16_lo(w.y) + bf16_hi(w.y)) +
-               (bf16_lo(w.z) + bf16_hi(w.z)) + (bf16_lo(w.w) + bf16_hi(w.w));
-      }
-      qsum[tt][e] = sum;
-    }
-  }
-}
-
-__device__ __forceinline__ f32x4 mfma_16x16x32(const u32x4& a, const u32x4& b, f32x4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
-                                                  __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
-}
-
-__device__ __forceinline__ f32x4 mfma_16x16x16(const u32x2& a, const u32x2& b, f32x4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4_t, a),
-                                                    __builtin_bit_cast(s16x4_t, b), c, 0, 0, 0);
-}
-
-// Four residual bytes (dims in byte order) -> two bf16 pairs of r + 128, exact.
-__device__ __forceinline__ u32x2 residual_pairs(uint32_t w) {
-  const uint32_t u = w ^ 0x80808080u;
-  return u32x2{pack_bf16_exact((float)(u & 0xFF), (float)((u >> 8) & 0xFF)),
-               pack_bf16_exact((float)((u >> 16) & 0xFF), (float)(u >> 24))};
-}
-
 template <int D, int G>
 __global__ __launch_bounds__(kThreads) void ffd_kernel(FfdArgs a) {
   using Gm = Geo<uint16_t, D>;
@@ -370,68 +294,7 @@ __global__ __launch_bounds__(kThreads) void ffd_kernel(FfdArgs a) {
   }
 
   // ---- 1. 2-bit scan of the chunk: scores and candidate masks into LDS ----
-  if constexpr (D == 128 && (G == 4 || G == 8)) {
-    // On the matrix cores.  For each 16-row tile of heads 4*tt .. 4*tt+3 the
-    // four quantisation groups are stacked block-diagonally: row i = 4g + e
-    // is (group g, head 4*tt + e), and k-step t of v_mfma_f32_16x16x32_bf16
-    // gives lane quad g the 8 dims 32g + 8t .. +8 of group g.  A = query
-    // (zero outside the row's own group), B = codes of 16 positions as exact
-    // bf16 4 + c, so C[(g, h)][pos] = sum over group g of q_h,i (4 + c_i).
-    // Lane (pos n16, quad g) loads that position's codes and (zero, step) of
-    // group g and receives C for exactly that group: one fma per head gives
-    // the group's part of the score, two shuffles sum the four groups.
-    constexpr int NT = G / 4;
-    constexpr int TB = kScanTiles;            // 16-position tiles per load round
-    const int n16 = lane & 15, qg = lane >> 4;
-    u32x4 qa[NT][4];
-    float qsum[NT][4];
-    stacked_query<G>(a.q + hq0 * D, lane, qa, qsum);
-    for (int p0 = wave * 16 * TB; p0 < n; p0 += kWaves * 16 * TB) {
-      u32x2 cw[TB];
-      uint32_t zz[TB];
-#pragma unroll
-      for (int bt = 0; bt < TB; ++bt) {
-        const int jr = min(p0 + 16 * bt + n16, n - 1);
-        const size_t row = rbase + c0 + jr;
-        cw[bt] = ffd_load(reinterpret_cast<const u32x2*>(codes + row * CW + 2 * qg));
-        zz[bt] = ffd_load(reinterpret_cast<const uint32_t*>(zs + (row * NG + qg) * 2));
-      }
-#pragma unroll
-      for (int bt = 0; bt < TB; ++bt) {
-        const int jr = p0 + 16 * bt + n16;
-        u32x4 bk[4];
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          const uint32_t w = t < 2 ? cw[bt].x : cw[bt].y;
-          const int pb = 4 * (t & 1);
-          bk[t] = u32x4{code_pair(w, pb), code_pair(w, pb + 1), code_pair(w, pb + 2),
-                        code_pair(w, pb + 3)};
-        }
-        const float z = half_to_float(zz[bt] & 0xFFFF), st = half_to_float(zz[bt] >> 16);
-        const float zb = fmaf(-4.f, st, z);
-        uint32_t bits = 0;
-#pragma unroll
-        for (int tt = 0; tt < NT; ++tt) {
-          f32x4 cc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-          for (int t = 0; t < 4; ++t)
-            cc = mfma_16x16x32(qa[tt][t], bk[t], cc);
-          float sc[4];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            sc[e] = fmaf(zb, qsum[tt][e], st * cc[e]);
-            sc[e] = pair_sum<32>(pair_sum<16>(sc[e]));
-            const int h = 4 * tt + e;
-            const bool cand = (sc[e] >= thr[h]) || (c0 + jr == jst[h]);
-            bits |= cand ? (1u << h) : 0u;
-          }
-          if (qg == 0 && jr < n)
-            *reinterpret_cast<f32x4*>(&s_scan[jr][4 * tt]) = f32x4{sc[0], sc[1], sc[2], sc[3]};
-        }
-        if (qg == 0 && jr < n) s_mask[jr] = (uint8_t)bits;
-      }
-    }
-  } else {
+  {
     const int gi = lane % NG, tk = lane / NG;
     u32x4 qs[G][4];
     float qg[G];
@@ -530,208 +393,6 @@ __global__ __launch_bounds__(kThreads) void ffd_kernel(FfdArgs a) {
   }
 
   // ---- 3. refine + exact attention over the candidates ----
-  if constexpr (D == 128 && (G == 4 || G == 8)) {
-    // On the matrix cores, 16 candidates per tile (a wave takes tiles
-    // wave, wave + 4, ...):
-    //   residual: the same group-stacked tile as the scan, B = residual bytes
-    //     as exact bf16 r + 128: C[(g, h)][cand] = sum_g q_h,i (r_i + 128),
-    //     so the refinement is rs_g (C - 128 qsum_h,g), summed over g;
-    //   softmax per head across the tile's 16 lanes (DPP), p in fp32;
-    //   P V: p staged in LDS as [head][candidate] and read back as the A
-    //     operand of v_mfma_f32_16x16x16_bf16 (rows = heads, split bf16
-    //     hi + lo for fp32-level accuracy), V rows through an LDS tile read
-    //     back transposed (ds_read_b64_tr_b16) as the B operand.
-    constexpr int NT = G / 4;
-    constexpr int VSTR = 2 * D + 8;   // LDS row stride of the V tile
-    __shared__ __align__(16) unsigned char s_vt[kWaves][16 * VSTR];
-    __shared__ __align__(16) float s_pb[kWaves][G][16];
-    const int n16 = lane & 15, qg = lane >> 4;
-    u32x4 qa[NT][4];
-    float qsum[NT][4];
-    stacked_query<G>(a.q + hq0 * D, lane, qa, qsum);
-    unsigned char* lv = s_vt[wave];
-    const int tr_off = (4 * qg + (n16 >> 2)) * VSTR + 8 * (n16 & 3);
-    f32x4 o[D / 16];
-#pragma unroll
-    for (int db = 0; db < D / 16; ++db) o[db] = f32x4{0.f, 0.f, 0.f, 0.f};
-    float mh[G], lh[G];   // raw running maximum per head; this lane's part of l
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-      mh[h] = kNegInf;
-      lh[h] = 0.f;
-    }
-    // Loads of a tile go through buffer descriptors of this chunk's residual,
-    // step and V rows.  The next tile's residuals are requested as soon as
-    // the current ones are unpacked and its V rows as soon as the current
-    // ones are in LDS, so a tile's loads travel during the previous tile's
-    // math without extra registers.  Slots past the candidate list (and the
-    // whole tile after a wave's last) get an offset beyond the descriptor's
-    // limit: the load is still issued, so every path has the same loads in
-    // flight and the compiler's wait counts stay exact, but it reads zeros
-    // without touching memory.
-    const __amdgpu_buffer_rsrc_t rs_res = buffer_rsrc(res + (rbase + c0) * D, n * D);
-    const __amdgpu_buffer_rsrc_t rs_rs = buffer_rsrc(rsa + (rbase + c0) * NG, n * NG * 2);
-    const __amdgpu_buffer_rsrc_t rs_v = buffer_rsrc(vb + (size_t)c0 * Gm::kRow, n * Gm::kRow);
-    auto res_issue = [&](int t0, u32x4& r0, u32x4& r1, uint32_t& rsh) {
-      const int jn = t0 + n16;
-      const int jr = s_list[min(jn, nu - 1)];
-      const int off = jn < nu ? jr * D + 32 * qg : n * D;
-      r0 = ld16_buf(rs_res, off);
-      r1 = ld16_buf(rs_res, off + 16);
-      rsh = __builtin_amdgcn_raw_buffer_load_b16(
-          rs_rs, jn < nu ? (jr * NG + qg) * 2 : n * NG * 2, 0, kBufferNonTemporal);
-    };
-    auto v_issue = [&](int t0, u32x4 (&vr)[4]) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int jj = t0 + 4 * i + qg;
-        const int jv = s_list[min(jj, nu - 1)];
-        vr[i] = ld16_buf(rs_v, jj < nu ? jv * Gm::kRow + 16 * n16 : n * Gm::kRow);
-      }
-    };
-    u32x4 r0, r1;
-    uint32_t rsh = 0;
-    u32x4 vr[4];   // V rows of tile slots 4i + qg, 16 bytes at 16 * n16
-    if (wave * 16 < nu) {
-      res_issue(wave * 16, r0, r1, rsh);
-      v_issue(wave * 16, vr);
-    }
-    for (int t0 = wave * 16; t0 < nu; t0 += kWaves * 16) {
-      const int jn = t0 + n16;                      // this lane's candidate slot
-      const int jr = s_list[min(jn, nu - 1)];
-      const float rsf = half_to_float(rsh);
-      const uint32_t mk = s_mask[jr];
-      const bool valid = jn < nu;
-      u32x4 bk[4];
-      {
-        const uint32_t w[8] = {r0.x, r0.y, r0.z, r0.w, r1.x, r1.y, r1.z, r1.w};
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          const u32x2 lo = residual_pairs(w[2 * t]), hi = residual_pairs(w[2 * t + 1]);
-          bk[t] = u32x4{lo.x, lo.y, hi.x, hi.y};
-        }
-      }
-      res_issue(t0 + kWaves * 16, r0, r1, rsh);
-      float sh[G];   // refined raw scores of this lane's candidate
-#pragma unroll
-      for (int tt = 0; tt < NT; ++tt) {
-        f32x4 cc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int t = 0; t < 4; ++t) cc = mfma_16x16x32(qa[tt][t], bk[t], cc);
-        const f32x4 sv = *reinterpret_cast<const f32x4*>(&s_scan[jr][4 * tt]);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          float corr = rsf * fmaf(-128.f, qsum[tt][e], cc[e]);
-          corr = pair_sum<32>(pair_sum<16>(corr));
-          const int h = 4 * tt + e;
-          sh[h] = (valid && ((mk >> h) & 1u)) ? sv[e] + corr : kNegInf;
-        }
-      }
-      // online softmax per head over the tile (all lanes of a 16-lane row
-      // hold the same candidate set, every quad the same values)
-      bool grow = false;
-      float alpha[G];
-#pragma unroll
-      for (int h = 0; h < G; ++h) {
-        const float mn = fmaxf(mh[h], group_max<16>(sh[h]));
-        alpha[h] = (mn == mh[h]) ? 1.f : exp2_hw((mh[h] - mn) * a.c_log2);
-        grow |= mn > mh[h];
-        mh[h] = mn;
-      }
-      if (__any(grow)) {
-#pragma unroll
-        for (int h = 0; h < G; ++h) lh[h] *= alpha[h];
-        // O row 4*qg + e is head 4*qg + e (rows >= G are padding)
-        float ae[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          ae[e] = 1.f;
-#pragma unroll
-          for (int h = e; h < G; h += 4) ae[e] = (h == 4 * qg + e) ? alpha[h] : ae[e];
-        }
-#pragma unroll
-        for (int db = 0; db < D / 16; ++db)
-#pragma unroll
-          for (int e = 0; e < 4; ++e) o[db][e] *= ae[e];
-      }
-      float* pb = &s_pb[wave][0][0];
-#pragma unroll
-      for (int h = 0; h < G; ++h) {
-        // exponent (s - m) c: exactly 0, p exactly 1, at the running maximum
-        const float base = (mh[h] == kNegInf) ? 0.f : mh[h];
-        const float p = exp2_hw((sh[h] - base) * a.c_log2);
-        lh[h] += p;
-        if ((h & 3) == qg) pb[h * 16 + n16] = p;
-      }
-      // A operand: lane (head row n16, quad q) takes p[n16][4q .. 4q+3]
-      u32x2 ph = {0u, 0u}, pl = {0u, 0u};
-      if (n16 < G) {
-        const f32x4 pv = *reinterpret_cast<const f32x4*>(pb + n16 * 16 + 4 * qg);
-        // hi = bf16(p), lo = bf16(p - hi), rounded to nearest even by the
-        // hardware conversion (two values per instruction)
-        uint32_t hb[2], lb[2];
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          const float x0 = pv[2 * j], x1 = pv[2 * j + 1];
-          hb[j] = __builtin_bit_cast(uint32_t, bf16x2_t{(__bf16)x0, (__bf16)x1});
-          lb[j] = __builtin_bit_cast(
-              uint32_t, bf16x2_t{(__bf16)(x0 - __uint_as_float(hb[j] << 16)),
-                                 (__bf16)(x1 - __uint_as_float(hb[j] & 0xFFFF0000u))});
-        }
-        ph = u32x2{hb[0], hb[1]};
-        pl = u32x2{lb[0], lb[1]};
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        *reinterpret_cast<u32x4*>(lv + (4 * i + qg) * VSTR + 16 * n16) = vr[i];
-      v_issue(t0 + kWaves * 16, vr);
-#pragma unroll
-      for (int db = 0; db < D / 16; ++db) {
-        const u32x2 vv = __builtin_bit_cast(
-            u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                       (__attribute__((address_space(3))) s16x4_t*)(lv + tr_off + 32 * db)));
-        o[db] = mfma_16x16x16(ph, vv, o[db]);
-        o[db] = mfma_16x16x16(pl, vv, o[db]);
-      }
-    }
-    // ---- 4. waves merge into one partial per query head ----
-#pragma unroll
-    for (int h = 0; h < G; ++h) lh[h] = group_sum<16>(lh[h]);
-#pragma unroll
-    for (int db = 0; db < D / 16; ++db)
-#pragma unroll
-      for (int e = 0; e < 4; ++e)
-        if (4 * qg + e < G) s_cmb.acc[wave][4 * qg + e][16 * db + n16] = o[db][e];
-    if (lane == 0) {
-#pragma unroll
-      for (int h = 0; h < G; ++h) {
-        s_cmb.ml[wave][h][0] = (mh[h] == kNegInf) ? kNegInf : mh[h] * a.c_log2;
-        s_cmb.ml[wave][h][1] = lh[h];
-      }
-    }
-    __syncthreads();
-    const size_t prow0 = hq0 * a.nc + c;
-    for (int idx = tid; idx < G * D; idx += kThreads) {
-      const int h = idx / D, dd = idx % D;
-      float M = kNegInf;
-#pragma unroll
-      for (int w = 0; w < kWaves; ++w) M = fmaxf(M, s_cmb.ml[w][h][0]);
-      float ov = 0.f, ls = 0.f;
-#pragma unroll
-      for (int w = 0; w < kWaves; ++w) {
-        const float wt = exp2_diff(s_cmb.ml[w][h][0], M);
-        ov = fmaf(wt, s_cmb.acc[w][h][dd], ov);
-        ls = fmaf(wt, s_cmb.ml[w][h][1], ls);
-      }
-      const size_t prow = prow0 + (size_t)h * a.nc;
-      a.o_part[prow * D + dd] = ov;
-      if (dd == 0) {
-        a.ml_part[prow * 2] = M;
-        a.ml_part[prow * 2 + 1] = ls;
-      }
-    }
-    return;
-  }
   float acc[G][VEC], m[G], l[G];
   state_reset<G, VEC>(acc, m, l);
   const int per = (((nu + kWaves - 1) / kWaves) + TPL - 1) / TPL * TPL;
@@ -843,20 +504,34 @@ __global__ __launch_bounds__(kThreads) void ffd_pack_kernel(FfdPackArgs a) {
   a.rs[row * NG + gi] = __builtin_bit_cast(uint16_t, rs16);
 }
 
-hipError_t launch_ffd(int D, int G, const FfdArgs& a, hipStream_t s) {
-  const dim3 grid((unsigned)((size_t)a.B * a.Hkv * a.nc)), block(kThreads);
-#define FD_FFD_CASE(DD, GG)                                                          \
-  if (D == DD && G == GG) {                                                          \
-    hipLaunchKernelGGL((ffd_anchor_kernel<DD, GG>), dim3((unsigned)(a.B * a.Hkv)), block, 0, \
-                       s, a);                                                        \
-    hipError_t e = hipGetLastError();                                                \
-    if (e != hipSuccess) return e;                                                   \
-    hipLaunchKernelGGL((ffd_kernel<DD, GG>), grid, block, ffd_lds_bytes<GG>(a.chunk), s, a); \
-    return hipGetLastError();                                                        \
+// Anchors, then the kernel of the shape: d = 128 with G = 4 or 8 runs the
+// wave-streamed kernel of ffd_wave.hip, every other shape ffd_kernel.
+template <int D, int G>
+static hipError_t launch_ffd_dg(const FfdArgs& a, hipStream_t s) {
+  const dim3 block(kThreads);
+  hipLaunchKernelGGL((ffd_anchor_kernel<D, G>), dim3((unsigned)(a.B * a.Hkv)), block, 0, s, a);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if constexpr (D == 128 && (G == 4 || G == 8)) {
+    return launch_ffd_wave(G, a, s);
+  } else {
+    const dim3 grid((unsigned)((size_t)a.B * a.Hkv * a.nc));
+    hipLaunchKernelGGL((ffd_kernel<D, G>), grid, block, ffd_lds_bytes<G>(a.chunk), s, a);
+    return hipGetLastError();
   }
-  FD_FFD_CASE(64, 1) FD_FFD_CASE(64, 2) FD_FFD_CASE(64, 4) FD_FFD_CASE(64, 8)
-  FD_FFD_CASE(128, 1) FD_FFD_CASE(128, 2) FD_FFD_CASE(128, 4) FD_FFD_CASE(128, 8)
-#undef FD_FFD_CASE
+}
+
+hipError_t launch_ffd(int D, int G, const FfdArgs& a, hipStream_t s) {
+  switch (D * 16 + G) {
+    case 64 * 16 + 1: return launch_ffd_dg<64, 1>(a, s);
+    case 64 * 16 + 2: return launch_ffd_dg<64, 2>(a, s);
+    case 64 * 16 + 4: return launch_ffd_dg<64, 4>(a, s);
+    case 64 * 16 + 8: return launch_ffd_dg<64, 8>(a, s);
+    case 128 * 16 + 1: return launch_ffd_dg<128, 1>(a, s);
+    case 128 * 16 + 2: return launch_ffd_dg<128, 2>(a, s);
+    case 128 * 16 + 4: return launch_ffd_dg<128, 4>(a, s);
+    case 128 * 16 + 8: return launch_ffd_dg<128, 8>(a, s);
+  }
   return hipErrorInvalidValue;
 }
 

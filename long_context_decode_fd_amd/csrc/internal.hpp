@@ -69,6 +69,8 @@ struct FfdArgs {
   float scale, c_log2, delta_raw;  // delta / scale
 };
 hipError_t launch_ffd(int D, int G, const FfdArgs& a, hipStream_t s);
+// the wave-streamed FFD kernel (d = 128, G = 4 or 8), after the anchors
+hipError_t launch_ffd_wave(int G, const FfdArgs& a, hipStream_t s);
 
 // Multi-row decode: q [B, M, Hq, D] bf16, k/v [B, Hkv, L, D] bf16, partials
 // for the rows (b, r, h) in the same layout as PartialArgs with M*Hq heads.
