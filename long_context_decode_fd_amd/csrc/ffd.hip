@@ -4,13 +4,14 @@
 // the candidates and exact attention over them (sections 3-6, Fig. 2), plus
 // the packer that produces the key format (section 5).
 //
-//   0. Anchors (every shape).  ffd_anchor_kernel scores the anchor positions
-//      of every (sequence, kv-head) with the refined key (2-bit + residual)
-//      once and leaves m^ and j* per query head in the workspace.
-//   1-4. At d = 128 with G = 4 or 8 the wave-streamed kernel of ffd_wave.hip
-//      (matrix cores, one wavefront per chunk) does the rest.  Every other
-//      shape runs ffd_kernel below, one workgroup per unit = (sequence,
-//      kv-head, chunk), fused:
+// At d = 128 with G = 4 or 8 the wave-streamed kernel of ffd_wave.hip
+// (matrix cores, one wavefront per chunk, anchors included) does all of it.
+// Every other shape runs the two kernels below:
+//   0. Anchors.  ffd_anchor_kernel scores the anchor positions of every
+//      (sequence, kv-head) with the refined key (2-bit + residual) once and
+//      leaves m^ and j* per query head in the workspace.
+//   1-4. ffd_kernel, one workgroup per unit = (sequence, kv-head, chunk),
+//      fused:
 //   1. Scan.  4 lanes per position (one 32-dim quantisation group each) read
 //      8 B of codes and 4 B of (zero, step).  Codes become exact bf16 values
 //      4 + c (a rotate and an and-or per pair, since bf16 4..7 differ only in
@@ -504,17 +505,18 @@ __global__ __launch_bounds__(kThreads) void ffd_pack_kernel(FfdPackArgs a) {
   a.rs[row * NG + gi] = __builtin_bit_cast(uint16_t, rs16);
 }
 
-// Anchors, then the kernel of the shape: d = 128 with G = 4 or 8 runs the
-// wave-streamed kernel of ffd_wave.hip, every other shape ffd_kernel.
+// d = 128 with G = 4 or 8 runs the wave-streamed kernel of ffd_wave.hip
+// (which scores the anchors itself); every other shape the anchor kernel,
+// then ffd_kernel.
 template <int D, int G>
 static hipError_t launch_ffd_dg(const FfdArgs& a, hipStream_t s) {
-  const dim3 block(kThreads);
-  hipLaunchKernelGGL((ffd_anchor_kernel<D, G>), dim3((unsigned)(a.B * a.Hkv)), block, 0, s, a);
-  const hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
   if constexpr (D == 128 && (G == 4 || G == 8)) {
     return launch_ffd_wave(G, a, s);
   } else {
+    const dim3 block(kThreads);
+    hipLaunchKernelGGL((ffd_anchor_kernel<D, G>), dim3((unsigned)(a.B * a.Hkv)), block, 0, s, a);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
     const dim3 grid((unsigned)((size_t)a.B * a.Hkv * a.nc));
     hipLaunchKernelGGL((ffd_kernel<D, G>), grid, block, ffd_lds_bytes<G>(a.chunk), s, a);
     return hipGetLastError();

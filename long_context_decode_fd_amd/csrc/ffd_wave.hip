@@ -2,11 +2,13 @@
 // the 2-bit scan, top-delta selection, 8-bit refine and exact attention of
 // the "Faster Than Flash" digest (longzhangge.com, sections 3, 5 and 6,
 // Fig. 2) for one chunk per wavefront, fused, with no barrier and no
-// intermediate written to memory.  The pseudo-maximum m^ and its anchor j*
-// (section 4) come from ffd_anchor_kernel (ffd.hip).
+// intermediate written to memory, the pseudo-maximum m^ and its anchor j*
+// (section 4) included.
 //
-// A wavefront owns one unit = (sequence, kv-head, chunk) and walks it in
-// steps of kStep positions:
+// A wavefront owns one unit = (sequence, kv-head, chunk).  It first scores
+// the anchor positions (the first n_sink and the last n_local positions of
+// its sequence) with the refined keys, as below, for m^ and j*, then walks
+// its chunk in steps of kStep positions:
 //   * Scan.  Codes and (zero, step) of a step's 8 tiles of 16 positions come
 //     through buffer loads (one lane offset plus an immediate per tile).
 //     Codes become exact bf16 values 4 + c; v_mfma_f32_16x16x32_bf16 with the
@@ -89,7 +91,9 @@ struct PairRegs {
   u32x4 v[2][4];
 };
 
-template <int G>
+// MASK: the candidate bitmask output is requested (a separate instantiation,
+// so that the hot loop carries no mask code otherwise).
+template <int G, bool MASK>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
 void ffd_wave_kernel(FfdArgs a) {
   constexpr int D = 128, NG = D / 32, CW = D / 16, NT = G / 4;
@@ -115,19 +119,69 @@ void ffd_wave_kernel(FfdArgs a) {
   u32x4 qa[NT][4];
   float qsum[NT][4];
   stacked_query<G>(a.q + hq0 * D, lane, qa, qsum);
-  // this lane's heads 4 tt + qg: threshold m^ - delta and j* (within the chunk)
+  // this lane's heads 4 tt + qg: threshold m^ - delta and j* (within the
+  // chunk), set from the anchors below
   float thr[NT];
   int jst[NT];
-#pragma unroll
-  for (int tt = 0; tt < NT; ++tt) {
-    thr[tt] = a.anchor_max[hq0 + 4 * tt + qg] - a.delta_raw;
-    jst[tt] = a.anchor_pos[hq0 + 4 * tt + qg] - c0;
-  }
   // constants of the code -> bf16 conversion, held in registers so that one
   // v_and_or_b32 applies both (its encoding takes no literal)
   uint32_t k_mask = 0x00600060u, k_exp = 0x40804080u;
   asm volatile("" : "+s"(k_mask));
   asm volatile("" : "+v"(k_exp));
+
+  // ---- operands and dot products shared by the anchors, the scan and the
+  // refine.  Codes of a (position, group): the bf16 pairs 4 + c of k-steps
+  // 0 .. 3; (zero, step): the group's part of the 2-bit score of head
+  // 4 tt + qg after the transposed reduction ----
+  auto code_operands = [&](const u32x2& cwv, u32x4 (&bq)[4]) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const uint32_t w = k < 2 ? cwv.x : cwv.y;
+      const int pbit = 4 * (k & 1);
+      uint32_t pr[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        pr[j] = (__builtin_amdgcn_alignbit(w, w, (uint32_t)((2 * (pbit + j) - 5) & 31)) &
+                 k_mask) | k_exp;
+      bq[k] = u32x4{pr[0], pr[1], pr[2], pr[3]};
+    }
+  };
+  auto scan_scores = [&](const u32x4 (&bq)[4], uint32_t zzv, float (&sc)[NT]) {
+    const float z = half_to_float(zzv & 0xFFFF), st = half_to_float(zzv >> 16);
+    const float zb = fmaf(-4.f, st, z);
+#pragma unroll
+    for (int tt = 0; tt < NT; ++tt) {
+      f32x4 cc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int k = 0; k < 4; ++k) cc = mfma_16x16x32(qa[tt][k], bq[k], cc);
+      float part[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) part[e] = fmaf(zb, qsum[tt][e], st * cc[e]);
+      sc[tt] = quad_transpose_sum(part);
+    }
+  };
+  // residual bytes of a (position, group) as exact bf16 r + 128, and the
+  // refinement rs_g (sum q (r + 128) - 128 qsum) summed over the groups
+  auto residual_operands = [&](const u32x4& ra, const u32x4& rb, u32x4 (&bq)[4]) {
+    const uint32_t w[8] = {ra.x, ra.y, ra.z, ra.w, rb.x, rb.y, rb.z, rb.w};
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const u32x2 lo = residual_pairs(w[2 * t]), hi = residual_pairs(w[2 * t + 1]);
+      bq[t] = u32x4{lo.x, lo.y, hi.x, hi.y};
+    }
+  };
+  auto refinement = [&](const u32x4 (&bq)[4], float rsf, float (&corr)[NT]) {
+#pragma unroll
+    for (int tt = 0; tt < NT; ++tt) {
+      f32x4 cc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int t = 0; t < 4; ++t) cc = mfma_16x16x32(qa[tt][t], bq[t], cc);
+      float part[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) part[e] = rsf * fmaf(-128.f, qsum[tt][e], cc[e]);
+      corr[tt] = quad_transpose_sum(part);
+    }
+  };
 
   // ---- buffer descriptors of the chunk ----
   const char* codes_c = reinterpret_cast<const char*>(a.codes + rbase * CW);
@@ -139,7 +193,7 @@ void ffd_wave_kernel(FfdArgs a) {
   // ---- scan loads of step s (positions s kStep ..), no memory access for
   // positions at or past n ----
   const int lane_c = n16 * (CW * 4) + 8 * qg, lane_z = n16 * (NG * 4) + 4 * qg;
-  auto scan_issue = [&](ScanRegs<kTiles>& R, int s) {
+  auto scan_issue = [&](ScanRegs<kTiles>& R, int s) __attribute__((always_inline)) {
     const int p0 = s * kStep, cnt = max(0, min(n - p0, kStep));
     const __amdgpu_buffer_rsrc_t rc =
         buffer_rsrc(codes_c + (size_t)min(p0, n) * (CW * 4), cnt * CW * 4);
@@ -164,7 +218,7 @@ void ffd_wave_kernel(FfdArgs a) {
   constexpr int kOob = 1 << 30;
   float* const sc_w = &s_sc[wave][0][0];
   int* const pos_w = s_pos[wave];
-  auto res_issue = [&](PairRegs& P, int t0, int lim) {
+  auto res_issue = [&](PairRegs& P, int t0, int lim) __attribute__((always_inline)) {
     int jr[2], oob[2];
 #pragma unroll
     for (int k = 0; k < 2; ++k) {
@@ -181,7 +235,7 @@ void ffd_wave_kernel(FfdArgs a) {
                                                      kBufferNonTemporal);
     }
   };
-  auto v_issue = [&](PairRegs& P, int t0, int lim) {
+  auto v_issue = [&](PairRegs& P, int t0, int lim) __attribute__((always_inline)) {
     int off[2][4];
 #pragma unroll
     for (int k = 0; k < 2; ++k)
@@ -216,32 +270,20 @@ void ffd_wave_kernel(FfdArgs a) {
   // One refine pair: entries t0 .. t0 + 31 valid below lim, loads in P.
   // Issues the loads of the next pair (at nx, valid below nlim) into P as
   // soon as each part of P is consumed.
-  auto refine_pair = [&](PairRegs& P, int t0, int lim, int nx, int nlim) {
+  auto refine_pair = [&](PairRegs& P, int t0, int lim, int nx, int nlim) __attribute__((always_inline)) {
     float sh[2][NT];   // refined raw score of this lane's entries for head 4 tt + qg
 #pragma unroll
     for (int k = 0; k < 2; ++k) {
-      const float rsf = half_to_float(P.rs[k]);
       u32x4 bq[4];
-      const uint32_t w[8] = {P.r0[k].x, P.r0[k].y, P.r0[k].z, P.r0[k].w,
-                             P.r1[k].x, P.r1[k].y, P.r1[k].z, P.r1[k].w};
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const u32x2 lo = residual_pairs(w[2 * t]), hi = residual_pairs(w[2 * t + 1]);
-        bq[t] = u32x4{lo.x, lo.y, hi.x, hi.y};
-      }
+      residual_operands(P.r0[k], P.r1[k], bq);
+      float corr[NT];
+      refinement(bq, half_to_float(P.rs[k]), corr);
       const int jn = t0 + 16 * k + n16;
       const int idx = jn & (kRing - 1);
 #pragma unroll
       for (int tt = 0; tt < NT; ++tt) {
-        f32x4 cc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int t = 0; t < 4; ++t) cc = mfma_16x16x32(qa[tt][t], bq[t], cc);
-        float part[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) part[e] = rsf * fmaf(-128.f, qsum[tt][e], cc[e]);
-        const float corr = quad_transpose_sum(part);
         const float sv = sc_w[idx * G + 4 * tt + qg];
-        sh[k][tt] = jn < lim ? sv + corr : kNegInf;
+        sh[k][tt] = jn < lim ? sv + corr[tt] : kNegInf;
       }
     }
     res_issue(P, nx, nlim);
@@ -330,39 +372,21 @@ void ffd_wave_kernel(FfdArgs a) {
   const size_t mask_words = ((size_t)a.L + 31) / 32;
   const uint32_t below = (1u << n16) - 1u;   // positions of the tile before this lane's
   int tail = 0;                              // ring entries written so far (wave-uniform)
-  auto scan_step = [&](const ScanRegs<kTiles>& R, int s) {
+  auto scan_step = [&](const ScanRegs<kTiles>& R, int s) __attribute__((always_inline)) {
 #pragma unroll
     for (int t = 0; t < kTiles; ++t) {
       const int p0 = s * kStep + 16 * t;   // wave-uniform
       if (p0 >= n) break;
       const int jr = p0 + n16;
       u32x4 bq[4];
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const uint32_t w = k < 2 ? R.cw[t].x : R.cw[t].y;
-        const int pbit = 4 * (k & 1);
-        uint32_t pr[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          pr[j] = (__builtin_amdgcn_alignbit(w, w, (uint32_t)((2 * (pbit + j) - 5) & 31)) &
-                   k_mask) | k_exp;
-        bq[k] = u32x4{pr[0], pr[1], pr[2], pr[3]};
-      }
-      const float z = half_to_float(R.zz[t] & 0xFFFF), st = half_to_float(R.zz[t] >> 16);
-      const float zb = fmaf(-4.f, st, z);
+      code_operands(R.cw[t], bq);
       float sc[NT];
+      scan_scores(bq, R.zz[t], sc);
       bool sel[NT];
       uint64_t bal[NT];
       uint32_t uni = 0;   // positions of the tile selected by any head (wave-uniform)
 #pragma unroll
       for (int tt = 0; tt < NT; ++tt) {
-        f32x4 cc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int k = 0; k < 4; ++k) cc = mfma_16x16x32(qa[tt][k], bq[k], cc);
-        float part[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) part[e] = fmaf(zb, qsum[tt][e], st * cc[e]);
-        sc[tt] = quad_transpose_sum(part);
         sel[tt] = (jr < n) & ((sc[tt] >= thr[tt]) | (jr == jst[tt]));
         bal[tt] = __ballot(sel[tt]);
         const uint64_t f = bal[tt] | (bal[tt] >> 32);
@@ -377,7 +401,7 @@ void ffd_wave_kernel(FfdArgs a) {
         }
         tail += __builtin_popcount(uni);
       }
-      if (a.cand_mask != nullptr && lane < G) {
+      if (MASK && lane < G) {
         // 16 bits per head and tile; chunks start at multiples of 32, so
         // tile t of the chunk is half-word c0 / 16 + s * kTiles + t of the row
         const uint64_t bb = (NT == 2 && lane >= 4) ? bal[NT - 1] : bal[0];
@@ -399,9 +423,91 @@ void ffd_wave_kernel(FfdArgs a) {
   int head = 0, plim = 0;
   scan_issue(sA, 0);
   scan_issue(sB, 1);
-  res_issue(P, 0, 0);
+
+  // ---- pseudo-maximum (FFD digest, section 4), while the first two scan
+  // steps' loads travel: the refined scores of the anchor positions -- the
+  // first n_sink and the last n_local positions, a set -- for this lane's
+  // heads, computed as in the scan and the refine; m^ = their maximum and
+  // j* the lowest position attaining it.  Every wave of a (sequence,
+  // kv-head) reads the same anchor rows (cache-resident after the first)
+  // and computes the same values.  The next tile's rows are loaded before
+  // the current tile's products ----
+  {
+    const int n_sk = min(a.n_sink, a.L), loc0 = max(n_sk, a.L - a.n_local);
+    const int na = n_sk + (a.L - loc0);
+    const size_t row0 = rbase - c0;   // row of position 0
+    float mbest[NT];
+    int jbest[NT];
+#pragma unroll
+    for (int tt = 0; tt < NT; ++tt) {
+      mbest[tt] = kNegInf;
+      jbest[tt] = 0x7fffffff;
+    }
+    struct AnchorRows {
+      u32x2 cw;
+      uint32_t zz;
+      u32x4 ra, rb;
+      uint32_t rs;
+      int pos;
+    };
+    auto anchor_load = [&](int k0, AnchorRows& A) __attribute__((always_inline)) {
+      const int k = min(k0 + n16, na - 1);
+      A.pos = k < n_sk ? k : loc0 + (k - n_sk);
+      const size_t row = row0 + A.pos;
+      A.cw = *reinterpret_cast<const u32x2*>(a.codes + row * CW + 2 * qg);
+      A.zz = *reinterpret_cast<const uint32_t*>(a.zs + (row * NG + qg) * 2);
+      A.ra = ld16(a.res + row * D + 32 * qg);
+      A.rb = ld16(a.res + row * D + 32 * qg + 16);
+      A.rs = a.rs[row * NG + qg];
+    };
+    AnchorRows cur, nxt;
+    anchor_load(0, cur);
+    for (int k0 = 0; k0 < na; k0 += 16) {   // wave-uniform
+      anchor_load(min(k0 + 16, na - 1), nxt);
+      u32x4 bq[4];
+      code_operands(cur.cw, bq);
+      float sc[NT], corr[NT];
+      scan_scores(bq, cur.zz, sc);
+      residual_operands(cur.ra, cur.rb, bq);
+      refinement(bq, half_to_float(cur.rs), corr);
+      const bool valid = k0 + n16 < na;
+#pragma unroll
+      for (int tt = 0; tt < NT; ++tt) {
+        const float sh = sc[tt] + corr[tt];
+        if (valid && (sh > mbest[tt] || (sh == mbest[tt] && cur.pos < jbest[tt]))) {
+          mbest[tt] = sh;
+          jbest[tt] = cur.pos;
+        }
+      }
+      cur = nxt;
+    }
+    // (largest score, then lowest position) over the 16 lanes of a quad;
+    // the order is total, so every lane ends with the same pair
+#pragma unroll
+    for (int off = 1; off < 16; off <<= 1) {
+#pragma unroll
+      for (int tt = 0; tt < NT; ++tt) {
+        const float ob = __shfl_xor(mbest[tt], off);
+        const int oj = __shfl_xor(jbest[tt], off);
+        if (ob > mbest[tt] || (ob == mbest[tt] && oj < jbest[tt])) {
+          mbest[tt] = ob;
+          jbest[tt] = oj;
+        }
+      }
+    }
+#pragma unroll
+    for (int tt = 0; tt < NT; ++tt) {
+      thr[tt] = mbest[tt] - a.delta_raw;
+      jst[tt] = jbest[tt] - c0;
+      if (a.pseudo_max != nullptr && c == 0 && n16 == 0)
+        a.pseudo_max[hq0 + 4 * tt + qg] = mbest[tt] * a.scale;
+    }
+  }
+
+  res_issue(P, 0, 0);   // an empty pair: its loads read nothing
   v_issue(P, 0, 0);
-  auto refine_until = [&](int mark) {
+
+  auto refine_until = [&](int mark) __attribute__((always_inline)) {
     while (head < mark) {   // wave-uniform
       const int nx = min(head + 32, plim);
       refine_pair(P, head, plim, nx, tail);
@@ -470,8 +576,11 @@ void ffd_wave_kernel(FfdArgs a) {
 hipError_t launch_ffd_wave(int G, const FfdArgs& a, hipStream_t s) {
   const size_t units = (size_t)a.B * a.Hkv * a.nc;
   const dim3 grid((unsigned)((units + kWaves - 1) / kWaves)), block(kThreads);
-  if (G == 4) hipLaunchKernelGGL((ffd_wave_kernel<4>), grid, block, 0, s, a);
-  else if (G == 8) hipLaunchKernelGGL((ffd_wave_kernel<8>), grid, block, 0, s, a);
+  const bool mask = a.cand_mask != nullptr;
+  if (G == 4 && mask) hipLaunchKernelGGL((ffd_wave_kernel<4, true>), grid, block, 0, s, a);
+  else if (G == 4) hipLaunchKernelGGL((ffd_wave_kernel<4, false>), grid, block, 0, s, a);
+  else if (G == 8 && mask) hipLaunchKernelGGL((ffd_wave_kernel<8, true>), grid, block, 0, s, a);
+  else if (G == 8) hipLaunchKernelGGL((ffd_wave_kernel<8, false>), grid, block, 0, s, a);
   else return hipErrorInvalidValue;
   return hipGetLastError();
 }
