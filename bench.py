@@ -37,10 +37,21 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 PEAK_GBS = 8000.0       # MI355X HBM3E peak, GB/s
-VARIANTS = ("dense_128k", "paged", "unified_max", "ffd", "ffd_peaked", "multi_row", "append")
+VARIANTS = ("config1", "dense_128k", "paged", "unified_max", "ffd", "ffd_peaked", "multi_row",
+            "append")
 METRIC = "us/decode step and achieved KV-read HBM GB/s (% of peak) at 32K-128K ctx"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_partial_dense_b8_h32x8_d128_l32768.txt")
-KERNEL_SOURCES = ["attn.hip", "splitkv.hpp", "common.hpp"]
+# everything that decides the partial kernel's code: its sources, the
+# launch path and the compiler flags
+KERNEL_SOURCES = ["long_context_decode_fd_amd/csrc/attn.hip",
+                  "long_context_decode_fd_amd/csrc/splitkv.hpp",
+                  "long_context_decode_fd_amd/csrc/common.hpp",
+                  "long_context_decode_fd_amd/csrc/internal.hpp",
+                  "long_context_decode_fd_amd/csrc/api.hip",
+                  "long_context_decode_fd_amd/build.py"]
+# (name, function) pairs filled by the timed legs: each function compares a
+# sample of that leg's GPU output with the oracle (run in the CPU leg)
+PARITY_SAMPLES = []
 
 
 def parse_args():
@@ -66,7 +77,7 @@ def parse_args():
 def kernel_source_hash() -> str:
     h = hashlib.sha256()
     for name in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, "long_context_decode_fd_amd", "csrc", name), "rb") as f:
+        with open(os.path.join(ROOT, name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
 
@@ -182,6 +193,10 @@ def dense_headline(torch, fd, W, args, timer):
     t_full = timer.run(full, args.steps, args.warmup)
     t_part = timer.run(part, args.steps, args.warmup)
 
+    check_rc(lib, full[0]())
+    sample_rows(torch, "config2 dense GQA bf16 (sequence 0, all 32 heads)", case.q[:1], case.k[:1],
+                case.v[:1], out[:1], lse[:1], case.scale)
+
     kv_bytes = 2 * B * Hkv * L * d * 2
     q_bytes = B * Hq * d * 2
     out_bytes = B * Hq * d * 4 + B * Hq * 4
@@ -194,6 +209,71 @@ def dense_headline(torch, fd, W, args, timer):
         workload=dict(workload="dense GQA decode, contiguous bf16 KV cache", B=B, Hq=Hq,
                       Hkv=Hkv, head_dim=d, kv_len=L, chunk=chunk, n_chunks=L // chunk,
                       scale="1/sqrt(128)", kv_copies_rotated=args.copies))
+
+
+def _host(t):
+    """Exact host copy (bf16 stays bf16, fp32 stays fp32)."""
+    return t.detach().to("cpu").clone()
+
+
+def sample_rows(torch, name, q, k, v, out, lse, scale, tol=2e-3):
+    """Register a dense-definition parity sample: q [b, Hq, d], k/v [b, Hkv,
+    L, d] and the GPU's out/lse for those rows, copied to the host now."""
+    q, k, v, o, l_ = _host(q), _host(k), _host(v), _host(out), _host(lse)
+
+    def check():
+        import numpy as np
+        from oracle import flash_decoding as ofd
+        f = lambda t: t.to(torch.float64).numpy()  # noqa: E731
+        ref, lref = ofd.dense_attention(f(q), f(k), f(v), scale)
+        return _errs(np, f(o), f(l_), ref, lref, tol, q.shape[0] * q.shape[1])
+    PARITY_SAMPLES.append((name, check))
+
+
+def _errs(np, o, l_, ref, lref, tol, rows):
+    eo = float(np.abs(o - ref).max())
+    el = float(np.abs(l_ - lref).max())
+    return dict(rows=int(rows), max_abs_err_out=eo, max_abs_err_lse=el, tol=tol,
+                within_tol=bool(eo <= tol and el <= tol))
+
+
+def variant_config1(torch, fd, W, args, timer):
+    """Dense MHA fp32 (B 1, H 8, d 64, L 4096, chunk 1024: 4 chunks of 1024):
+    16 MiB of K/V per copy, so it is timed twice: rotating 64 copies (1 GiB,
+    every call reads from HBM) and on one copy (cache-resident after the
+    first call).  A call this small is bound by launch latency."""
+    c = W.config_case(1, device="cuda:0")
+    B, Hq, d = c.q.shape
+    Hkv, L = c.k.shape[1], c.k.shape[2]
+    copies = 64
+    ks = [c.k] + [c.k.clone() for _ in range(copies - 1)]
+    vs = [c.v] + [c.v.clone() for _ in range(copies - 1)]
+    lib = fd.lib()
+    out = torch.empty((B, Hq, d), dtype=torch.float32, device="cuda:0")
+    lse = torch.empty((B, Hq), dtype=torch.float32, device="cuda:0")
+    wsn = fd.workspace_bytes("fd_decode_attn", dt=fd.FD_F32, B=B, Hq=Hq, Hkv=Hkv, L=L, d=d,
+                             chunk=c.chunk)
+    ws = torch.empty(wsn, dtype=torch.uint8, device="cuda:0")
+    size = C.c_size_t(wsn)
+    st = C.c_void_p(torch.cuda.current_stream().cuda_stream)
+    calls = []
+    for k, v in zip(ks, vs):
+        a = (fd.FD_F32, vp(c.q), vp(k), vp(v), vp(out), vp(lse), B, Hq, Hkv, L, d, c.scale,
+             c.chunk, vp(ws), C.byref(size), st)
+        calls.append(lambda a=a: lib.fd_decode_attn(*a))
+    check_rc(lib, calls[0]())
+    sample_rows(torch, "config1 dense MHA fp32 (all 8 heads)", c.q, c.k, c.v, out, lse, c.scale,
+                tol=1e-5)
+    t = interleaved(timer, {"cold": calls, "warm": calls[:1]}, args.steps, args.warmup)
+    nbytes = 2 * B * Hkv * L * d * 4 + B * Hq * d * 4 + B * Hq * (d + 1) * 4
+    res = dict(workload=f"dense MHA decode fp32, B={B}, H={Hq}, d={d}, L={L}, chunk={c.chunk}",
+               bytes=nbytes)
+    for key, note in (("cold", f"{copies} rotated K/V copies (1 GiB): HBM reads"),
+                      ("warm", "one K/V copy: cache-resident after the first call")):
+        res[key] = dict(us_per_step=round(t[key]["ms"] * 1e3, 2),
+                        p10_us=round(t[key]["p10"] * 1e3, 2), p90_us=round(t[key]["p90"] * 1e3, 2),
+                        gbs=round(gbs(nbytes, t[key]["ms"]), 1), note=note)
+    return res
 
 
 def cpu_baseline(torch, case, target_s):
@@ -386,6 +466,28 @@ def variant_paged(torch, fd, W, args, timer):
     call = lambda: lib.fd_decode_attn_paged(*a)  # noqa: E731
     check_rc(lib, call())
     t = timer.run([call], args.steps, args.warmup)
+    check_rc(lib, call())
+    # parity sample: the shortest and the longest sequence, through the
+    # oracle's own block-table gather on a pool of just their pages
+    picks = [int(min(range(B), key=lambda i: lens[i])), int(max(range(B), key=lambda i: lens[i]))]
+    npg = [(int(lens[i]) + c.page - 1) // c.page for i in picks]
+    pages = torch.cat([c.block_table[i, :m].long() for i, m in zip(picks, npg)])
+    kp, vpool = _host(c.k_pool[pages]), _host(c.v_pool[pages])
+    table = torch.zeros((2, max(npg)), dtype=torch.int32)
+    table[0, :npg[0]] = torch.arange(npg[0], dtype=torch.int32)
+    table[1, :npg[1]] = torch.arange(npg[0], npg[0] + npg[1], dtype=torch.int32)
+    qs, os_, ls_ = _host(c.q[picks]), _host(out[picks]), _host(lse[picks])
+    plens = [int(lens[i]) for i in picks]
+
+    def check():
+        import numpy as np
+        from oracle import paged as opg
+        f = lambda t: t.to(torch.float64).numpy()  # noqa: E731
+        ref, lref = opg.paged_attention(f(qs), kp.float().numpy(), vpool.float().numpy(),
+                                        table.numpy(), np.array(plens), c.page, c.scale)
+        return _errs(np, f(os_), f(ls_), ref, lref, 2e-3, 2 * Hq)
+    PARITY_SAMPLES.append((f"config3 paged ragged bf16 (sequences of {plens[0]} and "
+                           f"{plens[1]} positions, all heads)", check))
     total_len = int(sum(lens))
     nbytes = (2 * total_len * Hkv * d * 2 + B * Hq * d * 2 + B * Hq * (d + 1) * 4
               + 4 * int(sum((L + c.page - 1) // c.page for L in lens)))
@@ -429,6 +531,10 @@ def variant_unified(torch, fd, W, args, timer):
     den = [mk_d(k, v) for k, v in zip(ks, vs)]
     check_rc(lib, uni[0]())
     torch.cuda.synchronize()
+    planted_b = sorted({b for b, _, _ in c.overflow_heads})
+    sample_rows(torch, f"config4 fixed maximum bf16 (sequences {planted_b} holding the heads "
+                f"planted above phi, all heads)", c.q[planted_b], c.k[planted_b],
+                c.v[planted_b], out[planted_b], lse[planted_b], c.scale)
     flagged_heads = int(flags.sum())
     G = Hq // Hkv
     unit_flags = flags.view(B, Hkv, G, nc).amax(2)
@@ -494,9 +600,65 @@ def selection_quality(torch, q, k, scale, mask, delta):
                 softmax_mass_kept_min=round(float(mass.min()), 6))
 
 
-def variant_ffd(torch, fd, W, args, timer):
+def _ffd_sample(torch, name, c, pack, delta, out, lse, b, groups):
+    """Register an FFD parity sample: sequence b, kv-groups `groups`, every
+    query head of them (the oracle packs the bf16 keys itself and must
+    produce the same bytes as the GPU packer)."""
+    G = c.q.shape[1] // c.v.shape[1]
+    q = _host(c.q[b])
+    ks = {g: _host(c.k[b, g]) for g in groups}
+    vs = {g: _host(c.v[b, g]) for g in groups}
+    gp = {g: {key: _host(val[b, g]) for key, val in pack.items()} for g in groups}
+    o, l_ = _host(out[b]), _host(lse[b])
+
+    def check():
+        import numpy as np
+        from oracle import ffd as offd
+        eo = el = 0.0
+        same_pack = True
+        for g in groups:
+            ref = offd.pack_keys(ks[g].to(torch.float64).numpy().astype(np.float32))
+            got = {"codes": gp[g]["codes"].numpy().view(np.uint32),
+                   "zs": gp[g]["zs"].numpy().view(np.float16),
+                   "res": gp[g]["res"].numpy(), "rs": gp[g]["rs"].numpy().view(np.float16)}
+            same_pack &= all(np.array_equal(got[key].view(np.uint8), ref[key].view(np.uint8))
+                             for key in ref)
+            K2, Kh = offd.dequant(ref, q.shape[-1])
+            V = vs[g].to(torch.float64).numpy()
+            for h in range(g * G, (g + 1) * G):
+                r = offd.ffd_row(q[h].to(torch.float64).numpy(), K2, Kh, V, c.scale, delta,
+                                 c.n_sink, c.n_local)
+                eo = max(eo, float(np.abs(o[h].to(torch.float64).numpy() - r["out"]).max()))
+                el = max(el, abs(float(l_[h]) - r["lse"]))
+        return dict(rows=len(groups) * G, max_abs_err_out=eo, max_abs_err_lse=el, tol=2e-3,
+                    within_tol=bool(eo <= 2e-3 and el <= 2e-3), pack_bytes_equal=bool(same_pack),
+                    note="positions within 1e-4 of the top-delta threshold may fall either way "
+                         "(the tests bound their effect exactly); none of these rows needs it "
+                         "when within_tol is true")
+    PARITY_SAMPLES.append((name, check))
+
+
+def _ffd_counts(np, mask, B, Hkv, G, L):
+    m = mask.cpu().numpy().view(np.uint32).reshape(B, Hkv, G, -1)
+    per_head = np.unpackbits(m.view(np.uint8), axis=-1).sum(-1)   # [B,Hkv,G]
+    n_union = int(np.unpackbits(np.bitwise_or.reduce(m, axis=2).view(np.uint8), axis=-1).sum())
+    return per_head, n_union
+
+
+def _ffd_bytes(B, Hkv, L, d, Hq, n_anchor, n_union):
+    return (B * Hkv * L * (d // 4 + d // 32 * 4) + n_union * (d + d // 32 * 2 + 2 * d)
+            + B * Hkv * n_anchor * (d // 4 + d // 32 * 6 + d)
+            + B * Hq * d * 2 + B * Hq * (d + 1) * 4)
+
+
+def _ffd_variant(torch, fd, W, args, timer, cfg_id, label):
+    """FFD sparse decode against dense attention on the same data: both
+    timed first, interleaved (median of 3 rounds, each with its own warm-up);
+    the candidate-set statistics and the selection quality (GPU-side
+    diagnostics) only afterwards, outside every timed region.  Dense reads
+    the bf16 keys, FFD the packed ones."""
     import numpy as np
-    c = W.config_case(5, device="cuda:0", **_ffd_override(args))
+    c = W.config_case(cfg_id, device="cuda:0", **_ffd_override(args))
     B, Hq, d = c.q.shape
     Hkv, L = c.v.shape[1], c.v.shape[2]
     G = Hq // Hkv
@@ -506,62 +668,6 @@ def variant_ffd(torch, fd, W, args, timer):
     packs = [fd.ffd_pack(c.k)]
     torch.cuda.synchronize()
     pack_ms = (time.perf_counter() - t0) * 1e3
-    for _ in range(args.copies - 1):
-        packs.append({k: v.clone() for k, v in packs[0].items()})
-    vs = [c.v] + [c.v.clone() for _ in range(args.copies - 1)]
-    out = torch.empty((B, Hq, d), dtype=torch.float32, device="cuda:0")
-    lse = torch.empty((B, Hq), dtype=torch.float32, device="cuda:0")
-    wsn = fd.workspace_bytes("fd_ffd_sparse_decode", B=B, Hq=Hq, Hkv=Hkv, L=L, d=d,
-                             chunk=c.chunk)
-    ws = torch.empty(wsn, dtype=torch.uint8, device="cuda:0")
-    size = C.c_size_t(wsn)
-    st = C.c_void_p(torch.cuda.current_stream().cuda_stream)
-    res = {}
-    for delta in c.deltas:
-        def mk(p, v):
-            a = (vp(c.q), vp(p["codes"]), vp(p["zs"]), vp(p["res"]), vp(p["rs"]), vp(v),
-                 vp(out), vp(lse), B, Hq, Hkv, L, d, c.scale, float(delta), c.n_sink,
-                 c.n_local, c.chunk, None, None, vp(ws), C.byref(size), st)
-            return lambda: lib.fd_ffd_sparse_decode(*a)
-        calls = [mk(p, v) for p, v in zip(packs, vs)]
-        check_rc(lib, calls[0]())
-        _, _, mask, _ = fd.ffd_sparse_decode(c.q, packs[0], c.v, delta, c.n_sink, c.n_local,
-                                             chunk=c.chunk, want_mask=True)
-        m = mask.cpu().numpy().view(np.uint32).reshape(B, Hkv, G, -1)
-        per_head = np.unpackbits(m.view(np.uint8), axis=-1).sum(-1)   # [B,Hkv,G]
-        union = np.bitwise_or.reduce(m, axis=2)
-        n_union = int(np.unpackbits(union.view(np.uint8), axis=-1).sum())
-        quality = selection_quality(torch, c.q, c.k, c.scale, mask, delta)
-        del mask
-        t = timer.run(calls, args.steps, args.warmup)
-        n_anchor = min(L, c.n_sink + c.n_local)
-        nbytes = (B * Hkv * L * (d // 4 + d // 32 * 4) + n_union * (d + d // 32 * 2 + 2 * d)
-                  + B * Hkv * n_anchor * (d // 4 + d // 32 * 6 + d)
-                  + B * Hq * d * 2 + B * Hq * (d + 1) * 4)
-        res[f"delta_{delta:g}"] = dict(
-            us_per_step=round(t["ms"] * 1e3, 2), p10_us=round(t["p10"] * 1e3, 2),
-            p90_us=round(t["p90"] * 1e3, 2), bytes=int(nbytes),
-            gbs=round(gbs(nbytes, t["ms"]), 1),
-            pct_of_peak=round(100 * gbs(nbytes, t["ms"]) / PEAK_GBS, 1),
-            kept_per_head=round(float(per_head.mean()) / L, 4),
-            kept_group_union=round(n_union / (B * Hkv * L), 4),
-            dense_bf16_equiv_bytes=2 * B * Hkv * L * d * 2, **quality)
-    return dict(workload=f"FFD sparse decode, B={B}, Hq={Hq}, Hkv={Hkv}, d={d}, L={L}, "
-                         f"chunk={c.chunk}, sinks={c.n_sink}, local={c.n_local}",
-                pack_ms_whole_cache=round(pack_ms, 2), **res)
-
-
-def variant_ffd_peaked(torch, fd, W, args, timer):
-    """FFD against dense attention on the same peaked data: sharp queries
-    whose heads of a group attend alike (per-head sparsity at the levels the
-    FFD digest reports).  Dense reads the bf16 keys, FFD the packed ones."""
-    import numpy as np
-    c = W.config_case(6, device="cuda:0", **_ffd_override(args))
-    B, Hq, d = c.q.shape
-    Hkv, L = c.v.shape[1], c.v.shape[2]
-    G = Hq // Hkv
-    lib = fd.lib()
-    packs = [fd.ffd_pack(c.k)]
     packs += [{k: v.clone() for k, v in packs[0].items()} for _ in range(args.copies - 1)]
     ks = [c.k] + [c.k.clone() for _ in range(args.copies - 1)]
     vs = [c.v] + [c.v.clone() for _ in range(args.copies - 1)]
@@ -578,43 +684,59 @@ def variant_ffd_peaked(torch, fd, W, args, timer):
         a = (fd.FD_BF16, vp(c.q), vp(k), vp(v), vp(out), vp(lse), B, Hq, Hkv, L, d, c.scale,
              512, vp(ws), C.byref(size), st)
         return lambda: lib.fd_decode_attn(*a)
+
+    def mk_f(p, v, delta):
+        a = (vp(c.q), vp(p["codes"]), vp(p["zs"]), vp(p["res"]), vp(p["rs"]), vp(v),
+             vp(out), vp(lse), B, Hq, Hkv, L, d, c.scale, float(delta), c.n_sink,
+             c.n_local, c.chunk, None, None, vp(ws), C.byref(size), st)
+        return lambda: lib.fd_ffd_sparse_decode(*a)
+
     groups = {"dense": [mk_d(k, v) for k, v in zip(ks, vs)]}
-    info = {}
     for delta in c.deltas:
-        def mk(p, v, delta=delta):
-            a = (vp(c.q), vp(p["codes"]), vp(p["zs"]), vp(p["res"]), vp(p["rs"]), vp(v),
-                 vp(out), vp(lse), B, Hq, Hkv, L, d, c.scale, float(delta), c.n_sink,
-                 c.n_local, c.chunk, None, None, vp(ws), C.byref(size), st)
-            return lambda: lib.fd_ffd_sparse_decode(*a)
-        key = f"delta_{delta:g}"
-        groups[key] = [mk(p, v) for p, v in zip(packs, vs)]
-        check_rc(lib, groups[key][0]())
-        _, _, mask, _ = fd.ffd_sparse_decode(c.q, packs[0], c.v, delta, c.n_sink, c.n_local,
-                                             chunk=c.chunk, want_mask=True)
-        m = mask.cpu().numpy().view(np.uint32).reshape(B, Hkv, G, -1)
-        per_head = np.unpackbits(m.view(np.uint8), axis=-1).sum(-1)
-        n_union = int(np.unpackbits(np.bitwise_or.reduce(m, axis=2).view(np.uint8),
-                                    axis=-1).sum())
-        n_anchor = min(L, c.n_sink + c.n_local)
-        nbytes = (B * Hkv * L * (d // 4 + d // 32 * 4) + n_union * (d + d // 32 * 2 + 2 * d)
-                  + B * Hkv * n_anchor * (d // 4 + d // 32 * 6 + d)
-                  + B * Hq * d * 2 + B * Hq * (d + 1) * 4)
-        info[key] = dict(bytes=int(nbytes), kept_per_head=round(float(per_head.mean()) / L, 4),
-                         kept_group_union=round(n_union / (B * Hkv * L), 4),
-                         **selection_quality(torch, c.q, c.k, c.scale, mask, delta))
-        del mask
-    check_rc(lib, groups["dense"][0]())
+        groups[f"delta_{delta:g}"] = [mk_f(p, v, delta) for p, v in zip(packs, vs)]
+    for calls in groups.values():
+        check_rc(lib, calls[0]())
     t = interleaved(timer, groups, args.steps, args.warmup)
+
+    # diagnostics, outside the timed region
     dense_bytes = 2 * B * Hkv * L * d * 2 + B * Hq * d * 2 + B * Hq * (d + 1) * 4
-    res = dict(dense_us_per_step=round(t["dense"]["ms"] * 1e3, 2),
-               dense_gbs=round(gbs(dense_bytes, t["dense"]["ms"]), 1))
-    for key, inf in info.items():
+    res = dict(workload=f"{label}, B={B}, Hq={Hq}, Hkv={Hkv}, d={d}, L={L}, chunk={c.chunk}, "
+                        f"sinks={c.n_sink}, local={c.n_local}",
+               pack_ms_whole_cache=round(pack_ms, 2),
+               dense_us_per_step=round(t["dense"]["ms"] * 1e3, 2),
+               dense_gbs=round(gbs(dense_bytes, t["dense"]["ms"]), 1),
+               dense_bf16_bytes=dense_bytes)
+    n_anchor = min(L, c.n_sink + c.n_local)
+    for delta in c.deltas:
+        key = f"delta_{delta:g}"
+        _, _, mask, _ = fd.ffd_sparse_decode(c.q, packs[0], c.v, delta, c.n_sink, c.n_local,
+                                             chunk=c.chunk, want_mask=True, out=out, lse=lse)
+        per_head, n_union = _ffd_counts(np, mask, B, Hkv, G, L)
+        quality = selection_quality(torch, c.q, c.k, c.scale, mask, delta)
+        del mask
+        _ffd_sample(torch, f"config{cfg_id} {label} delta {delta:g} (sequence 0, kv-groups 0 "
+                    f"and {Hkv - 1})", c, packs[0], delta, out, lse, 0, (0, Hkv - 1))
+        nbytes = _ffd_bytes(B, Hkv, L, d, Hq, n_anchor, n_union)
         ms = t[key]["ms"]
-        res[key] = dict(us_per_step=round(ms * 1e3, 2), gbs=round(gbs(inf["bytes"], ms), 1),
-                        pct_of_peak=round(100 * gbs(inf["bytes"], ms) / PEAK_GBS, 1),
-                        speedup_vs_dense=round(t["dense"]["ms"] / ms, 3), **inf)
-    return dict(workload=f"FFD vs dense on peaked queries (scale 5, group-shared 0.95), "
-                         f"B={B}, Hq={Hq}, Hkv={Hkv}, d={d}, L={L}, chunk={c.chunk}", **res)
+        res[key] = dict(us_per_step=round(ms * 1e3, 2), p10_us=round(t[key]["p10"] * 1e3, 2),
+                        p90_us=round(t[key]["p90"] * 1e3, 2), bytes=int(nbytes),
+                        gbs=round(gbs(nbytes, ms), 1),
+                        pct_of_peak=round(100 * gbs(nbytes, ms) / PEAK_GBS, 1),
+                        speedup_vs_dense=round(t["dense"]["ms"] / ms, 3),
+                        kept_per_head=round(float(per_head.mean()) / L, 4),
+                        kept_group_union=round(n_union / (B * Hkv * L), 4), **quality)
+    return res
+
+
+def variant_ffd(torch, fd, W, args, timer):
+    return _ffd_variant(torch, fd, W, args, timer, 5, "FFD sparse decode (iid scores)")
+
+
+def variant_ffd_peaked(torch, fd, W, args, timer):
+    """Sharp queries whose heads of a group attend alike (per-head sparsity
+    at the levels the FFD digest reports)."""
+    return _ffd_variant(torch, fd, W, args, timer, 6,
+                        "FFD vs dense on peaked queries (scale 5, group-shared 0.95)")
 
 
 def main():
@@ -664,13 +786,16 @@ def main():
         },
     }
     if not args.no_variants:
-        fns = dict(dense_128k=variant_dense_128k, paged=variant_paged,
+        fns = dict(config1=variant_config1, dense_128k=variant_dense_128k, paged=variant_paged,
                    unified_max=variant_unified, ffd=variant_ffd, ffd_peaked=variant_ffd_peaked,
                    multi_row=variant_multi, append=variant_append)
         line["variants"] = {name: fns[name](torch, fd, W, args, timer)
                             for name in VARIANTS if name in want}
     if not args.no_cpu_baseline:
+        # the CPU leg: the oracle timed on the host cores, then the sampled
+        # rows of every timed workload compared with it
         line["cpu_baseline"] = cpu_baseline(torch, case, args.cpu_seconds)
+        line["parity_sample"] = {name: fn() for name, fn in PARITY_SAMPLES}
     print(json.dumps(line), flush=True)
 
 
