@@ -361,13 +361,18 @@ int fd_decode_attn_multi(fd_dtype_t dt, const void* q, const void* k, const void
                         pa, ws, nullptr, L, stream);
   }
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  float *o_part, *ml_part;
-  split_ws(ws, B, M * Hq, nc, d, &o_part, &ml_part);
-  fdk::MultiArgs ma{q, k, v, o_part, ml_part, B, M, Hq, Hkv, L, chunk, nc,
+  fdk::MultiArgs ma{q, k, v, nullptr, nullptr, B, M, Hq, Hkv, L, chunk, nc,
                     (float)((double)scale * 1.4426950408889634)};
+  // splits of F consecutive chunks (fewer partials when the chunks outnumber
+  // the device's wave slots); the workspace sized for nc chunks holds them
+  const int F = fdk::multi_fold(d, ma);
+  const long long split = (long long)chunk * F;
+  ma.chunk = split > L ? L : (int)split;
+  ma.nc = n_chunks_of(L, ma.chunk);
+  split_ws(ws, B, M * Hq, ma.nc, d, &ma.o_part, &ma.ml_part);
   hipError_t e = fdk::launch_multi(d, ma, s);
   if (e != hipSuccess) return hip_status(e, "multi-row kernel launch");
-  fdk::MergeArgs mg{o_part, ml_part, out, lse, nullptr, M * Hq, nc, chunk, L};
+  fdk::MergeArgs mg{ma.o_part, ma.ml_part, out, lse, nullptr, M * Hq, ma.nc, ma.chunk, L};
   return hip_status(fdk::launch_merge(d, B, mg, s), "merge kernel launch");
 }
 

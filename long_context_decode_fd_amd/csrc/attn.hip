@@ -644,8 +644,7 @@ __global__ __launch_bounds__(W * kWave) void merge_kernel(MergeArgs a) {
   }
 }
 
-// Compute units of the current device (cached per device).
-static int cu_count() {
+int cu_count() {
   static std::atomic<int> cached[64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;

@@ -84,6 +84,13 @@ struct MultiArgs {
   float c_log2;
 };
 hipError_t launch_multi(int D, const MultiArgs& a, hipStream_t s);
+// Chunks per split for the multi-row kernels: the number of consecutive
+// chunks of a row that one split covers, chosen so that the splits fill the
+// device's wave slots with the fewest rounds (a.chunk and a.nc as called).
+int multi_fold(int D, const MultiArgs& a);
+
+// Compute units of the current device (cached per device).
+int cu_count();
 
 struct AppendArgs {
   const char* k_new;   // [B, Hkv, M, row]

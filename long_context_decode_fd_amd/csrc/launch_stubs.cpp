@@ -22,6 +22,7 @@ hipError_t launch_merge(int, int, const MergeArgs&, hipStream_t) { no_launch("me
 hipError_t launch_ffd_pack(int, const FfdPackArgs&, hipStream_t) { no_launch("FFD pack kernel"); }
 hipError_t launch_ffd(int, int, const FfdArgs&, hipStream_t) { no_launch("FFD kernel"); }
 hipError_t launch_multi(int, const MultiArgs&, hipStream_t) { no_launch("multi-row kernel"); }
+int multi_fold(int, const MultiArgs&) { no_launch("multi-row split"); }
 hipError_t launch_append(bool, const AppendArgs&, hipStream_t) { no_launch("append kernel"); }
 
 }  // namespace fdk

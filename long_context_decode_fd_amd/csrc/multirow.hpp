@@ -2,10 +2,11 @@
 // each attending to the cache up to its own position ("Flash Decoding"
 // explainer, section 1; the tokens' keys and values are already appended at
 // positions L-M .. L-1).  The G query heads of a kv-head times the M tokens
-// give R = G*M <= 32 query rows (one or two tiles of 16) that share every K
-// and V row -- the flat
-// GEMM case of the "FlashDecoding" deployment blog (section 1), which here
-// runs on the matrix cores:
+// give R = G*M query rows that share every K and V row -- the flat GEMM case
+// of the "FlashDecoding" deployment blog (section 1), which here runs on the
+// matrix cores.  This kernel takes R <= 16 rows (one query tile) per wave;
+// 16 < R <= 32 runs on a pair of waves (multirow_pair.hip) with the same
+// operand layouts:
 //
 //   * K and V rows arrive with fully coalesced 16-byte loads (one wave load
 //     = 1 KiB of consecutive rows) and pass through a small per-wave LDS
@@ -21,8 +22,8 @@
 //     bf16 hi + lo parts so that P V keeps fp32-level accuracy (two MFMAs).
 //   * V tiles are read back from LDS transposed with ds_read_b64_tr_b16 (four
 //     positions of one dim per lane, the B operand of P V).
-//   * Split-KV as in the single-query kernel: one wavefront per chunk,
-//     partials (O, m, l) per (token, head, chunk), merged by the common exact
+//   * Split-KV as in the single-query kernel: one wavefront per split,
+//     partials (O, m, l) per (token, head, split), merged by the common exact
 //     log-sum-exp kernel.
 #pragma once
 
@@ -36,15 +37,11 @@ namespace fdk {
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
 
-// 16-position tiles per wave batch: 8 K and 8 V loads at d = 128 with one
-// query tile; 4 tiles with two (deeper batches pay once the 16x16x32 P V and
-// the vector-register accumulators freed registers).
-template <int QT>
-constexpr int mr_tiles() { return QT == 1 ? 2 : 4; }
-// finished units held in registers before their partials are written (one
-// query tile)
+// 16-position tiles per wave batch: 2 K and 2 V tiles in flight (8 + 8
+// wave loads at d = 128)
+constexpr int kMrTiles = 2;
+// finished units held in registers before their partials are written
 constexpr int kMrHold = 4;
-
 
 __device__ __forceinline__ f32x4 mfma_qk(const u32x4& a, const u32x4& b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
@@ -73,14 +70,13 @@ __device__ __forceinline__ void split_bf16(const float (&p)[4], u32x2& hi, u32x2
   lo = u32x2{l[0], l[1]};
 }
 
-// QT = query tiles of 16 rows (R = G*M <= 16 * QT); both share every K and V
-// tile.
-template <int D, int QT>
+// One query tile of R = G*M <= 16 rows per wave.
+template <int D>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1)))
 void multi_kernel(MultiArgs a) {
   constexpr int KS = D / 32;             // QK k-steps (32 dims each)
   constexpr int DB = D / 16;             // 16-dim blocks of the P V product
-  constexpr int TT = mr_tiles<QT>();
+  constexpr int TT = kMrTiles;
   constexpr int STEP = 16 * TT;          // positions per wave batch
   constexpr int ROWB = D * 2;            // bytes per cache row
   constexpr int LPR = ROWB / 16;         // lanes per row in a coalesced load
@@ -122,26 +118,20 @@ void multi_kernel(MultiArgs a) {
   auto base_of = [&](const void* t, const UnitM& x) {
     return reinterpret_cast<const char*>(t) + ((size_t)x.b * a.Hkv + x.kvh) * (size_t)a.L * ROWB;
   };
-  // Query row n + 16*qt of this lane: token r = row / G, head kvh*G + row % G;
-  // its last visible position is L - M + r.  Rows >= R are padding (q = 0).
-  int lim[QT];
-#pragma unroll
-  for (int qt = 0; qt < QT; ++qt) lim[qt] = a.L - a.M + (n + 16 * qt) / G;
-  u32x4 qf[QT][KS];
+  // Query row n of this lane: token r = n / G, head kvh*G + n % G; its last
+  // visible position is L - M + r.  Rows >= R are padding (q = 0).
+  const int lim = a.L - a.M + n / G;
+  u32x4 qf[KS];
   auto load_q = [&](const UnitM& x) {
+    if (n < R) {
+      const uint16_t* qp = reinterpret_cast<const uint16_t*>(a.q) +
+                           (((size_t)x.b * a.M + n / G) * a.Hq + (size_t)x.kvh * G + n % G) * D +
+                           8 * qd;
 #pragma unroll
-    for (int qt = 0; qt < QT; ++qt) {
-      const int row = n + 16 * qt;
-      if (row < R) {
-        const uint16_t* qp =
-            reinterpret_cast<const uint16_t*>(a.q) +
-            (((size_t)x.b * a.M + row / G) * a.Hq + (size_t)x.kvh * G + row % G) * D + 8 * qd;
+      for (int s = 0; s < KS; ++s) qf[s] = ld16(qp + 32 * s);
+    } else {
 #pragma unroll
-        for (int s = 0; s < KS; ++s) qf[qt][s] = ld16(qp + 32 * s);
-      } else {
-#pragma unroll
-        for (int s = 0; s < KS; ++s) qf[qt][s] = u32x4{0, 0, 0, 0};
-      }
+      for (int s = 0; s < KS; ++s) qf[s] = u32x4{0, 0, 0, 0};
     }
   };
   // wave load i of tile tt: rows T + 16*tt + RPI*i + lrow, bytes 16*lcol.
@@ -170,90 +160,46 @@ void multi_kernel(MultiArgs a) {
       *reinterpret_cast<u32x4*>(dst + (RPI * i + lrow) * LSTR + 16 * lcol) = r[i];
   };
 
-  // Partials of unit uu, rows ((b*M + r)*Hq + h)*nc + c.  With one query
-  // tile, O goes through the wave's LDS tiles (free between units: the next
-  // unit's K rows are still in registers) so that every store writes 16
-  // bytes per lane and whole rows, instead of 4 bytes per lane in 64-byte
-  // pieces.
+  // Partials of unit uu, rows ((b*M + r)*Hq + h)*nc + c.  O goes through the
+  // wave's LDS tiles (free between units: the next unit's K rows are still
+  // in registers) so that every store writes 16 bytes per lane and whole
+  // rows, instead of 4 bytes per lane in 64-byte pieces.
   unsigned char* ost = s_kv[wave][0];
-  // staged (two query tiles): the unit's 32 O rows are in LDS there
-  auto store_unit = [&](const f32x4 (&o)[QT][DB], const float (&m)[QT], const float (&l)[QT],
-                        int uu, const unsigned char* staged = nullptr) {
+  auto store_unit = [&](const f32x4 (&o)[DB], float m, float l, int uu) {
     UnitM x;
     decode(uu, x);
+    if (qd == 0 && n < R) {
+      const size_t prow =
+          (((size_t)x.b * a.M + n / G) * a.Hq + (size_t)x.kvh * G + n % G) * a.nc + x.c;
+      *reinterpret_cast<f32x2*>(a.ml_part + prow * 2) =
+          f32x2{(m == kNegInf) ? kNegInf : m * c_log2, l};
+    }
+    // lane (n, qd) holds O rows 4*qd + e, dims 16*db + n
 #pragma unroll
-    for (int qt = 0; qt < QT; ++qt) {
-      const int rown = n + 16 * qt;
-      if (qd == 0 && rown < R) {
+    for (int e = 0; e < 4; ++e)
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+        *reinterpret_cast<float*>(ost + (4 * qd + e) * OSTR + (16 * db + n) * 4) = o[db][e];
+    // read back: wave store i covers rows ORPI*i .. +ORPI, 16 bytes per lane
+    constexpr int LPO = kWave / ORPI;   // lanes per O row
+#pragma unroll
+    for (int i = 0; i < 16 / ORPI; ++i) {
+      const int row = ORPI * i + lane / LPO, cb = 16 * (lane % LPO);
+      const f32x4 v = *reinterpret_cast<const f32x4*>(ost + row * OSTR + cb);
+      if (row < R) {
         const size_t prow =
-            (((size_t)x.b * a.M + rown / G) * a.Hq + (size_t)x.kvh * G + rown % G) * a.nc + x.c;
-        *reinterpret_cast<f32x2*>(a.ml_part + prow * 2) =
-            f32x2{(m[qt] == kNegInf) ? kNegInf : m[qt] * c_log2, l[qt]};
-      }
-      if constexpr (QT == 1) {
-        // lane (n, qd) holds O rows 4*qd + e, dims 16*db + n
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-#pragma unroll
-          for (int db = 0; db < DB; ++db)
-            *reinterpret_cast<float*>(ost + (4 * qd + e) * OSTR + (16 * db + n) * 4) = o[qt][db][e];
-        // read back: wave store i covers rows ORPI*i .. +ORPI, 16 bytes per lane
-        constexpr int LPO = kWave / ORPI;   // lanes per O row
-#pragma unroll
-        for (int i = 0; i < 16 / ORPI; ++i) {
-          const int rr = ORPI * i + lane / LPO, cb = 16 * (lane % LPO);
-          const f32x4 v = *reinterpret_cast<const f32x4*>(ost + rr * OSTR + cb);
-          const int row = 16 * qt + rr;
-          if (row < R) {
-            const size_t prow =
-                (((size_t)x.b * a.M + row / G) * a.Hq + (size_t)x.kvh * G + row % G) * a.nc + x.c;
-            *reinterpret_cast<f32x4*>(reinterpret_cast<unsigned char*>(a.o_part + prow * D) + cb) =
-                v;
-          }
-        }
-      } else if (staged != nullptr) {
-        // two query tiles held in LDS: rows 16 qt .. 16 qt + 15 at staged
-        constexpr int LPO = kWave / ORPI;   // lanes per O row
-#pragma unroll
-        for (int i = 0; i < 16 / ORPI; ++i) {
-          const int rr = 16 * qt + ORPI * i + lane / LPO, cb = 16 * (lane % LPO);
-          const f32x4 v = *reinterpret_cast<const f32x4*>(staged + rr * OSTR + cb);
-          if (rr < R) {
-            const size_t prow =
-                (((size_t)x.b * a.M + rr / G) * a.Hq + (size_t)x.kvh * G + rr % G) * a.nc + x.c;
-            *reinterpret_cast<f32x4*>(reinterpret_cast<unsigned char*>(a.o_part + prow * D) + cb) =
-                v;
-          }
-        }
-      } else {
-        // two query tiles: straight from the MFMA layout
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int row = 16 * qt + 4 * qd + e;
-          if (row < R) {
-            const size_t prow =
-                (((size_t)x.b * a.M + row / G) * a.Hq + (size_t)x.kvh * G + row % G) * a.nc + x.c;
-#pragma unroll
-            for (int db = 0; db < DB; ++db) a.o_part[prow * D + 16 * db + n] = o[qt][db][e];
-          }
-        }
+            (((size_t)x.b * a.M + row / G) * a.Hq + (size_t)x.kvh * G + row % G) * a.nc + x.c;
+        *reinterpret_cast<f32x4*>(reinterpret_cast<unsigned char*>(a.o_part + prow * D) + cb) = v;
       }
     }
   };
-  // Finished units wait in registers (up to H of them, one query tile only)
-  // and are written together when H are held or the wave has no unit left.
-  // Stores count on the same vector-memory counter as loads: partials
-  // stored between units made the next unit's first K wait for them.
-  constexpr int H = QT == 1 ? kMrHold : 1;
-  f32x4 hold_o[H][QT][DB];
-  // two query tiles: no registers to spare, so one finished unit waits in
-  // LDS (32 O rows) and is written together with the next one, which halves
-  // the store events between units
-  __shared__ __align__(16) unsigned char s_hold2[QT == 2 ? kWaves : 1][QT == 2 ? 32 * OSTR : 16];
-  float h2_m[QT], h2_l[QT];
-  int h2_u = 0;
-  bool h2_held = false;   // wave-uniform
-  float hold_m[H][QT], hold_l[H][QT];
+  // Finished units wait in registers (up to H of them) and are written
+  // together when H are held or the wave has no unit left.  Stores count on
+  // the same vector-memory counter as loads: partials stored between units
+  // made the next unit's first K wait for them.
+  constexpr int H = kMrHold;
+  f32x4 hold_o[H][DB];
+  float hold_m[H], hold_l[H];
   int hold_u[H];
   int held = 0;   // wave-uniform
 
@@ -283,45 +229,34 @@ void multi_kernel(MultiArgs a) {
     const char* kb = base_of(a.k, cur);
     const char* vb = base_of(a.v, cur);
 
-    f32x4 o[QT][DB];
-    float m[QT], l[QT];   // row's running maximum (raw) and this lane's part of l
+    f32x4 o[DB];
+    float m = kNegInf, l = 0.f;   // row's running maximum (raw) and this lane's part of l
 #pragma unroll
-    for (int qt = 0; qt < QT; ++qt) {
-      m[qt] = kNegInf;
-      l[qt] = 0.f;
-#pragma unroll
-      for (int db = 0; db < DB; ++db) o[qt][db] = f32x4{0.f, 0.f, 0.f, 0.f};
-    }
+    for (int db = 0; db < DB; ++db) o[db] = f32x4{0.f, 0.f, 0.f, 0.f};
     for (int T = c0; T < c1; T += STEP) {
       issue(vb, T, c1, vr);
-      float sc[QT][TT][4];
+      float sc[TT][4];
 #pragma unroll
       for (int tt = 0; tt < TT; ++tt) {
         // A operand of k-step s: dims 32s + 8 qd .. +8 of row n
         to_lds(lk, kr[tt]);
-        f32x4 acc[QT];
-#pragma unroll
-        for (int qt = 0; qt < QT; ++qt) acc[qt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int s = 0; s < KS; ++s) {
           const u32x4 ka = *reinterpret_cast<const u32x4*>(lk + n * LSTR + 64 * s + 16 * qd);
-#pragma unroll
-          for (int qt = 0; qt < QT; ++qt) acc[qt] = mfma_qk(ka, qf[qt][s], acc[qt]);
+          acc = mfma_qk(ka, qf[s], acc);
         }
 #pragma unroll
-        for (int qt = 0; qt < QT; ++qt)
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int pos = T + 16 * tt + 4 * qd + e;
-            sc[qt][tt][e] = (pos < c1 && pos <= lim[qt]) ? acc[qt][e] : kNegInf;
-          }
+        for (int e = 0; e < 4; ++e) {
+          const int pos = T + 16 * tt + 4 * qd + e;
+          sc[tt][e] = (pos < c1 && pos <= lim) ? acc[e] : kNegInf;
+        }
       }
-      if constexpr (QT == 1) {
-        // one query tile: K is requested on every path (after the wave's
-        // last batch, this batch's rows again, unused), so the compiler's
-        // wait counts agree on all paths and P V waits for this batch's V
-        // rows only, not for these loads (measured 189 -> 182 us at M = 4;
-        // with two tiles, whose registers are full, it measured slower)
+      // K is requested on every path (after the wave's last batch, this
+      // batch's rows again, unused), so the compiler's wait counts agree on
+      // all paths and P V waits for this batch's V rows only, not for these
+      // loads (measured 189 -> 182 us at M = 4)
+      {
         const char* src = kb;
         int t_next = T + STEP, c_end = c1;
         if (T + STEP >= c1 && has_next) {
@@ -333,155 +268,76 @@ void multi_kernel(MultiArgs a) {
           t_next = T;
         }
         issue(src, t_next, c_end, kr);
-      } else {
-        if (T + STEP < c1) {
-          issue(kb, T + STEP, c1, kr);
-        } else if (has_next) {
-          load_q(nxt);
-          issue(base_of(a.k, nxt), nxt.c0, nxt.c1, kr);
-        }
       }
 
-      float base[QT];   // running maximum (raw), 0 while it is -inf
-#pragma unroll
-      for (int qt = 0; qt < QT; ++qt) {
-        float bm = kNegInf;
-#pragma unroll
-        for (int tt = 0; tt < TT; ++tt)
-#pragma unroll
-          for (int e = 0; e < 4; ++e) bm = fmaxf(bm, sc[qt][tt][e]);
-        bm = pair_max<32>(pair_max<16>(bm));
-        const float mn = fmaxf(m[qt], bm);
-        if (__any(mn > m[qt])) {
-          const float alpha = (mn == m[qt]) ? 1.f : exp2_hw((m[qt] - mn) * c_log2);
-          l[qt] *= alpha;
-          // O rows 4*qd + e take the factors of those rows (held by lanes 4*qd + e)
-          float ae[4];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) ae[e] = __shfl(alpha, 4 * qd + e);
-#pragma unroll
-          for (int db = 0; db < DB; ++db)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) o[qt][db][e] *= ae[e];
-          m[qt] = mn;
-        }
-        // exponent (s - m) c: exactly 0 at the running maximum
-        base[qt] = (m[qt] == kNegInf) ? 0.f : m[qt];
-      }
-
-      u32x2 ph[QT][TT], pl[QT][TT];
+      float bm = kNegInf;
 #pragma unroll
       for (int tt = 0; tt < TT; ++tt)
 #pragma unroll
-        for (int qt = 0; qt < QT; ++qt) {
-          float p[4];
+        for (int e = 0; e < 4; ++e) bm = fmaxf(bm, sc[tt][e]);
+      bm = pair_max<32>(pair_max<16>(bm));
+      const float mn = fmaxf(m, bm);
+      if (__any(mn > m)) {
+        const float alpha = (mn == m) ? 1.f : exp2_hw((m - mn) * c_log2);
+        l *= alpha;
+        // O rows 4*qd + e take the factors of those rows (held by lanes 4*qd + e)
+        float ae[4];
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            p[e] = exp2_hw((sc[qt][tt][e] - base[qt]) * c_log2);
-            l[qt] += p[e];
-          }
-          split_bf16(p, ph[qt][tt], pl[qt][tt]);
-        }
-      // P V over pairs of 16-position tiles with v_mfma_f32_16x16x32_bf16:
-      // k = 8 qd + j stands for position 4 qd + j % 4 of tile 2 tp + j / 4,
-      // so a lane's A operand is its P values of both tiles and its B
-      // operand the transposed reads of both V tiles (each staged in one of
-      // the wave's two LDS tiles; the K tiles are no longer needed here, and
-      // LDS keeps the wave's order).
-      // (with one query tile this form measured 3 % slower: register pressure)
-      constexpr int NTP = QT == 2 ? TT / 2 : 0;   // tile pairs on 16x16x32
+        for (int e = 0; e < 4; ++e) ae[e] = __shfl(alpha, 4 * qd + e);
 #pragma unroll
-      for (int tp = 0; tp < NTP; ++tp) {
-        to_lds(lk, vr[2 * tp]);
-        to_lds(lv, vr[2 * tp + 1]);
-        auto vpair = [&](int db) {
-          const u32x2 v0 = __builtin_bit_cast(
-              u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                         (__attribute__((address_space(3))) s16x4_t*)(lk + tr_off + 32 * db)));
-          const u32x2 v1 = __builtin_bit_cast(
-              u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                         (__attribute__((address_space(3))) s16x4_t*)(lv + tr_off + 32 * db)));
-          return u32x4{v0.x, v0.y, v1.x, v1.y};
-        };
+        for (int db = 0; db < DB; ++db)
 #pragma unroll
-        for (int db = 0; db < DB; ++db) {
-          const u32x4 vb = vpair(db);
-#pragma unroll
-          for (int qt = 0; qt < QT; ++qt) {
-            const u32x2 h0 = ph[qt][2 * tp], h1 = ph[qt][2 * tp + 1];
-            const u32x2 l0 = pl[qt][2 * tp], l1 = pl[qt][2 * tp + 1];
-            o[qt][db] = mfma_qk(u32x4{h0.x, h0.y, h1.x, h1.y}, vb, o[qt][db]);
-            o[qt][db] = mfma_qk(u32x4{l0.x, l0.y, l1.x, l1.y}, vb, o[qt][db]);
-          }
-        }
+          for (int e = 0; e < 4; ++e) o[db][e] *= ae[e];
+        m = mn;
       }
-      // the remaining tiles one at a time on v_mfma_f32_16x16x16_bf16
-      // (position 4 qd + e)
+      // exponent (s - m) c: exactly 0 at the running maximum
+      const float base = (m == kNegInf) ? 0.f : m;
+
+      u32x2 ph[TT], pl[TT];
 #pragma unroll
-      for (int tt = 2 * NTP; tt < TT; ++tt) {
+      for (int tt = 0; tt < TT; ++tt) {
+        float p[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          p[e] = exp2_hw((sc[tt][e] - base) * c_log2);
+          l += p[e];
+        }
+        split_bf16(p, ph[tt], pl[tt]);
+      }
+      // P V one tile at a time on v_mfma_f32_16x16x16_bf16 (position 4 qd +
+      // e); the pairwise 16x16x32 form measured 3 % slower here (register
+      // pressure)
+#pragma unroll
+      for (int tt = 0; tt < TT; ++tt) {
         to_lds(lv, vr[tt]);
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
           const u32x2 vv = __builtin_bit_cast(
               u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
                          (__attribute__((address_space(3))) s16x4_t*)(lv + tr_off + 32 * db)));
-#pragma unroll
-          for (int qt = 0; qt < QT; ++qt) {
-            o[qt][db] = mfma_pv(ph[qt][tt], vv, o[qt][db]);
-            o[qt][db] = mfma_pv(pl[qt][tt], vv, o[qt][db]);
-          }
+          o[db] = mfma_pv(ph[tt], vv, o[db]);
+          o[db] = mfma_pv(pl[tt], vv, o[db]);
         }
       }
     }
 
+    // l of row n: the four lanes of the row hold parts
+    l = pair_sum<32>(pair_sum<16>(l));
 #pragma unroll
-    for (int qt = 0; qt < QT; ++qt) {
-      // l of row n + 16*qt: the four lanes of the row hold parts
-      l[qt] = pair_sum<32>(pair_sum<16>(l[qt]));
+    for (int h = 0; h < H; ++h) {
+      if (held == h) {   // wave-uniform
+        hold_m[h] = m;
+        hold_l[h] = l;
+#pragma unroll
+        for (int db = 0; db < DB; ++db) hold_o[h][db] = o[db];
+        hold_u[h] = u;
+      }
     }
-    if constexpr (H > 1) {
+    if (++held == H || !has_next) {
 #pragma unroll
-      for (int h = 0; h < H; ++h) {
-        if (held == h) {   // wave-uniform
-#pragma unroll
-          for (int qt = 0; qt < QT; ++qt) {
-            hold_m[h][qt] = m[qt];
-            hold_l[h][qt] = l[qt];
-#pragma unroll
-            for (int db = 0; db < DB; ++db) hold_o[h][qt][db] = o[qt][db];
-          }
-          hold_u[h] = u;
-        }
-      }
-      if (++held == H || !has_next) {
-#pragma unroll
-        for (int h = 0; h < H; ++h)
-          if (h < held) store_unit(hold_o[h], hold_m[h], hold_l[h], hold_u[h]);
-        held = 0;
-      }
-    } else {
-      if constexpr (QT != 2) {
-        store_unit(o, m, l, u);
-      } else if (!h2_held && has_next) {
-        // lane (n, qd) holds rows 16 qt + 4 qd + e, dims 16 db + n
-#pragma unroll
-        for (int qt = 0; qt < QT; ++qt) {
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-#pragma unroll
-            for (int db = 0; db < DB; ++db)
-              *reinterpret_cast<float*>(s_hold2[wave] + (16 * qt + 4 * qd + e) * OSTR +
-                                        (16 * db + n) * 4) = o[qt][db][e];
-          h2_m[qt] = m[qt];
-          h2_l[qt] = l[qt];
-        }
-        h2_u = u;
-        h2_held = true;
-      } else {
-        if (h2_held) store_unit(o, h2_m, h2_l, h2_u, s_hold2[wave]);
-        store_unit(o, m, l, u);
-        h2_held = false;
-      }
+      for (int h = 0; h < H; ++h)
+        if (h < held) store_unit(hold_o[h], hold_m[h], hold_l[h], hold_u[h]);
+      held = 0;
     }
     if (!has_next) break;
     cur = nxt;
@@ -499,21 +355,21 @@ static int multi_blocks_per_cu(K kernel) {
   return n;
 }
 
-template <int D, int QT>
+// Units (sequence, kv-head, split) that run at once: one per wave.
+template <int D>
+size_t multi_wave_slots() {
+  static const int per_cu = multi_blocks_per_cu(multi_kernel<D>);
+  return (size_t)cu_count() * per_cu * kWaves;
+}
+
+template <int D>
 hipError_t launch_multi_d(const MultiArgs& a, hipStream_t s) {
-  auto kernel = multi_kernel<D, QT>;
-  static const int per_cu = multi_blocks_per_cu(kernel);
-  int dev = 0, cus = 256;
-  if (hipGetDevice(&dev) != hipSuccess ||
-      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-      cus <= 0)
-    cus = 256;
   // equal rounds for every wave, as for the single-query kernel
   const size_t units = (size_t)a.B * a.Hkv * a.nc;
-  const size_t slots = (size_t)cus * per_cu * kWaves;
+  const size_t slots = multi_wave_slots<D>();
   const size_t rounds = (units + slots - 1) / slots;
   const unsigned grid = (unsigned)((units + kWaves * rounds - 1) / (kWaves * rounds));
-  hipLaunchKernelGGL(kernel, dim3(grid), dim3(kThreads), 0, s, a);
+  hipLaunchKernelGGL(multi_kernel<D>, dim3(grid), dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }
 

@@ -1,0 +1,314 @@
+// Multi-row decode with two query tiles (16 < R = G*M <= 32 query rows per
+// kv-head) on a pair of waves ("Flash Decoding" explainer, section 1; the
+// flat GEMM case of the "FlashDecoding" deployment blog, section 1).
+//
+// A workgroup is two waves working on the same unit (sequence, kv-head,
+// chunk).  Wave w owns query rows 16 w .. 16 w + 15, so each keeps the
+// one-tile register budget (two waves per SIMD) instead of one wave holding
+// both tiles.  The K and V rows of a batch are read from HBM once: each wave
+// loads half of the batch's 16-position tiles (tiles w and w + 2) with
+// coalesced 16-byte loads and writes them into the workgroup's LDS, where
+// both waves read every tile:
+//
+//   barrier 1   both waves are done reading the previous batch's tiles
+//   own tiles   registers -> LDS, then the next batch's loads are issued
+//   barrier 2   the batch is complete in LDS
+//   compute     S^T = K Q^T per tile (v_mfma_f32_16x16x32_bf16, K rows the
+//               A operand), online softmax per query row, P V over pairs of
+//               tiles with 16x16x32 (V read back transposed with
+//               ds_read_b64_tr_b16), p split into bf16 hi + lo parts
+//
+// The operand layouts and the softmax are those of the one-tile kernel
+// (multirow.hpp).  At the end of a unit each wave stages its 16 O rows in
+// its own two K tiles (after a barrier) so that every partial store writes
+// 16 bytes per lane and whole rows.
+#include "multirow.hpp"
+
+namespace fdk {
+
+namespace {
+
+constexpr int kPairTiles = 4;   // 16-position tiles per batch (two per wave)
+
+template <int D>
+__global__ __launch_bounds__(2 * kWave) __attribute__((amdgpu_waves_per_eu(2)))
+void multi_pair_kernel(MultiArgs a) {
+  constexpr int KS = D / 32;             // QK k-steps (32 dims each)
+  constexpr int DB = D / 16;             // 16-dim blocks of the P V product
+  constexpr int TT = kPairTiles;
+  constexpr int TW = TT / 2;             // tiles of K and of V each wave loads
+  constexpr int STEP = 16 * TT;          // positions per batch
+  constexpr int ROWB = D * 2;            // bytes per cache row
+  constexpr int LPR = ROWB / 16;         // lanes per row in a coalesced load
+  constexpr int RPI = kWave / LPR;       // rows per wave load
+  constexpr int NI = 16 / RPI;           // wave loads per 16-row tile
+  constexpr int LSTR = ROWB + 8;         // LDS row stride: rows 4 apart sit 8 banks apart
+  constexpr int OSTR = D * 4 + 16;       // fp32 O row stride of the store staging
+  constexpr int ORPI = kWave * 16 / (D * 4);   // O rows per wave store
+  constexpr int LPO = kWave / ORPI;            // lanes per O row
+  static_assert(8 * OSTR <= 16 * LSTR, "eight O rows must fit one K tile");
+  __shared__ __align__(16) unsigned char s_k[TT][16 * LSTR];
+  __shared__ __align__(16) unsigned char s_v[TT][16 * LSTR];
+
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & (kWave - 1);
+  const int n = lane & 15, qd = lane >> 4;
+  const int G = a.Hq / a.Hkv, R = G * a.M;
+  const int n_units = a.B * a.Hkv * a.nc;
+  const int row0 = 16 * wave;            // this wave's first query row
+  const int lrow = lane / LPR, lcol = lane % LPR;
+  const int lane_off = lrow * ROWB + 16 * lcol;
+  // transposing read of a V tile: lane (n, qd) gets V[4 qd + e][16 db + n]
+  const int tr_off = (4 * qd + (n >> 2)) * LSTR + 8 * (n & 3);
+  const float c_log2 = a.c_log2;
+
+  struct UnitM {
+    int b, kvh, c, c0, c1;
+  };
+  auto decode = [&](int u, UnitM& x) {
+    x.c = u % a.nc;
+    const int bk = u / a.nc;
+    x.kvh = bk % a.Hkv;
+    x.b = bk / a.Hkv;
+    x.c0 = x.c * a.chunk;
+    x.c1 = min(x.c0 + a.chunk, a.L);
+  };
+  auto base_of = [&](const void* t, const UnitM& x) {
+    return reinterpret_cast<const char*>(t) + ((size_t)x.b * a.Hkv + x.kvh) * (size_t)a.L * ROWB;
+  };
+  // query row row0 + n: token r = row / G, head kvh*G + row % G, last
+  // visible position L - M + r; rows >= R are padding (q = 0)
+  const int qrow = row0 + n;
+  const int lim = a.L - a.M + qrow / G;
+  u32x4 qf[KS];
+  auto load_q = [&](const UnitM& x) {
+    if (qrow < R) {
+      const uint16_t* qp = reinterpret_cast<const uint16_t*>(a.q) +
+                           (((size_t)x.b * a.M + qrow / G) * a.Hq + (size_t)x.kvh * G + qrow % G) * D +
+                           8 * qd;
+#pragma unroll
+      for (int s = 0; s < KS; ++s) qf[s] = ld16(qp + 32 * s);
+    } else {
+#pragma unroll
+      for (int s = 0; s < KS; ++s) qf[s] = u32x4{0, 0, 0, 0};
+    }
+  };
+  // this wave's tiles 2 j + wave of the batch at T: one buffer descriptor per
+  // tile, limited to the chunk end c1 (rows past it read as zeros, untouched)
+  auto issue = [&](const char* __restrict__ src, int T, int c1, u32x4 (&r)[TW][NI]) {
+#pragma unroll
+    for (int j = 0; j < TW; ++j) {
+      const int t0 = T + 16 * (2 * j + wave);
+      const int nrow = min(max(c1 - t0, 0), 16);
+      const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(src + (size_t)t0 * ROWB, nrow * ROWB);
+#pragma unroll
+      for (int i = 0; i < NI; ++i) r[j][i] = ld16_buf(rs, lane_off + RPI * i * ROWB);
+    }
+  };
+  auto to_lds = [&](unsigned char* dst, const u32x4 (&r)[NI]) {
+#pragma unroll
+    for (int i = 0; i < NI; ++i)
+      *reinterpret_cast<u32x4*>(dst + (RPI * i + lrow) * LSTR + 16 * lcol) = r[i];
+  };
+  // O rows 0-7 of this wave staged in K tile `wave`, rows 8-15 in K tile
+  // wave + 2 (tiles that only this wave writes)
+  auto o_stage = [&](int r) { return s_k[wave + 2 * (r >> 3)] + (r & 7) * OSTR; };
+
+  // partials of unit uu: rows ((b*M + r)*Hq + h)*nc + c; called after a
+  // barrier, when no wave reads the tiles any more
+  auto store_unit = [&](const f32x4 (&o)[DB], float m, float l, int uu) {
+    UnitM x;
+    decode(uu, x);
+    if (qd == 0 && qrow < R) {
+      const size_t prow =
+          (((size_t)x.b * a.M + qrow / G) * a.Hq + (size_t)x.kvh * G + qrow % G) * a.nc + x.c;
+      *reinterpret_cast<f32x2*>(a.ml_part + prow * 2) =
+          f32x2{(m == kNegInf) ? kNegInf : m * c_log2, l};
+    }
+    // lane (n, qd) holds O rows 4 qd + e, dims 16 db + n
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+        *reinterpret_cast<float*>(o_stage(4 * qd + e) + (16 * db + n) * 4) = o[db][e];
+#pragma unroll
+    for (int i = 0; i < 16 / ORPI; ++i) {
+      const int rr = ORPI * i + lane / LPO, cb = 16 * (lane % LPO);
+      const f32x4 v = *reinterpret_cast<const f32x4*>(o_stage(rr) + cb);
+      const int row = row0 + rr;
+      if (row < R) {
+        const size_t prow =
+            (((size_t)x.b * a.M + row / G) * a.Hq + (size_t)x.kvh * G + row % G) * a.nc + x.c;
+        *reinterpret_cast<f32x4*>(reinterpret_cast<unsigned char*>(a.o_part + prow * D) + cb) = v;
+      }
+    }
+  };
+
+  // workgroup w takes the consecutive units [w*per, (w+1)*per)
+  const int per = (n_units + (int)gridDim.x - 1) / (int)gridDim.x;
+  int u = (int)blockIdx.x * per;
+  const int u_end = min(u + per, n_units);
+  if (u >= n_units) return;   // both waves of the workgroup
+  UnitM cur;
+  decode(u, cur);
+  u32x4 kr[TW][NI], vr[TW][NI];
+  load_q(cur);
+  issue(base_of(a.k, cur), cur.c0, cur.c1, kr);
+  issue(base_of(a.v, cur), cur.c0, cur.c1, vr);
+  while (true) {
+    const int un = u + 1;
+    const bool has_next = un < u_end;
+    UnitM nxt = cur;
+    if (has_next) decode(un, nxt);
+    const int c0 = cur.c0, c1 = cur.c1;
+    const char* kb = base_of(a.k, cur);
+    const char* vb = base_of(a.v, cur);
+
+    f32x4 o[DB];
+    float m = kNegInf, l = 0.f;   // row's running maximum (raw), this lane's part of l
+#pragma unroll
+    for (int db = 0; db < DB; ++db) o[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int T = c0; T < c1; T += STEP) {
+      __syncthreads();   // the previous batch's tiles are read
+#pragma unroll
+      for (int j = 0; j < TW; ++j) {
+        to_lds(s_k[2 * j + wave], kr[j]);
+        to_lds(s_v[2 * j + wave], vr[j]);
+      }
+      // next batch's loads, the next unit's first after the last batch; one
+      // issue path (scalar selects), so that the compiler's wait counts
+      // agree on every path.  After the wave's last batch the limit is 0:
+      // the loads return zeros without touching memory.
+      const bool last = T + STEP >= c1;
+      const char* ks = kb;
+      const char* vs = vb;
+      int t_next = T + STEP, c_end = c1;
+      if (last) {
+        ks = base_of(a.k, nxt);
+        vs = base_of(a.v, nxt);
+        t_next = has_next ? nxt.c0 : T;
+        c_end = has_next ? nxt.c1 : T;
+      }
+      issue(ks, t_next, c_end, kr);
+      issue(vs, t_next, c_end, vr);
+      __syncthreads();   // the batch is in LDS
+
+      float sc[TT][4];
+#pragma unroll
+      for (int tt = 0; tt < TT; ++tt) {
+        // A operand of k-step s: dims 32 s + 8 qd .. +8 of K row n
+        f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < KS; ++s) {
+          const u32x4 ka = *reinterpret_cast<const u32x4*>(s_k[tt] + n * LSTR + 64 * s + 16 * qd);
+          acc = mfma_qk(ka, qf[s], acc);
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int pos = T + 16 * tt + 4 * qd + e;
+          sc[tt][e] = (pos < c1 && pos <= lim) ? acc[e] : kNegInf;
+        }
+      }
+      // the query of the next unit (qf is no longer needed for this one)
+      if (last && has_next) load_q(nxt);
+
+      float bm = kNegInf;
+#pragma unroll
+      for (int tt = 0; tt < TT; ++tt)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) bm = fmaxf(bm, sc[tt][e]);
+      bm = pair_max<32>(pair_max<16>(bm));
+      const float mn = fmaxf(m, bm);
+      if (__any(mn > m)) {
+        const float alpha = (mn == m) ? 1.f : exp2_hw((m - mn) * c_log2);
+        l *= alpha;
+        // O rows 4*qd + e take the factors of those rows (held by lanes 4*qd + e)
+        float ae[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) ae[e] = __shfl(alpha, 4 * qd + e);
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) o[db][e] *= ae[e];
+        m = mn;
+      }
+      // exponent (s - m) c: exactly 0 at the running maximum
+      const float base = (m == kNegInf) ? 0.f : m;
+      u32x2 ph[TT], pl[TT];
+#pragma unroll
+      for (int tt = 0; tt < TT; ++tt) {
+        float p[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          p[e] = exp2_hw((sc[tt][e] - base) * c_log2);
+          l += p[e];
+        }
+        split_bf16(p, ph[tt], pl[tt]);
+      }
+      // P V over pairs of tiles: k = 8 qd + j stands for position 4 qd + j % 4
+      // of tile 2 tp + j / 4
+#pragma unroll
+      for (int tp = 0; tp < TT / 2; ++tp) {
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+          const u32x2 v0 = __builtin_bit_cast(
+              u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                         (__attribute__((address_space(3))) s16x4_t*)(s_v[2 * tp] + tr_off + 32 * db)));
+          const u32x2 v1 = __builtin_bit_cast(
+              u32x2,
+              __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                  (__attribute__((address_space(3))) s16x4_t*)(s_v[2 * tp + 1] + tr_off + 32 * db)));
+          const u32x4 vv = u32x4{v0.x, v0.y, v1.x, v1.y};
+          const u32x2 h0 = ph[2 * tp], h1 = ph[2 * tp + 1];
+          const u32x2 l0 = pl[2 * tp], l1 = pl[2 * tp + 1];
+          o[db] = mfma_qk(u32x4{h0.x, h0.y, h1.x, h1.y}, vv, o[db]);
+          o[db] = mfma_qk(u32x4{l0.x, l0.y, l1.x, l1.y}, vv, o[db]);
+        }
+      }
+    }
+    // l of row n: the four lanes of the row hold parts
+    l = pair_sum<32>(pair_sum<16>(l));
+    __syncthreads();   // no wave reads the tiles any more
+    store_unit(o, m, l, u);
+    if (!has_next) break;
+    cur = nxt;
+    u = un;
+  }
+}
+
+// Units that run at once: one per workgroup (wave pair).
+template <int D>
+size_t pair_slots() {
+  static const int per_cu = [] {
+    int nb = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, multi_pair_kernel<D>, 2 * kWave, 0) !=
+            hipSuccess ||
+        nb <= 0)
+      nb = 1;
+    return nb;
+  }();
+  return (size_t)cu_count() * per_cu;
+}
+
+template <int D>
+hipError_t launch_pair(const MultiArgs& a, hipStream_t s) {
+  auto kernel = multi_pair_kernel<D>;
+  // equal rounds for every workgroup
+  const size_t units = (size_t)a.B * a.Hkv * a.nc;
+  const size_t slots = pair_slots<D>();
+  const size_t rounds = (units + slots - 1) / slots;
+  const unsigned grid = (unsigned)((units + rounds - 1) / rounds);
+  hipLaunchKernelGGL(kernel, dim3(grid), dim3(2 * kWave), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+size_t multi_pair_slots(int D) { return D == 64 ? pair_slots<64>() : pair_slots<128>(); }
+
+hipError_t launch_multi_pair(int D, const MultiArgs& a, hipStream_t s) {
+  if (D == 64) return launch_pair<64>(a, s);
+  if (D == 128) return launch_pair<128>(a, s);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace fdk

@@ -81,8 +81,9 @@ def test_multi_row_full_size():
 
 
 def test_multi_row_two_query_tiles_full_size():
-    """Headline shape with eight new tokens per sequence (G*M = 32 rows: two
-    query tiles sharing every K and V tile): every row."""
+    """Headline shape with eight new tokens per sequence (G*M = 32 rows: a
+    pair of waves, one query tile each, sharing every K and V tile through
+    LDS): every row.  64 chunks of 512 per row fold into splits of 4."""
     banner("multi full size B=8 L=32768 M=8")
     c = W.multi_case(8, 8, 32, 8, 32768, 128, seed=108, device=DEV)
     _check(c, chunk=512)
@@ -92,17 +93,18 @@ def test_multi_row_two_query_tiles_full_size():
 # streams a row's whole fp64 K and V prefix for every row (64 MB per row at
 # L 32768, 2 GB at 2^20), so every row would take minutes of host time; the
 # two headline-shape tests above check every row.
-def test_multi_row_many_units_per_wave_sampled():
-    """Chunks of 32 at the headline shape: 16,384 units, so every wave
-    finishes many units and writes its held partials several times."""
+def test_multi_row_small_chunks_folded_sampled():
+    """Chunks of 32 at the headline shape: 1,024 chunks per row, folded into
+    splits of 64 chunks (one split per wave slot)."""
     banner("multi full size B=8 L=32768 M=4 chunk=32")
     c = W.multi_case(8, 4, 32, 8, 32768, 128, seed=103, device=DEV)
     rows = [(0, 0, 0), (1, 3, 31), (4, 2, 9), (6, 1, 20), (7, 3, 2)]
     _check(c, chunk=32, rows=rows)
 
 
-def test_multi_row_many_units_two_query_tiles_sampled():
-    """As above with two query tiles (G*M = 32) and a ragged last chunk."""
+def test_multi_row_small_chunks_two_query_tiles_sampled():
+    """Chunks of 48 with G*M = 32 rows (wave pairs) and a ragged last chunk:
+    417 chunks per row, folded into splits whose last one is ragged."""
     banner("multi B=4 L=20000 M=8 chunk=48")
     c = W.multi_case(4, 8, 32, 8, 20000, 128, seed=109, device=DEV)
     rows = [(0, 0, 0), (1, 7, 31), (2, 4, 16), (3, 6, 5)]
@@ -117,3 +119,21 @@ def test_multi_row_one_million_positions_sampled(M):
     c = W.multi_case(1, M, 16, 4, (1 << 20) + 3, 128, seed=1208 + M, device=DEV)
     rows = [(0, 0, 0), (0, M - 1, 15), (0, M // 2, 6)]
     _check(c, chunk=512, rows=rows)
+
+
+@pytest.mark.parametrize("M,L,chunk", [(4, 100, 128), (8, 100, 128), (4, 1000, 128),
+                                       (8, 1000, 128), (8, 300, 32)])
+def test_multi_row_more_rows_than_wave_slots(M, L, chunk):
+    """More (sequence, kv-head) rows than the device runs at once (8,192 or
+    2,048 rows of G = 4 heads; 1,024 wave slots for one query tile, 1,024
+    wave pairs for two): every wave or pair takes several units in a row,
+    holds finished partials, crosses from one row to the next and prefetches
+    the next unit's query and keys; with 300 positions in chunks of 32 a
+    split of 5 chunks crosses rows mid-way.  Sampled rows, first and last
+    sequences included."""
+    banner(f"multi many rows M={M} L={L} chunk={chunk}")
+    B = 256 if L <= 128 else (64 if L == 1000 else 48)
+    c = W.multi_case(B, M, 128, 32, L, 128, seed=1300 + M + L, device=DEV)
+    rows = [(0, 0, 0), (0, M - 1, 127), (B // 2, M // 2, 64), (B // 2 + 1, 1, 3),
+            (B - 1, M - 1, 127), (B - 1, 0, 77)]
+    _check(c, chunk=chunk, rows=rows)
