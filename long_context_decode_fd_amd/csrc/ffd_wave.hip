@@ -1,14 +1,15 @@
 // FFD sparse decode, streamed by single wavefronts (d = 128, G = 4 or 8):
 // the 2-bit scan, top-delta selection, 8-bit refine and exact attention of
 // the "Faster Than Flash" digest (longzhangge.com, sections 3, 5 and 6,
-// Fig. 2) for one chunk per wavefront, fused, with no barrier and no
-// intermediate written to memory, the pseudo-maximum m^ and its anchor j*
-// (section 4) included.
+// Fig. 2) for one chunk per wavefront, fused, with no intermediate written
+// to memory, the pseudo-maximum m^ and its anchor j* (section 4) included.
 //
 // A wavefront owns one unit = (sequence, kv-head, chunk).  It first scores
 // the anchor positions (the first n_sink and the last n_local positions of
-// its sequence) with the refined keys, as below, for m^ and j*, then walks
-// its chunk in steps of kStep positions:
+// its sequence) with the refined keys, as below, for m^ and j* -- split
+// over the four waves of the workgroup when they share a (sequence,
+// kv-head), the kernel's one barrier -- then walks its chunk in steps of
+// kStep positions:
 //   * Scan.  Codes and (zero, step) of a step's 8 tiles of 16 positions come
 //     through buffer loads (one lane offset plus an immediate per tile).
 //     Codes become exact bf16 values 4 + c; v_mfma_f32_16x16x32_bf16 with the
@@ -104,6 +105,8 @@ void ffd_wave_kernel(FfdArgs a) {
   __shared__ int s_pos[kWaves][kRing];                       // position within the chunk
   __shared__ __align__(16) unsigned char s_vt[kWaves][2][16 * kVStr];
   __shared__ __align__(16) float s_pb[kWaves][G][32];
+  __shared__ float s_am[kWaves][G];   // anchors: each wave's best score per head
+  __shared__ int s_aj[kWaves][G];     // and its lowest position
 
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & (kWave - 1);
   const int n16 = lane & 15, qg = lane >> 4;
@@ -428,11 +431,19 @@ void ffd_wave_kernel(FfdArgs a) {
   // steps' loads travel: the refined scores of the anchor positions -- the
   // first n_sink and the last n_local positions, a set -- for this lane's
   // heads, computed as in the scan and the refine; m^ = their maximum and
-  // j* the lowest position attaining it.  Every wave of a (sequence,
+  // j* the lowest position attaining it.  Every workgroup of a (sequence,
   // kv-head) reads the same anchor rows (cache-resident after the first)
-  // and computes the same values.  The next tile's rows are loaded before
-  // the current tile's products ----
+  // and computes the same values.  A workgroup's units are consecutive
+  // chunks: when its four waves share one (sequence, kv-head), wave w
+  // scores the anchor tiles w, w + 4, ... and the four results meet in LDS
+  // (the maximum with the lowest position is a total order, so the result
+  // does not depend on the split); otherwise each wave scores all of them.
+  // The next tile's rows are loaded before the current tile's products ----
   {
+    const int u_first = (int)blockIdx.x * kWaves;
+    const bool share = u_first + kWaves <= a.B * a.Hkv * a.nc &&
+                       u_first / a.nc == (u_first + kWaves - 1) / a.nc;   // workgroup-uniform
+    const int t_step = share ? kWaves : 1;
     const int n_sk = min(a.n_sink, a.L), loc0 = max(n_sk, a.L - a.n_local);
     const int na = n_sk + (a.L - loc0);
     const size_t row0 = rbase - c0;   // row of position 0
@@ -461,9 +472,10 @@ void ffd_wave_kernel(FfdArgs a) {
       A.rs = a.rs[row * NG + qg];
     };
     AnchorRows cur, nxt;
-    anchor_load(0, cur);
-    for (int k0 = 0; k0 < na; k0 += 16) {   // wave-uniform
-      anchor_load(min(k0 + 16, na - 1), nxt);
+    const int k_first = share ? 16 * wave : 0;
+    anchor_load(min(k_first, na - 1), cur);
+    for (int k0 = k_first; k0 < na; k0 += 16 * t_step) {   // wave-uniform
+      anchor_load(min(k0 + 16 * t_step, na - 1), nxt);
       u32x4 bq[4];
       code_operands(cur.cw, bq);
       float sc[NT], corr[NT];
@@ -492,6 +504,30 @@ void ffd_wave_kernel(FfdArgs a) {
         if (ob > mbest[tt] || (ob == mbest[tt] && oj < jbest[tt])) {
           mbest[tt] = ob;
           jbest[tt] = oj;
+        }
+      }
+    }
+    if (share) {
+      if (n16 == 0) {
+#pragma unroll
+        for (int tt = 0; tt < NT; ++tt) {
+          s_am[wave][4 * tt + qg] = mbest[tt];
+          s_aj[wave][4 * tt + qg] = jbest[tt];
+        }
+      }
+      __syncthreads();
+#pragma unroll
+      for (int tt = 0; tt < NT; ++tt) {
+        mbest[tt] = s_am[0][4 * tt + qg];
+        jbest[tt] = s_aj[0][4 * tt + qg];
+#pragma unroll
+        for (int w = 1; w < kWaves; ++w) {
+          const float ob = s_am[w][4 * tt + qg];
+          const int oj = s_aj[w][4 * tt + qg];
+          if (ob > mbest[tt] || (ob == mbest[tt] && oj < jbest[tt])) {
+            mbest[tt] = ob;
+            jbest[tt] = oj;
+          }
         }
       }
     }
