@@ -12,7 +12,8 @@
 // kStep positions:
 //   * Scan.  Codes and (zero, step) of a step's 8 tiles of 16 positions come
 //     through buffer loads (one lane offset plus an immediate per tile).
-//     Codes become exact bf16 values 4 + c; v_mfma_f32_16x16x32_bf16 with the
+//     Codes become exact fp16 values 4 + c and the query fp16 after an exact
+//     power-of-two scaling; v_mfma_f32_16x16x32_f16 with the
 //     query groups stacked block-diagonally gives each lane (position n,
 //     quad g) the group-g dot products of heads 4tt .. 4tt+3, and a
 //     transposed reduction over the four quads (two v_permlane32_swap, one
@@ -24,15 +25,16 @@
 //     scalar registers) the positions that need a refine.  Those positions
 //     and their per-head scan scores (-inf where a head did not select the
 //     position) are appended to a ring in this wave's LDS.
-//   * Refine + attend, 16 ring entries per tile, while the next step's scan
-//     loads are in flight: residual bytes as exact bf16 r + 128 in the same
-//     group-stacked tile (refinement = rs_g (C - 128 qsum), reduced the same
-//     transposed way), online softmax per head over the tile, P V on
-//     v_mfma_f32_16x16x16_bf16 with p split bf16 hi + lo and the candidates'
-//     V rows read back transposed from an LDS tile.  The next tile's loads
-//     are issued as soon as the current tile's registers are free.  A step
-//     refines only full tiles; the rest waits in the ring for the next step
-//     (the last step refines everything).
+//   * Refine + attend, pairs of up to 32 ring entries (two tiles of 16),
+//     while the next steps' scan loads are in flight: residual bytes as
+//     exact fp16 1152 + r (one byte permute per pair of dims) in the same
+//     group-stacked tile (refinement = rs_g (C - 1152 qsum), reduced the
+//     same transposed way), online softmax per head over the pair, P V on
+//     v_mfma_f32_16x16x32_bf16 over both tiles with p split bf16 hi + lo and
+//     the candidates' V rows read back transposed from LDS.  The next
+//     pair's loads are issued as soon as the current pair's registers are
+//     free.  After each half-step the entries appended before it are
+//     refined; the last entries after the walk.
 //   * One partial (O, m, l) per query head at the end; the chunks merge in
 //     the common log-sum-exp kernel.
 #include "ffd_common.hpp"
@@ -117,23 +119,29 @@ void ffd_wave_kernel(FfdArgs a) {
   const int c0 = c * a.chunk, n = min(c0 + a.chunk, a.L) - c0;
   const size_t rbase = ((size_t)b * a.Hkv + kvh) * (size_t)a.L + c0;   // row of position c0
   const size_t hq0 = (size_t)b * a.Hq + (size_t)kvh * G;
-  const float cl2 = a.c_log2;
 
+  // The query as fp16, scaled by pw = 2^k (exact; see stacked_query_f16):
+  // every score below is pw times the unscaled one, bit for bit, so
+  // thresholds and maxima live in the scaled units and the softmax exponent
+  // takes c log2 e / pw.  Set up after the first anchor and scan loads are
+  // issued (below).
+  float pw = 1.f, ipw = 1.f, cl2 = a.c_log2;
   u32x4 qa[NT][4];
   float qsum[NT][4];
-  stacked_query<G>(a.q + hq0 * D, lane, qa, qsum);
   // this lane's heads 4 tt + qg: threshold m^ - delta and j* (within the
   // chunk), set from the anchors below
   float thr[NT];
   int jst[NT];
-  // constants of the code -> bf16 conversion, held in registers so that one
-  // v_and_or_b32 applies both (its encoding takes no literal)
-  uint32_t k_mask = 0x00600060u, k_exp = 0x40804080u;
+  // constants of the code and residual -> fp16 conversions, held in
+  // registers (v_and_or_b32 takes no literal; v_perm_b32 takes the
+  // exponent byte from a register)
+  uint32_t k_mask = 0x03000300u, k_exp = 0x44004400u, k64 = 0x64646464u;
   asm volatile("" : "+s"(k_mask));
   asm volatile("" : "+v"(k_exp));
+  asm volatile("" : "+v"(k64));
 
   // ---- operands and dot products shared by the anchors, the scan and the
-  // refine.  Codes of a (position, group): the bf16 pairs 4 + c of k-steps
+  // refine.  Codes of a (position, group): the fp16 pairs 4 + c of k-steps
   // 0 .. 3; (zero, step): the group's part of the 2-bit score of head
   // 4 tt + qg after the transposed reduction ----
   auto code_operands = [&](const u32x2& cwv, u32x4 (&bq)[4]) {
@@ -141,12 +149,9 @@ void ffd_wave_kernel(FfdArgs a) {
     for (int k = 0; k < 4; ++k) {
       const uint32_t w = k < 2 ? cwv.x : cwv.y;
       const int pbit = 4 * (k & 1);
-      uint32_t pr[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        pr[j] = (__builtin_amdgcn_alignbit(w, w, (uint32_t)((2 * (pbit + j) - 5) & 31)) &
-                 k_mask) | k_exp;
-      bq[k] = u32x4{pr[0], pr[1], pr[2], pr[3]};
+      bq[k] = u32x4{code_pair_f16(w, pbit, k_mask, k_exp), code_pair_f16(w, pbit + 1, k_mask, k_exp),
+                    code_pair_f16(w, pbit + 2, k_mask, k_exp),
+                    code_pair_f16(w, pbit + 3, k_mask, k_exp)};
     }
   };
   auto scan_scores = [&](const u32x4 (&bq)[4], uint32_t zzv, float (&sc)[NT]) {
@@ -156,20 +161,20 @@ void ffd_wave_kernel(FfdArgs a) {
     for (int tt = 0; tt < NT; ++tt) {
       f32x4 cc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int k = 0; k < 4; ++k) cc = mfma_16x16x32(qa[tt][k], bq[k], cc);
+      for (int k = 0; k < 4; ++k) cc = mfma_16x16x32_f16(qa[tt][k], bq[k], cc);
       float part[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) part[e] = fmaf(zb, qsum[tt][e], st * cc[e]);
       sc[tt] = quad_transpose_sum(part);
     }
   };
-  // residual bytes of a (position, group) as exact bf16 r + 128, and the
-  // refinement rs_g (sum q (r + 128) - 128 qsum) summed over the groups
+  // residual bytes of a (position, group) as exact fp16 1152 + r, and the
+  // refinement rs_g (sum q (1152 + r) - 1152 qsum) summed over the groups
   auto residual_operands = [&](const u32x4& ra, const u32x4& rb, u32x4 (&bq)[4]) {
     const uint32_t w[8] = {ra.x, ra.y, ra.z, ra.w, rb.x, rb.y, rb.z, rb.w};
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
-      const u32x2 lo = residual_pairs(w[2 * t]), hi = residual_pairs(w[2 * t + 1]);
+      const u32x2 lo = residual_pairs_f16(w[2 * t], k64), hi = residual_pairs_f16(w[2 * t + 1], k64);
       bq[t] = u32x4{lo.x, lo.y, hi.x, hi.y};
     }
   };
@@ -178,10 +183,10 @@ void ffd_wave_kernel(FfdArgs a) {
     for (int tt = 0; tt < NT; ++tt) {
       f32x4 cc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int t = 0; t < 4; ++t) cc = mfma_16x16x32(qa[tt][t], bq[t], cc);
+      for (int t = 0; t < 4; ++t) cc = mfma_16x16x32_f16(qa[tt][t], bq[t], cc);
       float part[4];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) part[e] = rsf * fmaf(-128.f, qsum[tt][e], cc[e]);
+      for (int e = 0; e < 4; ++e) part[e] = rsf * fmaf(-1152.f, qsum[tt][e], cc[e]);
       corr[tt] = quad_transpose_sum(part);
     }
   };
@@ -424,8 +429,6 @@ void ffd_wave_kernel(FfdArgs a) {
   ScanRegs<kTiles> sA, sB;
   PairRegs P;
   int head = 0, plim = 0;
-  scan_issue(sA, 0);
-  scan_issue(sB, 1);
 
   // ---- pseudo-maximum (FFD digest, section 4), while the first two scan
   // steps' loads travel: the refined scores of the anchor positions -- the
@@ -438,7 +441,7 @@ void ffd_wave_kernel(FfdArgs a) {
   // scores the anchor tiles w, w + 4, ... and the four results meet in LDS
   // (the maximum with the lowest position is a total order, so the result
   // does not depend on the split); otherwise each wave scores all of them.
-  // The next tile's rows are loaded before the current tile's products ----
+  // Anchor rows are loaded one tile ahead of the products ----
   {
     const int u_first = (int)blockIdx.x * kWaves;
     const bool share = u_first + kWaves <= a.B * a.Hkv * a.nc &&
@@ -473,9 +476,22 @@ void ffd_wave_kernel(FfdArgs a) {
     };
     AnchorRows cur, nxt;
     const int k_first = share ? 16 * wave : 0;
+    // the query, the first two anchor tiles and the first two scan steps,
+    // requested in the order they are needed: the vector-memory counter
+    // completes in issue order, so each wait covers only what came before
+    // (the scan loads after the query's: at kernel start every wave
+    // requests at once, and the query came back 1.5 us sooner so)
+    u32x4 qraw[NT][4];
+    query_load<G>(a.q + hq0 * D, lane, qraw);
+    const int kst = 16 * t_step;   // anchor tiles k_first, k_first + kst, ...
     anchor_load(min(k_first, na - 1), cur);
-    for (int k0 = k_first; k0 < na; k0 += 16 * t_step) {   // wave-uniform
-      anchor_load(min(k0 + 16 * t_step, na - 1), nxt);
+    anchor_load(min(k_first + kst, na - 1), nxt);
+    pw = stacked_query_f16<G>(qraw, lane, qa, qsum);
+    ipw = 1.f / pw;   // a power of two: exact
+    cl2 = a.c_log2 * ipw;
+    scan_issue(sA, 0);
+    scan_issue(sB, 1);
+    for (int k0 = k_first; k0 < na; k0 += kst) {   // wave-uniform
       u32x4 bq[4];
       code_operands(cur.cw, bq);
       float sc[NT], corr[NT];
@@ -492,6 +508,7 @@ void ffd_wave_kernel(FfdArgs a) {
         }
       }
       cur = nxt;
+      if (k0 + 2 * kst < na) anchor_load(k0 + 2 * kst, nxt);   // wave-uniform
     }
     // (largest score, then lowest position) over the 16 lanes of a quad;
     // the order is total, so every lane ends with the same pair
@@ -533,10 +550,10 @@ void ffd_wave_kernel(FfdArgs a) {
     }
 #pragma unroll
     for (int tt = 0; tt < NT; ++tt) {
-      thr[tt] = mbest[tt] - a.delta_raw;
+      thr[tt] = mbest[tt] - a.delta_raw * pw;
       jst[tt] = jbest[tt] - c0;
       if (a.pseudo_max != nullptr && c == 0 && n16 == 0)
-        a.pseudo_max[hq0 + 4 * tt + qg] = mbest[tt] * a.scale;
+        a.pseudo_max[hq0 + 4 * tt + qg] = (mbest[tt] * ipw) * a.scale;
     }
   }
 
