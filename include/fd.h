@@ -197,7 +197,13 @@ int fd_decode_attn_unified_max(fd_dtype_t dt, const void* q, const void* k,
  *   out   fp32 [B, M, Hq, d];  lse fp32 [B, M, Hq] or NULL
  *   M = 1: dt bf16 or fp32.  M >= 2: bf16 only and G*M <= 32, else
  *   FD_ERR_UNSUPPORTED.  Workspace: chunk partials of the B*M*Hq rows
- *   (same layout as fd_decode_attn_partials with M*Hq heads).
+ *   (same layout as fd_decode_attn_partials with M*Hq heads), sized for
+ *   `chunk`.  For M >= 2, chunk is the split granule: when the rows' chunks
+ *   outnumber what the device runs at once, one split covers F consecutive
+ *   chunks, F chosen for the fewest rounds of splits (the latency estimate
+ *   of the "Flash Decoding" explainer, section 2: splits beyond the
+ *   hardware's parallelism only add merge work).  The result is the same up
+ *   to fp32 rounding.
  *   chunk: each chunk writes G*M partial rows of (d + 2) floats per kv-head
  *   and the merge reads them back, so large M favours long chunks (on
  *   MI355X at L = 32768, B = 8: 2048 beat 512 by 4 % at M = 2 and 12 % at
