@@ -77,6 +77,23 @@ __device__ __forceinline__ float lane_value(float x, int src) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), src));
 }
 
+// Two waves share each SIMD (two workgroups per compute unit), and the
+// hardware issues for the older one first: with equal work the younger
+// workgroup finished 8 us (peaked scores) to 28 us (iid) after the older on
+// every compute unit, then ran alone at one wave per SIMD.  Each wave
+// therefore raises its issue priority (s_setprio) in alternate 5.12 us
+// slices of the 100 MHz clock, the two waves of a SIMD (hardware wave slots
+// 0 and 1) in opposite slices: the end gap fell to 3 us (peaked) and 12 us
+// (iid); iid 150.8 -> 148.9 us per call, peaked unchanged (same process,
+// interleaved).
+__device__ __forceinline__ void fair_share_priority(uint32_t slot) {
+  const uint64_t t = __builtin_amdgcn_s_memrealtime();
+  if ((((uint32_t)(t >> 9)) ^ slot) & 1u)
+    __builtin_amdgcn_s_setprio(1);
+  else
+    __builtin_amdgcn_s_setprio(0);
+}
+
 // Registers of one scan step: tile t's codes and (zero, step) of position
 // 16 t + n16, quantisation group qg.
 template <int T>
@@ -560,8 +577,11 @@ void ffd_wave_kernel(FfdArgs a) {
   res_issue(P, 0, 0);   // an empty pair: its loads read nothing
   v_issue(P, 0, 0);
 
+  // hardware wave slot within the SIMD (HW_ID bits 3:0)
+  const uint32_t wslot = __builtin_amdgcn_s_getreg((3 << 11) | 4) & 1u;
   auto refine_until = [&](int mark) __attribute__((always_inline)) {
     while (head < mark) {   // wave-uniform
+      fair_share_priority(wslot);
       const int nx = min(head + 32, plim);
       refine_pair(P, head, plim, nx, tail);
       head = nx;
@@ -580,10 +600,12 @@ void ffd_wave_kernel(FfdArgs a) {
   // leaves the other step's loads in flight instead of draining them all.
   for (int s = 0; s < nsteps; s += 2) {
     int mark = tail;
+    fair_share_priority(wslot);
     scan_step(sA, s);
     scan_issue(sA, s + 2);
     refine_until(mark);
     mark = tail;
+    fair_share_priority(wslot);
     scan_step(sB, s + 1);
     scan_issue(sB, s + 3);
     refine_until(mark);
