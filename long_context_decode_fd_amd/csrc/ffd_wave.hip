@@ -48,7 +48,10 @@ template <int G>
 constexpr int scan_tiles() { return G == 4 ? 8 : 4; }
 // ring entries per wave: at most two steps of entries wait for a refine
 constexpr int kRing = 256;
-constexpr int kVStr = 2 * 128 + 8;        // LDS row stride of a V tile (bytes)
+// LDS row stride of a V tile (bytes): row r starts 8 r banks on, so the
+// transposing 8-byte reads never share a bank (an 8-byte padding had 4x
+// conflicts)
+constexpr int kVStr = 2 * 128 + 32;
 }  // namespace
 
 // out = lanes' sum of x over the quad pair {g, g ^ 2} for lanes of quads 0
