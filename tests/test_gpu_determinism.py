@@ -61,6 +61,17 @@ def test_multi_repeatable(M):
     _same_every_time(lambda: fd.decode_attn_multi(c.q, c.k, c.v, chunk=48))
 
 
+@pytest.mark.parametrize("M", [4, 8])
+def test_multi_many_units_repeatable(M):
+    """More (sequence, kv-head) rows than wave slots (256 sequences x 32
+    kv-heads): each wave, or wave pair, takes 8 units in a row, so partials
+    are held, staged through LDS and written between units, and the next
+    unit's query and keys are requested across the boundary."""
+    banner(f"determinism multi many units M={M}")
+    c = W.multi_case(256, M, 128, 32, 100, 128, seed=960 + M, device=DEV)
+    _same_every_time(lambda: fd.decode_attn_multi(c.q, c.k, c.v, chunk=128))
+
+
 def test_paged_repeatable():
     banner("determinism paged")
     lens = [0, 17, 1000, 5000, 16 * 300 + 3, 64]
