@@ -53,8 +53,9 @@ def test_ffd_repeatable(d, G, chunk):
 
 @pytest.mark.parametrize("M", [2, 4, 8])
 def test_multi_repeatable(M):
-    """Multi-row kernel: one query tile (M 2, 4) and two (M 8), per-wave LDS
-    tiles and the transposing read."""
+    """Multi-row kernels: one query tile per wave (M 2, 4: per-wave LDS
+    tiles) and the wave pair (M 8: tiles shared through LDS behind barriers),
+    with the transposing read."""
     banner(f"determinism multi M={M}")
     c = W.multi_case(2, M, 32, 8, 6000, 128, seed=920 + M, device=DEV)
     _same_every_time(lambda: fd.decode_attn_multi(c.q, c.k, c.v, chunk=512))

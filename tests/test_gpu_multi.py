@@ -114,7 +114,7 @@ def test_multi_row_small_chunks_two_query_tiles_sampled():
 @pytest.mark.parametrize("M", [4, 8])
 def test_multi_row_one_million_positions_sampled(M):
     """M new tokens at the end of a cache of 2^20 + 3 positions (2,049 chunks
-    of 512): one and two query tiles."""
+    of 512): one query tile and the wave pair."""
     banner(f"multi 1M M={M}")
     c = W.multi_case(1, M, 16, 4, (1 << 20) + 3, 128, seed=1208 + M, device=DEV)
     rows = [(0, 0, 0), (0, M - 1, 15), (0, M // 2, 6)]
