@@ -644,6 +644,72 @@ __global__ __launch_bounds__(W * kWave) void merge_kernel(MergeArgs a) {
   }
 }
 
+// The same merge for rows of at most 64 chunks on one wavefront per
+// (row, column slice of D / CS floats), with no barrier and no LDS: lane c
+// holds chunk c's (m, l), the maximum and the denominator are wave
+// reductions, lane (cl, cg) sums chunks cl, cl + CL, ... of its 4 columns
+// (every O load issued before the maximum is known) with the weights taken
+// from the chunks' lanes, and the CL chunk lanes of a column group add up
+// through pair exchanges.  Fixed summation order.
+template <int D, int CS>
+__global__ __launch_bounds__(kWave) void merge_wave_kernel(MergeArgs a) {
+  constexpr int CG = D / 4 / CS;   // 16-byte column groups of the slice
+  constexpr int CL = kWave / CG;   // chunk lanes
+  constexpr int KP = kWave / CL;   // chunks per lane (64 chunks at most)
+  static_assert(CL == 2 || CL == 4 || CL == 8, "chunk lanes");
+  const int lane = threadIdx.x;
+  const int cl = lane / CG, cg = lane % CG;
+  const size_t row = blockIdx.x / CS;
+  const int cs = (int)(blockIdx.x % CS);
+  int n = a.nc;
+  if (a.seq_lens != nullptr) {
+    const int b = (int)(row / a.Hq);
+    const int L = min(max(a.seq_lens[b], 0), a.max_seq_len);
+    n = min((L + a.chunk - 1) / a.chunk, a.nc);
+  }
+  if (n == 0) {   // wave-uniform
+    for (int c = lane; c < D / CS; c += kWave) a.out[row * D + cs * (D / CS) + c] = 0.f;
+    if (lane == 0 && cs == 0 && a.lse != nullptr) a.lse[row] = kNegInf;
+    return;
+  }
+  const f32x4* op = reinterpret_cast<const f32x4*>(a.o_part + row * a.nc * D) + cs * CG + cg;
+  const f32x2* mlp = reinterpret_cast<const f32x2*>(a.ml_part + row * a.nc * 2);
+  f32x4 o[KP];
+#pragma unroll
+  for (int j = 0; j < KP; ++j) {
+    const int k = cl + j * CL;
+    o[j] = k < n ? op[(size_t)k * (D / 4)] : f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  const f32x2 ml = lane < n ? mlp[lane] : f32x2{kNegInf, 0.f};
+  const float M = wave_max(ml.x);
+  const float w = lane < n ? exp2_diff(ml.x, M) : 0.f;
+  const float den = wave_sum(w * ml.y);
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int j = 0; j < KP; ++j) {
+    const int k = cl + j * CL;
+    const float wk = __shfl(w, k);
+    acc.x = fmaf(wk, o[j].x, acc.x);
+    acc.y = fmaf(wk, o[j].y, acc.y);
+    acc.z = fmaf(wk, o[j].z, acc.z);
+    acc.w = fmaf(wk, o[j].w, acc.w);
+  }
+  // chunk lane cl of column group cg is lane cl * CG + cg
+  auto sum_lanes = [&](float x) {
+    if constexpr (CL >= 8) x = pair_sum<8>(x);
+    if constexpr (CL >= 4) x = pair_sum<16>(x);
+    return pair_sum<32>(x);
+  };
+  acc.x = sum_lanes(acc.x);
+  acc.y = sum_lanes(acc.y);
+  acc.z = sum_lanes(acc.z);
+  acc.w = sum_lanes(acc.w);
+  if (cl == 0)
+    reinterpret_cast<f32x4*>(a.out + row * D)[cs * CG + cg] =
+        f32x4{acc.x / den, acc.y / den, acc.z / den, acc.w / den};
+  if (lane == 0 && cs == 0 && a.lse != nullptr) a.lse[row] = (M + log2_hw(den)) * kLn2;
+}
+
 int cu_count() {
   static std::atomic<int> cached[64];
   int dev = 0;
@@ -725,6 +791,19 @@ hipError_t launch_partial(int mode, int is_bf16, int D, int G, const PartialArgs
 
 hipError_t launch_merge(int D, int B, const MergeArgs& a, hipStream_t s) {
   const size_t rows = (size_t)B * a.Hq;
+  // rows of at most 64 chunks: one wave per (row, column slice)
+  if (a.nc <= 64) {
+    if (D == 128 && a.nc <= 32) {
+      hipLaunchKernelGGL((merge_wave_kernel<128, 1>), dim3((unsigned)rows), dim3(kWave), 0, s, a);
+    } else if (D == 128) {
+      hipLaunchKernelGGL((merge_wave_kernel<128, 2>), dim3((unsigned)(rows * 2)), dim3(kWave), 0, s, a);
+    } else if (D == 64) {
+      hipLaunchKernelGGL((merge_wave_kernel<64, 1>), dim3((unsigned)rows), dim3(kWave), 0, s, a);
+    } else {
+      return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+  }
   // Rows of 64 chunks or more split their columns over 2 workgroups, rows
   // of 128 or more over 4 (of 4 waves each): more workgroups in flight for
   // the same latency-bound walk over the chunks.

@@ -178,10 +178,12 @@ def test_merge_of_many_chunks(d):
 
 
 @pytest.mark.parametrize("d", [64, 128])
-@pytest.mark.parametrize("nc", [63, 64, 100, 127, 128])
+@pytest.mark.parametrize("nc", [1, 2, 32, 33, 63, 64, 65, 100, 127, 128])
 def test_merge_tier_edges(d, nc):
-    """Rows of 63 / 64-127 / 128+ chunks take the merge with its columns in
-    1 / 2 / 4 workgroups; the last chunk is ragged."""
+    """Each side of every merge tier: rows of up to 64 chunks on one
+    wavefront (d 128: its columns on 1 wavefront up to 32 chunks, on 2 from
+    33), rows of 65-127 on two 4-wave workgroups, 128 and more on four; the
+    last chunk is ragged."""
     banner(f"dense merge tiers d={d} nc={nc}")
     c = W.dense_case(2, 8, 2, 16 * (nc - 1) + 7, d, "bf16", 16, seed=300 + nc + d, device=DEV)
     _check(c)
