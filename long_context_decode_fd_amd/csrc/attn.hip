@@ -525,14 +525,15 @@ void partial_kernel(PartialArgs a) {
 // section 2, steps 2-4, with unnormalised O_i):
 //   M = max_i m_i,  w_i = 2^(m_i - M),
 //   out = sum_i w_i O_i / sum_i w_i l_i,  lse = (M + log2 sum_i w_i l_i) ln 2.
-// One workgroup of W waves per (sequence, query head).  The weights of up to
-// 64 W chunks at a time go to LDS; thread (chunk lane cl, column group cg)
-// then sums chunks cl, cl + CL, ... of 4 columns with independent 16-byte
-// loads, 16 W chunks at a time (the loads of the first 16 W are issued
-// before the maximum is known), and the chunk lanes are reduced through LDS.
-// Rows of many chunks split their columns over CS workgroups, so that
-// more loads share one memory latency.  The order of every sum is fixed, so runs are bitwise
-// reproducible.  Rows whose chunks all carry the same m (the fixed-maximum
+// This kernel takes rows of more than 256 chunks (shorter rows take
+// merge_wave_kernel below): one workgroup of W waves per (sequence, query
+// head, slice of D / CS columns), so that more loads share one memory
+// latency.  The weights of up to 64 W chunks at a time go to LDS; thread
+// (chunk lane cl, column group cg) then sums chunks cl, cl + CL, ... of 4
+// columns with independent 16-byte loads, 16 W CS chunks at a time (the
+// loads of the first group are issued before the maximum is known), and the
+// chunk lanes are reduced through LDS.  The order of every sum is fixed, so
+// runs are bitwise reproducible.  Rows whose chunks all carry the same m (the fixed-maximum
 // path without fallback) get weights of exactly 1.
 template <int D, int W, int CS>
 __global__ __launch_bounds__(W * kWave) void merge_kernel(MergeArgs a) {
@@ -644,19 +645,20 @@ __global__ __launch_bounds__(W * kWave) void merge_kernel(MergeArgs a) {
   }
 }
 
-// The same merge for rows of at most 64 chunks on one wavefront per
+// The same merge for rows of at most 64 NM chunks on one wavefront per
 // (row, column slice of D / CS floats), with no barrier and no LDS: lane c
-// holds chunk c's (m, l), the maximum and the denominator are wave
-// reductions, lane (cl, cg) sums chunks cl, cl + CL, ... of its 4 columns
-// (every O load issued before the maximum is known) with the weights taken
-// from the chunks' lanes, and the CL chunk lanes of a column group add up
-// through pair exchanges.  Fixed summation order.
-template <int D, int CS>
+// holds the (m, l) of chunks c, c + 64, ... (NM of them), the maximum and
+// the denominator are wave reductions, lane (cl, cg) sums chunks cl,
+// cl + CL, ... of its 4 columns (every O load issued before the maximum is
+// known) with the weights taken from the chunks' lanes, and the CL chunk
+// lanes of a column group add up through pair exchanges.  Fixed summation
+// order.
+template <int D, int CS, int NM>
 __global__ __launch_bounds__(kWave) void merge_wave_kernel(MergeArgs a) {
-  constexpr int CG = D / 4 / CS;   // 16-byte column groups of the slice
-  constexpr int CL = kWave / CG;   // chunk lanes
-  constexpr int KP = kWave / CL;   // chunks per lane (64 chunks at most)
-  static_assert(CL == 2 || CL == 4 || CL == 8, "chunk lanes");
+  constexpr int CG = D / 4 / CS;        // 16-byte column groups of the slice
+  constexpr int CL = kWave / CG;        // chunk lanes
+  constexpr int KP = kWave * NM / CL;   // chunks per lane
+  static_assert(CL == 2 || CL == 4 || CL == 8 || CL == 16, "chunk lanes");
   const int lane = threadIdx.x;
   const int cl = lane / CG, cg = lane % CG;
   const size_t row = blockIdx.x / CS;
@@ -680,15 +682,29 @@ __global__ __launch_bounds__(kWave) void merge_wave_kernel(MergeArgs a) {
     const int k = cl + j * CL;
     o[j] = k < n ? op[(size_t)k * (D / 4)] : f32x4{0.f, 0.f, 0.f, 0.f};
   }
-  const f32x2 ml = lane < n ? mlp[lane] : f32x2{kNegInf, 0.f};
-  const float M = wave_max(ml.x);
-  const float w = lane < n ? exp2_diff(ml.x, M) : 0.f;
-  const float den = wave_sum(w * ml.y);
+  f32x2 ml[NM];
+  float mx = kNegInf;
+#pragma unroll
+  for (int i = 0; i < NM; ++i) {
+    const int k = lane + i * kWave;
+    ml[i] = k < n ? mlp[k] : f32x2{kNegInf, 0.f};
+    mx = fmaxf(mx, ml[i].x);
+  }
+  const float M = wave_max(mx);
+  float w[NM], ls = 0.f;
+#pragma unroll
+  for (int i = 0; i < NM; ++i) {
+    w[i] = lane + i * kWave < n ? exp2_diff(ml[i].x, M) : 0.f;
+    ls = fmaf(w[i], ml[i].y, ls);
+  }
+  const float den = wave_sum(ls);
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int j = 0; j < KP; ++j) {
+    // chunk k = cl + j CL sits in lane k % 64 of weight set k / 64, the same
+    // set in every lane (CL divides 64)
     const int k = cl + j * CL;
-    const float wk = __shfl(w, k);
+    const float wk = __shfl(w[j * CL / kWave], k % kWave);
     acc.x = fmaf(wk, o[j].x, acc.x);
     acc.y = fmaf(wk, o[j].y, acc.y);
     acc.z = fmaf(wk, o[j].z, acc.z);
@@ -696,6 +712,7 @@ __global__ __launch_bounds__(kWave) void merge_wave_kernel(MergeArgs a) {
   }
   // chunk lane cl of column group cg is lane cl * CG + cg
   auto sum_lanes = [&](float x) {
+    if constexpr (CL >= 16) x = pair_sum<4>(x);
     if constexpr (CL >= 8) x = pair_sum<8>(x);
     if constexpr (CL >= 4) x = pair_sum<16>(x);
     return pair_sum<32>(x);
@@ -791,37 +808,35 @@ hipError_t launch_partial(int mode, int is_bf16, int D, int G, const PartialArgs
 
 hipError_t launch_merge(int D, int B, const MergeArgs& a, hipStream_t s) {
   const size_t rows = (size_t)B * a.Hq;
-  // rows of at most 64 chunks: one wave per (row, column slice)
-  if (a.nc <= 64) {
-    if (D == 128 && a.nc <= 32) {
-      hipLaunchKernelGGL((merge_wave_kernel<128, 1>), dim3((unsigned)rows), dim3(kWave), 0, s, a);
-    } else if (D == 128) {
-      hipLaunchKernelGGL((merge_wave_kernel<128, 2>), dim3((unsigned)(rows * 2)), dim3(kWave), 0, s, a);
-    } else if (D == 64) {
-      hipLaunchKernelGGL((merge_wave_kernel<64, 1>), dim3((unsigned)rows), dim3(kWave), 0, s, a);
+  // rows of at most 256 chunks: one wave per (row, column slice), 16 chunks
+  // per lane (32 for d = 128 up to 32 chunks)
+  if (a.nc <= 256 && (D == 64 || D == 128)) {
+    const dim3 blk(kWave);
+    if (D == 128) {
+      if (a.nc <= 32)
+        hipLaunchKernelGGL((merge_wave_kernel<128, 1, 1>), dim3((unsigned)rows), blk, 0, s, a);
+      else if (a.nc <= 64)
+        hipLaunchKernelGGL((merge_wave_kernel<128, 2, 1>), dim3((unsigned)(rows * 2)), blk, 0, s, a);
+      else if (a.nc <= 128)
+        hipLaunchKernelGGL((merge_wave_kernel<128, 4, 2>), dim3((unsigned)(rows * 4)), blk, 0, s, a);
+      else
+        hipLaunchKernelGGL((merge_wave_kernel<128, 8, 4>), dim3((unsigned)(rows * 8)), blk, 0, s, a);
     } else {
-      return hipErrorInvalidValue;
+      if (a.nc <= 64)
+        hipLaunchKernelGGL((merge_wave_kernel<64, 1, 1>), dim3((unsigned)rows), blk, 0, s, a);
+      else if (a.nc <= 128)
+        hipLaunchKernelGGL((merge_wave_kernel<64, 2, 2>), dim3((unsigned)(rows * 2)), blk, 0, s, a);
+      else
+        hipLaunchKernelGGL((merge_wave_kernel<64, 4, 4>), dim3((unsigned)(rows * 4)), blk, 0, s, a);
     }
     return hipGetLastError();
   }
-  // Rows of 64 chunks or more split their columns over 2 workgroups, rows
-  // of 128 or more over 4 (of 4 waves each): more workgroups in flight for
-  // the same latency-bound walk over the chunks.
-  constexpr int WW = 4;
-  const int cs = a.nc >= 128 ? 4 : a.nc >= 64 ? 2 : 1;
-  const dim3 grid((unsigned)(rows * cs));
-  const dim3 block(cs > 1 ? WW * kWave : 4 * kWave);
-  if (D == 64) {
-    if (cs == 4) hipLaunchKernelGGL((merge_kernel<64, WW, 4>), grid, block, 0, s, a);
-    else if (cs == 2) hipLaunchKernelGGL((merge_kernel<64, WW, 2>), grid, block, 0, s, a);
-    else hipLaunchKernelGGL((merge_kernel<64, 4, 1>), grid, block, 0, s, a);
-  } else if (D == 128) {
-    if (cs == 4) hipLaunchKernelGGL((merge_kernel<128, WW, 4>), grid, block, 0, s, a);
-    else if (cs == 2) hipLaunchKernelGGL((merge_kernel<128, WW, 2>), grid, block, 0, s, a);
-    else hipLaunchKernelGGL((merge_kernel<128, 4, 1>), grid, block, 0, s, a);
-  } else {
-    return hipErrorInvalidValue;
-  }
+  // Longer rows: one workgroup of 4 waves per (row, quarter of the
+  // columns), walking the chunks in tiles of 256.
+  const dim3 grid((unsigned)(rows * 4)), block(4 * kWave);
+  if (D == 64) hipLaunchKernelGGL((merge_kernel<64, 4, 4>), grid, block, 0, s, a);
+  else if (D == 128) hipLaunchKernelGGL((merge_kernel<128, 4, 4>), grid, block, 0, s, a);
+  else return hipErrorInvalidValue;
   return hipGetLastError();
 }
 

@@ -113,7 +113,8 @@ def test_config2_full_size():
 
 def test_dense_128k():
     """The long end of the 32K-128K range: B 2, L 131072, chunk 512 (256
-    chunks per row: the merge with its columns over 4 workgroups)."""
+    chunks per row: the merge with its columns over 8 wavefronts, four
+    chunks' (m, l) per lane)."""
     banner("dense 128K")
     c = W.dense_case(2, 32, 8, 131072, 128, "bf16", 512, seed=1202, device=DEV)
     out, lse = fd.decode_attn(c.q, c.k, c.v, chunk=c.chunk)
@@ -170,20 +171,21 @@ def test_sequence_split_merged_from_two_halves():
 
 @pytest.mark.parametrize("d", [64, 128])
 def test_merge_of_many_chunks(d):
-    """Rows of 128 chunks or more take the merge whose columns are split over
-    several workgroups; 257 chunks also cross its 256-chunk weight tile."""
+    """Rows of 257 chunks take the workgroup merge and cross its 256-chunk
+    weight tile."""
     banner(f"dense many chunks d={d}")
     c = W.dense_case(2, 8, 2, 16 * 256 + 5, d, "bf16", 16, seed=41 + d, device=DEV)
     _check(c)
 
 
 @pytest.mark.parametrize("d", [64, 128])
-@pytest.mark.parametrize("nc", [1, 2, 32, 33, 63, 64, 65, 100, 127, 128])
+@pytest.mark.parametrize("nc", [1, 2, 32, 33, 63, 64, 65, 127, 128, 129, 255, 256, 257])
 def test_merge_tier_edges(d, nc):
-    """Each side of every merge tier: rows of up to 64 chunks on one
-    wavefront (d 128: its columns on 1 wavefront up to 32 chunks, on 2 from
-    33), rows of 65-127 on two 4-wave workgroups, 128 and more on four; the
-    last chunk is ragged."""
+    """Each side of every merge tier: rows of up to 256 chunks on single
+    wavefronts, the columns split over more of them as rows grow (d 128: 1
+    up to 32 chunks, 2 up to 64, 4 up to 128, 8 up to 256; d 64: 1 up to 64,
+    2 up to 128, 4 up to 256), longer rows on 4-wave workgroups; the last
+    chunk is ragged."""
     banner(f"dense merge tiers d={d} nc={nc}")
     c = W.dense_case(2, 8, 2, 16 * (nc - 1) + 7, d, "bf16", 16, seed=300 + nc + d, device=DEV)
     _check(c)

@@ -91,10 +91,12 @@ def test_fixed_max_repeatable():
                                                         margin_hi=1.0, margin_lo=1.5))
 
 
-@pytest.mark.parametrize("nc", [64, 100, 128, 300])
+@pytest.mark.parametrize("nc", [30, 64, 100, 200, 300])
 def test_split_column_merges_repeatable(nc):
-    """Rows of 64-127 chunks merge with their columns over 2 workgroups,
-    rows of 128 or more over 4."""
+    """Every merge tier: rows of up to 256 chunks on single wavefronts (the
+    columns over 1, 2, 4 or 8 of them, several chunks' (m, l) per lane past
+    64), longer rows on 4-wave workgroups that reduce through LDS behind
+    barriers."""
     banner(f"determinism merge nc={nc}")
     c = W.dense_case(2, 16, 4, 16 * (nc - 1) + 5, 128, "bf16", 16, seed=950 + nc, device=DEV)
     _same_every_time(lambda: fd.decode_attn(c.q, c.k, c.v, chunk=16))
