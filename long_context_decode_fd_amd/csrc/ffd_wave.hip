@@ -12,8 +12,9 @@
 // kStep positions:
 //   * Scan.  Codes and (zero, step) of a step's 8 tiles of 16 positions come
 //     through buffer loads (one lane offset plus an immediate per tile).
-//     Codes become exact fp16 values 4 + c and the query fp16 after an exact
-//     power-of-two scaling; v_mfma_f32_16x16x32_f16 with the
+//     Codes become exact fp16 subnormals c 2^(2i-24) with one mask per pair
+//     of dims (i = the pair's place in its 32-bit word) and the query fp16
+//     after exact power-of-two scalings; v_mfma_f32_16x16x32_f16 with the
 //     query groups stacked block-diagonally gives each lane (position n,
 //     quad g) the group-g dot products of heads 4tt .. 4tt+3, and a
 //     transposed reduction over the four quads (two v_permlane32_swap, one
@@ -27,9 +28,10 @@
 //     position) are appended to a ring in this wave's LDS.
 //   * Refine + attend, pairs of up to 32 ring entries (two tiles of 16),
 //     while the next steps' scan loads are in flight: residual bytes as
-//     exact fp16 1152 + r (one byte permute per pair of dims) in the same
-//     group-stacked tile (refinement = rs_g (C - 1152 qsum), reduced the
-//     same transposed way), online softmax per head over the pair, P V on
+//     exact fp16 subnormals (r + 128) 2^-24 (one byte permute per pair of
+//     dims) in the same group-stacked tile (refinement = rs_g 2^24
+//     (C - 2^-17 qsum), reduced the same transposed way), online softmax
+//     per head over the pair, P V on
 //     v_mfma_f32_16x16x32_bf16 over both tiles with p split bf16 hi + lo and
 //     the candidates' V rows read back transposed from LDS.  The next
 //     pair's loads are issued as soon as the current pair's registers are
@@ -146,59 +148,48 @@ void ffd_wave_kernel(FfdArgs a) {
   // takes c log2 e / pw.  Set up after the first anchor and scan loads are
   // issued (below).
   float pw = 1.f, ipw = 1.f, cl2 = a.c_log2;
-  u32x4 qa[NT][4];
+  u32x4 qa[NT][4], qs[NT][4];
   float qsum[NT][4];
   // this lane's heads 4 tt + qg: threshold m^ - delta and j* (within the
   // chunk), set from the anchors below
   float thr[NT];
   int jst[NT];
-  // constants of the code and residual -> fp16 conversions, held in
-  // registers (v_and_or_b32 takes no literal; v_perm_b32 takes the
-  // exponent byte from a register)
-  uint32_t k_mask = 0x03000300u, k_exp = 0x44004400u, k64 = 0x64646464u;
-  asm volatile("" : "+s"(k_mask));
-  asm volatile("" : "+v"(k_exp));
-  asm volatile("" : "+v"(k64));
-
   // ---- operands and dot products shared by the anchors, the scan and the
-  // refine.  Codes of a (position, group): the fp16 pairs 4 + c of k-steps
-  // 0 .. 3; (zero, step): the group's part of the 2-bit score of head
-  // 4 tt + qg after the transposed reduction ----
+  // refine.  Codes of a (position, group): k-step k takes pairs 4 (k % 2)
+  // .. +3 of word k / 2, each half c 2^(2i-24); the products with qs sum to
+  // 2^-24 pw sum q c, so the group's part of the 2-bit score of head
+  // 4 tt + qg is z qsum + 2^24 st C, summed over the groups by the
+  // transposed reduction ----
   auto code_operands = [&](const u32x2& cwv, u32x4 (&bq)[4]) {
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const uint32_t w = k < 2 ? cwv.x : cwv.y;
-      const int pbit = 4 * (k & 1);
-      bq[k] = u32x4{code_pair_f16(w, pbit, k_mask, k_exp), code_pair_f16(w, pbit + 1, k_mask, k_exp),
-                    code_pair_f16(w, pbit + 2, k_mask, k_exp),
-                    code_pair_f16(w, pbit + 3, k_mask, k_exp)};
-    }
+    for (int k = 0; k < 4; ++k) bq[k] = code_operand_f16(k < 2 ? cwv.x : cwv.y, k & 1);
   };
   auto scan_scores = [&](const u32x4 (&bq)[4], uint32_t zzv, float (&sc)[NT]) {
-    const float z = half_to_float(zzv & 0xFFFF), st = half_to_float(zzv >> 16);
-    const float zb = fmaf(-4.f, st, z);
+    const float z = half_to_float(zzv & 0xFFFF), st = half_to_float(zzv >> 16) * 0x1p24f;
 #pragma unroll
     for (int tt = 0; tt < NT; ++tt) {
       f32x4 cc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int k = 0; k < 4; ++k) cc = mfma_16x16x32_f16(qa[tt][k], bq[k], cc);
+      for (int k = 0; k < 4; ++k) cc = mfma_16x16x32_f16(qs[tt][k], bq[k], cc);
       float part[4];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) part[e] = fmaf(zb, qsum[tt][e], st * cc[e]);
+      for (int e = 0; e < 4; ++e) part[e] = fmaf(z, qsum[tt][e], st * cc[e]);
       sc[tt] = quad_transpose_sum(part);
     }
   };
-  // residual bytes of a (position, group) as exact fp16 1152 + r, and the
-  // refinement rs_g (sum q (1152 + r) - 1152 qsum) summed over the groups
+  // residual bytes of a (position, group) as exact fp16 (r + 128) 2^-24,
+  // and the refinement rs_g sum q r = rs_g 2^24 (C - 2^-17 qsum) summed over
+  // the groups (C = 2^-24 sum pw q (r + 128))
   auto residual_operands = [&](const u32x4& ra, const u32x4& rb, u32x4 (&bq)[4]) {
     const uint32_t w[8] = {ra.x, ra.y, ra.z, ra.w, rb.x, rb.y, rb.z, rb.w};
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
-      const u32x2 lo = residual_pairs_f16(w[2 * t], k64), hi = residual_pairs_f16(w[2 * t + 1], k64);
+      const u32x2 lo = residual_pairs_f16(w[2 * t]), hi = residual_pairs_f16(w[2 * t + 1]);
       bq[t] = u32x4{lo.x, lo.y, hi.x, hi.y};
     }
   };
   auto refinement = [&](const u32x4 (&bq)[4], float rsf, float (&corr)[NT]) {
+    const float rs24 = rsf * 0x1p24f;
 #pragma unroll
     for (int tt = 0; tt < NT; ++tt) {
       f32x4 cc = {0.f, 0.f, 0.f, 0.f};
@@ -206,7 +197,7 @@ void ffd_wave_kernel(FfdArgs a) {
       for (int t = 0; t < 4; ++t) cc = mfma_16x16x32_f16(qa[tt][t], bq[t], cc);
       float part[4];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) part[e] = rsf * fmaf(-1152.f, qsum[tt][e], cc[e]);
+      for (int e = 0; e < 4; ++e) part[e] = rs24 * fmaf(-0x1p-17f, qsum[tt][e], cc[e]);
       corr[tt] = quad_transpose_sum(part);
     }
   };
@@ -413,10 +404,12 @@ void ffd_wave_kernel(FfdArgs a) {
       bool sel[NT];
       uint64_t bal[NT];
       uint32_t uni = 0;   // positions of the tile selected by any head (wave-uniform)
+      const uint64_t b_in = __builtin_amdgcn_ballot_w64(jr < n);
 #pragma unroll
       for (int tt = 0; tt < NT; ++tt) {
-        sel[tt] = (jr < n) & ((sc[tt] >= thr[tt]) | (jr == jst[tt]));
-        bal[tt] = __ballot(sel[tt]);
+        const bool hit = sc[tt] >= thr[tt], js = jr == jst[tt];
+        sel[tt] = (jr < n) & (hit | js);
+        bal[tt] = (__builtin_amdgcn_ballot_w64(hit) | __builtin_amdgcn_ballot_w64(js)) & b_in;
         const uint64_t f = bal[tt] | (bal[tt] >> 32);
         uni |= (uint32_t)(f | (f >> 16)) & 0xFFFFu;
       }
@@ -506,7 +499,7 @@ void ffd_wave_kernel(FfdArgs a) {
     const int kst = 16 * t_step;   // anchor tiles k_first, k_first + kst, ...
     anchor_load(min(k_first, na - 1), cur);
     anchor_load(min(k_first + kst, na - 1), nxt);
-    pw = stacked_query_f16<G>(qraw, lane, qa, qsum);
+    pw = stacked_query_f16<G>(qraw, lane, qa, qs, qsum);
     ipw = 1.f / pw;   // a power of two: exact
     cl2 = a.c_log2 * ipw;
     scan_issue(sA, 0);
