@@ -40,8 +40,13 @@
  *     means nothing was launched (except FD_ERR_HIP, reported after a launch
  *     failed).  fd_last_error() then describes the failure.
  *   - Non-finite values in q/K/V propagate; the kernels do not check data.
- *   - Supported: d in {64, 128}; Hq / Hkv in {1, 2, 4, 8}; chunk a positive
- *     multiple of 16 no larger than 65536; B * (query rows per sequence) *
+ *   - Supported: d in {64, 128}; group size G = Hq / Hkv in {1, 2, 4, 8}
+ *     for every entry point, and for the dense ones (fd_decode_attn,
+ *     fd_decode_attn_noalloc, fd_decode_attn_partials, fd_decode_attn_multi)
+ *     also any other G with G * (query tokens) <= 32 on bf16 inputs, which
+ *     runs on the matrix-core kernel (e.g. 28 query heads over 4 kv-heads,
+ *     or 16 or 32 heads per kv-head); chunk a positive multiple of 16 no
+ *     larger than 65536; B * (query rows per sequence) *
  *     (number of chunks) at most 2^31 - 1 (the kernels index partial rows
  *     with 32-bit integers), else FD_ERR_UNSUPPORTED.
  */
@@ -82,6 +87,10 @@ int fd_abi_version(void);
  *   chunk   positions per split-KV chunk; chunk c covers
  *           [c*chunk, min((c+1)*chunk, L)), n_chunks = ceil(L / chunk).
  * The result does not depend on `chunk` beyond fp32 rounding.
+ * G in {1, 2, 4, 8}: the vector kernel, bf16 or fp32.  Other G <= 32 (bf16
+ * only, else FD_ERR_UNSUPPORTED): the matrix-core kernel of
+ * fd_decode_attn_multi with one token, whose splits may then cover several
+ * consecutive chunks (same result up to fp32 rounding).
  */
 int fd_decode_attn(fd_dtype_t dt, const void* q, const void* k, const void* v,
                    float* out, float* lse,
@@ -191,14 +200,14 @@ int fd_decode_attn_unified_max(fd_dtype_t dt, const void* q, const void* k,
  * positions 0 .. L-M+r ("Flash Decoding" explainer, section 1: a query sees
  * every key up to its own position).  The G*M query rows of a kv-head share
  * each K and V row (the flat-GEMM case of the "FlashDecoding" deployment
- * blog, section 1), computed on the matrix cores; M = 1 takes the
- * single-query kernel of fd_decode_attn.
+ * blog, section 1), computed on the matrix cores; M = 1 with G in
+ * {1, 2, 4, 8} takes the single-query vector kernel of fd_decode_attn.
  *   q     [B, M, Hq, d]; k, v [B, Hkv, L, d]; L >= M
  *   out   fp32 [B, M, Hq, d];  lse fp32 [B, M, Hq] or NULL
- *   M = 1: dt bf16 or fp32.  M >= 2: bf16 only and G*M <= 32, else
- *   FD_ERR_UNSUPPORTED.  Workspace: chunk partials of the B*M*Hq rows
+ *   M = 1 and G in {1, 2, 4, 8}: dt bf16 or fp32.  Otherwise bf16 only and
+ *   G*M <= 32, else FD_ERR_UNSUPPORTED.  Workspace: chunk partials of the B*M*Hq rows
  *   (same layout as fd_decode_attn_partials with M*Hq heads), sized for
- *   `chunk`.  For M >= 2, chunk is the split granule: when the rows' chunks
+ *   `chunk`.  On the matrix cores chunk is the split granule: when the rows' chunks
  *   outnumber what the device runs at once, one split covers F consecutive
  *   chunks, F chosen for the fewest rounds of splits (the latency estimate
  *   of the "Flash Decoding" explainer, section 2: splits beyond the

@@ -53,10 +53,33 @@ int check_heads(int B, int Hq, int Hkv, int d) {
   if (B <= 0 || Hq <= 0 || Hkv <= 0 || d <= 0)
     return fail(FD_ERR_ARG, "B=%d Hq=%d Hkv=%d d=%d must be positive", B, Hq, Hkv, d);
   if (Hq % Hkv != 0) return fail(FD_ERR_ARG, "Hq=%d is not a multiple of Hkv=%d", Hq, Hkv);
-  const int G = Hq / Hkv;
-  if (G != 1 && G != 2 && G != 4 && G != 8)
-    return fail(FD_ERR_UNSUPPORTED, "group size Hq/Hkv=%d not in {1,2,4,8}", G);
   if (d != 64 && d != 128) return fail(FD_ERR_UNSUPPORTED, "d=%d not in {64,128}", d);
+  return FD_OK;
+}
+
+// Group sizes of the single-query vector kernels (paged, fixed maximum, FFD
+// and the dense path's fast case).
+bool vector_group(int G) { return G == 1 || G == 2 || G == 4 || G == 8; }
+
+int check_vector_group(int G) {
+  if (!vector_group(G))
+    return fail(FD_ERR_UNSUPPORTED, "group size Hq/Hkv=%d not in {1,2,4,8}", G);
+  return FD_OK;
+}
+
+// Dense paths: M query tokens per sequence.  One token with G in {1,2,4,8}
+// takes the vector kernel (bf16 or fp32); every other case the matrix-core
+// kernels, which take bf16 and up to 32 query rows (G * M) per kv-head.
+bool matrix_path(int G, int M) { return M > 1 || !vector_group(G); }
+
+int check_dense_group(fd_dtype_t dt, int G, int M) {
+  if (!matrix_path(G, M)) return FD_OK;
+  if ((long long)G * M > 32)
+    return fail(FD_ERR_UNSUPPORTED, "G*M=%lld query rows per kv-head exceed 32",
+                (long long)G * M);
+  if (dt != FD_BF16)
+    return fail(FD_ERR_UNSUPPORTED, "several query tokens, or a group size outside "
+                                    "{1,2,4,8}, need bf16 inputs");
   return FD_OK;
 }
 
@@ -145,6 +168,30 @@ int run_split_kv(int mode, fd_dtype_t dt, const void* q, const void* k, const vo
   return hip_status(fdk::launch_merge(d, B, ma, s), "merge kernel launch");
 }
 
+// Enqueue the matrix-core kernel for M tokens of G*M <= 32 query rows per
+// kv-head and (when out != NULL) the merge.  fold: splits may cover several
+// consecutive chunks (fewer partials when the chunks outnumber the device's
+// wave slots); without it every chunk gets its own partial, as
+// fd_decode_attn_partials promises.  The workspace sized for nc chunks holds
+// either.
+int run_multi(const void* q, const void* k, const void* v, float* out, float* lse, int B,
+              int M, int Hq, int Hkv, int L, int d, float scale, int chunk, int nc, void* ws,
+              bool fold, void* stream) {
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  fdk::MultiArgs ma{q, k, v, nullptr, nullptr, B, M, Hq, Hkv, L, chunk, nc,
+                    (float)((double)scale * 1.4426950408889634)};
+  const int F = fold ? fdk::multi_fold(d, ma) : 1;
+  const long long split = (long long)chunk * F;
+  ma.chunk = split > L ? L : (int)split;
+  ma.nc = n_chunks_of(L, ma.chunk);
+  split_ws(ws, B, M * Hq, ma.nc, d, &ma.o_part, &ma.ml_part);
+  hipError_t e = fdk::launch_multi(d, ma, s);
+  if (e != hipSuccess) return hip_status(e, "multi-row kernel launch");
+  if (out == nullptr) return ok();
+  fdk::MergeArgs mg{ma.o_part, ma.ml_part, out, lse, nullptr, M * Hq, ma.nc, ma.chunk, L};
+  return hip_status(fdk::launch_merge(d, B, mg, s), "merge kernel launch");
+}
+
 // Device address of `scratch` on each device, resolved once per device
 // with that device current (the first fd_decode_attn_noalloc call there).
 constexpr int kMaxDevices = 64;
@@ -186,6 +233,7 @@ int fd_decode_attn(fd_dtype_t dt, const void* q, const void* k, const void* v, f
                    void* ws, size_t* ws_bytes, void* stream) {
   if (int e = check_dtype(&dt)) return e;
   if (int e = check_heads(B, Hq, Hkv, d)) return e;
+  if (int e = check_dense_group(dt, Hq / Hkv, 1)) return e;
   if (L <= 0) return fail(FD_ERR_ARG, "L=%d must be positive", L);
   if (int e = check_chunk(chunk)) return e;
   if (int e = check_scale(scale)) return e;
@@ -196,6 +244,8 @@ int fd_decode_attn(fd_dtype_t dt, const void* q, const void* k, const void* v, f
   if (!q || !k || !v || !out) return fail(FD_ERR_ARG, "q, k, v and out must not be NULL");
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
     return fail(FD_ERR_ARG, "q, k, v and out must be 16-byte aligned");
+  if (matrix_path(Hq / Hkv, 1))
+    return run_multi(q, k, v, out, lse, B, 1, Hq, Hkv, L, d, scale, chunk, nc, ws, true, stream);
   fdk::PartialArgs pa{};
   return run_split_kv(fdk::kDense, dt, q, k, v, out, lse, B, Hq, Hkv, L, d, scale, chunk, nc,
                       pa, ws, nullptr, L, stream);
@@ -206,6 +256,7 @@ int fd_decode_attn_noalloc(fd_dtype_t dt, const void* q, const void* k, const vo
                            float scale, int chunk, void* stream) {
   if (int e = check_dtype(&dt)) return e;
   if (int e = check_heads(B, Hq, Hkv, d)) return e;
+  if (int e = check_dense_group(dt, Hq / Hkv, 1)) return e;
   if (L <= 0) return fail(FD_ERR_ARG, "L=%d must be positive", L);
   if (int e = check_chunk(chunk)) return e;
   if (int e = check_scale(scale)) return e;
@@ -222,6 +273,8 @@ int fd_decode_attn_noalloc(fd_dtype_t dt, const void* q, const void* k, const vo
     return fail(FD_ERR_ARG, "q, k, v and out must be 16-byte aligned");
   void* ws = nullptr;
   if (int e = scratch_ptr(&ws)) return e;
+  if (matrix_path(Hq / Hkv, 1))
+    return run_multi(q, k, v, out, lse, B, 1, Hq, Hkv, L, d, scale, chunk, nc, ws, true, stream);
   fdk::PartialArgs pa{};
   return run_split_kv(fdk::kDense, dt, q, k, v, out, lse, B, Hq, Hkv, L, d, scale, chunk, nc,
                       pa, ws, nullptr, L, stream);
@@ -232,6 +285,7 @@ int fd_decode_attn_partials(fd_dtype_t dt, const void* q, const void* k, const v
                             void* ws, size_t* ws_bytes, void* stream) {
   if (int e = check_dtype(&dt)) return e;
   if (int e = check_heads(B, Hq, Hkv, d)) return e;
+  if (int e = check_dense_group(dt, Hq / Hkv, 1)) return e;
   if (L <= 0) return fail(FD_ERR_ARG, "L=%d must be positive", L);
   if (int e = check_chunk(chunk)) return e;
   if (int e = check_scale(scale)) return e;
@@ -242,6 +296,9 @@ int fd_decode_attn_partials(fd_dtype_t dt, const void* q, const void* k, const v
   if (!q || !k || !v) return fail(FD_ERR_ARG, "q, k and v must not be NULL");
   if (!aligned16(q) || !aligned16(k) || !aligned16(v))
     return fail(FD_ERR_ARG, "q, k and v must be 16-byte aligned");
+  if (matrix_path(Hq / Hkv, 1))
+    return run_multi(q, k, v, nullptr, nullptr, B, 1, Hq, Hkv, L, d, scale, chunk, nc, ws,
+                     false, stream);
   fdk::PartialArgs pa{};
   return run_split_kv(fdk::kDense, dt, q, k, v, nullptr, nullptr, B, Hq, Hkv, L, d, scale,
                       chunk, nc, pa, ws, nullptr, L, stream);
@@ -269,6 +326,7 @@ int fd_decode_attn_paged(fd_dtype_t dt, const void* q, const void* k_pool,
                          size_t* ws_bytes, void* stream) {
   if (int e = check_dtype(&dt)) return e;
   if (int e = check_heads(B, Hq, Hkv, d)) return e;
+  if (int e = check_vector_group(Hq / Hkv)) return e;
   if (int e = check_chunk(chunk)) return e;
   if (int e = check_scale(scale)) return e;
   if (page_size < 8 || page_size > 1024 || (page_size & (page_size - 1)) != 0)
@@ -310,6 +368,7 @@ int fd_decode_attn_unified_max(fd_dtype_t dt, const void* q, const void* k, cons
                                size_t* ws_bytes, void* stream) {
   if (int e = check_dtype(&dt)) return e;
   if (int e = check_heads(B, Hq, Hkv, d)) return e;
+  if (int e = check_vector_group(Hq / Hkv)) return e;
   if (L <= 0) return fail(FD_ERR_ARG, "L=%d must be positive", L);
   if (int e = check_chunk(chunk)) return e;
   if (int e = check_scale(scale)) return e;
@@ -341,11 +400,7 @@ int fd_decode_attn_multi(fd_dtype_t dt, const void* q, const void* k, const void
   if (L < M) return fail(FD_ERR_ARG, "L=%d must be at least M=%d", L, M);
   if (int e = check_chunk(chunk)) return e;
   if (int e = check_scale(scale)) return e;
-  const int G = Hq / Hkv;
-  if (M > 1 && G * M > 32)
-    return fail(FD_ERR_UNSUPPORTED, "G*M=%d query rows per kv-head exceed 32", G * M);
-  if (M > 1 && dt != FD_BF16)
-    return fail(FD_ERR_UNSUPPORTED, "several query tokens need bf16 inputs");
+  if (int e = check_dense_group(dt, Hq / Hkv, M)) return e;
   const int nc = n_chunks_of(L, chunk);
   if (int e = check_units(B, M * Hq, nc)) return e;
   if (int e = workspace_gate(ws, ws_bytes, partial_bytes(B, M * Hq, nc, d))) return e;
@@ -353,27 +408,14 @@ int fd_decode_attn_multi(fd_dtype_t dt, const void* q, const void* k, const void
   if (!q || !k || !v || !out) return fail(FD_ERR_ARG, "q, k, v and out must not be NULL");
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
     return fail(FD_ERR_ARG, "q, k, v and out must be 16-byte aligned");
-  if (M == 1) {
-    // one query row per head: the single-query kernel (q [B, 1, Hq, d] is
-    // q [B, Hq, d])
+  if (!matrix_path(Hq / Hkv, M)) {
+    // one query row per head of a group the vector kernel takes
+    // (q [B, 1, Hq, d] is q [B, Hq, d])
     fdk::PartialArgs pa{};
     return run_split_kv(fdk::kDense, dt, q, k, v, out, lse, B, Hq, Hkv, L, d, scale, chunk, nc,
                         pa, ws, nullptr, L, stream);
   }
-  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  fdk::MultiArgs ma{q, k, v, nullptr, nullptr, B, M, Hq, Hkv, L, chunk, nc,
-                    (float)((double)scale * 1.4426950408889634)};
-  // splits of F consecutive chunks (fewer partials when the chunks outnumber
-  // the device's wave slots); the workspace sized for nc chunks holds them
-  const int F = fdk::multi_fold(d, ma);
-  const long long split = (long long)chunk * F;
-  ma.chunk = split > L ? L : (int)split;
-  ma.nc = n_chunks_of(L, ma.chunk);
-  split_ws(ws, B, M * Hq, ma.nc, d, &ma.o_part, &ma.ml_part);
-  hipError_t e = fdk::launch_multi(d, ma, s);
-  if (e != hipSuccess) return hip_status(e, "multi-row kernel launch");
-  fdk::MergeArgs mg{ma.o_part, ma.ml_part, out, lse, nullptr, M * Hq, ma.nc, ma.chunk, L};
-  return hip_status(fdk::launch_merge(d, B, mg, s), "merge kernel launch");
+  return run_multi(q, k, v, out, lse, B, M, Hq, Hkv, L, d, scale, chunk, nc, ws, true, stream);
 }
 
 int fd_kv_append(fd_dtype_t dt, const void* k_new, const void* v_new, void* k_cache,
@@ -455,6 +497,7 @@ int fd_ffd_sparse_decode(const void* q, const uint32_t* codes, const uint16_t* z
                          float delta, int n_sink, int n_local, int chunk, uint32_t* cand_mask,
                          float* pseudo_max, void* ws, size_t* ws_bytes, void* stream) {
   if (int e = check_heads(B, Hq, Hkv, d)) return e;
+  if (int e = check_vector_group(Hq / Hkv)) return e;
   if (L <= 0) return fail(FD_ERR_ARG, "L=%d must be positive", L);
   if (int e = check_chunk(chunk)) return e;
   {

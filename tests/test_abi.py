@@ -132,7 +132,9 @@ def test_workspace_sizes():
 @pytest.mark.parametrize("kw,code", [
     (dict(d=96), _abi.FD_ERR_UNSUPPORTED),
     (dict(Hq=9), _abi.FD_ERR_ARG),             # not a multiple of Hkv
-    (dict(Hq=32, Hkv=2), _abi.FD_ERR_UNSUPPORTED),   # group of 16
+    (dict(Hq=32, Hkv=2, dt=_abi.FD_F32), _abi.FD_ERR_UNSUPPORTED),   # group of 16 in fp32
+    (dict(Hq=7, Hkv=1, dt=_abi.FD_F32), _abi.FD_ERR_UNSUPPORTED),    # group of 7 in fp32
+    (dict(Hq=66, Hkv=2), _abi.FD_ERR_UNSUPPORTED),                   # group of 33
     (dict(L=0), _abi.FD_ERR_ARG),
     (dict(chunk=24), _abi.FD_ERR_ARG),
     (dict(chunk=0), _abi.FD_ERR_ARG),
@@ -149,6 +151,25 @@ def test_validation_errors(kw, code):
     with pytest.raises(fd.FdError) as e:
         fd.workspace_bytes("fd_decode_attn", **args)
     assert e.value.code == code
+
+
+@pytest.mark.parametrize("Hq,Hkv", [(28, 4), (48, 8), (32, 2), (32, 1), (3, 1), (12, 2)])
+def test_any_group_up_to_32_on_bf16(Hq, Hkv):
+    """Group sizes outside {1, 2, 4, 8} (7, 6, 16, 32, 3, 6) take the
+    matrix-core kernel on bf16 inputs: the dense entry points accept them
+    with the usual workspace; the paged, fixed-maximum and FFD entry points
+    do not."""
+    n = fd.workspace_bytes("fd_decode_attn", B=2, Hq=Hq, Hkv=Hkv, L=1000, d=128, chunk=64)
+    assert n == 2 * Hq * 16 * 128 * 4 + -(-2 * Hq * 16 * 2 * 4 // 256) * 256
+    assert fd.workspace_bytes("fd_decode_attn_multi", B=2, M=1, Hq=Hq, Hkv=Hkv, L=1000, d=128,
+                              chunk=64) == n
+    for entry, kw in [("fd_decode_attn_unified_max", dict(L=1000, chunk=64)),
+                      ("fd_ffd_sparse_decode", dict(L=1000, chunk=64)),
+                      ("fd_decode_attn_paged", dict(page=16, max_pages=64, max_seq_len=1000,
+                                                    chunk=64))]:
+        with pytest.raises(fd.FdError) as e:
+            fd.workspace_bytes(entry, B=2, Hq=Hq, Hkv=Hkv, d=128, **kw)
+        assert e.value.code == _abi.FD_ERR_UNSUPPORTED, entry
 
 
 def test_chunk_count_near_int_max():

@@ -137,3 +137,52 @@ def test_multi_row_more_rows_than_wave_slots(M, L, chunk):
     rows = [(0, 0, 0), (0, M - 1, 127), (B // 2, M // 2, 64), (B // 2 + 1, 1, 3),
             (B - 1, M - 1, 127), (B - 1, 0, 77)]
     _check(c, chunk=chunk, rows=rows)
+
+
+@pytest.mark.parametrize("d", [128, 64])
+@pytest.mark.parametrize("G,M", [(3, 1), (7, 1), (16, 1), (32, 1), (6, 1), (7, 4), (16, 2),
+                                 (5, 3), (12, 2), (11, 2)])
+def test_group_sizes_outside_vector_kernel(d, G, M):
+    """Group sizes other than 1, 2, 4, 8 (e.g. 28 query heads over 4
+    kv-heads: 7; 16 or 32 heads per kv-head) run on the matrix-core kernel,
+    one token or several, one query tile (G*M <= 16) or two."""
+    banner(f"multi any group d={d} G={G} M={M}")
+    Hkv = 2
+    c = W.multi_case(2, M, G * Hkv, Hkv, 333, d, seed=500 + G * M + d, device=DEV)
+    _check(c, chunk=64)
+
+
+@pytest.mark.parametrize("G", [7, 16, 32])
+def test_single_query_entry_points_any_group(G):
+    """fd_decode_attn, its allocation-free variant and the partials + merge
+    pair take every group size up to 32 on bf16: each matches the fp64
+    oracle, and the partials (one per chunk) merge to the full call's
+    result."""
+    banner(f"single-query entry points G={G}")
+    Hkv = 2
+    c = W.multi_case(3, 1, G * Hkv, Hkv, 1500, 128, seed=600 + G, device=DEV)
+    q = c.q[:, 0].contiguous()
+    ref, lref = omr.multi_row_attention(f64(c.q), f64(c.k), f64(c.v), c.scale)
+    out, lse = fd.decode_attn(q, c.k, c.v, chunk=128)
+    torch.cuda.synchronize()
+    assert max_err(f64(out), ref[:, 0]) <= TOLB and max_err(f64(lse), lref[:, 0]) <= TOLB
+    o2, l2 = fd.decode_attn_noalloc(q, c.k, c.v, chunk=128)
+    torch.cuda.synchronize()
+    assert max_err(f64(o2), ref[:, 0]) <= TOLB and max_err(f64(l2), lref[:, 0]) <= TOLB
+    ws, nc = fd.decode_attn_partials(q, c.k, c.v, chunk=128)
+    assert nc == 12
+    o_part, ml_part = fd.partial_views(ws, 3, G * Hkv, nc, 128)
+    o3, l3 = fd.merge_partials(o_part, ml_part)
+    torch.cuda.synchronize()
+    assert max_err(f64(o3), ref[:, 0]) <= TOLB and max_err(f64(l3), lref[:, 0]) <= TOLB
+
+
+def test_group_of_sixteen_full_size():
+    """Sixteen query heads per kv-head at the headline cache (B 8, Hkv 8,
+    L 32768; Hq 128): every row against the oracle."""
+    banner("single query G=16 full size")
+    c = W.multi_case(8, 1, 128, 8, 32768, 128, seed=616, device=DEV)
+    out, lse = fd.decode_attn(c.q[:, 0].contiguous(), c.k, c.v, chunk=512)
+    torch.cuda.synchronize()
+    ref, lref = omr.multi_row_attention(f64(c.q), f64(c.k), f64(c.v), c.scale)
+    assert max_err(f64(out), ref[:, 0]) <= TOLB and max_err(f64(lse), lref[:, 0]) <= TOLB
