@@ -61,6 +61,8 @@ def parse_args():
     p.add_argument("--steps", type=int, default=50)
     p.add_argument("--warmup", type=int, default=200)
     p.add_argument("--copies", type=int, default=3, help="rotated K/V copies")
+    p.add_argument("--settle-ms", type=float, default=100.0,
+                   help="untimed run time before each extra workload's warm-up")
     p.add_argument("--no-variants", action="store_true")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0,
@@ -121,14 +123,31 @@ class Timer:
     costs the stream about 3 us (FFD peaked workload: 64.4 us per call with
     an event after every call, 61.5 without), so events after every call
     would add their own cost and jitter to each step; per window of 4 the
-    added cost is under 1 us per call."""
+    added cost is under 1 us per call.
 
-    def __init__(self, torch):
+    `settle_ms` (the extra workloads only; the headline step keeps exactly
+    the warm-up it is given): before the warm-up calls, the calls run
+    untimed for that much wall time.  The first ~100 back-to-back calls of a
+    workload swing by up to 8 % on these GPUs (power-management and memory
+    transients after idle periods or large allocations), which a warm-up of
+    a few calls does not cover; a serving loop decodes in the settled
+    state."""
+
+    def __init__(self, torch, settle_ms=0.0):
         self.torch = torch
+        self.settle_ms = settle_ms
 
-    def run(self, calls, steps, warmup):
+    def run(self, calls, steps, warmup, settle=True):
         torch = self.torch
         n = len(calls)
+        if settle and self.settle_ms > 0:
+            t_end = time.perf_counter() + self.settle_ms * 1e-3
+            i = 0
+            while time.perf_counter() < t_end:
+                for _ in range(8):
+                    calls[i % n]()
+                    i += 1
+                torch.cuda.synchronize()
         for i in range(warmup):
             calls[i % n]()
         torch.cuda.synchronize()
@@ -209,8 +228,8 @@ def dense_headline(torch, fd, W, args, timer):
     part = [mk_part(k, v) for k, v in zip(ks, vs)]
     check_rc(lib, full[0]())
     check_rc(lib, part[0]())
-    t_full = timer.run(full, args.steps, args.warmup)
-    t_part = timer.run(part, args.steps, args.warmup)
+    t_full = timer.run(full, args.steps, args.warmup, settle=False)
+    t_part = timer.run(part, args.steps, args.warmup, settle=False)
 
     check_rc(lib, full[0]())
     sample_rows(torch, "config2 dense GQA bf16 (sequence 0, all 32 heads)", case.q[:1], case.k[:1],
@@ -773,7 +792,7 @@ def main():
     import long_context_decode_fd_amd as fd
     import workloads as W
     assert torch.cuda.is_available(), "bench.py needs a GPU"
-    timer = Timer(torch)
+    timer = Timer(torch, args.settle_ms)
     case, h = dense_headline(torch, fd, W, args, timer)
     line = {
         "metric": METRIC,
