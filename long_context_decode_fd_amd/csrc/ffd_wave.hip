@@ -125,8 +125,11 @@ void ffd_wave_kernel(FfdArgs a) {
   constexpr int kTiles = scan_tiles<G>(), kStep = 16 * kTiles;
   static_assert(G == 4 || G == 8, "group-stacked tiles");
   static_assert(2 * kStep <= kRing, "two steps of entries fit in the ring");
-  __shared__ __align__(16) float s_sc[kWaves][kRing][G];   // scan score per head (-inf: not selected)
-  __shared__ int s_pos[kWaves][kRing];                       // position within the chunk
+  // ring entries, then discard slots for the lanes of a tile that append
+  // nothing (16 score rows, 64 positions), so that the appends are stores
+  // on every lane and a scan step needs no branch
+  __shared__ __align__(16) float s_sc[kWaves][kRing + 16][G];   // scan score per head (-inf: not selected)
+  __shared__ int s_pos[kWaves][kRing + kWave];                   // position within the chunk
   __shared__ __align__(16) unsigned char s_vt[kWaves][2][16 * kVStr];
   __shared__ __align__(16) float s_pb[kWaves][G][32];
   __shared__ float s_am[kWaves][G];   // anchors: each wave's best score per head
@@ -392,37 +395,41 @@ void ffd_wave_kernel(FfdArgs a) {
   const uint32_t below = (1u << n16) - 1u;   // positions of the tile before this lane's
   int tail = 0;                              // ring entries written so far (wave-uniform)
   auto scan_step = [&](const ScanRegs<kTiles>& R, int s) __attribute__((always_inline)) {
+    // every tile's scores first: no branch between the tiles, so the
+    // compiler interleaves one tile's matrix products with another's vector
+    // work (positions at or past n read zeros and are masked below)
+    float sc[kTiles][NT];
+#pragma unroll
+    for (int t = 0; t < kTiles; ++t) {
+      u32x4 bq[4];
+      code_operands(R.cw[t], bq);
+      scan_scores(bq, R.zz[t], sc[t]);
+    }
 #pragma unroll
     for (int t = 0; t < kTiles; ++t) {
       const int p0 = s * kStep + 16 * t;   // wave-uniform
-      if (p0 >= n) break;
       const int jr = p0 + n16;
-      u32x4 bq[4];
-      code_operands(R.cw[t], bq);
-      float sc[NT];
-      scan_scores(bq, R.zz[t], sc);
+      const uint64_t b_in = __builtin_amdgcn_ballot_w64(jr < n);
       bool sel[NT];
       uint64_t bal[NT];
       uint32_t uni = 0;   // positions of the tile selected by any head (wave-uniform)
-      const uint64_t b_in = __builtin_amdgcn_ballot_w64(jr < n);
 #pragma unroll
       for (int tt = 0; tt < NT; ++tt) {
-        const bool hit = sc[tt] >= thr[tt], js = jr == jst[tt];
+        const bool hit = sc[t][tt] >= thr[tt], js = jr == jst[tt];
         sel[tt] = (jr < n) & (hit | js);
         bal[tt] = (__builtin_amdgcn_ballot_w64(hit) | __builtin_amdgcn_ballot_w64(js)) & b_in;
         const uint64_t f = bal[tt] | (bal[tt] >> 32);
         uni |= (uint32_t)(f | (f >> 16)) & 0xFFFFu;
       }
-      if (uni != 0u) {
-        if ((uni >> n16) & 1u) {
-          const int idx = (tail + __builtin_popcount(uni & below)) & (kRing - 1);
+      // lanes of appended positions write ring entry tail + (their rank in
+      // the union); the others their discard slots
+      const bool mine = (uni >> n16) & 1u;
+      const int idx = mine ? (tail + __builtin_popcount(uni & below)) & (kRing - 1) : kRing + n16;
 #pragma unroll
-          for (int tt = 0; tt < NT; ++tt) sc_w[idx * G + 4 * tt + qg] = sel[tt] ? sc[tt] : kNegInf;
-          if (qg == 0) pos_w[idx] = jr;
-        }
-        tail += __builtin_popcount(uni);
-      }
-      if (MASK && lane < G) {
+      for (int tt = 0; tt < NT; ++tt) sc_w[idx * G + 4 * tt + qg] = sel[tt] ? sc[t][tt] : kNegInf;
+      pos_w[(mine && qg == 0) ? idx : kRing + lane] = jr;
+      tail += __builtin_popcount(uni);
+      if (MASK && lane < G && p0 < n) {
         // 16 bits per head and tile; chunks start at multiples of 32, so
         // tile t of the chunk is half-word c0 / 16 + s * kTiles + t of the row
         const uint64_t bb = (NT == 2 && lane >= 4) ? bal[NT - 1] : bal[0];
