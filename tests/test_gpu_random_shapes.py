@@ -102,6 +102,31 @@ def test_multi_random(i):
 
 
 @pytest.mark.parametrize("i", range(N))
+def test_any_group_random(i):
+    """Group sizes drawn from 1-32 (most outside {1, 2, 4, 8}) with as many
+    tokens as fit 32 query rows, through the multi-row entry point and, for
+    one token, the single-query one."""
+    rs = np.random.default_rng(8500 + i)
+    G = int(rs.integers(1, 33))
+    M = int(rs.integers(1, 32 // G + 1))
+    Hkv, B = int(rs.integers(1, 4)), int(rs.integers(1, 5))
+    d = int(rs.choice([64, 128]))
+    L = int(rs.integers(M, 2501))
+    chunk = 16 * int(rs.integers(1, 65))
+    banner(f"random any-group B={B} M={M} G={G} Hkv={Hkv} d={d} L={L} chunk={chunk}")
+    c = W.multi_case(B, M, G * Hkv, Hkv, L, d, chunk, seed=8500 + i, device=DEV)
+    out, lse = fd.decode_attn_multi(c.q, c.k, c.v, chunk=chunk)
+    torch.cuda.synchronize()
+    ref, lref = omr.multi_row_attention(f64(c.q), f64(c.k), f64(c.v), c.scale)
+    tol = TOL[torch.bfloat16]
+    assert max_err(f64(out), ref) <= tol and max_err(f64(lse), lref) <= tol
+    if M == 1:
+        o1, l1 = fd.decode_attn(c.q[:, 0].contiguous(), c.k, c.v, chunk=chunk)
+        torch.cuda.synchronize()
+        assert max_err(f64(o1), ref[:, 0]) <= tol and max_err(f64(l1), lref[:, 0]) <= tol
+
+
+@pytest.mark.parametrize("i", range(N))
 def test_ffd_random(i):
     rs = np.random.default_rng(9000 + i)
     B, Hq, Hkv, G, d = _heads(rs)
