@@ -131,3 +131,67 @@ def test_unified_attention_target_is_dense():
                                           40.0, fd.chunk_bounds(L, 64))
             np.testing.assert_allclose(o, ref[b, h], atol=1e-12)
             assert np.array_equal(f, flags[b, h].astype(bool))
+
+
+def test_paged_multi_row_matches_contiguous_multi_row():
+    """Several new tokens over a scattered page pool equal the contiguous
+    multi-row oracle on each sequence's own cache (pinned on its own), and
+    relabelling the pool's pages changes nothing."""
+    from oracle import multi_row
+    B, M, Hq, Hkv, d, page = 3, 4, 6, 2, 16, 8
+    lens = [37, 9, 130]
+    q = _rand((B, M, Hq, d), 11)
+    k = _rand((B, Hkv, max(lens), d), 12)
+    v = _rand((B, Hkv, max(lens), d), 13)
+    kp, table = _scatter_into_pool(k, lens, page, 4)
+    vp, _ = _scatter_into_pool(v, lens, page, 4)
+    out, lse = paged.paged_multi_row_attention(q, kp, vp, table, lens, page, 0.3)
+    for b, L in enumerate(lens):
+        ref, lref = multi_row.multi_row_attention(q[b:b + 1], k[b:b + 1, :, :L],
+                                                  v[b:b + 1, :, :L], 0.3)
+        np.testing.assert_allclose(out[b], ref[0], atol=1e-13)
+        np.testing.assert_allclose(lse[b], lref[0], atol=1e-13)
+    relabel = np.random.default_rng(6).permutation(kp.shape[0])
+    inv = np.argsort(relabel)
+    t2 = np.where(table >= 0, inv[np.maximum(table, 0)], -1)
+    out2, _ = paged.paged_multi_row_attention(q, kp[relabel], vp[relabel], t2, lens, page, 0.3)
+    np.testing.assert_allclose(out2, out, atol=1e-15)
+
+
+def test_paged_multi_row_one_token_is_paged_decode():
+    B, Hq, Hkv, d, page = 2, 4, 1, 8, 16
+    lens = [50, 0]
+    q = _rand((B, 1, Hq, d), 14)
+    k, v = _rand((B, Hkv, 50, d), 15), _rand((B, Hkv, 50, d), 16)
+    kp, table = _scatter_into_pool(k, lens, page, 2)
+    vp, _ = _scatter_into_pool(v, lens, page, 2)
+    out, lse = paged.paged_multi_row_attention(q, kp, vp, table, lens, page, 0.5)
+    ref, lref = paged.paged_attention(q[:, 0], kp, vp, table, lens, page, 0.5)
+    np.testing.assert_array_equal(out[:, 0], ref)
+    np.testing.assert_array_equal(lse[:, 0], lref)
+
+
+def test_paged_multi_row_short_sequences_by_brute_force():
+    """Sequences shorter than the token count: token r sees the first
+    L - M + r + 1 positions, none when that is not positive (out 0, lse
+    -inf); the rest by an explicit softmax sum over the visible keys."""
+    M, Hq, Hkv, d, page = 5, 2, 1, 4, 8
+    lens = [3, 5, 0]
+    B = len(lens)
+    q = _rand((B, M, Hq, d), 17)
+    k, v = _rand((B, Hkv, 8, d), 18), _rand((B, Hkv, 8, d), 19)
+    kp, table = _scatter_into_pool(k, lens, page, 1)
+    vp, _ = _scatter_into_pool(v, lens, page, 1)
+    out, lse = paged.paged_multi_row_attention(q, kp, vp, table, lens, page, 0.7)
+    for b, L in enumerate(lens):
+        for r in range(M):
+            n = L - M + r + 1
+            for h in range(Hq):
+                if n <= 0:
+                    assert np.all(out[b, r, h] == 0) and lse[b, r, h] == -np.inf
+                    continue
+                s = [0.7 * sum(k[b, 0, j, i] * q[b, r, h, i] for i in range(d)) for j in range(n)]
+                e = [math.exp(x) for x in s]
+                want = [sum(e[j] * v[b, 0, j, i] for j in range(n)) / sum(e) for i in range(d)]
+                np.testing.assert_allclose(out[b, r, h], want, atol=1e-12)
+                assert abs(lse[b, r, h] - math.log(sum(e))) < 1e-12
