@@ -14,8 +14,9 @@ decode-attention call over the whole batch (every kernel of the call).
                launch / mean launch time, against 8 TB/s
   cpu_baseline = the fp64 CPU oracle on a bounded sample of the same workload
   variants   = config 1, dense at 128K, a group of 16 query heads per kv-head,
-               the paged, fixed-maximum, FFD, multi-row and cache-append entry
-               points on their own workloads (same timing method)
+               the paged (one and four tokens), fixed-maximum, FFD, multi-row
+               and cache-append entry points on their own workloads (same
+               timing method)
 
 K/V live in several copies that the timed steps rotate through, so each call
 reads data that is not resident in the 256 MB last-level cache.
@@ -38,8 +39,8 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 PEAK_GBS = 8000.0       # MI355X HBM3E peak, GB/s
-VARIANTS = ("config1", "dense_128k", "group16", "paged", "unified_max", "ffd", "ffd_peaked",
-            "multi_row", "append")
+VARIANTS = ("config1", "dense_128k", "group16", "paged", "paged_multi", "unified_max", "ffd",
+            "ffd_peaked", "multi_row", "append")
 METRIC = "us/decode step and achieved KV-read HBM GB/s (% of peak) at 32K-128K ctx"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_partial_dense_b8_h32x8_d128_l32768.txt")
 # everything that decides the partial kernel's code: its sources, the
@@ -571,6 +572,46 @@ def variant_paged(torch, fd, W, args, timer):
                 pct_of_peak=round(100 * gbs(nbytes, t["ms"]) / PEAK_GBS, 1))
 
 
+def variant_paged_multi(torch, fd, W, args, timer):
+    """Four new tokens per sequence over the paged workload's cache (16
+    sequences of U[1024, 131072] positions, pages of 16, chunk 1024): G*M =
+    16 query rows per kv-head on the matrix-core kernel."""
+    cfg = W.CONFIGS[3]
+    M = 4
+    c = W.paged_case(cfg["B"], cfg["Hq"], cfg["Hkv"], cfg["d"], cfg["len_lo"], cfg["len_hi"],
+                     page=cfg["page"], chunk=cfg["chunk"], seed=cfg["seed"], device="cuda:0",
+                     M=M)
+    B, _, Hq, d = c.q.shape
+    Hkv = c.k_pool.shape[1]
+    lens = c.meta["lens"]
+    max_len = int(max(lens))
+    lib = fd.lib()
+    out = torch.empty((B, M, Hq, d), dtype=torch.float32, device="cuda:0")
+    lse = torch.empty((B, M, Hq), dtype=torch.float32, device="cuda:0")
+    wsn = fd.workspace_bytes("fd_decode_attn_multi_paged", B=B, M=M, Hq=Hq, Hkv=Hkv, d=d,
+                             page=c.page, max_pages=c.block_table.shape[1],
+                             max_seq_len=max_len, chunk=c.chunk)
+    ws = torch.empty(wsn, dtype=torch.uint8, device="cuda:0")
+    size = C.c_size_t(wsn)
+    st = C.c_void_p(torch.cuda.current_stream().cuda_stream)
+    a = (fd.FD_BF16, vp(c.q), vp(c.k_pool), vp(c.v_pool), vp(c.block_table), vp(c.seq_lens),
+         vp(out), vp(lse), B, M, Hq, Hkv, d, c.page, c.block_table.shape[1],
+         c.k_pool.shape[0], max_len, c.scale, c.chunk, vp(ws), C.byref(size), st)
+    call = lambda: lib.fd_decode_attn_multi_paged(*a)  # noqa: E731
+    check_rc(lib, call())
+    t = timer.run([call], args.steps, args.warmup)
+    total_len = int(sum(lens))
+    nbytes = (2 * total_len * Hkv * d * 2 + B * M * Hq * d * 2 + B * M * Hq * (d + 1) * 4
+              + 4 * int(sum((L + c.page - 1) // c.page for L in lens)))
+    return dict(workload=f"paged ragged multi-row decode bf16, M={M} tokens, B={B}, Hq={Hq}, "
+                         f"Hkv={Hkv}, d={d}, page={c.page}, lens U[{cfg['len_lo']},"
+                         f"{cfg['len_hi']}] (sum {total_len}), chunk={c.chunk}",
+                us_per_step=round(t["ms"] * 1e3, 2), p10_us=round(t["p10"] * 1e3, 2),
+                p90_us=round(t["p90"] * 1e3, 2), bytes=nbytes,
+                gbs=round(gbs(nbytes, t["ms"]), 1),
+                pct_of_peak=round(100 * gbs(nbytes, t["ms"]) / PEAK_GBS, 1))
+
+
 def variant_unified(torch, fd, W, args, timer):
     c = W.config_case(4, device="cuda:0")
     B, Hq, d = c.q.shape
@@ -860,6 +901,7 @@ def main():
     if not args.no_variants:
         fns = dict(config1=variant_config1, dense_128k=variant_dense_128k,
                    group16=variant_group16, paged=variant_paged,
+                   paged_multi=variant_paged_multi,
                    unified_max=variant_unified, ffd=variant_ffd, ffd_peaked=variant_ffd_peaked,
                    multi_row=variant_multi, append=variant_append)
         line["variants"] = {name: fns[name](torch, fd, W, args, timer)

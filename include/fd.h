@@ -137,7 +137,8 @@ int fd_decode_attn_noalloc(fd_dtype_t dt, const void* q, const void* k, const vo
  * fp32 [B, Hq] (nullable):
  *   M = max_c m_c, out = sum_c 2^(m_c-M) O_c / sum_c 2^(m_c-M) l_c,
  *   lse = ln 2 * (M + log2 sum_c 2^(m_c-M) l_c).
- * n_chunks >= 1; o_part and ml_part 16-byte aligned.
+ * A row whose chunks are all empty (every l_c = 0, m_c = -inf) gets out = 0
+ * and lse = -inf.  n_chunks >= 1; o_part and ml_part 16-byte aligned.
  */
 int fd_decode_attn_partials(fd_dtype_t dt, const void* q, const void* k,
                             const void* v, int B, int Hq, int Hkv, int L, int d,
@@ -222,6 +223,32 @@ int fd_decode_attn_multi(fd_dtype_t dt, const void* q, const void* k,
                          const void* v, float* out, float* lse, int B, int M,
                          int Hq, int Hkv, int L, int d, float scale, int chunk,
                          void* ws, size_t* ws_bytes, void* stream);
+
+/*
+ * fd_decode_attn_multi over a paged cache (the pools, block table and
+ * lengths of fd_decode_attn_paged): sequence b holds seq_lens[b] positions,
+ * its M new tokens' keys and values among them at seq_lens[b]-M ..
+ * seq_lens[b]-1, and token r attends to positions 0 .. seq_lens[b]-M+r
+ * ("Flash Decoding" explainer, sections 1 and 3).  A token with no position
+ * to attend to (seq_lens[b]-M+r < 0) gets out = 0, lse = -inf.
+ *   q    [B, M, Hq, d];  out fp32 [B, M, Hq, d];  lse fp32 [B, M, Hq] or NULL
+ *   M = 1 and G in {1, 2, 4, 8}: the kernel of fd_decode_attn_paged (bf16
+ *   or fp32, page_size in [8, 1024]).  Otherwise the matrix-core kernels:
+ *   bf16, G*M <= 32, page_size a power of two in [16, 1024] and chunk /
+ *   page_size <= 256, else FD_ERR_UNSUPPORTED.  The chunk is the split (the
+ *   lengths live on the device), and only chunks that hold positions are
+ *   computed, spread evenly over the device.
+ * Workspace: the partials of B*M*Hq rows over ceil(max_seq_len / chunk)
+ * chunks (layout of fd_decode_attn_partials with M*Hq heads).  Device-side
+ * values are clamped as in fd_decode_attn_paged.
+ */
+int fd_decode_attn_multi_paged(fd_dtype_t dt, const void* q, const void* k_pool,
+                               const void* v_pool, const int32_t* block_table,
+                               const int32_t* seq_lens, float* out, float* lse,
+                               int B, int M, int Hq, int Hkv, int d, int page_size,
+                               int max_pages_per_seq, int num_pages, int max_seq_len,
+                               float scale, int chunk, void* ws, size_t* ws_bytes,
+                               void* stream);
 
 /*
  * Cache append ("Flash Decoding" explainer, section 3: each generated token

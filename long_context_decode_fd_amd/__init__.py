@@ -258,6 +258,42 @@ def decode_attn_multi(q, k, v, chunk=512, scale=None, out=None, lse=None, want_l
     return out, lse
 
 
+def decode_attn_multi_paged(q, k_pool, v_pool, block_table, seq_lens, max_seq_len, chunk=512,
+                            scale=None, out=None, lse=None, want_lse=True, workspace=None):
+    """Multi-row decode over a paged cache: q [B,M,Hq,d], pools [P,Hkv,page,d],
+    block_table int32 [B,max_pages], seq_lens int32 [B] (device; sequence b's M
+    new tokens sit at seq_lens[b]-M..seq_lens[b]-1), max_seq_len a host bound.
+    Returns (out fp32 [B,M,Hq,d], lse fp32 [B,M,Hq] or None)."""
+    B, M, Hq, d = q.shape
+    P, Hkv, page = k_pool.shape[0], k_pool.shape[1], k_pool.shape[2]
+    dev = q.device
+    _need(q, "q", device=dev)
+    _need(k_pool, "k_pool", (P, Hkv, page, d), q.dtype, dev)
+    _need(v_pool, "v_pool", (P, Hkv, page, d), q.dtype, dev)
+    _need(block_table, "block_table", dtype=torch.int32, device=dev)
+    _need(seq_lens, "seq_lens", (B,), torch.int32, dev)
+    if block_table.dim() != 2 or block_table.shape[0] != B:
+        raise ValueError("block_table must be [B, max_pages]")
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    if out is None:
+        out = torch.empty((B, M, Hq, d), dtype=torch.float32, device=dev)
+    _need(out, "out", (B, M, Hq, d), torch.float32, dev)
+    if lse is None and want_lse:
+        lse = torch.empty((B, M, Hq), dtype=torch.float32, device=dev)
+    if lse is not None:
+        _need(lse, "lse", (B, M, Hq), torch.float32, dev)
+    L_ = lib()
+    st = _stream(dev)
+
+    def args(ws, wsb):
+        return (_dt(q), _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(block_table),
+                _ptr(seq_lens), _ptr(out), _ptr(lse), B, M, Hq, Hkv, d, page,
+                block_table.shape[1], P, int(max_seq_len), scale, int(chunk), ws, wsb, st)
+    workspace, size = _workspace(L_.fd_decode_attn_multi_paged, args, workspace, dev)
+    _abi.check(L_.fd_decode_attn_multi_paged(*args(_ptr(workspace), C.byref(size))))
+    return out, lse
+
+
 def kv_append(k_new, v_new, k_cache, v_cache, t):
     """Write k_new/v_new [B,Hkv,M,d] into rows t..t+M-1 of the contiguous
     caches [B,Hkv,L_cap,d] (same dtype)."""
@@ -364,6 +400,13 @@ def workspace_bytes(entry: str, **kw) -> int:
         rc = L_.fd_decode_attn_multi(g("dt", FD_BF16), None, None, None, None, None, g("B"),
                                      g("M"), g("Hq"), g("Hkv"), g("L"), g("d"), g("scale", 0.1),
                                      g("chunk"), None, C.byref(need), None)
+    elif entry == "fd_decode_attn_multi_paged":
+        rc = L_.fd_decode_attn_multi_paged(g("dt", FD_BF16), None, None, None, None, None,
+                                           None, None, g("B"), g("M"), g("Hq"), g("Hkv"),
+                                           g("d"), g("page", 16), g("max_pages"),
+                                           g("num_pages", 1), g("max_seq_len"),
+                                           g("scale", 0.1), g("chunk"), None, C.byref(need),
+                                           None)
     elif entry == "fd_decode_attn_unified_max":
         rc = L_.fd_decode_attn_unified_max(g("dt", FD_BF16), None, None, None, None, None,
                                            g("B"), g("Hq"), g("Hkv"), g("L"), g("d"),

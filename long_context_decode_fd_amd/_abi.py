@@ -36,6 +36,8 @@ SIGNATURES = {
                                    _f, _i, _f, _f, _f, _vp, _vp, _szp, _vp],
     "fd_decode_attn_multi": [_i, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _f, _i,
                              _vp, _szp, _vp],
+    "fd_decode_attn_multi_paged": [_i, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i,
+                                   _i, _i, _i, _i, _i, _f, _i, _vp, _szp, _vp],
     "fd_kv_append": [_i, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _vp],
     "fd_kv_append_paged": [_i, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i,
                            _vp],

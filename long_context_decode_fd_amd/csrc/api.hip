@@ -83,6 +83,24 @@ int check_dense_group(fd_dtype_t dt, int G, int M) {
   return FD_OK;
 }
 
+// Paged cache arguments of both paged entry points; *shift = log2(page).
+int check_pages(int chunk, int page_size, int min_page, int max_pages_per_seq, int num_pages,
+                int max_seq_len, int* shift) {
+  if (page_size < min_page || page_size > 1024 || (page_size & (page_size - 1)) != 0)
+    return fail(FD_ERR_ARG, "page_size=%d must be a power of two in [%d, 1024]", page_size,
+                min_page);
+  if (chunk % page_size != 0)
+    return fail(FD_ERR_ARG, "chunk=%d must be a multiple of page_size=%d", chunk, page_size);
+  if (max_pages_per_seq <= 0 || num_pages <= 0)
+    return fail(FD_ERR_ARG, "max_pages_per_seq and num_pages must be positive");
+  if (max_seq_len < 0 || (long long)max_seq_len > (long long)max_pages_per_seq * page_size)
+    return fail(FD_ERR_ARG, "max_seq_len=%d outside [0, max_pages_per_seq*page_size]",
+                max_seq_len);
+  *shift = 0;
+  while ((1 << *shift) < page_size) ++*shift;
+  return FD_OK;
+}
+
 int check_chunk(int chunk) {
   if (chunk <= 0 || chunk % 16 != 0 || chunk > 65536)
     return fail(FD_ERR_ARG, "chunk=%d must be a positive multiple of 16 <= 65536", chunk);
@@ -176,19 +194,33 @@ int run_split_kv(int mode, fd_dtype_t dt, const void* q, const void* k, const vo
 // either.
 int run_multi(const void* q, const void* k, const void* v, float* out, float* lse, int B,
               int M, int Hq, int Hkv, int L, int d, float scale, int chunk, int nc, void* ws,
-              bool fold, void* stream) {
+              bool fold, void* stream, const fdk::MultiArgs* paged = nullptr) {
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   fdk::MultiArgs ma{q, k, v, nullptr, nullptr, B, M, Hq, Hkv, L, chunk, nc,
-                    (float)((double)scale * 1.4426950408889634)};
-  const int F = fold ? fdk::multi_fold(d, ma) : 1;
-  const long long split = (long long)chunk * F;
-  ma.chunk = split > L ? L : (int)split;
-  ma.nc = n_chunks_of(L, ma.chunk);
+                    (float)((double)scale * 1.4426950408889634), nullptr, nullptr, 0, 0, 0};
+  if (paged != nullptr) {
+    ma.block_table = paged->block_table;
+    ma.seq_lens = paged->seq_lens;
+    ma.page_shift = paged->page_shift;
+    ma.max_pages = paged->max_pages;
+    ma.num_pages = paged->num_pages;
+  }
+  if (nc > 0) {
+    // paged: the caller's chunk is the split (the lengths that would decide
+    // a longer one live on the device; the kernels spread the chunks that
+    // hold positions evenly over the waves)
+    const int F = fold && paged == nullptr ? fdk::multi_fold(d, ma) : 1;
+    const long long split = (long long)chunk * F;
+    ma.chunk = split > L ? L : (int)split;
+    ma.nc = n_chunks_of(L, ma.chunk);
+  }
   split_ws(ws, B, M * Hq, ma.nc, d, &ma.o_part, &ma.ml_part);
-  hipError_t e = fdk::launch_multi(d, ma, s);
-  if (e != hipSuccess) return hip_status(e, "multi-row kernel launch");
+  if (ma.nc > 0) {
+    hipError_t e = fdk::launch_multi(d, ma, s);
+    if (e != hipSuccess) return hip_status(e, "multi-row kernel launch");
+  }
   if (out == nullptr) return ok();
-  fdk::MergeArgs mg{ma.o_part, ma.ml_part, out, lse, nullptr, M * Hq, ma.nc, ma.chunk, L};
+  fdk::MergeArgs mg{ma.o_part, ma.ml_part, out, lse, ma.seq_lens, M * Hq, ma.nc, ma.chunk, L};
   return hip_status(fdk::launch_merge(d, B, mg, s), "merge kernel launch");
 }
 
@@ -329,19 +361,11 @@ int fd_decode_attn_paged(fd_dtype_t dt, const void* q, const void* k_pool,
   if (int e = check_vector_group(Hq / Hkv)) return e;
   if (int e = check_chunk(chunk)) return e;
   if (int e = check_scale(scale)) return e;
-  if (page_size < 8 || page_size > 1024 || (page_size & (page_size - 1)) != 0)
-    return fail(FD_ERR_ARG, "page_size=%d must be a power of two in [8, 1024]", page_size);
-  if (chunk % page_size != 0)
-    return fail(FD_ERR_ARG, "chunk=%d must be a multiple of page_size=%d", chunk, page_size);
+  int shift = 0;
+  if (int e = check_pages(chunk, page_size, 8, max_pages_per_seq, num_pages, max_seq_len, &shift))
+    return e;
   if (chunk / page_size > 1024)
     return fail(FD_ERR_UNSUPPORTED, "chunk/page_size=%d exceeds 1024", chunk / page_size);
-  if (max_pages_per_seq <= 0 || num_pages <= 0)
-    return fail(FD_ERR_ARG, "max_pages_per_seq and num_pages must be positive");
-  if (max_seq_len < 0 || (long long)max_seq_len > (long long)max_pages_per_seq * page_size)
-    return fail(FD_ERR_ARG, "max_seq_len=%d outside [0, max_pages_per_seq*page_size]",
-                max_seq_len);
-  int shift = 0;
-  while ((1 << shift) < page_size) ++shift;
   const int nc = n_chunks_of(max_seq_len, chunk);
   if (int e = check_units(B, Hq, nc)) return e;
   if (int e = workspace_gate(ws, ws_bytes, partial_bytes(B, Hq, nc, d))) return e;
@@ -416,6 +440,58 @@ int fd_decode_attn_multi(fd_dtype_t dt, const void* q, const void* k, const void
                         pa, ws, nullptr, L, stream);
   }
   return run_multi(q, k, v, out, lse, B, M, Hq, Hkv, L, d, scale, chunk, nc, ws, true, stream);
+}
+
+int fd_decode_attn_multi_paged(fd_dtype_t dt, const void* q, const void* k_pool,
+                               const void* v_pool, const int32_t* block_table,
+                               const int32_t* seq_lens, float* out, float* lse, int B, int M,
+                               int Hq, int Hkv, int d, int page_size, int max_pages_per_seq,
+                               int num_pages, int max_seq_len, float scale, int chunk, void* ws,
+                               size_t* ws_bytes, void* stream) {
+  if (int e = check_dtype(&dt)) return e;
+  if (int e = check_heads(B, Hq, Hkv, d)) return e;
+  if (M <= 0) return fail(FD_ERR_ARG, "M=%d must be positive", M);
+  if (int e = check_dense_group(dt, Hq / Hkv, M)) return e;
+  if (int e = check_chunk(chunk)) return e;
+  if (int e = check_scale(scale)) return e;
+  const bool matrix = matrix_path(Hq / Hkv, M);
+  int shift = 0;
+  if (int e = check_pages(chunk, page_size, 8, max_pages_per_seq, num_pages, max_seq_len, &shift))
+    return e;
+  if (matrix && page_size < 16)
+    return fail(FD_ERR_UNSUPPORTED, "page_size=%d: the matrix-core kernels take pages of 16 "
+                                    "positions or more", page_size);
+  if (chunk / page_size > (matrix ? fdk::kMultiPagePids : 1024))
+    return fail(FD_ERR_UNSUPPORTED, "chunk/page_size=%d exceeds %d", chunk / page_size,
+                matrix ? fdk::kMultiPagePids : 1024);
+  const int nc = n_chunks_of(max_seq_len, chunk);
+  if (int e = check_units(B, M * Hq, nc)) return e;
+  if (int e = workspace_gate(ws, ws_bytes, partial_bytes(B, M * Hq, nc, d))) return e;
+  if (ws == nullptr) return ok();
+  if (!q || !k_pool || !v_pool || !block_table || !seq_lens || !out)
+    return fail(FD_ERR_ARG, "q, pools, block_table, seq_lens and out must not be NULL");
+  if (!aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool) || !aligned16(out))
+    return fail(FD_ERR_ARG, "q, pools and out must be 16-byte aligned");
+  if (!matrix) {
+    // one token, a group the vector kernel takes: the paged single-query path
+    fdk::PartialArgs pa{};
+    pa.block_table = block_table;
+    pa.seq_lens = seq_lens;
+    pa.page_shift = shift;
+    pa.max_pages = max_pages_per_seq;
+    pa.num_pages = num_pages;
+    pa.max_seq_len = max_seq_len;
+    return run_split_kv(fdk::kPaged, dt, q, k_pool, v_pool, out, lse, B, Hq, Hkv, 0, d, scale,
+                        chunk, nc, pa, ws, seq_lens, max_seq_len, stream);
+  }
+  fdk::MultiArgs pg{};
+  pg.block_table = block_table;
+  pg.seq_lens = seq_lens;
+  pg.page_shift = shift;
+  pg.max_pages = max_pages_per_seq;
+  pg.num_pages = num_pages;
+  return run_multi(q, k_pool, v_pool, out, lse, B, M, Hq, Hkv, max_seq_len, d, scale, chunk, nc,
+                   ws, true, stream, &pg);
 }
 
 int fd_kv_append(fd_dtype_t dt, const void* k_new, const void* v_new, void* k_cache,

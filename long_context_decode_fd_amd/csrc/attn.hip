@@ -525,6 +525,9 @@ void partial_kernel(PartialArgs a) {
 // section 2, steps 2-4, with unnormalised O_i):
 //   M = max_i m_i,  w_i = 2^(m_i - M),
 //   out = sum_i w_i O_i / sum_i w_i l_i,  lse = (M + log2 sum_i w_i l_i) ln 2.
+// A row whose chunks are all empty (a query token of a paged sequence
+// shorter than its position) has sum_i w_i l_i = 0: out = 0, lse = -inf,
+// the empty softmax.
 // This kernel takes rows of more than 256 chunks (shorter rows take
 // merge_wave_kernel below): one workgroup of W waves per (sequence, query
 // head, slice of D / CS columns), so that more loads share one memory
@@ -640,7 +643,7 @@ __global__ __launch_bounds__(W * kWave) void merge_kernel(MergeArgs a) {
 #pragma unroll
     for (int i = 0; i < W; i += 2) den += s_red[i] + s_red[i + 1];
     reinterpret_cast<f32x4*>(a.out + row * D)[cs * CG + tid] =
-        f32x4{t.x / den, t.y / den, t.z / den, t.w / den};
+        den > 0.f ? f32x4{t.x / den, t.y / den, t.z / den, t.w / den} : f32x4{0.f, 0.f, 0.f, 0.f};
     if (tid == 0 && cs == 0 && a.lse != nullptr) a.lse[row] = (M + log2_hw(den)) * kLn2;
   }
 }
@@ -723,7 +726,8 @@ __global__ __launch_bounds__(kWave) void merge_wave_kernel(MergeArgs a) {
   acc.w = sum_lanes(acc.w);
   if (cl == 0)
     reinterpret_cast<f32x4*>(a.out + row * D)[cs * CG + cg] =
-        f32x4{acc.x / den, acc.y / den, acc.z / den, acc.w / den};
+        den > 0.f ? f32x4{acc.x / den, acc.y / den, acc.z / den, acc.w / den}
+                  : f32x4{0.f, 0.f, 0.f, 0.f};
   if (lane == 0 && cs == 0 && a.lse != nullptr) a.lse[row] = (M + log2_hw(den)) * kLn2;
 }
 

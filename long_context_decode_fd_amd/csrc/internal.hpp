@@ -82,7 +82,16 @@ struct MultiArgs {
   float* ml_part;
   int B, M, Hq, Hkv, L, chunk, nc;
   float c_log2;
+  // Paged caches (block_table != nullptr): k and v are pools [P, Hkv, page,
+  // D], page = 2^page_shift >= 16; sequence b holds min(max(seq_lens[b], 0),
+  // L) positions (L = the longest) through block_table[b * max_pages + i];
+  // page ids are clamped to [0, num_pages).  A split (= chunk) covers at
+  // most kMultiPagePids pages.
+  const int32_t* block_table;
+  const int32_t* seq_lens;
+  int page_shift, max_pages, num_pages;
 };
+constexpr int kMultiPagePids = 256;
 hipError_t launch_multi(int D, const MultiArgs& a, hipStream_t s);
 // Chunks per split for the multi-row kernels: the number of consecutive
 // chunks of a row that one split covers, chosen so that the splits fill the

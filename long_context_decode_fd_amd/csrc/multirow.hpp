@@ -70,8 +70,105 @@ __device__ __forceinline__ void split_bf16(const float (&p)[4], u32x2& hi, u32x2
   lo = u32x2{l[0], l[1]};
 }
 
-// One query tile of R = G*M <= 16 rows per wave.
-template <int D>
+// Paged caches: the block-table entries of a split [c0, c1) of sequence b,
+// kMultiPagePids / 64 per lane, read into registers first and written to
+// the wave's LDS copy later (clamped to [0, num_pages)), so that the wait for
+// them does not hold up the K and V loads issued before them.
+constexpr int kPidPerLane = kMultiPagePids / kWave;
+
+__device__ __forceinline__ void page_ids_load(const MultiArgs& a, int b, int c0, int c1,
+                                              int lane, int (&v)[kPidPerLane]) {
+  const int shift = a.page_shift;
+  const int npg = c1 > c0 ? (c1 - c0 + (1 << shift) - 1) >> shift : 0;
+  const int32_t* bt = a.block_table + (size_t)b * a.max_pages + (c0 >> shift);
+#pragma unroll
+  for (int j = 0; j < kPidPerLane; ++j) {
+    const int i = lane + j * kWave;
+    v[j] = i < npg ? bt[i] : 0;
+  }
+}
+
+__device__ __forceinline__ void page_ids_store(const MultiArgs& a, int* dst, int lane,
+                                               const int (&v)[kPidPerLane]) {
+#pragma unroll
+  for (int j = 0; j < kPidPerLane; ++j) dst[lane + j * kWave] = min(max(v[j], 0), a.num_pages - 1);
+}
+
+// Paged caches: the units that hold positions, (b, kvh, c) with
+// c < ceil(L_b / chunk), numbered sequence after sequence, kv-head-major
+// inside a sequence, so that a wave's consecutive units are consecutive
+// chunks of one (sequence, kv-head) and no wave waits on empty ones.  The
+// walker's state is wave-uniform; lengths come through the scalar cache
+// (their wait is on the scalar counter, not on the vector-memory counter of
+// the K and V loads in flight).
+struct PagedWalk {
+  int b, first, units;   // sequence b's units are [first, first + units)
+};
+
+__device__ __forceinline__ int paged_len_u(const MultiArgs& a, int b) {
+  const auto* sl = (const __attribute__((address_space(4))) int32_t*)a.seq_lens;
+  return min(max(sl[__builtin_amdgcn_readfirstlane(b)], 0), a.L);
+}
+
+// units of sequence b (b < B)
+__device__ __forceinline__ int paged_units_u(const MultiArgs& a, int b) {
+  return a.Hkv * ((paged_len_u(a, b) + a.chunk - 1) / a.chunk);
+}
+
+// Units of the whole call, and the walker positioned at the sequence that
+// holds unit u (u below the total; else at the end): 64 sequences per step,
+// an inclusive scan across the lanes, the first lane whose running total
+// passes u.
+__device__ __forceinline__ int paged_walk_start(const MultiArgs& a, int lane, int u,
+                                                PagedWalk& w) {
+  int first = 0, found = 0;
+  w.b = a.B;
+  w.first = 0;
+  w.units = 0;
+  for (int base = 0; base < a.B; base += kWave) {   // wave-uniform
+    const int bb = base + lane;
+    const int mine = bb < a.B
+                         ? a.Hkv * ((min(max(a.seq_lens[bb], 0), a.L) + a.chunk - 1) / a.chunk)
+                         : 0;
+    int incl = mine;
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+      const int t = __shfl_up(incl, o);
+      if (lane >= o) incl += t;
+    }
+    const int total = __builtin_amdgcn_readlane(incl, kWave - 1);
+    if (!found && u < first + total) {
+      const uint64_t past = __builtin_amdgcn_ballot_w64(first + incl > u);
+      const int l = (int)__builtin_ctzll(past);
+      w.b = base + l;
+      w.units = __builtin_amdgcn_readlane(mine, l);
+      w.first = first + __builtin_amdgcn_readlane(incl, l) - w.units;
+      found = 1;
+    }
+    first += total;
+  }
+  return first;
+}
+
+// (b, kvh, c) of unit u; u must not decrease from call to call
+__device__ __forceinline__ void paged_walk_decode(const MultiArgs& a, int u, PagedWalk& w,
+                                                  int& b, int& kvh, int& c) {
+  while (u >= w.first + w.units) {   // wave-uniform
+    w.first += w.units;
+    ++w.b;
+    w.units = paged_units_u(a, w.b);
+  }
+  b = w.b;
+  const int ns = w.units / a.Hkv;
+  const int r = u - w.first;
+  kvh = r / ns;
+  c = r - kvh * ns;
+}
+
+// One query tile of R = G*M <= 16 rows per wave.  PAGED: k and v are page
+// pools (MultiArgs), each 16-row tile lies in one page (pages of 16 rows or
+// more, tiles aligned to 16).
+template <int D, bool PAGED>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1)))
 void multi_kernel(MultiArgs a) {
   constexpr int KS = D / 32;             // QK k-steps (32 dims each)
@@ -87,6 +184,8 @@ void multi_kernel(MultiArgs a) {
   constexpr int ORPI = kWave * 16 / (D * 4);   // O rows per wave store
   static_assert(16 * OSTR <= 2 * 16 * LSTR, "O staging must fit the wave's K/V tiles");
   __shared__ __align__(16) unsigned char s_kv[kWaves][2][16 * LSTR];
+  // paged: page ids of the wave's current and next split
+  __shared__ int s_pid[PAGED ? kWaves : 1][2][PAGED ? kMultiPagePids : 1];
 
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & (kWave - 1);
   const int n = lane & 15, qd = lane >> 4;
@@ -104,23 +203,49 @@ void multi_kernel(MultiArgs a) {
   const int tr_off = (4 * qd + (n >> 2)) * LSTR + 8 * (n & 3);
   const float c_log2 = a.c_log2;
 
+  // a unit: sequence b (holding L positions), kv-head, split c = [c0, c1)
+  // (empty when a paged sequence is shorter than the split's start)
   struct UnitM {
-    int b, kvh, c, c0, c1;
+    int b, kvh, c, c0, c1, L;
   };
+  auto seq_len = [&](int b) {
+    if constexpr (PAGED) {
+      const auto* sl = (const __attribute__((address_space(4))) int32_t*)a.seq_lens;
+      return min(max(sl[__builtin_amdgcn_readfirstlane(b)], 0), a.L);
+    } else {
+      return a.L;
+    }
+  };
+  PagedWalk walk{};   // paged: the units that hold positions
   auto decode = [&](int u, UnitM& x) {
-    x.c = u % a.nc;
-    const int bk = u / a.nc;
-    x.kvh = bk % a.Hkv;
-    x.b = bk / a.Hkv;
+    if constexpr (PAGED) {
+      paged_walk_decode(a, u, walk, x.b, x.kvh, x.c);
+    } else {
+      x.c = u % a.nc;
+      const int bk = u / a.nc;
+      x.kvh = bk % a.Hkv;
+      x.b = bk / a.Hkv;
+    }
+    x.L = seq_len(x.b);
     x.c0 = x.c * a.chunk;
-    x.c1 = min(x.c0 + a.chunk, a.L);
+    x.c1 = min(x.c0 + a.chunk, x.L);
   };
-  auto base_of = [&](const void* t, const UnitM& x) {
-    return reinterpret_cast<const char*>(t) + ((size_t)x.b * a.Hkv + x.kvh) * (size_t)a.L * ROWB;
+  // first byte of row t0 (a multiple of 16 in [c0, c1) when `used`; else
+  // nothing is read there and any row will do) of unit x's K or V
+  const int shift = a.page_shift, pmask = (1 << a.page_shift) - 1;
+  auto row_base = [&](const void* t, const UnitM& x, int buf, int t0, bool used) {
+    if constexpr (PAGED) {
+      const int p = used ? s_pid[wave][buf][(t0 - x.c0) >> shift] : 0;
+      const int pc = __builtin_amdgcn_readfirstlane(p);
+      return reinterpret_cast<const char*>(t) +
+             ((((size_t)pc * a.Hkv + x.kvh) << shift) + (size_t)(t0 & pmask)) * ROWB;
+    } else {
+      return reinterpret_cast<const char*>(t) +
+             (((size_t)x.b * a.Hkv + x.kvh) * (size_t)a.L + (size_t)t0) * ROWB;
+    }
   };
   // Query row n of this lane: token r = n / G, head kvh*G + n % G; its last
   // visible position is L - M + r.  Rows >= R are padding (q = 0).
-  const int lim = a.L - a.M + n / G;
   u32x4 qf[KS];
   auto load_q = [&](const UnitM& x) {
     if (n < R) {
@@ -143,12 +268,13 @@ void multi_kernel(MultiArgs a) {
   // their p is 0).  The range check covers the lane offset plus the
   // immediate; the scalar offset is 0.
   const int lane_off = lrow * ROWB + 16 * lcol;
-  auto issue = [&](const char* __restrict__ src, int T, int c1, u32x4 (&r)[TT][NI]) {
+  auto issue = [&](const void* t, const UnitM& x, int buf, int T, int c1,
+                   u32x4 (&r)[TT][NI]) {
 #pragma unroll
     for (int tt = 0; tt < TT; ++tt) {
       const int t0 = T + 16 * tt;
       const int nrow = min(max(c1 - t0, 0), 16);
-      const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(src + (size_t)t0 * ROWB, nrow * ROWB);
+      const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(row_base(t, x, buf, t0, nrow > 0), nrow * ROWB);
 #pragma unroll
       for (int i = 0; i < NI; ++i) r[tt][i] = ld16_buf(rs, lane_off + RPI * i * ROWB);
     }
@@ -160,14 +286,13 @@ void multi_kernel(MultiArgs a) {
       *reinterpret_cast<u32x4*>(dst + (RPI * i + lrow) * LSTR + 16 * lcol) = r[i];
   };
 
-  // Partials of unit uu, rows ((b*M + r)*Hq + h)*nc + c.  O goes through the
+  // Partials of unit x, rows ((b*M + r)*Hq + h)*nc + c.  O goes through the
   // wave's LDS tiles (free between units: the next unit's K rows are still
   // in registers) so that every store writes 16 bytes per lane and whole
   // rows, instead of 4 bytes per lane in 64-byte pieces.
   unsigned char* ost = s_kv[wave][0];
-  auto store_unit = [&](const f32x4 (&o)[DB], float m, float l, int uu) {
-    UnitM x;
-    decode(uu, x);
+  // (x as decoded when the unit ran: the paged walker only moves forward)
+  auto store_unit = [&](const f32x4 (&o)[DB], float m, float l, const UnitM& x) {
     if (qd == 0 && n < R) {
       const size_t prow =
           (((size_t)x.b * a.M + n / G) * a.Hq + (size_t)x.kvh * G + n % G) * a.nc + x.c;
@@ -200,23 +325,38 @@ void multi_kernel(MultiArgs a) {
   constexpr int H = kMrHold;
   f32x4 hold_o[H][DB];
   float hold_m[H], hold_l[H];
-  int hold_u[H];
+  UnitM hold_x[H];
   int held = 0;   // wave-uniform
 
   // wave w takes the consecutive units [w*per, (w+1)*per): consecutive
   // chunks of one (sequence, kv-head), a single contiguous stretch of K and
   // V (measured 186 -> 174 us at M = 4 against taking every W-th unit)
-  const int per = (n_units + stride - 1) / stride;
+  const int wid = (int)blockIdx.x * kWaves + wave;
+  int total = n_units;
+  if constexpr (PAGED) {
+    // the units that hold positions, split evenly (the walker is placed at
+    // the wave's first unit below)
+    const int t = paged_walk_start(a, lane, 0, walk);
+    total = t;
+  }
+  const int per = (total + stride - 1) / stride;
   // wave-uniform by construction; readfirstlane lets the compiler keep the
   // unit (and the descriptors built from it) in scalar registers
-  int u = __builtin_amdgcn_readfirstlane(((int)blockIdx.x * kWaves + wave) * per);
-  const int u_end = min(u + per, n_units);
-  if (u >= n_units) return;
+  int u = __builtin_amdgcn_readfirstlane(wid * per);
+  const int u_end = min(u + per, total);
+  if (u >= total) return;
+  if constexpr (PAGED) paged_walk_start(a, lane, u, walk);
   UnitM cur;
   decode(u, cur);
   u32x4 kr[TT][NI], vr[TT][NI];
+  int buf = 0;   // LDS copy of the current unit's page ids (paged)
+  int pid[kPidPerLane];
+  if constexpr (PAGED) {
+    page_ids_load(a, cur.b, cur.c0, cur.c1, lane, pid);
+    page_ids_store(a, s_pid[wave][0], lane, pid);
+  }
   load_q(cur);
-  issue(base_of(a.k, cur), cur.c0, cur.c1, kr);
+  issue(a.k, cur, buf, cur.c0, cur.c1, kr);
   // The last batch of a unit requests the next unit's query and first K rows
   // before the unit's partials are stored: stores count on the same
   // vector-memory counter as loads, so loads issued after them would wait.
@@ -225,16 +365,18 @@ void multi_kernel(MultiArgs a) {
     const bool has_next = un < u_end;
     UnitM nxt = cur;
     if (has_next) decode(un, nxt);
+    if constexpr (PAGED) {
+      if (has_next) page_ids_load(a, nxt.b, nxt.c0, nxt.c1, lane, pid);
+    }
     const int c0 = cur.c0, c1 = cur.c1;
-    const char* kb = base_of(a.k, cur);
-    const char* vb = base_of(a.v, cur);
+    const int lim = cur.L - a.M + n / G;
 
     f32x4 o[DB];
     float m = kNegInf, l = 0.f;   // row's running maximum (raw) and this lane's part of l
 #pragma unroll
     for (int db = 0; db < DB; ++db) o[db] = f32x4{0.f, 0.f, 0.f, 0.f};
     for (int T = c0; T < c1; T += STEP) {
-      issue(vb, T, c1, vr);
+      issue(a.v, cur, buf, T, c1, vr);
       float sc[TT][4];
 #pragma unroll
       for (int tt = 0; tt < TT; ++tt) {
@@ -257,17 +399,19 @@ void multi_kernel(MultiArgs a) {
       // all paths and P V waits for this batch's V rows only, not for these
       // loads (measured 189 -> 182 us at M = 4)
       {
-        const char* src = kb;
-        int t_next = T + STEP, c_end = c1;
+        UnitM xs = cur;
+        int t_next = T + STEP, c_end = c1, b_next = buf;
         if (T + STEP >= c1 && has_next) {
           load_q(nxt);
-          src = base_of(a.k, nxt);
+          if constexpr (PAGED) page_ids_store(a, s_pid[wave][buf ^ 1], lane, pid);
+          xs = nxt;
           t_next = nxt.c0;
           c_end = nxt.c1;
+          b_next = buf ^ 1;
         } else if (T + STEP >= c1) {
           t_next = T;
         }
-        issue(src, t_next, c_end, kr);
+        issue(a.k, xs, b_next, t_next, c_end, kr);
       }
 
       float bm = kNegInf;
@@ -330,18 +474,28 @@ void multi_kernel(MultiArgs a) {
         hold_l[h] = l;
 #pragma unroll
         for (int db = 0; db < DB; ++db) hold_o[h][db] = o[db];
-        hold_u[h] = u;
+        hold_x[h] = cur;
+      }
+    }
+    if constexpr (PAGED) {
+      // an empty split ran no batch, so nothing requested the next one's
+      // query and first K rows yet
+      if (c1 <= c0 && has_next) {
+        load_q(nxt);
+        page_ids_store(a, s_pid[wave][buf ^ 1], lane, pid);
+        issue(a.k, nxt, buf ^ 1, nxt.c0, nxt.c1, kr);
       }
     }
     if (++held == H || !has_next) {
 #pragma unroll
       for (int h = 0; h < H; ++h)
-        if (h < held) store_unit(hold_o[h], hold_m[h], hold_l[h], hold_u[h]);
+        if (h < held) store_unit(hold_o[h], hold_m[h], hold_l[h], hold_x[h]);
       held = 0;
     }
     if (!has_next) break;
     cur = nxt;
     u = un;
+    if constexpr (PAGED) buf ^= 1;
   }
 }
 
@@ -358,7 +512,7 @@ static int multi_blocks_per_cu(K kernel) {
 // Units (sequence, kv-head, split) that run at once: one per wave.
 template <int D>
 size_t multi_wave_slots() {
-  static const int per_cu = multi_blocks_per_cu(multi_kernel<D>);
+  static const int per_cu = multi_blocks_per_cu(multi_kernel<D, false>);
   return (size_t)cu_count() * per_cu * kWaves;
 }
 
@@ -369,7 +523,10 @@ hipError_t launch_multi_d(const MultiArgs& a, hipStream_t s) {
   const size_t slots = multi_wave_slots<D>();
   const size_t rounds = (units + slots - 1) / slots;
   const unsigned grid = (unsigned)((units + kWaves * rounds - 1) / (kWaves * rounds));
-  hipLaunchKernelGGL(multi_kernel<D>, dim3(grid), dim3(kThreads), 0, s, a);
+  if (a.block_table != nullptr)
+    hipLaunchKernelGGL((multi_kernel<D, true>), dim3(grid), dim3(kThreads), 0, s, a);
+  else
+    hipLaunchKernelGGL((multi_kernel<D, false>), dim3(grid), dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }
 

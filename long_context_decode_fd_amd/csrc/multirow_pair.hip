@@ -45,7 +45,8 @@ constexpr int kKStride = 2 * D + 16;
 template <int D>
 constexpr int kVStride = 2 * D + 32;
 
-template <int D>
+// PAGED: k and v are page pools, as in the one-tile kernel.
+template <int D, bool PAGED>
 __global__ __launch_bounds__(2 * kWave) __attribute__((amdgpu_waves_per_eu(2)))
 void multi_pair_kernel(MultiArgs a) {
   constexpr int KS = D / 32;             // QK k-steps (32 dims each)
@@ -65,6 +66,8 @@ void multi_pair_kernel(MultiArgs a) {
   static_assert(8 * OSTR <= 16 * KSTR, "eight O rows must fit one K tile");
   __shared__ __align__(16) unsigned char s_k[TT][16 * KSTR];
   __shared__ __align__(16) unsigned char s_v[TT][16 * VSTR];
+  // paged: each wave's copy of the page ids of the current and next split
+  __shared__ int s_pid[PAGED ? 2 : 1][2][PAGED ? kMultiPagePids : 1];
 
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & (kWave - 1);
   const int n = lane & 15, qd = lane >> 4;
@@ -77,24 +80,50 @@ void multi_pair_kernel(MultiArgs a) {
   const int tr_off = (4 * qd + (n >> 2)) * VSTR + 8 * (n & 3);
   const float c_log2 = a.c_log2;
 
+  // a unit: sequence b (holding L positions), kv-head, split c = [c0, c1)
+  // (empty when a paged sequence is shorter than the split's start)
   struct UnitM {
-    int b, kvh, c, c0, c1;
+    int b, kvh, c, c0, c1, L;
   };
+  auto seq_len = [&](int b) {
+    if constexpr (PAGED) {
+      const auto* sl = (const __attribute__((address_space(4))) int32_t*)a.seq_lens;
+      return min(max(sl[__builtin_amdgcn_readfirstlane(b)], 0), a.L);
+    } else {
+      return a.L;
+    }
+  };
+  PagedWalk walk{};   // paged: the units that hold positions
   auto decode = [&](int u, UnitM& x) {
-    x.c = u % a.nc;
-    const int bk = u / a.nc;
-    x.kvh = bk % a.Hkv;
-    x.b = bk / a.Hkv;
+    if constexpr (PAGED) {
+      paged_walk_decode(a, u, walk, x.b, x.kvh, x.c);
+    } else {
+      x.c = u % a.nc;
+      const int bk = u / a.nc;
+      x.kvh = bk % a.Hkv;
+      x.b = bk / a.Hkv;
+    }
+    x.L = seq_len(x.b);
     x.c0 = x.c * a.chunk;
-    x.c1 = min(x.c0 + a.chunk, a.L);
+    x.c1 = min(x.c0 + a.chunk, x.L);
   };
-  auto base_of = [&](const void* t, const UnitM& x) {
-    return reinterpret_cast<const char*>(t) + ((size_t)x.b * a.Hkv + x.kvh) * (size_t)a.L * ROWB;
+  // first byte of row t0 (a multiple of 16 in [c0, c1) when `used`; else
+  // nothing is read there and any row will do) of unit x's K or V
+  const int shift = a.page_shift, pmask = (1 << a.page_shift) - 1;
+  auto row_base = [&](const void* t, const UnitM& x, int buf, int t0, bool used) {
+    if constexpr (PAGED) {
+      const int p = used ? s_pid[wave][buf][(t0 - x.c0) >> shift] : 0;
+      const int pc = __builtin_amdgcn_readfirstlane(p);
+      return reinterpret_cast<const char*>(t) +
+             ((((size_t)pc * a.Hkv + x.kvh) << shift) + (size_t)(t0 & pmask)) * ROWB;
+    } else {
+      return reinterpret_cast<const char*>(t) +
+             (((size_t)x.b * a.Hkv + x.kvh) * (size_t)a.L + (size_t)t0) * ROWB;
+    }
   };
   // query row row0 + n: token r = row / G, head kvh*G + row % G, last
   // visible position L - M + r; rows >= R are padding (q = 0)
   const int qrow = row0 + n;
-  const int lim = a.L - a.M + qrow / G;
   u32x4 qf[KS];
   auto load_q = [&](const UnitM& x) {
     if (qrow < R) {
@@ -110,12 +139,13 @@ void multi_pair_kernel(MultiArgs a) {
   };
   // this wave's tiles 2 j + wave of the batch at T: one buffer descriptor per
   // tile, limited to the chunk end c1 (rows past it read as zeros, untouched)
-  auto issue = [&](const char* __restrict__ src, int T, int c1, u32x4 (&r)[TW][NI]) {
+  auto issue = [&](const void* t, const UnitM& x, int buf, int T, int c1,
+                   u32x4 (&r)[TW][NI]) {
 #pragma unroll
     for (int j = 0; j < TW; ++j) {
       const int t0 = T + 16 * (2 * j + wave);
       const int nrow = min(max(c1 - t0, 0), 16);
-      const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(src + (size_t)t0 * ROWB, nrow * ROWB);
+      const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(row_base(t, x, buf, t0, nrow > 0), nrow * ROWB);
 #pragma unroll
       for (int i = 0; i < NI; ++i) r[j][i] = ld16_buf(rs, lane_off + RPI * i * ROWB);
     }
@@ -129,11 +159,10 @@ void multi_pair_kernel(MultiArgs a) {
   // wave + 2 (tiles that only this wave writes)
   auto o_stage = [&](int r) { return s_k[wave + 2 * (r >> 3)] + (r & 7) * OSTR; };
 
-  // partials of unit uu: rows ((b*M + r)*Hq + h)*nc + c; called after a
+  // partials of unit x: rows ((b*M + r)*Hq + h)*nc + c; called after a
   // barrier, when no wave reads the tiles any more
-  auto store_unit = [&](const f32x4 (&o)[DB], float m, float l, int uu) {
-    UnitM x;
-    decode(uu, x);
+  // (x as decoded when the unit ran: the paged walker only moves forward)
+  auto store_unit = [&](const f32x4 (&o)[DB], float m, float l, const UnitM& x) {
     if (qd == 0 && qrow < R) {
       const size_t prow =
           (((size_t)x.b * a.M + qrow / G) * a.Hq + (size_t)x.kvh * G + qrow % G) * a.nc + x.c;
@@ -159,25 +188,37 @@ void multi_pair_kernel(MultiArgs a) {
     }
   };
 
-  // workgroup w takes the consecutive units [w*per, (w+1)*per)
-  const int per = (n_units + (int)gridDim.x - 1) / (int)gridDim.x;
+  // workgroup w takes the consecutive units [w*per, (w+1)*per) (paged: of
+  // the units that hold positions)
+  int total = n_units;
+  if constexpr (PAGED) total = paged_walk_start(a, lane, 0, walk);
+  const int per = (total + (int)gridDim.x - 1) / (int)gridDim.x;
   int u = (int)blockIdx.x * per;
-  const int u_end = min(u + per, n_units);
-  if (u >= n_units) return;   // both waves of the workgroup
+  const int u_end = min(u + per, total);
+  if (u >= total) return;   // both waves of the workgroup
+  if constexpr (PAGED) paged_walk_start(a, lane, u, walk);
   UnitM cur;
   decode(u, cur);
   u32x4 kr[TW][NI], vr[TW][NI];
+  int buf = 0;   // LDS copy of the current unit's page ids (paged)
+  int pid[kPidPerLane];
+  if constexpr (PAGED) {
+    page_ids_load(a, cur.b, cur.c0, cur.c1, lane, pid);
+    page_ids_store(a, s_pid[wave][0], lane, pid);
+  }
   load_q(cur);
-  issue(base_of(a.k, cur), cur.c0, cur.c1, kr);
-  issue(base_of(a.v, cur), cur.c0, cur.c1, vr);
+  issue(a.k, cur, buf, cur.c0, cur.c1, kr);
+  issue(a.v, cur, buf, cur.c0, cur.c1, vr);
   while (true) {
     const int un = u + 1;
     const bool has_next = un < u_end;
     UnitM nxt = cur;
     if (has_next) decode(un, nxt);
+    if constexpr (PAGED) {
+      if (has_next) page_ids_load(a, nxt.b, nxt.c0, nxt.c1, lane, pid);
+    }
     const int c0 = cur.c0, c1 = cur.c1;
-    const char* kb = base_of(a.k, cur);
-    const char* vb = base_of(a.v, cur);
+    const int lim = cur.L - a.M + qrow / G;
 
     f32x4 o[DB];
     float m = kNegInf, l = 0.f;   // row's running maximum (raw), this lane's part of l
@@ -195,17 +236,19 @@ void multi_pair_kernel(MultiArgs a) {
       // agree on every path.  After the wave's last batch the limit is 0:
       // the loads return zeros without touching memory.
       const bool last = T + STEP >= c1;
-      const char* ks = kb;
-      const char* vs = vb;
-      int t_next = T + STEP, c_end = c1;
+      UnitM xs = cur;
+      int t_next = T + STEP, c_end = c1, b_next = buf;
       if (last) {
-        ks = base_of(a.k, nxt);
-        vs = base_of(a.v, nxt);
+        if constexpr (PAGED) {
+          if (has_next) page_ids_store(a, s_pid[wave][buf ^ 1], lane, pid);
+        }
+        xs = nxt;
+        b_next = buf ^ 1;
         t_next = has_next ? nxt.c0 : T;
         c_end = has_next ? nxt.c1 : T;
       }
-      issue(ks, t_next, c_end, kr);
-      issue(vs, t_next, c_end, vr);
+      issue(a.k, xs, b_next, t_next, c_end, kr);
+      issue(a.v, xs, b_next, t_next, c_end, vr);
       __syncthreads();   // the batch is in LDS
 
       float sc[TT][4];
@@ -284,10 +327,21 @@ void multi_pair_kernel(MultiArgs a) {
     // l of row n: the four lanes of the row hold parts
     l = pair_sum<32>(pair_sum<16>(l));
     __syncthreads();   // no wave reads the tiles any more
-    store_unit(o, m, l, u);
+    store_unit(o, m, l, cur);
+    if constexpr (PAGED) {
+      // an empty split ran no batch, so nothing requested the next one's
+      // query and first rows yet
+      if (c1 <= c0 && has_next) {
+        load_q(nxt);
+        page_ids_store(a, s_pid[wave][buf ^ 1], lane, pid);
+        issue(a.k, nxt, buf ^ 1, nxt.c0, nxt.c1, kr);
+        issue(a.v, nxt, buf ^ 1, nxt.c0, nxt.c1, vr);
+      }
+    }
     if (!has_next) break;
     cur = nxt;
     u = un;
+    if constexpr (PAGED) buf ^= 1;
   }
 }
 
@@ -296,7 +350,8 @@ template <int D>
 size_t pair_slots() {
   static const int per_cu = [] {
     int nb = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, multi_pair_kernel<D>, 2 * kWave, 0) !=
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, multi_pair_kernel<D, false>, 2 * kWave,
+                                                     0) !=
             hipSuccess ||
         nb <= 0)
       nb = 1;
@@ -307,7 +362,7 @@ size_t pair_slots() {
 
 template <int D>
 hipError_t launch_pair(const MultiArgs& a, hipStream_t s) {
-  auto kernel = multi_pair_kernel<D>;
+  auto kernel = a.block_table != nullptr ? multi_pair_kernel<D, true> : multi_pair_kernel<D, false>;
   // equal rounds for every workgroup
   const size_t units = (size_t)a.B * a.Hkv * a.nc;
   const size_t slots = pair_slots<D>();

@@ -64,6 +64,12 @@ EXPECTED_PROTOTYPES = {
         "fd_dtype_t dt", "const void* q", "const void* k", "const void* v", "float* out",
         "float* lse", "int B", "int M", "int Hq", "int Hkv", "int L", "int d", "float scale",
         "int chunk", "void* ws", "size_t* ws_bytes", "void* stream"]),
+    "fd_decode_attn_multi_paged": ("int", [
+        "fd_dtype_t dt", "const void* q", "const void* k_pool", "const void* v_pool",
+        "const int32_t* block_table", "const int32_t* seq_lens", "float* out", "float* lse",
+        "int B", "int M", "int Hq", "int Hkv", "int d", "int page_size", "int max_pages_per_seq",
+        "int num_pages", "int max_seq_len", "float scale", "int chunk", "void* ws",
+        "size_t* ws_bytes", "void* stream"]),
     "fd_kv_append": ("int", [
         "fd_dtype_t dt", "const void* k_new", "const void* v_new", "void* k_cache",
         "void* v_cache", "int B", "int Hkv", "int M", "int L_cap", "int d", "int t",
@@ -272,3 +278,26 @@ def test_ffd_pack_rejects_misaligned_zs():
     for args in [(p, p, C.c_void_p(258), p, p, p, p, p, 1, 8, 2, 64, 128, 0.1, 5.0, 4, 64, 32,
                   None, None, p, C.byref(C.c_size_t(1 << 30)), None)]:
         assert lib.fd_ffd_sparse_decode(*args) == _abi.FD_ERR_ARG
+
+
+def test_multi_paged_validation_and_workspace():
+    base = dict(B=3, M=4, Hq=8, Hkv=2, d=128, page=16, max_pages=8, max_seq_len=100, chunk=32)
+    # partials of B*M*Hq rows over ceil(100 / 32) = 4 chunks
+    assert fd.workspace_bytes("fd_decode_attn_multi_paged", **base) == \
+        3 * 4 * 8 * 4 * 128 * 4 + 3 * 4 * 8 * 4 * 2 * 4
+    assert fd.workspace_bytes("fd_decode_attn_multi_paged", **dict(base, max_seq_len=0)) == 256
+    for bad, code in [(dict(page=8, max_pages=16), _abi.FD_ERR_UNSUPPORTED),  # matrix path: pages >= 16
+                      (dict(page=12), _abi.FD_ERR_ARG),
+                      (dict(page=32, chunk=48), _abi.FD_ERR_ARG),       # not a multiple of the page
+                      (dict(page=16, chunk=16 * 512, max_pages=600), _abi.FD_ERR_UNSUPPORTED),
+                      (dict(max_seq_len=129), _abi.FD_ERR_ARG),         # beyond max_pages * page
+                      (dict(M=9), _abi.FD_ERR_UNSUPPORTED),             # G*M = 36 rows
+                      (dict(dt=_abi.FD_F32), _abi.FD_ERR_UNSUPPORTED),
+                      (dict(M=0), _abi.FD_ERR_ARG)]:
+        kw = dict(base); kw.update(bad)
+        with pytest.raises(fd.FdError) as e:
+            fd.workspace_bytes("fd_decode_attn_multi_paged", **kw)
+        assert e.value.code == code, bad
+    # one token of a vector-kernel group: the paged single-query path (pages of 8, fp32)
+    assert fd.workspace_bytes("fd_decode_attn_multi_paged",
+                              **dict(base, M=1, page=8, max_pages=16, dt=_abi.FD_F32)) > 0

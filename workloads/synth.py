@@ -104,7 +104,7 @@ class DenseCase:
 
 @dataclass
 class PagedCase:
-    q: torch.Tensor           # [B, Hq, d]
+    q: torch.Tensor           # [B, Hq, d], or [B, M, Hq, d] for several tokens
     k_pool: torch.Tensor      # [P, Hkv, page, d]
     v_pool: torch.Tensor      # [P, Hkv, page, d]
     block_table: torch.Tensor  # int32 [B, max_pages]; unused entries -1
@@ -169,8 +169,11 @@ def multi_case(B, M, Hq, Hkv, L, d, chunk=512, seed=0, device="cpu",
 
 
 def paged_case(B, Hq, Hkv, d, len_lo, len_hi, page=16, chunk=512, seed=0,
-               device="cpu", lens=None, max_pages=None) -> PagedCase:
+               device="cpu", lens=None, max_pages=None, M=None) -> PagedCase:
     """Ragged sequences in a shared page pool.
+
+    M: several new query tokens per sequence, q [B, M, Hq, d] (their keys
+    and values are each sequence's last M positions); None: q [B, Hq, d].
 
     Lengths are uniform integers in [len_lo, len_hi] (unless ``lens`` is
     given).  The pool holds exactly the pages the sequences need; a random
@@ -197,7 +200,7 @@ def paged_case(B, Hq, Hkv, d, len_lo, len_hi, page=16, chunk=512, seed=0,
         off += int(n_pages[b])
 
     g = _gen(seed, device)
-    q = _randn((B, Hq, d), g, device).to(torch.bfloat16)
+    q = _randn((B, Hq, d) if M is None else (B, M, Hq, d), g, device).to(torch.bfloat16)
     k_pool = torch.zeros((max(total, 1), Hkv, page, d), dtype=torch.bfloat16,
                          device=device)
     v_pool = torch.zeros_like(k_pool)
