@@ -72,26 +72,28 @@ __device__ __forceinline__ void split_bf16(const float (&p)[4], u32x2& hi, u32x2
 
 // Paged caches: the block-table entries of a split [c0, c1) of sequence b,
 // kMultiPagePids / 64 per lane, read into registers first and written to
-// the wave's LDS copy later (clamped to [0, num_pages)), so that the wait for
-// them does not hold up the K and V loads issued before them.
+// the wave's LDS copy later, as read: any arithmetic on them here would let
+// the compiler move it (and a wait for every load in flight) up to the
+// loads; they are clamped to [0, num_pages) where a tile reads them.
 constexpr int kPidPerLane = kMultiPagePids / kWave;
 
+// Every lane loads (entries past the split repeat its last page), so that no
+// register is written but by a load: a default value written into a
+// register whose previous load may still be in flight would make the
+// compiler wait for every load issued before it.  A split holds positions
+// (c0 < c1 <= the sequence's length), so its entries lie inside the table row.
 __device__ __forceinline__ void page_ids_load(const MultiArgs& a, int b, int c0, int c1,
                                               int lane, int (&v)[kPidPerLane]) {
   const int shift = a.page_shift;
-  const int npg = c1 > c0 ? (c1 - c0 + (1 << shift) - 1) >> shift : 0;
+  const int last = max((c1 - c0 + (1 << shift) - 1) >> shift, 1) - 1;
   const int32_t* bt = a.block_table + (size_t)b * a.max_pages + (c0 >> shift);
 #pragma unroll
-  for (int j = 0; j < kPidPerLane; ++j) {
-    const int i = lane + j * kWave;
-    v[j] = i < npg ? bt[i] : 0;
-  }
+  for (int j = 0; j < kPidPerLane; ++j) v[j] = bt[min(lane + j * kWave, last)];
 }
 
-__device__ __forceinline__ void page_ids_store(const MultiArgs& a, int* dst, int lane,
-                                               const int (&v)[kPidPerLane]) {
+__device__ __forceinline__ void page_ids_store(int* dst, int lane, const int (&v)[kPidPerLane]) {
 #pragma unroll
-  for (int j = 0; j < kPidPerLane; ++j) dst[lane + j * kWave] = min(max(v[j], 0), a.num_pages - 1);
+  for (int j = 0; j < kPidPerLane; ++j) dst[lane + j * kWave] = v[j];
 }
 
 // Paged caches: the units that hold positions, (b, kvh, c) with
@@ -236,7 +238,7 @@ void multi_kernel(MultiArgs a) {
   auto row_base = [&](const void* t, const UnitM& x, int buf, int t0, bool used) {
     if constexpr (PAGED) {
       const int p = used ? s_pid[wave][buf][(t0 - x.c0) >> shift] : 0;
-      const int pc = __builtin_amdgcn_readfirstlane(p);
+      const int pc = min(max(__builtin_amdgcn_readfirstlane(p), 0), a.num_pages - 1);
       return reinterpret_cast<const char*>(t) +
              ((((size_t)pc * a.Hkv + x.kvh) << shift) + (size_t)(t0 & pmask)) * ROWB;
     } else {
@@ -353,7 +355,7 @@ void multi_kernel(MultiArgs a) {
   int pid[kPidPerLane];
   if constexpr (PAGED) {
     page_ids_load(a, cur.b, cur.c0, cur.c1, lane, pid);
-    page_ids_store(a, s_pid[wave][0], lane, pid);
+    page_ids_store(s_pid[wave][0], lane, pid);
   }
   load_q(cur);
   issue(a.k, cur, buf, cur.c0, cur.c1, kr);
@@ -403,7 +405,7 @@ void multi_kernel(MultiArgs a) {
         int t_next = T + STEP, c_end = c1, b_next = buf;
         if (T + STEP >= c1 && has_next) {
           load_q(nxt);
-          if constexpr (PAGED) page_ids_store(a, s_pid[wave][buf ^ 1], lane, pid);
+          if constexpr (PAGED) page_ids_store(s_pid[wave][buf ^ 1], lane, pid);
           xs = nxt;
           t_next = nxt.c0;
           c_end = nxt.c1;
@@ -482,7 +484,7 @@ void multi_kernel(MultiArgs a) {
       // query and first K rows yet
       if (c1 <= c0 && has_next) {
         load_q(nxt);
-        page_ids_store(a, s_pid[wave][buf ^ 1], lane, pid);
+        page_ids_store(s_pid[wave][buf ^ 1], lane, pid);
         issue(a.k, nxt, buf ^ 1, nxt.c0, nxt.c1, kr);
       }
     }

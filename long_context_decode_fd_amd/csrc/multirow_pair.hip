@@ -113,7 +113,7 @@ void multi_pair_kernel(MultiArgs a) {
   auto row_base = [&](const void* t, const UnitM& x, int buf, int t0, bool used) {
     if constexpr (PAGED) {
       const int p = used ? s_pid[wave][buf][(t0 - x.c0) >> shift] : 0;
-      const int pc = __builtin_amdgcn_readfirstlane(p);
+      const int pc = min(max(__builtin_amdgcn_readfirstlane(p), 0), a.num_pages - 1);
       return reinterpret_cast<const char*>(t) +
              ((((size_t)pc * a.Hkv + x.kvh) << shift) + (size_t)(t0 & pmask)) * ROWB;
     } else {
@@ -204,7 +204,7 @@ void multi_pair_kernel(MultiArgs a) {
   int pid[kPidPerLane];
   if constexpr (PAGED) {
     page_ids_load(a, cur.b, cur.c0, cur.c1, lane, pid);
-    page_ids_store(a, s_pid[wave][0], lane, pid);
+    page_ids_store(s_pid[wave][0], lane, pid);
   }
   load_q(cur);
   issue(a.k, cur, buf, cur.c0, cur.c1, kr);
@@ -240,7 +240,7 @@ void multi_pair_kernel(MultiArgs a) {
       int t_next = T + STEP, c_end = c1, b_next = buf;
       if (last) {
         if constexpr (PAGED) {
-          if (has_next) page_ids_store(a, s_pid[wave][buf ^ 1], lane, pid);
+          if (has_next) page_ids_store(s_pid[wave][buf ^ 1], lane, pid);
         }
         xs = nxt;
         b_next = buf ^ 1;
@@ -333,7 +333,7 @@ void multi_pair_kernel(MultiArgs a) {
       // query and first rows yet
       if (c1 <= c0 && has_next) {
         load_q(nxt);
-        page_ids_store(a, s_pid[wave][buf ^ 1], lane, pid);
+        page_ids_store(s_pid[wave][buf ^ 1], lane, pid);
         issue(a.k, nxt, buf ^ 1, nxt.c0, nxt.c1, kr);
         issue(a.v, nxt, buf ^ 1, nxt.c0, nxt.c1, vr);
       }
