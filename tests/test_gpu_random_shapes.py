@@ -127,6 +127,36 @@ def test_any_group_random(i):
 
 
 @pytest.mark.parametrize("i", range(N))
+def test_multi_paged_random(i):
+    """Several tokens (or a group outside {1, 2, 4, 8}) over a paged cache:
+    group 1-32, tokens as fit 32 query rows, pages 16-128, chunks of 1-8
+    pages, ragged lengths with empty and shorter-than-M sequences."""
+    rs = np.random.default_rng(8700 + i)
+    G = int(rs.integers(1, 33))
+    M = int(rs.integers(1, 32 // G + 1))
+    Hkv, B = int(rs.integers(1, 4)), int(rs.integers(1, 6))
+    d = int(rs.choice([64, 128]))
+    page = int(rs.choice([16, 32, 64, 128]))
+    chunk = page * int(rs.integers(1, 9))
+    lens = rs.integers(0, 2001, size=B)
+    lens[rs.random(B) < 0.2] = 0
+    lens[rs.random(B) < 0.2] = int(rs.integers(0, M + 1))
+    banner(f"random multi paged B={B} M={M} G={G} Hkv={Hkv} d={d} page={page} chunk={chunk} "
+           f"lens={lens.tolist()}")
+    c = W.paged_case(B, G * Hkv, Hkv, d, 0, 2000, page=page, chunk=chunk, seed=8700 + i,
+                     device=DEV, lens=lens, M=M)
+    mx = int(lens.max())
+    out, lse = fd.decode_attn_multi_paged(c.q, c.k_pool, c.v_pool, c.block_table, c.seq_lens,
+                                          mx, chunk=chunk)
+    torch.cuda.synchronize()
+    ref, lref = opg.paged_multi_row_attention(
+        f64(c.q), c.k_pool.float().cpu().numpy(), c.v_pool.float().cpu().numpy(),
+        c.block_table.cpu().numpy(), lens, page, c.scale)
+    tol = TOL[torch.bfloat16]
+    assert max_err(f64(out), ref) <= tol and max_err(f64(lse), lref) <= tol
+
+
+@pytest.mark.parametrize("i", range(N))
 def test_ffd_random(i):
     rs = np.random.default_rng(9000 + i)
     B, Hq, Hkv, G, d = _heads(rs)
