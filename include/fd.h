@@ -86,7 +86,12 @@ int fd_abi_version(void);
  *   L       cached positions per sequence (>= 1)
  *   chunk   positions per split-KV chunk; chunk c covers
  *           [c*chunk, min((c+1)*chunk, L)), n_chunks = ceil(L / chunk).
- * The result does not depend on `chunk` beyond fp32 rounding.
+ * The result does not depend on `chunk` beyond fp32 rounding.  A call with
+ * fewer than 1,024 (sequence, kv-head, chunk) units (MI355X's SIMD count)
+ * splits its chunks further, halving down to 32 positions while the halves
+ * stay multiples of 16, so that every SIMD reads a share of the cache; the
+ * workspace query accounts for it (the same rule holds for the paged entry
+ * points, whose splits stay multiples of the page, with max_seq_len as L).
  * G in {1, 2, 4, 8}: the vector kernel, bf16 or fp32.  Other G <= 32 (bf16
  * only, else FD_ERR_UNSUPPORTED): the matrix-core kernel of
  * fd_decode_attn_multi with one token, whose splits may then cover several
@@ -106,8 +111,9 @@ int fd_decode_attn(fd_dtype_t dt, const void* q, const void* k, const void* v,
  * runs on, held until the process ends.  The call uses the current device's
  * buffer (`stream` must belong to the current device).
  *   - FD_ERR_WORKSPACE, with nothing launched, when the partials need more:
- *     round_up(B*Hq*n_chunks*d*4, 256) + round_up(B*Hq*n_chunks*8, 256)
- *     bytes (8.5 MB at B 8, Hq 32, d 128, 64 chunks).
+ *     round_up(B*Hq*n*d*4, 256) + round_up(B*Hq*n*8, 256) bytes, n the
+ *     call's splits per sequence (fd_decode_attn's workspace size; 8.5 MB
+ *     at B 8, Hq 32, d 128, 64 chunks).
  *   - Every call on one device shares that device's buffer, and it keeps the
  *     last call's contents (nothing in it needs clearing: every partial a
  *     call reads, that call writes first).  Calls that may overlap on one

@@ -157,6 +157,24 @@ void split_ws(void* ws, int B, int Hq, int nc, int d, float** o_part, float** ml
                                       align256(rows * d * sizeof(float)));
 }
 
+// Split for a full call on the vector kernel.  A call whose (sequence,
+// kv-head, chunk) units are fewer than MI355X's 1,024 SIMDs (256 compute
+// units x 4) would leave SIMDs without a share of the cache, so the split
+// halves (down to 32 positions, staying a multiple of 16 and of `unit`, the
+// page of a paged cache) until the units reach 1,024; the merge takes blocks
+// of any length ("Flash Decoding" explainer, section 2), so only fp32
+// rounding changes.  L is the longest sequence.  A fixed device model keeps
+// the workspace size a pure function of the arguments.
+constexpr long long kSimdUnits = 1024;
+
+int full_call_split(int B, int Hkv, int L, int chunk, int unit = 16) {
+  int split = chunk;
+  while ((long long)B * Hkv * n_chunks_of(L, split) < kSimdUnits && split % 32 == 0 &&
+         split / 2 >= 32 && (split / 2) % unit == 0)
+    split /= 2;
+  return split;
+}
+
 // Enqueue the partial kernel and (when out != NULL) the merge.
 int run_split_kv(int mode, fd_dtype_t dt, const void* q, const void* k, const void* v,
                  float* out, float* lse, int B, int Hq, int Hkv, int L, int d,
@@ -271,15 +289,19 @@ int fd_decode_attn(fd_dtype_t dt, const void* q, const void* k, const void* v, f
   if (int e = check_scale(scale)) return e;
   const int nc = n_chunks_of(L, chunk);
   if (int e = check_units(B, Hq, nc)) return e;
-  if (int e = workspace_gate(ws, ws_bytes, partial_bytes(B, Hq, nc, d))) return e;
+  const bool matrix = matrix_path(Hq / Hkv, 1);
+  const int split = matrix ? chunk : full_call_split(B, Hkv, L, chunk);
+  const int ns = n_chunks_of(L, split);
+  if (int e = check_units(B, Hq, ns)) return e;
+  if (int e = workspace_gate(ws, ws_bytes, partial_bytes(B, Hq, ns, d))) return e;
   if (ws == nullptr) return ok();
   if (!q || !k || !v || !out) return fail(FD_ERR_ARG, "q, k, v and out must not be NULL");
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
     return fail(FD_ERR_ARG, "q, k, v and out must be 16-byte aligned");
-  if (matrix_path(Hq / Hkv, 1))
+  if (matrix)
     return run_multi(q, k, v, out, lse, B, 1, Hq, Hkv, L, d, scale, chunk, nc, ws, true, stream);
   fdk::PartialArgs pa{};
-  return run_split_kv(fdk::kDense, dt, q, k, v, out, lse, B, Hq, Hkv, L, d, scale, chunk, nc,
+  return run_split_kv(fdk::kDense, dt, q, k, v, out, lse, B, Hq, Hkv, L, d, scale, split, ns,
                       pa, ws, nullptr, L, stream);
 }
 
@@ -294,7 +316,11 @@ int fd_decode_attn_noalloc(fd_dtype_t dt, const void* q, const void* k, const vo
   if (int e = check_scale(scale)) return e;
   const int nc = n_chunks_of(L, chunk);
   if (int e = check_units(B, Hq, nc)) return e;
-  const size_t need = partial_bytes(B, Hq, nc, d);
+  const bool matrix = matrix_path(Hq / Hkv, 1);
+  const int split = matrix ? chunk : full_call_split(B, Hkv, L, chunk);
+  const int ns = n_chunks_of(L, split);
+  if (int e = check_units(B, Hq, ns)) return e;
+  const size_t need = partial_bytes(B, Hq, ns, d);
   if (need > (size_t)FD_NOALLOC_BYTES)
     return fail(FD_ERR_WORKSPACE,
                 "%zu bytes of chunk partials exceed the library's %zu-byte buffer "
@@ -305,10 +331,10 @@ int fd_decode_attn_noalloc(fd_dtype_t dt, const void* q, const void* k, const vo
     return fail(FD_ERR_ARG, "q, k, v and out must be 16-byte aligned");
   void* ws = nullptr;
   if (int e = scratch_ptr(&ws)) return e;
-  if (matrix_path(Hq / Hkv, 1))
+  if (matrix)
     return run_multi(q, k, v, out, lse, B, 1, Hq, Hkv, L, d, scale, chunk, nc, ws, true, stream);
   fdk::PartialArgs pa{};
-  return run_split_kv(fdk::kDense, dt, q, k, v, out, lse, B, Hq, Hkv, L, d, scale, chunk, nc,
+  return run_split_kv(fdk::kDense, dt, q, k, v, out, lse, B, Hq, Hkv, L, d, scale, split, ns,
                       pa, ws, nullptr, L, stream);
 }
 
@@ -366,7 +392,8 @@ int fd_decode_attn_paged(fd_dtype_t dt, const void* q, const void* k_pool,
     return e;
   if (chunk / page_size > 1024)
     return fail(FD_ERR_UNSUPPORTED, "chunk/page_size=%d exceeds 1024", chunk / page_size);
-  const int nc = n_chunks_of(max_seq_len, chunk);
+  const int split = full_call_split(B, Hkv, max_seq_len, chunk, page_size);
+  const int nc = n_chunks_of(max_seq_len, split);
   if (int e = check_units(B, Hq, nc)) return e;
   if (int e = workspace_gate(ws, ws_bytes, partial_bytes(B, Hq, nc, d))) return e;
   if (ws == nullptr) return ok();
@@ -382,7 +409,7 @@ int fd_decode_attn_paged(fd_dtype_t dt, const void* q, const void* k_pool,
   pa.num_pages = num_pages;
   pa.max_seq_len = max_seq_len;
   return run_split_kv(fdk::kPaged, dt, q, k_pool, v_pool, out, lse, B, Hq, Hkv, 0, d, scale,
-                      chunk, nc, pa, ws, seq_lens, max_seq_len, stream);
+                      split, nc, pa, ws, seq_lens, max_seq_len, stream);
 }
 
 int fd_decode_attn_unified_max(fd_dtype_t dt, const void* q, const void* k, const void* v,
@@ -427,16 +454,20 @@ int fd_decode_attn_multi(fd_dtype_t dt, const void* q, const void* k, const void
   if (int e = check_dense_group(dt, Hq / Hkv, M)) return e;
   const int nc = n_chunks_of(L, chunk);
   if (int e = check_units(B, M * Hq, nc)) return e;
-  if (int e = workspace_gate(ws, ws_bytes, partial_bytes(B, M * Hq, nc, d))) return e;
+  const bool matrix = matrix_path(Hq / Hkv, M);
+  const int split = matrix ? chunk : full_call_split(B, Hkv, L, chunk);
+  const int ns = n_chunks_of(L, split);
+  if (int e = check_units(B, M * Hq, ns)) return e;
+  if (int e = workspace_gate(ws, ws_bytes, partial_bytes(B, M * Hq, ns, d))) return e;
   if (ws == nullptr) return ok();
   if (!q || !k || !v || !out) return fail(FD_ERR_ARG, "q, k, v and out must not be NULL");
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
     return fail(FD_ERR_ARG, "q, k, v and out must be 16-byte aligned");
-  if (!matrix_path(Hq / Hkv, M)) {
+  if (!matrix) {
     // one query row per head of a group the vector kernel takes
-    // (q [B, 1, Hq, d] is q [B, Hq, d])
+    // (q [B, 1, Hq, d] is q [B, Hq, d]): fd_decode_attn
     fdk::PartialArgs pa{};
-    return run_split_kv(fdk::kDense, dt, q, k, v, out, lse, B, Hq, Hkv, L, d, scale, chunk, nc,
+    return run_split_kv(fdk::kDense, dt, q, k, v, out, lse, B, Hq, Hkv, L, d, scale, split, ns,
                         pa, ws, nullptr, L, stream);
   }
   return run_multi(q, k, v, out, lse, B, M, Hq, Hkv, L, d, scale, chunk, nc, ws, true, stream);
@@ -464,7 +495,8 @@ int fd_decode_attn_multi_paged(fd_dtype_t dt, const void* q, const void* k_pool,
   if (chunk / page_size > (matrix ? fdk::kMultiPagePids : 1024))
     return fail(FD_ERR_UNSUPPORTED, "chunk/page_size=%d exceeds %d", chunk / page_size,
                 matrix ? fdk::kMultiPagePids : 1024);
-  const int nc = n_chunks_of(max_seq_len, chunk);
+  const int split = matrix ? chunk : full_call_split(B, Hkv, max_seq_len, chunk, page_size);
+  const int nc = n_chunks_of(max_seq_len, split);
   if (int e = check_units(B, M * Hq, nc)) return e;
   if (int e = workspace_gate(ws, ws_bytes, partial_bytes(B, M * Hq, nc, d))) return e;
   if (ws == nullptr) return ok();
@@ -482,7 +514,7 @@ int fd_decode_attn_multi_paged(fd_dtype_t dt, const void* q, const void* k_pool,
     pa.num_pages = num_pages;
     pa.max_seq_len = max_seq_len;
     return run_split_kv(fdk::kPaged, dt, q, k_pool, v_pool, out, lse, B, Hq, Hkv, 0, d, scale,
-                        chunk, nc, pa, ws, seq_lens, max_seq_len, stream);
+                        split, nc, pa, ws, seq_lens, max_seq_len, stream);
   }
   fdk::MultiArgs pg{};
   pg.block_table = block_table;

@@ -130,7 +130,13 @@ def test_workspace_sizes():
     assert n == 8 * 32 * 64 * 128 * 4 + 8 * 32 * 64 * 2 * 4
     n = fd.workspace_bytes("fd_decode_attn", B=1, Hq=1, Hkv=1, L=1, d=64, chunk=16)
     assert n == 512
+    # 12 units of 64 positions: the call's split halves to 32 (a multiple of
+    # the page), 5 chunks per sequence
     n = fd.workspace_bytes("fd_decode_attn_paged", B=2, Hq=8, Hkv=2, d=128, page=16,
+                           max_pages=10, max_seq_len=160, chunk=64)
+    assert n == 2 * 8 * 5 * 128 * 4 + 768      # 640 B of (m, l) rounded up to 768
+    # pages of 64: the split stays at the chunk
+    n = fd.workspace_bytes("fd_decode_attn_paged", B=2, Hq=8, Hkv=2, d=128, page=64,
                            max_pages=10, max_seq_len=160, chunk=64)
     assert n == 2 * 8 * 3 * 128 * 4 + 512      # 384 B of (m, l) rounded up to 512
 
@@ -301,3 +307,24 @@ def test_multi_paged_validation_and_workspace():
     # one token of a vector-kernel group: the paged single-query path (pages of 8, fp32)
     assert fd.workspace_bytes("fd_decode_attn_multi_paged",
                               **dict(base, M=1, page=8, max_pages=16, dt=_abi.FD_F32)) > 0
+
+
+def test_short_calls_take_shorter_splits():
+    """fd_decode_attn halves the split of a call with fewer (sequence,
+    kv-head, chunk) units than the 1,024 SIMDs, down to 32 positions, and
+    sizes its workspace for that; fd_decode_attn_partials keeps one partial
+    per chunk."""
+    def size(B, Hq, n, d):
+        return B * Hq * n * d * 4 + -(-(B * Hq * n * 8) // 256) * 256
+    # 512 units -> splits of 256: 128 per sequence and kv-head
+    assert fd.workspace_bytes("fd_decode_attn", B=1, Hq=32, Hkv=8, L=32768, d=128,
+                              chunk=512) == size(1, 32, 128, 128)
+    # the fp32 MHA workload: 32 units -> splits of 32 positions, 1,024 units
+    assert fd.workspace_bytes("fd_decode_attn", dt=_abi.FD_F32, B=1, Hq=8, Hkv=8, L=4096, d=64,
+                              chunk=1024) == size(1, 8, 128, 64)
+    # enough units already: the caller's chunk
+    assert fd.workspace_bytes("fd_decode_attn", B=2, Hq=32, Hkv=8, L=32768, d=128,
+                              chunk=512) == size(2, 32, 64, 128)
+    # a chunk that is not a multiple of 32 stays
+    assert fd.workspace_bytes("fd_decode_attn", B=1, Hq=8, Hkv=8, L=4096, d=64,
+                              chunk=48) == size(1, 8, 86, 64)

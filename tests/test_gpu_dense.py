@@ -134,12 +134,30 @@ def test_many_units_per_wave():
 
 
 def test_partials_then_merge_equals_full_call():
-    c = W.dense_case(2, 16, 4, 3000, 128, "bf16", 256, seed=41, device=DEV)
+    """With at least 1,024 units the full call keeps the caller's chunk, so
+    its two stages give it bit for bit."""
+    c = W.dense_case(8, 32, 8, 4100, 128, "bf16", 256, seed=41, device=DEV)
     out, lse = fd.decode_attn(c.q, c.k, c.v, chunk=256)
     ws, nc = fd.decode_attn_partials(c.q, c.k, c.v, chunk=256)
-    o_part, ml_part = fd.partial_views(ws, 2, 16, nc, 128)
+    o_part, ml_part = fd.partial_views(ws, 8, 32, nc, 128)
     out2, lse2 = fd.merge_partials(o_part, ml_part)
     assert torch.equal(out, out2) and torch.equal(lse, lse2)
+
+
+@pytest.mark.parametrize("dt,d", [("bf16", 128), ("f32", 64)])
+def test_short_call_splits_match_the_chunked_stages(dt, d):
+    """A call of few units (B 1, 8 kv-heads) takes shorter splits than its
+    chunk; its result equals the chunk's partials merged, to fp32 rounding,
+    and the oracle."""
+    banner(f"dense short call {dt} d={d}")
+    c = W.dense_case(1, 32 if d == 128 else 8, 8, 3000, d, dt, 512, seed=44, device=DEV)
+    out, lse = fd.decode_attn(c.q, c.k, c.v, chunk=512)
+    ws, nc = fd.decode_attn_partials(c.q, c.k, c.v, chunk=512)
+    o_part, ml_part = fd.partial_views(ws, 1, c.q.shape[1], nc, d)
+    out2, lse2 = fd.merge_partials(o_part, ml_part)
+    torch.cuda.synchronize()
+    assert max_err(f64(out), f64(out2)) <= 1e-6 and max_err(f64(lse), f64(lse2)) <= 1e-6
+    _check(c, chunk=512)
 
 
 def test_merge_independent_of_chunk_order():
