@@ -13,7 +13,8 @@ decode-attention call over the whole batch (every kernel of the call).
                with HIP events on the launch stream: KV + query bytes per
                launch / mean launch time, against 8 TB/s
   cpu_baseline = the fp64 CPU oracle on a bounded sample of the same workload
-  variants   = config 1, dense at 128K, a group of 16 query heads per kv-head,
+  variants   = config 1, one sequence at 8K and 32K, dense at 128K, a group
+               of 16 query heads per kv-head,
                the paged (one and four tokens), fixed-maximum, FFD, multi-row
                and cache-append entry points on their own workloads (same
                timing method)
@@ -39,8 +40,8 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 PEAK_GBS = 8000.0       # MI355X HBM3E peak, GB/s
-VARIANTS = ("config1", "dense_128k", "group16", "paged", "paged_multi", "unified_max", "ffd",
-            "ffd_peaked", "multi_row", "append")
+VARIANTS = ("config1", "dense_b1", "dense_128k", "group16", "paged", "paged_multi", "unified_max",
+            "ffd", "ffd_peaked", "multi_row", "append")
 METRIC = "us/decode step and achieved KV-read HBM GB/s (% of peak) at 32K-128K ctx"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_partial_dense_b8_h32x8_d128_l32768.txt")
 # everything that decides the partial kernel's code: its sources, the
@@ -355,6 +356,40 @@ def cpu_baseline(torch, case, target_s):
                         f"bf16->fp64 input conversion {t_conv:.2f} s excluded"),
                 us_per_step_equiv=round(t_oracle / done * B * 1e6, 1),
                 host_cpus=len(os.sched_getaffinity(0)))
+
+
+def variant_dense_b1(torch, fd, W, args, timer):
+    """One sequence at 8K and 32K positions (Hq 32, Hkv 8, d 128, chunk 512):
+    fewer units than SIMDs, so the call splits its chunks further; 24 and 8
+    rotated K/V copies (0.8 and 1.1 GB), so every call reads HBM."""
+    res = dict(workload="dense GQA decode bf16, B=1, Hq=32, Hkv=8, d=128, chunk=512 "
+                        "(short calls: splits shorter than the chunk)")
+    for L, copies in ((8192, 24), (32768, 8)):
+        B, Hq, Hkv, d, chunk = 1, 32, 8, 128, 512
+        c = W.dense_case(B, Hq, Hkv, L, d, "bf16", chunk, seed=1201, device="cuda:0")
+        ks = [c.k] + [c.k.clone() for _ in range(copies - 1)]
+        vs = [c.v] + [c.v.clone() for _ in range(copies - 1)]
+        lib = fd.lib()
+        out = torch.empty((B, Hq, d), dtype=torch.float32, device="cuda:0")
+        lse = torch.empty((B, Hq), dtype=torch.float32, device="cuda:0")
+        wsn = fd.workspace_bytes("fd_decode_attn", B=B, Hq=Hq, Hkv=Hkv, L=L, d=d, chunk=chunk)
+        ws = torch.empty(wsn, dtype=torch.uint8, device="cuda:0")
+        size = C.c_size_t(wsn)
+        st = C.c_void_p(torch.cuda.current_stream().cuda_stream)
+        calls = []
+        for k, v in zip(ks, vs):
+            a = (fd.FD_BF16, vp(c.q), vp(k), vp(v), vp(out), vp(lse), B, Hq, Hkv, L, d,
+                 c.scale, chunk, vp(ws), C.byref(size), st)
+            calls.append(lambda a=a: lib.fd_decode_attn(*a))
+        check_rc(lib, calls[0]())
+        t = timer.run(calls, args.steps, args.warmup)
+        nbytes = 2 * B * Hkv * L * d * 2 + B * Hq * d * 2 + B * Hq * (d + 1) * 4
+        res[f"L_{L}"] = dict(us_per_step=round(t["ms"] * 1e3, 2), p10_us=round(t["p10"] * 1e3, 2),
+                             p90_us=round(t["p90"] * 1e3, 2), bytes=nbytes,
+                             gbs=round(gbs(nbytes, t["ms"]), 1),
+                             pct_of_peak=round(100 * gbs(nbytes, t["ms"]) / PEAK_GBS, 1))
+        del ks, vs, c
+    return res
 
 
 def variant_dense_128k(torch, fd, W, args, timer):
@@ -899,7 +934,8 @@ def main():
         },
     }
     if not args.no_variants:
-        fns = dict(config1=variant_config1, dense_128k=variant_dense_128k,
+        fns = dict(config1=variant_config1, dense_b1=variant_dense_b1,
+                   dense_128k=variant_dense_128k,
                    group16=variant_group16, paged=variant_paged,
                    paged_multi=variant_paged_multi,
                    unified_max=variant_unified, ffd=variant_ffd, ffd_peaked=variant_ffd_peaked,
