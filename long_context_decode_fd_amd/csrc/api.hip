@@ -5,6 +5,7 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <algorithm>
 #include <atomic>
 #include <mutex>
 #include <string>
@@ -133,6 +134,19 @@ size_t partial_bytes(int B, int Hq, int nc, int d) {
   return n > 256 ? n : 256;
 }
 
+// Paged multi-row calls: worker slots for the parts split off a chunk's
+// start (at most one per worker, and never more workers than units).
+int multi_worker_slots(int B, int Hkv, int nc) {
+  const long long units = (long long)B * Hkv * nc;
+  return (int)std::min<long long>(std::max<long long>(units, 1), fdk::kMultiWorkerCap);
+}
+
+size_t multi_worker_bytes(int B, int Hkv, int nc, int R, int d) {
+  const size_t slots = (size_t)multi_worker_slots(B, Hkv, nc);
+  return align256(slots * R * d * sizeof(float)) + align256(slots * R * 2 * sizeof(float)) +
+         align256(slots * 4 * sizeof(int32_t));
+}
+
 int workspace_gate(void* ws, size_t* ws_bytes, size_t need) {
   if (ws_bytes == nullptr) return fail(FD_ERR_ARG, "ws_bytes is NULL");
   if (ws == nullptr) {
@@ -215,24 +229,34 @@ int run_multi(const void* q, const void* k, const void* v, float* out, float* ls
               bool fold, void* stream, const fdk::MultiArgs* paged = nullptr) {
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   fdk::MultiArgs ma{q, k, v, nullptr, nullptr, B, M, Hq, Hkv, L, chunk, nc,
-                    (float)((double)scale * 1.4426950408889634), nullptr, nullptr, 0, 0, 0};
+                    (float)((double)scale * 1.4426950408889634), nullptr, nullptr, 0, 0, 0,
+                    nullptr, nullptr, nullptr, 0};
   if (paged != nullptr) {
     ma.block_table = paged->block_table;
     ma.seq_lens = paged->seq_lens;
     ma.page_shift = paged->page_shift;
     ma.max_pages = paged->max_pages;
     ma.num_pages = paged->num_pages;
-  }
-  if (nc > 0) {
-    // paged: the caller's chunk is the split (the lengths that would decide
-    // a longer one live on the device; the kernels spread the chunks that
-    // hold positions evenly over the waves)
-    const int F = fold && paged == nullptr ? fdk::multi_fold(d, ma) : 1;
+  } else if (nc > 0) {
+    // paged calls keep the caller's chunk as the split (the lengths that
+    // would decide a longer one live on the device; the kernels split the
+    // pages that hold positions evenly over the workers)
+    const int F = fold ? fdk::multi_fold(d, ma) : 1;
     const long long split = (long long)chunk * F;
     ma.chunk = split > L ? L : (int)split;
     ma.nc = n_chunks_of(L, ma.chunk);
   }
   split_ws(ws, B, M * Hq, ma.nc, d, &ma.o_part, &ma.ml_part);
+  if (paged != nullptr) {
+    const int R = (Hq / Hkv) * M;
+    ma.x_cap = multi_worker_slots(B, Hkv, ma.nc);
+    char* x = reinterpret_cast<char*>(ws) + partial_bytes(B, M * Hq, ma.nc, d);
+    ma.x_o = reinterpret_cast<float*>(x);
+    x += align256((size_t)ma.x_cap * R * d * sizeof(float));
+    ma.x_ml = reinterpret_cast<float*>(x);
+    x += align256((size_t)ma.x_cap * R * 2 * sizeof(float));
+    ma.x_meta = reinterpret_cast<int32_t*>(x);
+  }
   if (ma.nc > 0) {
     hipError_t e = fdk::launch_multi(d, ma, s);
     if (e != hipSuccess) return hip_status(e, "multi-row kernel launch");
@@ -498,7 +522,9 @@ int fd_decode_attn_multi_paged(fd_dtype_t dt, const void* q, const void* k_pool,
   const int split = matrix ? chunk : full_call_split(B, Hkv, max_seq_len, chunk, page_size);
   const int nc = n_chunks_of(max_seq_len, split);
   if (int e = check_units(B, M * Hq, nc)) return e;
-  if (int e = workspace_gate(ws, ws_bytes, partial_bytes(B, M * Hq, nc, d))) return e;
+  const size_t need = partial_bytes(B, M * Hq, nc, d) +
+                      (matrix ? multi_worker_bytes(B, Hkv, nc, (Hq / Hkv) * M, d) : 0);
+  if (int e = workspace_gate(ws, ws_bytes, need)) return e;
   if (ws == nullptr) return ok();
   if (!q || !k_pool || !v_pool || !block_table || !seq_lens || !out)
     return fail(FD_ERR_ARG, "q, pools, block_table, seq_lens and out must not be NULL");

@@ -90,8 +90,20 @@ struct MultiArgs {
   const int32_t* block_table;
   const int32_t* seq_lens;
   int page_shift, max_pages, num_pages;
+  // Paged: worker w's range of pages may start inside a chunk; that part's
+  // partials go to row w * R + r of x_o [x_cap * R, D] and x_ml [x_cap * R,
+  // 2] (R = G * M query rows) and x_meta[4 w ..] = (b, kv-head, chunk, 1)
+  // (0 in the last entry when the range starts at a chunk start or is
+  // empty), and a fix-up folds them into the chunks' partials.
+  float* x_o;
+  float* x_ml;
+  int32_t* x_meta;
+  int x_cap;
 };
 constexpr int kMultiPagePids = 256;
+// Workers of a paged multi-row call that get a slot for a part split off
+// their first chunk (the workspace holds min(this, B * Hkv * nc) slots).
+constexpr int kMultiWorkerCap = 2048;
 hipError_t launch_multi(int D, const MultiArgs& a, hipStream_t s);
 // Chunks per split for the multi-row kernels: the number of consecutive
 // chunks of a row that one split covers, chosen so that the splits fill the

@@ -4,7 +4,7 @@
 
 namespace fdk {
 
-hipError_t launch_multi_pair(int D, const MultiArgs& a, hipStream_t s);
+hipError_t launch_multi_pair(int D, const MultiArgs& a, hipStream_t s, int* workers);
 
 size_t multi_pair_slots(int D);
 
@@ -40,11 +40,59 @@ int multi_fold(int D, const MultiArgs& a) {
   return best;
 }
 
+// Paged calls: each part that a worker's range cut off a chunk's start
+// (slot w, flagged in x_meta) is folded into that chunk's partials by the
+// exact merge of two parts ("Flash Decoding" explainer, section 2):
+// m = max(m1, m2), O = 2^(m1 - m) O1 + 2^(m2 - m) O2, l likewise (m in log2
+// units).  A chunk has at most one such part, and its first part -- the
+// previous worker's last -- sits in the chunk's own partials.  One wave per
+// slot; a row neither part saw (m1 = m2 = -inf) keeps the empty partial.
+template <int D>
+__global__ __launch_bounds__(kWave) void multi_fixup_kernel(MultiArgs a, int workers) {
+  const int w = (int)blockIdx.x;
+  if (w >= workers) return;
+  const int32_t* mt = a.x_meta + 4 * (size_t)w;
+  if (mt[3] == 0) return;
+  const int b = mt[0], kvh = mt[1], c = mt[2];
+  const int G = a.Hq / a.Hkv, R = G * a.M;
+  constexpr int CPR = D / 4;          // 16-byte pieces per row
+  constexpr int RPW = kWave / CPR;    // rows per pass of the wave
+  const int lane = (int)threadIdx.x;
+  for (int r0 = 0; r0 < R; r0 += RPW) {
+    const int r = r0 + lane / CPR, col = lane % CPR;
+    if (r >= R) continue;
+    const size_t prow =
+        (((size_t)b * a.M + r / G) * a.Hq + (size_t)kvh * G + r % G) * a.nc + c;
+    const size_t xrow = (size_t)w * R + r;
+    const f32x2 p1 = *reinterpret_cast<const f32x2*>(a.ml_part + prow * 2);
+    const f32x2 p2 = *reinterpret_cast<const f32x2*>(a.x_ml + xrow * 2);
+    const float M = fmaxf(p1.x, p2.x);
+    if (M == kNegInf) continue;
+    const float w1 = exp2_diff(p1.x, M), w2 = exp2_diff(p2.x, M);
+    f32x4* const op = reinterpret_cast<f32x4*>(a.o_part + prow * D) + col;
+    const f32x4 o1 = *op;
+    const f32x4 o2 = reinterpret_cast<const f32x4*>(a.x_o + xrow * D)[col];
+    *op = f32x4{fmaf(w1, o1.x, w2 * o2.x), fmaf(w1, o1.y, w2 * o2.y), fmaf(w1, o1.z, w2 * o2.z),
+                fmaf(w1, o1.w, w2 * o2.w)};
+    if (col == 0)
+      *reinterpret_cast<f32x2*>(a.ml_part + prow * 2) = f32x2{M, fmaf(w1, p1.y, w2 * p2.y)};
+  }
+}
+
 hipError_t launch_multi(int D, const MultiArgs& a, hipStream_t s) {
-  if ((a.Hq / a.Hkv) * a.M > 16) return launch_multi_pair(D, a, s);
-  if (D == 64) return launch_multi_d<64>(a, s);
-  if (D == 128) return launch_multi_d<128>(a, s);
-  return hipErrorInvalidValue;
+  int workers = 0;
+  hipError_t e = hipErrorInvalidValue;
+  if ((a.Hq / a.Hkv) * a.M > 16) e = launch_multi_pair(D, a, s, &workers);
+  else if (D == 64) e = launch_multi_d<64>(a, s, &workers);
+  else if (D == 128) e = launch_multi_d<128>(a, s, &workers);
+  if (e != hipSuccess || a.block_table == nullptr) return e;
+  workers = std::min(workers, a.x_cap);
+  if (workers <= 0) return hipSuccess;
+  if (D == 64)
+    hipLaunchKernelGGL((multi_fixup_kernel<64>), dim3((unsigned)workers), dim3(kWave), 0, s, a, workers);
+  else
+    hipLaunchKernelGGL((multi_fixup_kernel<128>), dim3((unsigned)workers), dim3(kWave), 0, s, a, workers);
+  return hipGetLastError();
 }
 
 }  // namespace fdk

@@ -117,39 +117,102 @@ __device__ __forceinline__ int paged_units_u(const MultiArgs& a, int b) {
   return a.Hkv * ((paged_len_u(a, b) + a.chunk - 1) / a.chunk);
 }
 
-// Units of the whole call, and the walker positioned at the sequence that
-// holds unit u (u below the total; else at the end): 64 sequences per step,
-// an inclusive scan across the lanes, the first lane whose running total
-// passes u.
-__device__ __forceinline__ int paged_walk_start(const MultiArgs& a, int lane, int u,
-                                                PagedWalk& w) {
-  int first = 0, found = 0;
-  w.b = a.B;
-  w.first = 0;
-  w.units = 0;
+// A worker's share of a paged call.  The call's pages are counted in unit
+// order (sequence after sequence, kv-head-major inside a sequence: a
+// (sequence, kv-head) holds ceil(L_b / page) of them) and split evenly:
+// worker w of n' takes pages [w P / n', (w + 1) P / n'), with n' = min(n,
+// x_cap, P / pages-per-chunk), so every range spans at least a chunk's
+// pages and a chunk is cut at most once.  Whole units would leave workers
+// idle or a whole unit apart (7,224 units of 1,024 positions over 1,016
+// waves: 903 waves with 8 units, 113 with none).  The range's units run
+// from the one holding its first page (from that page's position on: a
+// part cut off the chunk's start) to the one holding its last page (up to
+// that page's end).
+struct PagedSpot {
+  int u;                 // unit holding the page
+  int pos;               // the page's first position in its (sequence, kv-head)
+  int b, kvh, c;         // that unit
+  int first, units;      // sequence b's units are [first, first + units)
+};
+
+// a wave-uniform 64-bit value into scalar registers
+__device__ __forceinline__ long long uniform_ll(long long x) {
+  const unsigned lo = __builtin_amdgcn_readfirstlane((unsigned)x);
+  const unsigned hi = __builtin_amdgcn_readfirstlane((unsigned)((unsigned long long)x >> 32));
+  return (long long)(((unsigned long long)hi << 32) | lo);
+}
+
+__device__ __forceinline__ long long scan_incl_ll(long long x, int lane) {
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    const long long t = __shfl_up(x, o);
+    if (lane >= o) x += t;
+  }
+  return x;
+}
+
+// false: worker w has no pages.  Else s0 / s1 locate its first / last page.
+__device__ __forceinline__ bool paged_worker_range(const MultiArgs& a, int lane, int w, int n,
+                                                   PagedSpot& s0, PagedSpot& s1) {
+  const int shift = a.page_shift, page = 1 << shift;
+  const int cpp = a.chunk >> shift;   // pages per chunk (the chunk is a multiple of the page)
+  auto lens = [&](int bb, int& Lb, int& npb, int& nsb) {
+    Lb = bb < a.B ? min(max(a.seq_lens[bb], 0), a.L) : 0;
+    npb = (Lb + page - 1) >> shift;
+    nsb = (Lb + a.chunk - 1) / a.chunk;
+  };
+  long long P = 0;
   for (int base = 0; base < a.B; base += kWave) {   // wave-uniform
-    const int bb = base + lane;
-    const int mine = bb < a.B
-                         ? a.Hkv * ((min(max(a.seq_lens[bb], 0), a.L) + a.chunk - 1) / a.chunk)
-                         : 0;
-    int incl = mine;
+    int Lb, npb, nsb;
+    lens(base + lane, Lb, npb, nsb);
+    P += uniform_ll(__shfl(scan_incl_ll((long long)a.Hkv * npb, lane), kWave - 1));
+  }
+  const long long na = P > 0 ? max(min((long long)min(n, a.x_cap), P / cpp), 1LL) : 0;
+  if (w >= na) return false;
+  const long long g0 = (long long)w * P / na, g1 = (long long)(w + 1) * P / na - 1;
+  long long fp = 0;
+  int fu = 0;
+  bool f0 = false, f1 = false;
+  for (int base = 0; base < a.B && !(f0 && f1); base += kWave) {   // wave-uniform
+    int Lb, npb, nsb;
+    lens(base + lane, Lb, npb, nsb);
+    const long long ip = scan_incl_ll((long long)a.Hkv * npb, lane);
+    int iu = a.Hkv * nsb;
 #pragma unroll
     for (int o = 1; o < kWave; o <<= 1) {
-      const int t = __shfl_up(incl, o);
-      if (lane >= o) incl += t;
+      const int t = __shfl_up(iu, o);
+      if (lane >= o) iu += t;
     }
-    const int total = __builtin_amdgcn_readlane(incl, kWave - 1);
-    if (!found && u < first + total) {
-      const uint64_t past = __builtin_amdgcn_ballot_w64(first + incl > u);
-      const int l = (int)__builtin_ctzll(past);
-      w.b = base + l;
-      w.units = __builtin_amdgcn_readlane(mine, l);
-      w.first = first + __builtin_amdgcn_readlane(incl, l) - w.units;
-      found = 1;
+    const long long totp = uniform_ll(__shfl(ip, kWave - 1));
+    const int totu = __builtin_amdgcn_readfirstlane(__shfl(iu, kWave - 1));
+    auto locate = [&](long long g, PagedSpot& sp) {
+      const int l = __builtin_amdgcn_readfirstlane(
+          (int)__builtin_ctzll(__builtin_amdgcn_ballot_w64(fp + ip > g)));
+      const int npl = __shfl(npb, l), nsl = __shfl(nsb, l);
+      const int npu = __builtin_amdgcn_readfirstlane(npl), nsu = __builtin_amdgcn_readfirstlane(nsl);
+      const long long pstart = fp + uniform_ll(__shfl(ip, l)) - (long long)a.Hkv * npu;
+      const int off = (int)(g - pstart);
+      sp.b = base + l;
+      sp.units = a.Hkv * nsu;
+      sp.first = __builtin_amdgcn_readfirstlane(fu + __shfl(iu, l)) - sp.units;
+      sp.kvh = off / npu;
+      const int p = off - sp.kvh * npu;
+      sp.c = p / cpp;
+      sp.pos = p << shift;
+      sp.u = sp.first + sp.kvh * nsu + sp.c;
+    };
+    if (!f0 && g0 < fp + totp) {
+      locate(g0, s0);
+      f0 = true;
     }
-    first += total;
+    if (!f1 && g1 < fp + totp) {
+      locate(g1, s1);
+      f1 = true;
+    }
+    fp += totp;
+    fu += totu;
   }
-  return first;
+  return true;
 }
 
 // (b, kvh, c) of unit u; u must not decrease from call to call
@@ -206,9 +269,10 @@ void multi_kernel(MultiArgs a) {
   const float c_log2 = a.c_log2;
 
   // a unit: sequence b (holding L positions), kv-head, split c = [c0, c1)
-  // (empty when a paged sequence is shorter than the split's start)
+  // (empty when a paged sequence is shorter than the split's start); xw >= 0:
+  // a part cut off the split's start, whose partials go to worker slot xw
   struct UnitM {
-    int b, kvh, c, c0, c1, L;
+    int b, kvh, c, c0, c1, L, xw;
   };
   auto seq_len = [&](int b) {
     if constexpr (PAGED) {
@@ -218,7 +282,11 @@ void multi_kernel(MultiArgs a) {
       return a.L;
     }
   };
+  const int wid = __builtin_amdgcn_readfirstlane((int)blockIdx.x * kWaves + wave);
   PagedWalk walk{};   // paged: the units that hold positions
+  // paged: this worker's units [u_first, u_last], the first from position
+  // pos0, the last up to pos1
+  int u_first = -1, u_last = -1, pos0 = 0, pos1 = 0;
   auto decode = [&](int u, UnitM& x) {
     if constexpr (PAGED) {
       paged_walk_decode(a, u, walk, x.b, x.kvh, x.c);
@@ -231,6 +299,14 @@ void multi_kernel(MultiArgs a) {
     x.L = seq_len(x.b);
     x.c0 = x.c * a.chunk;
     x.c1 = min(x.c0 + a.chunk, x.L);
+    x.xw = -1;
+    if constexpr (PAGED) {
+      if (u == u_first && x.c0 < pos0) {
+        x.c0 = pos0;
+        x.xw = wid;
+      }
+      if (u == u_last) x.c1 = min(x.c1, pos1);
+    }
   };
   // first byte of row t0 (a multiple of 16 in [c0, c1) when `used`; else
   // nothing is read there and any row will do) of unit x's K or V
@@ -294,13 +370,19 @@ void multi_kernel(MultiArgs a) {
   // rows, instead of 4 bytes per lane in 64-byte pieces.
   unsigned char* ost = s_kv[wave][0];
   // (x as decoded when the unit ran: the paged walker only moves forward)
+  // partial row of query row r (< R) of unit x, in o_part / ml_part or, for
+  // a part cut off a split's start, in x_o / x_ml
+  auto part_row = [&](const UnitM& x, int r) {
+    return x.xw >= 0 ? (size_t)x.xw * R + r
+                     : (((size_t)x.b * a.M + r / G) * a.Hq + (size_t)x.kvh * G + r % G) * a.nc +
+                           x.c;
+  };
   auto store_unit = [&](const f32x4 (&o)[DB], float m, float l, const UnitM& x) {
-    if (qd == 0 && n < R) {
-      const size_t prow =
-          (((size_t)x.b * a.M + n / G) * a.Hq + (size_t)x.kvh * G + n % G) * a.nc + x.c;
-      *reinterpret_cast<f32x2*>(a.ml_part + prow * 2) =
+    float* const op = x.xw >= 0 ? a.x_o : a.o_part;
+    float* const mlp = x.xw >= 0 ? a.x_ml : a.ml_part;
+    if (qd == 0 && n < R)
+      *reinterpret_cast<f32x2*>(mlp + part_row(x, n) * 2) =
           f32x2{(m == kNegInf) ? kNegInf : m * c_log2, l};
-    }
     // lane (n, qd) holds O rows 4*qd + e, dims 16*db + n
 #pragma unroll
     for (int e = 0; e < 4; ++e)
@@ -313,11 +395,9 @@ void multi_kernel(MultiArgs a) {
     for (int i = 0; i < 16 / ORPI; ++i) {
       const int row = ORPI * i + lane / LPO, cb = 16 * (lane % LPO);
       const f32x4 v = *reinterpret_cast<const f32x4*>(ost + row * OSTR + cb);
-      if (row < R) {
-        const size_t prow =
-            (((size_t)x.b * a.M + row / G) * a.Hq + (size_t)x.kvh * G + row % G) * a.nc + x.c;
-        *reinterpret_cast<f32x4*>(reinterpret_cast<unsigned char*>(a.o_part + prow * D) + cb) = v;
-      }
+      if (row < R)
+        *reinterpret_cast<f32x4*>(reinterpret_cast<unsigned char*>(op + part_row(x, row) * D) +
+                                  cb) = v;
     }
   };
   // Finished units wait in registers (up to H of them) and are written
@@ -332,22 +412,38 @@ void multi_kernel(MultiArgs a) {
 
   // wave w takes the consecutive units [w*per, (w+1)*per): consecutive
   // chunks of one (sequence, kv-head), a single contiguous stretch of K and
-  // V (measured 186 -> 174 us at M = 4 against taking every W-th unit)
-  const int wid = (int)blockIdx.x * kWaves + wave;
-  int total = n_units;
+  // V (measured 186 -> 174 us at M = 4 against taking every W-th unit).
+  // Paged: the units of the wave's range of pages (paged_worker_range).
+  // Wave-uniform by construction; readfirstlane lets the compiler keep the
+  // unit (and the descriptors built from it) in scalar registers.
+  int u, u_end;
   if constexpr (PAGED) {
-    // the units that hold positions, split evenly (the walker is placed at
-    // the wave's first unit below)
-    const int t = paged_walk_start(a, lane, 0, walk);
-    total = t;
+    PagedSpot s0{}, s1{};
+    const bool any = paged_worker_range(a, lane, wid, stride, s0, s1);
+    // every worker with a slot says whether its range starts inside a chunk
+    if (wid < a.x_cap && lane == 0) {
+      int32_t* mt = a.x_meta + 4 * (size_t)wid;
+      mt[0] = s0.b;
+      mt[1] = s0.kvh;
+      mt[2] = s0.c;
+      mt[3] = any && s0.pos % a.chunk != 0 ? 1 : 0;
+    }
+    if (!any) return;
+    u = __builtin_amdgcn_readfirstlane(s0.u);
+    u_end = __builtin_amdgcn_readfirstlane(s1.u) + 1;
+    u_first = u;
+    u_last = u_end - 1;
+    pos0 = __builtin_amdgcn_readfirstlane(s0.pos);
+    pos1 = __builtin_amdgcn_readfirstlane(s1.pos) + (1 << a.page_shift);
+    walk.b = __builtin_amdgcn_readfirstlane(s0.b);
+    walk.first = __builtin_amdgcn_readfirstlane(s0.first);
+    walk.units = __builtin_amdgcn_readfirstlane(s0.units);
+  } else {
+    const int per = (n_units + stride - 1) / stride;
+    u = __builtin_amdgcn_readfirstlane(wid * per);
+    u_end = min(u + per, n_units);
+    if (u >= n_units) return;
   }
-  const int per = (total + stride - 1) / stride;
-  // wave-uniform by construction; readfirstlane lets the compiler keep the
-  // unit (and the descriptors built from it) in scalar registers
-  int u = __builtin_amdgcn_readfirstlane(wid * per);
-  const int u_end = min(u + per, total);
-  if (u >= total) return;
-  if constexpr (PAGED) paged_walk_start(a, lane, u, walk);
   UnitM cur;
   decode(u, cur);
   u32x4 kr[TT][NI], vr[TT][NI];
@@ -518,13 +614,19 @@ size_t multi_wave_slots() {
   return (size_t)cu_count() * per_cu * kWaves;
 }
 
+// *workers: the waves launched (each a worker of a paged call).
 template <int D>
-hipError_t launch_multi_d(const MultiArgs& a, hipStream_t s) {
+hipError_t launch_multi_d(const MultiArgs& a, hipStream_t s, int* workers) {
   // equal rounds for every wave, as for the single-query kernel
   const size_t units = (size_t)a.B * a.Hkv * a.nc;
   const size_t slots = multi_wave_slots<D>();
   const size_t rounds = (units + slots - 1) / slots;
-  const unsigned grid = (unsigned)((units + kWaves * rounds - 1) / (kWaves * rounds));
+  // paged: every resident wave (the pages are divided over the workers)
+  const unsigned grid =
+      a.block_table != nullptr
+          ? (unsigned)((std::min(units, slots) + kWaves - 1) / kWaves)
+          : (unsigned)((units + kWaves * rounds - 1) / (kWaves * rounds));
+  *workers = (int)grid * kWaves;
   if (a.block_table != nullptr)
     hipLaunchKernelGGL((multi_kernel<D, true>), dim3(grid), dim3(kThreads), 0, s, a);
   else

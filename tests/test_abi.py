@@ -288,10 +288,23 @@ def test_ffd_pack_rejects_misaligned_zs():
 
 def test_multi_paged_validation_and_workspace():
     base = dict(B=3, M=4, Hq=8, Hkv=2, d=128, page=16, max_pages=8, max_seq_len=100, chunk=32)
-    # partials of B*M*Hq rows over ceil(100 / 32) = 4 chunks
+
+    def a256(x):
+        return -(-x // 256) * 256
+
+    def slots(S, R=16, d=128):   # worker slots: S*R*d and S*R*2 floats, S*4 int32
+        return a256(S * R * d * 4) + a256(S * R * 2 * 4) + a256(S * 16)
+    # partials of B*M*Hq rows over ceil(100 / 32) = 4 chunks, then B*Hkv*4 = 24
+    # worker slots of R = G*M = 16 rows
     assert fd.workspace_bytes("fd_decode_attn_multi_paged", **base) == \
-        3 * 4 * 8 * 4 * 128 * 4 + 3 * 4 * 8 * 4 * 2 * 4
-    assert fd.workspace_bytes("fd_decode_attn_multi_paged", **dict(base, max_seq_len=0)) == 256
+        3 * 4 * 8 * 4 * 128 * 4 + 3 * 4 * 8 * 4 * 2 * 4 + slots(24)
+    assert fd.workspace_bytes("fd_decode_attn_multi_paged", **dict(base, max_seq_len=0)) == \
+        256 + slots(1)
+    # the slots stop at 2,048 workers
+    big = dict(base, B=64, Hkv=8, Hq=128, M=1, max_pages=8192, max_seq_len=131072, chunk=1024)
+    nc = 128
+    assert fd.workspace_bytes("fd_decode_attn_multi_paged", **big) == \
+        a256(64 * 128 * nc * 128 * 4) + a256(64 * 128 * nc * 8) + slots(2048)
     for bad, code in [(dict(page=8, max_pages=16), _abi.FD_ERR_UNSUPPORTED),  # matrix path: pages >= 16
                       (dict(page=12), _abi.FD_ERR_ARG),
                       (dict(page=32, chunk=48), _abi.FD_ERR_ARG),       # not a multiple of the page
