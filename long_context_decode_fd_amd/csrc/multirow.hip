@@ -85,7 +85,8 @@ hipError_t launch_multi(int D, const MultiArgs& a, hipStream_t s) {
   if ((a.Hq / a.Hkv) * a.M > 16) e = launch_multi_pair(D, a, s, &workers);
   else if (D == 64) e = launch_multi_d<64>(a, s, &workers);
   else if (D == 128) e = launch_multi_d<128>(a, s, &workers);
-  if (e != hipSuccess || a.block_table == nullptr) return e;
+  // the wave-pair kernel keeps whole units per workgroup
+  if (e != hipSuccess || a.block_table == nullptr || (a.Hq / a.Hkv) * a.M > 16) return e;
   workers = std::min(workers, a.x_cap);
   if (workers <= 0) return hipSuccess;
   if (D == 64)

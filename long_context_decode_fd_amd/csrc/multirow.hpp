@@ -117,6 +117,41 @@ __device__ __forceinline__ int paged_units_u(const MultiArgs& a, int b) {
   return a.Hkv * ((paged_len_u(a, b) + a.chunk - 1) / a.chunk);
 }
 
+// Units of the whole call, and the walker positioned at the sequence that
+// holds unit u (u below the total; else at the end): 64 sequences per step,
+// an inclusive scan across the lanes, the first lane whose running total
+// passes u.
+__device__ __forceinline__ int paged_walk_start(const MultiArgs& a, int lane, int u,
+                                                PagedWalk& w) {
+  int first = 0, found = 0;
+  w.b = a.B;
+  w.first = 0;
+  w.units = 0;
+  for (int base = 0; base < a.B; base += kWave) {   // wave-uniform
+    const int bb = base + lane;
+    const int mine = bb < a.B
+                         ? a.Hkv * ((min(max(a.seq_lens[bb], 0), a.L) + a.chunk - 1) / a.chunk)
+                         : 0;
+    int incl = mine;
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+      const int t = __shfl_up(incl, o);
+      if (lane >= o) incl += t;
+    }
+    const int total = __builtin_amdgcn_readlane(incl, kWave - 1);
+    if (!found && u < first + total) {
+      const uint64_t past = __builtin_amdgcn_ballot_w64(first + incl > u);
+      const int l = (int)__builtin_ctzll(past);
+      w.b = base + l;
+      w.units = __builtin_amdgcn_readlane(mine, l);
+      w.first = first + __builtin_amdgcn_readlane(incl, l) - w.units;
+      found = 1;
+    }
+    first += total;
+  }
+  return first;
+}
+
 // A worker's share of a paged call.  The call's pages are counted in unit
 // order (sequence after sequence, kv-head-major inside a sequence: a
 // (sequence, kv-head) holds ceil(L_b / page) of them) and split evenly:
