@@ -54,28 +54,37 @@ __global__ __launch_bounds__(kWave) void multi_fixup_kernel(MultiArgs a, int wor
   const int32_t* mt = a.x_meta + 4 * (size_t)w;
   if (mt[3] == 0) return;
   const int b = mt[0], kvh = mt[1], c = mt[2];
-  const int G = a.Hq / a.Hkv, R = G * a.M;
-  constexpr int CPR = D / 4;          // 16-byte pieces per row
-  constexpr int RPW = kWave / CPR;    // rows per pass of the wave
+  const int G = a.Hq / a.Hkv, R = G * a.M;   // at most 16 rows
+  constexpr int CPR = D / 4;                 // 16-byte pieces per row
+  constexpr int NP = 16 * CPR / kWave;       // pieces of 16 rows per lane
   const int lane = (int)threadIdx.x;
-  for (int r0 = 0; r0 < R; r0 += RPW) {
-    const int r = r0 + lane / CPR, col = lane % CPR;
-    if (r >= R) continue;
-    const size_t prow =
-        (((size_t)b * a.M + r / G) * a.Hq + (size_t)kvh * G + r % G) * a.nc + c;
+  // every load first (one memory latency); rows past R read row R - 1 and
+  // write nothing
+  f32x4 o1[NP], o2[NP];
+  f32x2 p1[NP], p2[NP];
+  size_t prow[NP];
+#pragma unroll
+  for (int j = 0; j < NP; ++j) {
+    const int f = j * kWave + lane, r = min(f / CPR, R - 1), col = f % CPR;
+    prow[j] = (((size_t)b * a.M + r / G) * a.Hq + (size_t)kvh * G + r % G) * a.nc + c;
     const size_t xrow = (size_t)w * R + r;
-    const f32x2 p1 = *reinterpret_cast<const f32x2*>(a.ml_part + prow * 2);
-    const f32x2 p2 = *reinterpret_cast<const f32x2*>(a.x_ml + xrow * 2);
-    const float M = fmaxf(p1.x, p2.x);
-    if (M == kNegInf) continue;
-    const float w1 = exp2_diff(p1.x, M), w2 = exp2_diff(p2.x, M);
-    f32x4* const op = reinterpret_cast<f32x4*>(a.o_part + prow * D) + col;
-    const f32x4 o1 = *op;
-    const f32x4 o2 = reinterpret_cast<const f32x4*>(a.x_o + xrow * D)[col];
-    *op = f32x4{fmaf(w1, o1.x, w2 * o2.x), fmaf(w1, o1.y, w2 * o2.y), fmaf(w1, o1.z, w2 * o2.z),
-                fmaf(w1, o1.w, w2 * o2.w)};
+    o1[j] = reinterpret_cast<const f32x4*>(a.o_part + prow[j] * D)[col];
+    o2[j] = reinterpret_cast<const f32x4*>(a.x_o + xrow * D)[col];
+    p1[j] = *reinterpret_cast<const f32x2*>(a.ml_part + prow[j] * 2);
+    p2[j] = *reinterpret_cast<const f32x2*>(a.x_ml + xrow * 2);
+  }
+#pragma unroll
+  for (int j = 0; j < NP; ++j) {
+    const int f = j * kWave + lane, col = f % CPR;
+    const float M = fmaxf(p1[j].x, p2[j].x);
+    if (f / CPR >= R || M == kNegInf) continue;   // padding, or a row neither part saw
+    const float w1 = exp2_diff(p1[j].x, M), w2 = exp2_diff(p2[j].x, M);
+    reinterpret_cast<f32x4*>(a.o_part + prow[j] * D)[col] =
+        f32x4{fmaf(w1, o1[j].x, w2 * o2[j].x), fmaf(w1, o1[j].y, w2 * o2[j].y),
+              fmaf(w1, o1[j].z, w2 * o2[j].z), fmaf(w1, o1[j].w, w2 * o2[j].w)};
     if (col == 0)
-      *reinterpret_cast<f32x2*>(a.ml_part + prow * 2) = f32x2{M, fmaf(w1, p1.y, w2 * p2.y)};
+      *reinterpret_cast<f32x2*>(a.ml_part + prow[j] * 2) =
+          f32x2{M, fmaf(w1, p1[j].y, w2 * p2[j].y)};
   }
 }
 
