@@ -126,3 +126,17 @@ def test_paged_multi_row_long_ragged_sampled(M):
     picks = [int(np.argmin(lens)), int(np.argmax(lens))]
     rows = [(b, r, h) for b in picks for r in range(M) for h in range(32)]
     _check(c, int(lens.max()), 512, rows=rows)
+
+
+@pytest.mark.parametrize("M", [4, 8])
+def test_paged_multi_row_one_million_positions(M):
+    """A sequence of 2^20 + 77 positions (65,541 pages of 16) beside a short
+    one, M new tokens, chunk 1024: 1,025 chunks per row, so the merge walks
+    its tiles of 256 chunks; the one-tile kernel (M = 4) divides the 131,120
+    pages of both kv-heads over its workers, the wave pair (M = 8) takes
+    whole chunks.  Every token and head against the oracle."""
+    banner(f"paged multi 1M M={M}")
+    lens = [(1 << 20) + 77, 300]
+    c = W.paged_case(2, 8, 2, 128, 0, lens[0], page=16, chunk=1024, seed=104 + M, device=DEV,
+                     lens=lens, M=M)
+    _check(c, lens[0], 1024)
