@@ -144,7 +144,7 @@ int multi_worker_slots(int B, int Hkv, int nc) {
 size_t multi_worker_bytes(int B, int Hkv, int nc, int R, int d) {
   const size_t slots = (size_t)multi_worker_slots(B, Hkv, nc);
   return align256(slots * R * d * sizeof(float)) + align256(slots * R * 2 * sizeof(float)) +
-         align256(slots * 4 * sizeof(int32_t));
+         align256(slots * 4 * sizeof(int32_t)) + 256;
 }
 
 int workspace_gate(void* ws, size_t* ws_bytes, size_t need) {
@@ -214,7 +214,7 @@ int run_split_kv(int mode, fd_dtype_t dt, const void* q, const void* k, const vo
     if (e != hipSuccess) return hip_status(e, "partial kernel launch");
   }
   if (out == nullptr) return ok();
-  fdk::MergeArgs ma{o_part, ml_part, out, lse, seq_lens, Hq, nc, chunk, max_seq_len};
+  fdk::MergeArgs ma{o_part, ml_part, out, lse, seq_lens, Hq, nc, chunk, max_seq_len, nullptr};
   return hip_status(fdk::launch_merge(d, B, ma, s), "merge kernel launch");
 }
 
@@ -230,7 +230,7 @@ int run_multi(const void* q, const void* k, const void* v, float* out, float* ls
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   fdk::MultiArgs ma{q, k, v, nullptr, nullptr, B, M, Hq, Hkv, L, chunk, nc,
                     (float)((double)scale * 1.4426950408889634), nullptr, nullptr, 0, 0, 0,
-                    nullptr, nullptr, nullptr, 0};
+                    nullptr, nullptr, nullptr, 0, nullptr};
   if (paged != nullptr) {
     ma.block_table = paged->block_table;
     ma.seq_lens = paged->seq_lens;
@@ -256,13 +256,16 @@ int run_multi(const void* q, const void* k, const void* v, float* out, float* ls
     ma.x_ml = reinterpret_cast<float*>(x);
     x += align256((size_t)ma.x_cap * R * 2 * sizeof(float));
     ma.x_meta = reinterpret_cast<int32_t*>(x);
+    x += align256((size_t)ma.x_cap * 4 * sizeof(int32_t));
+    ma.x_split = reinterpret_cast<int32_t*>(x);
   }
   if (ma.nc > 0) {
     hipError_t e = fdk::launch_multi(d, ma, s);
     if (e != hipSuccess) return hip_status(e, "multi-row kernel launch");
   }
   if (out == nullptr) return ok();
-  fdk::MergeArgs mg{ma.o_part, ma.ml_part, out, lse, ma.seq_lens, M * Hq, ma.nc, ma.chunk, L};
+  fdk::MergeArgs mg{ma.o_part, ma.ml_part, out, lse, ma.seq_lens, M * Hq, ma.nc, ma.chunk, L,
+                    ma.x_split};
   return hip_status(fdk::launch_merge(d, B, mg, s), "merge kernel launch");
 }
 
@@ -395,7 +398,7 @@ int fd_merge_partials(const float* o_part, const float* ml_part, float* out, flo
   if (!o_part || !ml_part || !out) return fail(FD_ERR_ARG, "o_part, ml_part, out NULL");
   if (!aligned16(o_part) || !aligned16(ml_part) || !aligned16(out))
     return fail(FD_ERR_ARG, "o_part, ml_part and out must be 16-byte aligned");
-  fdk::MergeArgs ma{o_part, ml_part, out, lse, nullptr, Hq, n_chunks, 1, 0};
+  fdk::MergeArgs ma{o_part, ml_part, out, lse, nullptr, Hq, n_chunks, 1, 0, nullptr};
   return hip_status(fdk::launch_merge(d, B, ma, reinterpret_cast<hipStream_t>(stream)),
                     "merge kernel launch");
 }
@@ -687,7 +690,7 @@ int fd_ffd_sparse_decode(const void* q, const uint32_t* codes, const uint16_t* z
   fa.delta_raw = isinf(delta) ? delta : (float)((double)delta / (double)scale);
   hipError_t e = fdk::launch_ffd(d, Hq / Hkv, fa, s);
   if (e != hipSuccess) return hip_status(e, "ffd kernel launch");
-  fdk::MergeArgs ma{o_part, ml_part, out, lse, nullptr, Hq, nc, chunk, L};
+  fdk::MergeArgs ma{o_part, ml_part, out, lse, nullptr, Hq, nc, chunk, L, nullptr};
   return hip_status(fdk::launch_merge(d, B, ma, s), "merge kernel launch");
 }
 

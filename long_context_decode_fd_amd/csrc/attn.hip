@@ -555,7 +555,9 @@ __global__ __launch_bounds__(W * kWave) void merge_kernel(MergeArgs a) {
   if (a.seq_lens != nullptr) {
     const int b = (int)(row / a.Hq);
     const int L = min(max(a.seq_lens[b], 0), a.max_seq_len);
-    n = min((L + a.chunk - 1) / a.chunk, a.nc);
+    const int split = a.chunk_scale != nullptr ? a.chunk * min(max(*a.chunk_scale, 1), 256)
+                                               : a.chunk;
+    n = min((int)(((long long)L + split - 1) / split), a.nc);
   }
   if (n == 0) {
     if (tid < D / CS) a.out[row * D + cs * (D / CS) + tid] = 0.f;
@@ -670,7 +672,9 @@ __global__ __launch_bounds__(kWave) void merge_wave_kernel(MergeArgs a) {
   if (a.seq_lens != nullptr) {
     const int b = (int)(row / a.Hq);
     const int L = min(max(a.seq_lens[b], 0), a.max_seq_len);
-    n = min((L + a.chunk - 1) / a.chunk, a.nc);
+    const int split = a.chunk_scale != nullptr ? a.chunk * min(max(*a.chunk_scale, 1), 256)
+                                               : a.chunk;
+    n = min((int)(((long long)L + split - 1) / split), a.nc);
   }
   if (n == 0) {   // wave-uniform
     for (int c = lane; c < D / CS; c += kWave) a.out[row * D + cs * (D / CS) + c] = 0.f;

@@ -36,6 +36,9 @@ struct MergeArgs {
   float* lse;                // [B, Hq] or null
   const int32_t* seq_lens;   // paged: chunk count per sequence; else null
   int Hq, nc, chunk, max_seq_len;
+  // paged multi-row: the split is chunk * (*chunk_scale), the factor the
+  // kernel chose on the device (values below 1 read as 1); else null
+  const int32_t* chunk_scale;
 };
 
 hipError_t launch_partial(int mode, int is_bf16, int D, int G,
@@ -99,6 +102,10 @@ struct MultiArgs {
   float* x_ml;
   int32_t* x_meta;
   int x_cap;
+  // Paged, one query tile: the kernel lengthens the split to chunk * F (F a
+  // power of two, at most kMultiPagePids pages) as far as the workers keep
+  // their number, and writes F here for the merge.
+  int32_t* x_split;
 };
 constexpr int kMultiPagePids = 256;
 // Workers of a paged multi-row call that get a slot for a part split off

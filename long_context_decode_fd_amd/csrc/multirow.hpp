@@ -156,12 +156,12 @@ __device__ __forceinline__ int paged_walk_start(const MultiArgs& a, int lane, in
 // order (sequence after sequence, kv-head-major inside a sequence: a
 // (sequence, kv-head) holds ceil(L_b / page) of them) and split evenly:
 // worker w of n' takes pages [w P / n', (w + 1) P / n'), with n' = min(n,
-// x_cap, P / pages-per-chunk), so every range spans at least a chunk's
-// pages and a chunk is cut at most once.  Whole units would leave workers
+// x_cap, P / pages-per-split), so every range spans at least a split's
+// pages and a split is cut at most once.  Whole units would leave workers
 // idle or a whole unit apart (7,224 units of 1,024 positions over 1,016
 // waves: 903 waves with 8 units, 113 with none).  The range's units run
 // from the one holding its first page (from that page's position on: a
-// part cut off the chunk's start) to the one holding its last page (up to
+// part cut off the split's start) to the one holding its last page (up to
 // that page's end).
 struct PagedSpot {
   int u;                 // unit holding the page
@@ -186,23 +186,51 @@ __device__ __forceinline__ long long scan_incl_ll(long long x, int lane) {
   return x;
 }
 
+// Pages of the call (wave-uniform).
+__device__ __forceinline__ long long paged_pages(const MultiArgs& a, int lane) {
+  const int shift = a.page_shift;
+  long long P = 0;
+  for (int base = 0; base < a.B; base += kWave) {   // wave-uniform
+    const int bb = base + lane;
+    const int Lb = bb < a.B ? min(max(a.seq_lens[bb], 0), a.L) : 0;
+    const long long npb = (Lb + (1 << shift) - 1) >> shift;
+    P += uniform_ll(__shfl(scan_incl_ll((long long)a.Hkv * npb, lane), kWave - 1));
+  }
+  return P;
+}
+
+// Workers that take part: n, at most x_cap, and few enough that each range
+// spans a split's pages (at least one while there are pages).
+__device__ __forceinline__ long long paged_workers(const MultiArgs& a, long long P, int n) {
+  const int cpp = a.chunk >> a.page_shift;   // pages per split (a multiple of the page)
+  return P > 0 ? max(min((long long)min(n, a.x_cap), P / cpp), 1LL) : 0;
+}
+
+// Split factor F: the split grows to chunk * F (F a power of two, at most
+// kMultiPagePids pages) while the same number of workers still get a
+// split's pages each.  Longer splits cut the partials written and merged
+// and the unit changes; the workers' count keeps the device busy (the
+// lengths decide it, so it is chosen here, not by the host).
+__device__ __forceinline__ int paged_split_factor(const MultiArgs& a, long long P, int n) {
+  const int cpp = a.chunk >> a.page_shift;
+  const long long na = paged_workers(a, P, n);
+  int F = 1;
+  while (cpp * 2 * F <= kMultiPagePids && P / ((long long)cpp * 2 * F) >= na) F *= 2;
+  return F;
+}
+
 // false: worker w has no pages.  Else s0 / s1 locate its first / last page.
+// P: paged_pages(a).
 __device__ __forceinline__ bool paged_worker_range(const MultiArgs& a, int lane, int w, int n,
-                                                   PagedSpot& s0, PagedSpot& s1) {
+                                                   long long P, PagedSpot& s0, PagedSpot& s1) {
   const int shift = a.page_shift, page = 1 << shift;
-  const int cpp = a.chunk >> shift;   // pages per chunk (the chunk is a multiple of the page)
+  const int cpp = a.chunk >> shift;   // pages per split (the split is a multiple of the page)
   auto lens = [&](int bb, int& Lb, int& npb, int& nsb) {
     Lb = bb < a.B ? min(max(a.seq_lens[bb], 0), a.L) : 0;
     npb = (Lb + page - 1) >> shift;
     nsb = (Lb + a.chunk - 1) / a.chunk;
   };
-  long long P = 0;
-  for (int base = 0; base < a.B; base += kWave) {   // wave-uniform
-    int Lb, npb, nsb;
-    lens(base + lane, Lb, npb, nsb);
-    P += uniform_ll(__shfl(scan_incl_ll((long long)a.Hkv * npb, lane), kWave - 1));
-  }
-  const long long na = P > 0 ? max(min((long long)min(n, a.x_cap), P / cpp), 1LL) : 0;
+  const long long na = paged_workers(a, P, n);
   if (w >= na) return false;
   const long long g0 = (long long)w * P / na, g1 = (long long)(w + 1) * P / na - 1;
   long long fp = 0;
@@ -270,7 +298,9 @@ __device__ __forceinline__ void paged_walk_decode(const MultiArgs& a, int u, Pag
 // more, tiles aligned to 16).
 template <int D, bool PAGED>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1)))
-void multi_kernel(MultiArgs a) {
+void multi_kernel(MultiArgs a0) {
+  // paged: the split may grow on the device (paged_split_factor)
+  MultiArgs a = a0;
   constexpr int KS = D / 32;             // QK k-steps (32 dims each)
   constexpr int DB = D / 16;             // 16-dim blocks of the P V product
   constexpr int TT = kMrTiles;
@@ -453,8 +483,12 @@ void multi_kernel(MultiArgs a) {
   // unit (and the descriptors built from it) in scalar registers.
   int u, u_end;
   if constexpr (PAGED) {
+    const long long P = paged_pages(a, lane);
+    const int F = paged_split_factor(a, P, stride);
+    a.chunk *= F;
+    if (wid == 0 && lane == 0) *a.x_split = F;   // for the merge
     PagedSpot s0{}, s1{};
-    const bool any = paged_worker_range(a, lane, wid, stride, s0, s1);
+    const bool any = paged_worker_range(a, lane, wid, stride, P, s0, s1);
     // every worker with a slot says whether its range starts inside a chunk
     if (wid < a.x_cap && lane == 0) {
       int32_t* mt = a.x_meta + 4 * (size_t)wid;

@@ -292,8 +292,8 @@ def test_multi_paged_validation_and_workspace():
     def a256(x):
         return -(-x // 256) * 256
 
-    def slots(S, R=16, d=128):   # worker slots: S*R*d and S*R*2 floats, S*4 int32
-        return a256(S * R * d * 4) + a256(S * R * 2 * 4) + a256(S * 16)
+    def slots(S, R=16, d=128):   # worker slots: S*R*d and S*R*2 floats, S*4 int32, one word
+        return a256(S * R * d * 4) + a256(S * R * 2 * 4) + a256(S * 16) + 256
     # partials of B*M*Hq rows over ceil(100 / 32) = 4 chunks, then B*Hkv*4 = 24
     # worker slots of R = G*M = 16 rows
     assert fd.workspace_bytes("fd_decode_attn_multi_paged", **base) == \
