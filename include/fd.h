@@ -242,19 +242,18 @@ int fd_decode_attn_multi(fd_dtype_t dt, const void* q, const void* k,
  *   or fp32, page_size in [8, 1024]).  Otherwise the matrix-core kernels:
  *   bf16, G*M <= 32, page_size a power of two in [16, 1024] and chunk /
  *   page_size <= 256, else FD_ERR_UNSUPPORTED.  The chunk is the split (the
- *   lengths live on the device).  With R = G*M <= 16 the pages that hold
- *   positions are divided evenly over the device's workers, so a worker may
- *   take a split from a page inside it on, and a second kernel folds that
- *   part into the split's partials with the same exact merge; the kernel
- *   also lengthens the split to chunk * F (F a power of two, at most 256
- *   pages) as long as every worker still gets a split's pages.  With 17-32
- *   rows each workgroup takes whole chunks.
+ *   lengths live on the device): the pages that hold positions are
+ *   divided evenly over the device's workers, so a worker may take a split
+ *   from a page inside it on, and a second kernel folds that part into the
+ *   split's partials with the same exact merge; the kernels also lengthen
+ *   the split to chunk * F (F a power of two, at most 256 pages) as long as
+ *   every worker still gets a split's pages.
  * Workspace: the partials of B*M*Hq rows over nc = ceil(max_seq_len / chunk)
  * chunks (layout of fd_decode_attn_partials with M*Hq heads; a longer split
- * uses the first slots of each row); with R <= 16 on the matrix-core kernel
- * followed by S = min(B*Hkv*nc (at least 1), 2048) worker slots:
- * 256-byte-aligned blocks of S*R*d and S*R*2 floats and S*4 int32, and 256
- * bytes.  Device-side values are clamped as in fd_decode_attn_paged.
+ * uses the first slots of each row); on the matrix-core kernels followed by
+ * S = min(B*Hkv*nc (at least 1), 2048) worker slots: 256-byte-aligned blocks
+ * of S*R*d and S*R*2 floats and S*4 int32 (R = G*M), and 256 bytes.
+ * Device-side values are clamped as in fd_decode_attn_paged.
  */
 int fd_decode_attn_multi_paged(fd_dtype_t dt, const void* q, const void* k_pool,
                                const void* v_pool, const int32_t* block_table,

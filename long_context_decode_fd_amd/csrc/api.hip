@@ -247,7 +247,7 @@ int run_multi(const void* q, const void* k, const void* v, float* out, float* ls
     ma.nc = n_chunks_of(L, ma.chunk);
   }
   split_ws(ws, B, M * Hq, ma.nc, d, &ma.o_part, &ma.ml_part);
-  if (paged != nullptr && (Hq / Hkv) * M <= 16) {
+  if (paged != nullptr) {
     const int R = (Hq / Hkv) * M;
     ma.x_cap = multi_worker_slots(B, Hkv, ma.nc);
     char* x = reinterpret_cast<char*>(ws) + partial_bytes(B, M * Hq, ma.nc, d);
@@ -527,7 +527,7 @@ int fd_decode_attn_multi_paged(fd_dtype_t dt, const void* q, const void* k_pool,
   if (int e = check_units(B, M * Hq, nc)) return e;
   const int R = (Hq / Hkv) * M;
   const size_t need = partial_bytes(B, M * Hq, nc, d) +
-                      (matrix && R <= 16 ? multi_worker_bytes(B, Hkv, nc, R, d) : 0);
+                      (matrix ? multi_worker_bytes(B, Hkv, nc, R, d) : 0);
   if (int e = workspace_gate(ws, ws_bytes, need)) return e;
   if (ws == nullptr) return ok();
   if (!q || !k_pool || !v_pool || !block_table || !seq_lens || !out)

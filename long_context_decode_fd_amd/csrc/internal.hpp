@@ -102,9 +102,9 @@ struct MultiArgs {
   float* x_ml;
   int32_t* x_meta;
   int x_cap;
-  // Paged, one query tile: the kernel lengthens the split to chunk * F (F a
-  // power of two, at most kMultiPagePids pages) as far as the workers keep
-  // their number, and writes F here for the merge.
+  // Paged: the kernel lengthens the split to chunk * F (F a power of two, at
+  // most kMultiPagePids pages) as far as the workers keep their number, and
+  // writes F here for the merge.
   int32_t* x_split;
 };
 constexpr int kMultiPagePids = 256;

@@ -40,7 +40,7 @@ int multi_fold(int D, const MultiArgs& a) {
   return best;
 }
 
-// Paged calls: each part that a worker's range cut off a chunk's start
+// Paged calls: each part that a worker's range cut off a split's start
 // (slot w, flagged in x_meta) is folded into that chunk's partials by the
 // exact merge of two parts ("Flash Decoding" explainer, section 2):
 // m = max(m1, m2), O = 2^(m1 - m) O1 + 2^(m2 - m) O2, l likewise (m in log2
@@ -54,9 +54,9 @@ __global__ __launch_bounds__(kWave) void multi_fixup_kernel(MultiArgs a, int wor
   const int32_t* mt = a.x_meta + 4 * (size_t)w;
   if (mt[3] == 0) return;
   const int b = mt[0], kvh = mt[1], c = mt[2];
-  const int G = a.Hq / a.Hkv, R = G * a.M;   // at most 16 rows
+  const int G = a.Hq / a.Hkv, R = G * a.M;   // at most 32 rows
   constexpr int CPR = D / 4;                 // 16-byte pieces per row
-  constexpr int NP = 16 * CPR / kWave;       // pieces of 16 rows per lane
+  constexpr int NP = 32 * CPR / kWave;       // pieces of 32 rows per lane
   const int lane = (int)threadIdx.x;
   // every load first (one memory latency); rows past R read row R - 1 and
   // write nothing
@@ -94,8 +94,7 @@ hipError_t launch_multi(int D, const MultiArgs& a, hipStream_t s) {
   if ((a.Hq / a.Hkv) * a.M > 16) e = launch_multi_pair(D, a, s, &workers);
   else if (D == 64) e = launch_multi_d<64>(a, s, &workers);
   else if (D == 128) e = launch_multi_d<128>(a, s, &workers);
-  // the wave-pair kernel keeps whole units per workgroup
-  if (e != hipSuccess || a.block_table == nullptr || (a.Hq / a.Hkv) * a.M > 16) return e;
+  if (e != hipSuccess || a.block_table == nullptr) return e;
   workers = std::min(workers, a.x_cap);
   if (workers <= 0) return hipSuccess;
   if (D == 64)

@@ -48,7 +48,9 @@ constexpr int kVStride = 2 * D + 32;
 // PAGED: k and v are page pools, as in the one-tile kernel.
 template <int D, bool PAGED>
 __global__ __launch_bounds__(2 * kWave) __attribute__((amdgpu_waves_per_eu(2)))
-void multi_pair_kernel(MultiArgs a) {
+void multi_pair_kernel(MultiArgs a0) {
+  // paged: the split may grow on the device (paged_split_factor)
+  MultiArgs a = a0;
   constexpr int KS = D / 32;             // QK k-steps (32 dims each)
   constexpr int DB = D / 16;             // 16-dim blocks of the P V product
   constexpr int TT = kPairTiles;
@@ -83,7 +85,7 @@ void multi_pair_kernel(MultiArgs a) {
   // a unit: sequence b (holding L positions), kv-head, split c = [c0, c1)
   // (empty when a paged sequence is shorter than the split's start)
   struct UnitM {
-    int b, kvh, c, c0, c1, L;
+    int b, kvh, c, c0, c1, L, xw;
   };
   auto seq_len = [&](int b) {
     if constexpr (PAGED) {
@@ -94,6 +96,9 @@ void multi_pair_kernel(MultiArgs a) {
     }
   };
   PagedWalk walk{};   // paged: the units that hold positions
+  // paged: this workgroup's units [u_first, u_last], the first from
+  // position pos0, the last up to pos1 (paged_worker_range)
+  int u_first = -1, u_last = -1, pos0 = 0, pos1 = 0;
   auto decode = [&](int u, UnitM& x) {
     if constexpr (PAGED) {
       paged_walk_decode(a, u, walk, x.b, x.kvh, x.c);
@@ -106,6 +111,14 @@ void multi_pair_kernel(MultiArgs a) {
     x.L = seq_len(x.b);
     x.c0 = x.c * a.chunk;
     x.c1 = min(x.c0 + a.chunk, x.L);
+    x.xw = -1;
+    if constexpr (PAGED) {
+      if (u == u_first && x.c0 < pos0) {
+        x.c0 = pos0;
+        x.xw = (int)blockIdx.x;
+      }
+      if (u == u_last) x.c1 = min(x.c1, pos1);
+    }
   };
   // first byte of row t0 (a multiple of 16 in [c0, c1) when `used`; else
   // nothing is read there and any row will do) of unit x's K or V
@@ -162,13 +175,19 @@ void multi_pair_kernel(MultiArgs a) {
   // partials of unit x: rows ((b*M + r)*Hq + h)*nc + c; called after a
   // barrier, when no wave reads the tiles any more
   // (x as decoded when the unit ran: the paged walker only moves forward)
+  // partial row of query row r (< R) of unit x, in o_part / ml_part or, for
+  // a part cut off a split's start, in x_o / x_ml
+  auto part_row = [&](const UnitM& x, int r) {
+    return x.xw >= 0 ? (size_t)x.xw * R + r
+                     : (((size_t)x.b * a.M + r / G) * a.Hq + (size_t)x.kvh * G + r % G) * a.nc +
+                           x.c;
+  };
   auto store_unit = [&](const f32x4 (&o)[DB], float m, float l, const UnitM& x) {
-    if (qd == 0 && qrow < R) {
-      const size_t prow =
-          (((size_t)x.b * a.M + qrow / G) * a.Hq + (size_t)x.kvh * G + qrow % G) * a.nc + x.c;
-      *reinterpret_cast<f32x2*>(a.ml_part + prow * 2) =
+    float* const op = x.xw >= 0 ? a.x_o : a.o_part;
+    float* const mlp = x.xw >= 0 ? a.x_ml : a.ml_part;
+    if (qd == 0 && qrow < R)
+      *reinterpret_cast<f32x2*>(mlp + part_row(x, qrow) * 2) =
           f32x2{(m == kNegInf) ? kNegInf : m * c_log2, l};
-    }
     // lane (n, qd) holds O rows 4 qd + e, dims 16 db + n
 #pragma unroll
     for (int e = 0; e < 4; ++e)
@@ -180,24 +199,47 @@ void multi_pair_kernel(MultiArgs a) {
       const int rr = ORPI * i + lane / LPO, cb = 16 * (lane % LPO);
       const f32x4 v = *reinterpret_cast<const f32x4*>(o_stage(rr) + cb);
       const int row = row0 + rr;
-      if (row < R) {
-        const size_t prow =
-            (((size_t)x.b * a.M + row / G) * a.Hq + (size_t)x.kvh * G + row % G) * a.nc + x.c;
-        *reinterpret_cast<f32x4*>(reinterpret_cast<unsigned char*>(a.o_part + prow * D) + cb) = v;
-      }
+      if (row < R)
+        *reinterpret_cast<f32x4*>(reinterpret_cast<unsigned char*>(op + part_row(x, row) * D) +
+                                  cb) = v;
     }
   };
 
-  // workgroup w takes the consecutive units [w*per, (w+1)*per) (paged: of
-  // the units that hold positions; dividing the pages evenly over the
-  // workgroups, as the one-tile kernel does, measured 1.7 % slower here)
-  int total = n_units;
-  if constexpr (PAGED) total = paged_walk_start(a, lane, 0, walk);
-  const int per = (total + (int)gridDim.x - 1) / (int)gridDim.x;
-  int u = (int)blockIdx.x * per;
-  const int u_end = min(u + per, total);
-  if (u >= total) return;   // both waves of the workgroup
-  if constexpr (PAGED) paged_walk_start(a, lane, u, walk);
+  // workgroup w takes the consecutive units [w*per, (w+1)*per) (paged: the
+  // units of its range of pages, paged_worker_range; both waves compute
+  // the same range)
+  int u, u_end;
+  if constexpr (PAGED) {
+    const long long P = paged_pages(a, lane);
+    const int F = paged_split_factor(a, P, (int)gridDim.x);
+    a.chunk *= F;
+    if (blockIdx.x == 0 && threadIdx.x == 0) *a.x_split = F;   // for the merge
+    PagedSpot s0{}, s1{};
+    const bool any =
+        paged_worker_range(a, lane, (int)blockIdx.x, (int)gridDim.x, P, s0, s1);
+    if ((int)blockIdx.x < a.x_cap && threadIdx.x == 0) {
+      int32_t* mt = a.x_meta + 4 * (size_t)blockIdx.x;
+      mt[0] = s0.b;
+      mt[1] = s0.kvh;
+      mt[2] = s0.c;
+      mt[3] = any && s0.pos % a.chunk != 0 ? 1 : 0;
+    }
+    if (!any) return;   // both waves of the workgroup
+    u = __builtin_amdgcn_readfirstlane(s0.u);
+    u_end = __builtin_amdgcn_readfirstlane(s1.u) + 1;
+    u_first = u;
+    u_last = u_end - 1;
+    pos0 = __builtin_amdgcn_readfirstlane(s0.pos);
+    pos1 = __builtin_amdgcn_readfirstlane(s1.pos) + (1 << a.page_shift);
+    walk.b = __builtin_amdgcn_readfirstlane(s0.b);
+    walk.first = __builtin_amdgcn_readfirstlane(s0.first);
+    walk.units = __builtin_amdgcn_readfirstlane(s0.units);
+  } else {
+    const int per = (n_units + (int)gridDim.x - 1) / (int)gridDim.x;
+    u = (int)blockIdx.x * per;
+    u_end = min(u + per, n_units);
+    if (u >= n_units) return;   // both waves of the workgroup
+  }
   UnitM cur;
   decode(u, cur);
   u32x4 kr[TW][NI], vr[TW][NI];
@@ -361,7 +403,7 @@ size_t pair_slots() {
   return (size_t)cu_count() * per_cu;
 }
 
-// *workers: the workgroups launched.
+// *workers: the workgroups launched (each a worker of a paged call).
 template <int D>
 hipError_t launch_pair(const MultiArgs& a, hipStream_t s, int* workers) {
   auto kernel = a.block_table != nullptr ? multi_pair_kernel<D, true> : multi_pair_kernel<D, false>;
@@ -369,7 +411,9 @@ hipError_t launch_pair(const MultiArgs& a, hipStream_t s, int* workers) {
   const size_t units = (size_t)a.B * a.Hkv * a.nc;
   const size_t slots = pair_slots<D>();
   const size_t rounds = (units + slots - 1) / slots;
-  const unsigned grid = (unsigned)((units + rounds - 1) / rounds);
+  // paged: every resident workgroup (the pages are divided over the workers)
+  const unsigned grid = a.block_table != nullptr ? (unsigned)std::min(units, slots)
+                                                 : (unsigned)((units + rounds - 1) / rounds);
   *workers = (int)grid;
   hipLaunchKernelGGL(kernel, dim3(grid), dim3(2 * kWave), 0, s, a);
   return hipGetLastError();

@@ -300,9 +300,9 @@ def test_multi_paged_validation_and_workspace():
         3 * 4 * 8 * 4 * 128 * 4 + 3 * 4 * 8 * 4 * 2 * 4 + slots(24)
     assert fd.workspace_bytes("fd_decode_attn_multi_paged", **dict(base, max_seq_len=0)) == \
         256 + slots(1)
-    # 17-32 rows (the wave-pair kernel): whole chunks per workgroup, no slots
+    # 17-32 rows (the wave-pair kernel): slots of R = 32 rows
     assert fd.workspace_bytes("fd_decode_attn_multi_paged", **dict(base, M=8)) == \
-        3 * 8 * 8 * 4 * 128 * 4 + 3 * 8 * 8 * 4 * 2 * 4
+        3 * 8 * 8 * 4 * 128 * 4 + 3 * 8 * 8 * 4 * 2 * 4 + slots(24, R=32)
     # the slots stop at 2,048 workers
     big = dict(base, B=64, Hkv=8, Hq=128, M=1, max_pages=8192, max_seq_len=131072, chunk=1024)
     nc = 128
