@@ -92,10 +92,14 @@ int fd_abi_version(void);
  * stay multiples of 16, so that every SIMD reads a share of the cache; the
  * workspace query accounts for it (the same rule holds for the paged entry
  * points, whose splits stay multiples of the page, with max_seq_len as L).
- * G in {1, 2, 4, 8}: the vector kernel, bf16 or fp32.  Other G <= 32 (bf16
- * only, else FD_ERR_UNSUPPORTED): the matrix-core kernel of
+ * G in {1, 2, 4, 8}: the vector kernel, bf16 or fp32, except bf16 with
+ * G = 8 on calls of at least 1,024 units, which take the matrix-core kernel
+ * (eight heads per kv-head keep the vector kernel issue-bound).  Other
+ * G <= 32 (bf16 only, else FD_ERR_UNSUPPORTED): the matrix-core kernel of
  * fd_decode_attn_multi with one token, whose splits may then cover several
- * consecutive chunks (same result up to fp32 rounding).
+ * consecutive chunks (same result up to fp32 rounding).  The same choice
+ * holds for fd_decode_attn_noalloc and fd_decode_attn_partials (whose
+ * partials stay per chunk).
  */
 int fd_decode_attn(fd_dtype_t dt, const void* q, const void* k, const void* v,
                    float* out, float* lse,
@@ -166,6 +170,10 @@ int fd_merge_partials(const float* o_part, const float* ml_part, float* out,
  *   max_seq_len     host-side upper bound of seq_lens (sizes grid and
  *                   workspace); must not exceed max_pages_per_seq * page_size
  *   page_size       a power of two in [8, 1024]; chunk % page_size == 0
+ * bf16 with G = 8, at least 1,024 (sequence, kv-head, chunk) units over
+ * max_seq_len, pages of 16 or more and chunk / page_size <= 256 runs as
+ * fd_decode_attn_multi_paged with one token (its kernel, workspace and
+ * result); otherwise the vector kernel.
  * Device-side values are clamped so that nothing is read out of bounds: a
  * length above max_seq_len is treated as max_seq_len and a page id outside
  * [0, num_pages) as the nearest valid id (the result is then meaningless).
@@ -211,7 +219,8 @@ int fd_decode_attn_unified_max(fd_dtype_t dt, const void* q, const void* k,
  * {1, 2, 4, 8} takes the single-query vector kernel of fd_decode_attn.
  *   q     [B, M, Hq, d]; k, v [B, Hkv, L, d]; L >= M
  *   out   fp32 [B, M, Hq, d];  lse fp32 [B, M, Hq] or NULL
- *   M = 1 and G in {1, 2, 4, 8}: dt bf16 or fp32.  Otherwise bf16 only and
+ *   M = 1 and G in {1, 2, 4, 8}: dt bf16 or fp32 (the kernel fd_decode_attn
+ *   picks).  Otherwise bf16 only and
  *   G*M <= 32, else FD_ERR_UNSUPPORTED.  Workspace: chunk partials of the B*M*Hq rows
  *   (same layout as fd_decode_attn_partials with M*Hq heads), sized for
  *   `chunk`.  On the matrix cores chunk is the split granule: when the rows' chunks
@@ -238,8 +247,10 @@ int fd_decode_attn_multi(fd_dtype_t dt, const void* q, const void* k,
  * ("Flash Decoding" explainer, sections 1 and 3).  A token with no position
  * to attend to (seq_lens[b]-M+r < 0) gets out = 0, lse = -inf.
  *   q    [B, M, Hq, d];  out fp32 [B, M, Hq, d];  lse fp32 [B, M, Hq] or NULL
- *   M = 1 and G in {1, 2, 4, 8}: the kernel of fd_decode_attn_paged (bf16
- *   or fp32, page_size in [8, 1024]).  Otherwise the matrix-core kernels:
+ *   M = 1 and G in {1, 2, 4, 8}: the vector kernel of fd_decode_attn_paged
+ *   (bf16 or fp32, page_size in [8, 1024]; bf16 with G = 8 takes the
+ *   matrix-core kernel where fd_decode_attn_paged does).  Otherwise the
+ *   matrix-core kernels:
  *   bf16, G*M <= 32, page_size a power of two in [16, 1024] and chunk /
  *   page_size <= 256, else FD_ERR_UNSUPPORTED.  The chunk is the split (the
  *   lengths live on the device): the pages that hold positions are

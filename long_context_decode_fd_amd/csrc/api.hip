@@ -68,13 +68,14 @@ int check_vector_group(int G) {
   return FD_OK;
 }
 
-// Dense paths: M query tokens per sequence.  One token with G in {1,2,4,8}
-// takes the vector kernel (bf16 or fp32); every other case the matrix-core
-// kernels, which take bf16 and up to 32 query rows (G * M) per kv-head.
-bool matrix_path(int G, int M) { return M > 1 || !vector_group(G); }
+// Dense paths: M query tokens per sequence.  Every case the vector kernel
+// (one token, G in {1,2,4,8}, bf16 or fp32) does not take runs on the
+// matrix-core kernels, which take bf16 and up to 32 query rows (G * M) per
+// kv-head.
+bool matrix_needed(int G, int M) { return M > 1 || !vector_group(G); }
 
 int check_dense_group(fd_dtype_t dt, int G, int M) {
-  if (!matrix_path(G, M)) return FD_OK;
+  if (!matrix_needed(G, M)) return FD_OK;
   if ((long long)G * M > 32)
     return fail(FD_ERR_UNSUPPORTED, "G*M=%lld query rows per kv-head exceed 32",
                 (long long)G * M);
@@ -187,6 +188,18 @@ int full_call_split(int B, int Hkv, int L, int chunk, int unit = 16) {
          split / 2 >= 32 && (split / 2) % unit == 0)
     split /= 2;
   return split;
+}
+
+// The matrix-core kernels also take, by choice, bf16 single-token calls
+// with G = 8 once they have at least 1,024 (sequence, kv-head, chunk) units
+// (L: the longest sequence): eight query heads per lane group leave the
+// vector kernel issue-bound (B 8, Hkv 8, L 32768, d 128: 240.7 us, 56 % of
+// 8 TB/s) where the matrix cores take the products (161.6 us, 83 %); d 64:
+// 126.8 -> 100.6 us.  Shorter calls keep the vector kernel and its shorter
+// splits (B 1, L 32768: 39.4 against 44.1 us).
+bool matrix_path(fd_dtype_t dt, int G, int M, int B, int Hkv, int L, int chunk) {
+  if (matrix_needed(G, M)) return true;
+  return dt == FD_BF16 && G == 8 && (long long)B * Hkv * n_chunks_of(L, chunk) >= kSimdUnits;
 }
 
 // Enqueue the partial kernel and (when out != NULL) the merge.
@@ -316,7 +329,7 @@ int fd_decode_attn(fd_dtype_t dt, const void* q, const void* k, const void* v, f
   if (int e = check_scale(scale)) return e;
   const int nc = n_chunks_of(L, chunk);
   if (int e = check_units(B, Hq, nc)) return e;
-  const bool matrix = matrix_path(Hq / Hkv, 1);
+  const bool matrix = matrix_path(dt, Hq / Hkv, 1, B, Hkv, L, chunk);
   const int split = matrix ? chunk : full_call_split(B, Hkv, L, chunk);
   const int ns = n_chunks_of(L, split);
   if (int e = check_units(B, Hq, ns)) return e;
@@ -343,7 +356,7 @@ int fd_decode_attn_noalloc(fd_dtype_t dt, const void* q, const void* k, const vo
   if (int e = check_scale(scale)) return e;
   const int nc = n_chunks_of(L, chunk);
   if (int e = check_units(B, Hq, nc)) return e;
-  const bool matrix = matrix_path(Hq / Hkv, 1);
+  const bool matrix = matrix_path(dt, Hq / Hkv, 1, B, Hkv, L, chunk);
   const int split = matrix ? chunk : full_call_split(B, Hkv, L, chunk);
   const int ns = n_chunks_of(L, split);
   if (int e = check_units(B, Hq, ns)) return e;
@@ -381,7 +394,7 @@ int fd_decode_attn_partials(fd_dtype_t dt, const void* q, const void* k, const v
   if (!q || !k || !v) return fail(FD_ERR_ARG, "q, k and v must not be NULL");
   if (!aligned16(q) || !aligned16(k) || !aligned16(v))
     return fail(FD_ERR_ARG, "q, k and v must be 16-byte aligned");
-  if (matrix_path(Hq / Hkv, 1))
+  if (matrix_path(dt, Hq / Hkv, 1, B, Hkv, L, chunk))
     return run_multi(q, k, v, nullptr, nullptr, B, 1, Hq, Hkv, L, d, scale, chunk, nc, ws,
                      false, stream);
   fdk::PartialArgs pa{};
@@ -419,6 +432,13 @@ int fd_decode_attn_paged(fd_dtype_t dt, const void* q, const void* k_pool,
     return e;
   if (chunk / page_size > 1024)
     return fail(FD_ERR_UNSUPPORTED, "chunk/page_size=%d exceeds 1024", chunk / page_size);
+  // bf16 with G = 8 on a long call: the matrix-core kernel of the multi-row
+  // entry point with one token (q [B, Hq, d] is q [B, 1, Hq, d])
+  if (matrix_path(dt, Hq / Hkv, 1, B, Hkv, max_seq_len, chunk) && page_size >= 16 &&
+      chunk / page_size <= fdk::kMultiPagePids)
+    return fd_decode_attn_multi_paged(dt, q, k_pool, v_pool, block_table, seq_lens, out, lse, B,
+                                      1, Hq, Hkv, d, page_size, max_pages_per_seq, num_pages,
+                                      max_seq_len, scale, chunk, ws, ws_bytes, stream);
   const int split = full_call_split(B, Hkv, max_seq_len, chunk, page_size);
   const int nc = n_chunks_of(max_seq_len, split);
   if (int e = check_units(B, Hq, nc)) return e;
@@ -481,7 +501,7 @@ int fd_decode_attn_multi(fd_dtype_t dt, const void* q, const void* k, const void
   if (int e = check_dense_group(dt, Hq / Hkv, M)) return e;
   const int nc = n_chunks_of(L, chunk);
   if (int e = check_units(B, M * Hq, nc)) return e;
-  const bool matrix = matrix_path(Hq / Hkv, M);
+  const bool matrix = matrix_path(dt, Hq / Hkv, M, B, Hkv, L, chunk);
   const int split = matrix ? chunk : full_call_split(B, Hkv, L, chunk);
   const int ns = n_chunks_of(L, split);
   if (int e = check_units(B, M * Hq, ns)) return e;
@@ -512,10 +532,13 @@ int fd_decode_attn_multi_paged(fd_dtype_t dt, const void* q, const void* k_pool,
   if (int e = check_dense_group(dt, Hq / Hkv, M)) return e;
   if (int e = check_chunk(chunk)) return e;
   if (int e = check_scale(scale)) return e;
-  const bool matrix = matrix_path(Hq / Hkv, M);
   int shift = 0;
   if (int e = check_pages(chunk, page_size, 8, max_pages_per_seq, num_pages, max_seq_len, &shift))
     return e;
+  // the optional matrix-core case (G = 8) only where its page limits hold
+  const bool matrix = matrix_needed(Hq / Hkv, M) ||
+                      (matrix_path(dt, Hq / Hkv, M, B, Hkv, max_seq_len, chunk) &&
+                       page_size >= 16 && chunk / page_size <= fdk::kMultiPagePids);
   if (matrix && page_size < 16)
     return fail(FD_ERR_UNSUPPORTED, "page_size=%d: the matrix-core kernels take pages of 16 "
                                     "positions or more", page_size);

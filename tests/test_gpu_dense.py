@@ -219,3 +219,21 @@ def test_dense_one_million_positions():
     out, lse = fd.decode_attn(c.q, c.k, c.v, chunk=c.chunk)
     torch.cuda.synchronize()
     _check_every_row(c, out, lse)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("d", [64, 128])
+def test_group_of_eight_long_calls(dtype, d):
+    """G = 8 on a call of 1,024 (sequence, kv-head, chunk) units: bf16 runs on
+    the matrix-core kernel, fp32 on the vector kernel; every row against the
+    oracle, and the partials entry point merged gives the same rows."""
+    banner(f"dense G=8 long call {dtype} d={d}")
+    c = W.dense_case(8, 64, 8, 8192 - 5, d, dtype, 512, seed=1300 + d, device=DEV)
+    out, _ = _check(c)
+    ws, nc = fd.decode_attn_partials(c.q, c.k, c.v, chunk=512)
+    o_part, ml_part = fd.partial_views(ws, 8, 64, nc, d)
+    out2, lse2 = fd.merge_partials(o_part, ml_part)
+    torch.cuda.synchronize()
+    ref, lref = ofd.dense_attention(f64(c.q), f64(c.k), f64(c.v), c.scale)
+    assert max_err(f64(out2), ref) <= TOL[c.q.dtype]
+    assert max_err(f64(lse2), lref) <= TOL[c.q.dtype]

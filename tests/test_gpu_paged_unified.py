@@ -234,3 +234,20 @@ def test_unified_one_million_positions():
     c = W.dense_case(1, 8, 2, (1 << 20) + 9, 128, "bf16", 512, seed=1207, device=DEV)
     flags = _unified_check(c, 1.0, 1.0, 1.5)
     assert 0 < int(flags.sum()) < flags.size
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+@pytest.mark.parametrize("page", [16, 64])
+def test_paged_group_of_eight_long_calls(dtype, page):
+    """G = 8 over a ragged paged cache with 1,024 or more (sequence, kv-head,
+    chunk) units: bf16 takes the matrix-core kernel (pages divided over the
+    workers), fp32 the vector kernel; every row against the oracle."""
+    banner(f"paged G=8 long call {dtype} page={page}")
+    c = W.paged_case(16, 64, 8, 128, 1024, 16384, page=page, chunk=512, seed=1400 + page,
+                     device=DEV)
+    if dtype == torch.float32:
+        c.q, c.k_pool, c.v_pool = c.q.float(), c.k_pool.float(), c.v_pool.float()
+    out, lse = _paged_run(c)
+    ref, lref = _paged_ref(c)
+    assert max_err(f64(out), ref) <= TOL[dtype]
+    assert max_err(f64(lse), lref) <= TOL[dtype]
