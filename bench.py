@@ -13,8 +13,8 @@ decode-attention call over the whole batch (every kernel of the call).
                with HIP events on the launch stream: KV + query bytes per
                launch / mean launch time, against 8 TB/s
   cpu_baseline = the fp64 CPU oracle on a bounded sample of the same workload
-  variants   = config 1, one sequence at 8K and 32K, dense at 128K, a group
-               of 16 query heads per kv-head,
+  variants   = config 1, one sequence at 8K and 32K, dense at 128K, group
+               sizes 1, 2, 8, 16 and 32 on the headline cache,
                the paged (one and four tokens), fixed-maximum, FFD, multi-row
                and cache-append entry points on their own workloads (same
                timing method)
@@ -40,7 +40,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 PEAK_GBS = 8000.0       # MI355X HBM3E peak, GB/s
-VARIANTS = ("config1", "dense_b1", "dense_128k", "group16", "paged", "paged_multi", "unified_max",
+VARIANTS = ("config1", "dense_b1", "dense_128k", "groups", "paged", "paged_multi", "unified_max",
             "ffd", "ffd_peaked", "multi_row", "append")
 METRIC = "us/decode step and achieved KV-read HBM GB/s (% of peak) at 32K-128K ctx"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_partial_dense_b8_h32x8_d128_l32768.txt")
@@ -421,36 +421,42 @@ def variant_dense_128k(torch, fd, W, args, timer):
                 pct_of_peak=round(100 * gbs(nbytes, t["ms"]) / PEAK_GBS, 1))
 
 
-def variant_group16(torch, fd, W, args, timer):
-    """Single-query decode with 16 query heads per kv-head (B 8, Hq 128,
-    Hkv 8, d 128, L 32768, chunk 512: the headline cache), which runs on the
-    matrix-core kernel: its 16 query rows of a kv-head fill one tile."""
-    B, Hq, Hkv, L, d, chunk = 8, 128, 8, 32768, 128, 512
-    c = W.multi_case(B, 1, Hq, Hkv, L, d, chunk=chunk, seed=1216, device="cuda:0")
-    q = c.q[:, 0].contiguous()
+def variant_groups(torch, fd, W, args, timer):
+    """Single-query decode on the headline cache (B 8, Hkv 8, d 128, L 32768,
+    chunk 512, bf16) with G = 1, 2, 8, 16 and 32 query heads per kv-head
+    (Hq = 8 G): the vector kernel for G 1 and 2, the matrix-core kernel for
+    G 8 (chosen: the vector kernel is issue-bound there), 16 and 32 (one and
+    two query tiles)."""
+    B, Hkv, L, d, chunk = 8, 8, 32768, 128, 512
+    c = W.multi_case(B, 1, 32 * Hkv, Hkv, L, d, chunk=chunk, seed=1216, device="cuda:0")
     ks = [c.k] + [c.k.clone() for _ in range(args.copies - 1)]
     vs = [c.v] + [c.v.clone() for _ in range(args.copies - 1)]
     lib = fd.lib()
-    out = torch.empty((B, Hq, d), dtype=torch.float32, device="cuda:0")
-    lse = torch.empty((B, Hq), dtype=torch.float32, device="cuda:0")
-    wsn = fd.workspace_bytes("fd_decode_attn", B=B, Hq=Hq, Hkv=Hkv, L=L, d=d, chunk=chunk)
-    ws = torch.empty(wsn, dtype=torch.uint8, device="cuda:0")
-    size = C.c_size_t(wsn)
     st = C.c_void_p(torch.cuda.current_stream().cuda_stream)
-    calls = []
-    for k, v in zip(ks, vs):
-        a = (fd.FD_BF16, vp(q), vp(k), vp(v), vp(out), vp(lse), B, Hq, Hkv, L, d, c.scale,
-             chunk, vp(ws), C.byref(size), st)
-        calls.append(lambda a=a: lib.fd_decode_attn(*a))
-    check_rc(lib, calls[0]())
-    t = timer.run(calls, args.steps, args.warmup)
-    nbytes = 2 * B * Hkv * L * d * 2 + B * Hq * d * 2 + B * Hq * (d + 1) * 4
-    return dict(workload=f"dense GQA decode bf16, group of 16: B={B}, Hq={Hq}, Hkv={Hkv}, d={d}, "
-                         f"L={L}, chunk={chunk} (matrix-core kernel)",
-                us_per_step=round(t["ms"] * 1e3, 2), p10_us=round(t["p10"] * 1e3, 2),
-                p90_us=round(t["p90"] * 1e3, 2), bytes=nbytes,
-                gbs=round(gbs(nbytes, t["ms"]), 1),
-                pct_of_peak=round(100 * gbs(nbytes, t["ms"]) / PEAK_GBS, 1))
+    res = dict(workload=f"dense decode bf16 by group size: B={B}, Hkv={Hkv}, d={d}, L={L}, "
+                        f"chunk={chunk}, Hq = 8 G (G 1, 2: vector kernel; 8, 16, 32: "
+                        f"matrix-core kernel)")
+    for G in (1, 2, 8, 16, 32):
+        Hq = G * Hkv
+        q = c.q[:, 0, :Hq].contiguous()
+        out = torch.empty((B, Hq, d), dtype=torch.float32, device="cuda:0")
+        lse = torch.empty((B, Hq), dtype=torch.float32, device="cuda:0")
+        wsn = fd.workspace_bytes("fd_decode_attn", B=B, Hq=Hq, Hkv=Hkv, L=L, d=d, chunk=chunk)
+        ws = torch.empty(wsn, dtype=torch.uint8, device="cuda:0")
+        size = C.c_size_t(wsn)
+        calls = []
+        for k, v in zip(ks, vs):
+            a = (fd.FD_BF16, vp(q), vp(k), vp(v), vp(out), vp(lse), B, Hq, Hkv, L, d, c.scale,
+                 chunk, vp(ws), C.byref(size), st)
+            calls.append(lambda a=a: lib.fd_decode_attn(*a))
+        check_rc(lib, calls[0]())
+        t = timer.run(calls, args.steps, args.warmup)
+        nbytes = 2 * B * Hkv * L * d * 2 + B * Hq * d * 2 + B * Hq * (d + 1) * 4
+        res[f"G_{G}"] = dict(Hq=Hq, us_per_step=round(t["ms"] * 1e3, 2),
+                             p10_us=round(t["p10"] * 1e3, 2), p90_us=round(t["p90"] * 1e3, 2),
+                             bytes=nbytes, gbs=round(gbs(nbytes, t["ms"]), 1),
+                             pct_of_peak=round(100 * gbs(nbytes, t["ms"]) / PEAK_GBS, 1))
+    return res
 
 
 def variant_multi(torch, fd, W, args, timer):
@@ -944,7 +950,7 @@ def main():
     if not args.no_variants:
         fns = dict(config1=variant_config1, dense_b1=variant_dense_b1,
                    dense_128k=variant_dense_128k,
-                   group16=variant_group16, paged=variant_paged,
+                   groups=variant_groups, paged=variant_paged,
                    paged_multi=variant_paged_multi,
                    unified_max=variant_unified, ffd=variant_ffd, ffd_peaked=variant_ffd_peaked,
                    multi_row=variant_multi, append=variant_append)
