@@ -196,7 +196,10 @@ int fd_decode_attn_paged(fd_dtype_t dt, const void* q, const void* k_pool,
  * phi + margin_hi or falls below phi - margin_lo; such chunks are recomputed
  * exactly with their own maximum, inside the same kernel, before the merge.
  * The result is the dense result (softmax is shift invariant) for any finite
- * phi.
+ * phi.  bf16 with G = 8 on a call of at least 1,024 units (where the vector
+ * kernel is issue-bound) computes every chunk with its own maximum on the
+ * matrix-core kernel instead, and sets the flags from the chunks' maxima
+ * by the same range test.
  *   Arguments as fd_decode_attn, plus
  *   phi, margin_hi, margin_lo   finite; margins >= 0
  *   chunk_flags   uint8 [B, Hq, n_chunks] or NULL: 1 where the chunk was out

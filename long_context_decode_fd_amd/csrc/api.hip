@@ -480,6 +480,25 @@ int fd_decode_attn_unified_max(fd_dtype_t dt, const void* q, const void* k, cons
   if (!q || !k || !v || !out) return fail(FD_ERR_ARG, "q, k, v and out must not be NULL");
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
     return fail(FD_ERR_ARG, "q, k, v and out must be 16-byte aligned");
+  if (matrix_path(dt, Hq / Hkv, 1, B, Hkv, L, chunk)) {
+    // bf16 with G = 8 on a long call: every chunk with its own maximum on
+    // the matrix-core kernel (exact; the fixed maximum saves no work there),
+    // and the range flags from the chunks' maxima, kept per chunk (m in
+    // log2 units of the scaled score: the bounds times log2 e)
+    if (int e = run_multi(q, k, v, out, lse, B, 1, Hq, Hkv, L, d, scale, chunk, nc, ws, false,
+                          stream))
+      return e;
+    if (chunk_flags == nullptr) return ok();
+    float *o_part, *ml_part;
+    split_ws(ws, B, Hq, nc, d, &o_part, &ml_part);
+    const double l2e = 1.4426950408889634;
+    return hip_status(
+        fdk::launch_range_flags(ml_part, chunk_flags, (size_t)B * Hq * nc,
+                                (float)(((double)phi + margin_hi) * l2e),
+                                (float)(((double)phi - margin_lo) * l2e),
+                                reinterpret_cast<hipStream_t>(stream)),
+        "range flags launch");
+  }
   fdk::PartialArgs pa{};
   pa.flags = chunk_flags;
   pa.phi_raw = (float)((double)phi / (double)scale);

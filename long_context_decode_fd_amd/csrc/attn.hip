@@ -814,6 +814,24 @@ hipError_t launch_partial(int mode, int is_bf16, int D, int G, const PartialArgs
   return hipErrorInvalidValue;
 }
 
+// Range flags of the fixed maximum from chunk partials (the chunks' own
+// maxima): one thread per (sequence, head, chunk).
+__global__ __launch_bounds__(256) void range_flags_kernel(const float* ml, uint8_t* flags,
+                                                         size_t n, float hi, float lo) {
+  const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n) return;
+  const float m = ml[2 * i];
+  flags[i] = (uint8_t)((m > hi || m < lo) ? 1 : 0);
+}
+
+hipError_t launch_range_flags(const float* ml, uint8_t* flags, size_t n, float hi, float lo,
+                              hipStream_t s) {
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL(range_flags_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, ml,
+                     flags, n, hi, lo);
+  return hipGetLastError();
+}
+
 hipError_t launch_merge(int D, int B, const MergeArgs& a, hipStream_t s) {
   const size_t rows = (size_t)B * a.Hq;
   // rows of at most 256 chunks: one wave per (row, column slice), 16 chunks

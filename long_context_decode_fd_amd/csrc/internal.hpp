@@ -44,6 +44,10 @@ struct MergeArgs {
 hipError_t launch_partial(int mode, int is_bf16, int D, int G,
                           const PartialArgs& a, hipStream_t s);
 hipError_t launch_merge(int D, int B, const MergeArgs& a, hipStream_t s);
+// flags[i] = 1 where a chunk maximum m_i (ml[2 i], log2 units of the scaled
+// score) lies above hi or below lo, else 0; n entries.
+hipError_t launch_range_flags(const float* ml, uint8_t* flags, size_t n, float hi, float lo,
+                              hipStream_t s);
 
 struct FfdPackArgs {
   const uint16_t* k;   // bf16 [B, Hkv, Lcap, D]

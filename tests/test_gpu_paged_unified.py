@@ -251,3 +251,16 @@ def test_paged_group_of_eight_long_calls(dtype, page):
     ref, lref = _paged_ref(c)
     assert max_err(f64(out), ref) <= TOL[dtype]
     assert max_err(f64(lse), lref) <= TOL[dtype]
+
+
+@pytest.mark.parametrize("phi,margin_hi,margin_lo", [(3.0, 0.5, 0.5), (0.0, 10.0, 40.0)])
+def test_unified_group_of_eight_long_call(phi, margin_hi, margin_lo):
+    """bf16 with G = 8 on a call of 1,024 units computes every chunk with its
+    own maximum on the matrix-core kernel and derives the range flags from
+    the chunk maxima: the dense result and the oracle's flags (narrow
+    margins flag many chunks on both sides)."""
+    banner(f"unified G=8 long call phi={phi}")
+    c = W.dense_case(8, 64, 8, 8192 - 5, 128, "bf16", 512, seed=1500, device=DEV)
+    flags = _unified_check(c, phi, margin_hi, margin_lo)
+    if margin_hi < 1:
+        assert 0 < flags.mean() < 1
