@@ -19,6 +19,9 @@ hipError_t launch_partial(int, int, int, int, const PartialArgs&, hipStream_t) {
   no_launch("partial kernel");
 }
 hipError_t launch_merge(int, int, const MergeArgs&, hipStream_t) { no_launch("merge kernel"); }
+hipError_t launch_range_flags(const float*, uint8_t*, size_t, float, float, hipStream_t) {
+  no_launch("range flags kernel");
+}
 hipError_t launch_ffd_pack(int, const FfdPackArgs&, hipStream_t) { no_launch("FFD pack kernel"); }
 hipError_t launch_ffd(int, int, const FfdArgs&, hipStream_t) { no_launch("FFD kernel"); }
 hipError_t launch_multi(int, const MultiArgs&, hipStream_t) { no_launch("multi-row kernel"); }
