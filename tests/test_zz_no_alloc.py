@@ -1,7 +1,7 @@
 """fd_decode_attn_noalloc (library-owned partials buffer, no workspace, no
 allocation) against fd_decode_attn, which runs the same kernels on a caller
 workspace: bitwise equal, and within the parity bar of the fp64 oracle, on
-two calls in a row, the second with a smaller input."""
+calls in a row, each with a smaller input than the one before."""
 import ctypes as C
 
 import pytest
@@ -19,7 +19,10 @@ DEV = "cuda:0"
 @pytest.mark.gpu
 def test_noalloc_matches_workspace_entry_point_twice():
     cases = [
-        # larger first: B 4, Hq 32, Hkv 8, d 128, L 20000 (40 chunks of 512, ragged)
+        # largest first: eight heads per kv-head on 1,024 units, which runs on
+        # the matrix-core kernel (B 8, Hq 64, Hkv 8, d 128, L 8187)
+        (8, 64, 8, 8187, 128, "bf16", 512, 73),
+        # B 4, Hq 32, Hkv 8, d 128, L 20000 (40 chunks of 512, ragged)
         (4, 32, 8, 20000, 128, "bf16", 512, 71),
         # then smaller, another dtype and head size: what the first call left
         # in the buffer must not leak into this one
