@@ -78,9 +78,34 @@ def test_calls_on_two_streams_match_eager():
             assert torch.equal(outs[i], ref[i]), (rep, i)
 
 
+def _more_calls(calls, outs):
+    """Fixed maximum (with its flags) and FFD on fixed buffers."""
+    c = W.dense_case(4, 32, 8, 16384, 128, "bf16", 512, seed=1604, device=DEV)
+    o = torch.empty((4, 32, 128), dtype=torch.float32, device=DEV)
+    l = torch.empty((4, 32), dtype=torch.float32, device=DEV)
+    f = torch.empty((4, 32, 32), dtype=torch.uint8, device=DEV)
+    ws = torch.empty(fd.workspace_bytes("fd_decode_attn_unified_max", B=4, Hq=32, Hkv=8, L=16384,
+                                        d=128, chunk=512), dtype=torch.uint8, device=DEV)
+    calls.append(lambda: fd.decode_attn_unified_max(c.q, c.k, c.v, 3.0, chunk=512, margin_hi=0.5,
+                                                    margin_lo=0.5, out=o, lse=l, flags=f,
+                                                    workspace=ws))
+    outs += [o, l, f]
+    fc = W.ffd_case(2, 32, 8, 8192, 128, seed=1605, device=DEV)
+    pk = fd.ffd_pack(fc.k)
+    o2 = torch.empty((2, 32, 128), dtype=torch.float32, device=DEV)
+    l2 = torch.empty((2, 32), dtype=torch.float32, device=DEV)
+    ws2 = torch.empty(fd.workspace_bytes("fd_ffd_sparse_decode", B=2, Hq=32, Hkv=8, L=8192,
+                                         d=128, chunk=1024), dtype=torch.uint8, device=DEV)
+    calls.append(lambda: fd.ffd_sparse_decode(fc.q, pk, fc.v, 5.0, chunk=1024, out=o2, lse=l2,
+                                              workspace=ws2))
+    outs += [o2, l2]
+    return c, fc, pk
+
+
 def test_graph_replays_match_eager():
     dense, g8, pm = _cases()
     calls, outs = _preallocated(dense, g8, pm)
+    keep = _more_calls(calls, outs)   # noqa: F841 (inputs stay alive for the replays)
     for call in calls:
         call()
     torch.cuda.synchronize()
@@ -91,7 +116,7 @@ def test_graph_replays_match_eager():
             call()
     for rep in range(3):
         for t in outs:
-            t.fill_(float("nan"))
+            t.fill_(float("nan") if t.is_floating_point() else 255)
         torch.cuda.synchronize()
         graph.replay()
         torch.cuda.synchronize()
