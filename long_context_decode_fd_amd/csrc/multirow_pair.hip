@@ -3,12 +3,14 @@
 // flat GEMM case of the "FlashDecoding" deployment blog, section 1).
 //
 // A workgroup is two waves working on the same unit (sequence, kv-head,
-// chunk).  Wave w owns query rows 16 w .. 16 w + 15, so each keeps the
-// one-tile register budget (two waves per SIMD) instead of one wave holding
-// both tiles.  The K and V rows of a batch are read from HBM once: each wave
-// loads half of the batch's 16-position tiles (tiles w and w + 2) with
-// coalesced 16-byte loads and writes them into the workgroup's LDS, where
-// both waves read every tile:
+// chunk).  Wave w owns query rows 16 w .. 16 w + 15, so each holds one
+// query tile's accumulators instead of one wave holding both tiles.  A batch
+// is eight 16-position tiles (128 positions) and a wave has the SIMD to
+// itself, so its registers hold its four K and four V tiles in flight.  The
+// K and V rows of a batch are read from HBM once: each wave loads half of
+// the batch's tiles (tiles w, w + 2, w + 4, w + 6) with coalesced 16-byte
+// loads and writes them into the workgroup's LDS, where both waves read
+// every tile:
 //
 //   barrier 1   both waves are done reading the previous batch's tiles
 //   own tiles   registers -> LDS, then the next batch's loads are issued
@@ -28,7 +30,7 @@ namespace fdk {
 
 namespace {
 
-constexpr int kPairTiles = 4;   // 16-position tiles per batch (two per wave)
+constexpr int kPairTiles = 8;   // 16-position tiles per batch (four per wave)
 
 // LDS row strides (bytes) of the 16-row K and V tiles.  Row r of a K tile
 // starts 4 r banks (of 4 bytes) on, so the 16-byte operand reads of rows
@@ -47,7 +49,7 @@ constexpr int kVStride = 2 * D + 32;
 
 // PAGED: k and v are page pools, as in the one-tile kernel.
 template <int D, bool PAGED>
-__global__ __launch_bounds__(2 * kWave) __attribute__((amdgpu_waves_per_eu(2)))
+__global__ __launch_bounds__(2 * kWave) __attribute__((amdgpu_waves_per_eu(1)))
 void multi_pair_kernel(MultiArgs a0) {
   // paged: the split may grow on the device (paged_split_factor)
   MultiArgs a = a0;
