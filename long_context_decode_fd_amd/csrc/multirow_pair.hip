@@ -122,15 +122,27 @@ void multi_pair_kernel(MultiArgs a0) {
       if (u == u_last) x.c1 = min(x.c1, pos1);
     }
   };
-  // first byte of row t0 (a multiple of 16 in [c0, c1) when `used`; else
-  // nothing is read there and any row will do) of unit x's K or V
+  // paged: the pool page of each of this wave's tiles of the batch at T
+  // (uniform; 0 for tiles past the chunk end c1, which read nothing).  Read
+  // from LDS before the batch's tiles are written there, so that waiting
+  // for these reads does not also wait for those writes.
   const int shift = a.page_shift, pmask = (1 << a.page_shift) - 1;
-  auto row_base = [&](const void* t, const UnitM& x, int buf, int t0, bool used) {
+  auto tile_pages = [&](const UnitM& x, int buf, int T, int c1, int (&pg)[TW]) {
     if constexpr (PAGED) {
-      const int p = used ? s_pid[wave][buf][(t0 - x.c0) >> shift] : 0;
-      const int pc = min(max(__builtin_amdgcn_readfirstlane(p), 0), a.num_pages - 1);
+#pragma unroll
+      for (int j = 0; j < TW; ++j) {
+        const int t0 = T + 16 * (2 * j + wave);
+        const int p = t0 < c1 ? s_pid[wave][buf][(t0 - x.c0) >> shift] : 0;
+        pg[j] = min(max(__builtin_amdgcn_readfirstlane(p), 0), a.num_pages - 1);
+      }
+    }
+  };
+  // first byte of row t0 (a multiple of 16) of unit x's K or V; pg: its
+  // pool page (paged)
+  auto row_base = [&](const void* t, const UnitM& x, int pg, int t0) {
+    if constexpr (PAGED) {
       return reinterpret_cast<const char*>(t) +
-             ((((size_t)pc * a.Hkv + x.kvh) << shift) + (size_t)(t0 & pmask)) * ROWB;
+             ((((size_t)pg * a.Hkv + x.kvh) << shift) + (size_t)(t0 & pmask)) * ROWB;
     } else {
       return reinterpret_cast<const char*>(t) +
              (((size_t)x.b * a.Hkv + x.kvh) * (size_t)a.L + (size_t)t0) * ROWB;
@@ -152,15 +164,16 @@ void multi_pair_kernel(MultiArgs a0) {
       for (int s = 0; s < KS; ++s) qf[s] = u32x4{0, 0, 0, 0};
     }
   };
-  // this wave's tiles 2 j + wave of the batch at T: one buffer descriptor per
-  // tile, limited to the chunk end c1 (rows past it read as zeros, untouched)
-  auto issue = [&](const void* t, const UnitM& x, int buf, int T, int c1,
+  // this wave's tiles 2 j + wave of the batch at T (pages pg, tile_pages):
+  // one buffer descriptor per tile, limited to the chunk end c1 (rows past
+  // it read as zeros, untouched)
+  auto issue = [&](const void* t, const UnitM& x, const int (&pg)[TW], int T, int c1,
                    u32x4 (&r)[TW][NI]) {
 #pragma unroll
     for (int j = 0; j < TW; ++j) {
       const int t0 = T + 16 * (2 * j + wave);
       const int nrow = min(max(c1 - t0, 0), 16);
-      const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(row_base(t, x, buf, t0, nrow > 0), nrow * ROWB);
+      const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(row_base(t, x, pg[j], t0), nrow * ROWB);
 #pragma unroll
       for (int i = 0; i < NI; ++i) r[j][i] = ld16_buf(rs, lane_off + RPI * i * ROWB);
     }
@@ -252,8 +265,10 @@ void multi_pair_kernel(MultiArgs a0) {
     page_ids_store(s_pid[wave][0], lane, pid);
   }
   load_q(cur);
-  issue(a.k, cur, buf, cur.c0, cur.c1, kr);
-  issue(a.v, cur, buf, cur.c0, cur.c1, vr);
+  int pg[TW] = {};
+  tile_pages(cur, buf, cur.c0, cur.c1, pg);
+  issue(a.k, cur, pg, cur.c0, cur.c1, kr);
+  issue(a.v, cur, pg, cur.c0, cur.c1, vr);
   while (true) {
     const int un = u + 1;
     const bool has_next = un < u_end;
@@ -271,11 +286,6 @@ void multi_pair_kernel(MultiArgs a0) {
     for (int db = 0; db < DB; ++db) o[db] = f32x4{0.f, 0.f, 0.f, 0.f};
     for (int T = c0; T < c1; T += STEP) {
       __syncthreads();   // the previous batch's tiles are read
-#pragma unroll
-      for (int j = 0; j < TW; ++j) {
-        to_lds(s_k[2 * j + wave], kr[j], KSTR);
-        to_lds(s_v[2 * j + wave], vr[j], VSTR);
-      }
       // next batch's loads, the next unit's first after the last batch; one
       // issue path (scalar selects), so that the compiler's wait counts
       // agree on every path.  After the wave's last batch the limit is 0:
@@ -292,8 +302,14 @@ void multi_pair_kernel(MultiArgs a0) {
         t_next = has_next ? nxt.c0 : T;
         c_end = has_next ? nxt.c1 : T;
       }
-      issue(a.k, xs, b_next, t_next, c_end, kr);
-      issue(a.v, xs, b_next, t_next, c_end, vr);
+      tile_pages(xs, b_next, t_next, c_end, pg);
+#pragma unroll
+      for (int j = 0; j < TW; ++j) {
+        to_lds(s_k[2 * j + wave], kr[j], KSTR);
+        to_lds(s_v[2 * j + wave], vr[j], VSTR);
+      }
+      issue(a.k, xs, pg, t_next, c_end, kr);
+      issue(a.v, xs, pg, t_next, c_end, vr);
       __syncthreads();   // the batch is in LDS
 
       float sc[TT][4];
@@ -379,8 +395,9 @@ void multi_pair_kernel(MultiArgs a0) {
       if (c1 <= c0 && has_next) {
         load_q(nxt);
         page_ids_store(s_pid[wave][buf ^ 1], lane, pid);
-        issue(a.k, nxt, buf ^ 1, nxt.c0, nxt.c1, kr);
-        issue(a.v, nxt, buf ^ 1, nxt.c0, nxt.c1, vr);
+        tile_pages(nxt, buf ^ 1, nxt.c0, nxt.c1, pg);
+        issue(a.k, nxt, pg, nxt.c0, nxt.c1, kr);
+        issue(a.v, nxt, pg, nxt.c0, nxt.c1, vr);
       }
     }
     if (!has_next) break;
