@@ -23,7 +23,8 @@
 // The operand layouts and the softmax are those of the one-tile kernel
 // (multirow.hpp).  At the end of a unit each wave stages its 16 O rows in
 // its own two K tiles (after a barrier) so that every partial store writes
-// 16 bytes per lane and whole rows.
+// 16 bytes per lane and whole rows; the stores go out beside the next
+// batch's loads.
 #include "multirow.hpp"
 
 namespace fdk {
@@ -197,12 +198,18 @@ void multi_pair_kernel(MultiArgs a0) {
                      : (((size_t)x.b * a.M + r / G) * a.Hq + (size_t)x.kvh * G + r % G) * a.nc +
                            x.c;
   };
-  auto store_unit = [&](const f32x4 (&o)[DB], float m, float l, const UnitM& x) {
-    float* const op = x.xw >= 0 ? a.x_o : a.o_part;
-    float* const mlp = x.xw >= 0 ? a.x_ml : a.ml_part;
-    if (qd == 0 && qrow < R)
-      *reinterpret_cast<f32x2*>(mlp + part_row(x, qrow) * 2) =
-          f32x2{(m == kNegInf) ? kNegInf : m * c_log2, l};
+  // A finished unit's partials are staged into registers (through the
+  // wave's own two K tiles, for 16-byte stores of whole rows) and written,
+  // non-temporally (the merge reads them once, in another launch), after
+  // the next batch's loads are issued: stores and loads share one wait
+  // counter, and beside the next loads their latency overlaps theirs.
+  constexpr int NST = 16 / ORPI;   // 16-byte stores per lane per unit
+  f32x4 pv[NST];
+  f32x2 pml = f32x2{0.f, 0.f};
+  UnitM px{};
+  bool pend = false;   // wave-uniform
+  auto stage_unit = [&](const f32x4 (&o)[DB], float m, float l, const UnitM& x) {
+    pml = f32x2{(m == kNegInf) ? kNegInf : m * c_log2, l};
     // lane (n, qd) holds O rows 4 qd + e, dims 16 db + n
 #pragma unroll
     for (int e = 0; e < 4; ++e)
@@ -210,13 +217,28 @@ void multi_pair_kernel(MultiArgs a0) {
       for (int db = 0; db < DB; ++db)
         *reinterpret_cast<float*>(o_stage(4 * qd + e) + (16 * db + n) * 4) = o[db][e];
 #pragma unroll
-    for (int i = 0; i < 16 / ORPI; ++i) {
+    for (int i = 0; i < NST; ++i) {
       const int rr = ORPI * i + lane / LPO, cb = 16 * (lane % LPO);
-      const f32x4 v = *reinterpret_cast<const f32x4*>(o_stage(rr) + cb);
+      pv[i] = *reinterpret_cast<const f32x4*>(o_stage(rr) + cb);
+    }
+    px = x;
+    pend = true;
+  };
+  auto flush = [&]() {
+    if (!pend) return;
+    pend = false;
+    float* const op = px.xw >= 0 ? a.x_o : a.o_part;
+    float* const mlp = px.xw >= 0 ? a.x_ml : a.ml_part;
+    if (qd == 0 && qrow < R)
+      __builtin_nontemporal_store(pml, reinterpret_cast<f32x2*>(mlp + part_row(px, qrow) * 2));
+#pragma unroll
+    for (int i = 0; i < NST; ++i) {
+      const int rr = ORPI * i + lane / LPO, cb = 16 * (lane % LPO);
       const int row = row0 + rr;
       if (row < R)
-        *reinterpret_cast<f32x4*>(reinterpret_cast<unsigned char*>(op + part_row(x, row) * D) +
-                                  cb) = v;
+        __builtin_nontemporal_store(
+            pv[i], reinterpret_cast<f32x4*>(reinterpret_cast<unsigned char*>(op + part_row(px, row) * D) +
+                                            cb));
     }
   };
 
@@ -310,6 +332,7 @@ void multi_pair_kernel(MultiArgs a0) {
       }
       issue(a.k, xs, pg, t_next, c_end, kr);
       issue(a.v, xs, pg, t_next, c_end, vr);
+      flush();   // the previous unit's partials
       __syncthreads();   // the batch is in LDS
 
       float sc[TT][4];
@@ -388,7 +411,8 @@ void multi_pair_kernel(MultiArgs a0) {
     // l of row n: the four lanes of the row hold parts
     l = pair_sum<32>(pair_sum<16>(l));
     __syncthreads();   // no wave reads the tiles any more
-    store_unit(o, m, l, cur);
+    flush();   // still pending only when this unit ran no batch
+    stage_unit(o, m, l, cur);
     if constexpr (PAGED) {
       // an empty split ran no batch, so nothing requested the next one's
       // query and first rows yet
@@ -405,6 +429,7 @@ void multi_pair_kernel(MultiArgs a0) {
     u = un;
     if constexpr (PAGED) buf ^= 1;
   }
+  flush();
 }
 
 // Units that run at once: one per workgroup (wave pair).
