@@ -616,49 +616,58 @@ def variant_paged(torch, fd, W, args, timer):
 def variant_paged_multi(torch, fd, W, args, timer):
     """Four new tokens per sequence over the paged workload's cache (16
     sequences of U[1024, 131072] positions, pages of 16, chunk 1024 and 2048
-    beside it): G*M = 16 query rows per kv-head on the matrix-core kernel."""
+    beside it): G*M = 16 query rows per kv-head on the matrix-core kernel;
+    under M_8 the same with eight tokens (32 rows, the wave pair)."""
     cfg = W.CONFIGS[3]
-    M = 4
-    c = W.paged_case(cfg["B"], cfg["Hq"], cfg["Hkv"], cfg["d"], cfg["len_lo"], cfg["len_hi"],
-                     page=cfg["page"], chunk=cfg["chunk"], seed=cfg["seed"], device="cuda:0",
-                     M=M)
-    B, _, Hq, d = c.q.shape
-    Hkv = c.k_pool.shape[1]
-    lens = c.meta["lens"]
-    max_len = int(max(lens))
-    lib = fd.lib()
-    out = torch.empty((B, M, Hq, d), dtype=torch.float32, device="cuda:0")
-    lse = torch.empty((B, M, Hq), dtype=torch.float32, device="cuda:0")
-    st = C.c_void_p(torch.cuda.current_stream().cuda_stream)
 
-    def timed(chunk):
-        wsn = fd.workspace_bytes("fd_decode_attn_multi_paged", B=B, M=M, Hq=Hq, Hkv=Hkv, d=d,
-                                 page=c.page, max_pages=c.block_table.shape[1],
-                                 max_seq_len=max_len, chunk=chunk)
-        ws = torch.empty(wsn, dtype=torch.uint8, device="cuda:0")
-        size = C.c_size_t(wsn)
-        a = (fd.FD_BF16, vp(c.q), vp(c.k_pool), vp(c.v_pool), vp(c.block_table),
-             vp(c.seq_lens), vp(out), vp(lse), B, M, Hq, Hkv, d, c.page,
-             c.block_table.shape[1], c.k_pool.shape[0], max_len, c.scale, chunk, vp(ws),
-             C.byref(size), st)
-        call = lambda: lib.fd_decode_attn_multi_paged(*a)  # noqa: E731
-        check_rc(lib, call())
-        return timer.run([call], args.steps, args.warmup)
+    def measure(M):
+        c = W.paged_case(cfg["B"], cfg["Hq"], cfg["Hkv"], cfg["d"], cfg["len_lo"], cfg["len_hi"],
+                         page=cfg["page"], chunk=cfg["chunk"], seed=cfg["seed"], device="cuda:0",
+                         M=M)
+        B, _, Hq, d = c.q.shape
+        Hkv = c.k_pool.shape[1]
+        lens = c.meta["lens"]
+        max_len = int(max(lens))
+        lib = fd.lib()
+        out = torch.empty((B, M, Hq, d), dtype=torch.float32, device="cuda:0")
+        lse = torch.empty((B, M, Hq), dtype=torch.float32, device="cuda:0")
+        st = C.c_void_p(torch.cuda.current_stream().cuda_stream)
 
-    t = timed(c.chunk)
-    t2 = timed(2 * c.chunk)
-    total_len = int(sum(lens))
-    nbytes = (2 * total_len * Hkv * d * 2 + B * M * Hq * d * 2 + B * M * Hq * (d + 1) * 4
-              + 4 * int(sum((L + c.page - 1) // c.page for L in lens)))
-    return dict(workload=f"paged ragged multi-row decode bf16, M={M} tokens, B={B}, Hq={Hq}, "
-                         f"Hkv={Hkv}, d={d}, page={c.page}, lens U[{cfg['len_lo']},"
-                         f"{cfg['len_hi']}] (sum {total_len}), chunk={c.chunk}",
-                us_per_step=round(t["ms"] * 1e3, 2), p10_us=round(t["p10"] * 1e3, 2),
-                p90_us=round(t["p90"] * 1e3, 2), bytes=nbytes,
-                gbs=round(gbs(nbytes, t["ms"]), 1),
-                pct_of_peak=round(100 * gbs(nbytes, t["ms"]) / PEAK_GBS, 1),
-                us_per_step_chunk2048=round(t2["ms"] * 1e3, 2),
-                pct_of_peak_chunk2048=round(100 * gbs(nbytes, t2["ms"]) / PEAK_GBS, 1))
+        def timed(chunk):
+            wsn = fd.workspace_bytes("fd_decode_attn_multi_paged", B=B, M=M, Hq=Hq, Hkv=Hkv, d=d,
+                                     page=c.page, max_pages=c.block_table.shape[1],
+                                     max_seq_len=max_len, chunk=chunk)
+            ws = torch.empty(wsn, dtype=torch.uint8, device="cuda:0")
+            size = C.c_size_t(wsn)
+            a = (fd.FD_BF16, vp(c.q), vp(c.k_pool), vp(c.v_pool), vp(c.block_table),
+                 vp(c.seq_lens), vp(out), vp(lse), B, M, Hq, Hkv, d, c.page,
+                 c.block_table.shape[1], c.k_pool.shape[0], max_len, c.scale, chunk, vp(ws),
+                 C.byref(size), st)
+            call = lambda: lib.fd_decode_attn_multi_paged(*a)  # noqa: E731
+            check_rc(lib, call())
+            return timer.run([call], args.steps, args.warmup)
+
+        t = timed(c.chunk)
+        t2 = timed(2 * c.chunk)
+        total_len = int(sum(lens))
+        nbytes = (2 * total_len * Hkv * d * 2 + B * M * Hq * d * 2 + B * M * Hq * (d + 1) * 4
+                  + 4 * int(sum((L + c.page - 1) // c.page for L in lens)))
+        res = dict(workload=f"paged ragged multi-row decode bf16, M={M} tokens, B={B}, Hq={Hq}, "
+                            f"Hkv={Hkv}, d={d}, page={c.page}, lens U[{cfg['len_lo']},"
+                            f"{cfg['len_hi']}] (sum {total_len}), chunk={c.chunk}",
+                   us_per_step=round(t["ms"] * 1e3, 2), p10_us=round(t["p10"] * 1e3, 2),
+                   p90_us=round(t["p90"] * 1e3, 2), bytes=nbytes,
+                   gbs=round(gbs(nbytes, t["ms"]), 1),
+                   pct_of_peak=round(100 * gbs(nbytes, t["ms"]) / PEAK_GBS, 1),
+                   us_per_step_chunk2048=round(t2["ms"] * 1e3, 2),
+                   pct_of_peak_chunk2048=round(100 * gbs(nbytes, t2["ms"]) / PEAK_GBS, 1))
+        del c, out, lse
+        torch.cuda.empty_cache()
+        return res
+
+    res = measure(4)
+    res["M_8"] = measure(8)
+    return res
 
 
 def variant_unified(torch, fd, W, args, timer):
