@@ -132,11 +132,25 @@ def test_paged_multi_row_long_ragged_sampled(M):
 def test_paged_multi_row_one_million_positions(M):
     """A sequence of 2^20 + 77 positions (65,541 pages of 16) beside a short
     one, M new tokens, chunk 1024: 1,025 chunks per row, so the merge walks
-    its tiles of 256 chunks; the one-tile kernel (M = 4) divides the 131,120
-    pages of both kv-heads over its workers, the wave pair (M = 8) takes
-    whole chunks.  Every token and head against the oracle."""
+    its tiles of 256 chunks; the one-tile kernel (M = 4) and the wave pair
+    (M = 8) each divide the 131,120 pages of both kv-heads over their
+    workers.  Every token and head against the oracle."""
     banner(f"paged multi 1M M={M}")
     lens = [(1 << 20) + 77, 300]
     c = W.paged_case(2, 8, 2, 128, 0, lens[0], page=16, chunk=1024, seed=104 + M, device=DEV,
                      lens=lens, M=M)
     _check(c, lens[0], 1024)
+
+
+def test_paged_multi_row_many_short_units():
+    """Forty-eight sequences of 1-600 positions, M = 8 (32 rows per kv-head,
+    the wave pair), chunk 64: about two units and a cut split per worker, so
+    each worker writes one unit's partials beside the next unit's loads
+    several times and the fix-up folds the cut parts.  Every row against
+    the oracle."""
+    banner("paged multi many short units M=8")
+    rs = np.random.RandomState(105)
+    lens = [int(x) for x in rs.randint(1, 601, size=48)]
+    c = W.paged_case(len(lens), 32, 8, 128, 0, max(lens), page=16, chunk=64, seed=105,
+                     device=DEV, lens=lens, M=8)
+    _check(c, max(lens), 64)
