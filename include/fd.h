@@ -260,7 +260,8 @@ int fd_decode_attn_multi(fd_dtype_t dt, const void* q, const void* k,
  *   divided evenly over the device's workers, so a worker may take a split
  *   from a page inside it on, and a second kernel folds that part into the
  *   split's partials with the same exact merge; the kernels also lengthen
- *   the split to chunk * F (F a power of two, at most 256 pages) as long as
+ *   the split to chunk * F (F a power of two up to 256; at most 256 pages
+ *   per split on the one-tile kernel, 512 on the wave pair) as long as
  *   every worker still gets a split's pages.
  * Workspace: the partials of B*M*Hq rows over nc = ceil(max_seq_len / chunk)
  * chunks (layout of fd_decode_attn_partials with M*Hq heads; a longer split

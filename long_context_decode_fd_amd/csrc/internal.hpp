@@ -106,8 +106,9 @@ struct MultiArgs {
   float* x_ml;
   int32_t* x_meta;
   int x_cap;
-  // Paged: the kernel lengthens the split to chunk * F (F a power of two, at
-  // most kMultiPagePids pages) as far as the workers keep their number, and
+  // Paged: the kernel lengthens the split to chunk * F (F a power of two up
+  // to 256, within the kernel's page-id buffer: kMultiPagePids pages, twice
+  // that on the wave pair) as far as the workers keep their number, and
   // writes F here for the merge.
   int32_t* x_split;
 };

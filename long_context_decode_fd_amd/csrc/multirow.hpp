@@ -82,18 +82,20 @@ constexpr int kPidPerLane = kMultiPagePids / kWave;
 // register whose previous load may still be in flight would make the
 // compiler wait for every load issued before it.  A split holds positions
 // (c0 < c1 <= the sequence's length), so its entries lie inside the table row.
+template <int NP = kMultiPagePids>
 __device__ __forceinline__ void page_ids_load(const MultiArgs& a, int b, int c0, int c1,
-                                              int lane, int (&v)[kPidPerLane]) {
+                                              int lane, int (&v)[NP / kWave]) {
   const int shift = a.page_shift;
   const int last = max((c1 - c0 + (1 << shift) - 1) >> shift, 1) - 1;
   const int32_t* bt = a.block_table + (size_t)b * a.max_pages + (c0 >> shift);
 #pragma unroll
-  for (int j = 0; j < kPidPerLane; ++j) v[j] = bt[min(lane + j * kWave, last)];
+  for (int j = 0; j < NP / kWave; ++j) v[j] = bt[min(lane + j * kWave, last)];
 }
 
-__device__ __forceinline__ void page_ids_store(int* dst, int lane, const int (&v)[kPidPerLane]) {
+template <int NP = kMultiPagePids>
+__device__ __forceinline__ void page_ids_store(int* dst, int lane, const int (&v)[NP / kWave]) {
 #pragma unroll
-  for (int j = 0; j < kPidPerLane; ++j) dst[lane + j * kWave] = v[j];
+  for (int j = 0; j < NP / kWave; ++j) dst[lane + j * kWave] = v[j];
 }
 
 // Paged caches: the units that hold positions, (b, kvh, c) with
@@ -207,15 +209,17 @@ __device__ __forceinline__ long long paged_workers(const MultiArgs& a, long long
 }
 
 // Split factor F: the split grows to chunk * F (F a power of two, at most
-// kMultiPagePids pages) while the same number of workers still get a
-// split's pages each.  Longer splits cut the partials written and merged
-// and the unit changes; the workers' count keeps the device busy (the
-// lengths decide it, so it is chosen here, not by the host).
-__device__ __forceinline__ int paged_split_factor(const MultiArgs& a, long long P, int n) {
+// 256, and at most max_pages pages: the kernel's page-id buffer) while the
+// same number of workers still get a split's pages each.  Longer splits cut
+// the partials written and merged and the unit changes; the workers' count
+// keeps the device busy (the lengths decide it, so it is chosen here, not
+// by the host).
+__device__ __forceinline__ int paged_split_factor(const MultiArgs& a, long long P, int n,
+                                                  int max_pages = kMultiPagePids) {
   const int cpp = a.chunk >> a.page_shift;
   const long long na = paged_workers(a, P, n);
   int F = 1;
-  while (cpp * 2 * F <= kMultiPagePids && P / ((long long)cpp * 2 * F) >= na) F *= 2;
+  while (2 * F <= 256 && cpp * 2 * F <= max_pages && P / ((long long)cpp * 2 * F) >= na) F *= 2;
   return F;
 }
 

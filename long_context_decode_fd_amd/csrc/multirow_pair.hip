@@ -32,6 +32,9 @@ namespace fdk {
 namespace {
 
 constexpr int kPairTiles = 8;   // 16-position tiles per batch (four per wave)
+// paged: pages per split at most (the page-id buffer); twice the one-tile
+// kernel's, so that a worker of a ragged cache ends fewer units
+constexpr int kPairPagePids = 2 * kMultiPagePids;
 
 // LDS row strides (bytes) of the 16-row K and V tiles.  Row r of a K tile
 // starts 4 r banks (of 4 bytes) on, so the 16-byte operand reads of rows
@@ -72,7 +75,7 @@ void multi_pair_kernel(MultiArgs a0) {
   __shared__ __align__(16) unsigned char s_k[TT][16 * KSTR];
   __shared__ __align__(16) unsigned char s_v[TT][16 * VSTR];
   // paged: each wave's copy of the page ids of the current and next split
-  __shared__ int s_pid[PAGED ? 2 : 1][2][PAGED ? kMultiPagePids : 1];
+  __shared__ int s_pid[PAGED ? 2 : 1][2][PAGED ? kPairPagePids : 1];
 
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & (kWave - 1);
   const int n = lane & 15, qd = lane >> 4;
@@ -248,7 +251,7 @@ void multi_pair_kernel(MultiArgs a0) {
   int u, u_end;
   if constexpr (PAGED) {
     const long long P = paged_pages(a, lane);
-    const int F = paged_split_factor(a, P, (int)gridDim.x);
+    const int F = paged_split_factor(a, P, (int)gridDim.x, kPairPagePids);
     a.chunk *= F;
     if (blockIdx.x == 0 && threadIdx.x == 0) *a.x_split = F;   // for the merge
     PagedSpot s0{}, s1{};
@@ -281,10 +284,10 @@ void multi_pair_kernel(MultiArgs a0) {
   decode(u, cur);
   u32x4 kr[TW][NI], vr[TW][NI];
   int buf = 0;   // LDS copy of the current unit's page ids (paged)
-  int pid[kPidPerLane];
+  int pid[kPairPagePids / kWave];
   if constexpr (PAGED) {
-    page_ids_load(a, cur.b, cur.c0, cur.c1, lane, pid);
-    page_ids_store(s_pid[wave][0], lane, pid);
+    page_ids_load<kPairPagePids>(a, cur.b, cur.c0, cur.c1, lane, pid);
+    page_ids_store<kPairPagePids>(s_pid[wave][0], lane, pid);
   }
   load_q(cur);
   int pg[TW] = {};
@@ -297,7 +300,7 @@ void multi_pair_kernel(MultiArgs a0) {
     UnitM nxt = cur;
     if (has_next) decode(un, nxt);
     if constexpr (PAGED) {
-      if (has_next) page_ids_load(a, nxt.b, nxt.c0, nxt.c1, lane, pid);
+      if (has_next) page_ids_load<kPairPagePids>(a, nxt.b, nxt.c0, nxt.c1, lane, pid);
     }
     const int c0 = cur.c0, c1 = cur.c1;
     const int lim = cur.L - a.M + qrow / G;
@@ -317,7 +320,7 @@ void multi_pair_kernel(MultiArgs a0) {
       int t_next = T + STEP, c_end = c1, b_next = buf;
       if (last) {
         if constexpr (PAGED) {
-          if (has_next) page_ids_store(s_pid[wave][buf ^ 1], lane, pid);
+          if (has_next) page_ids_store<kPairPagePids>(s_pid[wave][buf ^ 1], lane, pid);
         }
         xs = nxt;
         b_next = buf ^ 1;
@@ -418,7 +421,7 @@ void multi_pair_kernel(MultiArgs a0) {
       // query and first rows yet
       if (c1 <= c0 && has_next) {
         load_q(nxt);
-        page_ids_store(s_pid[wave][buf ^ 1], lane, pid);
+        page_ids_store<kPairPagePids>(s_pid[wave][buf ^ 1], lane, pid);
         tile_pages(nxt, buf ^ 1, nxt.c0, nxt.c1, pg);
         issue(a.k, nxt, pg, nxt.c0, nxt.c1, kr);
         issue(a.v, nxt, pg, nxt.c0, nxt.c1, vr);
